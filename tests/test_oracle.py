@@ -1,0 +1,406 @@
+"""Pins of the CPU oracle against facts that do not depend on the oracle itself:
+exact integer arithmetic, hand-worked rounding cases, textbook error bounds,
+brute force on tiny inputs, library routines (torch CPU softmax, SwiGLU and
+autograd, torch's float8_e4m3fn cast), closed forms and invariants.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from moe_inputs import Workload, make_inputs, LayerInputs
+
+
+def tiny(T=16, H=64, I=32, E=4, k=2, **kw):
+    return Workload("pin", T=T, H=H, I=I, E=E, k=k, stream=9000 + T + H + I + E + k, **kw)
+
+
+# ---------------------------------------------------------------- logits
+
+def test_logits_integer_inputs_are_exact_dot_products():
+    rng = np.random.default_rng(1)
+    T, H, E = 5, 256, 7
+    x = rng.integers(-8, 9, size=(T, H)).astype(np.float32)
+    Wr = rng.integers(-8, 9, size=(H, E)).astype(np.float32)
+    bias = rng.integers(-100, 100, size=E).astype(np.float32)
+    got = O.router_logits(x, Wr, bias)
+    exact = [[sum(int(x[t, h]) * int(Wr[h, e]) for h in range(H)) + int(bias[e]) for e in range(E)]
+             for t in range(T)]
+    assert (got == np.array(exact, dtype=np.float32)).all()
+
+
+def _one_hot_dot(H, entries):
+    """x = 1 at the given h, Wr[:,0] = value there; all else 0."""
+    x = np.zeros((1, H), np.float32)
+    Wr = np.zeros((H, 1), np.float32)
+    for h, (xv, wv) in entries.items():
+        x[0, h] = xv
+        Wr[h, 0] = wv
+    return O.router_logits(x, Wr)[0, 0]
+
+
+def test_logits_lane_then_tree_order():
+    # lane 0 sums h=0 (2^24) then h=64 (+1): 2^24+1 is a tie, rounds to even 2^24.
+    # lane 1 holds -2^24.  Tree merges lanes 0 and 1 last: result 0.
+    # Plain left-to-right summation would give 1.
+    v = _one_hot_dot(128, {0: (1.0, 2.0 ** 24), 1: (1.0, -2.0 ** 24), 64: (1.0, 1.0)})
+    assert v == 0.0
+    # lane 32 (+1) merges into lane 0 (2^24) at the first tree level (tie -> 2^24),
+    # before lane 1 (-2^24) does at the last: 0.  A pairwise tree of neighbours gives 1.
+    v = _one_hot_dot(64, {0: (1.0, 2.0 ** 24), 1: (1.0, -2.0 ** 24), 32: (1.0, 1.0)})
+    assert v == 0.0
+    # lane 2 (+1) merges into lane 0 at s=2, before lane 1 at s=1: 0 again.
+    v = _one_hot_dot(64, {0: (1.0, 2.0 ** 24), 1: (1.0, -2.0 ** 24), 2: (1.0, 1.0)})
+    assert v == 0.0
+    # lane 1 (-2^24) and lane 33 (+1) merge first: -2^24+1 = -(2^24-1), exact.
+    # then lane 0 (2^24) + that = 1.
+    v = _one_hot_dot(64, {0: (1.0, 2.0 ** 24), 1: (1.0, -2.0 ** 24), 33: (1.0, 1.0)})
+    assert v == 1.0
+
+
+def test_logits_use_fused_multiply_add():
+    # lane 0: first -1, then (1+2^-12)^2 = 1 + 2^-11 + 2^-24 added in one rounding.
+    # A separate multiply would round the product to 1 + 2^-11 and give 2^-11.
+    a = 1.0 + 2.0 ** -12
+    v = _one_hot_dot(128, {0: (-1.0, 1.0), 64: (a, a)})
+    assert v == np.float32(2.0 ** -11 + 2.0 ** -24)
+
+
+def test_logits_within_textbook_bound():
+    rng = np.random.default_rng(2)
+    T, H, E = 32, 2048, 16
+    x = torch.randn(T, H, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    Wr = rng.normal(0, 0.02, size=(H, E)).astype(np.float32)
+    got = O.router_logits(x, Wr).astype(np.float64)
+    x64 = x.double().numpy()
+    exact = x64 @ Wr.astype(np.float64)
+    # each logit passes through at most H/64 + 6 fp32 roundings
+    n = H // 64 + 6
+    u = 2.0 ** -24
+    gamma = n * u / (1 - n * u)
+    bound = gamma * (np.abs(x64) @ np.abs(Wr.astype(np.float64)))
+    assert (np.abs(got - exact) <= bound).all()
+
+
+def test_logits_reject_h_not_multiple_of_64():
+    with pytest.raises(ValueError):
+        O.router_logits(np.zeros((1, 96), np.float32), np.zeros((96, 2), np.float32))
+
+
+# ---------------------------------------------------------------- selection
+
+def test_topk_matches_brute_force_sort():
+    rng = np.random.default_rng(4)
+    logits = rng.normal(size=(50, 9)).astype(np.float32)
+    logits[3, 2] = logits[3, 5]  # a tie
+    logits[7, :] = 0.0
+    logits[8, 1], logits[8, 4] = -0.0, 0.0  # signed zeros compare equal
+    for k in (1, 3, 9):
+        idx = O.topk_select(logits, k)
+        for t in range(logits.shape[0]):
+            want = sorted(range(9), key=lambda e: (-float(logits[t, e]), e))[:k]
+            assert list(idx[t]) == want
+
+
+def test_topk_ties_from_identical_router_columns_pick_lower_index():
+    w = tiny(T=32, E=6, k=3)
+    inp = make_inputs(w)
+    Wr = O.as_f32(inp.Wr).copy()
+    Wr[:, 4] = Wr[:, 1]  # experts 1 and 4 always tie exactly
+    logits, idx, _ = O.route(inp.x, Wr, None, 6)
+    for t in range(32):
+        row = list(idx[t])
+        assert row.index(1) < row.index(4)
+
+
+def test_gate_weights_closed_forms():
+    rng = np.random.default_rng(5)
+    logits = rng.normal(size=(40, 8)).astype(np.float32)
+    # k=1: a single weight of exactly 1
+    idx = O.topk_select(logits, 1)
+    assert (O.gate_weights(logits, idx) == 1.0).all()
+    # k=E: the full softmax (torch CPU, fp64), reordered by selection
+    idx = O.topk_select(logits, 8)
+    ref = torch.softmax(torch.from_numpy(logits.astype(np.float64)), dim=1).numpy()
+    np.testing.assert_allclose(O.gate_weights(logits, idx), np.take_along_axis(ref, idx, 1),
+                               rtol=1e-13, atol=0)
+    # renormalised top-k softmax: weights sum to one, ratios follow exp(l_i - l_j)
+    idx = O.topk_select(logits, 3)
+    gw = O.gate_weights(logits, idx)
+    np.testing.assert_allclose(gw.sum(1), 1.0, rtol=0, atol=1e-15)
+    sel = np.take_along_axis(logits.astype(np.float64), idx.astype(np.int64), 1)
+    np.testing.assert_allclose(gw[:, 1] / gw[:, 0], np.exp(sel[:, 1] - sel[:, 0]), rtol=1e-13)
+
+
+# ---------------------------------------------------------------- layout
+
+def _check_layout(idx, E, counts, offsets, row_token, tok_row):
+    T, k = idx.shape
+    assert counts.sum() == T * k
+    assert offsets[0] == 0 and (np.diff(offsets) == counts).all()
+    # brute force: count directly
+    for e in range(E):
+        assert counts[e] == sum(1 for t in range(T) for j in range(k) if idx[t, j] == e)
+    # rows of each expert are contiguous and in ascending token order
+    for e in range(E):
+        toks = row_token[offsets[e]:offsets[e + 1]]
+        assert (np.diff(toks) > 0).all()
+        for t in toks:
+            assert e in idx[t]
+    # tok_row inverts row_token, and is a bijection onto the rows
+    assert sorted(tok_row.ravel().tolist()) == list(range(T * k))
+    for t in range(T):
+        for j in range(k):
+            r = tok_row[t, j]
+            assert row_token[r] == t
+            assert offsets[idx[t, j]] <= r < offsets[idx[t, j] + 1]
+
+
+def test_layout_invariants_and_brute_force():
+    for (T, E, k, seed) in [(64, 8, 2, 0), (37, 5, 3, 1), (1, 4, 4, 2), (200, 16, 6, 3)]:
+        rng = np.random.default_rng(seed)
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+        _check_layout(idx, E, *O.dispatch_layout(idx, E))
+
+
+def test_layout_empty_experts_and_minibatch_slices():
+    idx = np.array([[0, 3], [3, 0], [0, 3]], np.int32)
+    counts, offsets, row_token, tok_row = O.dispatch_layout(idx, 5)
+    assert counts.tolist() == [3, 0, 0, 3, 0]
+    assert offsets.tolist() == [0, 3, 3, 3, 6, 6]
+    assert row_token.tolist() == [0, 1, 2, 0, 1, 2]
+    assert tok_row.tolist() == [[0, 3], [4, 1], [2, 5]]
+    mbs = O.minibatch_layouts(idx, 5, 2)
+    assert len(mbs) == 2
+    assert mbs[1][0].tolist() == [1, 0, 0, 1, 0] and mbs[1][2].tolist() == [0, 0]
+
+
+# ---------------------------------------------------------------- FFN / forward
+
+def test_single_expert_top1_is_a_dense_swiglu_ffn_torch():
+    w = tiny(T=24, H=128, I=64, E=1, k=1)
+    inp = make_inputs(w)
+    out = O.layer_forward(inp)["out"]
+    x = inp.x.double()
+    ref = (torch.nn.functional.silu(x @ inp.Wg[0].double()) * (x @ inp.Wu[0].double())) @ inp.Wd[0].double()
+    np.testing.assert_allclose(out, ref.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_forward_matches_pure_python_brute_force():
+    w = tiny(T=6, H=64, I=8, E=4, k=2)
+    inp = make_inputs(w)
+    res = O.layer_forward(inp)
+    X = inp.x.double().tolist()
+    Wg, Wu, Wd = (t.double().tolist() for t in (inp.Wg, inp.Wu, inp.Wd))
+    logits = res["logits"]
+    for t in range(w.T):
+        # every expert on the token, then keep the top-k by logit
+        ys = []
+        for e in range(w.E):
+            h = []
+            for i in range(w.I):
+                g = sum(X[t][hh] * Wg[e][hh][i] for hh in range(w.H))
+                u = sum(X[t][hh] * Wu[e][hh][i] for hh in range(w.H))
+                h.append(g / (1 + math.exp(-g)) * u)
+            ys.append([sum(h[i] * Wd[e][i][hh] for i in range(w.I)) for hh in range(w.H)])
+        sel = sorted(range(w.E), key=lambda e: (-float(logits[t, e]), e))[:w.k]
+        z = [math.exp(float(logits[t, e]) - float(logits[t, sel[0]])) for e in sel]
+        ws = [v / sum(z) for v in z]
+        want = [sum(ws[j] * ys[sel[j]][hh] for j in range(w.k)) for hh in range(w.H)]
+        np.testing.assert_allclose(res["out"][t], want, rtol=1e-11, atol=1e-15)
+
+
+def test_identity_experts_return_the_input():
+    inp = make_inputs(tiny(T=40, E=8, k=3))
+    out = O.layer_forward(inp, identity_experts=True)["out"]
+    np.testing.assert_allclose(out, inp.x.double().numpy(), rtol=1e-15, atol=0)
+
+
+def test_top1_combine_returns_the_expert_output():
+    w = tiny(T=30, E=5, k=1)
+    inp = make_inputs(w)
+    res = O.layer_forward(inp, keep=True)
+    np.testing.assert_array_equal(res["out"], res["Y"][:, 0, :])
+
+
+def test_linearity_in_down_projection_is_exact():
+    w = tiny(T=20, E=4, k=2)
+    inp = make_inputs(w)
+    base = O.layer_forward(inp)["out"]
+    inp2 = LayerInputs(w, inp.x, inp.Wr, inp.bias, inp.Wg, inp.Wu, inp.Wd * 2)
+    np.testing.assert_array_equal(O.layer_forward(inp2)["out"], 2 * base)
+
+
+def test_token_permutation_equivariance():
+    w = tiny(T=33, E=6, k=2)
+    inp = make_inputs(w)
+    perm = np.random.default_rng(7).permutation(w.T)
+    a = O.layer_forward(inp)["out"]
+    b = O.layer_forward(inp, tokens=perm)["out"]
+    # per-token math; only BLAS blocking (a function of the row count) may differ
+    np.testing.assert_allclose(a[perm], b, rtol=1e-12, atol=1e-18)
+
+
+def test_token_subset_matches_full_forward():
+    w = tiny(T=50, E=6, k=3)
+    inp = make_inputs(w)
+    full = O.layer_forward(inp)["out"]
+    sub = O.layer_forward(inp, tokens=[3, 17, 49])["out"]
+    np.testing.assert_allclose(full[[3, 17, 49]], sub, rtol=1e-12, atol=1e-18)
+
+
+def test_shared_expert_adds_a_dense_ffn():
+    w = tiny(T=12, E=4, k=2, shared_expert=True)
+    inp = make_inputs(w)
+    with_s = O.layer_forward(inp)["out"]
+    without = O.layer_forward(inp, shared=False)["out"]
+    x = inp.x.double()
+    s = (torch.nn.functional.silu(x @ inp.Wsg.double()) * (x @ inp.Wsu.double())) @ inp.Wsd.double()
+    np.testing.assert_allclose(with_s - without, s.numpy(), rtol=1e-10, atol=1e-14)
+
+
+# ---------------------------------------------------------------- MXFP8
+
+def test_e4m3_decode_table_matches_torch():
+    codes = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    finite = ~np.isnan(codes)
+    assert np.isnan(O.E4M3_TABLE[~finite]).all()
+    np.testing.assert_array_equal(O.E4M3_TABLE[finite], codes[finite])
+    assert O.E4M3_TABLE[0x7E] == 448.0 and O.E4M3_TABLE[0x01] == 2.0 ** -9
+
+
+def test_e4m3_encode_roundtrips_and_matches_torch_rne():
+    finite = [c for c in range(256) if not np.isnan(O.E4M3_TABLE[c])]
+    assert O.e4m3_encode(O.E4M3_TABLE[finite]).tolist() == finite
+    rng = np.random.default_rng(8)
+    v = np.concatenate([rng.normal(0, 60, 20000), rng.normal(0, 0.01, 20000),
+                        (O.E4M3_TABLE[1:0x7E] + O.E4M3_TABLE[2:0x7F]) / 2])  # exact midpoints
+    v = np.clip(v, -448, 448).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(O.e4m3_encode(v), ref)
+    # saturation
+    assert O.e4m3_encode(np.array([1e4, -1e4, 464.0])).tolist() == [0x7E, 0xFE, 0x7E]
+
+
+def test_e8m0_scale_is_the_smallest_power_of_two_within_448():
+    rng = np.random.default_rng(9)
+    amax = np.concatenate([np.abs(rng.normal(0, 1, 2000)) * 10.0 ** rng.integers(-30, 30, 2000),
+                           [448.0, 449.0, 1.0, 2.0 ** -140, 896.0, 897.0]])
+    e = O.e8m0_scale_exponent(amax)
+    for a, ee in zip(amax, e):
+        want = next(q for q in range(-200, 200) if a <= 448.0 * 2.0 ** q)
+        assert ee == max(-127, min(127, want))
+    assert O.e8m0_scale_exponent(np.array([448.0, 449.0, 1.0, 0.0])).tolist() == [0, 1, -8, 0]
+
+
+def test_mx_quantise_hand_blocks():
+    blk = np.zeros((3, 32), np.float32)
+    blk[0, 0] = 448.0; blk[0, 1] = -1.0; blk[0, 2] = 2.0 ** -9; blk[0, 3] = 2.0 ** -10
+    blk[1, :] = 0.0
+    blk[2, 0] = 896.0; blk[2, 1] = 3.0
+    codes, scales = O.mx_quantize(blk, axis=1)
+    assert scales[:, 0].tolist() == [127, 127, 128]
+    assert codes[0, :4].tolist() == [0x7E, 0xB8, 0x01, 0x00]  # 2^-10 is half the step: tie -> 0
+    assert (codes[1] == 0).all()
+    assert codes[2, :2].tolist() == [0x7E, 0x3C]  # 896/2 = 448 (S.1111.110); 3/2 = 1.5 (S.0111.100)
+    np.testing.assert_array_equal(O.mx_dequantize(codes, scales, 1)[2, :2], [896.0, 3.0])
+
+
+def test_mx_quantise_axis_and_error_bound():
+    rng = np.random.default_rng(10)
+    a = rng.normal(size=(64, 96)).astype(np.float32)
+    q0 = O.mx_roundtrip(a, 0)
+    np.testing.assert_array_equal(q0, O.mx_roundtrip(a.T, 1).T)
+    # relative error of E4M3 normal numbers is at most 2^-4 (half of the 3-bit step)
+    blk = np.abs(a.reshape(64, 3, 32)).max(-1, keepdims=True)
+    err = np.abs(O.mx_roundtrip(a, 1) - a).reshape(64, 3, 32)
+    scale = 2.0 ** O.e8m0_scale_exponent(blk)
+    assert (err <= np.maximum(np.abs(a.reshape(64, 3, 32)) * 2.0 ** -4, scale * 2.0 ** -10)).all()
+
+
+def test_mx_forward_equals_plain_forward_on_representable_values():
+    # every x, weight and h already on the MXFP8 grid: quantisation is the identity.
+    w = tiny(T=8, H=64, I=32, E=2, k=1, prec="mxfp8")
+    inp = make_inputs(w)
+    x = torch.zeros(8, 64); x[:, 0] = 1.0  # x = e_0 -> g, u = row 0 of the weights
+    Wg = torch.zeros(2, 64, 32); Wu = torch.zeros(2, 64, 32); Wd = torch.zeros(2, 32, 64)
+    Wg[:, 0, :] = 64.0  # g = 64: silu(64) rounds to exactly 64 in fp64
+    Wu[:, 0, :] = 0.5  # u = 0.5, so h = 32 on every i
+    Wd[:, :, :] = 0.25  # y = 32 inputs * 32 * 0.25 = 256 on every h
+    inp2 = LayerInputs(w, x.to(torch.bfloat16), inp.Wr, None, Wg.to(torch.bfloat16),
+                       Wu.to(torch.bfloat16), Wd.to(torch.bfloat16))
+    a = O.layer_forward(inp2, mx=True)["out"]
+    b = O.layer_forward(inp2, mx=False)["out"]
+    np.testing.assert_allclose(a, b, rtol=1e-12)
+    np.testing.assert_array_equal(b, np.full_like(b, 256.0))
+
+
+# ---------------------------------------------------------------- backward
+
+def _fd_inputs(w, seed):
+    inp = make_inputs(w, with_dout=True)
+    f64 = lambda t: t.double().numpy().copy() if t is not None else None
+    return LayerInputs(w, f64(inp.x), f64(inp.Wr), f64(inp.bias), f64(inp.Wg), f64(inp.Wu),
+                       f64(inp.Wd), f64(inp.Wsg), f64(inp.Wsu), f64(inp.Wsd), f64(inp.dout))
+
+
+def _objective(inp):
+    return float((O.layer_forward(inp, logits64=True)["out"] * inp.dout).sum())
+
+
+def test_backward_matches_central_finite_differences():
+    w = tiny(T=10, H=64, I=16, E=4, k=2, shared_expert=True, router_bias="normal")
+    inp = _fd_inputs(w, 0)
+    fwd = O.layer_forward(inp, keep=True, logits64=True)
+    g = O.layer_backward(inp, fwd=fwd)
+    logits = fwd["logits"]
+    srt = np.sort(logits, 1)[:, ::-1]
+    assert (srt[:, w.k - 1] - srt[:, w.k] > 1e-4).all()  # no selection flips under +-eps
+    rng = np.random.default_rng(11)
+    eps = 1e-6
+    checks = [("x", "dx"), ("Wr", "dWr"), ("Wg", "dWg"), ("Wu", "dWu"), ("Wd", "dWd"),
+              ("Wsg", "dWsg"), ("Wsu", "dWsu"), ("Wsd", "dWsd")]
+    for name, gname in checks:
+        arr = getattr(inp, name)
+        for _ in range(6):
+            pos = tuple(rng.integers(0, s) for s in arr.shape)
+            old = arr[pos]
+            arr[pos] = old + eps; fp = _objective(inp)
+            arr[pos] = old - eps; fm = _objective(inp)
+            arr[pos] = old
+            fd = (fp - fm) / (2 * eps)
+            assert abs(fd - g[gname][pos]) <= 1e-6 * max(1.0, abs(fd)), (name, pos, fd, g[gname][pos])
+
+
+def test_backward_matches_torch_autograd():
+    w = tiny(T=20, H=128, I=32, E=6, k=3, router_bias="normal")
+    inp = _fd_inputs(w, 1)
+    fwd = O.layer_forward(inp, keep=True, logits64=True)
+    g = O.layer_backward(inp, fwd=fwd)
+    idx = torch.from_numpy(fwd["idx"].astype(np.int64))
+    t = {n: torch.tensor(getattr(inp, n), requires_grad=True) for n in ("x", "Wr", "Wg", "Wu", "Wd")}
+    logits = t["x"] @ t["Wr"] + torch.from_numpy(inp.bias)
+    wsel = torch.softmax(torch.gather(logits, 1, idx), dim=1)
+    out = torch.zeros(w.T, w.H, dtype=torch.float64)
+    for j in range(w.k):
+        e = idx[:, j]
+        gg = torch.einsum("th,thi->ti", t["x"], t["Wg"][e])
+        uu = torch.einsum("th,thi->ti", t["x"], t["Wu"][e])
+        yy = torch.einsum("ti,tih->th", torch.nn.functional.silu(gg) * uu, t["Wd"][e])
+        out = out + wsel[:, j:j + 1] * yy
+    (out * torch.from_numpy(inp.dout)).sum().backward()
+    for n, gn in [("x", "dx"), ("Wr", "dWr"), ("Wg", "dWg"), ("Wu", "dWu"), ("Wd", "dWd")]:
+        np.testing.assert_allclose(g[gn], t[n].grad.numpy(), rtol=1e-9, atol=1e-12)
+
+
+def test_backward_scales_exactly_with_dout():
+    w = tiny(T=12, E=4, k=2)
+    inp = _fd_inputs(w, 2)
+    fwd = O.layer_forward(inp, keep=True)
+    g1 = O.layer_backward(inp, fwd=fwd)
+    g2 = O.layer_backward(inp, dout=2 * inp.dout, fwd=fwd)
+    for n in ("dx", "dWg", "dWu", "dWd", "dWr", "dgate"):
+        np.testing.assert_array_equal(g2[n], 2 * g1[n])
