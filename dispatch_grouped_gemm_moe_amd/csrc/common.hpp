@@ -1,0 +1,57 @@
+// Internal helpers of the gfx950 MoE kernels (device types, bf16 rounding,
+// tile constants and the per-minibatch layout record).  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef int intx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// Grouped-GEMM tile: 256 x 256 output per workgroup, 64-deep K steps, four
+// waves in a 2 x 2 arrangement, each wave owning a 128 x 128 sub-tile made of
+// 4 x 4 MFMA 32x32x16 fragments.
+constexpr int BM = 256;
+constexpr int BN = 256;
+constexpr int BK = 64;
+constexpr int kGemmThreads = 256;
+
+// The gate/up weights are packed so that every 64 output columns of the
+// first GEMM hold 32 gate columns followed by the 32 up columns with the same
+// intermediate index; a wave's neighbouring 32-wide fragments then carry g and
+// u of the same element and SwiGLU is applied in registers.
+constexpr int kGluGroup = 64;
+
+// Largest expert count (router output range) and k the kernels accept.
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopK = 16;
+
+// Per-minibatch layout record written by the layout kernel and read by the
+// GEMM and combine kernels.  Experts are the E routed experts plus, when the
+// shared expert is on, one more "expert" E that takes every token in order.
+struct LayoutHeader {
+    int32_t m_tiles;  // total BM-row tiles over all experts
+    int32_t rows;     // routed rows (T_mb * k)
+    int32_t error;    // non-zero: an expert index was out of range
+    int32_t pad;
+};
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+    uint32_t u = __builtin_bit_cast(uint32_t, f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __builtin_bit_cast(float, (uint32_t)h << 16);
+}
+
+__host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace moe

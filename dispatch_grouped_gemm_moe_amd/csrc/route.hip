@@ -1,0 +1,266 @@
+// Router and dispatch-layout kernels (gfx950).
+//
+// Router: the router scores every expert for every token and picks several,
+// re-deciding at each step (KuCoin flash "Cursor's MoK achieves 2.37x
+// performance boost on NVIDIA GB300 NVL72", section 01).  The logits decide
+// integers (the expert choice), so their fp32 rounding order is fixed: lane l
+// of a wave accumulates h = l, l+64, ... with fused multiply-add, and a
+// halving tree over the 64 lanes finishes the sum.  This runs on the vector
+// ALUs, never on MFMA, whose internal accumulation order is not this one.
+//
+// Layout: count the rows of every expert, place each expert's rows next to
+// each other, ascending in token, and build the padded tile map the grouped
+// GEMM walks (same page, section 01: count, place, keep an expert's tokens
+// adjacent; section 02: the receiving side decides the placement itself).
+// The count uses integer atomics only (order-free); ranks come from wave
+// ballots in token order, so the layout is deterministic.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+#pragma clang fp contract(off)
+
+constexpr int kRouteTokens = 16;   // tokens per workgroup
+constexpr int kRouteExperts = 8;   // experts per wave pass
+constexpr int kRouteThreads = 256; // four waves
+
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ Wr, const float* __restrict__ bias,
+    int T, int H, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    float* __restrict__ logits_out) {
+    __shared__ float s_logit[kRouteTokens][kMaxExperts];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int t0 = blockIdx.x * kRouteTokens;
+    const int nt = min(kRouteTokens, T - t0);
+    const int nchunks = ceil_div(E, kRouteExperts);
+
+    for (int c = wave; c < nchunks; c += kRouteThreads / kWave) {
+        const int e0 = c * kRouteExperts;
+        float acc[kRouteTokens][kRouteExperts];
+#pragma unroll
+        for (int tt = 0; tt < kRouteTokens; ++tt)
+#pragma unroll
+            for (int ee = 0; ee < kRouteExperts; ++ee) acc[tt][ee] = 0.0f;
+        for (int h = lane; h < H; h += kWave) {
+            float wv[kRouteExperts];
+#pragma unroll
+            for (int ee = 0; ee < kRouteExperts; ++ee)
+                wv[ee] = (e0 + ee < E) ? Wr[(size_t)h * E + e0 + ee] : 0.0f;
+#pragma unroll
+            for (int tt = 0; tt < kRouteTokens; ++tt) {
+                const float xv = (tt < nt) ? bf16_to_f32(x[(size_t)(t0 + tt) * H + h]) : 0.0f;
+#pragma unroll
+                for (int ee = 0; ee < kRouteExperts; ++ee) acc[tt][ee] = __builtin_fmaf(xv, wv[ee], acc[tt][ee]);
+            }
+        }
+        // Halving tree over the 64 lane partials: p[l] = p[l] + p[l+s], s = 32..1.
+#pragma unroll
+        for (int tt = 0; tt < kRouteTokens; ++tt)
+#pragma unroll
+            for (int ee = 0; ee < kRouteExperts; ++ee) {
+                float v = acc[tt][ee];
+#pragma unroll
+                for (int s = 32; s >= 1; s >>= 1) v = v + __shfl_down(v, s, kWave);
+                if (lane == 0 && e0 + ee < E && tt < nt) {
+                    if (bias) v = v + bias[e0 + ee];
+                    s_logit[tt][e0 + ee] = v;
+                }
+            }
+    }
+    __syncthreads();
+
+    // Top-k per token: one wave per token; lane l holds experts l, l+64, ...
+    for (int tt = wave; tt < nt; tt += kRouteThreads / kWave) {
+        const int t = t0 + tt;
+        float v[kMaxExperts / kWave];
+#pragma unroll
+        for (int q = 0; q < kMaxExperts / kWave; ++q) {
+            const int e = lane + q * kWave;
+            v[q] = e < E ? s_logit[tt][e] : 0.0f;
+            if (logits_out && e < E) logits_out[(size_t)t * E + e] = v[q];
+        }
+        unsigned taken = 0;  // bit q: expert lane + 64q already selected (or absent)
+#pragma unroll
+        for (int q = 0; q < kMaxExperts / kWave; ++q)
+            if (lane + q * kWave >= E) taken |= 1u << q;
+        float sel_v[kMaxTopK];
+        int sel_i[kMaxTopK];
+        for (int j = 0; j < k; ++j) {
+            float bv = 0.0f;
+            int bi = 0x7fffffff;
+#pragma unroll
+            for (int q = 0; q < kMaxExperts / kWave; ++q) {
+                const int e = lane + q * kWave;
+                if (!(taken & (1u << q)) && (bi == 0x7fffffff || v[q] > bv)) { bv = v[q]; bi = e; }
+            }
+            // wave arg-max: larger value wins, equal values go to the lower index
+#pragma unroll
+            for (int s = 32; s >= 1; s >>= 1) {
+                const float ov = __shfl_xor(bv, s, kWave);
+                const int oi = __shfl_xor(bi, s, kWave);
+                const bool better = (oi != 0x7fffffff) &&
+                                    (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi));
+                if (better) { bv = ov; bi = oi; }
+            }
+            sel_v[j] = bv;
+            sel_i[j] = bi;
+            if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
+        }
+        if (lane == 0) {
+            // softmax over the selected logits, summed in slot order
+            float ez[kMaxTopK];
+            float den = 0.0f;
+            for (int j = 0; j < k; ++j) {
+                ez[j] = expf(sel_v[j] - sel_v[0]);
+                den = den + ez[j];
+            }
+            for (int j = 0; j < k; ++j) {
+                topk_idx[(size_t)t * k + j] = sel_i[j];
+                topk_w[(size_t)t * k + j] = ez[j] / den;
+            }
+        }
+    }
+}
+
+void launch_route(const uint16_t* x, const float* Wr, const float* bias, int T, int H, int E, int k,
+                  int32_t* topk_idx, float* topk_w, float* logits, hipStream_t stream) {
+    const int blocks = ceil_div(T, kRouteTokens);
+    hipLaunchKernelGGL(route_kernel, dim3(blocks), dim3(kRouteThreads), 0, stream, x, Wr, bias, T, H,
+                       E, k, topk_idx, topk_w, logits);
+}
+
+// ---------------------------------------------------------------------------
+// layout
+// ---------------------------------------------------------------------------
+
+constexpr int kLayoutThreads = 1024;
+constexpr int kLayoutWaves = kLayoutThreads / kWave;
+
+__global__ __launch_bounds__(kLayoutThreads) void layout_kernel(const int32_t* __restrict__ idx, int Tm,
+                                                                 int E, int k, int with_shared,
+                                                                 LayoutOut o) {
+    __shared__ int s_cnt[kLayoutWaves][kMaxExperts + 1];  // per-wave counts, then running bases
+    __shared__ int s_off[kMaxExperts + 2];                 // unpadded row offsets
+    __shared__ int s_poff[kMaxExperts + 2];                // padded (tile-aligned) row offsets
+    __shared__ int s_tot[kMaxExperts + 1];                 // rows per expert
+    __shared__ int s_err;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int Et = E + (with_shared ? 1 : 0);
+    for (int i = tid; i < kLayoutWaves * (kMaxExperts + 1); i += kLayoutThreads) (&s_cnt[0][0])[i] = 0;
+    if (tid == 0) s_err = 0;
+    __syncthreads();
+
+    // Wave w owns the contiguous token chunk [c0, c1); chunks ascend with w.
+    const int chunk = ceil_div(Tm, kLayoutWaves);
+    const int c0 = min(Tm, wave * chunk), c1 = min(Tm, c0 + chunk);
+
+    // 1. count (integer atomics: the totals do not depend on their order)
+    for (int t = c0 + lane; t < c1; t += kWave) {
+        int ids[kMaxTopK];
+        bool bad = false;
+        for (int j = 0; j < k; ++j) {
+            ids[j] = idx[(size_t)t * k + j];
+            bad |= (unsigned)ids[j] >= (unsigned)E;
+            for (int q = 0; q < j; ++q) bad |= ids[q] == ids[j];
+        }
+        if (bad) {
+            s_err = 1;
+            continue;
+        }
+        for (int j = 0; j < k; ++j) atomicAdd(&s_cnt[wave][ids[j]], 1);
+    }
+    __syncthreads();
+    if (s_err) {
+        if (tid == 0) {
+            if (o.offsets) o.offsets[E] = -1;
+            if (o.hdr) { o.hdr->m_tiles = 0; o.hdr->rows = 0; o.hdr->error = 1; }
+        }
+        return;
+    }
+
+    // 2a. per expert: exclusive prefix over waves (each wave's first rank) and total
+    for (int e = tid; e < E; e += kLayoutThreads) {
+        int run = 0;
+        for (int w = 0; w < kLayoutWaves; ++w) {
+            const int c = s_cnt[w][e];
+            s_cnt[w][e] = run;
+            run += c;
+        }
+        s_tot[e] = run;
+    }
+    if (tid == 0 && with_shared) s_tot[E] = Tm;  // the shared expert takes every token
+    __syncthreads();
+    // 2b. offsets and tile map (one thread: at most 257 experts)
+    if (tid == 0) {
+        int off = 0, mt = 0;
+        for (int e = 0; e < Et; ++e) {
+            const int tot = s_tot[e];
+            s_off[e] = off;
+            s_poff[e] = mt * BM;
+            if (o.mt_start) o.mt_start[e] = mt;
+            if (e < E) {
+                if (o.counts) o.counts[e] = tot;
+                if (o.offsets) o.offsets[e] = off;
+                off += tot;
+            }
+            mt += ceil_div(tot, BM);
+        }
+        s_off[Et] = off;
+        s_poff[Et] = mt * BM;
+        if (o.offsets) o.offsets[E] = off;
+        if (o.mt_start) o.mt_start[Et] = mt;
+        if (o.hdr) { o.hdr->m_tiles = mt; o.hdr->rows = off; o.hdr->error = 0; }
+    }
+    __syncthreads();
+
+    // 3. rank: 64 tokens at a time in lane order, experts in index order
+    for (int g0 = c0; g0 < c1; g0 += kWave) {
+        const int t = g0 + lane;
+        const bool valid = t < c1;
+        int ids[kMaxTopK];
+        for (int j = 0; j < k; ++j) ids[j] = valid ? idx[(size_t)t * k + j] : -1;
+        for (int e = 0; e < E; ++e) {
+            int js = -1;
+            for (int j = 0; j < k; ++j) js = (ids[j] == e) ? j : js;
+            const uint64_t mask = __ballot(js >= 0);
+            if (mask == 0) continue;
+            const int base = s_cnt[wave][e];
+            if (js >= 0) {
+                const int rank = base + __popcll(mask & ((1ull << lane) - 1ull));
+                const int row = s_off[e] + rank;
+                const int prow = s_poff[e] + rank;
+                if (o.row_token) o.row_token[row] = t;
+                if (o.tok_row) o.tok_row[(size_t)t * k + js] = row;
+                if (o.prow_token) o.prow_token[prow] = o.token_base + t;
+                if (o.tok_prow) o.tok_prow[(size_t)t * o.tok_prow_ld + js] = prow;
+            }
+            if (lane == 0) s_cnt[wave][e] = base + __popcll(mask);
+        }
+        if (with_shared && valid) {
+            const int prow = s_poff[E] + t;
+            if (o.prow_token) o.prow_token[prow] = o.token_base + t;
+            if (o.tok_prow) o.tok_prow[(size_t)t * o.tok_prow_ld + k] = prow;
+        }
+    }
+    __syncthreads();
+
+    // 4. padding rows of each expert's last tile repeat the expert's first token,
+    //    so every GEMM input row is a real, finite row (their outputs are unused).
+    if (o.prow_token) {
+        for (int e = wave; e < Et; e += kLayoutWaves) {
+            const int tot = (e < E) ? s_off[e + 1] - s_off[e] : Tm;
+            if (tot == 0) continue;
+            const int first = o.prow_token[s_poff[e]];
+            for (int r = s_poff[e] + tot + lane; r < s_poff[e + 1]; r += kWave) o.prow_token[r] = first;
+        }
+    }
+}
+
+void launch_layout(const int32_t* idx, int Tm, int E, int k, int with_shared, const LayoutOut& o,
+                   hipStream_t stream) {
+    hipLaunchKernelGGL(layout_kernel, dim3(1), dim3(kLayoutThreads), 0, stream, idx, Tm, E, k,
+                       with_shared, o);
+}
+
+}  // namespace moe

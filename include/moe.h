@@ -1,0 +1,226 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) fused mixture-of-experts layer.
+ *
+ * One layer, on one GPU: top-k routing, a dispatch that gathers each expert's
+ * tokens into contiguous GEMM tiles, the expert SwiGLU FFN as a grouped GEMM,
+ * and a combine that forms the weighted sum back in token order, plus the
+ * backward pass.  Sources of the method (cited per entry point below):
+ *   [KC]  KuCoin flash, "Cursor's MoK achieves 2.37x performance boost on
+ *         NVIDIA GB300 NVL72" (sections 01, 02, 03);
+ *   [RW]  RuntimeWire, "Cursor open-sources MoK MoE training kernel"
+ *         (sections "Cursor's benchmark claims" and "Rebuilding the MoE layer
+ *         around communication").
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller (the library
+ *     never allocates, frees or keeps them).  Tensors are dense row-major.
+ *     "bf16" tensors are passed as uint16_t bit patterns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call that takes a stream only enqueues work on it and returns;
+ *     nothing synchronises with the host except moe_read_device_status.
+ *   - Arguments are validated on the host before anything is enqueued.  A
+ *     failed check returns a non-zero moe_status and enqueues nothing.
+ *   - Calls are re-entrant.  A workspace belongs to one stream at a time.
+ *   - Results are deterministic: every floating-point reduction has a fixed
+ *     order and no floating-point atomics are used, so the same inputs give
+ *     bitwise-identical outputs on every call ([RW], "Rebuilding the MoE layer
+ *     around communication": fixed floating-point order for bitwise-identical
+ *     output).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_E_INVALID = 1,     /* null/misaligned pointer, bad size or inconsistent cfg */
+    MOE_E_UNSUPPORTED = 2, /* valid request outside what the kernels implement */
+    MOE_E_WORKSPACE = 3,   /* workspace / saved / packed buffer smaller than required */
+    MOE_E_HIP = 4,         /* a HIP runtime call failed (launch error, bad device) */
+    MOE_E_DEVICE = 5       /* a kernel reported an error through the device status word */
+} moe_status;
+
+typedef enum moe_prec {
+    MOE_PREC_BF16 = 0, /* bf16 operands, fp32 accumulation */
+    MOE_PREC_MXFP8 = 1 /* routed experts in MXFP8: OCP E4M3 values, one E8M0 scale per
+                          32 elements along each GEMM's contraction axis ([KC] 02:
+                          MXFP8 activations inside dispatch / grouped GEMM / SwiGLU) */
+} moe_prec;
+
+enum moe_flags {
+    /* add one always-on SwiGLU expert of the same shape, in bf16, weight 1, after
+       the routed weighted sum ([RW] "Rebuilding...": shared expert kept in BF16) */
+    MOE_F_SHARED_EXPERT = 1u << 0,
+    /* test mode: every routed expert is the identity (y = x), so combine must
+       return the weighted sum of copies of the input */
+    MOE_F_IDENTITY_EXPERTS = 1u << 1
+};
+
+/* Layer shape and execution choices. */
+typedef struct moe_cfg {
+    int32_t T;          /* tokens in this call, >= 1 */
+    int32_t H;          /* hidden size: multiple of 64 */
+    int32_t I;          /* expert intermediate size: multiple of 64 */
+    int32_t E;          /* experts on this GPU: 1..256 */
+    int32_t k;          /* experts per token: 1..min(E, 16) */
+    int32_t minibatch;  /* tokens per ring slot; 0 = automatic (see moe_query_sizes) */
+    int32_t ring_slots; /* ring token buffer slots; 0 = automatic */
+    int32_t comm_cus;   /* CUs reserved for route/dispatch/combine work; 0 = automatic */
+    int32_t prec;       /* moe_prec */
+    uint32_t flags;     /* moe_flags */
+} moe_cfg;
+
+/* Sizes, in bytes, of the buffers the caller allocates for a cfg. */
+typedef struct moe_sizes {
+    size_t packed_weights; /* moe_prepare_weights output (routed + shared experts) */
+    size_t workspace_fwd;  /* scratch of moe_layer_fwd */
+    size_t saved;          /* what moe_layer_fwd keeps for moe_layer_bwd */
+    size_t workspace_bwd;  /* scratch of moe_layer_bwd */
+    int32_t minibatch;     /* effective tokens per ring slot */
+    int32_t ring_slots;    /* effective ring slots */
+    int32_t num_minibatches;
+    int32_t comm_cus;      /* effective CUs of the route/dispatch/combine role */
+} moe_sizes;
+
+/* Device buffers of one layer's parameters. */
+typedef struct moe_weights {
+    const float *Wr;    /* [H, E] fp32 router weight */
+    const float *bias;  /* [E] fp32 router logit bias, or NULL */
+    const void *packed; /* moe_prepare_weights output */
+    size_t packed_bytes;
+} moe_weights;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *moe_status_string(moe_status s);
+
+/* MOE_ABI_VERSION of the loaded library. */
+int32_t moe_abi_version(void);
+
+/*
+ * Host-only check of a cfg (no GPU needed).  MOE_E_INVALID for T<1, E<1, k<1,
+ * k>E, unknown prec or flags; MOE_E_UNSUPPORTED for H or I not a multiple of
+ * 64, E>256, k>16, or a cfg whose buffers would overflow 32-bit row indices.
+ */
+moe_status moe_validate_cfg(const moe_cfg *cfg);
+
+/*
+ * Host-only: buffer sizes and the effective minibatch / ring / CU split of a
+ * cfg.  The automatic minibatch gives the GEMM role at least two full waves of
+ * output tiles per minibatch ([KC] 02: a minibatch must fill the compute SMs
+ * with at least two complete waves of GEMM tasks; too small starves them, too
+ * large delays the first compute).
+ */
+moe_status moe_query_sizes(const moe_cfg *cfg, moe_sizes *out);
+
+/*
+ * Convert the caller's bf16 expert weights into the kernels' packed layout
+ * (and, for MOE_PREC_MXFP8, into E4M3 codes with E8M0 block scales).
+ *   Wg, Wu : [E, H, I] bf16   gate / up projections (g = x Wg[e], u = x Wu[e])
+ *   Wd     : [E, I, H] bf16   down projection (y = h Wd[e])
+ *   Wsg, Wsu [H, I], Wsd [I, H] bf16: shared expert; NULL unless
+ *            cfg->flags has MOE_F_SHARED_EXPERT.
+ *   packed : device buffer of at least moe_sizes.packed_weights bytes.
+ * Runs on `stream`; the inputs may be freed once the stream has passed it.
+ */
+moe_status moe_prepare_weights(const moe_cfg *cfg, const uint16_t *Wg, const uint16_t *Wu,
+                               const uint16_t *Wd, const uint16_t *Wsg, const uint16_t *Wsu,
+                               const uint16_t *Wsd, void *packed, size_t packed_bytes,
+                               void *stream);
+
+/*
+ * Router ([KC] 01: the router picks several experts for each token and
+ * re-decides at every step).  For each of cfg->T tokens:
+ *   logits[t,e] = sum_h x[t,h] * Wr[h,e] (+ bias[e]), fp32, summed in a fixed
+ *       order: 64 lane partials p[h mod 64] accumulated with fused
+ *       multiply-add for ascending h, then a halving tree p[l] += p[l+s] for
+ *       s = 32, 16, ..., 1; the bias is one fp32 add after the tree;
+ *   topk_idx[t,0..k-1] = the k largest logits, descending, ties to the lower
+ *       expert index;
+ *   topk_w[t,j] = softmax over the k selected logits (fp32).
+ *   x [T,H] bf16; Wr [H,E] fp32; bias [E] fp32 or NULL;
+ *   topk_idx [T,k] int32; topk_w [T,k] fp32; logits [T,E] fp32 or NULL.
+ * Inputs must be finite.
+ */
+moe_status moe_route(const moe_cfg *cfg, const uint16_t *x, const float *Wr, const float *bias,
+                     int32_t *topk_idx, float *topk_w, float *logits, void *stream);
+
+/*
+ * Dispatch layout ([KC] 01: count the tokens of every expert, decide where each
+ * lands, and keep each expert's tokens adjacent so that the grouped GEMM gets
+ * ordered input; [KC] 02: the receiving side picks the placement itself).
+ *   topk_idx [T,k] int32 (values in [0,E), distinct within a token)
+ *   counts   [E]   rows of each expert
+ *   offsets  [E+1] exclusive prefix sum of counts (offsets[E] = T*k)
+ *   row_token[T*k] token of each row; rows of expert e are
+ *                  offsets[e] .. offsets[e+1]-1 in ascending token order
+ *   tok_row  [T,k] row holding slot j of token t (inverse of row_token)
+ * Needs no workspace.  If any index lies outside [0,E) the kernel writes
+ * offsets[E] = -1 and leaves the other outputs unspecified (the host cannot see
+ * device data without a sync, so this is the error report of this call).
+ * An expert repeated within a token gets one row per slot, in slot order.
+ */
+moe_status moe_dispatch_layout(const moe_cfg *cfg, const int32_t *topk_idx, int32_t *counts,
+                               int32_t *offsets, int32_t *row_token, int32_t *tok_row,
+                               void *stream);
+
+/*
+ * Layer forward: route, layout, dispatch, expert SwiGLU FFN, combine and the
+ * final weighted sum ([KC] 03: the measured layer covers scheduling, dispatch,
+ * expert FFN, combine and the final weighted sum), minibatch by minibatch
+ * through a fixed-size ring token buffer ([KC] 02: a fixed-size ring buffer is
+ * reused as soon as combine has sent a batch's results, with no CPU round trip).
+ *   out[t] = sum_j topk_w[t,j] * FFN_{topk_idx[t,j]}(x[t])  (+ shared FFN(x[t]))
+ *   FFN_e(v) = (silu(v Wg[e]) * (v Wu[e])) Wd[e],  silu(z) = z / (1 + exp(-z))
+ *   x [T,H] bf16, out [T,H] bf16.
+ *   saved: NULL, or at least moe_sizes.saved bytes that moe_layer_bwd will read.
+ *       It starts with the routing of every token: topk_idx [T,k] int32 at
+ *       byte 0, then topk_w [T,k] fp32 at the next 256-byte boundary.
+ *   ws: at least moe_sizes.workspace_fwd bytes, 256-byte aligned.  Its first 256
+ *       bytes hold the device status word: zero them once when the workspace
+ *       is allocated (moe_read_device_status clears the word after reading).
+ */
+moe_status moe_layer_fwd(const moe_cfg *cfg, const moe_weights *w, const uint16_t *x,
+                         uint16_t *out, void *saved, size_t saved_bytes, void *ws,
+                         size_t ws_bytes, void *stream);
+
+/*
+ * Layer backward ([KC] 01: training adds two exchanges in the reverse
+ * direction; [KC] 02: reverse-combine then reverse-dispatch).  Gradients of
+ * sum(out * dout) with the routing of the forward held fixed:
+ *   dx [T,H] bf16; dWg, dWu [E,H,I], dWd [E,I,H], dWr [H,E] fp32 (overwritten);
+ *   dWs: NULL, or the shared expert's [H*I | H*I | I*H] fp32 (gate, up, down);
+ *   dgate: NULL, or [T,k] fp32 = d(sum out*dout)/d topk_w.
+ *   saved: what moe_layer_fwd wrote for the same cfg, weights and x.
+ * The router bias is an input, not a parameter: it has no gradient.
+ */
+moe_status moe_layer_bwd(const moe_cfg *cfg, const moe_weights *w, const uint16_t *x,
+                         const uint16_t *dout, const void *saved, size_t saved_bytes,
+                         uint16_t *dx, float *dWg, float *dWu, float *dWd, float *dWr,
+                         float *dWs, float *dgate, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Read (and clear) the device status word kept at the start of a forward or
+ * backward workspace: waits for `stream`, then returns MOE_OK, or MOE_E_DEVICE
+ * with *code / *detail set to the first error a kernel of that workspace
+ * recorded (codes are listed in moe_device_error).  The only call that
+ * synchronises with the host.
+ */
+typedef enum moe_device_error {
+    MOE_DEV_OK = 0,
+    MOE_DEV_WAIT_TIMEOUT = 1 /* a bounded device-side wait expired; detail = wait site */
+} moe_device_error;
+
+moe_status moe_read_device_status(void *ws, void *stream, int32_t *code, int32_t *detail);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,45 @@
+"""Helpers of the GPU tests: upload a workload's inputs, run the library
+through its binding, read results back.  No layer arithmetic here."""
+import torch
+
+import dispatch_grouped_gemm_moe_amd as moe
+
+
+def cfg_of(w, minibatch=None, flags=0, T=None):
+    if w.shared_expert:
+        flags |= moe.MOE_F_SHARED_EXPERT
+    return moe.make_cfg(T or w.T, w.H, w.I, w.E, w.k,
+                        minibatch=w.minibatch if minibatch is None else minibatch,
+                        prec=moe.MOE_PREC_MXFP8 if w.prec == "mxfp8" else moe.MOE_PREC_BF16,
+                        flags=flags)
+
+
+class Layer:
+    """One layer's device tensors and packed weights."""
+
+    def __init__(self, inp, minibatch=None, flags=0, device="cuda"):
+        w = inp.w
+        self.inp, self.cfg = inp, cfg_of(w, minibatch, flags)
+        self.bufs = moe.alloc_buffers(self.cfg, device=device, with_saved=True)
+        dev = lambda t: None if t is None else t.to(device).contiguous()
+        self.x, self.Wr, self.bias = dev(inp.x), dev(inp.Wr), dev(inp.bias)
+        Wg, Wu, Wd = dev(inp.Wg), dev(inp.Wu), dev(inp.Wd)
+        moe.moe_prepare_weights(self.cfg, Wg, Wu, Wd, self.bufs.packed,
+                                dev(inp.Wsg), dev(inp.Wsu), dev(inp.Wsd))
+        torch.cuda.synchronize()
+        del Wg, Wu, Wd
+        self.out = torch.empty_like(self.x)
+
+    def forward(self):
+        moe.moe_layer_fwd(self.cfg, self.Wr, self.bias, self.bufs.packed, self.x, self.out,
+                          self.bufs.ws, saved=self.bufs.saved)
+        return self.out
+
+    def saved_routing(self):
+        T, k = self.cfg.T, self.cfg.k
+        n = T * k * 4
+        off = (n + 255) // 256 * 256
+        raw = self.bufs.saved
+        idx = raw[:n].view(torch.int32).view(T, k)
+        w = raw[off:off + n].view(torch.float32).view(T, k)
+        return idx, w

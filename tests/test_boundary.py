@@ -1,0 +1,120 @@
+"""CPU-only checks of the C ABI boundary: the library loads, exports every
+function include/moe.h declares, and its host-side validation and size
+queries behave as documented (no kernel is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dispatch_grouped_gemm_moe_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert len(names) >= 10
+    assert sorted(moe.EXPORTS) == names
+    lib = ctypes.CDLL(moe.build.lib_path())
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings():
+    assert moe.moe_abi_version() == 1
+    lib = moe.lib()
+    assert lib.moe_status_string(0) == b"ok"
+    assert lib.moe_status_string(3) == b"buffer too small"
+    assert lib.moe_status_string(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(), moe.MOE_OK),
+    (dict(T=0), moe.MOE_E_INVALID),
+    (dict(k=9), moe.MOE_E_INVALID),  # k > E
+    (dict(k=0), moe.MOE_E_INVALID),
+    (dict(prec=7), moe.MOE_E_INVALID),
+    (dict(flags=1 << 9), moe.MOE_E_INVALID),
+    (dict(minibatch=-1), moe.MOE_E_INVALID),
+    (dict(H=96), moe.MOE_E_UNSUPPORTED),
+    (dict(I=32), moe.MOE_E_UNSUPPORTED),
+    (dict(E=300, k=2), moe.MOE_E_UNSUPPORTED),
+    (dict(E=32, k=17), moe.MOE_E_UNSUPPORTED),
+])
+def test_validate_cfg(kw, want):
+    base = dict(T=64, H=128, I=64, E=8, k=2)
+    base.update(kw)
+    assert moe.moe_validate_cfg(moe.make_cfg(**base)) == want
+
+
+def test_query_sizes_h7168_i2048():
+    cfg = moe.make_cfg(16384, 7168, 2048, 32, 8, minibatch=2560)
+    s = moe.moe_query_sizes(cfg)
+    assert s.minibatch == 2560 and s.num_minibatches == 7 and s.ring_slots == 2
+    # packed: gate|up [E,2I,H] + down [E,H,I], bf16
+    assert s.packed_weights >= 32 * 3 * 7168 * 2048 * 2
+    # per slot the Y buffer alone holds (rows + padding) x H bf16
+    assert s.workspace_fwd >= 2 * (2560 * 8) * 7168 * 2
+    assert s.saved >= 16384 * 8 * 8
+
+
+def test_query_sizes_automatic_minibatch_and_shared_expert():
+    s = moe.moe_query_sizes(moe.make_cfg(4096, 2048, 1024, 64, 6))
+    assert 1 <= s.num_minibatches <= 2 and s.minibatch * s.num_minibatches >= 4096
+    a = moe.moe_query_sizes(moe.make_cfg(1024, 512, 256, 8, 2))
+    b = moe.moe_query_sizes(moe.make_cfg(1024, 512, 256, 8, 2, flags=moe.MOE_F_SHARED_EXPERT))
+    assert b.packed_weights > a.packed_weights and b.workspace_fwd > a.workspace_fwd
+
+
+def test_null_pointers_are_rejected_before_any_launch():
+    lib = moe.lib()
+    cfg = moe.make_cfg(64, 128, 64, 8, 2)
+    st = lib.moe_route(ctypes.byref(cfg), None, None, None, None, None, None, None)
+    assert st == moe.MOE_E_INVALID
+    st = lib.moe_dispatch_layout(ctypes.byref(cfg), None, None, None, None, None, None)
+    assert st == moe.MOE_E_INVALID
+    st = lib.moe_layer_fwd(ctypes.byref(cfg), None, None, None, None, 0, None, 0, None)
+    assert st == moe.MOE_E_INVALID
+    st = lib.moe_route(None, None, None, None, None, None, None, None)
+    assert st == moe.MOE_E_INVALID
+
+
+def test_small_buffers_are_rejected():
+    lib = moe.lib()
+    cfg = moe.make_cfg(64, 128, 64, 8, 2)
+    s = moe.moe_query_sizes(cfg)
+    fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: the size check fails first
+    w = moe.moe_weights(fake.value, None, fake.value, s.packed_weights)
+    st = lib.moe_layer_fwd(ctypes.byref(cfg), ctypes.byref(w), fake, fake, None, 0, fake,
+                           s.workspace_fwd - 1, None)
+    assert st == moe.MOE_E_WORKSPACE
+    w.packed_bytes = s.packed_weights - 1
+    st = lib.moe_layer_fwd(ctypes.byref(cfg), ctypes.byref(w), fake, fake, None, 0, fake,
+                           s.workspace_fwd, None)
+    assert st == moe.MOE_E_WORKSPACE
+    st = lib.moe_prepare_weights(ctypes.byref(cfg), fake, fake, fake, None, None, None, fake,
+                                 s.packed_weights - 1, None)
+    assert st == moe.MOE_E_WORKSPACE
+    # the shared expert needs its three weights
+    cfg_s = moe.make_cfg(64, 128, 64, 8, 2, flags=moe.MOE_F_SHARED_EXPERT)
+    st = lib.moe_prepare_weights(ctypes.byref(cfg_s), fake, fake, fake, None, None, None, fake,
+                                 1 << 40, None)
+    assert st == moe.MOE_E_INVALID
+
+
+def test_misaligned_pointers_are_rejected():
+    lib = moe.lib()
+    cfg = moe.make_cfg(64, 128, 64, 8, 2)
+    s = moe.moe_query_sizes(cfg)
+    good = (1 << 20)
+    w = moe.moe_weights(good, None, good, s.packed_weights)
+    st = lib.moe_layer_fwd(ctypes.byref(cfg), ctypes.byref(w), ctypes.c_void_p(good + 2),
+                           ctypes.c_void_p(good), None, 0, ctypes.c_void_p(good), s.workspace_fwd, None)
+    assert st == moe.MOE_E_INVALID
