@@ -23,7 +23,8 @@ MOE_F_IDENTITY_EXPERTS = 1 << 1
 # every symbol include/moe.h declares
 EXPORTS = ("moe_status_string", "moe_abi_version", "moe_validate_cfg", "moe_query_sizes",
            "moe_prepare_weights", "moe_route", "moe_dispatch_layout", "moe_layer_fwd",
-           "moe_layer_bwd", "moe_read_device_status")
+           "moe_layer_bwd", "moe_read_device_status", "moe_timing_enable", "moe_timing_read")
+KERNEL_KINDS = ("route", "layout", "gemm_gate_up", "gemm_down", "combine", "gather", "other")
 
 
 class moe_cfg(ctypes.Structure):
@@ -43,6 +44,10 @@ class moe_sizes(ctypes.Structure):
 class moe_weights(ctypes.Structure):
     _fields_ = [("Wr", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("packed", ctypes.c_void_p),
                 ("packed_bytes", ctypes.c_size_t)]
+
+
+class moe_kernel_times(ctypes.Structure):
+    _fields_ = [("launches", ctypes.c_int32 * 7), ("ms", ctypes.c_double * 7), ("dropped", ctypes.c_int32)]
 
 
 class MoeError(RuntimeError):
@@ -76,6 +81,8 @@ def _load():
             "moe_layer_bwd": (ctypes.c_int, [cfgp, ctypes.POINTER(moe_weights), P, P, P, SZ, P, P, P,
                                              P, P, P, P, P, SZ, P]),
             "moe_read_device_status": (ctypes.c_int, [P, P, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
+            "moe_timing_enable": (ctypes.c_int, [I32]),
+            "moe_timing_read": (ctypes.c_int, [ctypes.POINTER(moe_kernel_times)]),
         }
         for name, (res, args) in sig.items():
             f = getattr(lib, name)
@@ -168,6 +175,19 @@ def moe_read_device_status(ws, stream=None):
     code, detail = ctypes.c_int32(0), ctypes.c_int32(0)
     st = _load().moe_read_device_status(_ptr(ws), _stream(stream), ctypes.byref(code), ctypes.byref(detail))
     return st, code.value, detail.value
+
+
+def moe_timing_enable(on: bool):
+    _check("moe_timing_enable", _load().moe_timing_enable(1 if on else 0))
+
+
+def moe_timing_read() -> dict:
+    """{kind: (launches, total_ms)} since the last moe_timing_enable(True)."""
+    t = moe_kernel_times()
+    _check("moe_timing_read", _load().moe_timing_read(ctypes.byref(t)))
+    res = {n: (t.launches[i], t.ms[i]) for i, n in enumerate(KERNEL_KINDS)}
+    res["dropped"] = t.dropped
+    return res
 
 
 # ---------------------------------------------------------------- buffers

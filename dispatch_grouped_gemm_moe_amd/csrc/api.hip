@@ -3,6 +3,8 @@
 // moe_read_device_status).
 #include <string.h>
 
+#include <vector>
+
 #include "../../include/moe.h"
 #include "common.hpp"
 #include "kernels.hpp"
@@ -112,6 +114,37 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
 
 bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
 
+// Optional per-launch event timing (moe_timing_enable / moe_timing_read).
+struct Timing {
+    bool on = false;
+    std::vector<hipEvent_t> ev;  // 2 per launch
+    std::vector<int> kind;
+    int used = 0, dropped = 0;
+};
+Timing g_timing;
+constexpr int kTimingPairs = 4096;
+
+struct TimedLaunch {
+    int slot = -1;
+    hipStream_t s;
+    TimedLaunch(moe_kernel_kind k, hipStream_t stream) : s(stream) {
+        if (!g_timing.on) return;
+        if (g_timing.used >= kTimingPairs) { ++g_timing.dropped; return; }
+        slot = g_timing.used++;
+        g_timing.kind[slot] = k;
+        (void)hipEventRecord(g_timing.ev[2 * slot], s);
+    }
+    ~TimedLaunch() {
+        if (slot >= 0) (void)hipEventRecord(g_timing.ev[2 * slot + 1], s);
+    }
+};
+
+#define TIMED(kind, stream, call) \
+    do {                          \
+        TimedLaunch tl_(kind, stream); \
+        call;                     \
+    } while (0)
+
 moe_status check_launch() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP; }
 
 }  // namespace
@@ -179,7 +212,8 @@ moe_status moe_route(const moe_cfg* cfg, const uint16_t* x, const float* Wr, con
     moe_status st = validate(cfg);
     if (st != MOE_OK) return st;
     if (!x || !Wr || !topk_idx || !topk_w) return MOE_E_INVALID;
-    launch_route(x, Wr, bias, cfg->T, cfg->H, cfg->E, cfg->k, topk_idx, topk_w, logits, (hipStream_t)stream);
+    TIMED(MOE_K_ROUTE, (hipStream_t)stream,
+          launch_route(x, Wr, bias, cfg->T, cfg->H, cfg->E, cfg->k, topk_idx, topk_w, logits, (hipStream_t)stream));
     return check_launch();
 }
 
@@ -194,7 +228,7 @@ moe_status moe_dispatch_layout(const moe_cfg* cfg, const int32_t* topk_idx, int3
     o.offsets = offsets;
     o.row_token = row_token;
     o.tok_row = tok_row;
-    launch_layout(topk_idx, cfg->T, cfg->E, cfg->k, 0, o, (hipStream_t)stream);
+    TIMED(MOE_K_LAYOUT, (hipStream_t)stream, launch_layout(topk_idx, cfg->T, cfg->E, cfg->k, 0, o, (hipStream_t)stream));
     return check_launch();
 }
 
@@ -217,7 +251,7 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
     const uint16_t* W1t = (const uint16_t*)(pk + p.pk_w1t);
     const uint16_t* W2t = (const uint16_t*)(pk + p.pk_w2t);
 
-    launch_route(x, w->Wr, w->bias, p.T, p.H, p.E, p.k, idx, gw, nullptr, s);
+    TIMED(MOE_K_ROUTE, s, launch_route(x, w->Wr, w->bias, p.T, p.H, p.E, p.k, idx, gw, nullptr, s));
     const int grid = kNumCUs;
     for (int b = 0; b < p.nmb; ++b) {
         const int t0 = b * p.Mb;
@@ -238,10 +272,10 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
         o.tok_prow = tok_prow;
         o.tok_prow_ld = p.ld_tok_prow;
         o.token_base = t0;
-        launch_layout(idx + (size_t)t0 * p.k, Tm, p.E, p.k, p.shared ? 1 : 0, o, s);
+        TIMED(MOE_K_LAYOUT, s, launch_layout(idx + (size_t)t0 * p.k, Tm, p.E, p.k, p.shared ? 1 : 0, o, s));
 
         if (p.identity) {
-            launch_gather_rows(x, p.H, prow_token, hdr, (int)p.rpad, ybuf, p.H, s);
+            TIMED(MOE_K_GATHER, s, launch_gather_rows(x, p.H, prow_token, hdr, (int)p.rpad, ybuf, p.H, s));
         } else {
             GemmArgs g1;
             g1.A = x; g1.a_row_map = prow_token; g1.lda = p.H;
@@ -249,17 +283,18 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             g1.C = hbuf; g1.ldc = p.I;
             g1.N = 2 * p.I; g1.K = p.H;
             g1.mt_start = mt; g1.hdr = hdr; g1.Et = p.Et;
-            launch_grouped_gemm(g1, kEpiSwiGLU, grid, s);
+            TIMED(MOE_K_GEMM_GATE_UP, s, launch_grouped_gemm(g1, kEpiSwiGLU, grid, s));
             GemmArgs g2;
             g2.A = hbuf; g2.a_row_map = nullptr; g2.lda = p.I;
             g2.B = W2t; g2.b_stride = (int64_t)p.H * p.I;
             g2.C = ybuf; g2.ldc = p.H;
             g2.N = p.H; g2.K = p.I;
             g2.mt_start = mt; g2.hdr = hdr; g2.Et = p.Et;
-            launch_grouped_gemm(g2, kEpiStore, grid, s);
+            TIMED(MOE_K_GEMM_DOWN, s, launch_grouped_gemm(g2, kEpiStore, grid, s));
         }
-        launch_combine(ybuf, p.H, tok_prow, p.ld_tok_prow, gw + (size_t)t0 * p.k, p.k,
-                       (p.shared && !p.identity) ? 1 : 0, p.H, Tm, out + (size_t)t0 * p.H, s);
+        TIMED(MOE_K_COMBINE, s,
+              launch_combine(ybuf, p.H, tok_prow, p.ld_tok_prow, gw + (size_t)t0 * p.k, p.k,
+                             (p.shared && !p.identity) ? 1 : 0, p.H, Tm, out + (size_t)t0 * p.H, s));
     }
     return check_launch();
 }
@@ -288,6 +323,38 @@ moe_status moe_read_device_status(void* ws, void* stream, int32_t* code, int32_t
         if (hipMemcpy(ws, z, sizeof(z), hipMemcpyHostToDevice) != hipSuccess) return MOE_E_HIP;
         return MOE_E_DEVICE;
     }
+    return MOE_OK;
+}
+
+moe_status moe_timing_enable(int32_t on) {
+    if (on) {
+        if (g_timing.ev.empty()) {
+            g_timing.ev.resize(2 * kTimingPairs);
+            g_timing.kind.resize(kTimingPairs);
+            for (auto& e : g_timing.ev)
+                if (hipEventCreate(&e) != hipSuccess) {
+                    g_timing.ev.clear();
+                    return MOE_E_HIP;
+                }
+        }
+        g_timing.used = 0;
+        g_timing.dropped = 0;
+    }
+    g_timing.on = on != 0;
+    return MOE_OK;
+}
+
+moe_status moe_timing_read(moe_kernel_times* out) {
+    if (!out) return MOE_E_INVALID;
+    memset(out, 0, sizeof(*out));
+    for (int i = 0; i < g_timing.used; ++i) {
+        if (hipEventSynchronize(g_timing.ev[2 * i + 1]) != hipSuccess) return MOE_E_HIP;
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, g_timing.ev[2 * i], g_timing.ev[2 * i + 1]) != hipSuccess) return MOE_E_HIP;
+        out->launches[g_timing.kind[i]] += 1;
+        out->ms[g_timing.kind[i]] += ms;
+    }
+    out->dropped = g_timing.dropped;
     return MOE_OK;
 }
 

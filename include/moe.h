@@ -220,6 +220,35 @@ typedef enum moe_device_error {
 
 moe_status moe_read_device_status(void *ws, void *stream, int32_t *code, int32_t *detail);
 
+/*
+ * Kernel timing (diagnostics, for benchmarks).  While enabled, every kernel
+ * the library launches is bracketed by a pair of HIP events recorded on the
+ * stream it is launched on; moe_timing_read waits for those events and
+ * returns, per kernel kind, the launch count and the summed event time since
+ * the last moe_timing_enable(1).  Recording costs a few microseconds per
+ * launch; with timing off nothing is recorded.  Not re-entrant across threads.
+ * moe_timing_enable allocates HIP events (host call; never inside a capture).
+ */
+typedef enum moe_kernel_kind {
+    MOE_K_ROUTE = 0,
+    MOE_K_LAYOUT = 1,
+    MOE_K_GEMM_GATE_UP = 2, /* grouped GEMM of gate|up with the SwiGLU epilogue */
+    MOE_K_GEMM_DOWN = 3,    /* grouped GEMM of the down projection */
+    MOE_K_COMBINE = 4,
+    MOE_K_GATHER = 5,
+    MOE_K_OTHER = 6,
+    MOE_K_COUNT = 7
+} moe_kernel_kind;
+
+typedef struct moe_kernel_times {
+    int32_t launches[MOE_K_COUNT];
+    double ms[MOE_K_COUNT];
+    int32_t dropped; /* launches not timed because the event pool was full */
+} moe_kernel_times;
+
+moe_status moe_timing_enable(int32_t on);
+moe_status moe_timing_read(moe_kernel_times *out);
+
 #ifdef __cplusplus
 }
 #endif
