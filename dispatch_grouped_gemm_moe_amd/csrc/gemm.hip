@@ -17,13 +17,44 @@ namespace moe {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void gbl_cvoid;
 
-// LDS of one pipeline stage: A tile [BM][BK] then B tile [BN][BK], bf16.
-// A row of a tile is 128 bytes = eight 16-byte chunks; chunk c of row r is
-// stored at position c ^ (r & 7), so the 32 rows an MFMA fragment read
-// touches spread over all banks.
-constexpr int kStageA = BM * BK * 2;
-constexpr int kStageBytes = (BM + BN) * BK * 2;
-constexpr int kStages = 2;
+// LDS ring of kStages pipeline stages; a stage holds the A tile [BM][BK] then
+// the B tile [BN][BK] (bf16, BK = 32: 64-byte rows of four 16-byte chunks).
+// Chunk c of row r sits at position c ^ f(r), f(r) = (r >> 2) & 3.  With this
+// swizzle the 128-bit fragment reads (lane l: row l%32, chunk 2*kstep + l/32)
+// are free of bank conflicts on gfx950's LDS; swizzles that also mix in row
+// bit 1 (or use r & 3) measured 2-way conflicted with rocprofv3's
+// SQ_LDS_BANK_CONFLICT, as did unswizzled rows.
+constexpr int kBK = 32;
+constexpr int kRowBytes = kBK * 2;
+constexpr int kStageA = BM * kRowBytes;
+constexpr int kStageBytes = (BM + BN) * kRowBytes;
+constexpr int kStages = 5;  // 160 KB of LDS: loads run up to 4 K steps ahead
+
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+
+__device__ __forceinline__ void mfma_block(floatx16 (&acc)[4][4], const bf16x8 (&a)[4], const bf16x8 (&b)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+}
+
+// Wait until at most c K steps (8 loads each) of this wave are in flight and
+// all of its LDS reads are done.  c is clamped to [0, kStages-1].
+__device__ __forceinline__ void wait_vm_steps(int c) {
+    switch (c < 0 ? 0 : c) {
+        case 0: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); break;
+        case 1: asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory"); break;
+        case 2: asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory"); break;
+        case 3: asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)" ::: "memory"); break;
+        default: asm volatile("s_waitcnt vmcnt(32) lgkmcnt(0)" ::: "memory"); break;
+    }
+}
+static_assert(kStages <= 5, "wait_vm_steps covers at most 4 steps in flight");
+
+// Scheduling masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMFMA = 0x008, kSchedVMEM = 0x020, kSchedDSRead = 0x100;
 
 template <int EPI>
 __global__ __attribute__((amdgpu_flat_work_group_size(kGemmThreads, kGemmThreads), amdgpu_waves_per_eu(1, 1)))
@@ -38,8 +69,7 @@ void grouped_gemm_kernel(GemmArgs p) {
     // one XCD take consecutive tiles so that they share weight and row tiles
     // in that XCD's L2.
     const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
-    const int KT = p.K / BK;
-    const int lchunk = (lane & 7) ^ (lane >> 3);
+    const int KT = p.K / kBK;
 
     for (int it = 0;; ++it) {
         const int v = it * G + xcd * per + local;
@@ -57,16 +87,21 @@ void grouped_gemm_kernel(GemmArgs p) {
         const int prow0 = (mt0 + ml) * BM;
         const int n0 = ntile * BN;
 
-        const uint16_t* ga[8];
-        const uint16_t* gb[8];
+        // Byte offsets of the 4 A rows and 4 B rows this lane stages per K step:
+        // instruction i fills tile rows wave*64 + 16i .. +15 (lane/4 picks the row,
+        // lane%4 the fixed LDS chunk; the lane loads the logical chunk stored there).
+        const char* a_base = (const char*)p.A;
+        const char* b_base = (const char*)(p.B + (int64_t)e * p.b_stride);
+        uint32_t aoff[4], boff[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = wave * 64 + i * 8 + (lane >> 3);
+        for (int i = 0; i < 4; ++i) {
+            const int r = wave * 64 + i * 16 + (lane >> 2);
+            const int lchunk = (lane & 3) ^ swz(r);
             const int prow = prow0 + r;
             const int arow = p.a_row_map ? p.a_row_map[prow] : prow;
-            ga[i] = p.A + (int64_t)arow * p.lda + lchunk * 8;
+            aoff[i] = (uint32_t)(((int64_t)arow * p.lda + lchunk * 8) * 2);
             const int n = min(n0 + r, p.N - 1);
-            gb[i] = p.B + (int64_t)e * p.b_stride + (int64_t)n * p.K + lchunk * 8;
+            boff[i] = (uint32_t)(((int64_t)n * p.K + lchunk * 8) * 2);
         }
 
         floatx16 acc[4][4];
@@ -75,42 +110,75 @@ void grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
 
-        auto issue = [&](int kt, int s) {
-            const int koff = kt * BK;
-            uint8_t* base = smem + s * kStageBytes + (wave * 64) * 128;
+        auto issue = [&](int kt) {
+            const uint32_t kb = (uint32_t)kt * kBK * 2;
+            uint8_t* base = smem + (kt % kStages) * kStageBytes + (wave * 64) * kRowBytes;
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                __builtin_amdgcn_global_load_lds((gbl_cvoid*)(ga[i] + koff), (lds_void*)(base + i * 8 * 128), 16, 0, 0);
+            for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_global_load_lds((gbl_cvoid*)(a_base + aoff[i] + kb), (lds_void*)(base + i * 1024), 16, 0, 0);
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                __builtin_amdgcn_global_load_lds((gbl_cvoid*)(gb[i] + koff), (lds_void*)(base + kStageA + i * 8 * 128), 16, 0, 0);
+            for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_global_load_lds((gbl_cvoid*)(b_base + boff[i] + kb), (lds_void*)(base + kStageA + i * 1024), 16, 0, 0);
+        };
+        // MFMA operand fragments of k-step kk (16 deep) of K step kt.
+        const int fr = lane & 31;
+        const int arow_b = (wm * 128 + fr) * kRowBytes, brow_b = kStageA + (wn * 128 + fr) * kRowBytes;
+        const int fsw = swz(fr);
+        auto frags = [&](int kt, int kk, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
+            const uint8_t* st = smem + (kt % kStages) * kStageBytes;
+            const int pc = ((kk * 2 + (lane >> 5)) ^ fsw) * 16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8*)(st + arow_b + i * 32 * kRowBytes + pc);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = *(const bf16x8*)(st + brow_b + j * 32 * kRowBytes + pc);
         };
 
-        __syncthreads();  // every wave is done reading the previous tile's stages
-        issue(0, 0);
+        // Ring protocol (S = kStages slots, K step j lives in slot j % S, each
+        // step is 8 direct-to-LDS loads per lane, counted by vmcnt):
+        //  - prologue: issue steps 0..min(S,KT)-1, wait for step 0;
+        //  - K step kt: before the barrier wait for step kt+1, i.e. allow the
+        //    c = min(KT-2-kt, S-2) newer steps in flight (vmcnt(8c)), and for this
+        //    wave's own LDS reads of step kt (lgkmcnt(0)); after the barrier no
+        //    wave reads step kt any more, so its slot takes step kt+S.
+        // the previous tile's stores leave the vmcnt count, and every wave is
+        // done reading the previous tile's stages
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kStages; ++j)
+            if (j < KT) issue(j);
+        wait_vm_steps(KT - 1 < kStages - 1 ? KT - 1 : kStages - 1);
+        __syncthreads();
+        bf16x8 a0[4], b0[4], a1[4], b1[4];
+        frags(0, 0, a0, b0);
         for (int kt = 0; kt < KT; ++kt) {
-            const int s = kt & 1;
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-            if (kt + 1 < KT) issue(kt + 1, s ^ 1);
-            const uint8_t* As = smem + s * kStageBytes;
-            const uint8_t* Bs = As + kStageA;
+            // k-step 0 of this K step: read k-step 1's fragments under 16 MFMAs
+            frags(kt, 1, a1, b1);
+            mfma_block(acc, a0, b0);
 #pragma unroll
-            for (int kk = 0; kk < BK / 16; ++kk) {
-                const int pc = (kk * 2 + (lane >> 5)) ^ (lane & 7);
-                bf16x8 a[4], b[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    a[i] = *(const bf16x8*)(As + (wm * 128 + i * 32 + (lane & 31)) * 128 + pc * 16);
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    b[j] = *(const bf16x8*)(Bs + (wn * 128 + j * 32 + (lane & 31)) * 128 + pc * 16);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+            for (int q = 0; q < 8; ++q) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 8, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            // Every wave has read step kt (its reads done) and step kt+1 has
+            // landed: refill step kt's slot with step kt+kStages-1 and read
+            // step kt+1's first fragments under the last 16 MFMAs.
+            const int ahead = KT - 2 - kt;
+            wait_vm_steps(ahead < kStages - 2 ? ahead : kStages - 2);
+            __syncthreads();
+            if (kt + kStages < KT) issue(kt + kStages);
+            frags(kt + 1, 0, a0, b0);  // a stale but in-bounds read after the last step
+            mfma_block(acc, a1, b1);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedVMEM, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 8, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
 
         // Epilogue.  Fragment element r of lane l sits at row 8*(r/4) + 4*(l/32) + r%4,
