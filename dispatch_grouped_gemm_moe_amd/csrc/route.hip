@@ -21,10 +21,31 @@ namespace moe {
 
 #pragma clang fp contract(off)
 
-constexpr int kRouteTokens = 16;   // tokens per workgroup
-constexpr int kRouteExperts = 8;   // experts per wave pass
-constexpr int kRouteThreads = 256; // four waves
+constexpr int kRouteWaveTokens = 4;                       // tokens per wave
+constexpr int kRouteThreads = 256;                        // four waves
+constexpr int kRouteTokens = kRouteWaveTokens * kRouteThreads / kWave;  // per workgroup
+constexpr int kRouteEC = 32;                              // experts per accumulation pass
 
+// Lane l holds p[l]; returns in lane 0 the fixed halving tree
+// p[l] = p[l] + p[l+s] for s = 32, 16, 8, 4, 2, 1.  At each step only lanes
+// l < s must be right, and each of them receives p[l+s]: lanes 16 and 32 apart
+// through ds_bpermute, the rest through DPP row shifts / quad permutes.
+__device__ __forceinline__ float lane_tree64(float v) {
+    v = v + __shfl_xor(v, 32, kWave);
+    v = v + __shfl_xor(v, 16, kWave);
+    v = v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x108, 0xF, 0xF, false));  // row_shl:8
+    v = v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x104, 0xF, 0xF, false));  // row_shl:4
+    v = v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));   // quad [2,3,0,1]
+    v = v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));   // quad [1,0,3,2]
+    return v;
+}
+
+// A wave scores 4 tokens against up to 32 experts per pass: lane l runs the
+// partial sums p[l] of all 128 (token, expert) pairs, so one Wr row slice
+// (32 experts, 128 contiguous bytes when E >= 32) is read per lane per step
+// and reused for the 4 tokens; the 4 waves of a workgroup read the same Wr
+// rows at about the same time and share them through L1.
+template <bool kVec4>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ Wr, const float* __restrict__ bias,
     int T, int H, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
@@ -33,38 +54,45 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int t0 = blockIdx.x * kRouteTokens;
     const int nt = min(kRouteTokens, T - t0);
-    const int nchunks = ceil_div(E, kRouteExperts);
+    const int tw0 = t0 + wave * kRouteWaveTokens;  // this wave's first token
+    const int ntw = max(0, min(kRouteWaveTokens, T - tw0));
 
-    for (int c = wave; c < nchunks; c += kRouteThreads / kWave) {
-        const int e0 = c * kRouteExperts;
-        float acc[kRouteTokens][kRouteExperts];
+    for (int e0 = 0; e0 < E; e0 += kRouteEC) {
+        float acc[kRouteWaveTokens][kRouteEC];
 #pragma unroll
-        for (int tt = 0; tt < kRouteTokens; ++tt)
+        for (int tt = 0; tt < kRouteWaveTokens; ++tt)
 #pragma unroll
-            for (int ee = 0; ee < kRouteExperts; ++ee) acc[tt][ee] = 0.0f;
+            for (int ee = 0; ee < kRouteEC; ++ee) acc[tt][ee] = 0.0f;
         for (int h = lane; h < H; h += kWave) {
-            float wv[kRouteExperts];
+            float wv[kRouteEC];
+            const float* wrow = Wr + (size_t)h * E + e0;
+            if (kVec4) {
 #pragma unroll
-            for (int ee = 0; ee < kRouteExperts; ++ee)
-                wv[ee] = (e0 + ee < E) ? Wr[(size_t)h * E + e0 + ee] : 0.0f;
+                for (int q = 0; q < kRouteEC / 4; ++q) {
+                    const floatx4 w4 = (e0 + 4 * q < E) ? *(const floatx4*)(wrow + 4 * q) : floatx4{0, 0, 0, 0};
+                    wv[4 * q] = w4[0]; wv[4 * q + 1] = w4[1]; wv[4 * q + 2] = w4[2]; wv[4 * q + 3] = w4[3];
+                }
+            } else {
 #pragma unroll
-            for (int tt = 0; tt < kRouteTokens; ++tt) {
-                const float xv = (tt < nt) ? bf16_to_f32(x[(size_t)(t0 + tt) * H + h]) : 0.0f;
-#pragma unroll
-                for (int ee = 0; ee < kRouteExperts; ++ee) acc[tt][ee] = __builtin_fmaf(xv, wv[ee], acc[tt][ee]);
+                for (int ee = 0; ee < kRouteEC; ++ee) wv[ee] = (e0 + ee < E) ? wrow[ee] : 0.0f;
             }
+            float xv[kRouteWaveTokens];
+#pragma unroll
+            for (int tt = 0; tt < kRouteWaveTokens; ++tt)
+                xv[tt] = (tt < ntw) ? bf16_to_f32(x[(size_t)(tw0 + tt) * H + h]) : 0.0f;
+#pragma unroll
+            for (int tt = 0; tt < kRouteWaveTokens; ++tt)
+#pragma unroll
+                for (int ee = 0; ee < kRouteEC; ++ee) acc[tt][ee] = __builtin_fmaf(xv[tt], wv[ee], acc[tt][ee]);
         }
-        // Halving tree over the 64 lane partials: p[l] = p[l] + p[l+s], s = 32..1.
 #pragma unroll
-        for (int tt = 0; tt < kRouteTokens; ++tt)
+        for (int tt = 0; tt < kRouteWaveTokens; ++tt)
 #pragma unroll
-            for (int ee = 0; ee < kRouteExperts; ++ee) {
-                float v = acc[tt][ee];
-#pragma unroll
-                for (int s = 32; s >= 1; s >>= 1) v = v + __shfl_down(v, s, kWave);
-                if (lane == 0 && e0 + ee < E && tt < nt) {
+            for (int ee = 0; ee < kRouteEC; ++ee) {
+                float v = lane_tree64(acc[tt][ee]);
+                if (lane == 0 && e0 + ee < E && tt < ntw) {
                     if (bias) v = v + bias[e0 + ee];
-                    s_logit[tt][e0 + ee] = v;
+                    s_logit[wave * kRouteWaveTokens + tt][e0 + ee] = v;
                 }
             }
     }
@@ -126,8 +154,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
 void launch_route(const uint16_t* x, const float* Wr, const float* bias, int T, int H, int E, int k,
                   int32_t* topk_idx, float* topk_w, float* logits, hipStream_t stream) {
     const int blocks = ceil_div(T, kRouteTokens);
-    hipLaunchKernelGGL(route_kernel, dim3(blocks), dim3(kRouteThreads), 0, stream, x, Wr, bias, T, H,
-                       E, k, topk_idx, topk_w, logits);
+    const bool vec4 = (E % 4 == 0) && (((uintptr_t)Wr & 15) == 0);
+    if (vec4)
+        hipLaunchKernelGGL(route_kernel<true>, dim3(blocks), dim3(kRouteThreads), 0, stream, x, Wr, bias, T,
+                           H, E, k, topk_idx, topk_w, logits);
+    else
+        hipLaunchKernelGGL(route_kernel<false>, dim3(blocks), dim3(kRouteThreads), 0, stream, x, Wr, bias, T,
+                           H, E, k, topk_idx, topk_w, logits);
 }
 
 // ---------------------------------------------------------------------------
