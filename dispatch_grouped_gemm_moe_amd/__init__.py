@@ -24,7 +24,7 @@ MOE_F_IDENTITY_EXPERTS = 1 << 1
 EXPORTS = ("moe_status_string", "moe_abi_version", "moe_validate_cfg", "moe_query_sizes",
            "moe_prepare_weights", "moe_route", "moe_dispatch_layout", "moe_layer_fwd",
            "moe_layer_bwd", "moe_read_device_status", "moe_timing_enable", "moe_timing_read")
-KERNEL_KINDS = ("route", "layout", "gemm_gate_up", "gemm_down", "combine", "gather", "other")
+KERNEL_KINDS = ("route", "layout", "gemm_gate_up", "gemm_down", "combine", "gather", "other", "wgrad")
 
 
 class moe_cfg(ctypes.Structure):
@@ -47,7 +47,7 @@ class moe_weights(ctypes.Structure):
 
 
 class moe_kernel_times(ctypes.Structure):
-    _fields_ = [("launches", ctypes.c_int32 * 7), ("ms", ctypes.c_double * 7), ("dropped", ctypes.c_int32)]
+    _fields_ = [("launches", ctypes.c_int32 * 8), ("ms", ctypes.c_double * 8), ("dropped", ctypes.c_int32)]
 
 
 class MoeError(RuntimeError):
@@ -207,6 +207,7 @@ def alloc_buffers(cfg: moe_cfg, device="cuda", with_saved=False) -> LayerBuffers
     import torch
     s = moe_query_sizes(cfg)
     packed = torch.empty(s.packed_weights, dtype=torch.uint8, device=device)
-    ws = torch.zeros(s.workspace_fwd, dtype=torch.uint8, device=device)
+    ws = torch.zeros(max(s.workspace_fwd, s.workspace_bwd) if with_saved else s.workspace_fwd,
+                     dtype=torch.uint8, device=device)
     saved = torch.empty(s.saved, dtype=torch.uint8, device=device) if with_saved else None
     return LayerBuffers(cfg, s, packed, ws, saved)

@@ -25,14 +25,17 @@ struct Plan {
     int ld_tok_prow;  // k (+1 with the shared expert)
     int64_t rpad;     // padded GEMM rows of one minibatch
     int max_mtiles;
-    // packed weights (bytes)
-    size_t pk_w1t, pk_w2t, packed;
+    // packed weights (bytes): forward gate|up [Et][2I][H], down [Et][H][I];
+    // backward down [Et][I][H] and gate|up rows [Et][H][2I]
+    size_t pk_w1t, pk_w2t, pk_wd, pk_wgu, packed;
     // forward workspace (bytes)
     size_t ws_status, ws_idx, ws_w, ws_slot0, slot_bytes, ws_fwd;
     size_t sl_hdr, sl_mt, sl_prow_token, sl_tok_prow, sl_h, sl_y;
-    // saved (bytes)
-    size_t sv_idx, sv_w, saved;
-    size_t ws_bwd;
+    // saved (bytes): routing, then per minibatch g|u [rpad][2I] and Y [rpad][H]
+    size_t sv_idx, sv_w, sv_mb0, sv_mb, sv_y, saved;
+    // backward workspace (bytes)
+    size_t wb_wrt, wb_mt, wb_lay0, lay_bytes, ly_hdr, ly_prow_token, ly_tok_prow, ly_prow_slot;
+    size_t wb_dyt, wb_xgt, wb_dgut, wb_ht, wb_dsel, wb_dy, wb_dgu, wb_dx, wb_dgp, ws_bwd;
 };
 
 moe_status validate(const moe_cfg* c) {
@@ -88,7 +91,9 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     const size_t H = c->H, I = c->I, Et = p->Et;
     p->pk_w1t = 0;
     p->pk_w2t = align_up(p->pk_w1t + Et * 2 * I * H * 2);
-    p->packed = align_up(p->pk_w2t + Et * H * I * 2);
+    p->pk_wd = align_up(p->pk_w2t + Et * H * I * 2);
+    p->pk_wgu = align_up(p->pk_wd + Et * I * H * 2);
+    p->packed = align_up(p->pk_wgu + Et * H * 2 * I * 2);
 
     const size_t Tk = (size_t)c->T * c->k;
     p->ws_status = 0;
@@ -105,10 +110,34 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     p->slot_bytes = o;
     p->ws_fwd = p->ws_slot0 + (size_t)p->slots * p->slot_bytes;
 
+    const size_t rp = (size_t)p->rpad, nmb = (size_t)p->nmb;
     p->sv_idx = 0;
     p->sv_w = align_up(Tk * 4);
-    p->saved = align_up(p->sv_w + Tk * 4);
-    p->ws_bwd = kAlign;
+    p->sv_mb0 = align_up(p->sv_w + Tk * 4);
+    p->sv_y = align_up(rp * 2 * I * 2);
+    p->sv_mb = align_up(p->sv_y + rp * H * 2);
+    p->saved = p->sv_mb0 + nmb * p->sv_mb;
+
+    o = kAlign;  // device status word
+    p->wb_wrt = o; o = align_up(o + (size_t)c->E * H * 4);
+    p->wb_mt = o; o = align_up(o + nmb * (Et + 1) * 4);
+    size_t l = 0;
+    p->ly_hdr = l; l = align_up(l + sizeof(LayoutHeader));
+    p->ly_prow_token = l; l = align_up(l + rp * 4);
+    p->ly_tok_prow = l; l = align_up(l + (size_t)p->Mb * p->ld_tok_prow * 4);
+    p->ly_prow_slot = l; l = align_up(l + rp * 4);
+    p->lay_bytes = l;
+    p->wb_lay0 = o; o += nmb * p->lay_bytes;
+    p->wb_dyt = o; o = align_up(o + nmb * H * rp * 2);
+    p->wb_xgt = o; o = align_up(o + nmb * H * rp * 2);
+    p->wb_dgut = o; o = align_up(o + nmb * 2 * I * rp * 2);
+    p->wb_ht = o; o = align_up(o + nmb * I * rp * 2);
+    p->wb_dsel = o; o = align_up(o + nmb * rp * 4);
+    p->wb_dy = o; o = align_up(o + rp * H * 2);
+    p->wb_dgu = o; o = align_up(o + rp * 2 * I * 2);
+    p->wb_dx = o; o = align_up(o + rp * H * 2);
+    p->wb_dgp = o; o = align_up(o + rp * (H / 64) * 4);
+    p->ws_bwd = o;
     return MOE_OK;
 }
 
@@ -198,11 +227,17 @@ moe_status moe_prepare_weights(const moe_cfg* cfg, const uint16_t* Wg, const uin
     uint16_t* W1t = (uint16_t*)(base + p.pk_w1t);
     uint16_t* W2t = (uint16_t*)(base + p.pk_w2t);
     const size_t H = p.H, I = p.I;
+    uint16_t* Wdc = (uint16_t*)(base + p.pk_wd);
+    uint16_t* Wgu = (uint16_t*)(base + p.pk_wgu);
     launch_pack_gate_up(Wg, Wu, p.E, p.H, p.I, W1t, s);
     launch_transpose(Wd, p.E, p.I, p.H, W2t, s);
+    launch_copy(Wd, (size_t)p.E * I * H * 2, Wdc, s);
+    launch_concat_gu(Wg, Wu, p.E, p.H, p.I, Wgu, s);
     if (p.shared) {
         launch_pack_gate_up(Wsg, Wsu, 1, p.H, p.I, W1t + (size_t)p.E * 2 * I * H, s);
         launch_transpose(Wsd, 1, p.I, p.H, W2t + (size_t)p.E * H * I, s);
+        launch_copy(Wsd, I * H * 2, Wdc + (size_t)p.E * I * H, s);
+        launch_concat_gu(Wsg, Wsu, 1, p.H, p.I, Wgu + (size_t)p.E * H * 2 * I, s);
     }
     return check_launch();
 }
@@ -263,6 +298,12 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
         int32_t* tok_prow = (int32_t*)(slot + p.sl_tok_prow);
         uint16_t* hbuf = (uint16_t*)(slot + p.sl_h);
         uint16_t* ybuf = (uint16_t*)(slot + p.sl_y);
+        uint16_t* gubuf = nullptr;
+        if (saved) {  // keep g|u and Y of every minibatch for the backward
+            uint8_t* mb = (uint8_t*)saved + p.sv_mb0 + (size_t)b * p.sv_mb;
+            gubuf = (uint16_t*)mb;
+            ybuf = (uint16_t*)(mb + p.sv_y);
+        }
 
         LayoutOut o;
         memset(&o, 0, sizeof(o));
@@ -283,6 +324,7 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             g1.C = hbuf; g1.ldc = p.I;
             g1.N = 2 * p.I; g1.K = p.H;
             g1.mt_start = mt; g1.hdr = hdr; g1.Et = p.Et;
+            g1.GU = gubuf; g1.CT = nullptr; g1.HT = nullptr; g1.ldct = 0;
             TIMED(MOE_K_GEMM_GATE_UP, s, launch_grouped_gemm(g1, kEpiSwiGLU, grid, s));
             GemmArgs g2;
             g2.A = hbuf; g2.a_row_map = nullptr; g2.lda = p.I;
@@ -290,6 +332,7 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             g2.C = ybuf; g2.ldc = p.H;
             g2.N = p.H; g2.K = p.I;
             g2.mt_start = mt; g2.hdr = hdr; g2.Et = p.Et;
+            g2.GU = nullptr; g2.CT = nullptr; g2.HT = nullptr; g2.ldct = 0;
             TIMED(MOE_K_GEMM_DOWN, s, launch_grouped_gemm(g2, kEpiStore, grid, s));
         }
         TIMED(MOE_K_COMBINE, s,
@@ -306,9 +349,108 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
     Plan p;
     moe_status st = make_plan(cfg, &p);
     if (st != MOE_OK) return st;
-    (void)w; (void)x; (void)dout; (void)saved; (void)saved_bytes; (void)dx; (void)dWg; (void)dWu;
-    (void)dWd; (void)dWr; (void)dWs; (void)dgate; (void)ws; (void)ws_bytes; (void)stream;
-    return MOE_E_UNSUPPORTED;
+    if (p.identity) return MOE_E_UNSUPPORTED;
+    if (!w || !w->Wr || !w->packed || !x || !dout || !saved || !dx || !dWg || !dWu || !dWd || !dWr || !ws)
+        return MOE_E_INVALID;
+    if (p.shared && !dWs) return MOE_E_INVALID;
+    if (!aligned(x, 16) || !aligned(dout, 16) || !aligned(dx, 16) || !aligned(ws, kAlign) ||
+        !aligned(saved, kAlign) || !aligned(w->packed, kAlign) || !aligned(w->Wr, 16))
+        return MOE_E_INVALID;
+    if (w->packed_bytes < p.packed || saved_bytes < p.saved || ws_bytes < p.ws_bwd) return MOE_E_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    const int E = p.E, H = p.H, I = p.I, k = p.k, Et = p.Et;
+    const int64_t rp = p.rpad;
+    const uint8_t* sv = (const uint8_t*)saved;
+    const int32_t* idx = (const int32_t*)(sv + p.sv_idx);
+    const float* gw = (const float*)(sv + p.sv_w);
+    const uint8_t* pk = (const uint8_t*)w->packed;
+    const uint16_t* Wdc = (const uint16_t*)(pk + p.pk_wd);
+    const uint16_t* Wgu = (const uint16_t*)(pk + p.pk_wgu);
+    uint8_t* wsb = (uint8_t*)ws;
+    float* WrT = (float*)(wsb + p.wb_wrt);
+    int32_t* mt_all = (int32_t*)(wsb + p.wb_mt);
+    uint16_t* dYT_all = (uint16_t*)(wsb + p.wb_dyt);
+    uint16_t* xgT_all = (uint16_t*)(wsb + p.wb_xgt);
+    uint16_t* dGUT_all = (uint16_t*)(wsb + p.wb_dgut);
+    uint16_t* HT_all = (uint16_t*)(wsb + p.wb_ht);
+    float* dsel_all = (float*)(wsb + p.wb_dsel);
+    uint16_t* dY = (uint16_t*)(wsb + p.wb_dy);
+    uint16_t* dGU = (uint16_t*)(wsb + p.wb_dgu);
+    uint16_t* dXb = (uint16_t*)(wsb + p.wb_dx);
+    float* dgp = (float*)(wsb + p.wb_dgp);
+    const int grid = kNumCUs;
+
+    TIMED(MOE_K_OTHER, s, launch_transpose_f32(w->Wr, H, E, WrT, s));
+    for (int b = 0; b < p.nmb; ++b) {
+        const int t0 = b * p.Mb;
+        const int Tm = (p.T - t0) < p.Mb ? (p.T - t0) : p.Mb;
+        uint8_t* lay = wsb + p.wb_lay0 + (size_t)b * p.lay_bytes;
+        LayoutHeader* hdr = (LayoutHeader*)(lay + p.ly_hdr);
+        int32_t* mt = mt_all + (size_t)b * (Et + 1);
+        int32_t* prow_token = (int32_t*)(lay + p.ly_prow_token);
+        int32_t* tok_prow = (int32_t*)(lay + p.ly_tok_prow);
+        int32_t* prow_slot = (int32_t*)(lay + p.ly_prow_slot);
+        const uint8_t* svb = sv + p.sv_mb0 + (size_t)b * p.sv_mb;
+        const uint16_t* GUb = (const uint16_t*)svb;
+        const uint16_t* Yb = (const uint16_t*)(svb + p.sv_y);
+        uint16_t* dYT = dYT_all + (size_t)b * H * rp;
+        uint16_t* xgT = xgT_all + (size_t)b * H * rp;
+        uint16_t* dGUT = dGUT_all + (size_t)b * 2 * I * rp;
+        uint16_t* HT = HT_all + (size_t)b * I * rp;
+        float* dsel = dsel_all + (size_t)b * rp;
+
+        LayoutOut o;
+        memset(&o, 0, sizeof(o));
+        o.hdr = hdr; o.mt_start = mt; o.prow_token = prow_token; o.tok_prow = tok_prow;
+        o.prow_slot = prow_slot; o.tok_prow_ld = p.ld_tok_prow; o.token_base = t0;
+        TIMED(MOE_K_LAYOUT, s, launch_layout(idx + (size_t)t0 * k, Tm, E, k, p.shared ? 1 : 0, o, s));
+
+        RcombArgs rc;
+        rc.dout = dout; rc.x = x; rc.Y = Yb; rc.topk_w = gw; rc.prow_token = prow_token;
+        rc.prow_slot = prow_slot; rc.hdr = hdr; rc.dY = dY; rc.dYT = dYT; rc.xgT = xgT; rc.dgp = dgp;
+        rc.dsel = dsel; rc.H = H; rc.k = k; rc.nhb = H / 64; rc.ldt = rp;
+        TIMED(MOE_K_GATHER, s, launch_rcomb_gather(rc, (int)rp, s));
+
+        GemmArgs g1;  // dH = dY Wd^T with the SwiGLU backward in the epilogue
+        g1.A = dY; g1.a_row_map = nullptr; g1.lda = H;
+        g1.B = Wdc; g1.b_stride = (int64_t)I * H;
+        g1.C = dGU; g1.ldc = 2 * I; g1.N = I; g1.K = H;
+        g1.mt_start = mt; g1.hdr = hdr; g1.Et = Et;
+        g1.GU = (uint16_t*)GUb; g1.CT = dGUT; g1.HT = HT; g1.ldct = rp;
+        TIMED(MOE_K_GEMM_DOWN, s, launch_grouped_gemm(g1, kEpiSwiGLUBwd, grid, s));
+        GemmArgs g2;  // dX = dG Wg^T + dU Wu^T
+        g2.A = dGU; g2.a_row_map = nullptr; g2.lda = 2 * I;
+        g2.B = Wgu; g2.b_stride = (int64_t)H * 2 * I;
+        g2.C = dXb; g2.ldc = H; g2.N = H; g2.K = 2 * I;
+        g2.mt_start = mt; g2.hdr = hdr; g2.Et = Et;
+        g2.GU = nullptr; g2.CT = nullptr; g2.HT = nullptr; g2.ldct = 0;
+        TIMED(MOE_K_GEMM_GATE_UP, s, launch_grouped_gemm(g2, kEpiStore, grid, s));
+
+        RdispArgs rd;
+        rd.dX = dXb; rd.dgp = dgp; rd.tok_prow = tok_prow; rd.topk_idx = idx; rd.topk_w = gw; rd.WrT = WrT;
+        rd.dsel = dsel; rd.dgate = dgate; rd.dx = dx; rd.t0 = t0; rd.H = H; rd.k = k; rd.ld = p.ld_tok_prow;
+        rd.with_shared = p.shared ? 1 : 0; rd.nhb = H / 64;
+        TIMED(MOE_K_COMBINE, s, launch_rdispatch(rd, Tm, s));
+    }
+    WgradArgs wa;  // [dWg | dWu][e] = x_e^T [dG | dU]_e over every row of expert e
+    wa.A = xgT_all; wa.B = dGUT_all; wa.ld = rp;
+    wa.a_mb = (int64_t)H * rp * 2; wa.b_mb = (int64_t)2 * I * rp * 2;
+    wa.M = H; wa.N = 2 * I; wa.n_split = I; wa.Et = Et; wa.nmb = p.nmb; wa.mt_ld = Et + 1; wa.mt = mt_all;
+    wa.C0 = dWg; wa.C1 = dWu;
+    wa.Cs0 = p.shared ? dWs : nullptr; wa.Cs1 = p.shared ? dWs + (size_t)H * I : nullptr;
+    TIMED(MOE_K_WGRAD, s, launch_wgrad(wa, grid, s));
+    WgradArgs wd;  // dWd[e] = h_e^T dY_e
+    wd.A = HT_all; wd.B = dYT_all; wd.ld = rp;
+    wd.a_mb = (int64_t)I * rp * 2; wd.b_mb = (int64_t)H * rp * 2;
+    wd.M = I; wd.N = H; wd.n_split = H; wd.Et = Et; wd.nmb = p.nmb; wd.mt_ld = Et + 1; wd.mt = mt_all;
+    wd.C0 = dWd; wd.C1 = nullptr;
+    wd.Cs0 = p.shared ? dWs + (size_t)2 * H * I : nullptr; wd.Cs1 = nullptr;
+    TIMED(MOE_K_WGRAD, s, launch_wgrad(wd, grid, s));
+    DwrArgs dr;
+    dr.xgT = xgT_all; dr.dsel = dsel_all; dr.mt = mt_all; dr.dWr = dWr; dr.ldt = rp;
+    dr.x_mb = (int64_t)H * rp; dr.d_mb = rp; dr.H = H; dr.E = E; dr.nmb = p.nmb; dr.mt_ld = Et + 1;
+    TIMED(MOE_K_OTHER, s, launch_dwr(dr, s));
+    return check_launch();
 }
 
 moe_status moe_read_device_status(void* ws, void* stream, int32_t* code, int32_t* detail) {

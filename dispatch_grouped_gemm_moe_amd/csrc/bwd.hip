@@ -1,0 +1,256 @@
+// Backward-pass data movement and reductions of the MoE layer (gfx950).
+//
+// Training runs the two exchanges of the layer in reverse (KuCoin flash
+// "Cursor's MoK achieves 2.37x performance boost on NVIDIA GB300 NVL72",
+// section 01; section 02 names them reverse-combine and reverse-dispatch).
+// On one GPU they become:
+//   reverse-combine: every expert row r = (token t, slot j) receives
+//     dY_r = w[t,j] * dout[t], and d out / d w[t,j] = <dout[t], Y_r>;
+//   reverse-dispatch: dx[t] = sum_j dX_r(t,j) (+ the shared expert's rows)
+//     plus the router term sum_j dsel[t,j] * Wr[:, idx[t,j]], where
+//     dsel = w * (dgate - <w, dgate>) is the softmax backward.
+// Every floating-point sum has a fixed order (no atomics), so results are
+// bitwise reproducible.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+constexpr int kTile = 64;
+
+// One workgroup per 64 padded rows x 64 hidden columns of a minibatch.
+//   dY[prow][h]   = bf16(w * dout[t][h])  (0 on padding rows)
+//   dYT[h][prow]  = the same, transposed (weight-gradient operand)
+//   xgT[h][prow]  = x[t][h], transposed (weight-gradient operand)
+//   dgp[prow][hb] = sum over the block's 64 columns of dout[t][h] * Y[prow][h]
+//                   (routed rows; in column order, then a fixed pair tree)
+//   dsel[prow]    = 0 (filled for routed rows by the reverse-dispatch)
+__global__ __launch_bounds__(256) void rcomb_gather_kernel(RcombArgs p) {
+    __shared__ uint16_t sY[kTile][kTile + 2];
+    __shared__ uint16_t sX[kTile][kTile + 2];
+    const int prow0 = blockIdx.x * kTile, h0 = blockIdx.y * kTile;
+    if (prow0 >= p.hdr->m_tiles * BM) return;
+    const int tid = threadIdx.x;
+    const int r = tid >> 2, c0 = (tid & 3) * 16;
+    const int prow = prow0 + r;
+    const int slot = p.prow_slot[prow];
+    const int t = p.prow_token[prow];
+    const float w = slot < 0 ? 0.0f : (slot < p.k ? p.topk_w[(int64_t)t * p.k + slot] : 1.0f);
+    float d[16], xv[16];
+    {
+        const intx4* src = (const intx4*)(p.dout + (int64_t)t * p.H + h0 + c0);
+        const intx4* xs = (const intx4*)(p.x + (int64_t)t * p.H + h0 + c0);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const intx4 a = src[q], b = xs[q];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                d[8 * q + 2 * e] = __builtin_bit_cast(float, (uint32_t)a[e] << 16);
+                d[8 * q + 2 * e + 1] = __builtin_bit_cast(float, (uint32_t)a[e] & 0xffff0000u);
+                xv[8 * q + 2 * e] = __builtin_bit_cast(float, (uint32_t)b[e] << 16);
+                xv[8 * q + 2 * e + 1] = __builtin_bit_cast(float, (uint32_t)b[e] & 0xffff0000u);
+            }
+        }
+    }
+    // reverse-combine partial dot product <dout[t], Y[prow]> over this block's columns
+    float part = 0.0f;
+    if (slot >= 0 && slot < p.k) {
+        const intx4* ys = (const intx4*)(p.Y + (int64_t)prow * p.H + h0 + c0);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const intx4 yv = ys[q];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                part = __builtin_fmaf(d[8 * q + 2 * e], __builtin_bit_cast(float, (uint32_t)yv[e] << 16), part);
+                part = __builtin_fmaf(d[8 * q + 2 * e + 1], __builtin_bit_cast(float, (uint32_t)yv[e] & 0xffff0000u), part);
+            }
+        }
+    }
+    part = part + __shfl_xor(part, 1, kWave);
+    part = part + __shfl_xor(part, 2, kWave);
+    if ((tid & 3) == 0) {
+        if (slot >= 0 && slot < p.k) p.dgp[(int64_t)prow * p.nhb + blockIdx.y] = part;
+        if (blockIdx.y == 0) p.dsel[prow] = 0.0f;
+    }
+    uint16_t dy[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        dy[c] = f32_to_bf16_rne(w * d[c]);
+        sY[c0 + c][r] = dy[c];
+        sX[c0 + c][r] = f32_to_bf16_rne(xv[c]);
+    }
+    {
+        intx4* dst = (intx4*)(p.dY + (int64_t)prow * p.H + h0 + c0);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            intx4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = (int)((uint32_t)dy[8 * q + 2 * e] | ((uint32_t)dy[8 * q + 2 * e + 1] << 16));
+            dst[q] = o;
+        }
+    }
+    __syncthreads();
+    // transposed tiles: thread -> column h0 + tid/4, rows prow0 + 16*(tid%4) .. +16
+    const int hc = tid >> 2, r0 = (tid & 3) * 16;
+    intx4* dyt = (intx4*)(p.dYT + (int64_t)(h0 + hc) * p.ldt + prow0 + r0);
+    intx4* xgt = (intx4*)(p.xgT + (int64_t)(h0 + hc) * p.ldt + prow0 + r0);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        intx4 a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            a[e] = (int)((uint32_t)sY[hc][r0 + 8 * q + 2 * e] | ((uint32_t)sY[hc][r0 + 8 * q + 2 * e + 1] << 16));
+            b[e] = (int)((uint32_t)sX[hc][r0 + 8 * q + 2 * e] | ((uint32_t)sX[hc][r0 + 8 * q + 2 * e + 1] << 16));
+        }
+        dyt[q] = a;
+        xgt[q] = b;
+    }
+}
+
+void launch_rcomb_gather(const RcombArgs& a, int rpad, hipStream_t stream) {
+    hipLaunchKernelGGL(rcomb_gather_kernel, dim3(rpad / kTile, a.H / kTile), dim3(256), 0, stream, a);
+}
+
+// One workgroup per token of a minibatch: gate gradients, softmax backward and
+//   dx[t] = sum_j dX[prow_j] (+ dX[shared row]) + sum_j dsel_j * WrT[idx_j]
+constexpr int kRdThreads = 128;
+
+__global__ __launch_bounds__(kRdThreads) void rdispatch_kernel(RdispArgs p) {
+    __shared__ int s_row[kMaxTopK + 1];
+    __shared__ int s_idx[kMaxTopK];
+    __shared__ float s_w[kMaxTopK], s_dg[kMaxTopK], s_ds[kMaxTopK];
+    const int tl = blockIdx.x, t = p.t0 + tl, tid = threadIdx.x;
+    const int k = p.k;
+    if (tid < k + p.with_shared) s_row[tid] = p.tok_prow[(int64_t)tl * p.ld + tid];
+    if (tid < k) {
+        s_idx[tid] = p.topk_idx[(int64_t)t * k + tid];
+        s_w[tid] = p.topk_w[(int64_t)t * k + tid];
+    }
+    __syncthreads();
+    if (tid < k) {  // d out / d w[t,j]: the block partials in column order
+        const float* src = p.dgp + (int64_t)s_row[tid] * p.nhb;
+        float g = 0.0f;
+        for (int hb = 0; hb < p.nhb; ++hb) g = g + src[hb];
+        s_dg[tid] = g;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float dot = 0.0f;
+        for (int j = 0; j < k; ++j) dot = __builtin_fmaf(s_w[j], s_dg[j], dot);
+        for (int j = 0; j < k; ++j) {
+            const float ds = s_w[j] * (s_dg[j] - dot);
+            s_ds[j] = ds;
+            p.dsel[s_row[j]] = ds;
+            if (p.dgate) p.dgate[(int64_t)t * k + j] = s_dg[j];
+        }
+    }
+    __syncthreads();
+    for (int c = tid; c < p.H / 8; c += kRdThreads) {
+        float acc[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+        const int nrows = k + p.with_shared;
+        for (int j = 0; j < nrows; ++j) {
+            const intx4 raw = *(const intx4*)(p.dX + (int64_t)s_row[j] * p.H + c * 8);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] = acc[2 * e] + __builtin_bit_cast(float, (uint32_t)raw[e] << 16);
+                acc[2 * e + 1] = acc[2 * e + 1] + __builtin_bit_cast(float, (uint32_t)raw[e] & 0xffff0000u);
+            }
+        }
+        for (int j = 0; j < k; ++j) {
+            const floatx4* wr = (const floatx4*)(p.WrT + (int64_t)s_idx[j] * p.H + c * 8);
+            const floatx4 w0 = wr[0], w1 = wr[1];
+            const float ds = s_ds[j];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[q] = __builtin_fmaf(ds, w0[q], acc[q]);
+                acc[4 + q] = __builtin_fmaf(ds, w1[q], acc[4 + q]);
+            }
+        }
+        intx4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            o[e] = (int)((uint32_t)f32_to_bf16_rne(acc[2 * e]) | ((uint32_t)f32_to_bf16_rne(acc[2 * e + 1]) << 16));
+        *(intx4*)(p.dx + (int64_t)t * p.H + c * 8) = o;
+    }
+}
+
+void launch_rdispatch(const RdispArgs& a, int Tm, hipStream_t stream) {
+    hipLaunchKernelGGL(rdispatch_kernel, dim3(Tm), dim3(kRdThreads), 0, stream, a);
+}
+
+// Router weight gradient: dWr[h][e] = sum over expert e's rows, minibatch by
+// minibatch, row by row, of dsel[row] * x[token(row)][h] (read from the
+// transposed gathered copy; padding rows carry dsel = 0).
+__global__ __launch_bounds__(256) void dwr_kernel(DwrArgs p) {
+    const int e = blockIdx.x, h = blockIdx.y * 256 + threadIdx.x;
+    if (h >= p.H) return;
+    float acc = 0.0f;
+    for (int b = 0; b < p.nmb; ++b) {
+        const int r0 = p.mt[(int64_t)b * p.mt_ld + e] * BM, r1 = p.mt[(int64_t)b * p.mt_ld + e + 1] * BM;
+        const uint16_t* xr = p.xgT + (int64_t)b * p.x_mb + (int64_t)h * p.ldt;
+        const float* ds = p.dsel + (int64_t)b * p.d_mb;
+        for (int r = r0; r < r1; r += 8) {
+            const intx4 xv = *(const intx4*)(xr + r);
+            const floatx4 d0 = *(const floatx4*)(ds + r), d1 = *(const floatx4*)(ds + r + 4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float xa = __builtin_bit_cast(float, (uint32_t)xv[q] << 16);
+                const float xb = __builtin_bit_cast(float, (uint32_t)xv[q] & 0xffff0000u);
+                const float da = q < 2 ? d0[2 * q] : d1[2 * q - 4];
+                const float db = q < 2 ? d0[2 * q + 1] : d1[2 * q - 3];
+                acc = __builtin_fmaf(da, xa, acc);
+                acc = __builtin_fmaf(db, xb, acc);
+            }
+        }
+    }
+    p.dWr[(int64_t)h * p.E + e] = acc;
+}
+
+void launch_dwr(const DwrArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(dwr_kernel, dim3(a.E, ceil_div(a.H, 256)), dim3(256), 0, stream, a);
+}
+
+// dst[c][r] = src[r][c] for fp32 [rows][cols] (small matrices).
+__global__ __launch_bounds__(256) void transpose_f32_kernel(const float* __restrict__ src, int rows, int cols,
+                                                            float* __restrict__ dst) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)rows * cols) return;
+    const int r = (int)(i / cols), c = (int)(i % cols);
+    dst[(int64_t)c * rows + r] = src[i];
+}
+
+void launch_transpose_f32(const float* src, int rows, int cols, float* dst, hipStream_t stream) {
+    const int64_t n = (int64_t)rows * cols;
+    hipLaunchKernelGGL(transpose_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, src, rows, cols,
+                       dst);
+}
+
+// Row-wise concatenation of the gate and up weights for the input-gradient
+// GEMM: Wgu[e][h][c] = c < I ? Wg[e][h][c] : Wu[e][h][c - I].
+__global__ __launch_bounds__(256) void concat_gu_kernel(const uint16_t* __restrict__ Wg, const uint16_t* __restrict__ Wu,
+                                                        int H, int I, uint16_t* __restrict__ Wgu) {
+    const int64_t row = blockIdx.x;  // e * H + h
+    for (int c = threadIdx.x * 8; c < 2 * I; c += 256 * 8) {
+        const uint16_t* src = c < I ? Wg + row * I + c : Wu + row * I + (c - I);
+        *(intx4*)(Wgu + row * 2 * I + c) = *(const intx4*)src;
+    }
+}
+
+void launch_concat_gu(const uint16_t* Wg, const uint16_t* Wu, int E, int H, int I, uint16_t* Wgu, hipStream_t stream) {
+    hipLaunchKernelGGL(concat_gu_kernel, dim3(E * H), dim3(256), 0, stream, Wg, Wu, H, I, Wgu);
+}
+
+__global__ __launch_bounds__(256) void copy16_kernel(const intx4* __restrict__ src, int64_t n16, intx4* __restrict__ dst) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256) dst[i] = src[i];
+}
+
+void launch_copy(const void* src, size_t bytes, void* dst, hipStream_t stream) {
+    const int64_t n16 = (int64_t)(bytes / 16);
+    const int blocks = (int)((n16 + 255) / 256 < 8192 ? (n16 + 255) / 256 : 8192);
+    hipLaunchKernelGGL(copy16_kernel, dim3(blocks > 0 ? blocks : 1), dim3(256), 0, stream, (const intx4*)src, n16,
+                       (intx4*)dst);
+}
+
+}  // namespace moe

@@ -56,12 +56,125 @@ static_assert(kStages <= 5, "wait_vm_steps covers at most 4 steps in flight");
 // Scheduling masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMFMA = 0x008, kSchedVMEM = 0x020, kSchedDSRead = 0x100;
 
+// K sequence of a dense GEMM: K step kt sits kt * 64 bytes into every row.
+struct DenseK {
+    int kt = 0;
+    __device__ __forceinline__ void next(int64_t& a_off, int64_t& b_off) {
+        a_off = b_off = (int64_t)kt * kBK * 2;
+        ++kt;
+    }
+};
+
+// One 256 x 256 output tile: acc = A_tile * B_tile^T over KT K steps.
+// a_base/b_base + aoff[i]/boff[i] address the 4 A and 4 B rows this lane
+// stages (tile rows wave*64 + 16i + lane/4, swizzled chunk); kit.next() gives
+// the byte offset of each successive K step, called in K order.
+template <class KIt>
+__device__ __forceinline__ void tile_mainloop(floatx16 (&acc)[4][4], uint8_t* smem, const char* a_base,
+                                              const uint32_t (&aoff)[4], const char* b_base,
+                                              const uint32_t (&boff)[4], int KT, KIt kit) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
+    if (KT <= 0) return;
+
+    auto issue = [&](int kt) {
+        int64_t ka, kb;
+        kit.next(ka, kb);
+        uint8_t* base = smem + (kt % kStages) * kStageBytes + (wave * 64) * kRowBytes;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_global_load_lds((gbl_cvoid*)(a_base + ka + aoff[i]), (lds_void*)(base + i * 1024), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_global_load_lds((gbl_cvoid*)(b_base + kb + boff[i]), (lds_void*)(base + kStageA + i * 1024), 16, 0, 0);
+    };
+    // MFMA operand fragments of k-step kk (16 deep) of K step kt.
+    const int fr = lane & 31;
+    const int arow_b = (wm * 128 + fr) * kRowBytes, brow_b = kStageA + (wn * 128 + fr) * kRowBytes;
+    const int fsw = swz(fr);
+    auto frags = [&](int kt, int kk, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
+        const uint8_t* st = smem + (kt % kStages) * kStageBytes;
+        const int pc = ((kk * 2 + (lane >> 5)) ^ fsw) * 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8*)(st + arow_b + i * 32 * kRowBytes + pc);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = *(const bf16x8*)(st + brow_b + j * 32 * kRowBytes + pc);
+    };
+
+    // Ring protocol (S = kStages slots, K step j lives in slot j % S, each
+    // step is 8 direct-to-LDS loads per lane, counted by vmcnt):
+    //  - prologue: issue steps 0..min(S,KT)-1, wait for step 0;
+    //  - K step kt: before the barrier wait for step kt+1, i.e. allow the
+    //    c = min(KT-2-kt, S-2) newer steps in flight (vmcnt(8c)), and for this
+    //    wave's own LDS reads of step kt (lgkmcnt(0)); after the barrier no
+    //    wave reads step kt any more, so its slot takes step kt+S.
+    // First the previous tile's stores leave the vmcnt count and every wave is
+    // done reading the previous tile's stages.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kStages; ++j)
+        if (j < KT) issue(j);
+    wait_vm_steps(KT - 1 < kStages - 1 ? KT - 1 : kStages - 1);
+    __syncthreads();
+    bf16x8 a0[4], b0[4], a1[4], b1[4];
+    frags(0, 0, a0, b0);
+    for (int kt = 0; kt < KT; ++kt) {
+        // k-step 0 of this K step: read k-step 1's fragments under 16 MFMAs
+        frags(kt, 1, a1, b1);
+        mfma_block(acc, a0, b0);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 8, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        // Every wave has read step kt (its reads done) and step kt+1 has
+        // landed: refill step kt's slot with step kt+kStages and read step
+        // kt+1's first fragments under the last 16 MFMAs.
+        const int ahead = KT - 2 - kt;
+        wait_vm_steps(ahead < kStages - 2 ? ahead : kStages - 2);
+        __syncthreads();
+        if (kt + kStages < KT) issue(kt + kStages);
+        frags(kt + 1, 0, a0, b0);  // a stale but in-bounds read after the last step
+        mfma_block(acc, a1, b1);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedVMEM, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 8, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Accumulator element r of fragment (i, j) of lane l sits in tile row
+// wm*128 + 32i + 8(r/4) + 4(l/32) + r%4 and tile column wn*128 + 32j + l%32.
+__device__ __forceinline__ int frag_row(int i, int r) {
+    const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) >> 1;
+    return wm * 128 + i * 32 + (r >> 2) * 8 + 4 * (lane >> 5) + (r & 3);
+}
+__device__ __forceinline__ int frag_col(int j) {
+    const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
+    return wn * 128 + j * 32 + (lane & 31);
+}
+
+__device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
+    return uint2{(uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16),
+                 (uint32_t)f32_to_bf16_rne(c) | ((uint32_t)f32_to_bf16_rne(d) << 16)};
+}
+
 template <int EPI>
 __global__ __attribute__((amdgpu_flat_work_group_size(kGemmThreads, kGemmThreads), amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_kernel(GemmArgs p) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
     const int NT = ceil_div(p.N, BN);
     const int total = p.hdr->m_tiles * NT;
     const int G = gridDim.x, per = G >> 3;
@@ -90,8 +203,6 @@ void grouped_gemm_kernel(GemmArgs p) {
         // Byte offsets of the 4 A rows and 4 B rows this lane stages per K step:
         // instruction i fills tile rows wave*64 + 16i .. +15 (lane/4 picks the row,
         // lane%4 the fixed LDS chunk; the lane loads the logical chunk stored there).
-        const char* a_base = (const char*)p.A;
-        const char* b_base = (const char*)(p.B + (int64_t)e * p.b_stride);
         uint32_t aoff[4], boff[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -103,92 +214,16 @@ void grouped_gemm_kernel(GemmArgs p) {
             const int n = min(n0 + r, p.N - 1);
             boff[i] = (uint32_t)(((int64_t)n * p.K + lchunk * 8) * 2);
         }
-
         floatx16 acc[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
+        tile_mainloop(acc, smem, (const char*)p.A, aoff, (const char*)(p.B + (int64_t)e * p.b_stride), boff, KT,
+                      DenseK{});
 
-        auto issue = [&](int kt) {
-            const uint32_t kb = (uint32_t)kt * kBK * 2;
-            uint8_t* base = smem + (kt % kStages) * kStageBytes + (wave * 64) * kRowBytes;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                __builtin_amdgcn_global_load_lds((gbl_cvoid*)(a_base + aoff[i] + kb), (lds_void*)(base + i * 1024), 16, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                __builtin_amdgcn_global_load_lds((gbl_cvoid*)(b_base + boff[i] + kb), (lds_void*)(base + kStageA + i * 1024), 16, 0, 0);
-        };
-        // MFMA operand fragments of k-step kk (16 deep) of K step kt.
-        const int fr = lane & 31;
-        const int arow_b = (wm * 128 + fr) * kRowBytes, brow_b = kStageA + (wn * 128 + fr) * kRowBytes;
-        const int fsw = swz(fr);
-        auto frags = [&](int kt, int kk, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
-            const uint8_t* st = smem + (kt % kStages) * kStageBytes;
-            const int pc = ((kk * 2 + (lane >> 5)) ^ fsw) * 16;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8*)(st + arow_b + i * 32 * kRowBytes + pc);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = *(const bf16x8*)(st + brow_b + j * 32 * kRowBytes + pc);
-        };
-
-        // Ring protocol (S = kStages slots, K step j lives in slot j % S, each
-        // step is 8 direct-to-LDS loads per lane, counted by vmcnt):
-        //  - prologue: issue steps 0..min(S,KT)-1, wait for step 0;
-        //  - K step kt: before the barrier wait for step kt+1, i.e. allow the
-        //    c = min(KT-2-kt, S-2) newer steps in flight (vmcnt(8c)), and for this
-        //    wave's own LDS reads of step kt (lgkmcnt(0)); after the barrier no
-        //    wave reads step kt any more, so its slot takes step kt+S.
-        // the previous tile's stores leave the vmcnt count, and every wave is
-        // done reading the previous tile's stages
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < kStages; ++j)
-            if (j < KT) issue(j);
-        wait_vm_steps(KT - 1 < kStages - 1 ? KT - 1 : kStages - 1);
-        __syncthreads();
-        bf16x8 a0[4], b0[4], a1[4], b1[4];
-        frags(0, 0, a0, b0);
-        for (int kt = 0; kt < KT; ++kt) {
-            // k-step 0 of this K step: read k-step 1's fragments under 16 MFMAs
-            frags(kt, 1, a1, b1);
-            mfma_block(acc, a0, b0);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 8, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            // Every wave has read step kt (its reads done) and step kt+1 has
-            // landed: refill step kt's slot with step kt+kStages-1 and read
-            // step kt+1's first fragments under the last 16 MFMAs.
-            const int ahead = KT - 2 - kt;
-            wait_vm_steps(ahead < kStages - 2 ? ahead : kStages - 2);
-            __syncthreads();
-            if (kt + kStages < KT) issue(kt + kStages);
-            frags(kt + 1, 0, a0, b0);  // a stale but in-bounds read after the last step
-            mfma_block(acc, a1, b1);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(kSchedVMEM, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 8, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-
-        // Epilogue.  Fragment element r of lane l sits at row 8*(r/4) + 4*(l/32) + r%4,
-        // column l%32 of its 32x32 block.
-        const int rbase = prow0 + wm * 128 + 4 * (lane >> 5);
         if (EPI == kEpiSwiGLU) {
+            // columns come in 64-wide groups of 32 gate then 32 up columns
             const int I = p.N / 2;
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
-                const int hcol = n0 / 2 + wn * 64 + jj * 32 + (lane & 31);
+                const int hcol = n0 / 2 + (wave & 1) * 64 + jj * 32 + (lane & 31);
                 if (hcol < I) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
@@ -196,22 +231,57 @@ void grouped_gemm_kernel(GemmArgs p) {
                         for (int r = 0; r < 16; ++r) {
                             const float g = acc[i][2 * jj][r], u = acc[i][2 * jj + 1][r];
                             const float h = g / (1.0f + __expf(-g)) * u;
-                            const int row = rbase + i * 32 + (r >> 2) * 8 + (r & 3);
-                            p.C[(int64_t)row * p.ldc + hcol] = f32_to_bf16_rne(h);
+                            const int64_t row = prow0 + frag_row(i, r);
+                            p.C[row * p.ldc + hcol] = f32_to_bf16_rne(h);
+                            if (p.GU) {
+                                p.GU[row * 2 * I + hcol] = f32_to_bf16_rne(g);
+                                p.GU[row * 2 * I + I + hcol] = f32_to_bf16_rne(u);
+                            }
                         }
                 }
             }
-        } else {
+        } else if (EPI == kEpiStore) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int col = n0 + wn * 128 + j * 32 + (lane & 31);
+                const int col = n0 + frag_col(j);
                 if (col < p.N) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int row = rbase + i * 32 + (r >> 2) * 8 + (r & 3);
-                            p.C[(int64_t)row * p.ldc + col] = f32_to_bf16_rne(acc[i][j][r]);
+                        for (int r = 0; r < 16; ++r)
+                            p.C[(int64_t)(prow0 + frag_row(i, r)) * p.ldc + col] = f32_to_bf16_rne(acc[i][j][r]);
+                }
+            }
+        } else {  // kEpiSwiGLUBwd: acc = dH (N = I columns)
+            const int I = p.N;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int col = n0 + frag_col(j);
+                if (col < I) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            float dg[4], du[4], hh[4];
+                            const int row0 = prow0 + frag_row(i, 4 * q);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) {
+                                const int64_t row = row0 + r;
+                                const float g = bf16_to_f32(p.GU[row * 2 * I + col]);
+                                const float u = bf16_to_f32(p.GU[row * 2 * I + I + col]);
+                                const float sg = 1.0f / (1.0f + __expf(-g));
+                                const float silu = g * sg;
+                                const float dh = acc[i][j][4 * q + r];
+                                dg[r] = dh * u * (sg * (1.0f + g * (1.0f - sg)));
+                                du[r] = dh * silu;
+                                hh[r] = silu * u;
+                                p.C[row * 2 * I + col] = f32_to_bf16_rne(dg[r]);
+                                p.C[row * 2 * I + I + col] = f32_to_bf16_rne(du[r]);
+                            }
+                            // transposed copies for the weight-gradient GEMMs: 4 consecutive rows
+                            *(uint2*)(p.CT + (int64_t)col * p.ldct + row0) = pack4_bf16(dg[0], dg[1], dg[2], dg[3]);
+                            *(uint2*)(p.CT + (int64_t)(I + col) * p.ldct + row0) = pack4_bf16(du[0], du[1], du[2], du[3]);
+                            *(uint2*)(p.HT + (int64_t)col * p.ldct + row0) = pack4_bf16(hh[0], hh[1], hh[2], hh[3]);
                         }
                 }
             }
@@ -219,11 +289,91 @@ void grouped_gemm_kernel(GemmArgs p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// weight gradients: C[e] = A_e^T-rows x B_e^T-rows over every routed row of
+// expert e, minibatch by minibatch in order (a fixed summation order).
+// ---------------------------------------------------------------------------
+
+// K sequence of expert e's rows: for each minibatch b its padded row range
+// [mt_b[e], mt_b[e+1]) x BM, in 32-row K steps; A and B copies of
+// minibatch b lie a_mb / b_mb bytes after minibatch 0's.
+struct SegmentK {
+    const int32_t* mt;  // [nmb][mt_ld]
+    int mt_ld, e, nmb;
+    int64_t a_mb, b_mb;
+    int b = 0, step = 0;
+    __device__ __forceinline__ int steps_of(int bb) const {
+        return (mt[(int64_t)bb * mt_ld + e + 1] - mt[(int64_t)bb * mt_ld + e]) * (BM / kBK);
+    }
+    __device__ __forceinline__ void next(int64_t& a_off, int64_t& b_off) {
+        while (b < nmb && step >= steps_of(b)) { ++b; step = 0; }
+        const int64_t kbyte = ((int64_t)mt[(int64_t)b * mt_ld + e] * BM + (int64_t)step * kBK) * 2;
+        a_off = (int64_t)b * a_mb + kbyte;
+        b_off = (int64_t)b * b_mb + kbyte;
+        ++step;
+    }
+};
+
+__global__ __attribute__((amdgpu_flat_work_group_size(kGemmThreads, kGemmThreads), amdgpu_waves_per_eu(1, 1)))
+void wgrad_kernel(WgradArgs p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int MT = ceil_div(p.M, BM), NT = ceil_div(p.N, BN);
+    const int total = p.Et * MT * NT;
+    const int G = gridDim.x, per = G >> 3;
+    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+    for (int it = 0;; ++it) {
+        const int v = it * G + xcd * per + local;
+        if (v >= total) break;
+        // tile order: expert-major, then M tile, then N tile (N fastest)
+        const int e = v / (MT * NT), loc = v - e * MT * NT;
+        const int m0 = (loc / NT) * BM, n0 = (loc % NT) * BN;
+        int KT = 0;
+        for (int b = 0; b < p.nmb; ++b) KT += (p.mt[(int64_t)b * p.mt_ld + e + 1] - p.mt[(int64_t)b * p.mt_ld + e]) * (BM / kBK);
+        uint32_t aoff[4], boff[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = wave * 64 + i * 16 + (lane >> 2);
+            const int lchunk = (lane & 3) ^ swz(r);
+            aoff[i] = (uint32_t)(((int64_t)min(m0 + r, p.M - 1) * p.ld + lchunk * 8) * 2);
+            boff[i] = (uint32_t)(((int64_t)min(n0 + r, p.N - 1) * p.ld + lchunk * 8) * 2);
+        }
+        SegmentK kit{p.mt, p.mt_ld, e, p.nmb, p.a_mb, p.b_mb};
+        floatx16 acc[4][4];
+        tile_mainloop(acc, smem, (const char*)p.A, aoff, (const char*)p.B, boff, KT, kit);
+        // columns < n_split go to C0, the rest to C1 (column - n_split); the
+        // last expert writes to the shared-expert outputs when they are given
+        const bool shared = p.Cs0 && e == p.Et - 1;
+        float* c0 = shared ? p.Cs0 : p.C0 + (int64_t)e * p.M * p.n_split;
+        float* c1 = shared ? p.Cs1 : (p.C1 ? p.C1 + (int64_t)e * p.M * (p.N - p.n_split) : nullptr);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int col = n0 + frag_col(j);
+            if (col >= p.N) continue;
+            float* dst = col < p.n_split ? c0 + col : c1 + (col - p.n_split);
+            const int64_t ldc = col < p.n_split ? p.n_split : p.N - p.n_split;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int m = m0 + frag_row(i, r);
+                    if (m < p.M) dst[(int64_t)m * ldc] = acc[i][j][r];
+                }
+        }
+    }
+}
+
+void launch_wgrad(const WgradArgs& a, int grid, hipStream_t stream) {
+    hipLaunchKernelGGL(wgrad_kernel, dim3(grid), dim3(kGemmThreads), 0, stream, a);
+}
+
 void launch_grouped_gemm(const GemmArgs& a, GemmEpilogue epi, int grid, hipStream_t stream) {
     if (epi == kEpiSwiGLU)
         hipLaunchKernelGGL(grouped_gemm_kernel<kEpiSwiGLU>, dim3(grid), dim3(kGemmThreads), 0, stream, a);
-    else
+    else if (epi == kEpiStore)
         hipLaunchKernelGGL(grouped_gemm_kernel<kEpiStore>, dim3(grid), dim3(kGemmThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL(grouped_gemm_kernel<kEpiSwiGLUBwd>, dim3(grid), dim3(kGemmThreads), 0, stream, a);
 }
 
 // ---------------------------------------------------------------------------

@@ -18,6 +18,7 @@ struct LayoutOut {
     int32_t* mt_start;    // [Et+1]   first BM-tile of each expert (Et = E + shared)
     int32_t* prow_token;  // [R_pad]  token (absolute) feeding each padded GEMM row
     int32_t* tok_prow;    // [Tm, tok_prow_ld] padded row of each slot; column k = shared row
+    int32_t* prow_slot;   // [R_pad]  slot j of each padded row: 0..k-1 routed, k shared, -1 padding
     int32_t tok_prow_ld;
     int32_t token_base;   // added to tokens written into prow_token
 };
@@ -41,9 +42,35 @@ struct GemmArgs {
     const int32_t* mt_start;   // [Et+1]
     const LayoutHeader* hdr;
     int Et;
+    // kEpiSwiGLU: optional [R_pad][2I] copy of g | u (kept for the backward).
+    // kEpiSwiGLUBwd: the saved g | u to read; C receives dG | dU [R_pad][2I].
+    uint16_t* GU;
+    // kEpiSwiGLUBwd: transposed outputs [2I][ldct] (dG | dU) and [I][ldct] (h).
+    uint16_t* CT;
+    uint16_t* HT;
+    int64_t ldct;
 };
 
-enum GemmEpilogue { kEpiSwiGLU = 0, kEpiStore = 1 };
+enum GemmEpilogue { kEpiSwiGLU = 0, kEpiStore = 1, kEpiSwiGLUBwd = 2 };
+
+// Weight-gradient GEMM: C[e][m][n] = sum over expert e's padded rows r of every
+// minibatch of A[m][r] * B[n][r]; A, B are row-major [M or N][ld] copies, one
+// per minibatch, a_mb / b_mb bytes apart.  Padding rows must hold zeros in A
+// or B.  Columns n < n_split go to C0 [Et][M][n_split], the rest to
+// C1 [Et][M][N - n_split]; with Cs0 set, the last expert writes to Cs0/Cs1.
+struct WgradArgs {
+    const uint16_t* A;
+    const uint16_t* B;
+    int64_t ld, a_mb, b_mb;
+    int M, N, n_split, Et, nmb, mt_ld;
+    const int32_t* mt;  // [nmb][mt_ld] first BM-tile of each expert, per minibatch
+    float* C0;
+    float* C1;
+    float* Cs0;
+    float* Cs1;
+};
+
+void launch_wgrad(const WgradArgs& a, int grid, hipStream_t stream);
 
 void launch_grouped_gemm(const GemmArgs& a, GemmEpilogue epi, int grid, hipStream_t stream);
 
@@ -55,6 +82,55 @@ void launch_combine(const uint16_t* Y, int64_t ldy, const int32_t* tok_prow, int
 // Y[prow] = x[prow_token[prow]] for every padded row (identity-expert dispatch).
 void launch_gather_rows(const uint16_t* x, int H, const int32_t* prow_token, const LayoutHeader* hdr,
                         int max_rows, uint16_t* Y, int64_t ldy, hipStream_t stream);
+
+// Backward: reverse-combine gather over the padded rows of one minibatch.
+struct RcombArgs {
+    const uint16_t* dout;      // [T][H]
+    const uint16_t* x;         // [T][H]
+    const uint16_t* Y;         // [R_pad][H] saved expert outputs of the minibatch
+    const float* topk_w;       // [T][k]
+    const int32_t* prow_token;
+    const int32_t* prow_slot;
+    const LayoutHeader* hdr;
+    uint16_t* dY;              // [R_pad][H]
+    uint16_t* dYT;             // [H][ldt]
+    uint16_t* xgT;             // [H][ldt]
+    float* dgp;                // [R_pad][nhb] partial gate gradients
+    float* dsel;               // [R_pad] zeroed
+    int H, k, nhb;
+    int64_t ldt;
+};
+void launch_rcomb_gather(const RcombArgs& a, int rpad, hipStream_t stream);
+
+// Backward: reverse-dispatch of one minibatch (tokens t0 .. t0+Tm-1).
+struct RdispArgs {
+    const uint16_t* dX;        // [R_pad][H]
+    const float* dgp;          // [R_pad][nhb]
+    const int32_t* tok_prow;   // [Tm][ld]
+    const int32_t* topk_idx;   // [T][k]
+    const float* topk_w;       // [T][k]
+    const float* WrT;          // [E][H]
+    float* dsel;               // [R_pad]
+    float* dgate;              // [T][k] or NULL
+    uint16_t* dx;              // [T][H]
+    int t0, H, k, ld, with_shared, nhb;
+};
+void launch_rdispatch(const RdispArgs& a, int Tm, hipStream_t stream);
+
+// Backward: router weight gradient over all minibatches.
+struct DwrArgs {
+    const uint16_t* xgT;       // minibatch 0's [H][ldt]; minibatch b at + b * x_mb elements
+    const float* dsel;         // minibatch 0's [R_pad]; minibatch b at + b * d_mb elements
+    const int32_t* mt;         // [nmb][mt_ld]
+    float* dWr;                // [H][E]
+    int64_t ldt, x_mb, d_mb;
+    int H, E, nmb, mt_ld;
+};
+void launch_dwr(const DwrArgs& a, hipStream_t stream);
+
+void launch_transpose_f32(const float* src, int rows, int cols, float* dst, hipStream_t stream);
+void launch_concat_gu(const uint16_t* Wg, const uint16_t* Wu, int E, int H, int I, uint16_t* Wgu, hipStream_t stream);
+void launch_copy(const void* src, size_t bytes, void* dst, hipStream_t stream);
 
 // Weight packing (bf16).
 void launch_pack_gate_up(const uint16_t* Wg, const uint16_t* Wu, int E, int H, int I, uint16_t* W1t,

@@ -267,6 +267,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(const int32_t* _
                 if (o.tok_row) o.tok_row[(size_t)t * k + js] = row;
                 if (o.prow_token) o.prow_token[prow] = o.token_base + t;
                 if (o.tok_prow) o.tok_prow[(size_t)t * o.tok_prow_ld + js] = prow;
+                if (o.prow_slot) o.prow_slot[prow] = js;
             }
             if (lane == 0) s_cnt[wave][e] = base + __popcll(mask);
         }
@@ -274,6 +275,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(const int32_t* _
             const int prow = s_poff[E] + t;
             if (o.prow_token) o.prow_token[prow] = o.token_base + t;
             if (o.tok_prow) o.tok_prow[(size_t)t * o.tok_prow_ld + k] = prow;
+            if (o.prow_slot) o.prow_slot[prow] = k;
         }
     }
     __syncthreads();
@@ -285,7 +287,10 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(const int32_t* _
             const int tot = (e < E) ? s_off[e + 1] - s_off[e] : Tm;
             if (tot == 0) continue;
             const int first = o.prow_token[s_poff[e]];
-            for (int r = s_poff[e] + tot + lane; r < s_poff[e + 1]; r += kWave) o.prow_token[r] = first;
+            for (int r = s_poff[e] + tot + lane; r < s_poff[e + 1]; r += kWave) {
+                o.prow_token[r] = first;
+                if (o.prow_slot) o.prow_slot[r] = -1;
+            }
         }
     }
 }

@@ -182,7 +182,8 @@ moe_status moe_dispatch_layout(const moe_cfg *cfg, const int32_t *topk_idx, int3
  *   x [T,H] bf16, out [T,H] bf16.
  *   saved: NULL, or at least moe_sizes.saved bytes that moe_layer_bwd will read.
  *       It starts with the routing of every token: topk_idx [T,k] int32 at
- *       byte 0, then topk_w [T,k] fp32 at the next 256-byte boundary.
+ *       byte 0, then topk_w [T,k] fp32 at the next 256-byte boundary; the
+ *       rest (per-minibatch g|u and expert outputs, bf16) is internal.
  *   ws: at least moe_sizes.workspace_fwd bytes, 256-byte aligned.  Its first 256
  *       bytes hold the device status word: zero them once when the workspace
  *       is allocated (moe_read_device_status clears the word after reading).
@@ -199,7 +200,11 @@ moe_status moe_layer_fwd(const moe_cfg *cfg, const moe_weights *w, const uint16_
  *   dWs: NULL, or the shared expert's [H*I | H*I | I*H] fp32 (gate, up, down);
  *   dgate: NULL, or [T,k] fp32 = d(sum out*dout)/d topk_w.
  *   saved: what moe_layer_fwd wrote for the same cfg, weights and x.
+ *   ws: at least moe_sizes.workspace_bwd bytes, 256-byte aligned.
  * The router bias is an input, not a parameter: it has no gradient.
+ * Each weight gradient sums expert e's rows minibatch by minibatch in token
+ * order, so results are bitwise reproducible for a given minibatch size.
+ * MOE_E_UNSUPPORTED in identity-expert mode.
  */
 moe_status moe_layer_bwd(const moe_cfg *cfg, const moe_weights *w, const uint16_t *x,
                          const uint16_t *dout, const void *saved, size_t saved_bytes,
@@ -237,7 +242,8 @@ typedef enum moe_kernel_kind {
     MOE_K_COMBINE = 4,
     MOE_K_GATHER = 5,
     MOE_K_OTHER = 6,
-    MOE_K_COUNT = 7
+    MOE_K_WGRAD = 7,        /* weight-gradient grouped GEMMs of the backward */
+    MOE_K_COUNT = 8
 } moe_kernel_kind;
 
 typedef struct moe_kernel_times {

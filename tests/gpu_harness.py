@@ -35,6 +35,33 @@ class Layer:
                           self.bufs.ws, saved=self.bufs.saved)
         return self.out
 
+    def backward(self, dout, with_dgate=True):
+        """Gradients of sum(out * dout); returns a dict of CPU float tensors."""
+        w = self.inp.w
+        dev = self.x.device
+        T, H, I, E, k = w.T, w.H, w.I, w.E, w.k
+        g = {
+            "dx": torch.empty(T, H, dtype=torch.bfloat16, device=dev),
+            "dWg": torch.empty(E, H, I, dtype=torch.float32, device=dev),
+            "dWu": torch.empty(E, H, I, dtype=torch.float32, device=dev),
+            "dWd": torch.empty(E, I, H, dtype=torch.float32, device=dev),
+            "dWr": torch.empty(H, E, dtype=torch.float32, device=dev),
+        }
+        dWs = torch.empty(2 * H * I + I * H, dtype=torch.float32, device=dev) if w.shared_expert else None
+        dgate = torch.empty(T, k, dtype=torch.float32, device=dev) if with_dgate else None
+        moe.moe_layer_bwd(self.cfg, self.Wr, self.bias, self.bufs.packed, self.x, dout.to(dev).contiguous(),
+                          self.bufs.saved, g["dx"], g["dWg"], g["dWu"], g["dWd"], g["dWr"], self.bufs.ws,
+                          dWs=dWs, dgate=dgate)
+        torch.cuda.synchronize()
+        res = {n: t.float().cpu() for n, t in g.items()}
+        if dgate is not None:
+            res["dgate"] = dgate.cpu()
+        if dWs is not None:
+            res["dWsg"] = dWs[:H * I].view(H, I).cpu()
+            res["dWsu"] = dWs[H * I:2 * H * I].view(H, I).cpu()
+            res["dWsd"] = dWs[2 * H * I:].view(I, H).cpu()
+        return res
+
     def saved_routing(self):
         T, k = self.cfg.T, self.cfg.k
         n = T * k * 4
