@@ -35,7 +35,7 @@ struct Plan {
     size_t sv_idx, sv_w, sv_mb0, sv_mb, sv_y, saved;
     // backward workspace (bytes)
     size_t wb_wrt, wb_mt, wb_lay0, lay_bytes, ly_hdr, ly_prow_token, ly_tok_prow, ly_prow_slot;
-    size_t wb_dyt, wb_xgt, wb_dgut, wb_ht, wb_dsel, wb_dy, wb_dgu, wb_dx, wb_dgp, ws_bwd;
+    size_t wb_dyt, wb_xgt, wb_dgut, wb_ht, wb_dsel, wb_dy, wb_dgu, wb_dh, wb_dx, wb_dgp, ws_bwd;
 };
 
 moe_status validate(const moe_cfg* c) {
@@ -135,6 +135,7 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     p->wb_dsel = o; o = align_up(o + nmb * rp * 4);
     p->wb_dy = o; o = align_up(o + rp * H * 2);
     p->wb_dgu = o; o = align_up(o + rp * 2 * I * 2);
+    p->wb_dh = o; o = align_up(o + rp * I * 2);
     p->wb_dx = o; o = align_up(o + rp * H * 2);
     p->wb_dgp = o; o = align_up(o + rp * (H / 64) * 4);
     p->ws_bwd = o;
@@ -324,7 +325,7 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             g1.C = hbuf; g1.ldc = p.I;
             g1.N = 2 * p.I; g1.K = p.H;
             g1.mt_start = mt; g1.hdr = hdr; g1.Et = p.Et;
-            g1.GU = gubuf; g1.CT = nullptr; g1.HT = nullptr; g1.ldct = 0;
+            g1.GU = gubuf;
             TIMED(MOE_K_GEMM_GATE_UP, s, launch_grouped_gemm(g1, kEpiSwiGLU, grid, s));
             GemmArgs g2;
             g2.A = hbuf; g2.a_row_map = nullptr; g2.lda = p.I;
@@ -332,7 +333,7 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             g2.C = ybuf; g2.ldc = p.H;
             g2.N = p.H; g2.K = p.I;
             g2.mt_start = mt; g2.hdr = hdr; g2.Et = p.Et;
-            g2.GU = nullptr; g2.CT = nullptr; g2.HT = nullptr; g2.ldct = 0;
+            g2.GU = nullptr;
             TIMED(MOE_K_GEMM_DOWN, s, launch_grouped_gemm(g2, kEpiStore, grid, s));
         }
         TIMED(MOE_K_COMBINE, s,
@@ -376,6 +377,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
     float* dsel_all = (float*)(wsb + p.wb_dsel);
     uint16_t* dY = (uint16_t*)(wsb + p.wb_dy);
     uint16_t* dGU = (uint16_t*)(wsb + p.wb_dgu);
+    uint16_t* dH = (uint16_t*)(wsb + p.wb_dh);
     uint16_t* dXb = (uint16_t*)(wsb + p.wb_dx);
     float* dgp = (float*)(wsb + p.wb_dgp);
     const int grid = kNumCUs;
@@ -411,19 +413,21 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
         rc.dsel = dsel; rc.H = H; rc.k = k; rc.nhb = H / 64; rc.ldt = rp;
         TIMED(MOE_K_GATHER, s, launch_rcomb_gather(rc, (int)rp, s));
 
-        GemmArgs g1;  // dH = dY Wd^T with the SwiGLU backward in the epilogue
+        GemmArgs g1;  // dH = dY Wd^T
         g1.A = dY; g1.a_row_map = nullptr; g1.lda = H;
         g1.B = Wdc; g1.b_stride = (int64_t)I * H;
-        g1.C = dGU; g1.ldc = 2 * I; g1.N = I; g1.K = H;
-        g1.mt_start = mt; g1.hdr = hdr; g1.Et = Et;
-        g1.GU = (uint16_t*)GUb; g1.CT = dGUT; g1.HT = HT; g1.ldct = rp;
-        TIMED(MOE_K_GEMM_DOWN, s, launch_grouped_gemm(g1, kEpiSwiGLUBwd, grid, s));
+        g1.C = dH; g1.ldc = I; g1.N = I; g1.K = H;
+        g1.mt_start = mt; g1.hdr = hdr; g1.Et = Et; g1.GU = nullptr;
+        TIMED(MOE_K_GEMM_DOWN, s, launch_grouped_gemm(g1, kEpiStore, grid, s));
+        SwigluBwdArgs sb;
+        sb.dH = dH; sb.GU = GUb; sb.hdr = hdr; sb.dGU = dGU; sb.dGUT = dGUT; sb.HT = HT; sb.I = I; sb.ldt = rp;
+        TIMED(MOE_K_GATHER, s, launch_swiglu_bwd(sb, (int)rp, s));
         GemmArgs g2;  // dX = dG Wg^T + dU Wu^T
         g2.A = dGU; g2.a_row_map = nullptr; g2.lda = 2 * I;
         g2.B = Wgu; g2.b_stride = (int64_t)H * 2 * I;
         g2.C = dXb; g2.ldc = H; g2.N = H; g2.K = 2 * I;
         g2.mt_start = mt; g2.hdr = hdr; g2.Et = Et;
-        g2.GU = nullptr; g2.CT = nullptr; g2.HT = nullptr; g2.ldct = 0;
+        g2.GU = nullptr;
         TIMED(MOE_K_GEMM_GATE_UP, s, launch_grouped_gemm(g2, kEpiStore, grid, s));
 
         RdispArgs rd;

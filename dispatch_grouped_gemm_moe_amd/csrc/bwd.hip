@@ -111,6 +111,77 @@ void launch_rcomb_gather(const RcombArgs& a, int rpad, hipStream_t stream) {
     hipLaunchKernelGGL(rcomb_gather_kernel, dim3(rpad / kTile, a.H / kTile), dim3(256), 0, stream, a);
 }
 
+__device__ __forceinline__ void unpack16_bf16(const intx4* src, float* f) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const intx4 a = src[q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f[8 * q + 2 * e] = __builtin_bit_cast(float, (uint32_t)a[e] << 16);
+            f[8 * q + 2 * e + 1] = __builtin_bit_cast(float, (uint32_t)a[e] & 0xffff0000u);
+        }
+    }
+}
+
+__device__ __forceinline__ void pack16_bf16(const uint16_t* v, intx4* dst) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        intx4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (int)((uint32_t)v[8 * q + 2 * e] | ((uint32_t)v[8 * q + 2 * e + 1] << 16));
+        dst[q] = o;
+    }
+}
+
+// SwiGLU backward, one workgroup per 64 padded rows x 64 intermediate columns:
+// row-major dG | dU for the input-gradient GEMM, transposed dG | dU and h for
+// the weight-gradient GEMMs (through LDS, so every store is coalesced).
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdArgs p) {
+    __shared__ uint16_t sG[kTile][kTile + 2];
+    __shared__ uint16_t sU[kTile][kTile + 2];
+    __shared__ uint16_t sH[kTile][kTile + 2];
+    const int prow0 = blockIdx.x * kTile, i0 = blockIdx.y * kTile;
+    if (prow0 >= p.hdr->m_tiles * BM) return;
+    const int tid = threadIdx.x;
+    const int r = tid >> 2, c0 = (tid & 3) * 16;
+    const int64_t prow = prow0 + r;
+    const int I = p.I;
+    float dh[16], g[16], u[16];
+    unpack16_bf16((const intx4*)(p.dH + prow * I + i0 + c0), dh);
+    unpack16_bf16((const intx4*)(p.GU + prow * 2 * I + i0 + c0), g);
+    unpack16_bf16((const intx4*)(p.GU + prow * 2 * I + I + i0 + c0), u);
+    uint16_t dg[16], du[16], hh[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        const float sg = 1.0f / (1.0f + __expf(-g[c]));
+        const float silu = g[c] * sg;
+        dg[c] = f32_to_bf16_rne(dh[c] * u[c] * (sg * (1.0f + g[c] * (1.0f - sg))));
+        du[c] = f32_to_bf16_rne(dh[c] * silu);
+        hh[c] = f32_to_bf16_rne(silu * u[c]);
+        sG[c0 + c][r] = dg[c];
+        sU[c0 + c][r] = du[c];
+        sH[c0 + c][r] = hh[c];
+    }
+    pack16_bf16(dg, (intx4*)(p.dGU + prow * 2 * I + i0 + c0));
+    pack16_bf16(du, (intx4*)(p.dGU + prow * 2 * I + I + i0 + c0));
+    __syncthreads();
+    const int ic = tid >> 2, r0 = (tid & 3) * 16;
+    uint16_t v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v[q] = sG[ic][r0 + q];
+    pack16_bf16(v, (intx4*)(p.dGUT + (int64_t)(i0 + ic) * p.ldt + prow0 + r0));
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v[q] = sU[ic][r0 + q];
+    pack16_bf16(v, (intx4*)(p.dGUT + (int64_t)(I + i0 + ic) * p.ldt + prow0 + r0));
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v[q] = sH[ic][r0 + q];
+    pack16_bf16(v, (intx4*)(p.HT + (int64_t)(i0 + ic) * p.ldt + prow0 + r0));
+}
+
+void launch_swiglu_bwd(const SwigluBwdArgs& a, int rpad, hipStream_t stream) {
+    hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(rpad / kTile, a.I / kTile), dim3(256), 0, stream, a);
+}
+
 // One workgroup per token of a minibatch: gate gradients, softmax backward and
 //   dx[t] = sum_j dX[prow_j] (+ dX[shared row]) + sum_j dsel_j * WrT[idx_j]
 constexpr int kRdThreads = 128;

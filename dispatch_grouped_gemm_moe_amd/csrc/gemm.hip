@@ -165,11 +165,6 @@ __device__ __forceinline__ int frag_col(int j) {
     return wn * 128 + j * 32 + (lane & 31);
 }
 
-__device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
-    return uint2{(uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16),
-                 (uint32_t)f32_to_bf16_rne(c) | ((uint32_t)f32_to_bf16_rne(d) << 16)};
-}
-
 template <int EPI>
 __global__ __attribute__((amdgpu_flat_work_group_size(kGemmThreads, kGemmThreads), amdgpu_waves_per_eu(1, 1)))
 void grouped_gemm_kernel(GemmArgs p) {
@@ -240,7 +235,7 @@ void grouped_gemm_kernel(GemmArgs p) {
                         }
                 }
             }
-        } else if (EPI == kEpiStore) {
+        } else {  // kEpiStore
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int col = n0 + frag_col(j);
@@ -250,39 +245,6 @@ void grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r)
                             p.C[(int64_t)(prow0 + frag_row(i, r)) * p.ldc + col] = f32_to_bf16_rne(acc[i][j][r]);
-                }
-            }
-        } else {  // kEpiSwiGLUBwd: acc = dH (N = I columns)
-            const int I = p.N;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int col = n0 + frag_col(j);
-                if (col < I) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            float dg[4], du[4], hh[4];
-                            const int row0 = prow0 + frag_row(i, 4 * q);
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                const int64_t row = row0 + r;
-                                const float g = bf16_to_f32(p.GU[row * 2 * I + col]);
-                                const float u = bf16_to_f32(p.GU[row * 2 * I + I + col]);
-                                const float sg = 1.0f / (1.0f + __expf(-g));
-                                const float silu = g * sg;
-                                const float dh = acc[i][j][4 * q + r];
-                                dg[r] = dh * u * (sg * (1.0f + g * (1.0f - sg)));
-                                du[r] = dh * silu;
-                                hh[r] = silu * u;
-                                p.C[row * 2 * I + col] = f32_to_bf16_rne(dg[r]);
-                                p.C[row * 2 * I + I + col] = f32_to_bf16_rne(du[r]);
-                            }
-                            // transposed copies for the weight-gradient GEMMs: 4 consecutive rows
-                            *(uint2*)(p.CT + (int64_t)col * p.ldct + row0) = pack4_bf16(dg[0], dg[1], dg[2], dg[3]);
-                            *(uint2*)(p.CT + (int64_t)(I + col) * p.ldct + row0) = pack4_bf16(du[0], du[1], du[2], du[3]);
-                            *(uint2*)(p.HT + (int64_t)col * p.ldct + row0) = pack4_bf16(hh[0], hh[1], hh[2], hh[3]);
-                        }
                 }
             }
         }
@@ -370,10 +332,8 @@ void launch_wgrad(const WgradArgs& a, int grid, hipStream_t stream) {
 void launch_grouped_gemm(const GemmArgs& a, GemmEpilogue epi, int grid, hipStream_t stream) {
     if (epi == kEpiSwiGLU)
         hipLaunchKernelGGL(grouped_gemm_kernel<kEpiSwiGLU>, dim3(grid), dim3(kGemmThreads), 0, stream, a);
-    else if (epi == kEpiStore)
-        hipLaunchKernelGGL(grouped_gemm_kernel<kEpiStore>, dim3(grid), dim3(kGemmThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL(grouped_gemm_kernel<kEpiSwiGLUBwd>, dim3(grid), dim3(kGemmThreads), 0, stream, a);
+        hipLaunchKernelGGL(grouped_gemm_kernel<kEpiStore>, dim3(grid), dim3(kGemmThreads), 0, stream, a);
 }
 
 // ---------------------------------------------------------------------------

@@ -43,15 +43,24 @@ struct GemmArgs {
     const LayoutHeader* hdr;
     int Et;
     // kEpiSwiGLU: optional [R_pad][2I] copy of g | u (kept for the backward).
-    // kEpiSwiGLUBwd: the saved g | u to read; C receives dG | dU [R_pad][2I].
     uint16_t* GU;
-    // kEpiSwiGLUBwd: transposed outputs [2I][ldct] (dG | dU) and [I][ldct] (h).
-    uint16_t* CT;
-    uint16_t* HT;
-    int64_t ldct;
 };
 
-enum GemmEpilogue { kEpiSwiGLU = 0, kEpiStore = 1, kEpiSwiGLUBwd = 2 };
+enum GemmEpilogue { kEpiSwiGLU = 0, kEpiStore = 1 };
+
+// Backward SwiGLU over the padded rows of one minibatch, from dH and the saved
+// g | u:  dG = dH * u * silu'(g), dU = dH * silu(g), h = silu(g) * u.
+struct SwigluBwdArgs {
+    const uint16_t* dH;        // [R_pad][I]
+    const uint16_t* GU;        // [R_pad][2I]
+    const LayoutHeader* hdr;
+    uint16_t* dGU;             // [R_pad][2I]  dG | dU
+    uint16_t* dGUT;            // [2I][ldt]    transposed dG | dU
+    uint16_t* HT;              // [I][ldt]     transposed h
+    int I;
+    int64_t ldt;
+};
+void launch_swiglu_bwd(const SwigluBwdArgs& a, int rpad, hipStream_t stream);
 
 // Weight-gradient GEMM: C[e][m][n] = sum over expert e's padded rows r of every
 // minibatch of A[m][r] * B[n][r]; A, B are row-major [M or N][ld] copies, one
