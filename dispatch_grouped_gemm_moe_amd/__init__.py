@@ -23,7 +23,8 @@ MOE_F_IDENTITY_EXPERTS = 1 << 1
 # every symbol include/moe.h declares
 EXPORTS = ("moe_status_string", "moe_abi_version", "moe_validate_cfg", "moe_query_sizes",
            "moe_prepare_weights", "moe_route", "moe_dispatch_layout", "moe_layer_fwd",
-           "moe_layer_bwd", "moe_read_device_status", "moe_timing_enable", "moe_timing_read")
+           "moe_layer_bwd", "moe_read_device_status", "moe_mx_quantize", "moe_timing_enable",
+           "moe_timing_read")
 KERNEL_KINDS = ("route", "layout", "gemm_gate_up", "gemm_down", "combine", "gather", "other", "wgrad")
 
 
@@ -81,6 +82,7 @@ def _load():
             "moe_layer_bwd": (ctypes.c_int, [cfgp, ctypes.POINTER(moe_weights), P, P, P, SZ, P, P, P,
                                              P, P, P, P, P, SZ, P]),
             "moe_read_device_status": (ctypes.c_int, [P, P, ctypes.POINTER(I32), ctypes.POINTER(I32)]),
+            "moe_mx_quantize": (ctypes.c_int, [P, ctypes.c_int64, I32, P, P, P]),
             "moe_timing_enable": (ctypes.c_int, [I32]),
             "moe_timing_read": (ctypes.c_int, [ctypes.POINTER(moe_kernel_times)]),
         }
@@ -175,6 +177,12 @@ def moe_read_device_status(ws, stream=None):
     code, detail = ctypes.c_int32(0), ctypes.c_int32(0)
     st = _load().moe_read_device_status(_ptr(ws), _stream(stream), ctypes.byref(code), ctypes.byref(detail))
     return st, code.value, detail.value
+
+
+def moe_mx_quantize(src, codes, scales, stream=None):
+    rows, cols = src.shape
+    _check("moe_mx_quantize", _load().moe_mx_quantize(_ptr(src), rows, cols, _ptr(codes), _ptr(scales),
+                                                      _stream(stream)))
 
 
 def moe_timing_enable(on: bool):

@@ -28,9 +28,13 @@ struct Plan {
     // packed weights (bytes): forward gate|up [Et][2I][H], down [Et][H][I];
     // backward down [Et][I][H] and gate|up rows [Et][H][2I]
     size_t pk_w1t, pk_w2t, pk_wd, pk_wgu, packed;
+    // MXFP8 copies of the routed experts' forward weights: codes and scales
+    size_t pk_w1q, pk_s1, pk_w2q, pk_s2;
+    bool mx;
     // forward workspace (bytes)
     size_t ws_status, ws_idx, ws_w, ws_slot0, slot_bytes, ws_fwd;
-    size_t sl_hdr, sl_mt, sl_prow_token, sl_tok_prow, sl_h, sl_y;
+    size_t sl_hdr, sl_mt, sl_prow_token, sl_tok_prow, sl_h, sl_y, sl_hq, sl_sh;
+    size_t ws_xq, ws_sx;  // MXFP8 codes and scales of x
     // saved (bytes): routing, then per minibatch g|u [rpad][2I] and Y [rpad][H]
     size_t sv_idx, sv_w, sv_mb0, sv_mb, sv_y, saved;
     // backward workspace (bytes)
@@ -75,7 +79,7 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     p->T = c->T; p->H = c->H; p->I = c->I; p->E = c->E; p->k = c->k; p->prec = c->prec;
     p->shared = (c->flags & MOE_F_SHARED_EXPERT) != 0;
     p->identity = (c->flags & MOE_F_IDENTITY_EXPERTS) != 0;
-    if (p->prec != MOE_PREC_BF16) return MOE_E_UNSUPPORTED;
+    p->mx = p->prec == MOE_PREC_MXFP8;
     p->Et = c->E + (p->shared ? 1 : 0);
     p->Mb = c->minibatch > 0 ? (c->minibatch < c->T ? c->minibatch : c->T) : auto_minibatch(c);
     p->nmb = ceil_div(c->T, p->Mb);
@@ -93,20 +97,37 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     p->pk_w2t = align_up(p->pk_w1t + Et * 2 * I * H * 2);
     p->pk_wd = align_up(p->pk_w2t + Et * H * I * 2);
     p->pk_wgu = align_up(p->pk_wd + Et * I * H * 2);
-    p->packed = align_up(p->pk_wgu + Et * H * 2 * I * 2);
+    size_t o = align_up(p->pk_wgu + Et * H * 2 * I * 2);
+    if (p->mx) {
+        const size_t E = c->E;
+        p->pk_w1q = o; o = align_up(o + E * 2 * I * H);
+        p->pk_s1 = o; o = align_up(o + E * (H / 64) * 2 * I * 4);
+        p->pk_w2q = o; o = align_up(o + E * H * I);
+        p->pk_s2 = o; o = align_up(o + E * (I / 64) * H * 4);
+    }
+    p->packed = o;
 
     const size_t Tk = (size_t)c->T * c->k;
     p->ws_status = 0;
     p->ws_idx = kAlign;
     p->ws_w = align_up(p->ws_idx + Tk * 4);
-    p->ws_slot0 = align_up(p->ws_w + Tk * 4);
-    size_t o = 0;
+    o = align_up(p->ws_w + Tk * 4);
+    if (p->mx) {
+        p->ws_xq = o; o = align_up(o + (size_t)c->T * H);
+        p->ws_sx = o; o = align_up(o + (size_t)(H / 64) * c->T * 4);
+    }
+    p->ws_slot0 = o;
+    o = 0;
     p->sl_hdr = o; o = align_up(o + sizeof(LayoutHeader));
     p->sl_mt = o; o = align_up(o + (Et + 1) * 4);
     p->sl_prow_token = o; o = align_up(o + (size_t)p->rpad * 4);
     p->sl_tok_prow = o; o = align_up(o + (size_t)p->Mb * p->ld_tok_prow * 4);
     p->sl_h = o; o = align_up(o + (size_t)p->rpad * I * 2);
     p->sl_y = o; o = align_up(o + (size_t)p->rpad * H * 2);
+    if (p->mx) {
+        p->sl_hq = o; o = align_up(o + (size_t)p->rpad * I);
+        p->sl_sh = o; o = align_up(o + (size_t)(I / 64) * p->rpad * 4);
+    }
     p->slot_bytes = o;
     p->ws_fwd = p->ws_slot0 + (size_t)p->slots * p->slot_bytes;
 
@@ -234,6 +255,14 @@ moe_status moe_prepare_weights(const moe_cfg* cfg, const uint16_t* Wg, const uin
     launch_transpose(Wd, p.E, p.I, p.H, W2t, s);
     launch_copy(Wd, (size_t)p.E * I * H * 2, Wdc, s);
     launch_concat_gu(Wg, Wu, p.E, p.H, p.I, Wgu, s);
+    if (p.mx) {  // E4M3 codes + E8M0 scales along each forward GEMM's K, expert by expert
+        for (int e = 0; e < p.E; ++e) {
+            launch_mx_quant(W1t + (size_t)e * 2 * I * H, 2 * p.I, p.H, 1, base + p.pk_w1q + (size_t)e * 2 * I * H,
+                            base + p.pk_s1 + (size_t)e * (H / 64) * 2 * I * 4, s);
+            launch_mx_quant(W2t + (size_t)e * H * I, p.H, p.I, 1, base + p.pk_w2q + (size_t)e * H * I,
+                            base + p.pk_s2 + (size_t)e * (I / 64) * H * 4, s);
+        }
+    }
     if (p.shared) {
         launch_pack_gate_up(Wsg, Wsu, 1, p.H, p.I, W1t + (size_t)p.E * 2 * I * H, s);
         launch_transpose(Wsd, 1, p.I, p.H, W2t + (size_t)p.E * H * I, s);
@@ -289,6 +318,10 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
 
     TIMED(MOE_K_ROUTE, s, launch_route(x, w->Wr, w->bias, p.T, p.H, p.E, p.k, idx, gw, nullptr, s));
     const int grid = kNumCUs;
+    uint8_t* xq = wsb + p.ws_xq;
+    uint8_t* sx = wsb + p.ws_sx;
+    if (p.mx && !p.identity)  // dispatch-side quantisation: every token row once, along H
+        TIMED(MOE_K_GATHER, s, launch_mx_quant(x, p.T, p.H, 1, xq, sx, s));
     for (int b = 0; b < p.nmb; ++b) {
         const int t0 = b * p.Mb;
         const int Tm = (p.T - t0) < p.Mb ? (p.T - t0) : p.Mb;
@@ -319,22 +352,43 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
         if (p.identity) {
             TIMED(MOE_K_GATHER, s, launch_gather_rows(x, p.H, prow_token, hdr, (int)p.rpad, ybuf, p.H, s));
         } else {
+            const int e_bf16 = p.mx ? p.E : 0;  // MXFP8 covers the routed experts; bf16 the rest
+            if (p.mx) {
+                MxGemmArgs m1;
+                m1.A = xq; m1.a_row_map = prow_token; m1.lda = p.H; m1.SA = sx; m1.sa_kstride = (int64_t)p.T * 4;
+                m1.B = pk + p.pk_w1q; m1.b_stride = (int64_t)2 * p.I * p.H;
+                m1.SB = pk + p.pk_s1; m1.sb_stride = (int64_t)(p.H / 64) * 2 * p.I * 4; m1.sb_kstride = (int64_t)2 * p.I * 4;
+                m1.N = 2 * p.I; m1.K = p.H; m1.mt_start = mt; m1.hdr = hdr; m1.e_begin = 0; m1.e_end = p.E;
+                m1.C = nullptr; m1.ldc = 0;
+                m1.Cq = slot + p.sl_hq; m1.Cs = slot + p.sl_sh; m1.cs_rows = p.rpad;
+                TIMED(MOE_K_GEMM_GATE_UP, s, launch_mx_gemm(m1, kEpiSwiGLU, grid, s));
+            }
             GemmArgs g1;
             g1.A = x; g1.a_row_map = prow_token; g1.lda = p.H;
             g1.B = W1t; g1.b_stride = (int64_t)2 * p.I * p.H;
             g1.C = hbuf; g1.ldc = p.I;
             g1.N = 2 * p.I; g1.K = p.H;
             g1.mt_start = mt; g1.hdr = hdr; g1.Et = p.Et;
-            g1.GU = gubuf;
-            TIMED(MOE_K_GEMM_GATE_UP, s, launch_grouped_gemm(g1, kEpiSwiGLU, grid, s));
+            g1.GU = gubuf; g1.e_begin = e_bf16; g1.e_end = p.Et;
+            if (e_bf16 < p.Et) TIMED(MOE_K_GEMM_GATE_UP, s, launch_grouped_gemm(g1, kEpiSwiGLU, grid, s));
+            if (p.mx) {
+                MxGemmArgs m2;
+                m2.A = slot + p.sl_hq; m2.a_row_map = nullptr; m2.lda = p.I;
+                m2.SA = slot + p.sl_sh; m2.sa_kstride = (int64_t)p.rpad * 4;
+                m2.B = pk + p.pk_w2q; m2.b_stride = (int64_t)p.H * p.I;
+                m2.SB = pk + p.pk_s2; m2.sb_stride = (int64_t)(p.I / 64) * p.H * 4; m2.sb_kstride = (int64_t)p.H * 4;
+                m2.N = p.H; m2.K = p.I; m2.mt_start = mt; m2.hdr = hdr; m2.e_begin = 0; m2.e_end = p.E;
+                m2.C = ybuf; m2.ldc = p.H; m2.Cq = nullptr; m2.Cs = nullptr; m2.cs_rows = 0;
+                TIMED(MOE_K_GEMM_DOWN, s, launch_mx_gemm(m2, kEpiStore, grid, s));
+            }
             GemmArgs g2;
             g2.A = hbuf; g2.a_row_map = nullptr; g2.lda = p.I;
             g2.B = W2t; g2.b_stride = (int64_t)p.H * p.I;
             g2.C = ybuf; g2.ldc = p.H;
             g2.N = p.H; g2.K = p.I;
             g2.mt_start = mt; g2.hdr = hdr; g2.Et = p.Et;
-            g2.GU = nullptr;
-            TIMED(MOE_K_GEMM_DOWN, s, launch_grouped_gemm(g2, kEpiStore, grid, s));
+            g2.GU = nullptr; g2.e_begin = e_bf16; g2.e_end = p.Et;
+            if (e_bf16 < p.Et) TIMED(MOE_K_GEMM_DOWN, s, launch_grouped_gemm(g2, kEpiStore, grid, s));
         }
         TIMED(MOE_K_COMBINE, s,
               launch_combine(ybuf, p.H, tok_prow, p.ld_tok_prow, gw + (size_t)t0 * p.k, p.k,
@@ -350,7 +404,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
     Plan p;
     moe_status st = make_plan(cfg, &p);
     if (st != MOE_OK) return st;
-    if (p.identity) return MOE_E_UNSUPPORTED;
+    if (p.identity || p.mx) return MOE_E_UNSUPPORTED;
     if (!w || !w->Wr || !w->packed || !x || !dout || !saved || !dx || !dWg || !dWu || !dWd || !dWr || !ws)
         return MOE_E_INVALID;
     if (p.shared && !dWs) return MOE_E_INVALID;
@@ -417,7 +471,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
         g1.A = dY; g1.a_row_map = nullptr; g1.lda = H;
         g1.B = Wdc; g1.b_stride = (int64_t)I * H;
         g1.C = dH; g1.ldc = I; g1.N = I; g1.K = H;
-        g1.mt_start = mt; g1.hdr = hdr; g1.Et = Et; g1.GU = nullptr;
+        g1.mt_start = mt; g1.hdr = hdr; g1.Et = Et; g1.GU = nullptr; g1.e_begin = 0; g1.e_end = Et;
         TIMED(MOE_K_GEMM_DOWN, s, launch_grouped_gemm(g1, kEpiStore, grid, s));
         SwigluBwdArgs sb;
         sb.dH = dH; sb.GU = GUb; sb.hdr = hdr; sb.dGU = dGU; sb.dGUT = dGUT; sb.HT = HT; sb.I = I; sb.ldt = rp;
@@ -427,7 +481,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
         g2.B = Wgu; g2.b_stride = (int64_t)H * 2 * I;
         g2.C = dXb; g2.ldc = H; g2.N = H; g2.K = 2 * I;
         g2.mt_start = mt; g2.hdr = hdr; g2.Et = Et;
-        g2.GU = nullptr;
+        g2.GU = nullptr; g2.e_begin = 0; g2.e_end = Et;
         TIMED(MOE_K_GEMM_GATE_UP, s, launch_grouped_gemm(g2, kEpiStore, grid, s));
 
         RdispArgs rd;
@@ -470,6 +524,14 @@ moe_status moe_read_device_status(void* ws, void* stream, int32_t* code, int32_t
         return MOE_E_DEVICE;
     }
     return MOE_OK;
+}
+
+moe_status moe_mx_quantize(const uint16_t* src, int64_t rows, int32_t cols, uint8_t* codes, uint8_t* scales,
+                           void* stream) {
+    if (!src || !codes || !scales || rows < 1 || cols < 32) return MOE_E_INVALID;
+    if (cols % 32 || !aligned(src, 16) || !aligned(codes, 16)) return MOE_E_INVALID;
+    launch_mx_quant(src, rows, cols, 0, codes, scales, (hipStream_t)stream);
+    return check_launch();
 }
 
 moe_status moe_timing_enable(int32_t on) {

@@ -171,7 +171,8 @@ void grouped_gemm_kernel(GemmArgs p) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int NT = ceil_div(p.N, BN);
-    const int total = p.hdr->m_tiles * NT;
+    const int mt_lo = p.mt_start[p.e_begin];
+    const int total = (p.mt_start[p.e_end] - mt_lo) * NT;
     const int G = gridDim.x, per = G >> 3;
     // Workgroups are dealt to the 8 XCDs round-robin; the 'per' workgroups of
     // one XCD take consecutive tiles so that they share weight and row tiles
@@ -183,14 +184,14 @@ void grouped_gemm_kernel(GemmArgs p) {
         const int v = it * G + xcd * per + local;
         if (v >= total) break;
         // tile order: expert-major, then N tile, then M tile (M fastest)
-        int lo = 0, hi = p.Et - 1;
+        int lo = p.e_begin, hi = p.e_end - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if (p.mt_start[mid] * NT <= v) lo = mid; else hi = mid - 1;
+            if ((p.mt_start[mid] - mt_lo) * NT <= v) lo = mid; else hi = mid - 1;
         }
         const int e = lo;
         const int mt0 = p.mt_start[e], mte = p.mt_start[e + 1] - mt0;
-        const int loc = v - mt0 * NT;
+        const int loc = v - (mt0 - mt_lo) * NT;
         const int ntile = loc / mte, ml = loc - ntile * mte;
         const int prow0 = (mt0 + ml) * BM;
         const int n0 = ntile * BN;

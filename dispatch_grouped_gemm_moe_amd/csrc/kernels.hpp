@@ -44,9 +44,40 @@ struct GemmArgs {
     int Et;
     // kEpiSwiGLU: optional [R_pad][2I] copy of g | u (kept for the backward).
     uint16_t* GU;
+    int e_begin, e_end;        // experts [e_begin, e_end) are processed
 };
 
 enum GemmEpilogue { kEpiSwiGLU = 0, kEpiStore = 1 };
+
+// MXFP8 grouped GEMM: E4M3 codes with E8M0 scales on both operands.
+// Codes: A rows [.][lda] bytes (gathered through a_row_map), B [Et][N][K] bytes.
+// Scales (one dword per row and 64-element K step, bytes 0 and 1 used):
+// SA + kt * sa_kstride + row * 4 and SB + e * sb_stride + kt * sb_kstride + n * 4.
+struct MxGemmArgs {
+    const uint8_t* A;
+    const int32_t* a_row_map;
+    int64_t lda;
+    const uint8_t* SA;
+    int64_t sa_kstride;
+    const uint8_t* B;
+    int64_t b_stride;
+    const uint8_t* SB;
+    int64_t sb_stride, sb_kstride;
+    int N, K;
+    const int32_t* mt_start;
+    const LayoutHeader* hdr;
+    int e_begin, e_end;
+    uint16_t* C;               // kEpiStore: bf16 [R_pad][ldc]
+    int64_t ldc;
+    uint8_t* Cq;               // kEpiSwiGLU: h codes [R_pad][N/2]
+    uint8_t* Cs;               // kEpiSwiGLU: h scales [N/2/64][cs_rows][4]
+    int64_t cs_rows;
+};
+void launch_mx_gemm(const MxGemmArgs& a, GemmEpilogue epi, int grid, hipStream_t stream);
+// bf16 [rows][cols] -> E4M3 codes [rows][cols] and E8M0 scales; layout 0:
+// [rows][cols/32], layout 1: [cols/64][rows][4] (bytes 0, 1 = blocks 2j, 2j+1).
+void launch_mx_quant(const uint16_t* src, int64_t rows, int cols, int layout, uint8_t* codes, uint8_t* scales,
+                     hipStream_t stream);
 
 // Backward SwiGLU over the padded rows of one minibatch, from dH and the saved
 // g | u:  dG = dH * u * silu'(g), dU = dH * silu(g), h = silu(g) * u.

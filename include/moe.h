@@ -204,7 +204,8 @@ moe_status moe_layer_fwd(const moe_cfg *cfg, const moe_weights *w, const uint16_
  * The router bias is an input, not a parameter: it has no gradient.
  * Each weight gradient sums expert e's rows minibatch by minibatch in token
  * order, so results are bitwise reproducible for a given minibatch size.
- * MOE_E_UNSUPPORTED in identity-expert mode.
+ * MOE_E_UNSUPPORTED in identity-expert mode and for MOE_PREC_MXFP8 (the
+ * MXFP8 layer is forward-only in this version).
  */
 moe_status moe_layer_bwd(const moe_cfg *cfg, const moe_weights *w, const uint16_t *x,
                          const uint16_t *dout, const void *saved, size_t saved_bytes,
@@ -224,6 +225,19 @@ typedef enum moe_device_error {
 } moe_device_error;
 
 moe_status moe_read_device_status(void *ws, void *stream, int32_t *code, int32_t *detail);
+
+/*
+ * The MXFP8 quantiser the layer applies to activations and weights ([KC] 02:
+ * MXFP8 inside the dispatch / grouped GEMM / SwiGLU path), exposed on its own:
+ * OCP Microscaling v1.0 E4M3 codes with one E8M0 scale per 32 consecutive
+ * elements of a row.  The scale is 2^e for the smallest e with
+ * amax <= 448 * 2^e (clamped to [-127, 127]; an all-zero block gets e = 0);
+ * codes are x / 2^e rounded to nearest even, saturating at +-448.
+ *   src [rows, cols] bf16 (16-byte aligned), cols a multiple of 32;
+ *   codes [rows, cols] uint8 (16-byte aligned); scales [rows, cols/32] uint8 = e + 127.
+ */
+moe_status moe_mx_quantize(const uint16_t *src, int64_t rows, int32_t cols, uint8_t *codes,
+                           uint8_t *scales, void *stream);
 
 /*
  * Kernel timing (diagnostics, for benchmarks).  While enabled, every kernel

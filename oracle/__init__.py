@@ -45,7 +45,7 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "router_logits.c")
+_SRCS = [os.path.join(_HERE, "router_logits.c"), os.path.join(_HERE, "mx_quant.c")]
 _BUILD = os.path.join(_HERE, "_build")
 _SO = os.path.join(_BUILD, "liboracle_router.so")
 _lib_handle = None
@@ -60,7 +60,7 @@ def build() -> str:
     os.makedirs(_BUILD, exist_ok=True)
     tmp = _SO + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
-           "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"]
+           "-shared", "-fPIC", *_SRCS, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _SO)
     return _SO
@@ -69,13 +69,16 @@ def build() -> str:
 def _lib():
     global _lib_handle
     if _lib_handle is None:
-        if not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+        if not os.path.exists(_SO) or os.path.getmtime(_SO) < max(os.path.getmtime(f) for f in _SRCS):
             build()
         lib = ctypes.CDLL(_SO)
         fp = ctypes.POINTER(ctypes.c_float)
         lib.oracle_router_logits.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                              fp, fp, fp, fp]
         lib.oracle_router_logits.restype = ctypes.c_int
+        u8 = ctypes.POINTER(ctypes.c_uint8)
+        lib.oracle_mx_quantize.argtypes = [ctypes.c_int64, ctypes.c_int, fp, u8, u8]
+        lib.oracle_mx_quantize.restype = None
         _lib_handle = lib
     return _lib_handle
 
@@ -239,11 +242,31 @@ def e8m0_scale_exponent(amax: np.ndarray) -> np.ndarray:
 
 def mx_quantize(a, axis: int):
     """Quantise along `axis` in blocks of 32: (codes uint8 same shape, scale bytes
-    uint8 with that axis divided by 32).  The input is taken in fp32."""
+    uint8 with that axis divided by 32).  The input is taken in fp32; the work
+    is done by oracle_mx_quantize (mx_quant.c), the same rules as e4m3_encode
+    and e8m0_scale_exponent above."""
+    a32 = np.moveaxis(as_f32(a), axis, -1)
+    shape = a32.shape
+    n = shape[-1]
+    assert n % MX_BLOCK == 0
+    flat = np.ascontiguousarray(a32.reshape(-1, n))
+    assert np.isfinite(flat).all()
+    codes = np.empty(flat.shape, dtype=np.uint8)
+    scales = np.empty((flat.shape[0], n // MX_BLOCK), dtype=np.uint8)
+    u8 = ctypes.POINTER(ctypes.c_uint8)
+    _lib().oracle_mx_quantize(flat.shape[0], n, flat.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                              codes.ctypes.data_as(u8), scales.ctypes.data_as(u8))
+    codes = np.moveaxis(codes.reshape(shape), -1, axis)
+    scales = np.moveaxis(scales.reshape(shape[:-1] + (n // MX_BLOCK,)), -1, axis)
+    return np.ascontiguousarray(codes), np.ascontiguousarray(scales)
+
+
+def mx_quantize_reference(a, axis: int):
+    """The same quantisation written with the Python helpers (slow; used to
+    check the C quantiser)."""
     a32 = as_f32(a).astype(np.float64)
     a32 = np.moveaxis(a32, axis, -1)
     n = a32.shape[-1]
-    assert n % MX_BLOCK == 0
     blk = a32.reshape(a32.shape[:-1] + (n // MX_BLOCK, MX_BLOCK))
     e = e8m0_scale_exponent(np.abs(blk).max(axis=-1))
     codes = e4m3_encode(blk / np.ldexp(1.0, e)[..., None])

@@ -309,6 +309,22 @@ def test_mx_quantise_hand_blocks():
     np.testing.assert_array_equal(O.mx_dequantize(codes, scales, 1)[2, :2], [896.0, 3.0])
 
 
+def test_mx_quantiser_c_equals_python_helpers():
+    rng = np.random.default_rng(12)
+    a = np.concatenate([rng.normal(0, 1, (40, 96)), rng.normal(0, 1e-3, (8, 96)) * 10.0 ** rng.integers(-30, 30, (8, 1)),
+                        np.zeros((2, 96))]).astype(np.float32)
+    a[3, 5] = -0.0
+    a[7, :32] = np.float32(448.0 * 2.0 ** -3)  # exactly at a scale boundary
+    c1, s1 = O.mx_quantize(a, 1)
+    c2, s2 = O.mx_quantize_reference(a, 1)
+    np.testing.assert_array_equal(c1, c2)
+    np.testing.assert_array_equal(s1, s2)
+    c1, s1 = O.mx_quantize(a[:32], 0)
+    c2, s2 = O.mx_quantize_reference(a[:32], 0)
+    np.testing.assert_array_equal(c1, c2)
+    np.testing.assert_array_equal(s1, s2)
+
+
 def test_mx_quantise_axis_and_error_bound():
     rng = np.random.default_rng(10)
     a = rng.normal(size=(64, 96)).astype(np.float32)
