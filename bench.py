@@ -24,6 +24,7 @@ import sys
 import time
 
 PEAK_BF16_TFLOPS = 2516.6  # 256 CUs x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+PEAK_FP8_TFLOPS = 5033.2   # dense MXFP8 / FP8
 PEAK_HBM_GBS = 8000.0
 
 
@@ -41,7 +42,22 @@ def main():
     ap.add_argument("--minibatch", type=int, default=None)
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run one plain elementwise copy (negation) of this many MiB, "
+                         "the yardstick for HBM byte counters")
+    ap.add_argument("--summarize-stats", nargs=3, metavar=("KERNEL_STATS_CSV", "TITLE", "COMMAND"),
+                    help="print a rocprofv3 --stats kernel summary as markdown and exit")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="fold two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this workload, "
+                         "taken with --calibrate-copy-mib, into profiles/traffic.json and exit")
     args = ap.parse_args()
+    if args.summarize_stats:
+        summarize_stats(*args.summarize_stats)
+        return
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1], args.workload,
+                          args.calibrate_copy_mib)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this layer build has no multi-GPU path "
               "(expert parallelism across GPUs is out of scope); run with --gpus 1", file=sys.stderr)
@@ -55,14 +71,27 @@ def main():
     if args.minibatch is not None:
         w = w.replace(minibatch=args.minibatch)
     log("workload", w)
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 19  # bf16 elements
+        a = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        del a, b
     t_gen = time.time()
     from moe_inputs import make_inputs
+    mx = w.prec == "mxfp8"
     bwd = args.passes == "fwdbwd"
+    if mx and bwd:
+        log("the MXFP8 layer is forward-only in this version: measuring the forward")
+        bwd = False
     inp = make_inputs(w, with_dout=bwd)
     log("inputs drawn in %.1f s" % (time.time() - t_gen))
 
     flags = moe.MOE_F_SHARED_EXPERT if w.shared_expert else 0
-    cfg = moe.make_cfg(w.T, w.H, w.I, w.E, w.k, minibatch=w.minibatch, flags=flags)
+    cfg = moe.make_cfg(w.T, w.H, w.I, w.E, w.k, minibatch=w.minibatch, flags=flags,
+                       prec=moe.MOE_PREC_MXFP8 if mx else moe.MOE_PREC_BF16)
     sizes = moe.moe_query_sizes(cfg)
     bufs = moe.alloc_buffers(cfg, with_saved=bwd)
     dev = lambda t: None if t is None else t.to("cuda").contiguous()
@@ -104,21 +133,33 @@ def main():
     T, H, I, E, k = w.T, w.H, w.I, w.E, w.k
     rows = T * k + (T if w.shared_expert else 0)  # routed (+ shared) rows per step
     hi = float(H) * I * rows  # padding rows excluded from every figure below
-    # algorithmic flops per step of each grouped-GEMM kind (forward, plus the
-    # backward's input-gradient GEMMs of the same shape and the weight gradients)
-    flops = {"gemm_gate_up": 4 * hi * (2 if bwd else 1), "gemm_down": 2 * hi * (2 if bwd else 1),
-             "wgrad": 6 * hi if bwd else 0.0}
+    # algorithmic flops per step of each grouped-GEMM role, and the kernel
+    # symbol that runs it (rocprofv3 reports per symbol)
+    flops = {"gemm_gate_up": 4 * hi, "gemm_down": 2 * hi}
+    if bwd:
+        flops.update({"dgrad_down": 2 * hi, "dgrad_gate_up": 4 * hi, "wgrad": 6 * hi})
+    symbol = {"gemm_gate_up": "mx_gemm_kernel<0>" if mx else "grouped_gemm_kernel<0>",
+              "gemm_down": "mx_gemm_kernel<1>" if mx else "grouped_gemm_kernel<1>",
+              "dgrad_down": "grouped_gemm_kernel<1>", "dgrad_gate_up": "grouped_gemm_kernel<1>",
+              "wgrad": "wgrad_kernel"}
+    by_sym = {}
+    for kd, fl in flops.items():
+        n, ms = kt[kd]
+        agg = by_sym.setdefault(symbol[kd], [0.0, 0.0, 0, []])
+        agg[0] += fl * args.steps
+        agg[1] += ms
+        agg[2] += n
+        agg[3].append(kd)
     ms_step = elapsed * 1e3 / args.steps
     value = T * args.steps / elapsed
-    dom = max((kind for kind in flops if flops[kind] > 0), key=lambda kd: kt[kd][1])
-    n_dom, ms_dom = kt[dom]
-    achieved = flops[dom] * args.steps / (ms_dom / 1e3) / 1e12
-    kernel_names = {"gemm_gate_up": "grouped_gemm_kernel<0> gate|up SwiGLU (+ grouped_gemm_kernel<1> gate|up input gradient)",
-                    "gemm_down": "grouped_gemm_kernel<1> down (+ grouped_gemm_kernel<2> down input gradient, SwiGLU backward)",
-                    "wgrad": "wgrad_kernel (weight gradients)"}
+    dom = max(by_sym, key=lambda sy: by_sym[sy][1])
+    dom_flops, ms_dom, n_dom, dom_roles = by_sym[dom]
+    achieved = dom_flops / (ms_dom / 1e3) / 1e12
+    peak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
     total_flops = sum(flops.values())
     res = {
-        "metric": "MoE layer %s tokens/s at H=7168 I=2048 (bf16) + %% MFMA peak" % ("fwd+bwd" if bwd else "fwd"),
+        "metric": "MoE layer %s tokens/s at H=7168 I=2048 (%s) + %% MFMA peak" % ("fwd+bwd" if bwd else "fwd",
+                                                                                "MXFP8" if mx else "bf16"),
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -128,20 +169,20 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "mxfp8-e4m3" if mx else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": T, "hidden": H, "intermediate": I, "experts": E,
                    "top_k": k, "minibatch": sizes.minibatch, "minibatches": sizes.num_minibatches,
                    "router_bias": w.router_bias, "shared_expert": w.shared_expert,
                    "pass": "forward+backward" if bwd else "forward"},
-        "roofline": {"bound": "mfma", "kernel": kernel_names[dom], "kind": dom,
-                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+        "roofline": {"bound": "mfma", "kernel": "moe::" + dom, "roles": dom_roles,
+                     "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": traffic_for(dom, w.name, mx),
                      "avg_launch_ms": ms_dom / max(n_dom, 1), "launches": n_dom},
         "detail": {
-            "layer_mfma_frac": total_flops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
-            "tflops_by_kind": {kd: flops[kd] * args.steps / (kt[kd][1] / 1e3) / 1e12
-                               for kd in flops if flops[kd] > 0 and kt[kd][1] > 0},
+            "layer_mfma_frac": total_flops / (ms_step / 1e3) / 1e12 / peak,
+            "tflops_by_role": {kd: flops[kd] * args.steps / (kt[kd][1] / 1e3) / 1e12
+                               for kd in flops if kt[kd][1] > 0},
             "per_step_ms": {kind: v[1] / args.steps for kind, v in kt.items() if kind != "dropped"},
             "timing_dropped": kt["dropped"],
         },
@@ -151,6 +192,93 @@ def main():
         n = args.cpu_sample or (256 if bwd else 2048)
         res["cpu_baseline"] = cpu_baseline(inp, n, bwd)
     print(json.dumps(res), flush=True)
+
+
+def traffic_for(symbol: str, workload: str, mx: bool):
+    """HBM bytes per launch of `symbol` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or
+    None when there is none for this workload or the kernel source changed
+    since the counters were taken."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    ent = rec.get("kernels", {}).get("%s@%s" % (symbol, workload))
+    if not ent or ent.get("source_sha256") != _source_sha(mx):
+        return None
+    return ent["hbm_bytes_per_launch"]
+
+
+def _kernel_symbol(name: str) -> str:
+    return name.split("(")[0].replace("void ", "").strip()
+
+
+def _source_sha(mx: bool) -> str:
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for f in ("mx.hip" if mx else "gemm.hip", "common.hpp"):
+        h.update(open(os.path.join(here, "dispatch_grouped_gemm_moe_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def summarize_stats(path: str, title: str, cmd: str):
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    print("# %s\n" % title)
+    print("Command (run from the repository root on one MI355X):\n\n```\n%s\n```\n" % cmd)
+    print("| kernel | calls | total ms | avg us | min us | max us | % |")
+    print("|---|---|---|---|---|---|---|")
+    for r in rows:
+        print("| %s | %s | %.3f | %.1f | %.1f | %.1f | %.2f |" % (
+            _kernel_symbol(r["Name"])[:90], r["Calls"], int(r["TotalDurationNs"]) / 1e6,
+            float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+            float(r["Percentage"])))
+
+
+def summarize_traffic(fetch_csv: str, write_csv: str, workload: str, copy_mib: int):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of each moe:: kernel, scaled so
+    that the plain copy of copy_mib MiB reads and writes exactly that much."""
+    import csv
+    from collections import defaultdict
+    if not copy_mib:
+        sys.exit("--summarize-traffic needs the --calibrate-copy-mib the runs were taken with")
+
+    def per_symbol(path, counter):
+        acc = defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                acc[_kernel_symbol(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+        return acc
+
+    fetch, write = per_symbol(fetch_csv, "FETCH_SIZE"), per_symbol(write_csv, "WRITE_SIZE")
+    copy = [s for s in fetch if "neg_kernel" in s]
+    if len(copy) != 1 or len(fetch[copy[0]]) != 1:
+        sys.exit("expected exactly one copy (negation) dispatch in %s" % fetch_csv)
+    kib = copy_mib * 1024.0
+    f_fac, w_fac = kib / fetch[copy[0]][0], kib / write[copy[0]][0]
+    here = os.path.dirname(os.path.abspath(__file__))
+    out = os.path.join(here, "profiles", "traffic.json")
+    rec = json.load(open(out)) if os.path.exists(out) else {"kernels": {}}
+    rec["note"] = ("HBM bytes per launch = mean FETCH_SIZE * fetch_factor + mean WRITE_SIZE * write_factor "
+                   "(KiB -> bytes); the factors make a plain %d MiB elementwise copy read and write "
+                   "exactly %d MiB" % (copy_mib, copy_mib))
+    for sym in fetch:
+        if not sym.startswith("moe::") or sym not in write:
+            continue
+        mx = "mx_" in sym
+        fk = sum(fetch[sym]) / len(fetch[sym])
+        wk = sum(write[sym]) / len(write[sym])
+        rec["kernels"]["%s@%s" % (sym, workload)] = {
+            "dispatches": len(fetch[sym]), "fetch_kib": fk, "write_kib": wk,
+            "fetch_factor": f_fac, "write_factor": w_fac,
+            "hbm_bytes_per_launch": (fk * f_fac + wk * w_fac) * 1024.0,
+            "source_sha256": _source_sha(mx)}
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    print(json.dumps({k: v["hbm_bytes_per_launch"] for k, v in rec["kernels"].items()}, indent=1))
 
 
 def cpu_baseline(inp, n_tokens: int, bwd: bool) -> dict:

@@ -472,7 +472,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
         g1.B = Wdc; g1.b_stride = (int64_t)I * H;
         g1.C = dH; g1.ldc = I; g1.N = I; g1.K = H;
         g1.mt_start = mt; g1.hdr = hdr; g1.Et = Et; g1.GU = nullptr; g1.e_begin = 0; g1.e_end = Et;
-        TIMED(MOE_K_GEMM_DOWN, s, launch_grouped_gemm(g1, kEpiStore, grid, s));
+        TIMED(MOE_K_DGRAD_DOWN, s, launch_grouped_gemm(g1, kEpiStore, grid, s));
         SwigluBwdArgs sb;
         sb.dH = dH; sb.GU = GUb; sb.hdr = hdr; sb.dGU = dGU; sb.dGUT = dGUT; sb.HT = HT; sb.I = I; sb.ldt = rp;
         TIMED(MOE_K_GATHER, s, launch_swiglu_bwd(sb, (int)rp, s));
@@ -482,7 +482,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
         g2.C = dXb; g2.ldc = H; g2.N = H; g2.K = 2 * I;
         g2.mt_start = mt; g2.hdr = hdr; g2.Et = Et;
         g2.GU = nullptr; g2.e_begin = 0; g2.e_end = Et;
-        TIMED(MOE_K_GEMM_GATE_UP, s, launch_grouped_gemm(g2, kEpiStore, grid, s));
+        TIMED(MOE_K_DGRAD_GATE_UP, s, launch_grouped_gemm(g2, kEpiStore, grid, s));
 
         RdispArgs rd;
         rd.dX = dXb; rd.dgp = dgp; rd.tok_prow = tok_prow; rd.topk_idx = idx; rd.topk_w = gw; rd.WrT = WrT;

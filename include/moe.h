@@ -251,13 +251,15 @@ moe_status moe_mx_quantize(const uint16_t *src, int64_t rows, int32_t cols, uint
 typedef enum moe_kernel_kind {
     MOE_K_ROUTE = 0,
     MOE_K_LAYOUT = 1,
-    MOE_K_GEMM_GATE_UP = 2, /* grouped GEMM of gate|up with the SwiGLU epilogue */
-    MOE_K_GEMM_DOWN = 3,    /* grouped GEMM of the down projection */
-    MOE_K_COMBINE = 4,
-    MOE_K_GATHER = 5,
+    MOE_K_GEMM_GATE_UP = 2, /* forward grouped GEMM of gate|up with the SwiGLU epilogue */
+    MOE_K_GEMM_DOWN = 3,    /* forward grouped GEMM of the down projection */
+    MOE_K_COMBINE = 4,      /* combine, and the backward's reverse-dispatch */
+    MOE_K_GATHER = 5,       /* elementwise passes: MXFP8 dispatch quantisation, reverse-combine, SwiGLU backward */
     MOE_K_OTHER = 6,
     MOE_K_WGRAD = 7,        /* weight-gradient grouped GEMMs of the backward */
-    MOE_K_COUNT = 8
+    MOE_K_DGRAD_DOWN = 8,   /* backward: dH = dY Wd^T */
+    MOE_K_DGRAD_GATE_UP = 9, /* backward: dX = dG Wg^T + dU Wu^T */
+    MOE_K_COUNT = 10
 } moe_kernel_kind;
 
 typedef struct moe_kernel_times {
