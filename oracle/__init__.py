@@ -332,6 +332,15 @@ class Weights:
             Wg, Wu, Wd = mx_roundtrip(Wg, 0), mx_roundtrip(Wu, 0), mx_roundtrip(Wd, 0)
         return Wg, Wu, Wd
 
+    def expert_dgrad(self, e: int, quantizer=None):
+        """Operands of the backward input-gradient GEMMs: Wg, Wu [H,I] and Wd [I,H]
+        taken through `quantizer` along their contraction axis there (I for Wg and
+        Wu, H for Wd: axis 1 each), or unquantised."""
+        Wg, Wu, Wd = (as_f64(t[e]) for t in (self.inp.Wg, self.inp.Wu, self.inp.Wd))
+        if quantizer is not None:
+            Wg, Wu, Wd = quantizer(Wg, 1), quantizer(Wu, 1), quantizer(Wd, 1)
+        return Wg, Wu, Wd
+
     def shared(self):
         return tuple(as_f64(t) for t in (self.inp.Wsg, self.inp.Wsu, self.inp.Wsd))
 
@@ -397,17 +406,33 @@ def layer_forward(inp, tokens=None, *, identity_experts: bool = False, mx: bool 
 # backward (section 01: the backward pass runs the exchanges in reverse)
 # --------------------------------------------------------------------------
 
-def layer_backward(inp, dout=None, fwd=None):
-    """Gradients of sum(out * dout) for the bf16 layer (fp64, routing frozen at
-    the forward's selection).
+def mx_point(a, axis: int) -> np.ndarray:
+    """A quantisation point of the MXFP8 layer: the value is rounded to fp32 (the
+    precision it is produced in) and taken through the MXFP8 quantiser."""
+    return mx_roundtrip(np.asarray(a, dtype=np.float64).astype(np.float32), axis)
+
+
+def layer_backward(inp, dout=None, fwd=None, *, mx: bool | None = None, quantizer=None):
+    """Gradients of sum(out * dout) for the layer (fp64, routing frozen at the
+    forward's selection).
 
     Returns dict: dx [T,H], dWg/dWu [E,H,I], dWd [E,I,H], dWr [H,E], dgate [T,k]
     (d/dw of the slot weights), and dWsg/dWsu/dWsd with a shared expert.
     The router bias is an input, not a parameter: it gets no gradient.
+
+    MXFP8 (`mx`, default from the workload): the routed experts' two
+    input-gradient GEMMs take MXFP8 operands, quantised along their contraction
+    axis -- dY and Wd along H for dH = dY Wd^T, dG | dU and Wg | Wu along I for
+    dX = dG Wg^T + dU Wu^T -- and the weight-gradient GEMMs take the unquantised
+    operands (x rows, h = silu(g) u, dY, dG, dU).  The shared expert is bf16
+    throughout.  `fwd` must then be the MXFP8 forward (its g, u, Y include the
+    forward's quantisation).  `quantizer(a, axis)` replaces `mx_point`.
     """
     w_ = inp.w
+    mx = (w_.prec == "mxfp8") if mx is None else mx
     if fwd is None:
-        fwd = layer_forward(inp, keep=True, mx=False)
+        fwd = layer_forward(inp, keep=True, mx=mx)
+    q = (quantizer or mx_point) if mx else None
     dout = as_f64(inp.dout if dout is None else dout)
     x64, idx, gw, Y = fwd["x"], fwd["idx"], fwd["w"], fwd["Y"]
     T, H = x64.shape
@@ -419,16 +444,19 @@ def layer_backward(inp, dout=None, fwd=None):
     dWg = np.zeros((E, H, I)); dWu = np.zeros((E, H, I)); dWd = np.zeros((E, I, H))
     W = Weights(inp, mx=False)
     for e, (t_sel, j_sel, g, u, h) in fwd["saved"].items():
-        Wg, Wu, Wd = W.expert(e)
+        Wg, Wu, Wd = W.expert_dgrad(e, q)
         dy = gw[t_sel, j_sel][:, None] * dout[t_sel]
         X = x64[t_sel]
         dWd[e] = h.T @ dy
-        dh = dy @ Wd.T
+        dh = (q(dy, 1) if q else dy) @ Wd.T
         du = dh * silu(g)
         dg = dh * u * silu_grad(g)
         dWg[e] = X.T @ dg
         dWu[e] = X.T @ du
-        dxe = dg @ Wg.T + du @ Wu.T
+        if q:
+            dxe = q(dg, 1) @ Wg.T + q(du, 1) @ Wu.T
+        else:
+            dxe = dg @ Wg.T + du @ Wu.T
         np.add.at(dx, t_sel, dxe)
     # router: gate weights are the softmax of the selected logits
     dsel = gw * (dgate - (gw * dgate).sum(axis=1, keepdims=True))

@@ -420,3 +420,154 @@ def test_backward_scales_exactly_with_dout():
     g2 = O.layer_backward(inp, dout=2 * inp.dout, fwd=fwd)
     for n in ("dx", "dWg", "dWu", "dWd", "dWr", "dgate"):
         np.testing.assert_array_equal(g2[n], 2 * g1[n])
+
+
+# ---------------------------------------------------------------- MXFP8 backward
+
+def _e4m3_positive_values():
+    """The 127 finite non-negative E4M3 (OCP, bias 7) values by code, from the
+    format definition: exponent field 0 is subnormal (m/8 * 2^-6)."""
+    vals = []
+    for c in range(127):
+        ex, m = c >> 3, c & 7
+        vals.append(m / 8 * 2.0 ** -6 if ex == 0 else (1 + m / 8) * 2.0 ** (ex - 7))
+    return vals
+
+
+_E4M3_POS = _e4m3_positive_values()
+
+
+def _brute_quant_block(vals):
+    """Dequantised MXFP8 of one 32-element block by enumeration: the smallest
+    scale 2^e (e in [-127, 127]) with amax <= 448 * 2^e (e = 0 for an all-zero
+    block), each element / 2^e to the nearest E4M3 value, ties to the even code."""
+    vals = [float(np.float32(v)) for v in vals]
+    amax = max(abs(v) for v in vals)
+    e = 0
+    if amax > 0:
+        e = -127
+        while e < 127 and amax > 448.0 * 2.0 ** e:
+            e += 1
+    out = []
+    for v in vals:
+        t = abs(v) / 2.0 ** e
+        best = None
+        for c, cv in enumerate(_E4M3_POS):
+            d = abs(cv - t)
+            if best is None or d < best[0] or (d == best[0] and c % 2 == 0 and best[1] % 2 == 1):
+                best = (d, c)
+        out.append(math.copysign(_E4M3_POS[best[1]] * 2.0 ** e, v))
+    return out
+
+
+def _brute_quant_rows(M):
+    """Quantise every row of the nested list M in 32-element blocks along the row."""
+    return [sum((_brute_quant_block(r[b:b + 32]) for b in range(0, len(r), 32)), []) for r in M]
+
+
+def _T(M):
+    return [list(c) for c in zip(*M)]
+
+
+def _wide_range(inp):
+    """Scale every row and every column of x, dout and the expert weights by its
+    own power of two (exact in bf16), spanning 2^-6 .. 2^6.  A 32-element block
+    then mixes magnitudes along one axis and not along the other, so quantising
+    along the wrong axis changes the result (with N(0, s) entries nearly every
+    block of either axis gets the same scale, which hides the axis)."""
+    g = torch.Generator().manual_seed(77)
+
+    def scale(t, *axes):
+        f = torch.ones(t.shape, dtype=torch.float64)
+        for ax in axes:
+            shp = [1] * t.dim()
+            shp[ax] = t.shape[ax]
+            f = f * torch.pow(2.0, torch.randint(-3, 4, shp, generator=g).double())
+        return (t.double() * f).to(t.dtype)
+
+    return LayerInputs(inp.w, scale(inp.x, 0, 1), inp.Wr, inp.bias, scale(inp.Wg, 1, 2), scale(inp.Wu, 1, 2),
+                       scale(inp.Wd, 1, 2), inp.Wsg, inp.Wsu, inp.Wsd, scale(inp.dout, 0, 1))
+
+
+def test_mx_backward_matches_scalar_brute_force():
+    """Every MXFP8 quantisation point of the layer, and every contraction, by
+    scalar loops on a tiny layer: the forward (x along H; Wg, Wu along H; h
+    along I; Wd along I), the input-gradient GEMMs (dY and Wd along H; dG, dU
+    and Wg, Wu along I) and the unquantised weight gradients."""
+    w = tiny(T=5, H=64, I=64, E=3, k=2, router_bias="normal", prec="mxfp8")
+    inp = _wide_range(make_inputs(w, with_dout=True))
+    fwd = O.layer_forward(inp, keep=True)
+    g = O.layer_backward(inp, fwd=fwd)
+    T, H, I, E, k = w.T, w.H, w.I, w.E, w.k
+    x = inp.x.double().tolist()
+    dout = inp.dout.double().tolist()
+    Wr = inp.Wr.double().tolist()
+    idx, gw = fwd["idx"], fwd["w"]
+    sig = lambda z: 1.0 / (1.0 + math.exp(-z)) if z >= 0 else math.exp(z) / (1.0 + math.exp(z))
+    xq = _brute_quant_rows(x)
+    ref = {"dx": [[0.0] * H for _ in range(T)], "dWg": np.zeros((E, H, I)), "dWu": np.zeros((E, H, I)),
+           "dWd": np.zeros((E, I, H)), "dgate": np.zeros((T, k)), "dWr": np.zeros((H, E)), "out": np.zeros((T, H))}
+    for e in range(E):
+        Wg, Wu, Wd = (t[e].double().tolist() for t in (inp.Wg, inp.Wu, inp.Wd))  # [H][I], [H][I], [I][H]
+        Wgf, Wuf = _T(_brute_quant_rows(_T(Wg))), _T(_brute_quant_rows(_T(Wu)))  # forward: along H
+        Wdf = _T(_brute_quant_rows(_T(Wd)))                                      # forward: along I
+        Wgb, Wub, Wdb = _brute_quant_rows(Wg), _brute_quant_rows(Wu), _brute_quant_rows(Wd)  # dgrad
+        for t in range(T):
+            for j in range(k):
+                if idx[t, j] != e:
+                    continue
+                gg = [sum(xq[t][h] * Wgf[h][i] for h in range(H)) for i in range(I)]
+                uu = [sum(xq[t][h] * Wuf[h][i] for h in range(H)) for i in range(I)]
+                hh = [gg[i] * sig(gg[i]) * uu[i] for i in range(I)]
+                hq = _brute_quant_rows([hh])[0]
+                y = [sum(hq[i] * Wdf[i][h] for i in range(I)) for h in range(H)]
+                ref["out"][t] += gw[t, j] * np.array(y)
+                ref["dgate"][t, j] = sum(dout[t][h] * y[h] for h in range(H))
+                dy = [gw[t, j] * dout[t][h] for h in range(H)]
+                dyq = _brute_quant_rows([dy])[0]
+                dh = [sum(dyq[h] * Wdb[i][h] for h in range(H)) for i in range(I)]
+                dg = [dh[i] * uu[i] * sig(gg[i]) * (1 + gg[i] * (1 - sig(gg[i]))) for i in range(I)]
+                du = [dh[i] * gg[i] * sig(gg[i]) for i in range(I)]
+                dgq, duq = _brute_quant_rows([dg])[0], _brute_quant_rows([du])[0]
+                for h in range(H):
+                    ref["dx"][t][h] += sum(dgq[i] * Wgb[h][i] + duq[i] * Wub[h][i] for i in range(I))
+                    for i in range(I):
+                        ref["dWg"][e, h, i] += x[t][h] * dg[i]
+                        ref["dWu"][e, h, i] += x[t][h] * du[i]
+                        ref["dWd"][e, i, h] += hh[i] * dy[h]
+    for t in range(T):  # router: softmax over the selected logits
+        s = sum(gw[t, j] * ref["dgate"][t, j] for j in range(k))
+        for j in range(k):
+            dl = gw[t, j] * (ref["dgate"][t, j] - s)
+            e = idx[t, j]
+            for h in range(H):
+                ref["dx"][t][h] += dl * Wr[h][e]
+                ref["dWr"][h, e] += x[t][h] * dl
+    np.testing.assert_allclose(fwd["out"], ref["out"], rtol=1e-9, atol=1e-12)
+    for n in ("dx", "dWg", "dWu", "dWd", "dgate", "dWr"):
+        np.testing.assert_allclose(g[n], np.array(ref[n]), rtol=1e-9, atol=1e-12, err_msg=n)
+
+
+def test_mx_backward_with_identity_quantiser_is_the_plain_backward():
+    w = tiny(T=24, H=128, I=64, E=4, k=2, shared_expert=True, router_bias="normal", prec="mxfp8")
+    inp = make_inputs(w, with_dout=True)
+    fwd = O.layer_forward(inp, keep=True, mx=False)
+    plain = O.layer_backward(inp, fwd=fwd, mx=False)
+    ident = O.layer_backward(inp, fwd=fwd, mx=True, quantizer=lambda a, axis: np.asarray(a, np.float64))
+    for n in plain:
+        np.testing.assert_array_equal(ident[n], plain[n], err_msg=n)
+
+
+def test_mx_backward_scales_exactly_with_dout_and_stays_near_plain():
+    w = tiny(T=32, H=128, I=64, E=4, k=2, router_bias="normal", prec="mxfp8")
+    inp = make_inputs(w, with_dout=True)
+    fwd = O.layer_forward(inp, keep=True)
+    g1 = O.layer_backward(inp, fwd=fwd)
+    g2 = O.layer_backward(inp, dout=2 * inp.dout, fwd=fwd)
+    for n in ("dx", "dWg", "dWu", "dWd", "dWr", "dgate"):
+        np.testing.assert_array_equal(g2[n], 2 * g1[n], err_msg=n)
+    # E4M3 keeps 3 mantissa bits: per-operand relative error <= 2^-4, so the
+    # quantised gradients stay within a few per cent of the unquantised ones
+    plain = O.layer_backward(inp, fwd=O.layer_forward(inp, keep=True, mx=False), mx=False)
+    for n in ("dx", "dWg", "dWu", "dWd"):
+        assert 1e-4 < O.rel_inf_err(g1[n], plain[n]) < 0.15, n
