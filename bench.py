@@ -83,9 +83,6 @@ def main():
     from moe_inputs import make_inputs
     mx = w.prec == "mxfp8"
     bwd = args.passes == "fwdbwd"
-    if mx and bwd:
-        log("the MXFP8 layer is forward-only in this version: measuring the forward")
-        bwd = False
     inp = make_inputs(w, with_dout=bwd)
     log("inputs drawn in %.1f s" % (time.time() - t_gen))
 
@@ -131,17 +128,24 @@ def main():
     moe.moe_timing_enable(False)
 
     T, H, I, E, k = w.T, w.H, w.I, w.E, w.k
-    rows = T * k + (T if w.shared_expert else 0)  # routed (+ shared) rows per step
+    shared_rows = T if w.shared_expert else 0
+    rows = T * k + shared_rows  # routed (+ shared) rows per step
     hi = float(H) * I * rows  # padding rows excluded from every figure below
     # algorithmic flops per step of each grouped-GEMM role, and the kernel
-    # symbol that runs it (rocprofv3 reports per symbol)
-    flops = {"gemm_gate_up": 4 * hi, "gemm_down": 2 * hi}
+    # symbol that runs it (rocprofv3 reports per symbol).  MXFP8 runs the
+    # routed experts on the scaled-MFMA kernel and the shared expert in bf16
+    # (its own timing kind); bf16 runs both in the same launches.
+    hr = float(H) * I * (T * k if mx else rows)
+    flops = {"gemm_gate_up": 4 * hr, "gemm_down": 2 * hr}
     if bwd:
-        flops.update({"dgrad_down": 2 * hi, "dgrad_gate_up": 4 * hi, "wgrad": 6 * hi})
+        flops.update({"dgrad_down": 2 * hr, "dgrad_gate_up": 4 * hr, "wgrad": 6 * hi})
+    if mx and shared_rows:
+        flops["shared_gemm"] = (12.0 if bwd else 6.0) * H * I * shared_rows
     symbol = {"gemm_gate_up": "mx_gemm_kernel<0>" if mx else "grouped_gemm_kernel<0>",
               "gemm_down": "mx_gemm_kernel<1>" if mx else "grouped_gemm_kernel<1>",
-              "dgrad_down": "grouped_gemm_kernel<1>", "dgrad_gate_up": "grouped_gemm_kernel<1>",
-              "wgrad": "wgrad_kernel"}
+              "dgrad_down": "mx_gemm_kernel<1>" if mx else "grouped_gemm_kernel<1>",
+              "dgrad_gate_up": "mx_gemm_kernel<1>" if mx else "grouped_gemm_kernel<1>",
+              "wgrad": "wgrad_kernel", "shared_gemm": "grouped_gemm_kernel (bf16 shared expert)"}
     by_sym = {}
     for kd, fl in flops.items():
         n, ms = kt[kd]
@@ -155,11 +159,11 @@ def main():
     dom = max(by_sym, key=lambda sy: by_sym[sy][1])
     dom_flops, ms_dom, n_dom, dom_roles = by_sym[dom]
     achieved = dom_flops / (ms_dom / 1e3) / 1e12
-    peak = PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS
+    peak = PEAK_FP8_TFLOPS if (mx and dom.startswith("mx_")) else PEAK_BF16_TFLOPS
     total_flops = sum(flops.values())
     res = {
-        "metric": "MoE layer %s tokens/s at H=7168 I=2048 (%s) + %% MFMA peak" % ("fwd+bwd" if bwd else "fwd",
-                                                                                "MXFP8" if mx else "bf16"),
+        "metric": "MoE layer %s tokens/s at H=%d I=%d (%s) + %% MFMA peak" % (
+            "fwd+bwd" if bwd else "fwd", H, I, "MXFP8" if mx else "bf16"),
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -177,10 +181,10 @@ def main():
                    "pass": "forward+backward" if bwd else "forward"},
         "roofline": {"bound": "mfma", "kernel": "moe::" + dom, "roles": dom_roles,
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": traffic_for(dom, w.name, mx),
+                     "frac": achieved / peak, "traffic": traffic_for(dom, w.name),
                      "avg_launch_ms": ms_dom / max(n_dom, 1), "launches": n_dom},
         "detail": {
-            "layer_mfma_frac": total_flops / (ms_step / 1e3) / 1e12 / peak,
+            "layer_mfma_frac": total_flops / (ms_step / 1e3) / 1e12 / (PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS),
             "tflops_by_role": {kd: flops[kd] * args.steps / (kt[kd][1] / 1e3) / 1e12
                                for kd in flops if kt[kd][1] > 0},
             "per_step_ms": {kind: v[1] / args.steps for kind, v in kt.items() if kind != "dropped"},
@@ -194,7 +198,7 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-def traffic_for(symbol: str, workload: str, mx: bool):
+def traffic_for(symbol: str, workload: str):
     """HBM bytes per launch of `symbol` from the committed rocprofv3 counter
     summary (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or
     None when there is none for this workload or the kernel source changed
@@ -205,8 +209,8 @@ def traffic_for(symbol: str, workload: str, mx: bool):
         return None
     with open(path) as f:
         rec = json.load(f)
-    ent = rec.get("kernels", {}).get("%s@%s" % (symbol, workload))
-    if not ent or ent.get("source_sha256") != _source_sha(mx):
+    ent = rec.get("kernels", {}).get("moe::%s@%s" % (symbol, workload))
+    if not ent or ent.get("source_sha256") != _source_sha(symbol.startswith("mx_")):
         return None
     return ent["hbm_bytes_per_launch"]
 
@@ -294,7 +298,8 @@ def cpu_baseline(inp, n_tokens: int, bwd: bool) -> dict:
                       inp.Wsg, inp.Wsu, inp.Wsd, inp.dout[:n] if inp.dout is not None else None)
     oracle.router_logits(np.zeros((1, inp.w.H), np.float32), np.zeros((inp.w.H, 1), np.float32))
     t0 = time.perf_counter()
-    fwd = oracle.layer_forward(sub, keep=bwd, mx=False)
+    mx = inp.w.prec == "mxfp8"
+    fwd = oracle.layer_forward(sub, keep=bwd)
     if bwd:
         oracle.layer_backward(sub, fwd=fwd)
     dt = time.perf_counter() - t0
@@ -302,8 +307,9 @@ def cpu_baseline(inp, n_tokens: int, bwd: bool) -> dict:
     omp = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": n / dt, "unit": "tokens/s", "cores": max(blas, omp), "kind": "oracle",
             "sample": "first %d of %d tokens as a %d-token layer: fixed-order fp32 routing (C, OpenMP) + "
-                      "fp64 expert SwiGLU FFN and combine%s (numpy/OpenBLAS); %.1f s"
-                      % (n, inp.w.T, n, " + fp64 backward" if bwd else "", dt)}
+                      "fp64 expert SwiGLU FFN and combine%s%s (numpy/OpenBLAS); %.1f s"
+                      % (n, inp.w.T, n, " + fp64 backward" if bwd else "",
+                         " with the MXFP8 quantisation points (C quantiser)" if mx else "", dt)}
 
 
 if __name__ == "__main__":

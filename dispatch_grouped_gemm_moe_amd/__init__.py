@@ -26,7 +26,7 @@ EXPORTS = ("moe_status_string", "moe_abi_version", "moe_validate_cfg", "moe_quer
            "moe_layer_bwd", "moe_read_device_status", "moe_mx_quantize", "moe_timing_enable",
            "moe_timing_read")
 KERNEL_KINDS = ("route", "layout", "gemm_gate_up", "gemm_down", "combine", "gather", "other", "wgrad",
-                "dgrad_down", "dgrad_gate_up")
+                "dgrad_down", "dgrad_gate_up", "shared_gemm")
 
 
 class moe_cfg(ctypes.Structure):
@@ -49,7 +49,7 @@ class moe_weights(ctypes.Structure):
 
 
 class moe_kernel_times(ctypes.Structure):
-    _fields_ = [("launches", ctypes.c_int32 * 10), ("ms", ctypes.c_double * 10), ("dropped", ctypes.c_int32)]
+    _fields_ = [("launches", ctypes.c_int32 * 11), ("ms", ctypes.c_double * 11), ("dropped", ctypes.c_int32)]
 
 
 class MoeError(RuntimeError):

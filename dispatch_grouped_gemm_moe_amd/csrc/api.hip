@@ -28,8 +28,10 @@ struct Plan {
     // packed weights (bytes): forward gate|up [Et][2I][H], down [Et][H][I];
     // backward down [Et][I][H] and gate|up rows [Et][H][2I]
     size_t pk_w1t, pk_w2t, pk_wd, pk_wgu, packed;
-    // MXFP8 copies of the routed experts' forward weights: codes and scales
-    size_t pk_w1q, pk_s1, pk_w2q, pk_s2;
+    // MXFP8 copies of the routed experts' weights: codes and scales, forward
+    // (along H for gate|up, along I for down) and input-gradient (Wd along H,
+    // Wg|Wu along I)
+    size_t pk_w1q, pk_s1, pk_w2q, pk_s2, pk_wdq, pk_sd, pk_wguq, pk_sgu;
     bool mx;
     // forward workspace (bytes)
     size_t ws_status, ws_idx, ws_w, ws_slot0, slot_bytes, ws_fwd;
@@ -40,6 +42,7 @@ struct Plan {
     // backward workspace (bytes)
     size_t wb_wrt, wb_mt, wb_lay0, lay_bytes, ly_hdr, ly_prow_token, ly_tok_prow, ly_prow_slot;
     size_t wb_dyt, wb_xgt, wb_dgut, wb_ht, wb_dsel, wb_dy, wb_dgu, wb_dh, wb_dx, wb_dgp, ws_bwd;
+    size_t wb_dyq, wb_sdy, wb_dguq, wb_sdgu;  // MXFP8 operands of the input-gradient GEMMs
 };
 
 moe_status validate(const moe_cfg* c) {
@@ -104,6 +107,10 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
         p->pk_s1 = o; o = align_up(o + E * (H / 64) * 2 * I * 4);
         p->pk_w2q = o; o = align_up(o + E * H * I);
         p->pk_s2 = o; o = align_up(o + E * (I / 64) * H * 4);
+        p->pk_wdq = o; o = align_up(o + E * I * H);
+        p->pk_sd = o; o = align_up(o + E * (H / 64) * I * 4);
+        p->pk_wguq = o; o = align_up(o + E * H * 2 * I);
+        p->pk_sgu = o; o = align_up(o + E * (2 * I / 64) * H * 4);
     }
     p->packed = o;
 
@@ -159,6 +166,12 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     p->wb_dh = o; o = align_up(o + rp * I * 2);
     p->wb_dx = o; o = align_up(o + rp * H * 2);
     p->wb_dgp = o; o = align_up(o + rp * (H / 64) * 4);
+    if (p->mx) {
+        p->wb_dyq = o; o = align_up(o + rp * H);
+        p->wb_sdy = o; o = align_up(o + (H / 64) * rp * 4);
+        p->wb_dguq = o; o = align_up(o + rp * 2 * I);
+        p->wb_sdgu = o; o = align_up(o + (2 * I / 64) * rp * 4);
+    }
     p->ws_bwd = o;
     return MOE_OK;
 }
@@ -255,12 +268,16 @@ moe_status moe_prepare_weights(const moe_cfg* cfg, const uint16_t* Wg, const uin
     launch_transpose(Wd, p.E, p.I, p.H, W2t, s);
     launch_copy(Wd, (size_t)p.E * I * H * 2, Wdc, s);
     launch_concat_gu(Wg, Wu, p.E, p.H, p.I, Wgu, s);
-    if (p.mx) {  // E4M3 codes + E8M0 scales along each forward GEMM's K, expert by expert
+    if (p.mx) {  // E4M3 codes + E8M0 scales along each GEMM's K, expert by expert
         for (int e = 0; e < p.E; ++e) {
             launch_mx_quant(W1t + (size_t)e * 2 * I * H, 2 * p.I, p.H, 1, base + p.pk_w1q + (size_t)e * 2 * I * H,
                             base + p.pk_s1 + (size_t)e * (H / 64) * 2 * I * 4, s);
             launch_mx_quant(W2t + (size_t)e * H * I, p.H, p.I, 1, base + p.pk_w2q + (size_t)e * H * I,
                             base + p.pk_s2 + (size_t)e * (I / 64) * H * 4, s);
+            launch_mx_quant(Wdc + (size_t)e * I * H, p.I, p.H, 1, base + p.pk_wdq + (size_t)e * I * H,
+                            base + p.pk_sd + (size_t)e * (H / 64) * I * 4, s);
+            launch_mx_quant(Wgu + (size_t)e * H * 2 * I, p.H, 2 * p.I, 1, base + p.pk_wguq + (size_t)e * H * 2 * I,
+                            base + p.pk_sgu + (size_t)e * (2 * I / 64) * H * 4, s);
         }
     }
     if (p.shared) {
@@ -360,7 +377,7 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
                 m1.SB = pk + p.pk_s1; m1.sb_stride = (int64_t)(p.H / 64) * 2 * p.I * 4; m1.sb_kstride = (int64_t)2 * p.I * 4;
                 m1.N = 2 * p.I; m1.K = p.H; m1.mt_start = mt; m1.hdr = hdr; m1.e_begin = 0; m1.e_end = p.E;
                 m1.C = nullptr; m1.ldc = 0;
-                m1.Cq = slot + p.sl_hq; m1.Cs = slot + p.sl_sh; m1.cs_rows = p.rpad;
+                m1.Cq = slot + p.sl_hq; m1.Cs = slot + p.sl_sh; m1.cs_rows = p.rpad; m1.GU = gubuf;
                 TIMED(MOE_K_GEMM_GATE_UP, s, launch_mx_gemm(m1, kEpiSwiGLU, grid, s));
             }
             GemmArgs g1;
@@ -370,7 +387,8 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             g1.N = 2 * p.I; g1.K = p.H;
             g1.mt_start = mt; g1.hdr = hdr; g1.Et = p.Et;
             g1.GU = gubuf; g1.e_begin = e_bf16; g1.e_end = p.Et;
-            if (e_bf16 < p.Et) TIMED(MOE_K_GEMM_GATE_UP, s, launch_grouped_gemm(g1, kEpiSwiGLU, grid, s));
+            if (e_bf16 < p.Et)
+                TIMED(p.mx ? MOE_K_SHARED_GEMM : MOE_K_GEMM_GATE_UP, s, launch_grouped_gemm(g1, kEpiSwiGLU, grid, s));
             if (p.mx) {
                 MxGemmArgs m2;
                 m2.A = slot + p.sl_hq; m2.a_row_map = nullptr; m2.lda = p.I;
@@ -378,7 +396,7 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
                 m2.B = pk + p.pk_w2q; m2.b_stride = (int64_t)p.H * p.I;
                 m2.SB = pk + p.pk_s2; m2.sb_stride = (int64_t)(p.I / 64) * p.H * 4; m2.sb_kstride = (int64_t)p.H * 4;
                 m2.N = p.H; m2.K = p.I; m2.mt_start = mt; m2.hdr = hdr; m2.e_begin = 0; m2.e_end = p.E;
-                m2.C = ybuf; m2.ldc = p.H; m2.Cq = nullptr; m2.Cs = nullptr; m2.cs_rows = 0;
+                m2.C = ybuf; m2.ldc = p.H; m2.Cq = nullptr; m2.Cs = nullptr; m2.cs_rows = 0; m2.GU = nullptr;
                 TIMED(MOE_K_GEMM_DOWN, s, launch_mx_gemm(m2, kEpiStore, grid, s));
             }
             GemmArgs g2;
@@ -388,7 +406,8 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             g2.N = p.H; g2.K = p.I;
             g2.mt_start = mt; g2.hdr = hdr; g2.Et = p.Et;
             g2.GU = nullptr; g2.e_begin = e_bf16; g2.e_end = p.Et;
-            if (e_bf16 < p.Et) TIMED(MOE_K_GEMM_DOWN, s, launch_grouped_gemm(g2, kEpiStore, grid, s));
+            if (e_bf16 < p.Et)
+                TIMED(p.mx ? MOE_K_SHARED_GEMM : MOE_K_GEMM_DOWN, s, launch_grouped_gemm(g2, kEpiStore, grid, s));
         }
         TIMED(MOE_K_COMBINE, s,
               launch_combine(ybuf, p.H, tok_prow, p.ld_tok_prow, gw + (size_t)t0 * p.k, p.k,
@@ -404,7 +423,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
     Plan p;
     moe_status st = make_plan(cfg, &p);
     if (st != MOE_OK) return st;
-    if (p.identity || p.mx) return MOE_E_UNSUPPORTED;
+    if (p.identity) return MOE_E_UNSUPPORTED;
     if (!w || !w->Wr || !w->packed || !x || !dout || !saved || !dx || !dWg || !dWu || !dWd || !dWr || !ws)
         return MOE_E_INVALID;
     if (p.shared && !dWs) return MOE_E_INVALID;
@@ -467,22 +486,50 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
         rc.dsel = dsel; rc.H = H; rc.k = k; rc.nhb = H / 64; rc.ldt = rp;
         TIMED(MOE_K_GATHER, s, launch_rcomb_gather(rc, (int)rp, s));
 
+        // MXFP8: the routed experts' input-gradient GEMMs take E4M3 operands
+        // quantised along their K (dY along H here, dG | dU along I below);
+        // the shared expert stays bf16.
+        const int e_bf16 = p.mx ? E : 0;
+        if (p.mx) {
+            TIMED(MOE_K_GATHER, s, launch_mx_quant(dY, rp, H, 1, wsb + p.wb_dyq, wsb + p.wb_sdy, s, hdr));
+            MxGemmArgs m1;  // dH = Q(dY) Q(Wd)^T
+            m1.A = wsb + p.wb_dyq; m1.a_row_map = nullptr; m1.lda = H;
+            m1.SA = wsb + p.wb_sdy; m1.sa_kstride = rp * 4;
+            m1.B = pk + p.pk_wdq; m1.b_stride = (int64_t)I * H;
+            m1.SB = pk + p.pk_sd; m1.sb_stride = (int64_t)(H / 64) * I * 4; m1.sb_kstride = (int64_t)I * 4;
+            m1.N = I; m1.K = H; m1.mt_start = mt; m1.hdr = hdr; m1.e_begin = 0; m1.e_end = E;
+            m1.C = dH; m1.ldc = I; m1.Cq = nullptr; m1.Cs = nullptr; m1.cs_rows = 0; m1.GU = nullptr;
+            TIMED(MOE_K_DGRAD_DOWN, s, launch_mx_gemm(m1, kEpiStore, grid, s));
+        }
         GemmArgs g1;  // dH = dY Wd^T
         g1.A = dY; g1.a_row_map = nullptr; g1.lda = H;
         g1.B = Wdc; g1.b_stride = (int64_t)I * H;
         g1.C = dH; g1.ldc = I; g1.N = I; g1.K = H;
-        g1.mt_start = mt; g1.hdr = hdr; g1.Et = Et; g1.GU = nullptr; g1.e_begin = 0; g1.e_end = Et;
-        TIMED(MOE_K_DGRAD_DOWN, s, launch_grouped_gemm(g1, kEpiStore, grid, s));
+        g1.mt_start = mt; g1.hdr = hdr; g1.Et = Et; g1.GU = nullptr; g1.e_begin = e_bf16; g1.e_end = Et;
+        if (e_bf16 < Et)
+            TIMED(p.mx ? MOE_K_SHARED_GEMM : MOE_K_DGRAD_DOWN, s, launch_grouped_gemm(g1, kEpiStore, grid, s));
         SwigluBwdArgs sb;
         sb.dH = dH; sb.GU = GUb; sb.hdr = hdr; sb.dGU = dGU; sb.dGUT = dGUT; sb.HT = HT; sb.I = I; sb.ldt = rp;
         TIMED(MOE_K_GATHER, s, launch_swiglu_bwd(sb, (int)rp, s));
+        if (p.mx) {
+            TIMED(MOE_K_GATHER, s, launch_mx_quant(dGU, rp, 2 * I, 1, wsb + p.wb_dguq, wsb + p.wb_sdgu, s, hdr));
+            MxGemmArgs m2;  // dX = Q(dG | dU) Q(Wg | Wu)^T
+            m2.A = wsb + p.wb_dguq; m2.a_row_map = nullptr; m2.lda = 2 * I;
+            m2.SA = wsb + p.wb_sdgu; m2.sa_kstride = rp * 4;
+            m2.B = pk + p.pk_wguq; m2.b_stride = (int64_t)H * 2 * I;
+            m2.SB = pk + p.pk_sgu; m2.sb_stride = (int64_t)(2 * I / 64) * H * 4; m2.sb_kstride = (int64_t)H * 4;
+            m2.N = H; m2.K = 2 * I; m2.mt_start = mt; m2.hdr = hdr; m2.e_begin = 0; m2.e_end = E;
+            m2.C = dXb; m2.ldc = H; m2.Cq = nullptr; m2.Cs = nullptr; m2.cs_rows = 0; m2.GU = nullptr;
+            TIMED(MOE_K_DGRAD_GATE_UP, s, launch_mx_gemm(m2, kEpiStore, grid, s));
+        }
         GemmArgs g2;  // dX = dG Wg^T + dU Wu^T
         g2.A = dGU; g2.a_row_map = nullptr; g2.lda = 2 * I;
         g2.B = Wgu; g2.b_stride = (int64_t)H * 2 * I;
         g2.C = dXb; g2.ldc = H; g2.N = H; g2.K = 2 * I;
         g2.mt_start = mt; g2.hdr = hdr; g2.Et = Et;
-        g2.GU = nullptr; g2.e_begin = 0; g2.e_end = Et;
-        TIMED(MOE_K_DGRAD_GATE_UP, s, launch_grouped_gemm(g2, kEpiStore, grid, s));
+        g2.GU = nullptr; g2.e_begin = e_bf16; g2.e_end = Et;
+        if (e_bf16 < Et)
+            TIMED(p.mx ? MOE_K_SHARED_GEMM : MOE_K_DGRAD_GATE_UP, s, launch_grouped_gemm(g2, kEpiStore, grid, s));
 
         RdispArgs rd;
         rd.dX = dXb; rd.dgp = dgp; rd.tok_prow = tok_prow; rd.topk_idx = idx; rd.topk_w = gw; rd.WrT = WrT;

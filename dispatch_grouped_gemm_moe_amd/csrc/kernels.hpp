@@ -72,12 +72,14 @@ struct MxGemmArgs {
     uint8_t* Cq;               // kEpiSwiGLU: h codes [R_pad][N/2]
     uint8_t* Cs;               // kEpiSwiGLU: h scales [N/2/64][cs_rows][4]
     int64_t cs_rows;
+    uint16_t* GU;              // kEpiSwiGLU, optional: bf16 g | u [R_pad][N] kept for the backward
 };
 void launch_mx_gemm(const MxGemmArgs& a, GemmEpilogue epi, int grid, hipStream_t stream);
 // bf16 [rows][cols] -> E4M3 codes [rows][cols] and E8M0 scales; layout 0:
 // [rows][cols/32], layout 1: [cols/64][rows][4] (bytes 0, 1 = blocks 2j, 2j+1).
+// With hdr, rows from hdr->m_tiles * BM on are skipped.
 void launch_mx_quant(const uint16_t* src, int64_t rows, int cols, int layout, uint8_t* codes, uint8_t* scales,
-                     hipStream_t stream);
+                     hipStream_t stream, const LayoutHeader* hdr = nullptr);
 
 // Backward SwiGLU over the padded rows of one minibatch, from dH and the saved
 // g | u:  dG = dH * u * silu'(g), dU = dH * silu(g), h = silu(g) * u.

@@ -47,12 +47,13 @@ __device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restrict__ src, int64_t rows, int cols,
                                                        int layout, uint8_t* __restrict__ codes,
-                                                       uint8_t* __restrict__ scales) {
+                                                       uint8_t* __restrict__ scales, const LayoutHeader* hdr) {
     const int nb = cols / 32;
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= rows * nb) return;
     const int64_t r = i / nb;
     const int b = (int)(i - r * nb);
+    if (hdr && r >= (int64_t)hdr->m_tiles * BM) return;  // rows past the minibatch's last tile
     const intx4* s = (const intx4*)(src + r * cols + b * 32);
     float v[32];
 #pragma unroll
@@ -87,10 +88,10 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restric
 }
 
 void launch_mx_quant(const uint16_t* src, int64_t rows, int cols, int layout, uint8_t* codes, uint8_t* scales,
-                     hipStream_t stream) {
+                     hipStream_t stream, const LayoutHeader* hdr) {
     const int64_t n = rows * (cols / 32);
     hipLaunchKernelGGL(mx_quant_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, src, rows, cols,
-                       layout, codes, scales);
+                       layout, codes, scales, hdr);
 }
 
 // ---------------------------------------------------------------------------
@@ -279,6 +280,10 @@ void mx_gemm_kernel(MxGemmArgs p) {
                         m = fmaxf(m, __shfl_xor(m, 1, kWave));
                         const int ex = mx_scale_exp(m);
                         const int row = prow0 + wm * 128 + i * 32 + (r >> 2) * 8 + 4 * half + (r & 3);
+                        if (live && p.GU) {
+                            p.GU[(int64_t)row * p.N + hcol] = f32_to_bf16_rne(g);
+                            p.GU[(int64_t)row * p.N + I + hcol] = f32_to_bf16_rne(u);
+                        }
                         if (live) {
                             const int q = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(h, -ex), 0.0f, 0, false);
                             p.Cq[(int64_t)row * I + hcol] = (uint8_t)(q & 0xff);

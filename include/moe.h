@@ -204,8 +204,13 @@ moe_status moe_layer_fwd(const moe_cfg *cfg, const moe_weights *w, const uint16_
  * The router bias is an input, not a parameter: it has no gradient.
  * Each weight gradient sums expert e's rows minibatch by minibatch in token
  * order, so results are bitwise reproducible for a given minibatch size.
- * MOE_E_UNSUPPORTED in identity-expert mode and for MOE_PREC_MXFP8 (the
- * MXFP8 layer is forward-only in this version).
+ * MOE_PREC_MXFP8: the routed experts' input-gradient GEMMs take E4M3 operands
+ * with E8M0 scales per 32 elements of their contraction axis (dY and Wd along
+ * H for dH = dY Wd^T; dG|dU and Wg|Wu along I for dX = dG Wg^T + dU Wu^T; the
+ * MXFP8 routed experts of [RW] "Rebuilding the MoE layer around
+ * communication"); weight gradients use the unquantised bf16 operands and the
+ * shared expert stays bf16.
+ * MOE_E_UNSUPPORTED in identity-expert mode.
  */
 moe_status moe_layer_bwd(const moe_cfg *cfg, const moe_weights *w, const uint16_t *x,
                          const uint16_t *dout, const void *saved, size_t saved_bytes,
@@ -259,7 +264,8 @@ typedef enum moe_kernel_kind {
     MOE_K_WGRAD = 7,        /* weight-gradient grouped GEMMs of the backward */
     MOE_K_DGRAD_DOWN = 8,   /* backward: dH = dY Wd^T */
     MOE_K_DGRAD_GATE_UP = 9, /* backward: dX = dG Wg^T + dU Wu^T */
-    MOE_K_COUNT = 10
+    MOE_K_SHARED_GEMM = 10, /* MOE_PREC_MXFP8: the bf16 shared expert's forward and input-gradient GEMMs */
+    MOE_K_COUNT = 11
 } moe_kernel_kind;
 
 typedef struct moe_kernel_times {

@@ -23,7 +23,7 @@ import torch
 MASTER_SEED = 20261202
 
 # tensor ids inside a workload's stream space
-_X, _WR, _BIAS, _WG, _WU, _WD, _WSG, _WSU, _WSD, _DOUT, _PERM = range(1, 12)
+_X, _WR, _BIAS, _WG, _WU, _WD, _WSG, _WSU, _WSD, _DOUT, _PERM, _WIDE = range(1, 13)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -45,6 +45,10 @@ class Workload:
     x_sigma: float = 1.0
     w_sigma: float = 0.02
     zipf_s: float = 1.1
+    # scale every row and column of x, dout and the expert weights by its own
+    # power of two in 2^-3 .. 2^3 (exact in bf16), so 32-element blocks mix
+    # magnitudes along one axis only
+    wide_range: bool = False
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -131,4 +135,19 @@ def make_inputs(w: Workload, with_dout: bool | None = None) -> LayerInputs:
         li.Wsd = _normal(w, _WSD, (I, H), w.w_sigma).to(torch.bfloat16)
     if with_dout if with_dout is not None else w.backward:
         li.dout = _normal(w, _DOUT, (T, H), 1.0).to(torch.bfloat16)
+    if w.wide_range:
+        g = _gen(w, _WIDE)
+
+        def scale(t, *axes):
+            f = torch.ones(t.shape, dtype=torch.float64)
+            for ax in axes:
+                shp = [1] * t.dim()
+                shp[ax] = t.shape[ax]
+                f = f * torch.pow(2.0, torch.randint(-3, 4, shp, generator=g).double())
+            return (t.double() * f).to(t.dtype)
+
+        li.x = scale(li.x, 0, 1)
+        li.Wg, li.Wu, li.Wd = scale(li.Wg, 1, 2), scale(li.Wu, 1, 2), scale(li.Wd, 1, 2)
+        if li.dout is not None:
+            li.dout = scale(li.dout, 0, 1)
     return li

@@ -469,33 +469,13 @@ def _T(M):
     return [list(c) for c in zip(*M)]
 
 
-def _wide_range(inp):
-    """Scale every row and every column of x, dout and the expert weights by its
-    own power of two (exact in bf16), spanning 2^-6 .. 2^6.  A 32-element block
-    then mixes magnitudes along one axis and not along the other, so quantising
-    along the wrong axis changes the result (with N(0, s) entries nearly every
-    block of either axis gets the same scale, which hides the axis)."""
-    g = torch.Generator().manual_seed(77)
-
-    def scale(t, *axes):
-        f = torch.ones(t.shape, dtype=torch.float64)
-        for ax in axes:
-            shp = [1] * t.dim()
-            shp[ax] = t.shape[ax]
-            f = f * torch.pow(2.0, torch.randint(-3, 4, shp, generator=g).double())
-        return (t.double() * f).to(t.dtype)
-
-    return LayerInputs(inp.w, scale(inp.x, 0, 1), inp.Wr, inp.bias, scale(inp.Wg, 1, 2), scale(inp.Wu, 1, 2),
-                       scale(inp.Wd, 1, 2), inp.Wsg, inp.Wsu, inp.Wsd, scale(inp.dout, 0, 1))
-
-
 def test_mx_backward_matches_scalar_brute_force():
     """Every MXFP8 quantisation point of the layer, and every contraction, by
     scalar loops on a tiny layer: the forward (x along H; Wg, Wu along H; h
     along I; Wd along I), the input-gradient GEMMs (dY and Wd along H; dG, dU
     and Wg, Wu along I) and the unquantised weight gradients."""
-    w = tiny(T=5, H=64, I=64, E=3, k=2, router_bias="normal", prec="mxfp8")
-    inp = _wide_range(make_inputs(w, with_dout=True))
+    w = tiny(T=5, H=64, I=64, E=3, k=2, router_bias="normal", prec="mxfp8", wide_range=True)
+    inp = make_inputs(w, with_dout=True)
     fwd = O.layer_forward(inp, keep=True)
     g = O.layer_backward(inp, fwd=fwd)
     T, H, I, E, k = w.T, w.H, w.I, w.E, w.k
