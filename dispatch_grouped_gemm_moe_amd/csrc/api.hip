@@ -37,7 +37,8 @@ struct Plan {
     size_t ws_status, ws_idx, ws_w, ws_slot0, slot_bytes, ws_fwd;
     size_t sl_hdr, sl_mt, sl_prow_token, sl_tok_prow, sl_h, sl_y, sl_hq, sl_sh;
     size_t ws_xq, ws_sx;  // MXFP8 codes and scales of x
-    // saved (bytes): routing, then per minibatch g|u [rpad][2I] and Y [rpad][H]
+    // saved (bytes): routing, then per minibatch g|u [rpad][2I] (bf16, or fp32
+    // under MXFP8) and Y [rpad][H]
     size_t sv_idx, sv_w, sv_mb0, sv_mb, sv_y, saved;
     // backward workspace (bytes)
     size_t wb_wrt, wb_mt, wb_lay0, lay_bytes, ly_hdr, ly_prow_token, ly_tok_prow, ly_prow_slot;
@@ -142,7 +143,7 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     p->sv_idx = 0;
     p->sv_w = align_up(Tk * 4);
     p->sv_mb0 = align_up(p->sv_w + Tk * 4);
-    p->sv_y = align_up(rp * 2 * I * 2);
+    p->sv_y = align_up(rp * 2 * I * (p->mx ? 4 : 2));  // g|u: fp32 under MXFP8 (its quantisation input)
     p->sv_mb = align_up(p->sv_y + rp * H * 2);
     p->saved = p->sv_mb0 + nmb * p->sv_mb;
 
@@ -163,7 +164,7 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     p->wb_dsel = o; o = align_up(o + nmb * rp * 4);
     p->wb_dy = o; o = align_up(o + rp * H * 2);
     p->wb_dgu = o; o = align_up(o + rp * 2 * I * 2);
-    p->wb_dh = o; o = align_up(o + rp * I * 2);
+    p->wb_dh = o; o = align_up(o + rp * I * (p->mx ? 4 : 2));
     p->wb_dx = o; o = align_up(o + rp * H * 2);
     p->wb_dgp = o; o = align_up(o + rp * (H / 64) * 4);
     if (p->mx) {
@@ -350,9 +351,13 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
         uint16_t* hbuf = (uint16_t*)(slot + p.sl_h);
         uint16_t* ybuf = (uint16_t*)(slot + p.sl_y);
         uint16_t* gubuf = nullptr;
+        float* guf = nullptr;
         if (saved) {  // keep g|u and Y of every minibatch for the backward
             uint8_t* mb = (uint8_t*)saved + p.sv_mb0 + (size_t)b * p.sv_mb;
-            gubuf = (uint16_t*)mb;
+            if (p.mx)
+                guf = (float*)mb;
+            else
+                gubuf = (uint16_t*)mb;
             ybuf = (uint16_t*)(mb + p.sv_y);
         }
 
@@ -371,41 +376,41 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
         } else {
             const int e_bf16 = p.mx ? p.E : 0;  // MXFP8 covers the routed experts; bf16 the rest
             if (p.mx) {
-                MxGemmArgs m1;
+                MxGemmArgs m1{};
                 m1.A = xq; m1.a_row_map = prow_token; m1.lda = p.H; m1.SA = sx; m1.sa_kstride = (int64_t)p.T * 4;
                 m1.B = pk + p.pk_w1q; m1.b_stride = (int64_t)2 * p.I * p.H;
                 m1.SB = pk + p.pk_s1; m1.sb_stride = (int64_t)(p.H / 64) * 2 * p.I * 4; m1.sb_kstride = (int64_t)2 * p.I * 4;
                 m1.N = 2 * p.I; m1.K = p.H; m1.mt_start = mt; m1.hdr = hdr; m1.e_begin = 0; m1.e_end = p.E;
                 m1.C = nullptr; m1.ldc = 0;
-                m1.Cq = slot + p.sl_hq; m1.Cs = slot + p.sl_sh; m1.cs_rows = p.rpad; m1.GU = gubuf;
+                m1.Cq = slot + p.sl_hq; m1.Cs = slot + p.sl_sh; m1.cs_rows = p.rpad; m1.GU = guf; m1.Cf = nullptr;
                 TIMED(MOE_K_GEMM_GATE_UP, s, launch_mx_gemm(m1, kEpiSwiGLU, grid, s));
             }
-            GemmArgs g1;
+            GemmArgs g1{};
             g1.A = x; g1.a_row_map = prow_token; g1.lda = p.H;
             g1.B = W1t; g1.b_stride = (int64_t)2 * p.I * p.H;
             g1.C = hbuf; g1.ldc = p.I;
             g1.N = 2 * p.I; g1.K = p.H;
             g1.mt_start = mt; g1.hdr = hdr; g1.Et = p.Et;
-            g1.GU = gubuf; g1.e_begin = e_bf16; g1.e_end = p.Et;
+            g1.GU = gubuf; g1.e_begin = e_bf16; g1.e_end = p.Et; g1.GUf = guf; g1.Cf = nullptr;
             if (e_bf16 < p.Et)
                 TIMED(p.mx ? MOE_K_SHARED_GEMM : MOE_K_GEMM_GATE_UP, s, launch_grouped_gemm(g1, kEpiSwiGLU, grid, s));
             if (p.mx) {
-                MxGemmArgs m2;
+                MxGemmArgs m2{};
                 m2.A = slot + p.sl_hq; m2.a_row_map = nullptr; m2.lda = p.I;
                 m2.SA = slot + p.sl_sh; m2.sa_kstride = (int64_t)p.rpad * 4;
                 m2.B = pk + p.pk_w2q; m2.b_stride = (int64_t)p.H * p.I;
                 m2.SB = pk + p.pk_s2; m2.sb_stride = (int64_t)(p.I / 64) * p.H * 4; m2.sb_kstride = (int64_t)p.H * 4;
                 m2.N = p.H; m2.K = p.I; m2.mt_start = mt; m2.hdr = hdr; m2.e_begin = 0; m2.e_end = p.E;
-                m2.C = ybuf; m2.ldc = p.H; m2.Cq = nullptr; m2.Cs = nullptr; m2.cs_rows = 0; m2.GU = nullptr;
+                m2.C = ybuf; m2.ldc = p.H; m2.Cq = nullptr; m2.Cs = nullptr; m2.cs_rows = 0; m2.GU = nullptr; m2.Cf = nullptr;
                 TIMED(MOE_K_GEMM_DOWN, s, launch_mx_gemm(m2, kEpiStore, grid, s));
             }
-            GemmArgs g2;
+            GemmArgs g2{};
             g2.A = hbuf; g2.a_row_map = nullptr; g2.lda = p.I;
             g2.B = W2t; g2.b_stride = (int64_t)p.H * p.I;
             g2.C = ybuf; g2.ldc = p.H;
             g2.N = p.H; g2.K = p.I;
             g2.mt_start = mt; g2.hdr = hdr; g2.Et = p.Et;
-            g2.GU = nullptr; g2.e_begin = e_bf16; g2.e_end = p.Et;
+            g2.GU = nullptr; g2.e_begin = e_bf16; g2.e_end = p.Et; g2.GUf = nullptr; g2.Cf = nullptr;
             if (e_bf16 < p.Et)
                 TIMED(p.mx ? MOE_K_SHARED_GEMM : MOE_K_GEMM_DOWN, s, launch_grouped_gemm(g2, kEpiStore, grid, s));
         }
@@ -466,7 +471,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
         int32_t* tok_prow = (int32_t*)(lay + p.ly_tok_prow);
         int32_t* prow_slot = (int32_t*)(lay + p.ly_prow_slot);
         const uint8_t* svb = sv + p.sv_mb0 + (size_t)b * p.sv_mb;
-        const uint16_t* GUb = (const uint16_t*)svb;
+        const uint16_t* GUb = (const uint16_t*)svb;  // fp32 under MXFP8
         const uint16_t* Yb = (const uint16_t*)(svb + p.sv_y);
         uint16_t* dYT = dYT_all + (size_t)b * H * rp;
         uint16_t* xgT = xgT_all + (size_t)b * H * rp;
@@ -480,78 +485,84 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
         o.prow_slot = prow_slot; o.tok_prow_ld = p.ld_tok_prow; o.token_base = t0;
         TIMED(MOE_K_LAYOUT, s, launch_layout(idx + (size_t)t0 * k, Tm, E, k, p.shared ? 1 : 0, o, s));
 
-        RcombArgs rc;
+        RcombArgs rc{};
         rc.dout = dout; rc.x = x; rc.Y = Yb; rc.topk_w = gw; rc.prow_token = prow_token;
         rc.prow_slot = prow_slot; rc.hdr = hdr; rc.dY = dY; rc.dYT = dYT; rc.xgT = xgT; rc.dgp = dgp;
         rc.dsel = dsel; rc.H = H; rc.k = k; rc.nhb = H / 64; rc.ldt = rp;
+        rc.dYq = p.mx ? wsb + p.wb_dyq : nullptr;  // MXFP8: dY quantised from fp32 here
+        rc.sdY = p.mx ? wsb + p.wb_sdy : nullptr;
         TIMED(MOE_K_GATHER, s, launch_rcomb_gather(rc, (int)rp, s));
 
         // MXFP8: the routed experts' input-gradient GEMMs take E4M3 operands
         // quantised along their K (dY along H here, dG | dU along I below);
         // the shared expert stays bf16.
         const int e_bf16 = p.mx ? E : 0;
+        float* dHf = p.mx ? (float*)dH : nullptr;  // fp32 under MXFP8
         if (p.mx) {
-            TIMED(MOE_K_GATHER, s, launch_mx_quant(dY, rp, H, 1, wsb + p.wb_dyq, wsb + p.wb_sdy, s, hdr));
-            MxGemmArgs m1;  // dH = Q(dY) Q(Wd)^T
+            MxGemmArgs m1{};  // dH = Q(dY) Q(Wd)^T
             m1.A = wsb + p.wb_dyq; m1.a_row_map = nullptr; m1.lda = H;
             m1.SA = wsb + p.wb_sdy; m1.sa_kstride = rp * 4;
             m1.B = pk + p.pk_wdq; m1.b_stride = (int64_t)I * H;
             m1.SB = pk + p.pk_sd; m1.sb_stride = (int64_t)(H / 64) * I * 4; m1.sb_kstride = (int64_t)I * 4;
             m1.N = I; m1.K = H; m1.mt_start = mt; m1.hdr = hdr; m1.e_begin = 0; m1.e_end = E;
-            m1.C = dH; m1.ldc = I; m1.Cq = nullptr; m1.Cs = nullptr; m1.cs_rows = 0; m1.GU = nullptr;
+            m1.C = nullptr; m1.ldc = I; m1.Cq = nullptr; m1.Cs = nullptr; m1.cs_rows = 0; m1.GU = nullptr;
+            m1.Cf = dHf;
             TIMED(MOE_K_DGRAD_DOWN, s, launch_mx_gemm(m1, kEpiStore, grid, s));
         }
-        GemmArgs g1;  // dH = dY Wd^T
+        GemmArgs g1{};  // dH = dY Wd^T
         g1.A = dY; g1.a_row_map = nullptr; g1.lda = H;
         g1.B = Wdc; g1.b_stride = (int64_t)I * H;
         g1.C = dH; g1.ldc = I; g1.N = I; g1.K = H;
         g1.mt_start = mt; g1.hdr = hdr; g1.Et = Et; g1.GU = nullptr; g1.e_begin = e_bf16; g1.e_end = Et;
+        g1.GUf = nullptr; g1.Cf = dHf;
         if (e_bf16 < Et)
             TIMED(p.mx ? MOE_K_SHARED_GEMM : MOE_K_DGRAD_DOWN, s, launch_grouped_gemm(g1, kEpiStore, grid, s));
-        SwigluBwdArgs sb;
+        SwigluBwdArgs sb{};
         sb.dH = dH; sb.GU = GUb; sb.hdr = hdr; sb.dGU = dGU; sb.dGUT = dGUT; sb.HT = HT; sb.I = I; sb.ldt = rp;
+        sb.dHf = dHf; sb.GUf = p.mx ? (const float*)GUb : nullptr;  // MXFP8: fp32 inputs, dG|dU quantised here
+        sb.dGUq = p.mx ? wsb + p.wb_dguq : nullptr; sb.sdGU = p.mx ? wsb + p.wb_sdgu : nullptr;
         TIMED(MOE_K_GATHER, s, launch_swiglu_bwd(sb, (int)rp, s));
         if (p.mx) {
-            TIMED(MOE_K_GATHER, s, launch_mx_quant(dGU, rp, 2 * I, 1, wsb + p.wb_dguq, wsb + p.wb_sdgu, s, hdr));
-            MxGemmArgs m2;  // dX = Q(dG | dU) Q(Wg | Wu)^T
+            MxGemmArgs m2{};  // dX = Q(dG | dU) Q(Wg | Wu)^T
             m2.A = wsb + p.wb_dguq; m2.a_row_map = nullptr; m2.lda = 2 * I;
             m2.SA = wsb + p.wb_sdgu; m2.sa_kstride = rp * 4;
             m2.B = pk + p.pk_wguq; m2.b_stride = (int64_t)H * 2 * I;
             m2.SB = pk + p.pk_sgu; m2.sb_stride = (int64_t)(2 * I / 64) * H * 4; m2.sb_kstride = (int64_t)H * 4;
             m2.N = H; m2.K = 2 * I; m2.mt_start = mt; m2.hdr = hdr; m2.e_begin = 0; m2.e_end = E;
             m2.C = dXb; m2.ldc = H; m2.Cq = nullptr; m2.Cs = nullptr; m2.cs_rows = 0; m2.GU = nullptr;
+            m2.Cf = nullptr;
             TIMED(MOE_K_DGRAD_GATE_UP, s, launch_mx_gemm(m2, kEpiStore, grid, s));
         }
-        GemmArgs g2;  // dX = dG Wg^T + dU Wu^T
+        GemmArgs g2{};  // dX = dG Wg^T + dU Wu^T
         g2.A = dGU; g2.a_row_map = nullptr; g2.lda = 2 * I;
         g2.B = Wgu; g2.b_stride = (int64_t)H * 2 * I;
         g2.C = dXb; g2.ldc = H; g2.N = H; g2.K = 2 * I;
         g2.mt_start = mt; g2.hdr = hdr; g2.Et = Et;
-        g2.GU = nullptr; g2.e_begin = e_bf16; g2.e_end = Et;
+        g2.GU = nullptr; g2.e_begin = e_bf16; g2.e_end = Et; g2.GUf = nullptr; g2.Cf = nullptr;
         if (e_bf16 < Et)
             TIMED(p.mx ? MOE_K_SHARED_GEMM : MOE_K_DGRAD_GATE_UP, s, launch_grouped_gemm(g2, kEpiStore, grid, s));
 
-        RdispArgs rd;
+        RdispArgs rd{};
         rd.dX = dXb; rd.dgp = dgp; rd.tok_prow = tok_prow; rd.topk_idx = idx; rd.topk_w = gw; rd.WrT = WrT;
         rd.dsel = dsel; rd.dgate = dgate; rd.dx = dx; rd.t0 = t0; rd.H = H; rd.k = k; rd.ld = p.ld_tok_prow;
         rd.with_shared = p.shared ? 1 : 0; rd.nhb = H / 64;
         TIMED(MOE_K_COMBINE, s, launch_rdispatch(rd, Tm, s));
     }
-    WgradArgs wa;  // [dWg | dWu][e] = x_e^T [dG | dU]_e over every row of expert e
+    WgradArgs wa{};  // [dWg | dWu][e] = x_e^T [dG | dU]_e over every row of expert e
     wa.A = xgT_all; wa.B = dGUT_all; wa.ld = rp;
     wa.a_mb = (int64_t)H * rp * 2; wa.b_mb = (int64_t)2 * I * rp * 2;
     wa.M = H; wa.N = 2 * I; wa.n_split = I; wa.Et = Et; wa.nmb = p.nmb; wa.mt_ld = Et + 1; wa.mt = mt_all;
     wa.C0 = dWg; wa.C1 = dWu;
     wa.Cs0 = p.shared ? dWs : nullptr; wa.Cs1 = p.shared ? dWs + (size_t)H * I : nullptr;
     TIMED(MOE_K_WGRAD, s, launch_wgrad(wa, grid, s));
-    WgradArgs wd;  // dWd[e] = h_e^T dY_e
+    WgradArgs wd{};  // dWd[e] = h_e^T dY_e
     wd.A = HT_all; wd.B = dYT_all; wd.ld = rp;
     wd.a_mb = (int64_t)I * rp * 2; wd.b_mb = (int64_t)H * rp * 2;
     wd.M = I; wd.N = H; wd.n_split = H; wd.Et = Et; wd.nmb = p.nmb; wd.mt_ld = Et + 1; wd.mt = mt_all;
     wd.C0 = dWd; wd.C1 = nullptr;
     wd.Cs0 = p.shared ? dWs + (size_t)2 * H * I : nullptr; wd.Cs1 = nullptr;
     TIMED(MOE_K_WGRAD, s, launch_wgrad(wd, grid, s));
-    DwrArgs dr;
+    DwrArgs dr{};
     dr.xgT = xgT_all; dr.dsel = dsel_all; dr.mt = mt_all; dr.dWr = dWr; dr.ldt = rp;
     dr.x_mb = (int64_t)H * rp; dr.d_mb = rp; dr.H = H; dr.E = E; dr.nmb = p.nmb; dr.mt_ld = Et + 1;
     TIMED(MOE_K_OTHER, s, launch_dwr(dr, s));

@@ -13,6 +13,7 @@
 // bitwise reproducible.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "mxfp8.hpp"
 
 namespace moe {
 
@@ -73,12 +74,17 @@ __global__ __launch_bounds__(256) void rcomb_gather_kernel(RcombArgs p) {
         if (blockIdx.y == 0) p.dsel[prow] = 0.0f;
     }
     uint16_t dy[16];
+    float dyf[16];
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
-        dy[c] = f32_to_bf16_rne(w * d[c]);
+        dyf[c] = w * d[c];
+        dy[c] = f32_to_bf16_rne(dyf[c]);
         sY[c0 + c][r] = dy[c];
         sX[c0 + c][r] = f32_to_bf16_rne(xv[c]);
     }
+    if (p.dYq)  // MXFP8 operand of the down input-gradient GEMM, from the fp32 values
+        mx_quant_row64(dyf, tid & 3, p.dYq + (int64_t)prow * p.H + h0,
+                       (uint32_t*)(p.sdY + ((int64_t)(h0 / 64) * p.ldt + prow) * 4));
     {
         intx4* dst = (intx4*)(p.dY + (int64_t)prow * p.H + h0 + c0);
 #pragma unroll
@@ -147,16 +153,34 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdArgs p) {
     const int64_t prow = prow0 + r;
     const int I = p.I;
     float dh[16], g[16], u[16];
-    unpack16_bf16((const intx4*)(p.dH + prow * I + i0 + c0), dh);
-    unpack16_bf16((const intx4*)(p.GU + prow * 2 * I + i0 + c0), g);
-    unpack16_bf16((const intx4*)(p.GU + prow * 2 * I + I + i0 + c0), u);
+    if (p.dHf) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const floatx4 a = *(const floatx4*)(p.dHf + prow * I + i0 + c0 + 4 * q);
+            const floatx4 b = *(const floatx4*)(p.GUf + prow * 2 * I + i0 + c0 + 4 * q);
+            const floatx4 c = *(const floatx4*)(p.GUf + prow * 2 * I + I + i0 + c0 + 4 * q);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                dh[4 * q + e] = a[e];
+                g[4 * q + e] = b[e];
+                u[4 * q + e] = c[e];
+            }
+        }
+    } else {
+        unpack16_bf16((const intx4*)(p.dH + prow * I + i0 + c0), dh);
+        unpack16_bf16((const intx4*)(p.GU + prow * 2 * I + i0 + c0), g);
+        unpack16_bf16((const intx4*)(p.GU + prow * 2 * I + I + i0 + c0), u);
+    }
     uint16_t dg[16], du[16], hh[16];
+    float dgf[16], duf[16];
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
         const float sg = 1.0f / (1.0f + __expf(-g[c]));
         const float silu = g[c] * sg;
-        dg[c] = f32_to_bf16_rne(dh[c] * u[c] * (sg * (1.0f + g[c] * (1.0f - sg))));
-        du[c] = f32_to_bf16_rne(dh[c] * silu);
+        dgf[c] = dh[c] * u[c] * (sg * (1.0f + g[c] * (1.0f - sg)));
+        duf[c] = dh[c] * silu;
+        dg[c] = f32_to_bf16_rne(dgf[c]);
+        du[c] = f32_to_bf16_rne(duf[c]);
         hh[c] = f32_to_bf16_rne(silu * u[c]);
         sG[c0 + c][r] = dg[c];
         sU[c0 + c][r] = du[c];
@@ -164,6 +188,12 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdArgs p) {
     }
     pack16_bf16(dg, (intx4*)(p.dGU + prow * 2 * I + i0 + c0));
     pack16_bf16(du, (intx4*)(p.dGU + prow * 2 * I + I + i0 + c0));
+    if (p.dGUq) {  // MXFP8 operand of the gate|up input-gradient GEMM, from the fp32 values
+        mx_quant_row64(dgf, tid & 3, p.dGUq + prow * 2 * I + i0,
+                       (uint32_t*)(p.sdGU + ((int64_t)(i0 / 64) * p.ldt + prow) * 4));
+        mx_quant_row64(duf, tid & 3, p.dGUq + prow * 2 * I + I + i0,
+                       (uint32_t*)(p.sdGU + ((int64_t)((I + i0) / 64) * p.ldt + prow) * 4));
+    }
     __syncthreads();
     const int ic = tid >> 2, r0 = (tid & 3) * 16;
     uint16_t v[16];

@@ -229,7 +229,10 @@ void grouped_gemm_kernel(GemmArgs p) {
                             const float h = g / (1.0f + __expf(-g)) * u;
                             const int64_t row = prow0 + frag_row(i, r);
                             p.C[row * p.ldc + hcol] = f32_to_bf16_rne(h);
-                            if (p.GU) {
+                            if (p.GUf) {
+                                p.GUf[row * 2 * I + hcol] = g;
+                                p.GUf[row * 2 * I + I + hcol] = u;
+                            } else if (p.GU) {
                                 p.GU[row * 2 * I + hcol] = f32_to_bf16_rne(g);
                                 p.GU[row * 2 * I + I + hcol] = f32_to_bf16_rne(u);
                             }
@@ -244,8 +247,13 @@ void grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            p.C[(int64_t)(prow0 + frag_row(i, r)) * p.ldc + col] = f32_to_bf16_rne(acc[i][j][r]);
+                        for (int r = 0; r < 16; ++r) {
+                            const int64_t o = (int64_t)(prow0 + frag_row(i, r)) * p.ldc + col;
+                            if (p.Cf)
+                                p.Cf[o] = acc[i][j][r];
+                            else
+                                p.C[o] = f32_to_bf16_rne(acc[i][j][r]);
+                        }
                 }
             }
         }

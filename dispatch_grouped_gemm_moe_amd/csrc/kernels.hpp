@@ -42,9 +42,12 @@ struct GemmArgs {
     const int32_t* mt_start;   // [Et+1]
     const LayoutHeader* hdr;
     int Et;
-    // kEpiSwiGLU: optional [R_pad][2I] copy of g | u (kept for the backward).
+    // kEpiSwiGLU: optional [R_pad][2I] copy of g | u (kept for the backward),
+    // bf16 in GU or fp32 in GUf.
     uint16_t* GU;
     int e_begin, e_end;        // experts [e_begin, e_end) are processed
+    float* GUf;
+    float* Cf;                 // kEpiStore, optional: fp32 output instead of C
 };
 
 enum GemmEpilogue { kEpiSwiGLU = 0, kEpiStore = 1 };
@@ -72,7 +75,8 @@ struct MxGemmArgs {
     uint8_t* Cq;               // kEpiSwiGLU: h codes [R_pad][N/2]
     uint8_t* Cs;               // kEpiSwiGLU: h scales [N/2/64][cs_rows][4]
     int64_t cs_rows;
-    uint16_t* GU;              // kEpiSwiGLU, optional: bf16 g | u [R_pad][N] kept for the backward
+    float* GU;                 // kEpiSwiGLU, optional: fp32 g | u [R_pad][N] kept for the backward
+    float* Cf;                 // kEpiStore, optional: fp32 output instead of C
 };
 void launch_mx_gemm(const MxGemmArgs& a, GemmEpilogue epi, int grid, hipStream_t stream);
 // bf16 [rows][cols] -> E4M3 codes [rows][cols] and E8M0 scales; layout 0:
@@ -92,6 +96,12 @@ struct SwigluBwdArgs {
     uint16_t* HT;              // [I][ldt]     transposed h
     int I;
     int64_t ldt;
+    // MXFP8: fp32 inputs instead of dH / GU, and dG | dU also quantised along
+    // I from fp32: codes [R_pad][2I], scales [2I/64][ldt][4]
+    const float* dHf;
+    const float* GUf;
+    uint8_t* dGUq;
+    uint8_t* sdGU;
 };
 void launch_swiglu_bwd(const SwigluBwdArgs& a, int rpad, hipStream_t stream);
 
@@ -141,6 +151,10 @@ struct RcombArgs {
     float* dsel;               // [R_pad] zeroed
     int H, k, nhb;
     int64_t ldt;
+    // MXFP8, optional: dY quantised along H from fp32, codes [R_pad][H],
+    // scales [H/64][ldt][4]
+    uint8_t* dYq;
+    uint8_t* sdY;
 };
 void launch_rcomb_gather(const RcombArgs& a, int rpad, hipStream_t stream);
 

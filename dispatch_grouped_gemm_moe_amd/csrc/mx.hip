@@ -18,26 +18,13 @@
 // halves), and the E8M0 scale of (row m, block b) from lane m + 32 b.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "mxfp8.hpp"
 
 namespace moe {
 
 typedef int intx8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void gbl_cvoid;
-
-// smallest e with amax <= 448 * 2^e, clamped to [-127, 127]; 0 for amax = 0
-__device__ __forceinline__ int mx_scale_exp(float amax) {
-    if (!(amax > 0.0f)) return 0;
-    int p;
-    const float m = frexpf(amax, &p);  // amax = m * 2^p, m in [0.5, 1)
-    int e = p - 9 + (m > 0.875f ? 1 : 0);
-    return e < -127 ? -127 : (e > 127 ? 127 : e);
-}
-
-__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
-    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
-}
 
 // ---------------------------------------------------------------------------
 // quantiser: bf16 rows [rows][cols] -> E4M3 codes [rows][cols] + scales.
@@ -281,8 +268,8 @@ void mx_gemm_kernel(MxGemmArgs p) {
                         const int ex = mx_scale_exp(m);
                         const int row = prow0 + wm * 128 + i * 32 + (r >> 2) * 8 + 4 * half + (r & 3);
                         if (live && p.GU) {
-                            p.GU[(int64_t)row * p.N + hcol] = f32_to_bf16_rne(g);
-                            p.GU[(int64_t)row * p.N + I + hcol] = f32_to_bf16_rne(u);
+                            p.GU[(int64_t)row * p.N + hcol] = g;
+                            p.GU[(int64_t)row * p.N + I + hcol] = u;
                         }
                         if (live) {
                             const int q = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(h, -ex), 0.0f, 0, false);
@@ -305,7 +292,10 @@ void mx_gemm_kernel(MxGemmArgs p) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const int row = prow0 + wm * 128 + i * 32 + (r >> 2) * 8 + 4 * half + (r & 3);
-                            p.C[(int64_t)row * p.ldc + col] = f32_to_bf16_rne(acc[i][j][r]);
+                            if (p.Cf)
+                                p.Cf[(int64_t)row * p.ldc + col] = acc[i][j][r];
+                            else
+                                p.C[(int64_t)row * p.ldc + col] = f32_to_bf16_rne(acc[i][j][r]);
                         }
                 }
             }

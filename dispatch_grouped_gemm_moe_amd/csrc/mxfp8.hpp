@@ -1,0 +1,49 @@
+// MXFP8 element helpers shared by the quantising kernels: OCP Microscaling
+// v1.0 E4M3 elements with one E8M0 scale per 32 elements.
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+
+// smallest e with amax <= 448 * 2^e, clamped to [-127, 127]; 0 for amax = 0
+__device__ __forceinline__ int mx_scale_exp(float amax) {
+    if (!(amax > 0.0f)) return 0;
+    int p;
+    const float m = frexpf(amax, &p);  // amax = m * 2^p, m in [0.5, 1)
+    int e = p - 9 + (m > 0.875f ? 1 : 0);
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// four values -> four E4M3 codes (round to nearest even, saturating at 448)
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+// 16 consecutive values of one thread -> 16 codes scaled by 2^-e
+__device__ __forceinline__ intx4 fp8x16(const float* v, int e) {
+    intx4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        o[q] = (int)fp8x4(ldexpf(v[4 * q], -e), ldexpf(v[4 * q + 1], -e), ldexpf(v[4 * q + 2], -e),
+                          ldexpf(v[4 * q + 3], -e));
+    return o;
+}
+
+// A row's 64 values held as 16 per thread by four consecutive lanes (lane % 4 =
+// 16-column group): quantise along the row, write the 64 codes at `codes` (this
+// lane's 16 at codes + 16 * (lane % 4)) and the two block scales as one dword
+// {block 0, block 1, 0, 0} at `scale_dword` (GEMM operand scale layout).
+__device__ __forceinline__ void mx_quant_row64(const float* v, int lane4, uint8_t* codes, uint32_t* scale_dword) {
+    float m = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) m = fmaxf(m, fabsf(v[c]));
+    m = fmaxf(m, __shfl_xor(m, 1, kWave));  // lanes 0,1: block 0; lanes 2,3: block 1
+    const int e = mx_scale_exp(m);
+    *(intx4*)(codes + 16 * lane4) = fp8x16(v, e);
+    const int e_hi = __shfl_xor(e, 2, kWave);
+    if (lane4 == 0) *scale_dword = (uint32_t)(e + 127) | ((uint32_t)(e_hi + 127) << 8);
+}
+
+}  // namespace moe
