@@ -40,6 +40,10 @@ def main():
     ap.add_argument("--workload", default="h7168_i2048_e32_k8_bf16")
     ap.add_argument("--pass", dest="passes", choices=("fwd", "fwdbwd"), default="fwdbwd")
     ap.add_argument("--minibatch", type=int, default=None)
+    ap.add_argument("--comm-cus", type=int, default=0, help="combine workgroups of the layer kernel (0 = automatic)")
+    ap.add_argument("--ring-slots", type=int, default=0, help="ring slots (0 = automatic)")
+    ap.add_argument("--launch-per-gemm", action="store_true",
+                    help="forward as one launch per grouped GEMM instead of the persistent layer kernel")
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -86,9 +90,10 @@ def main():
     inp = make_inputs(w, with_dout=bwd)
     log("inputs drawn in %.1f s" % (time.time() - t_gen))
 
-    flags = moe.MOE_F_SHARED_EXPERT if w.shared_expert else 0
+    flags = (moe.MOE_F_SHARED_EXPERT if w.shared_expert else 0) | (moe.MOE_F_LAUNCH_PER_GEMM if args.launch_per_gemm else 0)
     cfg = moe.make_cfg(w.T, w.H, w.I, w.E, w.k, minibatch=w.minibatch, flags=flags,
-                       prec=moe.MOE_PREC_MXFP8 if mx else moe.MOE_PREC_BF16)
+                       prec=moe.MOE_PREC_MXFP8 if mx else moe.MOE_PREC_BF16,
+                       comm_cus=args.comm_cus, ring_slots=args.ring_slots)
     sizes = moe.moe_query_sizes(cfg)
     bufs = moe.alloc_buffers(cfg, with_saved=bwd)
     dev = lambda t: None if t is None else t.to("cuda").contiguous()
@@ -141,11 +146,14 @@ def main():
         flops.update({"dgrad_down": 2 * hr, "dgrad_gate_up": 4 * hr, "wgrad": 6 * hi})
     if mx and shared_rows:
         flops["shared_gemm"] = (12.0 if bwd else 6.0) * H * I * shared_rows
+    if kt["layer"][1] > 0:  # the persistent layer kernel runs both forward GEMMs (and combine)
+        flops["layer"] = flops.pop("gemm_gate_up") + flops.pop("gemm_down")
     symbol = {"gemm_gate_up": "mx_gemm_kernel<0>" if mx else "grouped_gemm_kernel<0>",
               "gemm_down": "mx_gemm_kernel<1>" if mx else "grouped_gemm_kernel<1>",
               "dgrad_down": "mx_gemm_kernel<1>" if mx else "grouped_gemm_kernel<1>",
               "dgrad_gate_up": "mx_gemm_kernel<1>" if mx else "grouped_gemm_kernel<1>",
-              "wgrad": "wgrad_kernel", "shared_gemm": "grouped_gemm_kernel (bf16 shared expert)"}
+              "wgrad": "wgrad_kernel", "shared_gemm": "grouped_gemm_kernel (bf16 shared expert)",
+              "layer": "mega_kernel<%s>" % ("true" if mx else "false")}
     by_sym = {}
     for kd, fl in flops.items():
         n, ms = kt[kd]
@@ -178,6 +186,8 @@ def main():
         "config": {"workload": w.name, "tokens": T, "hidden": H, "intermediate": I, "experts": E,
                    "top_k": k, "minibatch": sizes.minibatch, "minibatches": sizes.num_minibatches,
                    "router_bias": w.router_bias, "shared_expert": w.shared_expert,
+                   "ring_slots": sizes.ring_slots, "comm_cus": sizes.comm_cus,
+                   "forward": "per-GEMM launches" if kt["layer"][1] == 0 else "persistent layer kernel",
                    "pass": "forward+backward" if bwd else "forward"},
         "roofline": {"bound": "mfma", "kernel": "moe::" + dom, "roles": dom_roles,
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s",

@@ -19,6 +19,7 @@ MOE_OK, MOE_E_INVALID, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP, MOE_E_DEVI
 MOE_PREC_BF16, MOE_PREC_MXFP8 = 0, 1
 MOE_F_SHARED_EXPERT = 1 << 0
 MOE_F_IDENTITY_EXPERTS = 1 << 1
+MOE_F_LAUNCH_PER_GEMM = 1 << 2
 
 # every symbol include/moe.h declares
 EXPORTS = ("moe_status_string", "moe_abi_version", "moe_validate_cfg", "moe_query_sizes",
@@ -26,7 +27,7 @@ EXPORTS = ("moe_status_string", "moe_abi_version", "moe_validate_cfg", "moe_quer
            "moe_layer_bwd", "moe_read_device_status", "moe_mx_quantize", "moe_timing_enable",
            "moe_timing_read")
 KERNEL_KINDS = ("route", "layout", "gemm_gate_up", "gemm_down", "combine", "gather", "other", "wgrad",
-                "dgrad_down", "dgrad_gate_up", "shared_gemm")
+                "dgrad_down", "dgrad_gate_up", "shared_gemm", "layer")
 
 
 class moe_cfg(ctypes.Structure):
@@ -49,7 +50,7 @@ class moe_weights(ctypes.Structure):
 
 
 class moe_kernel_times(ctypes.Structure):
-    _fields_ = [("launches", ctypes.c_int32 * 11), ("ms", ctypes.c_double * 11), ("dropped", ctypes.c_int32)]
+    _fields_ = [("launches", ctypes.c_int32 * 12), ("ms", ctypes.c_double * 12), ("dropped", ctypes.c_int32)]
 
 
 class MoeError(RuntimeError):

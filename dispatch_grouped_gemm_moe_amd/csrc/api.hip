@@ -15,6 +15,8 @@ namespace {
 
 constexpr int kNumCUs = 256;      // MI355X compute units
 constexpr int kBalanceRows = 320;  // bf16 machine balance: ~2.5 PFLOP/s over 8 TB/s, in rows
+constexpr int kCommWorkers = 0;    // layer kernel: combine as tiles of the GEMM workgroups (no dedicated CUs)
+constexpr uint64_t kSpinTicks = 200000000;  // 2 s at the 100 MHz s_memrealtime clock: bound of every device wait
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
@@ -33,9 +35,12 @@ struct Plan {
     // Wg|Wu along I)
     size_t pk_w1q, pk_s1, pk_w2q, pk_s2, pk_wdq, pk_sd, pk_wguq, pk_sgu;
     bool mx;
-    // forward workspace (bytes)
-    size_t ws_status, ws_idx, ws_w, ws_slot0, slot_bytes, ws_fwd;
-    size_t sl_hdr, sl_mt, sl_prow_token, sl_tok_prow, sl_h, sl_y, sl_hq, sl_sh;
+    // forward workspace (bytes): routing, MXFP8 x, every minibatch's layout
+    // (first-tile maps [nmb][Et+1], then nmb blocks of lay_bytes), layer-kernel
+    // counters, ring slots (h, Y, MXFP8 h codes and scales)
+    size_t ws_status, ws_idx, ws_w, ws_mt, ws_lay0, ws_cnt, ws_slot0, slot_bytes, ws_fwd;
+    size_t sl_h, sl_y, sl_hq, sl_sh;
+    bool mega;  // forward through the persistent layer kernel
     size_t ws_xq, ws_sx;  // MXFP8 codes and scales of x
     // saved (bytes): routing, then per minibatch g|u [rpad][2I] (bf16, or fp32
     // under MXFP8) and Y [rpad][H]
@@ -51,7 +56,8 @@ moe_status validate(const moe_cfg* c) {
     if (c->T < 1 || c->E < 1 || c->k < 1 || c->k > c->E || c->H < 1 || c->I < 1) return MOE_E_INVALID;
     if (c->minibatch < 0 || c->ring_slots < 0 || c->comm_cus < 0) return MOE_E_INVALID;
     if (c->prec != MOE_PREC_BF16 && c->prec != MOE_PREC_MXFP8) return MOE_E_INVALID;
-    if (c->flags & ~(uint32_t)(MOE_F_SHARED_EXPERT | MOE_F_IDENTITY_EXPERTS)) return MOE_E_INVALID;
+    if (c->flags & ~(uint32_t)(MOE_F_SHARED_EXPERT | MOE_F_IDENTITY_EXPERTS | MOE_F_LAUNCH_PER_GEMM))
+        return MOE_E_INVALID;
     if (c->H % 64 || c->I % 64 || c->E > kMaxExperts || c->k > kMaxTopK) return MOE_E_UNSUPPORTED;
     if ((int64_t)c->T * c->k > (1ll << 30) || (int64_t)c->T * c->H > (1ll << 40)) return MOE_E_UNSUPPORTED;
     return MOE_OK;
@@ -87,9 +93,14 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     p->Et = c->E + (p->shared ? 1 : 0);
     p->Mb = c->minibatch > 0 ? (c->minibatch < c->T ? c->minibatch : c->T) : auto_minibatch(c);
     p->nmb = ceil_div(c->T, p->Mb);
-    p->slots = c->ring_slots > 0 ? c->ring_slots : 2;
+    p->slots = c->ring_slots > 0 ? c->ring_slots : 3;
     if (p->slots > p->nmb) p->slots = p->nmb;
-    p->comm_cus = c->comm_cus;
+    p->comm_cus = c->comm_cus > 0 ? c->comm_cus : kCommWorkers;  // dedicated combine workgroups
+    // The layer kernel's tile sequence runs gate|up(b+1) before down(b), so a
+    // ring of one slot would make gate|up(b+1) wait on a later tile.  MXFP8
+    // with the bf16 shared expert and identity experts take the per-GEMM path.
+    p->mega = !(c->flags & MOE_F_LAUNCH_PER_GEMM) && !p->identity && !(p->mx && p->shared) &&
+              (p->slots >= 2 || p->nmb == 1) && p->comm_cus < kNumCUs - 8;
     p->ld_tok_prow = c->k + (p->shared ? 1 : 0);
     const int64_t rows = (int64_t)p->Mb * p->ld_tok_prow;
     // sum over experts of ceil(c_e / BM) <= ceil(rows / BM) + Et - 1
@@ -124,12 +135,19 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
         p->ws_xq = o; o = align_up(o + (size_t)c->T * H);
         p->ws_sx = o; o = align_up(o + (size_t)(H / 64) * c->T * 4);
     }
+    {  // one minibatch's layout block (also used by the backward)
+        size_t l = 0;
+        p->ly_hdr = l; l = align_up(l + sizeof(LayoutHeader));
+        p->ly_prow_token = l; l = align_up(l + (size_t)p->rpad * 4);
+        p->ly_tok_prow = l; l = align_up(l + (size_t)p->Mb * p->ld_tok_prow * 4);
+        p->ly_prow_slot = l; l = align_up(l + (size_t)p->rpad * 4);
+        p->lay_bytes = l;
+    }
+    p->ws_mt = o; o = align_up(o + (size_t)p->nmb * (Et + 1) * 4);
+    p->ws_lay0 = o; o = align_up(o + (size_t)p->nmb * p->lay_bytes);
+    p->ws_cnt = o; o = align_up(o + (size_t)(3 * p->nmb + 1) * 4);
     p->ws_slot0 = o;
     o = 0;
-    p->sl_hdr = o; o = align_up(o + sizeof(LayoutHeader));
-    p->sl_mt = o; o = align_up(o + (Et + 1) * 4);
-    p->sl_prow_token = o; o = align_up(o + (size_t)p->rpad * 4);
-    p->sl_tok_prow = o; o = align_up(o + (size_t)p->Mb * p->ld_tok_prow * 4);
     p->sl_h = o; o = align_up(o + (size_t)p->rpad * I * 2);
     p->sl_y = o; o = align_up(o + (size_t)p->rpad * H * 2);
     if (p->mx) {
@@ -150,12 +168,6 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     o = kAlign;  // device status word
     p->wb_wrt = o; o = align_up(o + (size_t)c->E * H * 4);
     p->wb_mt = o; o = align_up(o + nmb * (Et + 1) * 4);
-    size_t l = 0;
-    p->ly_hdr = l; l = align_up(l + sizeof(LayoutHeader));
-    p->ly_prow_token = l; l = align_up(l + rp * 4);
-    p->ly_tok_prow = l; l = align_up(l + (size_t)p->Mb * p->ld_tok_prow * 4);
-    p->ly_prow_slot = l; l = align_up(l + rp * 4);
-    p->lay_bytes = l;
     p->wb_lay0 = o; o += nmb * p->lay_bytes;
     p->wb_dyt = o; o = align_up(o + nmb * H * rp * 2);
     p->wb_xgt = o; o = align_up(o + nmb * H * rp * 2);
@@ -178,6 +190,14 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
 }
 
 bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr & (a - 1)) == 0; }
+
+// Compute units of the current device (0 if the runtime cannot tell).
+int device_cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return n;
+}
 
 // Optional per-launch event timing (moe_timing_enable / moe_timing_read).
 struct Timing {
@@ -333,21 +353,90 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
     const uint8_t* pk = (const uint8_t*)w->packed;
     const uint16_t* W1t = (const uint16_t*)(pk + p.pk_w1t);
     const uint16_t* W2t = (const uint16_t*)(pk + p.pk_w2t);
-
-    TIMED(MOE_K_ROUTE, s, launch_route(x, w->Wr, w->bias, p.T, p.H, p.E, p.k, idx, gw, nullptr, s));
-    const int grid = kNumCUs;
+    int32_t* mt_all = (int32_t*)(wsb + p.ws_mt);
+    uint8_t* lay0 = wsb + p.ws_lay0;
     uint8_t* xq = wsb + p.ws_xq;
     uint8_t* sx = wsb + p.ws_sx;
+    const int grid = kNumCUs;
+
+    // route every token, then lay out every minibatch (one workgroup each)
+    TIMED(MOE_K_ROUTE, s, launch_route(x, w->Wr, w->bias, p.T, p.H, p.E, p.k, idx, gw, nullptr, s));
     if (p.mx && !p.identity)  // dispatch-side quantisation: every token row once, along H
         TIMED(MOE_K_GATHER, s, launch_mx_quant(x, p.T, p.H, 1, xq, sx, s));
+    {
+        LayoutOut o{};
+        o.hdr = (LayoutHeader*)(lay0 + p.ly_hdr);
+        o.mt_start = mt_all;
+        o.prow_token = (int32_t*)(lay0 + p.ly_prow_token);
+        o.tok_prow = (int32_t*)(lay0 + p.ly_tok_prow);
+        o.tok_prow_ld = p.ld_tok_prow;
+        LayoutStrides ls{};
+        ls.hdr = (int64_t)p.lay_bytes / (int64_t)sizeof(LayoutHeader);
+        ls.mt_start = p.Et + 1;
+        ls.prow_token = ls.tok_prow = (int64_t)p.lay_bytes / 4;
+        TIMED(MOE_K_LAYOUT, s, launch_layout_batched(idx, p.T, p.Mb, p.E, p.k, p.shared ? 1 : 0, o, ls, s));
+    }
+
+    // operands common to every minibatch
+    const int e_bf16 = p.mx ? p.E : 0;  // MXFP8 covers the routed experts; bf16 the rest
+    GemmArgs g1{};
+    g1.A = x; g1.lda = p.H; g1.B = W1t; g1.b_stride = (int64_t)2 * p.I * p.H;
+    g1.ldc = p.I; g1.N = 2 * p.I; g1.K = p.H; g1.Et = p.Et; g1.e_begin = e_bf16; g1.e_end = p.Et;
+    GemmArgs g2{};
+    g2.lda = p.I; g2.B = W2t; g2.b_stride = (int64_t)p.H * p.I;
+    g2.ldc = p.H; g2.N = p.H; g2.K = p.I; g2.Et = p.Et; g2.e_begin = e_bf16; g2.e_end = p.Et;
+    MxGemmArgs m1{};
+    MxGemmArgs m2{};
+    if (p.mx) {
+        m1.A = xq; m1.lda = p.H; m1.SA = sx; m1.sa_kstride = (int64_t)p.T * 4;
+        m1.B = pk + p.pk_w1q; m1.b_stride = (int64_t)2 * p.I * p.H;
+        m1.SB = pk + p.pk_s1; m1.sb_stride = (int64_t)(p.H / 64) * 2 * p.I * 4; m1.sb_kstride = (int64_t)2 * p.I * 4;
+        m1.N = 2 * p.I; m1.K = p.H; m1.e_begin = 0; m1.e_end = p.E; m1.cs_rows = p.rpad;
+        m2.lda = p.I; m2.sa_kstride = (int64_t)p.rpad * 4;
+        m2.B = pk + p.pk_w2q; m2.b_stride = (int64_t)p.H * p.I;
+        m2.SB = pk + p.pk_s2; m2.sb_stride = (int64_t)(p.I / 64) * p.H * 4; m2.sb_kstride = (int64_t)p.H * 4;
+        m2.N = p.H; m2.K = p.I; m2.e_begin = 0; m2.e_end = p.E; m2.ldc = p.H;
+    }
+
+    // one workgroup per CU: the combine workgroups, then a multiple of 8 GEMM
+    // workgroups (XCD-aware dealing)
+    // Combine tiles with Y in the ring need 3 slots (gate|up(b) waits on
+    // combine(b-2) otherwise, which follows it in the tile sequence).
+    const int ncu = device_cus();
+    const bool ring_ok = p.comm_cus > 0 || saved || p.slots >= 3 || p.nmb <= p.slots;
+    if (p.mega && ring_ok && ncu >= p.comm_cus + 16) {
+        MegaArgs a{};
+        a.T = p.T; a.H = p.H; a.I = p.I; a.k = p.k; a.Mb = p.Mb; a.nmb = p.nmb; a.S = p.slots;
+        a.comm = p.comm_cus; a.e_end = p.mx ? p.E : p.Et; a.with_shared = p.shared ? 1 : 0;
+        a.ld_tok_prow = p.ld_tok_prow; a.mx = p.mx ? 1 : 0;
+        a.lay0 = lay0; a.lay_bytes = p.lay_bytes; a.ly_prow_token = p.ly_prow_token; a.ly_tok_prow = p.ly_tok_prow;
+        a.mt_all = mt_all; a.mt_ld = p.Et + 1;
+        a.g1 = g1; a.g2 = g2; a.m1 = m1; a.m2 = m2;
+        a.g1.e_begin = a.g2.e_begin = 0;
+        a.slot0 = wsb + p.ws_slot0; a.slot_bytes = p.slot_bytes;
+        a.sl_h = p.sl_h; a.sl_y = p.sl_y; a.sl_hq = p.sl_hq; a.sl_sh = p.sl_sh;
+        a.saved_mb0 = saved ? (uint8_t*)saved + p.sv_mb0 : nullptr;
+        a.sv_mb = p.sv_mb; a.sv_y = p.sv_y;
+        a.gw = gw; a.out = out;
+        a.counters = (int*)(wsb + p.ws_cnt);
+        a.status = (int*)(wsb + p.ws_status);
+        a.spin_ticks = kSpinTicks;
+        const int mgrid = p.comm_cus + ((ncu - p.comm_cus) / 8) * 8;
+        hipError_t err = hipSuccess;
+        TIMED(MOE_K_LAYER, s, err = launch_mega(a, mgrid, s));
+        if (err != hipSuccess) return MOE_E_HIP;
+        return check_launch();
+    }
+
     for (int b = 0; b < p.nmb; ++b) {
         const int t0 = b * p.Mb;
         const int Tm = (p.T - t0) < p.Mb ? (p.T - t0) : p.Mb;
+        uint8_t* lay = lay0 + (size_t)b * p.lay_bytes;
+        LayoutHeader* hdr = (LayoutHeader*)(lay + p.ly_hdr);
+        int32_t* mt = mt_all + (size_t)b * (p.Et + 1);
+        int32_t* prow_token = (int32_t*)(lay + p.ly_prow_token);
+        int32_t* tok_prow = (int32_t*)(lay + p.ly_tok_prow);
         uint8_t* slot = wsb + p.ws_slot0 + (size_t)(b % p.slots) * p.slot_bytes;
-        LayoutHeader* hdr = (LayoutHeader*)(slot + p.sl_hdr);
-        int32_t* mt = (int32_t*)(slot + p.sl_mt);
-        int32_t* prow_token = (int32_t*)(slot + p.sl_prow_token);
-        int32_t* tok_prow = (int32_t*)(slot + p.sl_tok_prow);
         uint16_t* hbuf = (uint16_t*)(slot + p.sl_h);
         uint16_t* ybuf = (uint16_t*)(slot + p.sl_y);
         uint16_t* gubuf = nullptr;
@@ -361,58 +450,29 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             ybuf = (uint16_t*)(mb + p.sv_y);
         }
 
-        LayoutOut o;
-        memset(&o, 0, sizeof(o));
-        o.hdr = hdr;
-        o.mt_start = mt;
-        o.prow_token = prow_token;
-        o.tok_prow = tok_prow;
-        o.tok_prow_ld = p.ld_tok_prow;
-        o.token_base = t0;
-        TIMED(MOE_K_LAYOUT, s, launch_layout(idx + (size_t)t0 * p.k, Tm, p.E, p.k, p.shared ? 1 : 0, o, s));
-
         if (p.identity) {
             TIMED(MOE_K_GATHER, s, launch_gather_rows(x, p.H, prow_token, hdr, (int)p.rpad, ybuf, p.H, s));
         } else {
-            const int e_bf16 = p.mx ? p.E : 0;  // MXFP8 covers the routed experts; bf16 the rest
             if (p.mx) {
-                MxGemmArgs m1{};
-                m1.A = xq; m1.a_row_map = prow_token; m1.lda = p.H; m1.SA = sx; m1.sa_kstride = (int64_t)p.T * 4;
-                m1.B = pk + p.pk_w1q; m1.b_stride = (int64_t)2 * p.I * p.H;
-                m1.SB = pk + p.pk_s1; m1.sb_stride = (int64_t)(p.H / 64) * 2 * p.I * 4; m1.sb_kstride = (int64_t)2 * p.I * 4;
-                m1.N = 2 * p.I; m1.K = p.H; m1.mt_start = mt; m1.hdr = hdr; m1.e_begin = 0; m1.e_end = p.E;
-                m1.C = nullptr; m1.ldc = 0;
-                m1.Cq = slot + p.sl_hq; m1.Cs = slot + p.sl_sh; m1.cs_rows = p.rpad; m1.GU = guf; m1.Cf = nullptr;
-                TIMED(MOE_K_GEMM_GATE_UP, s, launch_mx_gemm(m1, kEpiSwiGLU, grid, s));
+                MxGemmArgs m = m1;
+                m.a_row_map = prow_token; m.mt_start = mt; m.hdr = hdr;
+                m.Cq = slot + p.sl_hq; m.Cs = slot + p.sl_sh; m.GU = guf;
+                TIMED(MOE_K_GEMM_GATE_UP, s, launch_mx_gemm(m, kEpiSwiGLU, grid, s));
             }
-            GemmArgs g1{};
-            g1.A = x; g1.a_row_map = prow_token; g1.lda = p.H;
-            g1.B = W1t; g1.b_stride = (int64_t)2 * p.I * p.H;
-            g1.C = hbuf; g1.ldc = p.I;
-            g1.N = 2 * p.I; g1.K = p.H;
-            g1.mt_start = mt; g1.hdr = hdr; g1.Et = p.Et;
-            g1.GU = gubuf; g1.e_begin = e_bf16; g1.e_end = p.Et; g1.GUf = guf; g1.Cf = nullptr;
+            GemmArgs ga = g1;
+            ga.a_row_map = prow_token; ga.mt_start = mt; ga.hdr = hdr;
+            ga.C = hbuf; ga.GU = gubuf; ga.GUf = guf;
             if (e_bf16 < p.Et)
-                TIMED(p.mx ? MOE_K_SHARED_GEMM : MOE_K_GEMM_GATE_UP, s, launch_grouped_gemm(g1, kEpiSwiGLU, grid, s));
+                TIMED(p.mx ? MOE_K_SHARED_GEMM : MOE_K_GEMM_GATE_UP, s, launch_grouped_gemm(ga, kEpiSwiGLU, grid, s));
             if (p.mx) {
-                MxGemmArgs m2{};
-                m2.A = slot + p.sl_hq; m2.a_row_map = nullptr; m2.lda = p.I;
-                m2.SA = slot + p.sl_sh; m2.sa_kstride = (int64_t)p.rpad * 4;
-                m2.B = pk + p.pk_w2q; m2.b_stride = (int64_t)p.H * p.I;
-                m2.SB = pk + p.pk_s2; m2.sb_stride = (int64_t)(p.I / 64) * p.H * 4; m2.sb_kstride = (int64_t)p.H * 4;
-                m2.N = p.H; m2.K = p.I; m2.mt_start = mt; m2.hdr = hdr; m2.e_begin = 0; m2.e_end = p.E;
-                m2.C = ybuf; m2.ldc = p.H; m2.Cq = nullptr; m2.Cs = nullptr; m2.cs_rows = 0; m2.GU = nullptr; m2.Cf = nullptr;
-                TIMED(MOE_K_GEMM_DOWN, s, launch_mx_gemm(m2, kEpiStore, grid, s));
+                MxGemmArgs m = m2;
+                m.A = slot + p.sl_hq; m.SA = slot + p.sl_sh; m.mt_start = mt; m.hdr = hdr; m.C = ybuf;
+                TIMED(MOE_K_GEMM_DOWN, s, launch_mx_gemm(m, kEpiStore, grid, s));
             }
-            GemmArgs g2{};
-            g2.A = hbuf; g2.a_row_map = nullptr; g2.lda = p.I;
-            g2.B = W2t; g2.b_stride = (int64_t)p.H * p.I;
-            g2.C = ybuf; g2.ldc = p.H;
-            g2.N = p.H; g2.K = p.I;
-            g2.mt_start = mt; g2.hdr = hdr; g2.Et = p.Et;
-            g2.GU = nullptr; g2.e_begin = e_bf16; g2.e_end = p.Et; g2.GUf = nullptr; g2.Cf = nullptr;
+            GemmArgs gb = g2;
+            gb.A = hbuf; gb.mt_start = mt; gb.hdr = hdr; gb.C = ybuf;
             if (e_bf16 < p.Et)
-                TIMED(p.mx ? MOE_K_SHARED_GEMM : MOE_K_GEMM_DOWN, s, launch_grouped_gemm(g2, kEpiStore, grid, s));
+                TIMED(p.mx ? MOE_K_SHARED_GEMM : MOE_K_GEMM_DOWN, s, launch_grouped_gemm(gb, kEpiStore, grid, s));
         }
         TIMED(MOE_K_COMBINE, s,
               launch_combine(ybuf, p.H, tok_prow, p.ld_tok_prow, gw + (size_t)t0 * p.k, p.k,
@@ -461,6 +521,21 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
     const int grid = kNumCUs;
 
     TIMED(MOE_K_OTHER, s, launch_transpose_f32(w->Wr, H, E, WrT, s));
+    {  // every minibatch's layout, with the slot of each padded row
+        uint8_t* lay0 = wsb + p.wb_lay0;
+        LayoutOut o{};
+        o.hdr = (LayoutHeader*)(lay0 + p.ly_hdr);
+        o.mt_start = mt_all;
+        o.prow_token = (int32_t*)(lay0 + p.ly_prow_token);
+        o.tok_prow = (int32_t*)(lay0 + p.ly_tok_prow);
+        o.prow_slot = (int32_t*)(lay0 + p.ly_prow_slot);
+        o.tok_prow_ld = p.ld_tok_prow;
+        LayoutStrides ls{};
+        ls.hdr = (int64_t)p.lay_bytes / (int64_t)sizeof(LayoutHeader);
+        ls.mt_start = Et + 1;
+        ls.prow_token = ls.tok_prow = ls.prow_slot = (int64_t)p.lay_bytes / 4;
+        TIMED(MOE_K_LAYOUT, s, launch_layout_batched(idx, p.T, p.Mb, E, k, p.shared ? 1 : 0, o, ls, s));
+    }
     for (int b = 0; b < p.nmb; ++b) {
         const int t0 = b * p.Mb;
         const int Tm = (p.T - t0) < p.Mb ? (p.T - t0) : p.Mb;
@@ -479,11 +554,6 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
         uint16_t* HT = HT_all + (size_t)b * I * rp;
         float* dsel = dsel_all + (size_t)b * rp;
 
-        LayoutOut o;
-        memset(&o, 0, sizeof(o));
-        o.hdr = hdr; o.mt_start = mt; o.prow_token = prow_token; o.tok_prow = tok_prow;
-        o.prow_slot = prow_slot; o.tok_prow_ld = p.ld_tok_prow; o.token_base = t0;
-        TIMED(MOE_K_LAYOUT, s, launch_layout(idx + (size_t)t0 * k, Tm, E, k, p.shared ? 1 : 0, o, s));
 
         RcombArgs rc{};
         rc.dout = dout; rc.x = x; rc.Y = Yb; rc.topk_w = gw; rc.prow_token = prow_token;

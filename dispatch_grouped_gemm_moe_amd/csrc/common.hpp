@@ -54,4 +54,11 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
 
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) const void gbl_cvoid;
+typedef int intx8 __attribute__((ext_vector_type(8)));
+
+// Scheduling masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMFMA = 0x008, kSchedVMEM = 0x020, kSchedDSRead = 0x100;
+
 }  // namespace moe

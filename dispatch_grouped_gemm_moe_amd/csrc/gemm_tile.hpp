@@ -1,0 +1,359 @@
+// Tile-level building blocks of the bf16 grouped GEMMs, shared by the
+// one-launch-per-GEMM kernels and the persistent layer kernel.
+#pragma once
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+// LDS ring of kStages pipeline stages; a stage holds the A tile [BM][BK] then
+// the B tile [BN][BK] (bf16, BK = 32: 64-byte rows of four 16-byte chunks).
+// Chunk c of row r sits at position c ^ f(r), f(r) = (r >> 2) & 3.  With this
+// swizzle the 128-bit fragment reads (lane l: row l%32, chunk 2*kstep + l/32)
+// are free of bank conflicts on gfx950's LDS; swizzles that also mix in row
+// bit 1 (or use r & 3) measured 2-way conflicted with rocprofv3's
+// SQ_LDS_BANK_CONFLICT, as did unswizzled rows.
+constexpr int kBK = 32;
+constexpr int kRowBytes = kBK * 2;
+constexpr int kStageA = BM * kRowBytes;
+constexpr int kStageBytes = (BM + BN) * kRowBytes;
+constexpr int kStages = 5;  // 160 KB of LDS: loads run up to 4 K steps ahead
+
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+
+__device__ __forceinline__ void mfma_block(floatx16 (&acc)[4][4], const bf16x8 (&a)[4], const bf16x8 (&b)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+}
+
+// Wait until at most c K steps (8 loads each) of this wave are in flight and
+// all of its LDS reads are done.  c is clamped to [0, kStages-1].
+__device__ __forceinline__ void wait_vm_steps(int c) {
+    switch (c < 0 ? 0 : c) {
+        case 0: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); break;
+        case 1: asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory"); break;
+        case 2: asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory"); break;
+        case 3: asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)" ::: "memory"); break;
+        default: asm volatile("s_waitcnt vmcnt(32) lgkmcnt(0)" ::: "memory"); break;
+    }
+}
+static_assert(kStages <= 5, "wait_vm_steps covers at most 4 steps in flight");
+
+// K sequence of a dense GEMM: K step kt sits kt * 64 bytes into every row.
+struct DenseK {
+    int kt = 0;
+    __device__ __forceinline__ void next(int64_t& a_off, int64_t& b_off) {
+        a_off = b_off = (int64_t)kt * kBK * 2;
+        ++kt;
+    }
+};
+
+// One 256 x 256 output tile: acc = A_tile * B_tile^T over KT K steps.
+// a_base/b_base + aoff[i]/boff[i] address the 4 A and 4 B rows this lane
+// stages (tile rows wave*64 + 16i + lane/4, swizzled chunk); kit.next() gives
+// the byte offset of each successive K step, called in K order.
+template <class KIt>
+__device__ __forceinline__ void tile_mainloop(floatx16 (&acc)[4][4], uint8_t* smem, const char* a_base,
+                                              const uint32_t (&aoff)[4], const char* b_base,
+                                              const uint32_t (&boff)[4], int KT, KIt kit) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
+    if (KT <= 0) return;
+
+    auto issue = [&](int kt) {
+        int64_t ka, kb;
+        kit.next(ka, kb);
+        uint8_t* base = smem + (kt % kStages) * kStageBytes + (wave * 64) * kRowBytes;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_global_load_lds((gbl_cvoid*)(a_base + ka + aoff[i]), (lds_void*)(base + i * 1024), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_global_load_lds((gbl_cvoid*)(b_base + kb + boff[i]), (lds_void*)(base + kStageA + i * 1024), 16, 0, 0);
+    };
+    // MFMA operand fragments of k-step kk (16 deep) of K step kt.
+    const int fr = lane & 31;
+    const int arow_b = (wm * 128 + fr) * kRowBytes, brow_b = kStageA + (wn * 128 + fr) * kRowBytes;
+    const int fsw = swz(fr);
+    auto frags = [&](int kt, int kk, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
+        const uint8_t* st = smem + (kt % kStages) * kStageBytes;
+        const int pc = ((kk * 2 + (lane >> 5)) ^ fsw) * 16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8*)(st + arow_b + i * 32 * kRowBytes + pc);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = *(const bf16x8*)(st + brow_b + j * 32 * kRowBytes + pc);
+    };
+
+    // Ring protocol (S = kStages slots, K step j lives in slot j % S, each
+    // step is 8 direct-to-LDS loads per lane, counted by vmcnt):
+    //  - prologue: issue steps 0..min(S,KT)-1, wait for step 0;
+    //  - K step kt: before the barrier wait for step kt+1, i.e. allow the
+    //    c = min(KT-2-kt, S-2) newer steps in flight (vmcnt(8c)), and for this
+    //    wave's own LDS reads of step kt (lgkmcnt(0)); after the barrier no
+    //    wave reads step kt any more, so its slot takes step kt+S.
+    // First the previous tile's stores leave the vmcnt count and every wave is
+    // done reading the previous tile's stages.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kStages; ++j)
+        if (j < KT) issue(j);
+    wait_vm_steps(KT - 1 < kStages - 1 ? KT - 1 : kStages - 1);
+    __syncthreads();
+    bf16x8 a0[4], b0[4], a1[4], b1[4];
+    frags(0, 0, a0, b0);
+    for (int kt = 0; kt < KT; ++kt) {
+        // k-step 0 of this K step: read k-step 1's fragments under 16 MFMAs
+        frags(kt, 1, a1, b1);
+        mfma_block(acc, a0, b0);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 8, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        // Every wave has read step kt (its reads done) and step kt+1 has
+        // landed: refill step kt's slot with step kt+kStages and read step
+        // kt+1's first fragments under the last 16 MFMAs.
+        const int ahead = KT - 2 - kt;
+        wait_vm_steps(ahead < kStages - 2 ? ahead : kStages - 2);
+        __syncthreads();
+        if (kt + kStages < KT) issue(kt + kStages);
+        frags(kt + 1, 0, a0, b0);  // a stale but in-bounds read after the last step
+        mfma_block(acc, a1, b1);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedVMEM, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 8, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// Accumulator element r of fragment (i, j) of lane l sits in tile row
+// wm*128 + 32i + 8(r/4) + 4(l/32) + r%4 and tile column wn*128 + 32j + l%32.
+__device__ __forceinline__ int frag_row(int i, int r) {
+    const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) >> 1;
+    return wm * 128 + i * 32 + (r >> 2) * 8 + 4 * (lane >> 5) + (r & 3);
+}
+__device__ __forceinline__ int frag_col(int j) {
+    const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
+    return wn * 128 + j * 32 + (lane & 31);
+}
+
+// Tile coordinates of tile v of a grouped GEMM over experts [e_begin, e_end):
+// expert-major, then N tile, then M tile (M fastest).
+__device__ __forceinline__ void tile_coords(const int32_t* mt_start, int e_begin, int e_end, int NT, int v,
+                                            int& e, int& ml, int& ntile) {
+    const int mt_lo = mt_start[e_begin];
+    int lo = e_begin, hi = e_end - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((mt_start[mid] - mt_lo) * NT <= v) lo = mid; else hi = mid - 1;
+    }
+    e = lo;
+    const int mt0 = mt_start[e], mte = mt_start[e + 1] - mt0;
+    const int loc = v - (mt0 - mt_lo) * NT;
+    ntile = loc / mte;
+    ml = loc - ntile * mte;
+}
+
+// Tiles of a grouped GEMM (M tiles of all processed experts times N tiles).
+__device__ __forceinline__ int grouped_tiles(const int32_t* mt_start, int e_begin, int e_end, int N) {
+    return (mt_start[e_end] - mt_start[e_begin]) * ceil_div(N, BN);
+}
+
+// One 256 x 256 output tile (expert e, M tile ml of the expert, N tile ntile)
+// of the bf16 grouped GEMM with its epilogue; smem is the kStages LDS ring.
+template <int EPI>
+__device__ __forceinline__ void gemm_tile(const GemmArgs p, int e, int ml, int ntile, uint8_t* smem) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int KT = p.K / kBK;
+    const int mt0 = p.mt_start[e];
+    const int prow0 = (mt0 + ml) * BM;
+    const int n0 = ntile * BN;
+
+    // Byte offsets of the 4 A rows and 4 B rows this lane stages per K step:
+    // instruction i fills tile rows wave*64 + 16i .. +15 (lane/4 picks the row,
+    // lane%4 the fixed LDS chunk; the lane loads the logical chunk stored there).
+    uint32_t aoff[4], boff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = wave * 64 + i * 16 + (lane >> 2);
+        const int lchunk = (lane & 3) ^ swz(r);
+        const int prow = prow0 + r;
+        const int arow = p.a_row_map ? p.a_row_map[prow] : prow;
+        aoff[i] = (uint32_t)(((int64_t)arow * p.lda + lchunk * 8) * 2);
+        const int n = min(n0 + r, p.N - 1);
+        boff[i] = (uint32_t)(((int64_t)n * p.K + lchunk * 8) * 2);
+    }
+    floatx16 acc[4][4];
+    tile_mainloop(acc, smem, (const char*)p.A, aoff, (const char*)(p.B + (int64_t)e * p.b_stride), boff, KT,
+                  DenseK{});
+
+    if (EPI == kEpiSwiGLU) {
+        // columns come in 64-wide groups of 32 gate then 32 up columns
+        const int I = p.N / 2;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int hcol = n0 / 2 + (wave & 1) * 64 + jj * 32 + (lane & 31);
+            if (hcol < I) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float g = acc[i][2 * jj][r], u = acc[i][2 * jj + 1][r];
+                        const float h = g / (1.0f + __expf(-g)) * u;
+                        const int64_t row = prow0 + frag_row(i, r);
+                        p.C[row * p.ldc + hcol] = f32_to_bf16_rne(h);
+                        if (p.GUf) {
+                            p.GUf[row * 2 * I + hcol] = g;
+                            p.GUf[row * 2 * I + I + hcol] = u;
+                        } else if (p.GU) {
+                            p.GU[row * 2 * I + hcol] = f32_to_bf16_rne(g);
+                            p.GU[row * 2 * I + I + hcol] = f32_to_bf16_rne(u);
+                        }
+                    }
+            }
+        }
+    } else if (p.Cf) {  // kEpiStore, fp32 output
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int col = n0 + frag_col(j);
+            if (col < p.N) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) p.Cf[(int64_t)(prow0 + frag_row(i, r)) * p.ldc + col] = acc[i][j][r];
+            }
+        }
+    } else {  // kEpiStore, bf16 output
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int col = n0 + frag_col(j);
+            if (col < p.N) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        p.C[(int64_t)(prow0 + frag_row(i, r)) * p.ldc + col] = f32_to_bf16_rne(acc[i][j][r]);
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void bf16x8_to_f32(const intx4 raw, float* f) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t v = (uint32_t)raw[q];
+        f[2 * q] = __builtin_bit_cast(float, v << 16);
+        f[2 * q + 1] = __builtin_bit_cast(float, v & 0xffff0000u);
+    }
+}
+
+// Combine of one token by nthreads threads (thread index tid):
+//   out[h] = bf16( sum_j fmaf(w[j], Y[rows[j]][h]) (+ Y[rows[k]][h]) ), j ascending,
+// the routed slots first in slot order, then the shared expert's row.
+__device__ __forceinline__ void combine_token(const uint16_t* __restrict__ Y, int64_t ldy, const int* rows,
+                                              const float* w, int k, int with_shared, int H,
+                                              uint16_t* __restrict__ out, int tid, int nthreads) {
+    for (int c = tid; c < H / 8; c += nthreads) {
+        float acc[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+        for (int j = 0; j < k; ++j) {
+            float y[8];
+            bf16x8_to_f32(*(const intx4*)(Y + (int64_t)rows[j] * ldy + c * 8), y);
+            const float wj = w[j];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[q] = __builtin_fmaf(wj, y[q], acc[q]);
+        }
+        if (with_shared) {
+            float y[8];
+            bf16x8_to_f32(*(const intx4*)(Y + (int64_t)rows[k] * ldy + c * 8), y);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[q] = acc[q] + y[q];
+        }
+        intx4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            o[q] = (int)((uint32_t)f32_to_bf16_rne(acc[2 * q]) | ((uint32_t)f32_to_bf16_rne(acc[2 * q + 1]) << 16));
+        *(intx4*)(out + c * 8) = o;
+    }
+}
+
+// Combine of up to kTok tokens by one workgroup, every load of a chunk issued
+// before its arithmetic (memory-level parallelism for the few workgroups of
+// the layer kernel's combine role).  rows[t][kMaxTopK + 1], w[t][kMaxTopK];
+// tokens t < ntok are written to out_rows[t].  Same arithmetic per element as
+// combine_token.
+template <int kTok>
+__device__ __forceinline__ void combine_tokens_mlp(const uint16_t* __restrict__ Y, int64_t ldy, const int (*rows)[kMaxTopK + 1],
+                                                   const float (*w)[kMaxTopK], int ntok, int k, int with_shared, int H,
+                                                   uint16_t* const* out_rows, int tid, int nthreads) {
+    for (int c = tid; c < H / 8; c += nthreads) {
+        float acc[kTok][8];
+#pragma unroll
+        for (int t = 0; t < kTok; ++t)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[t][q] = 0.0f;
+        int j = 0;
+        for (; j + 4 <= k; j += 4) {  // 4 slots x kTok tokens of loads in flight
+            intx4 raw[kTok][4];
+#pragma unroll
+            for (int t = 0; t < kTok; ++t)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    raw[t][u] = t < ntok ? *(const intx4*)(Y + (int64_t)rows[t][j + u] * ldy + c * 8) : intx4{};
+#pragma unroll
+            for (int t = 0; t < kTok; ++t)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    float y[8];
+                    bf16x8_to_f32(raw[t][u], y);
+                    const float wj = w[t][j + u];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) acc[t][q] = __builtin_fmaf(wj, y[q], acc[t][q]);
+                }
+        }
+        for (; j < k; ++j) {
+#pragma unroll
+            for (int t = 0; t < kTok; ++t) {
+                if (t >= ntok) continue;
+                float y[8];
+                bf16x8_to_f32(*(const intx4*)(Y + (int64_t)rows[t][j] * ldy + c * 8), y);
+                const float wj = w[t][j];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc[t][q] = __builtin_fmaf(wj, y[q], acc[t][q]);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < kTok; ++t) {
+            if (t >= ntok) continue;
+            if (with_shared) {
+                float y[8];
+                bf16x8_to_f32(*(const intx4*)(Y + (int64_t)rows[t][k] * ldy + c * 8), y);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc[t][q] = acc[t][q] + y[q];
+            }
+            intx4 o;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                o[q] = (int)((uint32_t)f32_to_bf16_rne(acc[t][2 * q]) | ((uint32_t)f32_to_bf16_rne(acc[t][2 * q + 1]) << 16));
+            *(intx4*)(out_rows[t] + c * 8) = o;
+        }
+    }
+}
+
+}  // namespace moe

@@ -29,6 +29,16 @@ void launch_route(const uint16_t* x, const float* Wr, const float* bias, int T, 
 void launch_layout(const int32_t* idx, int Tm, int E, int k, int with_shared, const LayoutOut& o,
                    hipStream_t stream);
 
+// Element strides between consecutive minibatches' copies of each LayoutOut
+// array (hdr in LayoutHeader units).
+struct LayoutStrides {
+    int64_t counts, offsets, row_token, tok_row, hdr, mt_start, prow_token, tok_prow, prow_slot;
+};
+// Every minibatch of Mb tokens (the last one possibly shorter) in one launch,
+// one workgroup each; o holds minibatch 0's pointers.
+void launch_layout_batched(const int32_t* idx, int T, int Mb, int E, int k, int with_shared, const LayoutOut& o,
+                           const LayoutStrides& st, hipStream_t stream);
+
 // Grouped GEMM over the experts of one minibatch: C[prow, n] = sum_k A[row(prow), k] * B[e][n][k].
 struct GemmArgs {
     const uint16_t* A;         // activation rows (bf16)
@@ -84,6 +94,35 @@ void launch_mx_gemm(const MxGemmArgs& a, GemmEpilogue epi, int grid, hipStream_t
 // With hdr, rows from hdr->m_tiles * BM on are skipped.
 void launch_mx_quant(const uint16_t* src, int64_t rows, int cols, int layout, uint8_t* codes, uint8_t* scales,
                      hipStream_t stream, const LayoutHeader* hdr = nullptr);
+
+// Persistent layer kernel (expert GEMMs of every minibatch + combine), see
+// mega.hip.  Layouts of every minibatch are precomputed: minibatch b's header
+// sits at lay0 + b * lay_bytes, its prow_token / tok_prow at + ly_prow_token /
+// + ly_tok_prow, its first-tile map at mt_all + b * mt_ld.  g1/g2 (bf16) or
+// m1/m2 (MXFP8) carry the per-layer operands; the per-minibatch pointers are
+// filled in by the kernel.  counters: 3 * nmb + 1 ints (per-minibatch gate|up,
+// down and combine progress, then the launch's abort word; zeroed by
+// launch_mega).  Wait sites recorded in the status detail: 0 ring slot (down),
+// 1 ring slot (combine), 2 combine input, 3 down input.
+struct MegaArgs {
+    int T, H, I, k, Mb, nmb, S, comm, e_end, with_shared, ld_tok_prow, mx;
+    const uint8_t* lay0;
+    int64_t lay_bytes, ly_prow_token, ly_tok_prow;
+    const int32_t* mt_all;
+    int mt_ld;
+    GemmArgs g1, g2;
+    MxGemmArgs m1, m2;
+    uint8_t* slot0;  // ring slot s at slot0 + s * slot_bytes: h (+ hq, sh), Y
+    int64_t slot_bytes, sl_h, sl_y, sl_hq, sl_sh;
+    uint8_t* saved_mb0;  // NULL: Y lives in the ring; else minibatch b's g|u at + b * sv_mb, Y at + sv_y
+    int64_t sv_mb, sv_y;
+    const float* gw;
+    uint16_t* out;
+    int* counters;
+    int* status;
+    uint64_t spin_ticks;  // bound of every wait, in s_memrealtime ticks (100 MHz)
+};
+hipError_t launch_mega(const MegaArgs& a, int grid, hipStream_t stream);
 
 // Backward SwiGLU over the padded rows of one minibatch, from dH and the saved
 // g | u:  dG = dH * u * silu'(g), dU = dH * silu(g), h = silu(g) * u.

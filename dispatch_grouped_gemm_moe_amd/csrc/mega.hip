@@ -1,0 +1,294 @@
+// Persistent layer kernel: the expert FFN of every minibatch and its combine
+// in one cooperative launch.
+//
+// MoK runs the MoE layer as one persistent megakernel: a few SMs move tokens
+// (dispatch / combine) while the rest run the grouped GEMMs, the two sides
+// signal each other through counters in device memory with no host round
+// trip, a fixed ring of token slots is reused as soon as combine has drained
+// one, and a minibatch is sized so the GEMM side keeps at least two full waves
+// of tiles (KuCoin flash "Cursor's MoK achieves 2.37x performance boost on
+// NVIDIA GB300 NVL72", sections 01-03; RuntimeWire "Cursor open-sources MoK",
+// "Rebuilding the MoE layer around communication").
+//
+// On one MI355X the layout of every minibatch is computed before this launch
+// (one workgroup per minibatch) and the dispatch gather is the GEMM's own
+// row-mapped direct-to-LDS load, so the token-moving work is combine.  The
+// GEMM workgroups walk one static sequence of tiles, dealt XCD-aware as in the
+// one-GEMM-per-launch kernels: step s holds gate|up(s), then combine(s-2) when
+// combine runs as tiles, then down(s-1):
+//   gate|up(0), gate|up(1), down(0), gate|up(2), [combine(0),] down(1), ...
+// The skew puts a whole phase between a phase and the one that reads its
+// output, so inputs are rarely unfinished when a workgroup reaches them, and a
+// workgroup waits at most once per phase.  Combine runs either
+//   * on comm dedicated workgroups (blockIdx < comm), minibatch by minibatch,
+//     as MoK splits its SMs between communication and GEMM work, or
+//   * (comm = 0) as tiles of 16 tokens in the same sequence, so that every CU
+//     runs GEMM tiles: on one GPU combine is a few per cent of the layer.
+// Ring: minibatch b writes h (and, without saved outputs, Y) into slot b % S.
+// Gate|up(b) waits until down(b-S) -- and combine(b-S) when Y is in the ring --
+// are done.  Every wait depends only on phases earlier in the sequence (S >= 2,
+// and S >= 3 for combine tiles with Y in the ring) or on the dedicated combine
+// workgroups, which only wait on earlier down phases; every workgroup takes
+// its tiles in sequence order, so the launch always drains (all workgroups are
+// co-resident: it is a cooperative launch).
+//
+// Cross-XCD visibility: each XCD has its own L2, so producers end a tile with
+// every wave's stores complete, a barrier, and one agent-scope release
+// (L2 write-back) on the counter; consumers poll the counter with relaxed
+// agent-scope loads and take one agent-scope acquire (L2 invalidate) when it
+// reaches the target, before reading.  Every wait is bounded in
+// wall-clock time: on expiry the workgroup records MOE_DEV_WAIT_TIMEOUT in the
+// device status word and every workgroup leaves.
+#include "common.hpp"
+#include "gemm_tile.hpp"
+#include "kernels.hpp"
+#include "moe.h"
+#include "mx_tile.hpp"
+
+namespace moe {
+
+namespace {
+
+enum PhaseKind { kGateUp = 0, kCombine = 1, kDown = 2 };
+constexpr int kCombTilesTok = 16;  // tokens per combine tile
+
+// Cursor over the phases of the tile sequence.  Step s holds gate|up(s), then
+// (with combine tiles) combine(s-2), then down(s-1), each only if its
+// minibatch exists: gate|up(0), gate|up(1), down(0), gate|up(2), combine(0),
+// down(1), ...  Every phase depends only on phases at least one phase earlier.
+struct PhaseCursor {
+    int s = 0, slot = -1, kind = 0, b = 0;
+    __device__ bool next(int nmb, bool with_combine) {
+        for (;;) {
+            if (++slot > 2) { slot = 0; ++s; }
+            if (s > nmb + 1) return false;
+            if (slot == 0) { kind = kGateUp; b = s; }
+            else if (slot == 1) { if (!with_combine) continue; kind = kCombine; b = s - 2; }
+            else { kind = kDown; b = s - 1; }
+            if (b >= 0 && b < nmb) return true;
+        }
+    }
+};
+
+__device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
+
+// Thread 0 waits until *ctr >= target (agent-scope acquire), then the whole
+// workgroup continues.  Returns false if this launch is being abandoned (this
+// wait expired, or another workgroup's did: the launch's abort word, zeroed
+// with the counters, is set).  An expiry is also recorded in the device status
+// word (first expiry wins; it stays until moe_read_device_status reads it).
+// acquire = false serves waits that only order this workgroup's later stores
+// after other workgroups' completed reads (a ring slot becoming free): no data
+// is read, so the L2 is left as it is.
+__device__ bool wait_counter(const MegaArgs& a, int* ctr, int target, int site, int* s_flag, bool acquire) {
+    if (threadIdx.x == 0) {
+        int ok = 1;
+        int* abort_word = a.counters + 3 * a.nmb;
+        const uint64_t t0 = now_ticks();
+        // Poll with relaxed loads (they read the coherent value past this XCD's
+        // L2) and acquire once at the end: an acquire per poll would invalidate
+        // the XCD's L2 on every iteration, under every GEMM tile running there.
+        while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            if (__hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) { ok = 0; break; }
+            if (now_ticks() - t0 > a.spin_ticks) {
+                __hip_atomic_store(abort_word, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                int expected = 0;
+                if (__hip_atomic_compare_exchange_strong(a.status, &expected, (int)MOE_DEV_WAIT_TIMEOUT,
+                                                         __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                    __hip_atomic_store(a.status + 1, site, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                ok = 0;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        if (acquire) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        *s_flag = ok;
+    }
+    __syncthreads();
+    const bool ok = *s_flag != 0;
+    __syncthreads();
+    return ok;
+}
+
+// End of a unit of work: every wave's stores complete, then one release.
+__device__ __forceinline__ void signal_counter(int* ctr) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The MXFP8 tile bodies are called as functions of their own: inlined side by
+// side, register allocation spilled inside their K loops (the bf16 bodies
+// inline without that, and run faster inlined).
+template <int EPI>
+__device__ __attribute__((noinline)) void mx_tile_fn(const MxGemmArgs p, int e, int ml, int ntile, uint8_t* smem) {
+    mx_gemm_tile<EPI>(p, e, ml, ntile, smem);
+}
+
+__device__ __forceinline__ int mb_tiles(const MegaArgs& a, int b, int NT) {
+    const int32_t* mt = a.mt_all + (int64_t)b * a.mt_ld;
+    return (mt[a.e_end] - mt[0]) * NT;
+}
+
+}  // namespace
+
+// Combine of tokens [c0, c1) of minibatch b (relative to the minibatch) by the
+// whole workgroup, two tokens at a time; LDS: the first 1.5 KB of smem.
+__device__ void combine_range(const MegaArgs& a, int b, int c0, int c1, uint8_t* smem) {
+    constexpr int kTok = 2;
+    int (*s_row)[kMaxTopK + 1] = (int (*)[kMaxTopK + 1])smem;
+    float (*s_w)[kMaxTopK] = (float (*)[kMaxTopK])(smem + 512);
+    uint16_t** s_out = (uint16_t**)(smem + 1024);
+    const int t0 = b * a.Mb;
+    const uint8_t* lay = a.lay0 + (int64_t)b * a.lay_bytes;
+    const int32_t* tok_prow = (const int32_t*)(lay + a.ly_tok_prow);
+    const uint16_t* Y = a.saved_mb0 ? (const uint16_t*)(a.saved_mb0 + (int64_t)b * a.sv_mb + a.sv_y)
+                                    : (const uint16_t*)(a.slot0 + (int64_t)(b % a.S) * a.slot_bytes + a.sl_y);
+    for (int t = c0; t < c1; t += kTok) {
+        const int ntok = min(kTok, c1 - t);
+        const int tt = threadIdx.x >> 5, j = threadIdx.x & 31;
+        if (tt < ntok) {
+            if (j < a.k + a.with_shared) s_row[tt][j] = tok_prow[(int64_t)(t + tt) * a.ld_tok_prow + j];
+            if (j < a.k) s_w[tt][j] = a.gw[(int64_t)(t0 + t + tt) * a.k + j];
+            if (j == 0) s_out[tt] = a.out + (int64_t)(t0 + t + tt) * a.H;
+        }
+        __syncthreads();
+        combine_tokens_mlp<kTok>(Y, a.H, s_row, s_w, ntok, a.k, a.with_shared, a.H, s_out, threadIdx.x,
+                                 kGemmThreads);
+        __syncthreads();
+    }
+}
+
+template <bool kMx>
+__global__ __attribute__((amdgpu_flat_work_group_size(kGemmThreads, kGemmThreads), amdgpu_waves_per_eu(1, 1)))
+void mega_kernel(MegaArgs a) {
+    constexpr int kSmem = kMx ? kMxStages * kMxStageBytes : kStages * kStageBytes;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
+    // wait result broadcast: the ring's last dword, free between tiles (the
+    // mainloop has drained its loads and every wave passed a barrier)
+    int& s_flag = *(int*)(smem + kSmem - 4);
+    int* gu_done = a.counters;
+    int* d_done = a.counters + a.nmb;
+    int* comb_done = a.counters + 2 * a.nmb;
+    const int NT1 = ceil_div(2 * a.I, BN), NT2 = ceil_div(a.H, BN);
+    const bool y_in_ring = a.saved_mb0 == nullptr;
+    const int G = gridDim.x - a.comm, g = blockIdx.x - a.comm;  // GEMM workgroups
+    const bool comb_tiles = a.comm == 0;                      // combine as tiles of the GEMM workgroups
+    const int comb_target = comb_tiles ? G : a.comm;
+
+    if ((int)blockIdx.x < a.comm) {
+        // ---- combine workers: minibatch by minibatch, tokens split in contiguous chunks
+        for (int b = 0; b < a.nmb; ++b) {
+            if (!wait_counter(a, d_done + b, G, 2, &s_flag, true)) return;
+            const int Tm = min(a.Mb, a.T - b * a.Mb);
+            const int chunk = ceil_div(Tm, a.comm);
+            const int c0 = min(Tm, (int)blockIdx.x * chunk), c1 = min(Tm, c0 + chunk);
+            combine_range(a, b, c0, c1, smem);
+            signal_counter(comb_done + b);
+        }
+        return;
+    }
+
+    // ---- GEMM workers.  Each phase counter counts the GEMM workgroups that have
+    // finished all of their tiles of that phase (each releases once per phase,
+    // owning tiles in it or not), so a phase is complete at G.
+    const int per = G >> 3, xcd = g & 7, local = g >> 3;
+    auto phase_tiles = [&](int kind, int b) -> int {
+        if (kind == kGateUp) return mb_tiles(a, b, NT1);
+        if (kind == kDown) return mb_tiles(a, b, NT2);
+        return ceil_div(min(a.Mb, a.T - b * a.Mb), kCombTilesTok);
+    };
+    auto counter_of = [&](int kind, int b) -> int* {
+        return kind == kGateUp ? gu_done + b : (kind == kDown ? d_done + b : comb_done + b);
+    };
+    PhaseCursor cur;
+    bool more = cur.next(a.nmb, comb_tiles);
+    int64_t qstart = 0;
+    int qtiles = phase_tiles(cur.kind, cur.b);
+    bool ready = false;  // inputs of the current phase waited for
+    for (int it = 0;; ++it) {
+        const int64_t v = (int64_t)it * G + xcd * per + local;
+        while (more && v >= qstart + qtiles) {  // done with this phase: publish
+            signal_counter(counter_of(cur.kind, cur.b));
+            qstart += qtiles;
+            more = cur.next(a.nmb, comb_tiles);
+            if (more) qtiles = phase_tiles(cur.kind, cur.b);
+            ready = false;
+        }
+        if (!more) break;
+        const int kind = cur.kind, b = cur.b;
+        if (!ready) {
+            if (kind == kGateUp && b >= a.S) {  // ring slot b % S free again
+                if (!wait_counter(a, d_done + (b - a.S), G, 0, &s_flag, false)) return;
+                if (y_in_ring && !wait_counter(a, comb_done + (b - a.S), comb_target, 1, &s_flag, false)) return;
+            }
+            if (kind == kDown && !wait_counter(a, gu_done + b, G, 3, &s_flag, true)) return;
+            if (kind == kCombine && !wait_counter(a, d_done + b, G, 2, &s_flag, true)) return;
+            ready = true;
+        }
+        const int lv = (int)(v - qstart);
+        if (kind == kCombine) {
+            const int Tm = min(a.Mb, a.T - b * a.Mb);
+            combine_range(a, b, lv * kCombTilesTok, min(Tm, (lv + 1) * kCombTilesTok), smem);
+            continue;
+        }
+        const uint8_t* lay = a.lay0 + (int64_t)b * a.lay_bytes;
+        const int32_t* mt = a.mt_all + (int64_t)b * a.mt_ld;
+        const LayoutHeader* hdr = (const LayoutHeader*)lay;
+        uint8_t* slot = a.slot0 + (int64_t)(b % a.S) * a.slot_bytes;
+        uint8_t* svb = a.saved_mb0 ? a.saved_mb0 + (int64_t)b * a.sv_mb : nullptr;
+        uint16_t* Y = svb ? (uint16_t*)(svb + a.sv_y) : (uint16_t*)(slot + a.sl_y);
+        int e, ml, ntile;
+        if (kind == kGateUp) {
+            tile_coords(mt, 0, a.e_end, NT1, lv, e, ml, ntile);
+            if constexpr (kMx) {
+                MxGemmArgs m = a.m1;
+                m.a_row_map = (const int32_t*)(lay + a.ly_prow_token);
+                m.mt_start = mt; m.hdr = hdr;
+                m.Cq = slot + a.sl_hq; m.Cs = slot + a.sl_sh;
+                m.GU = svb ? (float*)svb : nullptr;
+                mx_tile_fn<kEpiSwiGLU>(m, e, ml, ntile, smem);
+            } else {
+                GemmArgs gg = a.g1;
+                gg.a_row_map = (const int32_t*)(lay + a.ly_prow_token);
+                gg.mt_start = mt; gg.hdr = hdr;
+                gg.C = (uint16_t*)(slot + a.sl_h);
+                gg.GU = svb ? (uint16_t*)svb : nullptr;
+                gemm_tile<kEpiSwiGLU>(gg, e, ml, ntile, smem);
+            }
+        } else {
+            tile_coords(mt, 0, a.e_end, NT2, lv, e, ml, ntile);
+            if constexpr (kMx) {
+                MxGemmArgs m = a.m2;
+                m.A = slot + a.sl_hq; m.SA = slot + a.sl_sh;
+                m.mt_start = mt; m.hdr = hdr;
+                m.C = Y;
+                mx_tile_fn<kEpiStore>(m, e, ml, ntile, smem);
+            } else {
+                GemmArgs gg = a.g2;
+                gg.A = (const uint16_t*)(slot + a.sl_h);
+                gg.mt_start = mt; gg.hdr = hdr;
+                gg.C = Y;
+                gemm_tile<kEpiStore>(gg, e, ml, ntile, smem);
+            }
+        }
+    }
+}
+
+__global__ void zero_i32_kernel(int* p, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
+hipError_t launch_mega(const MegaArgs& a, int grid, hipStream_t stream) {
+    hipLaunchKernelGGL(zero_i32_kernel, dim3(ceil_div(3 * a.nmb + 1, 256)), dim3(256), 0, stream, a.counters,
+                       3 * a.nmb + 1);
+    MegaArgs args = a;
+    void* kargs[] = {&args};
+    return a.mx ? hipLaunchCooperativeKernel((const void*)mega_kernel<true>, dim3(grid), dim3(kGemmThreads), kargs,
+                                              0, stream)
+                  : hipLaunchCooperativeKernel((const void*)mega_kernel<false>, dim3(grid), dim3(kGemmThreads), kargs,
+                                              0, stream);
+}
+
+}  // namespace moe

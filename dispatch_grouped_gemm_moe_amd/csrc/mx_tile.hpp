@@ -1,0 +1,234 @@
+// Tile-level building blocks of the MXFP8 (scaled-MFMA) grouped GEMMs, shared
+// by the one-launch-per-GEMM kernels and the persistent layer kernel.
+#pragma once
+
+#include "common.hpp"
+#include "gemm_tile.hpp"
+#include "kernels.hpp"
+#include "mxfp8.hpp"
+
+namespace moe {
+
+// LDS stage: A codes [256][64 B], B codes [256][64 B], A scales [256][4 B],
+// B scales [256][4 B].  Code rows use the bf16 path's conflict-free swizzle.
+constexpr int kMxRow = 64;
+constexpr int kMxStageA = BM * kMxRow;
+constexpr int kMxStageSA = (BM + BN) * kMxRow;
+constexpr int kMxStageSB = kMxStageSA + BM * 4;
+constexpr int kMxStageBytes = kMxStageSB + BN * 4;
+constexpr int kMxStages = 4;  // 136 KB
+constexpr int kMxLoads = 10;  // direct-to-LDS loads per lane per K step
+
+__device__ __forceinline__ int mx_swz(int r) { return (r >> 2) & 3; }
+
+__device__ __forceinline__ void mx_wait_steps(int c) {
+    switch (c < 0 ? 0 : c) {
+        case 0: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); break;
+        case 1: asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)" ::: "memory"); break;
+        case 2: asm volatile("s_waitcnt vmcnt(20) lgkmcnt(0)" ::: "memory"); break;
+        default: asm volatile("s_waitcnt vmcnt(30) lgkmcnt(0)" ::: "memory"); break;
+    }
+}
+static_assert(kMxStages <= 4, "mx_wait_steps covers at most 3 steps in flight");
+
+// One 256 x 256 output tile (expert e, M tile ml of the expert, N tile ntile)
+// of the MXFP8 grouped GEMM with its epilogue; smem is the kMxStages LDS ring.
+template <int EPI>
+__device__ __forceinline__ void mx_gemm_tile(const MxGemmArgs p, int e, int ml, int ntile, uint8_t* smem) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int KT = p.K / 64;
+    const int mt0 = p.mt_start[e];
+    const int prow0 = (mt0 + ml) * BM;
+    const int n0 = ntile * BN;
+
+    // per-lane staging: code rows wave*64 + 16i + lane/4 (swizzled chunk),
+    // scale row wave*64 + lane (one dword per row and K step)
+    const char* a_base = (const char*)p.A;
+    const char* b_base = (const char*)(p.B + (int64_t)e * p.b_stride);
+    const char* sa_base = (const char*)p.SA;
+    const char* sb_base = (const char*)(p.SB + (int64_t)e * p.sb_stride);
+    uint32_t aoff[4], boff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = wave * 64 + i * 16 + (lane >> 2);
+        const int lchunk = (lane & 3) ^ mx_swz(r);
+        const int prow = prow0 + r;
+        const int arow = p.a_row_map ? p.a_row_map[prow] : prow;
+        aoff[i] = (uint32_t)((int64_t)arow * p.lda + lchunk * 16);
+        boff[i] = (uint32_t)((int64_t)min(n0 + r, p.N - 1) * p.K + lchunk * 16);
+    }
+    const int srow = wave * 64 + lane;
+    const int sarow = p.a_row_map ? p.a_row_map[prow0 + srow] : prow0 + srow;
+    const uint32_t saoff = (uint32_t)sarow * 4, sboff = (uint32_t)min(n0 + srow, p.N - 1) * 4;
+
+    auto issue = [&](int kt) {
+        uint8_t* st = smem + (kt % kMxStages) * kMxStageBytes;
+        uint8_t* base = st + (wave * 64) * kMxRow;
+        const uint32_t kb = (uint32_t)kt * 64;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_global_load_lds((gbl_cvoid*)(a_base + aoff[i] + kb), (lds_void*)(base + i * 1024), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_global_load_lds((gbl_cvoid*)(b_base + boff[i] + kb), (lds_void*)(base + kMxStageA + i * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gbl_cvoid*)(sa_base + (int64_t)kt * p.sa_kstride + saoff),
+                                         (lds_void*)(st + kMxStageSA + wave * 256), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds((gbl_cvoid*)(sb_base + (int64_t)kt * p.sb_kstride + sboff),
+                                         (lds_void*)(st + kMxStageSB + wave * 256), 4, 0, 0);
+    };
+    const int fr = lane & 31, half = lane >> 5;
+    const int fsw = mx_swz(fr);
+    const int pc0 = (half ^ fsw) * 16, pc1 = ((2 + half) ^ fsw) * 16;
+    const int arow_b = (wm * 128 + fr) * kMxRow, brow_b = kMxStageA + (wn * 128 + fr) * kMxRow;
+    auto frags = [&](int kt, intx8 (&a)[4], intx8 (&b)[4], int (&sa)[4], int (&sb)[4]) {
+        const uint8_t* st = smem + (kt % kMxStages) * kMxStageBytes;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const intx4 lo4 = *(const intx4*)(st + arow_b + i * 32 * kMxRow + pc0);
+            const intx4 hi4 = *(const intx4*)(st + arow_b + i * 32 * kMxRow + pc1);
+            a[i] = intx8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+            sa[i] = st[kMxStageSA + (wm * 128 + i * 32 + fr) * 4 + half];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const intx4 lo4 = *(const intx4*)(st + brow_b + j * 32 * kMxRow + pc0);
+            const intx4 hi4 = *(const intx4*)(st + brow_b + j * 32 * kMxRow + pc1);
+            b[j] = intx8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+            sb[j] = st[kMxStageSB + (wn * 128 + j * 32 + fr) * 4 + half];
+        }
+    };
+    floatx16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
+    auto mfmas = [&](const intx8 (&a)[4], const intx8 (&b)[4], const int (&sa)[4], const int (&sb)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 0, 0, 0, sa[i], 0,
+                                                                             sb[j]);
+    };
+
+    // Ring protocol as in the bf16 path, with 10 loads per K step: before
+    // computing step kt, wait until step kt+1 has landed and this wave's
+    // reads of step kt are done, barrier, refill step kt's slot with step
+    // kt + kMxStages, and read step kt+1's fragments under step kt's MFMAs.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kMxStages; ++j)
+        if (j < KT) issue(j);
+    mx_wait_steps(KT - 1 < kMxStages - 1 ? KT - 1 : kMxStages - 1);
+    __syncthreads();
+    intx8 a0[4], b0[4], a1[4], b1[4];
+    int s0a[4], s0b[4], s1a[4], s1b[4];
+    frags(0, a0, b0, s0a, s0b);
+    auto step = [&](int kt, intx8 (&ac)[4], intx8 (&bc)[4], int (&sac)[4], int (&sbc)[4], intx8 (&an)[4],
+                    intx8 (&bn)[4], int (&san)[4], int (&sbn)[4]) {
+        const int ahead = KT - 2 - kt;
+        mx_wait_steps(ahead < kMxStages - 2 ? ahead : kMxStages - 2);
+        __syncthreads();
+        if (kt + kMxStages < KT) issue(kt + kMxStages);
+        frags(kt + 1, an, bn, san, sbn);  // stale but in-bounds on the last step
+        mfmas(ac, bc, sac, sbc);
+#pragma unroll
+        for (int q = 0; q < 10; ++q) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 6, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    int kt = 0;
+    for (; kt + 1 < KT; kt += 2) {
+        step(kt, a0, b0, s0a, s0b, a1, b1, s1a, s1b);
+        step(kt + 1, a1, b1, s1a, s1b, a0, b0, s0a, s0b);
+    }
+    if (kt < KT) step(kt, a0, b0, s0a, s0b, a1, b1, s1a, s1b);
+
+    if (EPI == kEpiSwiGLU) {
+        // h = silu(g) * u, then MXFP8 along I: the 32 columns of a block are
+        // lanes 0..31 (or 32..63) of one fragment row; routed rows only.
+        const int I = p.N / 2;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int hcol = n0 / 2 + wn * 64 + jj * 32 + fr;
+            const int blk = (n0 / 2 + wn * 64 + jj * 32) / 32;
+            const bool live = n0 / 2 + wn * 64 + jj * 32 < I;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float g = acc[i][2 * jj][r], u = acc[i][2 * jj + 1][r];
+                    const float h = g / (1.0f + __expf(-g)) * u;
+                    float m = fabsf(h);
+                    m = fmaxf(m, __shfl_xor(m, 16, kWave));
+                    m = fmaxf(m, __shfl_xor(m, 8, kWave));
+                    m = fmaxf(m, __shfl_xor(m, 4, kWave));
+                    m = fmaxf(m, __shfl_xor(m, 2, kWave));
+                    m = fmaxf(m, __shfl_xor(m, 1, kWave));
+                    const int ex = mx_scale_exp(m);
+                    const int row = prow0 + wm * 128 + i * 32 + (r >> 2) * 8 + 4 * half + (r & 3);
+                    if (live) {
+                        const int q = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(h, -ex), 0.0f, 0, false);
+                        p.Cq[(int64_t)row * I + hcol] = (uint8_t)(q & 0xff);
+                        if (fr == 0) p.Cs[((int64_t)(blk >> 1) * p.cs_rows + row) * 4 + (blk & 1)] = (uint8_t)(ex + 127);
+                        if (fr == 0 && (blk & 1) == 0) {
+                            p.Cs[((int64_t)(blk >> 1) * p.cs_rows + row) * 4 + 2] = 0;
+                            p.Cs[((int64_t)(blk >> 1) * p.cs_rows + row) * 4 + 3] = 0;
+                        }
+                    }
+                }
+        }
+        if (p.GU) {  // g | u kept in fp32 for the backward
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int hcol = n0 / 2 + wn * 64 + jj * 32 + fr;
+                if (n0 / 2 + wn * 64 + jj * 32 < I) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int row = prow0 + wm * 128 + i * 32 + (r >> 2) * 8 + 4 * half + (r & 3);
+                            float* dst = p.GU + (int64_t)row * p.N + hcol;
+                            dst[0] = acc[i][2 * jj][r];
+                            dst[I] = acc[i][2 * jj + 1][r];
+                        }
+                }
+            }
+        }
+    } else if (p.Cf) {  // fp32 output
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int col = n0 + wn * 128 + j * 32 + fr;
+            if (col < p.N) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = prow0 + wm * 128 + i * 32 + (r >> 2) * 8 + 4 * half + (r & 3);
+                        p.Cf[(int64_t)row * p.ldc + col] = acc[i][j][r];
+                    }
+            }
+        }
+    } else {  // bf16 output
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int col = n0 + wn * 128 + j * 32 + fr;
+            if (col < p.N) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = prow0 + wm * 128 + i * 32 + (r >> 2) * 8 + 4 * half + (r & 3);
+                        p.C[(int64_t)row * p.ldc + col] = f32_to_bf16_rne(acc[i][j][r]);
+                    }
+            }
+        }
+    }
+}
+
+}  // namespace moe

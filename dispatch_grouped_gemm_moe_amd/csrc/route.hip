@@ -170,9 +170,26 @@ void launch_route(const uint16_t* x, const float* Wr, const float* bias, int T, 
 constexpr int kLayoutThreads = 1024;
 constexpr int kLayoutWaves = kLayoutThreads / kWave;
 
-__global__ __launch_bounds__(kLayoutThreads) void layout_kernel(const int32_t* __restrict__ idx, int Tm,
+__global__ __launch_bounds__(kLayoutThreads) void layout_kernel(const int32_t* __restrict__ idx, int T, int Mb,
                                                                  int E, int k, int with_shared,
-                                                                 LayoutOut o) {
+                                                                 LayoutOut o, LayoutStrides st) {
+    // workgroup b lays out minibatch b: tokens [b*Mb, min(T, (b+1)*Mb))
+    {
+        const int b = blockIdx.x;
+        const int t0 = b * Mb;
+        if (o.counts) o.counts += b * st.counts;
+        if (o.offsets) o.offsets += b * st.offsets;
+        if (o.row_token) o.row_token += b * st.row_token;
+        if (o.tok_row) o.tok_row += b * st.tok_row;
+        if (o.hdr) o.hdr += b * st.hdr;
+        if (o.mt_start) o.mt_start += b * st.mt_start;
+        if (o.prow_token) o.prow_token += b * st.prow_token;
+        if (o.tok_prow) o.tok_prow += b * st.tok_prow;
+        if (o.prow_slot) o.prow_slot += b * st.prow_slot;
+        o.token_base += t0;
+        idx += (int64_t)t0 * k;
+    }
+    const int Tm = min(Mb, T - (int)blockIdx.x * Mb);
     __shared__ int s_cnt[kLayoutWaves][kMaxExperts + 1];  // per-wave counts, then running bases
     __shared__ int s_off[kMaxExperts + 2];                 // unpadded row offsets
     __shared__ int s_poff[kMaxExperts + 2];                // padded (tile-aligned) row offsets
@@ -204,11 +221,13 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(const int32_t* _
         for (int j = 0; j < k; ++j) atomicAdd(&s_cnt[wave][ids[j]], 1);
     }
     __syncthreads();
-    if (s_err) {
+    if (s_err) {  // report, and leave an empty tile map so no GEMM tile runs
         if (tid == 0) {
             if (o.offsets) o.offsets[E] = -1;
             if (o.hdr) { o.hdr->m_tiles = 0; o.hdr->rows = 0; o.hdr->error = 1; }
         }
+        if (o.mt_start)
+            for (int e = tid; e <= Et; e += kLayoutThreads) o.mt_start[e] = 0;
         return;
     }
 
@@ -297,8 +316,14 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(const int32_t* _
 
 void launch_layout(const int32_t* idx, int Tm, int E, int k, int with_shared, const LayoutOut& o,
                    hipStream_t stream) {
-    hipLaunchKernelGGL(layout_kernel, dim3(1), dim3(kLayoutThreads), 0, stream, idx, Tm, E, k,
-                       with_shared, o);
+    hipLaunchKernelGGL(layout_kernel, dim3(1), dim3(kLayoutThreads), 0, stream, idx, Tm, Tm, E, k,
+                       with_shared, o, LayoutStrides{});
+}
+
+void launch_layout_batched(const int32_t* idx, int T, int Mb, int E, int k, int with_shared, const LayoutOut& o,
+                           const LayoutStrides& st, hipStream_t stream) {
+    hipLaunchKernelGGL(layout_kernel, dim3(ceil_div(T, Mb)), dim3(kLayoutThreads), 0, stream, idx, T, Mb, E, k,
+                       with_shared, o, st);
 }
 
 }  // namespace moe

@@ -61,7 +61,11 @@ enum moe_flags {
     MOE_F_SHARED_EXPERT = 1u << 0,
     /* test mode: every routed expert is the identity (y = x), so combine must
        return the weighted sum of copies of the input */
-    MOE_F_IDENTITY_EXPERTS = 1u << 1
+    MOE_F_IDENTITY_EXPERTS = 1u << 1,
+    /* run the forward's expert GEMMs and combine as one launch per grouped GEMM
+       and per combine, minibatch by minibatch, instead of the persistent layer
+       kernel (same results bit for bit) */
+    MOE_F_LAUNCH_PER_GEMM = 1u << 2
 };
 
 /* Layer shape and execution choices. */
@@ -72,8 +76,10 @@ typedef struct moe_cfg {
     int32_t E;          /* experts on this GPU: 1..256 */
     int32_t k;          /* experts per token: 1..min(E, 16) */
     int32_t minibatch;  /* tokens per ring slot; 0 = automatic (see moe_query_sizes) */
-    int32_t ring_slots; /* ring token buffer slots; 0 = automatic */
-    int32_t comm_cus;   /* CUs reserved for route/dispatch/combine work; 0 = automatic */
+    int32_t ring_slots; /* ring token buffer slots; 0 = automatic (3) */
+    int32_t comm_cus;   /* workgroups (one per CU) dedicated to combine in the
+                           persistent layer kernel; 0 = automatic: none, combine
+                           runs as tiles of the GEMM workgroups */
     int32_t prec;       /* moe_prec */
     uint32_t flags;     /* moe_flags */
 } moe_cfg;
@@ -87,7 +93,7 @@ typedef struct moe_sizes {
     int32_t minibatch;     /* effective tokens per ring slot */
     int32_t ring_slots;    /* effective ring slots */
     int32_t num_minibatches;
-    int32_t comm_cus;      /* effective CUs of the route/dispatch/combine role */
+    int32_t comm_cus;      /* effective dedicated combine workgroups (0: combine tiles) */
 } moe_sizes;
 
 /* Device buffers of one layer's parameters. */
@@ -265,7 +271,8 @@ typedef enum moe_kernel_kind {
     MOE_K_DGRAD_DOWN = 8,   /* backward: dH = dY Wd^T */
     MOE_K_DGRAD_GATE_UP = 9, /* backward: dX = dG Wg^T + dU Wu^T */
     MOE_K_SHARED_GEMM = 10, /* MOE_PREC_MXFP8: the bf16 shared expert's forward and input-gradient GEMMs */
-    MOE_K_COUNT = 11
+    MOE_K_LAYER = 11,       /* the persistent layer kernel: every forward expert GEMM and combine */
+    MOE_K_COUNT = 12
 } moe_kernel_kind;
 
 typedef struct moe_kernel_times {

@@ -17,9 +17,10 @@ def cfg_of(w, minibatch=None, flags=0, T=None):
 class Layer:
     """One layer's device tensors and packed weights."""
 
-    def __init__(self, inp, minibatch=None, flags=0, device="cuda"):
+    def __init__(self, inp, minibatch=None, flags=0, device="cuda", ring_slots=0, comm_cus=0):
         w = inp.w
         self.inp, self.cfg = inp, cfg_of(w, minibatch, flags)
+        self.cfg.ring_slots, self.cfg.comm_cus = ring_slots, comm_cus
         self.bufs = moe.alloc_buffers(self.cfg, device=device, with_saved=True)
         dev = lambda t: None if t is None else t.to(device).contiguous()
         self.x, self.Wr, self.bias = dev(inp.x), dev(inp.Wr), dev(inp.bias)
@@ -30,10 +31,14 @@ class Layer:
         del Wg, Wu, Wd
         self.out = torch.empty_like(self.x)
 
-    def forward(self):
+    def forward(self, keep=True):
+        """keep=False runs the inference forward (nothing saved for a backward)."""
         moe.moe_layer_fwd(self.cfg, self.Wr, self.bias, self.bufs.packed, self.x, self.out,
-                          self.bufs.ws, saved=self.bufs.saved)
+                          self.bufs.ws, saved=self.bufs.saved if keep else None)
         return self.out
+
+    def device_status(self):
+        return moe.moe_read_device_status(self.bufs.ws)
 
     def backward(self, dout, with_dgate=True):
         """Gradients of sum(out * dout); returns a dict of CPU float tensors."""
