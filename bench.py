@@ -167,7 +167,8 @@ def main():
     dom = max(by_sym, key=lambda sy: by_sym[sy][1])
     dom_flops, ms_dom, n_dom, dom_roles = by_sym[dom]
     achieved = dom_flops / (ms_dom / 1e3) / 1e12
-    peak = PEAK_FP8_TFLOPS if (mx and dom.startswith("mx_")) else PEAK_BF16_TFLOPS
+    # the scaled-MFMA kernels (and the MXFP8 layer kernel) are priced at the FP8 peak
+    peak = PEAK_FP8_TFLOPS if (mx and (dom.startswith("mx_") or dom == "mega_kernel<true>")) else PEAK_BF16_TFLOPS
     total_flops = sum(flops.values())
     res = {
         "metric": "MoE layer %s tokens/s at H=%d I=%d (%s) + %% MFMA peak" % (
@@ -220,7 +221,7 @@ def traffic_for(symbol: str, workload: str):
     with open(path) as f:
         rec = json.load(f)
     ent = rec.get("kernels", {}).get("moe::%s@%s" % (symbol, workload))
-    if not ent or ent.get("source_sha256") != _source_sha(symbol.startswith("mx_")):
+    if not ent or ent.get("source_sha256") != _source_sha():
         return None
     return ent["hbm_bytes_per_launch"]
 
@@ -229,12 +230,15 @@ def _kernel_symbol(name: str) -> str:
     return name.split("(")[0].replace("void ", "").strip()
 
 
-def _source_sha(mx: bool) -> str:
+def _source_sha() -> str:
+    """Hash of every kernel source: counter figures go stale with any change."""
     import hashlib
-    here = os.path.dirname(os.path.abspath(__file__))
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "dispatch_grouped_gemm_moe_amd", "csrc")
     h = hashlib.sha256()
-    for f in ("mx.hip" if mx else "gemm.hip", "common.hpp"):
-        h.update(open(os.path.join(here, "dispatch_grouped_gemm_moe_amd", "csrc", f), "rb").read())
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()
 
 
@@ -282,14 +286,13 @@ def summarize_traffic(fetch_csv: str, write_csv: str, workload: str, copy_mib: i
     for sym in fetch:
         if not sym.startswith("moe::") or sym not in write:
             continue
-        mx = "mx_" in sym
         fk = sum(fetch[sym]) / len(fetch[sym])
         wk = sum(write[sym]) / len(write[sym])
         rec["kernels"]["%s@%s" % (sym, workload)] = {
             "dispatches": len(fetch[sym]), "fetch_kib": fk, "write_kib": wk,
             "fetch_factor": f_fac, "write_factor": w_fac,
             "hbm_bytes_per_launch": (fk * f_fac + wk * w_fac) * 1024.0,
-            "source_sha256": _source_sha(mx)}
+            "source_sha256": _source_sha()}
     with open(out, "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
     print(json.dumps({k: v["hbm_bytes_per_launch"] for k, v in rec["kernels"].items()}, indent=1))
