@@ -49,6 +49,7 @@ struct Plan {
     size_t wb_wrt, wb_mt, wb_lay0, lay_bytes, ly_hdr, ly_prow_token, ly_tok_prow, ly_prow_slot;
     size_t wb_dyt, wb_xgt, wb_dgut, wb_ht, wb_dsel, wb_dy, wb_dgu, wb_dh, wb_dx, wb_dgp, ws_bwd;
     size_t wb_dyq, wb_sdy, wb_dguq, wb_sdgu;  // MXFP8 operands of the input-gradient GEMMs
+    size_t wb_dlog, wb_dwrp;                  // dense d out / d logits, router-gradient partial sums
 };
 
 moe_status validate(const moe_cfg* c) {
@@ -179,6 +180,8 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     p->wb_dh = o; o = align_up(o + rp * I * (p->mx ? 4 : 2));
     p->wb_dx = o; o = align_up(o + rp * H * 2);
     p->wb_dgp = o; o = align_up(o + rp * (H / 64) * 4);
+    p->wb_dlog = o; o = align_up(o + (size_t)c->T * c->E * 4);
+    p->wb_dwrp = o; o = align_up(o + (size_t)dwr_chunks(c->T) * H * c->E * 4);
     if (p->mx) {
         p->wb_dyq = o; o = align_up(o + rp * H);
         p->wb_sdy = o; o = align_up(o + (H / 64) * rp * 4);
@@ -616,6 +619,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
         rd.dX = dXb; rd.dgp = dgp; rd.tok_prow = tok_prow; rd.topk_idx = idx; rd.topk_w = gw; rd.WrT = WrT;
         rd.dsel = dsel; rd.dgate = dgate; rd.dx = dx; rd.t0 = t0; rd.H = H; rd.k = k; rd.ld = p.ld_tok_prow;
         rd.with_shared = p.shared ? 1 : 0; rd.nhb = H / 64;
+        rd.dlogits = (float*)(wsb + p.wb_dlog); rd.E = E;
         TIMED(MOE_K_COMBINE, s, launch_rdispatch(rd, Tm, s));
     }
     WgradArgs wa{};  // [dWg | dWu][e] = x_e^T [dG | dU]_e over every row of expert e
@@ -633,8 +637,8 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
     wd.Cs0 = p.shared ? dWs + (size_t)2 * H * I : nullptr; wd.Cs1 = nullptr;
     TIMED(MOE_K_WGRAD, s, launch_wgrad(wd, grid, s));
     DwrArgs dr{};
-    dr.xgT = xgT_all; dr.dsel = dsel_all; dr.mt = mt_all; dr.dWr = dWr; dr.ldt = rp;
-    dr.x_mb = (int64_t)H * rp; dr.d_mb = rp; dr.H = H; dr.E = E; dr.nmb = p.nmb; dr.mt_ld = Et + 1;
+    dr.x = x; dr.dlogits = (const float*)(wsb + p.wb_dlog); dr.partial = (float*)(wsb + p.wb_dwrp);
+    dr.dWr = dWr; dr.T = p.T; dr.H = H; dr.E = E;
     TIMED(MOE_K_OTHER, s, launch_dwr(dr, s));
     return check_launch();
 }

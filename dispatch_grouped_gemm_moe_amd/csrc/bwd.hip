@@ -246,6 +246,11 @@ __global__ __launch_bounds__(kRdThreads) void rdispatch_kernel(RdispArgs p) {
         }
     }
     __syncthreads();
+    for (int e = tid; e < p.E; e += kRdThreads) {  // dense row of d out / d logits
+        float v = 0.0f;
+        for (int j = 0; j < k; ++j) v = s_idx[j] == e ? s_ds[j] : v;
+        p.dlogits[(int64_t)t * p.E + e] = v;
+    }
     for (int c = tid; c < p.H / 8; c += kRdThreads) {
         float acc[8];
 #pragma unroll
@@ -281,36 +286,61 @@ void launch_rdispatch(const RdispArgs& a, int Tm, hipStream_t stream) {
     hipLaunchKernelGGL(rdispatch_kernel, dim3(Tm), dim3(kRdThreads), 0, stream, a);
 }
 
-// Router weight gradient: dWr[h][e] = sum over expert e's rows, minibatch by
-// minibatch, row by row, of dsel[row] * x[token(row)][h] (read from the
-// transposed gathered copy; padding rows carry dsel = 0).
-__global__ __launch_bounds__(256) void dwr_kernel(DwrArgs p) {
-    const int e = blockIdx.x, h = blockIdx.y * 256 + threadIdx.x;
-    if (h >= p.H) return;
-    float acc = 0.0f;
-    for (int b = 0; b < p.nmb; ++b) {
-        const int r0 = p.mt[(int64_t)b * p.mt_ld + e] * BM, r1 = p.mt[(int64_t)b * p.mt_ld + e + 1] * BM;
-        const uint16_t* xr = p.xgT + (int64_t)b * p.x_mb + (int64_t)h * p.ldt;
-        const float* ds = p.dsel + (int64_t)b * p.d_mb;
-        for (int r = r0; r < r1; r += 8) {
-            const intx4 xv = *(const intx4*)(xr + r);
-            const floatx4 d0 = *(const floatx4*)(ds + r), d1 = *(const floatx4*)(ds + r + 4);
+// Router weight gradient dWr = x^T dlogits, with dlogits [T][E] dense (zero
+// outside the selected experts), read once from x: workgroup (h block of 64,
+// token chunk c) sums its chunk's tokens in ascending order into
+// partial[c][h][e]; a second pass adds the chunks in ascending order, so the
+// sum over tokens has one fixed order.
+constexpr int kDwrChunk = 512, kDwrH = 64, kDwrSub = 64;
+
+__global__ __launch_bounds__(256) void dwr_partial_kernel(DwrArgs p) {
+    __shared__ float s_d[kDwrSub][32];  // this pass's 32 experts
+    __shared__ uint16_t s_x[kDwrSub][kDwrH];
+    const int tid = threadIdx.x, hl = tid & 63, eg = tid >> 6;
+    const int h0 = blockIdx.x * kDwrH, h = h0 + hl;
+    const int t0 = blockIdx.y * kDwrChunk, t1 = min(p.T, t0 + kDwrChunk);
+    for (int pass = 0; pass * 32 < p.E; ++pass) {
+        const int eb = pass * 32 + eg * 8;  // this thread's 8 experts
+        float acc[8];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float xa = __builtin_bit_cast(float, (uint32_t)xv[q] << 16);
-                const float xb = __builtin_bit_cast(float, (uint32_t)xv[q] & 0xffff0000u);
-                const float da = q < 2 ? d0[2 * q] : d1[2 * q - 4];
-                const float db = q < 2 ? d0[2 * q + 1] : d1[2 * q - 3];
-                acc = __builtin_fmaf(da, xa, acc);
-                acc = __builtin_fmaf(db, xb, acc);
+        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+        for (int ts = t0; ts < t1; ts += kDwrSub) {
+            const int n = min(kDwrSub, t1 - ts);
+            __syncthreads();
+            for (int f = tid; f < n * 32; f += 256) {
+                const int e = pass * 32 + (f & 31);
+                s_d[f >> 5][f & 31] = e < p.E ? p.dlogits[(int64_t)(ts + (f >> 5)) * p.E + e] : 0.0f;
+            }
+            // x tile [n][64] bf16: 8 threads per token, 16 bytes each
+            for (int f = tid; f < n * 8; f += 256)
+                *(intx4*)&s_x[f >> 3][(f & 7) * 8] = *(const intx4*)(p.x + (int64_t)(ts + (f >> 3)) * p.H + h0 + (f & 7) * 8);
+            __syncthreads();
+            for (int t = 0; t < n; ++t) {
+                const float xv = __builtin_bit_cast(float, (uint32_t)s_x[t][hl] << 16);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(xv, s_d[t][eg * 8 + i], acc[i]);
             }
         }
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (eb + i < p.E) p.partial[((int64_t)blockIdx.y * p.H + h) * p.E + eb + i] = acc[i];
     }
-    p.dWr[(int64_t)h * p.E + e] = acc;
 }
 
+__global__ __launch_bounds__(256) void dwr_reduce_kernel(DwrArgs p, int nchunk) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)p.H * p.E) return;
+    float acc = 0.0f;
+    for (int c = 0; c < nchunk; ++c) acc = acc + p.partial[(int64_t)c * p.H * p.E + i];
+    p.dWr[i] = acc;
+}
+
+int dwr_chunks(int T) { return ceil_div(T, kDwrChunk); }
+
 void launch_dwr(const DwrArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(dwr_kernel, dim3(a.E, ceil_div(a.H, 256)), dim3(256), 0, stream, a);
+    const int nchunk = dwr_chunks(a.T);
+    hipLaunchKernelGGL(dwr_partial_kernel, dim3(a.H / kDwrH, nchunk), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(dwr_reduce_kernel, dim3(ceil_div(a.H * a.E, 256)), dim3(256), 0, stream, a, nchunk);
 }
 
 // dst[c][r] = src[r][c] for fp32 [rows][cols] (small matrices).

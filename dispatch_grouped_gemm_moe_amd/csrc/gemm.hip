@@ -40,6 +40,8 @@ void grouped_gemm_kernel(GemmArgs p) {
 // expert e, minibatch by minibatch in order (a fixed summation order).
 // ---------------------------------------------------------------------------
 
+constexpr int kWgM = 4;  // M tiles per group in the weight-gradient tile order
+
 // K sequence of expert e's rows: for each minibatch b its padded row range
 // [mt_b[e], mt_b[e+1]) x BM, in 32-row K steps; A and B copies of
 // minibatch b lie a_mb / b_mb bytes after minibatch 0's.
@@ -71,9 +73,14 @@ void wgrad_kernel(WgradArgs p) {
     for (int it = 0;; ++it) {
         const int v = it * G + xcd * per + local;
         if (v >= total) break;
-        // tile order: expert-major, then M tile, then N tile (N fastest)
+        // tile order: expert-major, then groups of kWgM M tiles; inside a group
+        // the M tile is fastest, then N.  The 'per' consecutive tiles of one XCD
+        // then cover about kWgM M panels x per/kWgM N panels, which they share
+        // through its L2 (a row of N tiles would share only one A panel).
         const int e = v / (MT * NT), loc = v - e * MT * NT;
-        const int m0 = (loc / NT) * BM, n0 = (loc % NT) * BN;
+        const int gm0 = (loc / (kWgM * NT)) * kWgM, gm = min(kWgM, MT - gm0);
+        const int gl = loc - gm0 * NT;
+        const int m0 = (gm0 + gl % gm) * BM, n0 = (gl / gm) * BN;
         int KT = 0;
         for (int b = 0; b < p.nmb; ++b) KT += (p.mt[(int64_t)b * p.mt_ld + e + 1] - p.mt[(int64_t)b * p.mt_ld + e]) * (BM / kBK);
         uint32_t aoff[4], boff[4];

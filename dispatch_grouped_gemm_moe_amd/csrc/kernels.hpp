@@ -208,19 +208,22 @@ struct RdispArgs {
     float* dsel;               // [R_pad]
     float* dgate;              // [T][k] or NULL
     uint16_t* dx;              // [T][H]
-    int t0, H, k, ld, with_shared, nhb;
+    float* dlogits;            // [T][E] dense d out / d logits (0 off the selection)
+    int t0, H, k, ld, with_shared, nhb, E;
 };
 void launch_rdispatch(const RdispArgs& a, int Tm, hipStream_t stream);
 
-// Backward: router weight gradient over all minibatches.
+// Backward: router weight gradient dWr [H][E] = x^T dlogits, tokens summed in
+// ascending order in chunks, then the chunks in order (partial: dwr_chunks(T)
+// x H x E floats of scratch).
 struct DwrArgs {
-    const uint16_t* xgT;       // minibatch 0's [H][ldt]; minibatch b at + b * x_mb elements
-    const float* dsel;         // minibatch 0's [R_pad]; minibatch b at + b * d_mb elements
-    const int32_t* mt;         // [nmb][mt_ld]
+    const uint16_t* x;         // [T][H]
+    const float* dlogits;      // [T][E]
+    float* partial;
     float* dWr;                // [H][E]
-    int64_t ldt, x_mb, d_mb;
-    int H, E, nmb, mt_ld;
+    int T, H, E;
 };
+int dwr_chunks(int T);
 void launch_dwr(const DwrArgs& a, hipStream_t stream);
 
 void launch_transpose_f32(const float* src, int rows, int cols, float* dst, hipStream_t stream);
