@@ -3,6 +3,7 @@
 // moe_read_device_status).
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "../../include/moe.h"
@@ -16,6 +17,8 @@ namespace {
 constexpr int kNumCUs = 256;      // MI355X compute units
 constexpr int kBalanceRows = 320;  // bf16 machine balance: ~2.5 PFLOP/s over 8 TB/s, in rows
 constexpr int kCommWorkers = 0;    // layer kernel: combine as tiles of the GEMM workgroups (no dedicated CUs)
+constexpr int kGroupTokens = 8192; // layer kernel: tokens per GEMM phase (minibatches grouped up to this)
+constexpr int kMaxGroup = 4;
 constexpr uint64_t kSpinTicks = 200000000;  // 2 s at the 100 MHz s_memrealtime clock: bound of every device wait
 constexpr size_t kAlign = 256;
 
@@ -23,6 +26,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
 struct Plan {
     int T, H, I, E, k, Et, Mb, nmb, slots, comm_cus, prec;
+    int group;  // minibatches per phase of the layer kernel
     bool shared, identity;
     int ld_tok_prow;  // k (+1 with the shared expert)
     int64_t rpad;     // padded GEMM rows of one minibatch
@@ -94,14 +98,20 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     p->Et = c->E + (p->shared ? 1 : 0);
     p->Mb = c->minibatch > 0 ? (c->minibatch < c->T ? c->minibatch : c->T) : auto_minibatch(c);
     p->nmb = ceil_div(c->T, p->Mb);
-    p->slots = c->ring_slots > 0 ? c->ring_slots : 3;
-    if (p->slots > p->nmb) p->slots = p->nmb;
+    // The layer kernel runs its GEMM phases over groups of minibatches of about
+    // kGroupTokens tokens (an expert's weight panels then serve that many
+    // tokens' rows), with three groups of ring slots in flight.
+    const int g_auto = std::max(1, std::min({kMaxGroup, kGroupTokens / p->Mb, p->nmb}));
+    p->group = c->ring_slots > 0 ? std::max(1, std::min(c->ring_slots / 3, g_auto)) : g_auto;
+    p->slots = c->ring_slots > 0 ? c->ring_slots : 3 * p->group;
+    p->slots = std::min(p->slots, ceil_div(p->nmb, p->group) * p->group);  // no slot without a minibatch
+    p->slots -= p->slots % p->group;
     p->comm_cus = c->comm_cus > 0 ? c->comm_cus : kCommWorkers;  // dedicated combine workgroups
     // The layer kernel's tile sequence runs gate|up(b+1) before down(b), so a
     // ring of one slot would make gate|up(b+1) wait on a later tile.  MXFP8
     // with the bf16 shared expert and identity experts take the per-GEMM path.
     p->mega = !(c->flags & MOE_F_LAUNCH_PER_GEMM) && !p->identity && !(p->mx && p->shared) &&
-              (p->slots >= 2 || p->nmb == 1) && p->comm_cus < kNumCUs - 8;
+              p->comm_cus < kNumCUs - 8;
     p->ld_tok_prow = c->k + (p->shared ? 1 : 0);
     const int64_t rows = (int64_t)p->Mb * p->ld_tok_prow;
     // sum over experts of ceil(c_e / BM) <= ceil(rows / BM) + Et - 1
@@ -406,12 +416,13 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
     // Combine tiles with Y in the ring need 3 slots (gate|up(b) waits on
     // combine(b-2) otherwise, which follows it in the tile sequence).
     const int ncu = device_cus();
-    const bool ring_ok = p.comm_cus > 0 || saved || p.slots >= 3 || p.nmb <= p.slots;
+    const int Sg = p.slots / p.group, ng = ceil_div(p.nmb, p.group);
+    const bool ring_ok = ng <= Sg || (Sg >= 2 && (p.comm_cus > 0 || saved || Sg >= 3));
     if (p.mega && ring_ok && ncu >= p.comm_cus + 16) {
         MegaArgs a{};
         a.T = p.T; a.H = p.H; a.I = p.I; a.k = p.k; a.Mb = p.Mb; a.nmb = p.nmb; a.S = p.slots;
         a.comm = p.comm_cus; a.e_end = p.mx ? p.E : p.Et; a.with_shared = p.shared ? 1 : 0;
-        a.ld_tok_prow = p.ld_tok_prow; a.mx = p.mx ? 1 : 0;
+        a.ld_tok_prow = p.ld_tok_prow; a.mx = p.mx ? 1 : 0; a.group = p.group;
         a.lay0 = lay0; a.lay_bytes = p.lay_bytes; a.ly_prow_token = p.ly_prow_token; a.ly_tok_prow = p.ly_tok_prow;
         a.mt_all = mt_all; a.mt_ld = p.Et + 1;
         a.g1 = g1; a.g2 = g2; a.m1 = m1; a.m2 = m2;

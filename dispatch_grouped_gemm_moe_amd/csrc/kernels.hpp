@@ -106,6 +106,7 @@ void launch_mx_quant(const uint16_t* src, int64_t rows, int cols, int layout, ui
 // 1 ring slot (combine), 2 combine input, 3 down input.
 struct MegaArgs {
     int T, H, I, k, Mb, nmb, S, comm, e_end, with_shared, ld_tok_prow, mx;
+    int group;  // minibatches per GEMM / combine phase; S is a multiple of it
     const uint8_t* lay0;
     int64_t lay_bytes, ly_prow_token, ly_tok_prow;
     const int32_t* mt_all;

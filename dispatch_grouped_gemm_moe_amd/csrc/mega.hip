@@ -24,13 +24,17 @@
 //     as MoK splits its SMs between communication and GEMM work, or
 //   * (comm = 0) as tiles of 16 tokens in the same sequence, so that every CU
 //     runs GEMM tiles: on one GPU combine is a few per cent of the layer.
-// Ring: minibatch b writes h (and, without saved outputs, Y) into slot b % S.
-// Gate|up(b) waits until down(b-S) -- and combine(b-S) when Y is in the ring --
-// are done.  Every wait depends only on phases earlier in the sequence (S >= 2,
-// and S >= 3 for combine tiles with Y in the ring) or on the dedicated combine
-// workgroups, which only wait on earlier down phases; every workgroup takes
-// its tiles in sequence order, so the launch always drains (all workgroups are
-// co-resident: it is a cooperative launch).
+// Groups and ring: the phases run over groups of `group` consecutive
+// minibatches (the GEMM tiles of a group share each expert's weight panels);
+// minibatch b writes h (and, without saved outputs, Y) into slot b % S, S a
+// multiple of group, so group j holds Sg = S / group slot groups.  Gate|up(j)
+// waits until down(j-Sg) -- and combine(j-Sg) when Y is in the ring -- are
+// done.  Every wait depends only on phases earlier in the sequence (Sg >= 2,
+// and Sg >= 3 for combine tiles with Y in the ring) or on the dedicated
+// combine workgroups, which only wait on earlier down phases; every workgroup
+// takes its tiles in sequence order, so the launch always drains (all
+// workgroups are co-resident: it is a cooperative launch).  Outputs do not
+// depend on the grouping: every output row is computed by the same tile code.
 //
 // Cross-XCD visibility: each XCD has its own L2, so producers end a tile with
 // every wave's stores complete, a barrier, and one agent-scope release
@@ -52,20 +56,23 @@ namespace {
 enum PhaseKind { kGateUp = 0, kCombine = 1, kDown = 2 };
 constexpr int kCombTilesTok = 16;  // tokens per combine tile
 
-// Cursor over the phases of the tile sequence.  Step s holds gate|up(s), then
-// (with combine tiles) combine(s-2), then down(s-1), each only if its
-// minibatch exists: gate|up(0), gate|up(1), down(0), gate|up(2), combine(0),
-// down(1), ...  Every phase depends only on phases at least one phase earlier.
+// Cursor over the phases of the tile sequence, in units of minibatch groups
+// (a group is `group` consecutive minibatches whose GEMM tiles run as one
+// phase, so an expert's weight panels serve the row tiles of all of them).
+// Step s holds gate|up(s), then (with combine tiles) combine(s-2), then
+// down(s-1), each only if its group exists: gate|up(0), gate|up(1), down(0),
+// gate|up(2), combine(0), down(1), ...  Every phase depends only on phases at
+// least one phase earlier.
 struct PhaseCursor {
-    int s = 0, slot = -1, kind = 0, b = 0;
-    __device__ bool next(int nmb, bool with_combine) {
+    int s = 0, slot = -1, kind = 0, j = 0;
+    __device__ bool next(int ng, bool with_combine) {
         for (;;) {
             if (++slot > 2) { slot = 0; ++s; }
-            if (s > nmb + 1) return false;
-            if (slot == 0) { kind = kGateUp; b = s; }
-            else if (slot == 1) { if (!with_combine) continue; kind = kCombine; b = s - 2; }
-            else { kind = kDown; b = s - 1; }
-            if (b >= 0 && b < nmb) return true;
+            if (s > ng + 1) return false;
+            if (slot == 0) { kind = kGateUp; j = s; }
+            else if (slot == 1) { if (!with_combine) continue; kind = kCombine; j = s - 2; }
+            else { kind = kDown; j = s - 1; }
+            if (j >= 0 && j < ng) return true;
         }
     }
 };
@@ -125,9 +132,38 @@ __device__ __attribute__((noinline)) void mx_tile_fn(const MxGemmArgs p, int e, 
     mx_gemm_tile<EPI>(p, e, ml, ntile, smem);
 }
 
-__device__ __forceinline__ int mb_tiles(const MegaArgs& a, int b, int NT) {
-    const int32_t* mt = a.mt_all + (int64_t)b * a.mt_ld;
-    return (mt[a.e_end] - mt[0]) * NT;
+__device__ __forceinline__ const int32_t* mt_of(const MegaArgs& a, int b) { return a.mt_all + (int64_t)b * a.mt_ld; }
+
+__device__ __forceinline__ int tokens_of(const MegaArgs& a, int b) { return min(a.Mb, a.T - b * a.Mb); }
+
+// M tiles of experts [0, e) summed over the minibatches [b0, b1)
+__device__ __forceinline__ int group_mtiles_before(const MegaArgs& a, int b0, int b1, int e) {
+    int n = 0;
+    for (int b = b0; b < b1; ++b) n += mt_of(a, b)[e] - mt_of(a, b)[0];
+    return n;
+}
+
+// Tile lv of a GEMM phase over minibatches [b0, b1): expert-major, then N
+// tile, then M tile, the M tiles of expert e running over minibatch b0's, then
+// b0+1's, ...: returns the minibatch b and the tile (e, ml, ntile) in it.
+__device__ __forceinline__ void group_tile(const MegaArgs& a, int b0, int b1, int NT, int lv, int& b, int& e,
+                                           int& ml, int& ntile) {
+    int lo = 0, hi = a.e_end - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (group_mtiles_before(a, b0, b1, mid) * NT <= lv) lo = mid; else hi = mid - 1;
+    }
+    e = lo;
+    const int loc = lv - group_mtiles_before(a, b0, b1, e) * NT;
+    const int mte = group_mtiles_before(a, b0, b1, e + 1) - group_mtiles_before(a, b0, b1, e);
+    ntile = loc / mte;
+    int m = loc - ntile * mte;
+    for (b = b0; b < b1 - 1; ++b) {
+        const int mb = mt_of(a, b)[e + 1] - mt_of(a, b)[e];
+        if (m < mb) break;
+        m -= mb;
+    }
+    ml = m;
 }
 
 }  // namespace
@@ -175,16 +211,20 @@ void mega_kernel(MegaArgs a) {
     const int G = gridDim.x - a.comm, g = blockIdx.x - a.comm;  // GEMM workgroups
     const bool comb_tiles = a.comm == 0;                      // combine as tiles of the GEMM workgroups
     const int comb_target = comb_tiles ? G : a.comm;
+    const int ng = ceil_div(a.nmb, a.group), Sg = a.S / a.group;  // groups; ring slots in groups
 
     if ((int)blockIdx.x < a.comm) {
-        // ---- combine workers: minibatch by minibatch, tokens split in contiguous chunks
-        for (int b = 0; b < a.nmb; ++b) {
-            if (!wait_counter(a, d_done + b, G, 2, &s_flag, true)) return;
-            const int Tm = min(a.Mb, a.T - b * a.Mb);
-            const int chunk = ceil_div(Tm, a.comm);
-            const int c0 = min(Tm, (int)blockIdx.x * chunk), c1 = min(Tm, c0 + chunk);
-            combine_range(a, b, c0, c1, smem);
-            signal_counter(comb_done + b);
+        // ---- combine workers: group by group, each minibatch's tokens split in
+        // contiguous chunks
+        for (int j = 0; j < ng; ++j) {
+            if (!wait_counter(a, d_done + j, G, 2, &s_flag, true)) return;
+            for (int b = j * a.group; b < min(a.nmb, (j + 1) * a.group); ++b) {
+                const int Tm = tokens_of(a, b);
+                const int chunk = ceil_div(Tm, a.comm);
+                const int c0 = min(Tm, (int)blockIdx.x * chunk), c1 = min(Tm, c0 + chunk);
+                combine_range(a, b, c0, c1, smem);
+            }
+            signal_counter(comb_done + j);
         }
         return;
     }
@@ -193,54 +233,64 @@ void mega_kernel(MegaArgs a) {
     // finished all of their tiles of that phase (each releases once per phase,
     // owning tiles in it or not), so a phase is complete at G.
     const int per = G >> 3, xcd = g & 7, local = g >> 3;
-    auto phase_tiles = [&](int kind, int b) -> int {
-        if (kind == kGateUp) return mb_tiles(a, b, NT1);
-        if (kind == kDown) return mb_tiles(a, b, NT2);
-        return ceil_div(min(a.Mb, a.T - b * a.Mb), kCombTilesTok);
+    auto phase_tiles = [&](int kind, int j) -> int {
+        const int b0 = j * a.group, b1 = min(a.nmb, b0 + a.group);
+        if (kind == kCombine) {
+            int n = 0;
+            for (int b = b0; b < b1; ++b) n += ceil_div(tokens_of(a, b), kCombTilesTok);
+            return n;
+        }
+        return group_mtiles_before(a, b0, b1, a.e_end) * (kind == kGateUp ? NT1 : NT2);
     };
-    auto counter_of = [&](int kind, int b) -> int* {
-        return kind == kGateUp ? gu_done + b : (kind == kDown ? d_done + b : comb_done + b);
+    auto counter_of = [&](int kind, int j) -> int* {
+        return kind == kGateUp ? gu_done + j : (kind == kDown ? d_done + j : comb_done + j);
     };
     PhaseCursor cur;
-    bool more = cur.next(a.nmb, comb_tiles);
+    bool more = cur.next(ng, comb_tiles);
     int64_t qstart = 0;
-    int qtiles = phase_tiles(cur.kind, cur.b);
+    int qtiles = phase_tiles(cur.kind, cur.j);
     bool ready = false;  // inputs of the current phase waited for
     for (int it = 0;; ++it) {
         const int64_t v = (int64_t)it * G + xcd * per + local;
         while (more && v >= qstart + qtiles) {  // done with this phase: publish
-            signal_counter(counter_of(cur.kind, cur.b));
+            signal_counter(counter_of(cur.kind, cur.j));
             qstart += qtiles;
-            more = cur.next(a.nmb, comb_tiles);
-            if (more) qtiles = phase_tiles(cur.kind, cur.b);
+            more = cur.next(ng, comb_tiles);
+            if (more) qtiles = phase_tiles(cur.kind, cur.j);
             ready = false;
         }
         if (!more) break;
-        const int kind = cur.kind, b = cur.b;
+        const int kind = cur.kind, j = cur.j;
+        const int b0 = j * a.group, b1 = min(a.nmb, b0 + a.group);
         if (!ready) {
-            if (kind == kGateUp && b >= a.S) {  // ring slot b % S free again
-                if (!wait_counter(a, d_done + (b - a.S), G, 0, &s_flag, false)) return;
-                if (y_in_ring && !wait_counter(a, comb_done + (b - a.S), comb_target, 1, &s_flag, false)) return;
+            if (kind == kGateUp && j >= Sg) {  // the group's ring slots free again
+                if (!wait_counter(a, d_done + (j - Sg), G, 0, &s_flag, false)) return;
+                if (y_in_ring && !wait_counter(a, comb_done + (j - Sg), comb_target, 1, &s_flag, false)) return;
             }
-            if (kind == kDown && !wait_counter(a, gu_done + b, G, 3, &s_flag, true)) return;
-            if (kind == kCombine && !wait_counter(a, d_done + b, G, 2, &s_flag, true)) return;
+            if (kind == kDown && !wait_counter(a, gu_done + j, G, 3, &s_flag, true)) return;
+            if (kind == kCombine && !wait_counter(a, d_done + j, G, 2, &s_flag, true)) return;
             ready = true;
         }
-        const int lv = (int)(v - qstart);
+        int lv = (int)(v - qstart);
         if (kind == kCombine) {
-            const int Tm = min(a.Mb, a.T - b * a.Mb);
-            combine_range(a, b, lv * kCombTilesTok, min(Tm, (lv + 1) * kCombTilesTok), smem);
+            int b = b0;
+            for (; b < b1 - 1; ++b) {
+                const int nt = ceil_div(tokens_of(a, b), kCombTilesTok);
+                if (lv < nt) break;
+                lv -= nt;
+            }
+            combine_range(a, b, lv * kCombTilesTok, min(tokens_of(a, b), (lv + 1) * kCombTilesTok), smem);
             continue;
         }
+        int b, e, ml, ntile;
+        group_tile(a, b0, b1, kind == kGateUp ? NT1 : NT2, lv, b, e, ml, ntile);
         const uint8_t* lay = a.lay0 + (int64_t)b * a.lay_bytes;
         const int32_t* mt = a.mt_all + (int64_t)b * a.mt_ld;
         const LayoutHeader* hdr = (const LayoutHeader*)lay;
         uint8_t* slot = a.slot0 + (int64_t)(b % a.S) * a.slot_bytes;
         uint8_t* svb = a.saved_mb0 ? a.saved_mb0 + (int64_t)b * a.sv_mb : nullptr;
         uint16_t* Y = svb ? (uint16_t*)(svb + a.sv_y) : (uint16_t*)(slot + a.sl_y);
-        int e, ml, ntile;
         if (kind == kGateUp) {
-            tile_coords(mt, 0, a.e_end, NT1, lv, e, ml, ntile);
             if constexpr (kMx) {
                 MxGemmArgs m = a.m1;
                 m.a_row_map = (const int32_t*)(lay + a.ly_prow_token);
@@ -257,7 +307,6 @@ void mega_kernel(MegaArgs a) {
                 gemm_tile<kEpiSwiGLU>(gg, e, ml, ntile, smem);
             }
         } else {
-            tile_coords(mt, 0, a.e_end, NT2, lv, e, ml, ntile);
             if constexpr (kMx) {
                 MxGemmArgs m = a.m2;
                 m.A = slot + a.sl_hq; m.SA = slot + a.sl_sh;

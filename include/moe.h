@@ -76,7 +76,10 @@ typedef struct moe_cfg {
     int32_t E;          /* experts on this GPU: 1..256 */
     int32_t k;          /* experts per token: 1..min(E, 16) */
     int32_t minibatch;  /* tokens per ring slot; 0 = automatic (see moe_query_sizes) */
-    int32_t ring_slots; /* ring token buffer slots; 0 = automatic (3) */
+    int32_t ring_slots; /* ring token buffer slots (one minibatch each); 0 = automatic:
+                           three groups of minibatches, a group being the
+                           minibatches (~8192 tokens) whose expert GEMMs the
+                           layer kernel runs as one phase */
     int32_t comm_cus;   /* workgroups (one per CU) dedicated to combine in the
                            persistent layer kernel; 0 = automatic: none, combine
                            runs as tiles of the GEMM workgroups */

@@ -57,11 +57,11 @@ def test_validate_cfg(kw, want):
 def test_query_sizes_h7168_i2048():
     cfg = moe.make_cfg(16384, 7168, 2048, 32, 8, minibatch=2560)
     s = moe.moe_query_sizes(cfg)
-    assert s.minibatch == 2560 and s.num_minibatches == 7 and s.ring_slots == 3 and s.comm_cus == 0
+    assert s.minibatch == 2560 and s.num_minibatches == 7 and s.ring_slots == 9 and s.comm_cus == 0
     # packed: gate|up [E,2I,H] + down [E,H,I], bf16
     assert s.packed_weights >= 32 * 3 * 7168 * 2048 * 2
     # per slot the Y buffer alone holds (rows + padding) x H bf16
-    assert s.workspace_fwd >= 3 * (2560 * 8) * 7168 * 2
+    assert s.workspace_fwd >= 9 * (2560 * 8) * 7168 * 2
     # explicit ring size and combine workgroups are honoured (ring at most one slot per minibatch)
     s2 = moe.moe_query_sizes(moe.make_cfg(16384, 7168, 2048, 32, 8, minibatch=2560, ring_slots=2, comm_cus=8))
     assert s2.ring_slots == 2 and s2.comm_cus == 8 and s2.workspace_fwd < s.workspace_fwd

@@ -32,6 +32,12 @@ CASES = [
     (_wl("lk_mx", T=900, H=512, I=256, E=4, k=2, minibatch=160, router_bias="zipf", prec="mxfp8"), 0, 0, False),
     (_wl("lk_mx_saved", T=900, H=512, I=256, E=4, k=2, minibatch=160, prec="mxfp8"), 3, 8, True),
     (_wl("lk_mx_tiles", T=900, H=512, I=256, E=4, k=2, minibatch=128, prec="mxfp8"), 0, 0, False),
+    # minibatches grouped into phases (ring slots = 3 groups; ragged last group)
+    (_wl("lk_group2", T=1500, H=256, I=128, E=8, k=2, minibatch=192, router_bias="normal"), 6, 0, False),
+    (_wl("lk_group3_saved", T=1500, H=256, I=128, E=8, k=2, minibatch=160), 9, 0, True),
+    (_wl("lk_group2_comm8", T=1500, H=256, I=128, E=8, k=2, minibatch=192), 6, 8, False),
+    (_wl("lk_group_auto", T=2000, H=256, I=192, E=6, k=3, minibatch=256), 0, 0, False),
+    (_wl("lk_mx_group2", T=1200, H=512, I=256, E=4, k=2, minibatch=128, prec="mxfp8"), 6, 0, False),
 ]
 
 
