@@ -40,8 +40,6 @@ void grouped_gemm_kernel(GemmArgs p) {
 // expert e, minibatch by minibatch in order (a fixed summation order).
 // ---------------------------------------------------------------------------
 
-constexpr int kWgM = 4;  // M tiles per group in the weight-gradient tile order
-
 // K sequence of expert e's rows: for each minibatch b its padded row range
 // [mt_b[e], mt_b[e+1]) x BM, in 32-row K steps; A and B copies of
 // minibatch b lie a_mb / b_mb bytes after minibatch 0's.
@@ -49,13 +47,19 @@ struct SegmentK {
     const int32_t* mt;  // [nmb][mt_ld]
     int mt_ld, e, nmb;
     int64_t a_mb, b_mb;
-    int b = 0, step = 0;
-    __device__ __forceinline__ int steps_of(int bb) const {
-        return (mt[(int64_t)bb * mt_ld + e + 1] - mt[(int64_t)bb * mt_ld + e]) * (BM / kBK);
-    }
+    // current minibatch, K step within it, its step count and first row: the
+    // tile map is read only when the sequence enters the next minibatch
+    int b = -1, step = 0, nsteps = 0;
+    int64_t row0 = 0;
     __device__ __forceinline__ void next(int64_t& a_off, int64_t& b_off) {
-        while (b < nmb && step >= steps_of(b)) { ++b; step = 0; }
-        const int64_t kbyte = ((int64_t)mt[(int64_t)b * mt_ld + e] * BM + (int64_t)step * kBK) * 2;
+        while (step >= nsteps && b + 1 < nmb) {
+            ++b;
+            const int m0 = mt[(int64_t)b * mt_ld + e], m1 = mt[(int64_t)b * mt_ld + e + 1];
+            row0 = (int64_t)m0 * BM;
+            nsteps = (m1 - m0) * (BM / kBK);
+            step = 0;
+        }
+        const int64_t kbyte = (row0 + (int64_t)step * kBK) * 2;
         a_off = (int64_t)b * a_mb + kbyte;
         b_off = (int64_t)b * b_mb + kbyte;
         ++step;
@@ -67,20 +71,22 @@ void wgrad_kernel(WgradArgs p) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int MT = ceil_div(p.M, BM), NT = ceil_div(p.N, BN);
-    const int total = p.Et * MT * NT;
     const int G = gridDim.x, per = G >> 3;
     const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+    // Every expert's MT x NT tile grid is cut into mq x nq = 8 blocks, block
+    // (xcd % mq, xcd / mq) going to XCD xcd, so each A panel is fetched into
+    // nq XCDs' L2s and each B panel into mq (the host picks the cut with the
+    // least traffic).  An XCD's 'per' workgroups walk its blocks expert by
+    // expert, M tile fastest.
+    const int bm = xcd % p.mq, bn = xcd / p.mq;
+    const int mlo = bm * MT / p.mq, mhi = (bm + 1) * MT / p.mq;
+    const int nlo = bn * NT / p.nq, nhi = (bn + 1) * NT / p.nq;
+    const int bmt = mhi - mlo, cnt = bmt * (nhi - nlo);
     for (int it = 0;; ++it) {
-        const int v = it * G + xcd * per + local;
-        if (v >= total) break;
-        // tile order: expert-major, then groups of kWgM M tiles; inside a group
-        // the M tile is fastest, then N.  The 'per' consecutive tiles of one XCD
-        // then cover about kWgM M panels x per/kWgM N panels, which they share
-        // through its L2 (a row of N tiles would share only one A panel).
-        const int e = v / (MT * NT), loc = v - e * MT * NT;
-        const int gm0 = (loc / (kWgM * NT)) * kWgM, gm = min(kWgM, MT - gm0);
-        const int gl = loc - gm0 * NT;
-        const int m0 = (gm0 + gl % gm) * BM, n0 = (gl / gm) * BN;
+        const int li = it * per + local;
+        if (cnt == 0 || li >= p.Et * cnt) break;
+        const int e = li / cnt, t = li - e * cnt;
+        const int m0 = (mlo + t % bmt) * BM, n0 = (nlo + t / bmt) * BN;
         int KT = 0;
         for (int b = 0; b < p.nmb; ++b) KT += (p.mt[(int64_t)b * p.mt_ld + e + 1] - p.mt[(int64_t)b * p.mt_ld + e]) * (BM / kBK);
         uint32_t aoff[4], boff[4];
@@ -117,7 +123,16 @@ void wgrad_kernel(WgradArgs p) {
 }
 
 void launch_wgrad(const WgradArgs& a, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL(wgrad_kernel, dim3(grid), dim3(kGemmThreads), 0, stream, a);
+    // cut with the least L2 fill traffic: A panels (M rows) land in nq XCDs, B
+    // panels (N rows) in mq
+    WgradArgs w = a;
+    const int64_t cost[4] = {(int64_t)a.M + 8ll * a.N, 2ll * a.M + 4ll * a.N, 4ll * a.M + 2ll * a.N, 8ll * a.M + a.N};
+    int best = 0;
+    for (int i = 1; i < 4; ++i)
+        if (cost[i] < cost[best]) best = i;
+    w.mq = 8 >> best;
+    w.nq = 1 << best;
+    hipLaunchKernelGGL(wgrad_kernel, dim3(grid), dim3(kGemmThreads), 0, stream, w);
 }
 
 void launch_grouped_gemm(const GemmArgs& a, GemmEpilogue epi, int grid, hipStream_t stream) {

@@ -160,8 +160,10 @@ struct WgradArgs {
     float* C1;
     float* Cs0;
     float* Cs1;
+    int mq, nq;  // XCD blocking of each expert's tile grid (set by launch_wgrad)
 };
 
+// grid: a multiple of 8 workgroups (XCD-aware dealing).
 void launch_wgrad(const WgradArgs& a, int grid, hipStream_t stream);
 
 void launch_grouped_gemm(const GemmArgs& a, GemmEpilogue epi, int grid, hipStream_t stream);
