@@ -54,7 +54,12 @@ struct SegmentK {
     __device__ __forceinline__ void next(int64_t& a_off, int64_t& b_off) {
         while (step >= nsteps && b + 1 < nmb) {
             ++b;
-            const int m0 = mt[(int64_t)b * mt_ld + e], m1 = mt[(int64_t)b * mt_ld + e + 1];
+            // the tile map is read-only here: read it through the constant
+            // address space (scalar loads, counted by lgkmcnt) so that the
+            // ring's vmcnt accounting sees only the ring's own loads
+            const __attribute__((address_space(4))) int32_t* cmt =
+                (const __attribute__((address_space(4))) int32_t*)mt;
+            const int m0 = cmt[(int64_t)b * mt_ld + e], m1 = cmt[(int64_t)b * mt_ld + e + 1];
             row0 = (int64_t)m0 * BM;
             nsteps = (m1 - m0) * (BM / kBK);
             step = 0;

@@ -30,18 +30,6 @@ __device__ __forceinline__ void mfma_block(floatx16 (&acc)[4][4], const bf16x8 (
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
 }
 
-// Wait until at most c K steps (8 loads each) of this wave are in flight and
-// all of its LDS reads are done.  c is clamped to [0, kStages-1].
-__device__ __forceinline__ void wait_vm_steps(int c) {
-    switch (c < 0 ? 0 : c) {
-        case 0: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); break;
-        case 1: asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory"); break;
-        case 2: asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory"); break;
-        case 3: asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)" ::: "memory"); break;
-        default: asm volatile("s_waitcnt vmcnt(32) lgkmcnt(0)" ::: "memory"); break;
-    }
-}
-static_assert(kStages <= 5, "wait_vm_steps covers at most 4 steps in flight");
 
 // K sequence of a dense GEMM: K step kt sits kt * 64 bytes into every row.
 struct DenseK {
@@ -60,7 +48,9 @@ template <class KIt>
 __device__ __forceinline__ void tile_mainloop(floatx16 (&acc)[4][4], uint8_t* smem, const char* a_base,
                                               const uint32_t (&aoff)[4], const char* b_base,
                                               const uint32_t (&boff)[4], int KT, KIt kit) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    // the wave index is uniform: keep it (and every LDS base built from it) scalar
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 1, wn = wave & 1;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -68,10 +58,18 @@ __device__ __forceinline__ void tile_mainloop(floatx16 (&acc)[4][4], uint8_t* sm
         for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
     if (KT <= 0) return;
 
-    auto issue = [&](int kt) {
-        int64_t ka, kb;
-        kit.next(ka, kb);
-        uint8_t* base = smem + (kt % kStages) * kStageBytes + (wave * 64) * kRowBytes;
+    // Byte offsets of the next K step to load.  Past the last step the loads
+    // repeat it: they land in the slot of a step every wave has finished with,
+    // so the loads need no branch (and interleave with the MFMAs) and every
+    // vmcnt wait below is a constant.
+    int64_t ka = 0, kb = 0;
+    int issued = 0;
+    auto advance = [&]() {
+        if (issued < KT) kit.next(ka, kb);
+        ++issued;
+    };
+    auto issue = [&](int slot) {
+        uint8_t* base = smem + slot * kStageBytes + (wave * 64) * kRowBytes;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             __builtin_amdgcn_global_load_lds((gbl_cvoid*)(a_base + ka + aoff[i]), (lds_void*)(base + i * 1024), 16, 0, 0);
@@ -79,12 +77,12 @@ __device__ __forceinline__ void tile_mainloop(floatx16 (&acc)[4][4], uint8_t* sm
         for (int i = 0; i < 4; ++i)
             __builtin_amdgcn_global_load_lds((gbl_cvoid*)(b_base + kb + boff[i]), (lds_void*)(base + kStageA + i * 1024), 16, 0, 0);
     };
-    // MFMA operand fragments of k-step kk (16 deep) of K step kt.
+    // MFMA operand fragments of k-step kk (16 deep) of the K step in slot `slot`.
     const int fr = lane & 31;
     const int arow_b = (wm * 128 + fr) * kRowBytes, brow_b = kStageA + (wn * 128 + fr) * kRowBytes;
     const int fsw = swz(fr);
-    auto frags = [&](int kt, int kk, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
-        const uint8_t* st = smem + (kt % kStages) * kStageBytes;
+    auto frags = [&](int slot, int kk, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
+        const uint8_t* st = smem + slot * kStageBytes;
         const int pc = ((kk * 2 + (lane >> 5)) ^ fsw) * 16;
 #pragma unroll
         for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8*)(st + arow_b + i * 32 * kRowBytes + pc);
@@ -93,26 +91,33 @@ __device__ __forceinline__ void tile_mainloop(floatx16 (&acc)[4][4], uint8_t* sm
     };
 
     // Ring protocol (S = kStages slots, K step j lives in slot j % S, each
-    // step is 8 direct-to-LDS loads per lane, counted by vmcnt):
-    //  - prologue: issue steps 0..min(S,KT)-1, wait for step 0;
-    //  - K step kt: before the barrier wait for step kt+1, i.e. allow the
-    //    c = min(KT-2-kt, S-2) newer steps in flight (vmcnt(8c)), and for this
-    //    wave's own LDS reads of step kt (lgkmcnt(0)); after the barrier no
-    //    wave reads step kt any more, so its slot takes step kt+S.
+    // step is 8 direct-to-LDS loads per lane, counted by vmcnt; S steps are
+    // always in flight):
+    //  - prologue: issue steps 0..S-1, wait for step 0 (vmcnt(8(S-1)));
+    //  - K step kt: before the barrier wait for step kt+1 (the S-2 newer steps
+    //    stay in flight: vmcnt(8(S-2))) and for this wave's own LDS reads of
+    //    step kt (lgkmcnt(0)); after the barrier no wave reads step kt any
+    //    more, so its slot takes step kt+S, loaded under the next 16 MFMAs.
     // First the previous tile's stores leave the vmcnt count and every wave is
     // done reading the previous tile's stages.
+    static_assert(kStages == 5, "the vmcnt immediates below assume 5 stages of 8 loads");
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < kStages; ++j)
-        if (j < KT) issue(j);
-    wait_vm_steps(KT - 1 < kStages - 1 ? KT - 1 : kStages - 1);
+    for (int j = 0; j < kStages; ++j) {
+        advance();
+        issue(j);
+    }
+    asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
     __syncthreads();
     bf16x8 a0[4], b0[4], a1[4], b1[4];
     frags(0, 0, a0, b0);
+    int slot = 0;  // slot of step kt
     for (int kt = 0; kt < KT; ++kt) {
+        const int next_slot = slot + 1 == kStages ? 0 : slot + 1;
+        advance();  // offsets of step kt + S
         // k-step 0 of this K step: read k-step 1's fragments under 16 MFMAs
-        frags(kt, 1, a1, b1);
+        frags(slot, 1, a1, b1);
         mfma_block(acc, a0, b0);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
@@ -121,14 +126,13 @@ __device__ __forceinline__ void tile_mainloop(floatx16 (&acc)[4][4], uint8_t* sm
         }
         __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 8, 0);
         __builtin_amdgcn_sched_barrier(0);
-        // Every wave has read step kt (its reads done) and step kt+1 has
-        // landed: refill step kt's slot with step kt+kStages and read step
-        // kt+1's first fragments under the last 16 MFMAs.
-        const int ahead = KT - 2 - kt;
-        wait_vm_steps(ahead < kStages - 2 ? ahead : kStages - 2);
+        // Every wave has read step kt and step kt+1 has landed: refill step
+        // kt's slot with step kt+S and read step kt+1's first fragments under
+        // the last 16 MFMAs.
+        asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)" ::: "memory");
         __syncthreads();
-        if (kt + kStages < KT) issue(kt + kStages);
-        frags(kt + 1, 0, a0, b0);  // a stale but in-bounds read after the last step
+        issue(slot);
+        frags(next_slot, 0, a0, b0);  // a stale but in-bounds read after the last step
         mfma_block(acc, a1, b1);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
@@ -138,6 +142,7 @@ __device__ __forceinline__ void tile_mainloop(floatx16 (&acc)[4][4], uint8_t* sm
         }
         __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 8, 0);
         __builtin_amdgcn_sched_barrier(0);
+        slot = next_slot;
     }
 }
 

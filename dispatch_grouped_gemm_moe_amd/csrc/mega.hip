@@ -124,13 +124,6 @@ __device__ __forceinline__ void signal_counter(int* ctr) {
     if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// The MXFP8 tile bodies are called as functions of their own: inlined side by
-// side, register allocation spilled inside their K loops (the bf16 bodies
-// inline without that, and run faster inlined).
-template <int EPI>
-__device__ __attribute__((noinline)) void mx_tile_fn(const MxGemmArgs p, int e, int ml, int ntile, uint8_t* smem) {
-    mx_gemm_tile<EPI>(p, e, ml, ntile, smem);
-}
 
 __device__ __forceinline__ const int32_t* mt_of(const MegaArgs& a, int b) { return a.mt_all + (int64_t)b * a.mt_ld; }
 
@@ -297,7 +290,7 @@ void mega_kernel(MegaArgs a) {
                 m.mt_start = mt; m.hdr = hdr;
                 m.Cq = slot + a.sl_hq; m.Cs = slot + a.sl_sh;
                 m.GU = svb ? (float*)svb : nullptr;
-                mx_tile_fn<kEpiSwiGLU>(m, e, ml, ntile, smem);
+                mx_gemm_tile<kEpiSwiGLU>(m, e, ml, ntile, smem);
             } else {
                 GemmArgs gg = a.g1;
                 gg.a_row_map = (const int32_t*)(lay + a.ly_prow_token);
@@ -312,7 +305,7 @@ void mega_kernel(MegaArgs a) {
                 m.A = slot + a.sl_hq; m.SA = slot + a.sl_sh;
                 m.mt_start = mt; m.hdr = hdr;
                 m.C = Y;
-                mx_tile_fn<kEpiStore>(m, e, ml, ntile, smem);
+                mx_gemm_tile<kEpiStore>(m, e, ml, ntile, smem);
             } else {
                 GemmArgs gg = a.g2;
                 gg.A = (const uint16_t*)(slot + a.sl_h);

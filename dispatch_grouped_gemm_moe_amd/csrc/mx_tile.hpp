@@ -21,21 +21,13 @@ constexpr int kMxLoads = 10;  // direct-to-LDS loads per lane per K step
 
 __device__ __forceinline__ int mx_swz(int r) { return (r >> 2) & 3; }
 
-__device__ __forceinline__ void mx_wait_steps(int c) {
-    switch (c < 0 ? 0 : c) {
-        case 0: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); break;
-        case 1: asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)" ::: "memory"); break;
-        case 2: asm volatile("s_waitcnt vmcnt(20) lgkmcnt(0)" ::: "memory"); break;
-        default: asm volatile("s_waitcnt vmcnt(30) lgkmcnt(0)" ::: "memory"); break;
-    }
-}
-static_assert(kMxStages <= 4, "mx_wait_steps covers at most 3 steps in flight");
 
 // One 256 x 256 output tile (expert e, M tile ml of the expert, N tile ntile)
 // of the MXFP8 grouped GEMM with its epilogue; smem is the kMxStages LDS ring.
 template <int EPI>
 __device__ __forceinline__ void mx_gemm_tile(const MxGemmArgs p, int e, int ml, int ntile, uint8_t* smem) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar LDS bases
     const int wm = wave >> 1, wn = wave & 1;
     const int KT = p.K / 64;
     const int mt0 = p.mt_start[e];
@@ -62,8 +54,11 @@ __device__ __forceinline__ void mx_gemm_tile(const MxGemmArgs p, int e, int ml, 
     const int sarow = p.a_row_map ? p.a_row_map[prow0 + srow] : prow0 + srow;
     const uint32_t saoff = (uint32_t)sarow * 4, sboff = (uint32_t)min(n0 + srow, p.N - 1) * 4;
 
-    auto issue = [&](int kt) {
-        uint8_t* st = smem + (kt % kMxStages) * kMxStageBytes;
+    // Loads past the last K step repeat it (into the slot of a step every wave
+    // has finished with), so they need no branch and the waits are constants.
+    auto issue = [&](int kt_, int slot) {
+        const int kt = kt_ < KT ? kt_ : KT - 1;
+        uint8_t* st = smem + slot * kMxStageBytes;
         uint8_t* base = st + (wave * 64) * kMxRow;
         const uint32_t kb = (uint32_t)kt * 64;
 #pragma unroll
@@ -81,8 +76,8 @@ __device__ __forceinline__ void mx_gemm_tile(const MxGemmArgs p, int e, int ml, 
     const int fsw = mx_swz(fr);
     const int pc0 = (half ^ fsw) * 16, pc1 = ((2 + half) ^ fsw) * 16;
     const int arow_b = (wm * 128 + fr) * kMxRow, brow_b = kMxStageA + (wn * 128 + fr) * kMxRow;
-    auto frags = [&](int kt, intx8 (&a)[4], intx8 (&b)[4], int (&sa)[4], int (&sb)[4]) {
-        const uint8_t* st = smem + (kt % kMxStages) * kMxStageBytes;
+    auto frags = [&](int slot, intx8 (&a)[4], intx8 (&b)[4], int (&sa)[4], int (&sb)[4]) {
+        const uint8_t* st = smem + slot * kMxStageBytes;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const intx4 lo4 = *(const intx4*)(st + arow_b + i * 32 * kMxRow + pc0);
@@ -112,35 +107,39 @@ __device__ __forceinline__ void mx_gemm_tile(const MxGemmArgs p, int e, int ml, 
                                                                              sb[j]);
     };
 
-    // Ring protocol as in the bf16 path, with 10 loads per K step: before
-    // computing step kt, wait until step kt+1 has landed and this wave's
+    // Ring protocol as in the bf16 path, with 10 loads per K step and every
+    // slot always in flight: before computing step kt, wait until step kt+1
+    // has landed (the 2 newer steps stay in flight: vmcnt(20)) and this wave's
     // reads of step kt are done, barrier, refill step kt's slot with step
     // kt + kMxStages, and read step kt+1's fragments under step kt's MFMAs.
+    static_assert(kMxStages == 4, "the vmcnt immediates below assume 4 stages of 10 loads");
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < kMxStages; ++j)
-        if (j < KT) issue(j);
-    mx_wait_steps(KT - 1 < kMxStages - 1 ? KT - 1 : kMxStages - 1);
+    for (int j = 0; j < kMxStages; ++j) issue(j, j);
+    asm volatile("s_waitcnt vmcnt(30)" ::: "memory");
     __syncthreads();
     intx8 a0[4], b0[4], a1[4], b1[4];
     int s0a[4], s0b[4], s1a[4], s1b[4];
     frags(0, a0, b0, s0a, s0b);
+    int slot = 0;  // slot of step kt
     auto step = [&](int kt, intx8 (&ac)[4], intx8 (&bc)[4], int (&sac)[4], int (&sbc)[4], intx8 (&an)[4],
                     intx8 (&bn)[4], int (&san)[4], int (&sbn)[4]) {
-        const int ahead = KT - 2 - kt;
-        mx_wait_steps(ahead < kMxStages - 2 ? ahead : kMxStages - 2);
+        const int next_slot = slot + 1 == kMxStages ? 0 : slot + 1;
+        asm volatile("s_waitcnt vmcnt(20) lgkmcnt(0)" ::: "memory");
         __syncthreads();
-        if (kt + kMxStages < KT) issue(kt + kMxStages);
-        frags(kt + 1, an, bn, san, sbn);  // stale but in-bounds on the last step
+        issue(kt + kMxStages, slot);
+        frags(next_slot, an, bn, san, sbn);  // stale but in-bounds on the last step
         mfmas(ac, bc, sac, sbc);
 #pragma unroll
         for (int q = 0; q < 10; ++q) {
             __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedVMEM, 1, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
         }
         __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 6, 0);
         __builtin_amdgcn_sched_barrier(0);
+        slot = next_slot;
     };
     int kt = 0;
     for (; kt + 1 < KT; kt += 2) {
