@@ -22,9 +22,10 @@ namespace moe {
 #pragma clang fp contract(off)
 
 constexpr int kRouteWaveTokens = 4;                       // tokens per wave
-constexpr int kRouteThreads = 256;                        // four waves
+constexpr int kRouteThreads = 512;                        // eight waves
 constexpr int kRouteTokens = kRouteWaveTokens * kRouteThreads / kWave;  // per workgroup
 constexpr int kRouteEC = 32;                              // experts per accumulation pass
+constexpr int kRouteWRow = kRouteEC + 4;                  // padded LDS row (conflict-free 128-bit reads)
 
 // Lane l holds p[l]; returns in lane 0 the fixed halving tree
 // p[l] = p[l] + p[l+s] for s = 32, 16, 8, 4, 2, 1.  At each step only lanes
@@ -41,45 +42,67 @@ __device__ __forceinline__ float lane_tree64(float v) {
 }
 
 // A wave scores 4 tokens against up to 32 experts per pass: lane l runs the
-// partial sums p[l] of all 128 (token, expert) pairs, so one Wr row slice
-// (32 experts, 128 contiguous bytes when E >= 32) is read per lane per step
-// and reused for the 4 tokens; the 4 waves of a workgroup read the same Wr
-// rows at about the same time and share them through L1.
+// partial sums p[l] of all 128 (token, expert) pairs over h = l, l+64, ...
+// The router weight rows of each 64-wide h chunk (32 experts) are staged once
+// per workgroup in LDS, double-buffered, and read by its 8 waves (32 tokens),
+// so a Wr element is fetched once per 32 tokens instead of once per 4.
 template <bool kVec4>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ Wr, const float* __restrict__ bias,
     int T, int H, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     float* __restrict__ logits_out) {
     __shared__ float s_logit[kRouteTokens][kMaxExperts];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ __attribute__((aligned(16))) float s_w[2][kWave][kRouteWRow];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int t0 = blockIdx.x * kRouteTokens;
     const int nt = min(kRouteTokens, T - t0);
     const int tw0 = t0 + wave * kRouteWaveTokens;  // this wave's first token
     const int ntw = max(0, min(kRouteWaveTokens, T - tw0));
+    const int nchunk = H / kWave;
+    // staging: thread tid moves 4 consecutive experts of one h row of a chunk
+    const int sr = tid >> 3, sq = (tid & 7) * 4;
 
     for (int e0 = 0; e0 < E; e0 += kRouteEC) {
+        auto stage = [&](int c, int buf) {
+            const int h = c * kWave + sr;
+            const float* wrow = Wr + (size_t)h * E + e0 + sq;
+            floatx4 w4;
+            if (kVec4) {
+                w4 = (e0 + sq < E) ? *(const floatx4*)wrow : floatx4{0, 0, 0, 0};
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) w4[q] = (e0 + sq + q < E) ? wrow[q] : 0.0f;
+            }
+            *(floatx4*)&s_w[buf][sr][sq] = w4;
+        };
         float acc[kRouteWaveTokens][kRouteEC];
 #pragma unroll
         for (int tt = 0; tt < kRouteWaveTokens; ++tt)
 #pragma unroll
             for (int ee = 0; ee < kRouteEC; ++ee) acc[tt][ee] = 0.0f;
-        for (int h = lane; h < H; h += kWave) {
-            float wv[kRouteEC];
-            const float* wrow = Wr + (size_t)h * E + e0;
-            if (kVec4) {
-#pragma unroll
-                for (int q = 0; q < kRouteEC / 4; ++q) {
-                    const floatx4 w4 = (e0 + 4 * q < E) ? *(const floatx4*)(wrow + 4 * q) : floatx4{0, 0, 0, 0};
-                    wv[4 * q] = w4[0]; wv[4 * q + 1] = w4[1]; wv[4 * q + 2] = w4[2]; wv[4 * q + 3] = w4[3];
-                }
-            } else {
-#pragma unroll
-                for (int ee = 0; ee < kRouteEC; ++ee) wv[ee] = (e0 + ee < E) ? wrow[ee] : 0.0f;
-            }
-            float xv[kRouteWaveTokens];
+        // this lane's token values of chunk c (one h per lane), loaded a chunk ahead
+        auto load_x = [&](int c, uint16_t (&xr)[kRouteWaveTokens]) {
 #pragma unroll
             for (int tt = 0; tt < kRouteWaveTokens; ++tt)
-                xv[tt] = (tt < ntw) ? bf16_to_f32(x[(size_t)(tw0 + tt) * H + h]) : 0.0f;
+                xr[tt] = (tt < ntw) ? x[(size_t)(tw0 + tt) * H + c * kWave + lane] : (uint16_t)0;
+        };
+        uint16_t xnext[kRouteWaveTokens];
+        __syncthreads();  // previous pass done with s_w
+        stage(0, 0);
+        load_x(0, xnext);
+        for (int c = 0; c < nchunk; ++c) {
+            __syncthreads();  // chunk c staged; chunk c-1's buffer free
+            if (c + 1 < nchunk) stage(c + 1, (c + 1) & 1);
+            float xv[kRouteWaveTokens];
+#pragma unroll
+            for (int tt = 0; tt < kRouteWaveTokens; ++tt) xv[tt] = bf16_to_f32(xnext[tt]);
+            if (c + 1 < nchunk) load_x(c + 1, xnext);
+            float wv[kRouteEC];
+#pragma unroll
+            for (int q = 0; q < kRouteEC / 4; ++q) {
+                const floatx4 w4 = *(const floatx4*)&s_w[c & 1][lane][4 * q];
+                wv[4 * q] = w4[0]; wv[4 * q + 1] = w4[1]; wv[4 * q + 2] = w4[2]; wv[4 * q + 3] = w4[3];
+            }
 #pragma unroll
             for (int tt = 0; tt < kRouteWaveTokens; ++tt)
 #pragma unroll
