@@ -50,7 +50,7 @@ struct Plan {
     // under MXFP8) and Y [rpad][H]
     size_t sv_idx, sv_w, sv_mb0, sv_mb, sv_y, saved;
     // backward workspace (bytes)
-    size_t wb_wrt, wb_mt, wb_lay0, lay_bytes, ly_hdr, ly_prow_token, ly_tok_prow, ly_prow_slot;
+    size_t wb_wrt, wb_mt, wb_rows, wb_lay0, lay_bytes, ly_hdr, ly_prow_token, ly_tok_prow, ly_prow_slot;
     size_t wb_dyt, wb_xgt, wb_dgut, wb_ht, wb_dsel, wb_dy, wb_dgu, wb_dh, wb_dx, wb_dgp, ws_bwd;
     size_t wb_dyq, wb_sdy, wb_dguq, wb_sdgu;  // MXFP8 operands of the input-gradient GEMMs
     size_t wb_dlog, wb_dwrp;                  // dense d out / d logits, router-gradient partial sums
@@ -179,6 +179,7 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     o = kAlign;  // device status word
     p->wb_wrt = o; o = align_up(o + (size_t)c->E * H * 4);
     p->wb_mt = o; o = align_up(o + nmb * (Et + 1) * 4);
+    p->wb_rows = o; o = align_up(o + nmb * (Et + 1) * 4);
     p->wb_lay0 = o; o += nmb * p->lay_bytes;
     p->wb_dyt = o; o = align_up(o + nmb * H * rp * 2);
     p->wb_xgt = o; o = align_up(o + nmb * H * rp * 2);
@@ -543,10 +544,11 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
         o.prow_token = (int32_t*)(lay0 + p.ly_prow_token);
         o.tok_prow = (int32_t*)(lay0 + p.ly_tok_prow);
         o.prow_slot = (int32_t*)(lay0 + p.ly_prow_slot);
+        o.rows_e = (int32_t*)(wsb + p.wb_rows);
         o.tok_prow_ld = p.ld_tok_prow;
         LayoutStrides ls{};
         ls.hdr = (int64_t)p.lay_bytes / (int64_t)sizeof(LayoutHeader);
-        ls.mt_start = Et + 1;
+        ls.mt_start = ls.rows_e = Et + 1;
         ls.prow_token = ls.tok_prow = ls.prow_slot = (int64_t)p.lay_bytes / 4;
         TIMED(MOE_K_LAYOUT, s, launch_layout_batched(idx, p.T, p.Mb, E, k, p.shared ? 1 : 0, o, ls, s));
     }
@@ -636,14 +638,14 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
     WgradArgs wa{};  // [dWg | dWu][e] = x_e^T [dG | dU]_e over every row of expert e
     wa.A = xgT_all; wa.B = dGUT_all; wa.ld = rp;
     wa.a_mb = (int64_t)H * rp * 2; wa.b_mb = (int64_t)2 * I * rp * 2;
-    wa.M = H; wa.N = 2 * I; wa.n_split = I; wa.Et = Et; wa.nmb = p.nmb; wa.mt_ld = Et + 1; wa.mt = mt_all;
+    wa.M = H; wa.N = 2 * I; wa.n_split = I; wa.Et = Et; wa.nmb = p.nmb; wa.mt_ld = Et + 1; wa.mt = mt_all; wa.rows = (const int32_t*)(wsb + p.wb_rows);
     wa.C0 = dWg; wa.C1 = dWu;
     wa.Cs0 = p.shared ? dWs : nullptr; wa.Cs1 = p.shared ? dWs + (size_t)H * I : nullptr;
     TIMED(MOE_K_WGRAD, s, launch_wgrad(wa, grid, s));
     WgradArgs wd{};  // dWd[e] = h_e^T dY_e
     wd.A = HT_all; wd.B = dYT_all; wd.ld = rp;
     wd.a_mb = (int64_t)I * rp * 2; wd.b_mb = (int64_t)H * rp * 2;
-    wd.M = I; wd.N = H; wd.n_split = H; wd.Et = Et; wd.nmb = p.nmb; wd.mt_ld = Et + 1; wd.mt = mt_all;
+    wd.M = I; wd.N = H; wd.n_split = H; wd.Et = Et; wd.nmb = p.nmb; wd.mt_ld = Et + 1; wd.mt = mt_all; wd.rows = (const int32_t*)(wsb + p.wb_rows);
     wd.C0 = dWd; wd.C1 = nullptr;
     wd.Cs0 = p.shared ? dWs + (size_t)2 * H * I : nullptr; wd.Cs1 = nullptr;
     TIMED(MOE_K_WGRAD, s, launch_wgrad(wd, grid, s));

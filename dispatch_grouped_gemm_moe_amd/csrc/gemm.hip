@@ -44,7 +44,8 @@ void grouped_gemm_kernel(GemmArgs p) {
 // [mt_b[e], mt_b[e+1]) x BM, in 32-row K steps; A and B copies of
 // minibatch b lie a_mb / b_mb bytes after minibatch 0's.
 struct SegmentK {
-    const int32_t* mt;  // [nmb][mt_ld]
+    const int32_t* mt;    // [nmb][mt_ld]
+    const int32_t* rows;  // [nmb][mt_ld]
     int mt_ld, e, nmb;
     int64_t a_mb, b_mb;
     // current minibatch, K step within it, its step count and first row: the
@@ -59,9 +60,10 @@ struct SegmentK {
             // ring's vmcnt accounting sees only the ring's own loads
             const __attribute__((address_space(4))) int32_t* cmt =
                 (const __attribute__((address_space(4))) int32_t*)mt;
-            const int m0 = cmt[(int64_t)b * mt_ld + e], m1 = cmt[(int64_t)b * mt_ld + e + 1];
-            row0 = (int64_t)m0 * BM;
-            nsteps = (m1 - m0) * (BM / kBK);
+            const __attribute__((address_space(4))) int32_t* crows =
+                (const __attribute__((address_space(4))) int32_t*)rows;
+            row0 = (int64_t)cmt[(int64_t)b * mt_ld + e] * BM;
+            nsteps = ceil_div(crows[(int64_t)b * mt_ld + e], kBK);
             step = 0;
         }
         const int64_t kbyte = (row0 + (int64_t)step * kBK) * 2;
@@ -93,7 +95,7 @@ void wgrad_kernel(WgradArgs p) {
         const int e = li / cnt, t = li - e * cnt;
         const int m0 = (mlo + t % bmt) * BM, n0 = (nlo + t / bmt) * BN;
         int KT = 0;
-        for (int b = 0; b < p.nmb; ++b) KT += (p.mt[(int64_t)b * p.mt_ld + e + 1] - p.mt[(int64_t)b * p.mt_ld + e]) * (BM / kBK);
+        for (int b = 0; b < p.nmb; ++b) KT += ceil_div(p.rows[(int64_t)b * p.mt_ld + e], kBK);
         uint32_t aoff[4], boff[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -102,7 +104,7 @@ void wgrad_kernel(WgradArgs p) {
             aoff[i] = (uint32_t)(((int64_t)min(m0 + r, p.M - 1) * p.ld + lchunk * 8) * 2);
             boff[i] = (uint32_t)(((int64_t)min(n0 + r, p.N - 1) * p.ld + lchunk * 8) * 2);
         }
-        SegmentK kit{p.mt, p.mt_ld, e, p.nmb, p.a_mb, p.b_mb};
+        SegmentK kit{p.mt, p.rows, p.mt_ld, e, p.nmb, p.a_mb, p.b_mb};
         floatx16 acc[4][4];
         tile_mainloop(acc, smem, (const char*)p.A, aoff, (const char*)p.B, boff, KT, kit);
         // columns < n_split go to C0, the rest to C1 (column - n_split); the

@@ -19,6 +19,7 @@ struct LayoutOut {
     int32_t* prow_token;  // [R_pad]  token (absolute) feeding each padded GEMM row
     int32_t* tok_prow;    // [Tm, tok_prow_ld] padded row of each slot; column k = shared row
     int32_t* prow_slot;   // [R_pad]  slot j of each padded row: 0..k-1 routed, k shared, -1 padding
+    int32_t* rows_e;      // [Et]     rows of each expert (the shared expert: every token)
     int32_t tok_prow_ld;
     int32_t token_base;   // added to tokens written into prow_token
 };
@@ -32,7 +33,7 @@ void launch_layout(const int32_t* idx, int Tm, int E, int k, int with_shared, co
 // Element strides between consecutive minibatches' copies of each LayoutOut
 // array (hdr in LayoutHeader units).
 struct LayoutStrides {
-    int64_t counts, offsets, row_token, tok_row, hdr, mt_start, prow_token, tok_prow, prow_slot;
+    int64_t counts, offsets, row_token, tok_row, hdr, mt_start, prow_token, tok_prow, prow_slot, rows_e;
 };
 // Every minibatch of Mb tokens (the last one possibly shorter) in one launch,
 // one workgroup each; o holds minibatch 0's pointers.
@@ -156,6 +157,8 @@ struct WgradArgs {
     int64_t ld, a_mb, b_mb;
     int M, N, n_split, Et, nmb, mt_ld;
     const int32_t* mt;  // [nmb][mt_ld] first BM-tile of each expert, per minibatch
+    const int32_t* rows;  // [nmb][mt_ld] rows of each expert, per minibatch: K stops at the last
+                          // 32-row step holding one (the rest of the tile is zero padding)
     float* C0;
     float* C1;
     float* Cs0;

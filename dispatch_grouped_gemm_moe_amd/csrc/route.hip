@@ -209,6 +209,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(const int32_t* _
         if (o.prow_token) o.prow_token += b * st.prow_token;
         if (o.tok_prow) o.tok_prow += b * st.tok_prow;
         if (o.prow_slot) o.prow_slot += b * st.prow_slot;
+        if (o.rows_e) o.rows_e += b * st.rows_e;
         o.token_base += t0;
         idx += (int64_t)t0 * k;
     }
@@ -249,8 +250,10 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(const int32_t* _
             if (o.offsets) o.offsets[E] = -1;
             if (o.hdr) { o.hdr->m_tiles = 0; o.hdr->rows = 0; o.hdr->error = 1; }
         }
-        if (o.mt_start)
-            for (int e = tid; e <= Et; e += kLayoutThreads) o.mt_start[e] = 0;
+        for (int e = tid; e <= Et; e += kLayoutThreads) {
+            if (o.mt_start) o.mt_start[e] = 0;
+            if (o.rows_e && e < Et) o.rows_e[e] = 0;
+        }
         return;
     }
 
@@ -274,6 +277,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(const int32_t* _
             s_off[e] = off;
             s_poff[e] = mt * BM;
             if (o.mt_start) o.mt_start[e] = mt;
+            if (o.rows_e) o.rows_e[e] = tot;
             if (e < E) {
                 if (o.counts) o.counts[e] = tot;
                 if (o.offsets) o.offsets[e] = off;
