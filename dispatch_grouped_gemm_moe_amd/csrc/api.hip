@@ -42,7 +42,7 @@ struct Plan {
     // forward workspace (bytes): routing, MXFP8 x, every minibatch's layout
     // (first-tile maps [nmb][Et+1], then nmb blocks of lay_bytes), layer-kernel
     // counters, ring slots (h, Y, MXFP8 h codes and scales)
-    size_t ws_status, ws_idx, ws_w, ws_mt, ws_lay0, ws_cnt, ws_slot0, slot_bytes, ws_fwd;
+    size_t ws_status, ws_idx, ws_w, ws_mt, ws_rows, ws_lay0, ws_cnt, ws_slot0, slot_bytes, ws_fwd;
     size_t sl_h, sl_y, sl_hq, sl_sh;
     bool mega;  // forward through the persistent layer kernel
     size_t ws_xq, ws_sx;  // MXFP8 codes and scales of x
@@ -155,6 +155,7 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
         p->lay_bytes = l;
     }
     p->ws_mt = o; o = align_up(o + (size_t)p->nmb * (Et + 1) * 4);
+    p->ws_rows = o; o = align_up(o + (size_t)p->nmb * (Et + 1) * 4);
     p->ws_lay0 = o; o = align_up(o + (size_t)p->nmb * p->lay_bytes);
     p->ws_cnt = o; o = align_up(o + (size_t)(3 * p->nmb + 1) * 4);
     p->ws_slot0 = o;
@@ -368,6 +369,7 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
     const uint16_t* W1t = (const uint16_t*)(pk + p.pk_w1t);
     const uint16_t* W2t = (const uint16_t*)(pk + p.pk_w2t);
     int32_t* mt_all = (int32_t*)(wsb + p.ws_mt);
+    int32_t* rows_all = (int32_t*)(wsb + p.ws_rows);
     uint8_t* lay0 = wsb + p.ws_lay0;
     uint8_t* xq = wsb + p.ws_xq;
     uint8_t* sx = wsb + p.ws_sx;
@@ -383,10 +385,11 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
         o.mt_start = mt_all;
         o.prow_token = (int32_t*)(lay0 + p.ly_prow_token);
         o.tok_prow = (int32_t*)(lay0 + p.ly_tok_prow);
+        o.rows_e = rows_all;
         o.tok_prow_ld = p.ld_tok_prow;
         LayoutStrides ls{};
         ls.hdr = (int64_t)p.lay_bytes / (int64_t)sizeof(LayoutHeader);
-        ls.mt_start = p.Et + 1;
+        ls.mt_start = ls.rows_e = p.Et + 1;
         ls.prow_token = ls.tok_prow = (int64_t)p.lay_bytes / 4;
         TIMED(MOE_K_LAYOUT, s, launch_layout_batched(idx, p.T, p.Mb, p.E, p.k, p.shared ? 1 : 0, o, ls, s));
     }
@@ -425,7 +428,7 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
         a.comm = p.comm_cus; a.e_end = p.mx ? p.E : p.Et; a.with_shared = p.shared ? 1 : 0;
         a.ld_tok_prow = p.ld_tok_prow; a.mx = p.mx ? 1 : 0; a.group = p.group;
         a.lay0 = lay0; a.lay_bytes = p.lay_bytes; a.ly_prow_token = p.ly_prow_token; a.ly_tok_prow = p.ly_tok_prow;
-        a.mt_all = mt_all; a.mt_ld = p.Et + 1;
+        a.mt_all = mt_all; a.rows_all = rows_all; a.mt_ld = p.Et + 1;
         a.g1 = g1; a.g2 = g2; a.m1 = m1; a.m2 = m2;
         a.g1.e_begin = a.g2.e_begin = 0;
         a.slot0 = wsb + p.ws_slot0; a.slot_bytes = p.slot_bytes;
@@ -471,21 +474,22 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             if (p.mx) {
                 MxGemmArgs m = m1;
                 m.a_row_map = prow_token; m.mt_start = mt; m.hdr = hdr;
-                m.Cq = slot + p.sl_hq; m.Cs = slot + p.sl_sh; m.GU = guf;
+                m.Cq = slot + p.sl_hq; m.Cs = slot + p.sl_sh; m.GU = guf; m.rows_e = rows_all + (size_t)b * (p.Et + 1);
                 TIMED(MOE_K_GEMM_GATE_UP, s, launch_mx_gemm(m, kEpiSwiGLU, grid, s));
             }
             GemmArgs ga = g1;
-            ga.a_row_map = prow_token; ga.mt_start = mt; ga.hdr = hdr;
+            ga.a_row_map = prow_token; ga.mt_start = mt; ga.hdr = hdr; ga.rows_e = rows_all + (size_t)b * (p.Et + 1);
             ga.C = hbuf; ga.GU = gubuf; ga.GUf = guf;
             if (e_bf16 < p.Et)
                 TIMED(p.mx ? MOE_K_SHARED_GEMM : MOE_K_GEMM_GATE_UP, s, launch_grouped_gemm(ga, kEpiSwiGLU, grid, s));
             if (p.mx) {
                 MxGemmArgs m = m2;
                 m.A = slot + p.sl_hq; m.SA = slot + p.sl_sh; m.mt_start = mt; m.hdr = hdr; m.C = ybuf;
+                m.rows_e = rows_all + (size_t)b * (p.Et + 1);
                 TIMED(MOE_K_GEMM_DOWN, s, launch_mx_gemm(m, kEpiStore, grid, s));
             }
             GemmArgs gb = g2;
-            gb.A = hbuf; gb.mt_start = mt; gb.hdr = hdr; gb.C = ybuf;
+            gb.A = hbuf; gb.mt_start = mt; gb.hdr = hdr; gb.C = ybuf; gb.rows_e = rows_all + (size_t)b * (p.Et + 1);
             if (e_bf16 < p.Et)
                 TIMED(p.mx ? MOE_K_SHARED_GEMM : MOE_K_GEMM_DOWN, s, launch_grouped_gemm(gb, kEpiStore, grid, s));
         }
@@ -592,7 +596,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             m1.SB = pk + p.pk_sd; m1.sb_stride = (int64_t)(H / 64) * I * 4; m1.sb_kstride = (int64_t)I * 4;
             m1.N = I; m1.K = H; m1.mt_start = mt; m1.hdr = hdr; m1.e_begin = 0; m1.e_end = E;
             m1.C = nullptr; m1.ldc = I; m1.Cq = nullptr; m1.Cs = nullptr; m1.cs_rows = 0; m1.GU = nullptr;
-            m1.Cf = dHf;
+            m1.Cf = dHf; m1.rows_e = (const int32_t*)(wsb + p.wb_rows) + (size_t)b * (Et + 1);
             TIMED(MOE_K_DGRAD_DOWN, s, launch_mx_gemm(m1, kEpiStore, grid, s));
         }
         GemmArgs g1{};  // dH = dY Wd^T
@@ -600,7 +604,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
         g1.B = Wdc; g1.b_stride = (int64_t)I * H;
         g1.C = dH; g1.ldc = I; g1.N = I; g1.K = H;
         g1.mt_start = mt; g1.hdr = hdr; g1.Et = Et; g1.GU = nullptr; g1.e_begin = e_bf16; g1.e_end = Et;
-        g1.GUf = nullptr; g1.Cf = dHf;
+        g1.GUf = nullptr; g1.Cf = dHf; g1.rows_e = (const int32_t*)(wsb + p.wb_rows) + (size_t)b * (Et + 1);
         if (e_bf16 < Et)
             TIMED(p.mx ? MOE_K_SHARED_GEMM : MOE_K_DGRAD_DOWN, s, launch_grouped_gemm(g1, kEpiStore, grid, s));
         SwigluBwdArgs sb{};
@@ -616,7 +620,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             m2.SB = pk + p.pk_sgu; m2.sb_stride = (int64_t)(2 * I / 64) * H * 4; m2.sb_kstride = (int64_t)H * 4;
             m2.N = H; m2.K = 2 * I; m2.mt_start = mt; m2.hdr = hdr; m2.e_begin = 0; m2.e_end = E;
             m2.C = dXb; m2.ldc = H; m2.Cq = nullptr; m2.Cs = nullptr; m2.cs_rows = 0; m2.GU = nullptr;
-            m2.Cf = nullptr;
+            m2.Cf = nullptr; m2.rows_e = (const int32_t*)(wsb + p.wb_rows) + (size_t)b * (Et + 1);
             TIMED(MOE_K_DGRAD_GATE_UP, s, launch_mx_gemm(m2, kEpiStore, grid, s));
         }
         GemmArgs g2{};  // dX = dG Wg^T + dU Wu^T
@@ -625,6 +629,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
         g2.C = dXb; g2.ldc = H; g2.N = H; g2.K = 2 * I;
         g2.mt_start = mt; g2.hdr = hdr; g2.Et = Et;
         g2.GU = nullptr; g2.e_begin = e_bf16; g2.e_end = Et; g2.GUf = nullptr; g2.Cf = nullptr;
+        g2.rows_e = (const int32_t*)(wsb + p.wb_rows) + (size_t)b * (Et + 1);
         if (e_bf16 < Et)
             TIMED(p.mx ? MOE_K_SHARED_GEMM : MOE_K_DGRAD_GATE_UP, s, launch_grouped_gemm(g2, kEpiStore, grid, s));
 

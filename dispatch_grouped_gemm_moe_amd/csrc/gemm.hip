@@ -106,7 +106,7 @@ void wgrad_kernel(WgradArgs p) {
         }
         SegmentK kit{p.mt, p.rows, p.mt_ld, e, p.nmb, p.a_mb, p.b_mb};
         floatx16 acc[4][4];
-        tile_mainloop(acc, smem, (const char*)p.A, aoff, (const char*)p.B, boff, KT, kit);
+        tile_mainloop<4>(acc, smem, (const char*)p.A, aoff, (const char*)p.B, boff, KT, kit);
         // columns < n_split go to C0, the rest to C1 (column - n_split); the
         // last expert writes to the shared-expert outputs when they are given
         const bool shared = p.Cs0 && e == p.Et - 1;

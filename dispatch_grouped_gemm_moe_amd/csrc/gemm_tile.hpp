@@ -22,9 +22,23 @@ constexpr int kStages = 5;  // 160 KB of LDS: loads run up to 4 K steps ahead
 
 __device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 
+// Scheduling: interleave M MFMAs, V global loads and D LDS reads round robin.
+template <int M, int V, int D>
+struct Interleave {
+    static __device__ __forceinline__ void run() {
+        if constexpr (M > 0) __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+        if constexpr (V > 0) __builtin_amdgcn_sched_group_barrier(kSchedVMEM, 1, 0);
+        if constexpr (D > 0) __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+        if constexpr (M > 1 || V > 1 || D > 1)
+            Interleave<(M > 0 ? M - 1 : 0), (V > 0 ? V - 1 : 0), (D > 0 ? D - 1 : 0)>::run();
+    }
+};
+
+// MFMAs of the first NV row fragments (the others are all padding rows)
+template <int NV>
 __device__ __forceinline__ void mfma_block(floatx16 (&acc)[4][4], const bf16x8 (&a)[4], const bf16x8 (&b)[4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NV; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
@@ -44,7 +58,11 @@ struct DenseK {
 // a_base/b_base + aoff[i]/boff[i] address the 4 A and 4 B rows this lane
 // stages (tile rows wave*64 + 16i + lane/4, swizzled chunk); kit.next() gives
 // the byte offset of each successive K step, called in K order.
-template <class KIt>
+// Row fragments: fragment i of wave (wm, wn) holds tile rows 64i + 32wm ..
+// +31, so a tile's valid rows (a prefix) spread evenly over both wave rows, and
+// NV (the fragments of this wave holding any valid row) cuts the MFMAs and
+// fragment reads of both alike.  Loads and barriers do not depend on NV.
+template <int NV, class KIt>
 __device__ __forceinline__ void tile_mainloop(floatx16 (&acc)[4][4], uint8_t* smem, const char* a_base,
                                               const uint32_t (&aoff)[4], const char* b_base,
                                               const uint32_t (&boff)[4], int KT, KIt kit) {
@@ -79,13 +97,13 @@ __device__ __forceinline__ void tile_mainloop(floatx16 (&acc)[4][4], uint8_t* sm
     };
     // MFMA operand fragments of k-step kk (16 deep) of the K step in slot `slot`.
     const int fr = lane & 31;
-    const int arow_b = (wm * 128 + fr) * kRowBytes, brow_b = kStageA + (wn * 128 + fr) * kRowBytes;
+    const int arow_b = (wm * 32 + fr) * kRowBytes, brow_b = kStageA + (wn * 128 + fr) * kRowBytes;
     const int fsw = swz(fr);
     auto frags = [&](int slot, int kk, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
         const uint8_t* st = smem + slot * kStageBytes;
         const int pc = ((kk * 2 + (lane >> 5)) ^ fsw) * 16;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8*)(st + arow_b + i * 32 * kRowBytes + pc);
+        for (int i = 0; i < NV; ++i) a[i] = *(const bf16x8*)(st + arow_b + i * 64 * kRowBytes + pc);
 #pragma unroll
         for (int j = 0; j < 4; ++j) b[j] = *(const bf16x8*)(st + brow_b + j * 32 * kRowBytes + pc);
     };
@@ -118,13 +136,8 @@ __device__ __forceinline__ void tile_mainloop(floatx16 (&acc)[4][4], uint8_t* sm
         advance();  // offsets of step kt + S
         // k-step 0 of this K step: read k-step 1's fragments under 16 MFMAs
         frags(slot, 1, a1, b1);
-        mfma_block(acc, a0, b0);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 8, 0);
+        mfma_block<NV>(acc, a0, b0);
+        Interleave<4 * NV, 0, NV + 4>::run();
         __builtin_amdgcn_sched_barrier(0);
         // Every wave has read step kt and step kt+1 has landed: refill step
         // kt's slot with step kt+S and read step kt+1's first fragments under
@@ -133,24 +146,25 @@ __device__ __forceinline__ void tile_mainloop(floatx16 (&acc)[4][4], uint8_t* sm
         __syncthreads();
         issue(slot);
         frags(next_slot, 0, a0, b0);  // a stale but in-bounds read after the last step
-        mfma_block(acc, a1, b1);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedVMEM, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 8, 0);
+        mfma_block<NV>(acc, a1, b1);
+        Interleave<4 * NV, 8, NV + 4>::run();
         __builtin_amdgcn_sched_barrier(0);
         slot = next_slot;
     }
 }
 
 // Accumulator element r of fragment (i, j) of lane l sits in tile row
-// wm*128 + 32i + 8(r/4) + 4(l/32) + r%4 and tile column wn*128 + 32j + l%32.
+// 64i + 32wm + 8(r/4) + 4(l/32) + r%4 and tile column wn*128 + 32j + l%32.
 __device__ __forceinline__ int frag_row(int i, int r) {
     const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) >> 1;
-    return wm * 128 + i * 32 + (r >> 2) * 8 + 4 * (lane >> 5) + (r & 3);
+    return i * 64 + wm * 32 + (r >> 2) * 8 + 4 * (lane >> 5) + (r & 3);
+}
+
+// Row fragments of this wave holding any of the tile's first `valid` rows.
+__device__ __forceinline__ int valid_frags(int valid) {
+    const int wm = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >> 1;
+    const int n = (valid - 32 * wm + 63) / 64;
+    return n < 0 ? 0 : (n > 4 ? 4 : n);
 }
 __device__ __forceinline__ int frag_col(int j) {
     const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
@@ -181,7 +195,10 @@ __device__ __forceinline__ int grouped_tiles(const int32_t* mt_start, int e_begi
 
 // One 256 x 256 output tile (expert e, M tile ml of the expert, N tile ntile)
 // of the bf16 grouped GEMM with its epilogue; smem is the kStages LDS ring.
-template <int EPI>
+// kSkipPadding: with p.rows_e, the padding fragments of an expert's last tile
+// get no MFMAs (five mainloop variants; the persistent layer kernel, where
+// they would crowd its registers, compiles the full one only).
+template <int EPI, bool kSkipPadding = true>
 __device__ __forceinline__ void gemm_tile(const GemmArgs p, int e, int ml, int ntile, uint8_t* smem) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int KT = p.K / kBK;
@@ -204,8 +221,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs p, int e, int ml, int n
         boff[i] = (uint32_t)(((int64_t)n * p.K + lchunk * 8) * 2);
     }
     floatx16 acc[4][4];
-    tile_mainloop(acc, smem, (const char*)p.A, aoff, (const char*)(p.B + (int64_t)e * p.b_stride), boff, KT,
-                  DenseK{});
+    const char* bbase = (const char*)(p.B + (int64_t)e * p.b_stride);
+    // valid rows of this tile: padding rows of the expert's last tile get no MFMAs
+    const int nv = (kSkipPadding && p.rows_e) ? valid_frags(p.rows_e[e] - ml * BM) : 4;
+    if (!kSkipPadding) {
+        tile_mainloop<4>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT, DenseK{});
+    } else switch (nv) {
+        case 4: tile_mainloop<4>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT, DenseK{}); break;
+        case 3: tile_mainloop<3>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT, DenseK{}); break;
+        case 2: tile_mainloop<2>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT, DenseK{}); break;
+        case 1: tile_mainloop<1>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT, DenseK{}); break;
+        default: tile_mainloop<0>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT, DenseK{}); break;
+    }
 
     if (EPI == kEpiSwiGLU) {
         // columns come in 64-wide groups of 32 gate then 32 up columns

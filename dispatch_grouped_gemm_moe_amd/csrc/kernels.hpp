@@ -59,6 +59,7 @@ struct GemmArgs {
     int e_begin, e_end;        // experts [e_begin, e_end) are processed
     float* GUf;
     float* Cf;                 // kEpiStore, optional: fp32 output instead of C
+    const int32_t* rows_e;     // optional [Et] rows of each expert: padding fragments get no MFMAs
 };
 
 enum GemmEpilogue { kEpiSwiGLU = 0, kEpiStore = 1 };
@@ -88,6 +89,7 @@ struct MxGemmArgs {
     int64_t cs_rows;
     float* GU;                 // kEpiSwiGLU, optional: fp32 g | u [R_pad][N] kept for the backward
     float* Cf;                 // kEpiStore, optional: fp32 output instead of C
+    const int32_t* rows_e;     // optional [Et] rows of each expert: padding fragments get no MFMAs
 };
 void launch_mx_gemm(const MxGemmArgs& a, GemmEpilogue epi, int grid, hipStream_t stream);
 // bf16 [rows][cols] -> E4M3 codes [rows][cols] and E8M0 scales; layout 0:
@@ -111,6 +113,7 @@ struct MegaArgs {
     const uint8_t* lay0;
     int64_t lay_bytes, ly_prow_token, ly_tok_prow;
     const int32_t* mt_all;
+    const int32_t* rows_all;  // [nmb][mt_ld] rows of each expert per minibatch
     int mt_ld;
     GemmArgs g1, g2;
     MxGemmArgs m1, m2;

@@ -290,14 +290,14 @@ void mega_kernel(MegaArgs a) {
                 m.mt_start = mt; m.hdr = hdr;
                 m.Cq = slot + a.sl_hq; m.Cs = slot + a.sl_sh;
                 m.GU = svb ? (float*)svb : nullptr;
-                mx_gemm_tile<kEpiSwiGLU>(m, e, ml, ntile, smem);
+                mx_gemm_tile<kEpiSwiGLU, false>(m, e, ml, ntile, smem);
             } else {
                 GemmArgs gg = a.g1;
                 gg.a_row_map = (const int32_t*)(lay + a.ly_prow_token);
                 gg.mt_start = mt; gg.hdr = hdr;
                 gg.C = (uint16_t*)(slot + a.sl_h);
                 gg.GU = svb ? (uint16_t*)svb : nullptr;
-                gemm_tile<kEpiSwiGLU>(gg, e, ml, ntile, smem);
+                gemm_tile<kEpiSwiGLU, false>(gg, e, ml, ntile, smem);
             }
         } else {
             if constexpr (kMx) {
@@ -305,13 +305,13 @@ void mega_kernel(MegaArgs a) {
                 m.A = slot + a.sl_hq; m.SA = slot + a.sl_sh;
                 m.mt_start = mt; m.hdr = hdr;
                 m.C = Y;
-                mx_gemm_tile<kEpiStore>(m, e, ml, ntile, smem);
+                mx_gemm_tile<kEpiStore, false>(m, e, ml, ntile, smem);
             } else {
                 GemmArgs gg = a.g2;
                 gg.A = (const uint16_t*)(slot + a.sl_h);
                 gg.mt_start = mt; gg.hdr = hdr;
                 gg.C = Y;
-                gemm_tile<kEpiStore>(gg, e, ml, ntile, smem);
+                gemm_tile<kEpiStore, false>(gg, e, ml, ntile, smem);
             }
         }
     }

@@ -24,8 +24,11 @@ __device__ __forceinline__ int mx_swz(int r) { return (r >> 2) & 3; }
 
 // One 256 x 256 output tile (expert e, M tile ml of the expert, N tile ntile)
 // of the MXFP8 grouped GEMM with its epilogue; smem is the kMxStages LDS ring.
-template <int EPI>
-__device__ __forceinline__ void mx_gemm_tile(const MxGemmArgs p, int e, int ml, int ntile, uint8_t* smem) {
+// Row fragments as in the bf16 tile: fragment i of wave (wm, wn) holds tile
+// rows 64i + 32wm .. +31, and only the first NV of them (those holding a valid
+// row of the expert's last tile) get MFMAs and fragment reads.
+template <int EPI, int NV>
+__device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, int ntile, uint8_t* smem) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar LDS bases
     const int wm = wave >> 1, wn = wave & 1;
@@ -75,15 +78,15 @@ __device__ __forceinline__ void mx_gemm_tile(const MxGemmArgs p, int e, int ml, 
     const int fr = lane & 31, half = lane >> 5;
     const int fsw = mx_swz(fr);
     const int pc0 = (half ^ fsw) * 16, pc1 = ((2 + half) ^ fsw) * 16;
-    const int arow_b = (wm * 128 + fr) * kMxRow, brow_b = kMxStageA + (wn * 128 + fr) * kMxRow;
+    const int arow_b = (wm * 32 + fr) * kMxRow, brow_b = kMxStageA + (wn * 128 + fr) * kMxRow;
     auto frags = [&](int slot, intx8 (&a)[4], intx8 (&b)[4], int (&sa)[4], int (&sb)[4]) {
         const uint8_t* st = smem + slot * kMxStageBytes;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const intx4 lo4 = *(const intx4*)(st + arow_b + i * 32 * kMxRow + pc0);
-            const intx4 hi4 = *(const intx4*)(st + arow_b + i * 32 * kMxRow + pc1);
+        for (int i = 0; i < NV; ++i) {
+            const intx4 lo4 = *(const intx4*)(st + arow_b + i * 64 * kMxRow + pc0);
+            const intx4 hi4 = *(const intx4*)(st + arow_b + i * 64 * kMxRow + pc1);
             a[i] = intx8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-            sa[i] = st[kMxStageSA + (wm * 128 + i * 32 + fr) * 4 + half];
+            sa[i] = st[kMxStageSA + (i * 64 + wm * 32 + fr) * 4 + half];
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -100,7 +103,7 @@ __device__ __forceinline__ void mx_gemm_tile(const MxGemmArgs p, int e, int ml, 
         for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
     auto mfmas = [&](const intx8 (&a)[4], const intx8 (&b)[4], const int (&sa)[4], const int (&sb)[4]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < NV; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 0, 0, 0, sa[i], 0,
@@ -131,13 +134,8 @@ __device__ __forceinline__ void mx_gemm_tile(const MxGemmArgs p, int e, int ml, 
         issue(kt + kMxStages, slot);
         frags(next_slot, an, bn, san, sbn);  // stale but in-bounds on the last step
         mfmas(ac, bc, sac, sbc);
-#pragma unroll
-        for (int q = 0; q < 10; ++q) {
-            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedVMEM, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 6, 0);
+        // 4NV MFMAs, 10 loads, 3 LDS reads per fragment (two code halves, one scale)
+        Interleave<4 * NV, 10, 3 * (NV + 4)>::run();
         __builtin_amdgcn_sched_barrier(0);
         slot = next_slot;
     };
@@ -170,7 +168,7 @@ __device__ __forceinline__ void mx_gemm_tile(const MxGemmArgs p, int e, int ml, 
                     m = fmaxf(m, __shfl_xor(m, 2, kWave));
                     m = fmaxf(m, __shfl_xor(m, 1, kWave));
                     const int ex = mx_scale_exp(m);
-                    const int row = prow0 + wm * 128 + i * 32 + (r >> 2) * 8 + 4 * half + (r & 3);
+                    const int row = prow0 + i * 64 + wm * 32 + (r >> 2) * 8 + 4 * half + (r & 3);
                     if (live) {
                         const int q = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(h, -ex), 0.0f, 0, false);
                         p.Cq[(int64_t)row * I + hcol] = (uint8_t)(q & 0xff);
@@ -191,7 +189,7 @@ __device__ __forceinline__ void mx_gemm_tile(const MxGemmArgs p, int e, int ml, 
                     for (int i = 0; i < 4; ++i)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
-                            const int row = prow0 + wm * 128 + i * 32 + (r >> 2) * 8 + 4 * half + (r & 3);
+                            const int row = prow0 + i * 64 + wm * 32 + (r >> 2) * 8 + 4 * half + (r & 3);
                             float* dst = p.GU + (int64_t)row * p.N + hcol;
                             dst[0] = acc[i][2 * jj][r];
                             dst[I] = acc[i][2 * jj + 1][r];
@@ -208,7 +206,7 @@ __device__ __forceinline__ void mx_gemm_tile(const MxGemmArgs p, int e, int ml, 
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int row = prow0 + wm * 128 + i * 32 + (r >> 2) * 8 + 4 * half + (r & 3);
+                        const int row = prow0 + i * 64 + wm * 32 + (r >> 2) * 8 + 4 * half + (r & 3);
                         p.Cf[(int64_t)row * p.ldc + col] = acc[i][j][r];
                     }
             }
@@ -222,11 +220,30 @@ __device__ __forceinline__ void mx_gemm_tile(const MxGemmArgs p, int e, int ml, 
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int row = prow0 + wm * 128 + i * 32 + (r >> 2) * 8 + 4 * half + (r & 3);
+                        const int row = prow0 + i * 64 + wm * 32 + (r >> 2) * 8 + 4 * half + (r & 3);
                         p.C[(int64_t)row * p.ldc + col] = f32_to_bf16_rne(acc[i][j][r]);
                     }
             }
         }
+    }
+}
+
+
+// One 256 x 256 output tile (expert e, M tile ml, N tile ntile) of the MXFP8
+// grouped GEMM; with p.rows_e and kSkipPadding the padding fragments of an
+// expert's last tile get no MFMAs (the layer kernel compiles the full loop).
+template <int EPI, bool kSkipPadding = true>
+__device__ __forceinline__ void mx_gemm_tile(const MxGemmArgs p, int e, int ml, int ntile, uint8_t* smem) {
+    if (!kSkipPadding || !p.rows_e) {
+        mx_tile_body<EPI, 4>(p, e, ml, ntile, smem);
+        return;
+    }
+    switch (valid_frags(p.rows_e[e] - ml * BM)) {
+        case 4: mx_tile_body<EPI, 4>(p, e, ml, ntile, smem); break;
+        case 3: mx_tile_body<EPI, 3>(p, e, ml, ntile, smem); break;
+        case 2: mx_tile_body<EPI, 2>(p, e, ml, ntile, smem); break;
+        case 1: mx_tile_body<EPI, 1>(p, e, ml, ntile, smem); break;
+        default: mx_tile_body<EPI, 0>(p, e, ml, ntile, smem); break;
     }
 }
 
