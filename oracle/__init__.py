@@ -412,7 +412,8 @@ def mx_point(a, axis: int) -> np.ndarray:
     return mx_roundtrip(np.asarray(a, dtype=np.float64).astype(np.float32), axis)
 
 
-def layer_backward(inp, dout=None, fwd=None, *, mx: bool | None = None, quantizer=None):
+def layer_backward(inp, dout=None, fwd=None, *, mx: bool | None = None, quantizer=None,
+                   weight_grads: bool = True):
     """Gradients of sum(out * dout) for the layer (fp64, routing frozen at the
     forward's selection).
 
@@ -427,6 +428,8 @@ def layer_backward(inp, dout=None, fwd=None, *, mx: bool | None = None, quantize
     operands (x rows, h = silu(g) u, dY, dG, dU).  The shared expert is bf16
     throughout.  `fwd` must then be the MXFP8 forward (its g, u, Y include the
     forward's quantisation).  `quantizer(a, axis)` replaces `mx_point`.
+    weight_grads=False leaves out the expert weight gradients (dWg, dWu, dWd and
+    the shared expert's); every other result is unchanged.
     """
     w_ = inp.w
     mx = (w_.prec == "mxfp8") if mx is None else mx
@@ -441,18 +444,20 @@ def layer_backward(inp, dout=None, fwd=None, *, mx: bool | None = None, quantize
     # reverse combine: d out / d Y[t,j] = w[t,j] * dout[t]; d out / d w[t,j] = <dout[t], Y[t,j]>
     dgate = np.einsum("th,tjh->tj", dout, Y)
     dx = np.zeros((T, H), dtype=np.float64)
-    dWg = np.zeros((E, H, I)); dWu = np.zeros((E, H, I)); dWd = np.zeros((E, I, H))
+    if weight_grads:
+        dWg = np.zeros((E, H, I)); dWu = np.zeros((E, H, I)); dWd = np.zeros((E, I, H))
     W = Weights(inp, mx=False)
     for e, (t_sel, j_sel, g, u, h) in fwd["saved"].items():
         Wg, Wu, Wd = W.expert_dgrad(e, q)
         dy = gw[t_sel, j_sel][:, None] * dout[t_sel]
         X = x64[t_sel]
-        dWd[e] = h.T @ dy
         dh = (q(dy, 1) if q else dy) @ Wd.T
         du = dh * silu(g)
         dg = dh * u * silu_grad(g)
-        dWg[e] = X.T @ dg
-        dWu[e] = X.T @ du
+        if weight_grads:
+            dWd[e] = h.T @ dy
+            dWg[e] = X.T @ dg
+            dWu[e] = X.T @ du
         if q:
             dxe = q(dg, 1) @ Wg.T + q(du, 1) @ Wu.T
         else:
@@ -465,19 +470,70 @@ def layer_backward(inp, dout=None, fwd=None, *, mx: bool | None = None, quantize
     Wr64 = as_f64(inp.Wr)
     dx += dlogits @ Wr64.T
     dWr = x64.T @ dlogits
-    res = {"dx": dx, "dWg": dWg, "dWu": dWu, "dWd": dWd, "dWr": dWr, "dgate": dgate,
-           "dlogits": dlogits}
+    res = {"dx": dx, "dWr": dWr, "dgate": dgate, "dlogits": dlogits}
+    if weight_grads:
+        res.update(dWg=dWg, dWu=dWu, dWd=dWd)
     if "shared" in fwd:
         gs, us, hs = fwd["shared"]
         Wsg, Wsu, Wsd = W.shared()
-        res["dWsd"] = hs.T @ dout
         dhs = dout @ Wsd.T
         dus = dhs * silu(gs)
         dgs = dhs * us * silu_grad(gs)
-        res["dWsg"] = x64.T @ dgs
-        res["dWsu"] = x64.T @ dus
+        if weight_grads:
+            res["dWsd"] = hs.T @ dout
+            res["dWsg"] = x64.T @ dgs
+            res["dWsu"] = x64.T @ dus
         dx += dgs @ Wsg.T + dus @ Wsu.T
     return res
+
+
+def weight_grad_columns(inp, e: int, cols, dout=None, *, mx: bool | None = None, routing=None):
+    """Columns `cols` of one expert's weight gradients over all of its tokens:
+    dWg[:, cols] and dWu[:, cols] [H, n], dWd[cols, :] [n, H] (e >= 0, routing
+    frozen at the forward's selection), or the shared expert's dWsg, dWsu, dWsd
+    under the same keys (e = -1, every token, bf16 throughout).
+
+    Column i of the gate and up gradients and row i of the down gradient
+    involve only column i of the expert's gate/up activations and of dH, so the
+    products of `layer_backward` are taken here on those weight columns alone.
+    Every MXFP8 block of a forward weight lies inside one column of Wg / Wu
+    (blocks run along H) and every block of the backward's Wd inside one row
+    (blocks run along H), so restricting to the columns commutes with the
+    quantiser.  Same quantisation points as `layer_backward`: forward on the
+    MXFP8 x rows and weights, dH from MXFP8 dY and Wd, weight gradients on the
+    unquantised x, h and dY.
+    routing: (idx, w) of every token, from `route`, to reuse across calls.
+    """
+    w_ = inp.w
+    mx = (w_.prec == "mxfp8") if mx is None else mx
+    cols = np.asarray(cols, dtype=np.int64)
+    dout = inp.dout if dout is None else dout
+    if e < 0:
+        Wsg, Wsu, Wsd = (as_f64(t) for t in (inp.Wsg, inp.Wsu, inp.Wsd))
+        X, dy = as_f64(inp.x), as_f64(dout)
+        g, u = X @ Wsg[:, cols], X @ Wsu[:, cols]
+        dh = dy @ Wsd[cols, :].T
+    else:
+        if routing is None:
+            _, idx, gw = route(as_f32(inp.x), inp.Wr, inp.bias, w_.k)
+        else:
+            idx, gw = routing
+        t_sel, j_sel = np.nonzero(idx == e)
+        X = as_f64(inp.x[t_sel])  # rows picked before widening: same values, less memory
+        dy = gw[t_sel, j_sel][:, None] * as_f64(dout[t_sel])
+        Wg, Wu, Wd = (as_f64(t[e]) for t in (inp.Wg, inp.Wu, inp.Wd))
+        Wg, Wu, Wd = Wg[:, cols], Wu[:, cols], Wd[cols, :]
+        if mx:
+            xin = mx_roundtrip(X, axis=1)
+            g, u = xin @ mx_roundtrip(Wg, 0), xin @ mx_roundtrip(Wu, 0)
+            dh = mx_point(dy, 1) @ mx_point(Wd, 1).T
+        else:
+            g, u = X @ Wg, X @ Wu
+            dh = dy @ Wd.T
+    h = silu(g) * u
+    du = dh * silu(g)
+    dg = dh * u * silu_grad(g)
+    return {"dWg": X.T @ dg, "dWu": X.T @ du, "dWd": h.T @ dy}
 
 
 def rel_inf_err(got, ref) -> float:

@@ -40,8 +40,9 @@ class Layer:
     def device_status(self):
         return moe.moe_read_device_status(self.bufs.ws)
 
-    def backward(self, dout, with_dgate=True):
-        """Gradients of sum(out * dout); returns a dict of CPU float tensors."""
+    def backward(self, dout, with_dgate=True, to_cpu=True):
+        """Gradients of sum(out * dout); returns a dict of CPU float tensors, or
+        of the device tensors themselves with to_cpu=False."""
         w = self.inp.w
         dev = self.x.device
         T, H, I, E, k = w.T, w.H, w.I, w.E, w.k
@@ -58,13 +59,14 @@ class Layer:
                           self.bufs.saved, g["dx"], g["dWg"], g["dWu"], g["dWd"], g["dWr"], self.bufs.ws,
                           dWs=dWs, dgate=dgate)
         torch.cuda.synchronize()
-        res = {n: t.float().cpu() for n, t in g.items()}
+        host = (lambda t: t.float().cpu()) if to_cpu else (lambda t: t)
+        res = {n: host(t) for n, t in g.items()}
         if dgate is not None:
-            res["dgate"] = dgate.cpu()
+            res["dgate"] = host(dgate)
         if dWs is not None:
-            res["dWsg"] = dWs[:H * I].view(H, I).cpu()
-            res["dWsu"] = dWs[H * I:2 * H * I].view(H, I).cpu()
-            res["dWsd"] = dWs[2 * H * I:].view(I, H).cpu()
+            res["dWsg"] = host(dWs[:H * I].view(H, I))
+            res["dWsu"] = host(dWs[H * I:2 * H * I].view(H, I))
+            res["dWsd"] = host(dWs[2 * H * I:].view(I, H))
         return res
 
     def saved_routing(self):

@@ -422,6 +422,67 @@ def test_backward_scales_exactly_with_dout():
         np.testing.assert_array_equal(g2[n], 2 * g1[n])
 
 
+def test_weight_grad_columns_match_torch_autograd():
+    """Column-restricted weight gradients of every routed expert and of the
+    shared expert against autograd of a dense torch formulation (routing and
+    gate weights frozen at the oracle forward's)."""
+    w = tiny(T=40, H=128, I=64, E=5, k=3, shared_expert=True, router_bias="normal")
+    inp = _fd_inputs(w, 3)
+    fwd = O.layer_forward(inp, keep=True)
+    idx = torch.from_numpy(fwd["idx"].astype(np.int64))
+    gw = torch.from_numpy(fwd["w"])
+    names = ("Wg", "Wu", "Wd", "Wsg", "Wsu", "Wsd")
+    t = {n: torch.tensor(getattr(inp, n), requires_grad=True) for n in names}
+    x = torch.from_numpy(inp.x)
+    out = torch.zeros(w.T, w.H, dtype=torch.float64)
+    for j in range(w.k):
+        e = idx[:, j]
+        gg = torch.einsum("th,thi->ti", x, t["Wg"][e])
+        uu = torch.einsum("th,thi->ti", x, t["Wu"][e])
+        out = out + gw[:, j:j + 1] * torch.einsum("ti,tih->th", torch.nn.functional.silu(gg) * uu, t["Wd"][e])
+    out = out + (torch.nn.functional.silu(x @ t["Wsg"]) * (x @ t["Wsu"])) @ t["Wsd"]
+    (out * torch.from_numpy(inp.dout)).sum().backward()
+    cols = [0, 9, 31, 63]
+    routing = (fwd["idx"], fwd["w"])
+    for e in range(-1, w.E):
+        got = O.weight_grad_columns(inp, e, cols, routing=routing)
+        pre = "Ws" if e < 0 else "W"
+        sel = (lambda a: a) if e < 0 else (lambda a: a[e])
+        np.testing.assert_allclose(got["dWg"], sel(t[pre + "g"].grad.numpy())[:, cols], rtol=1e-9, atol=1e-12)
+        np.testing.assert_allclose(got["dWu"], sel(t[pre + "u"].grad.numpy())[:, cols], rtol=1e-9, atol=1e-12)
+        np.testing.assert_allclose(got["dWd"], sel(t[pre + "d"].grad.numpy())[cols, :], rtol=1e-9, atol=1e-12)
+    # default routing: the oracle's own fixed-order fp32 route of every token
+    got = O.weight_grad_columns(inp, 2, cols)
+    np.testing.assert_allclose(got["dWd"], t["Wd"].grad.numpy()[2][cols, :], rtol=1e-9, atol=1e-12)
+
+
+@pytest.mark.parametrize("prec", ["bf16", "mxfp8"])
+def test_backward_of_token_subset_equals_backward_with_masked_dout(prec):
+    """Gradients are linear in dout and every token's contribution depends on
+    that token alone (its MXFP8 blocks run along its own row), so the backward
+    with dout zero outside a token subset S equals the backward of the layer
+    restricted to S: same weight and router gradients, same dx and gate
+    gradients on S, exact zeros elsewhere."""
+    w = tiny(T=48, H=128, I=64, E=5, k=3, shared_expert=True, router_bias="normal", prec=prec)
+    inp = make_inputs(w, with_dout=True)
+    S = np.array([0, 7, 8, 30, 47])
+    masked = torch.zeros_like(inp.dout)
+    masked[S] = inp.dout[S]
+    full = O.layer_backward(inp, dout=masked, fwd=O.layer_forward(inp, keep=True))
+    sub = O.layer_backward(inp, dout=inp.dout[S], fwd=O.layer_forward(inp, tokens=S, keep=True))
+    rest = np.setdiff1d(np.arange(w.T), S)
+    assert (full["dx"][rest] == 0).all() and (full["dgate"][rest] == 0).all()
+    for n in ("dx", "dgate"):
+        np.testing.assert_allclose(full[n][S], sub[n], rtol=1e-12, atol=1e-15, err_msg=n)
+    for n in ("dWg", "dWu", "dWd", "dWr", "dWsg", "dWsu", "dWsd"):
+        np.testing.assert_allclose(full[n], sub[n], rtol=1e-12, atol=1e-15, err_msg=n)
+    lean = O.layer_backward(inp, dout=inp.dout[S], fwd=O.layer_forward(inp, tokens=S, keep=True),
+                            weight_grads=False)
+    assert sorted(lean) == ["dWr", "dgate", "dlogits", "dx"]
+    for n in lean:
+        np.testing.assert_array_equal(lean[n], sub[n], err_msg=n)
+
+
 # ---------------------------------------------------------------- MXFP8 backward
 
 def _e4m3_positive_values():
@@ -526,6 +587,12 @@ def test_mx_backward_matches_scalar_brute_force():
     np.testing.assert_allclose(fwd["out"], ref["out"], rtol=1e-9, atol=1e-12)
     for n in ("dx", "dWg", "dWu", "dWd", "dgate", "dWr"):
         np.testing.assert_allclose(g[n], np.array(ref[n]), rtol=1e-9, atol=1e-12, err_msg=n)
+    cols = [0, 17, 63]
+    for e in range(E):
+        c = O.weight_grad_columns(inp, e, cols)
+        np.testing.assert_allclose(c["dWg"], ref["dWg"][e][:, cols], rtol=1e-9, atol=1e-12)
+        np.testing.assert_allclose(c["dWu"], ref["dWu"][e][:, cols], rtol=1e-9, atol=1e-12)
+        np.testing.assert_allclose(c["dWd"], ref["dWd"][e][cols, :], rtol=1e-9, atol=1e-12)
 
 
 def test_mx_backward_with_identity_quantiser_is_the_plain_backward():
