@@ -112,19 +112,28 @@ void wgrad_kernel(WgradArgs p) {
         const bool shared = p.Cs0 && e == p.Et - 1;
         float* c0 = shared ? p.Cs0 : p.C0 + (int64_t)e * p.M * p.n_split;
         float* c1 = shared ? p.Cs1 : (p.C1 ? p.C1 + (int64_t)e * p.M * (p.N - p.n_split) : nullptr);
+        // Staged through LDS 64 rows at a time (full-line stores).  M, N and
+        // n_split are multiples of 64: a 16-byte chunk lies on one side of the
+        // split and inside or outside the matrix as a whole.
+        epi_begin();
+        const int rl = epi_row();
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int col = n0 + frag_col(j);
-            if (col >= p.N) continue;
-            float* dst = col < p.n_split ? c0 + col : c1 + (col - p.n_split);
-            const int64_t ldc = col < p.n_split ? p.n_split : p.N - p.n_split;
+        for (int i = 0; i < 4; ++i) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = m0 + frag_row(i, r);
-                    if (m < p.M) dst[(int64_t)m * ldc] = acc[i][j][r];
-                }
+                for (int q = 0; q < 4; ++q)
+                    *(floatx4*)(smem + rl * kEpiPitch64 + frag_col(j, q) * 4) =
+                        floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            __syncthreads();
+            for (int c = threadIdx.x; c < kEpiRows * 64; c += kGemmThreads) {
+                const int r = c >> 6, col = n0 + (c & 63) * 4, m = m0 + i * 64 + r;
+                if (m >= p.M || col >= p.N) continue;
+                float* dst = col < p.n_split ? c0 + (int64_t)m * p.n_split + col
+                                             : c1 + (int64_t)m * (p.N - p.n_split) + (col - p.n_split);
+                *(intx4*)dst = *(const intx4*)(smem + r * kEpiPitch64 + (c & 63) * 16);
+            }
+            __syncthreads();
         }
     }
 }

@@ -34,14 +34,17 @@ struct Interleave {
     }
 };
 
-// MFMAs of the first NV row fragments (the others are all padding rows)
+// MFMAs of the first NV row fragments (the others are all padding rows).
+// The B fragment is the MFMA's first operand, so each accumulator holds the
+// transposed 32 x 32 block: a lane keeps one tile row and runs of four
+// consecutive tile columns, which the epilogues store 8 or 16 bytes at a time.
 template <int NV>
 __device__ __forceinline__ void mfma_block(floatx16 (&acc)[4][4], const bf16x8 (&a)[4], const bf16x8 (&b)[4]) {
 #pragma unroll
     for (int i = 0; i < NV; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
 }
 
 
@@ -153,11 +156,11 @@ __device__ __forceinline__ void tile_mainloop(floatx16 (&acc)[4][4], uint8_t* sm
     }
 }
 
-// Accumulator element r of fragment (i, j) of lane l sits in tile row
-// 64i + 32wm + 8(r/4) + 4(l/32) + r%4 and tile column wn*128 + 32j + l%32.
-__device__ __forceinline__ int frag_row(int i, int r) {
+// Accumulator element 4q + s of fragment (i, j) of lane l sits in tile row
+// 64i + 32wm + l%32 and tile column wn*128 + 32j + 8q + 4(l/32) + s.
+__device__ __forceinline__ int frag_row(int i) {
     const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) >> 1;
-    return i * 64 + wm * 32 + (r >> 2) * 8 + 4 * (lane >> 5) + (r & 3);
+    return i * 64 + wm * 32 + (lane & 31);
 }
 
 // Row fragments of this wave holding any of the tile's first `valid` rows.
@@ -166,9 +169,16 @@ __device__ __forceinline__ int valid_frags(int valid) {
     const int n = (valid - 32 * wm + 63) / 64;
     return n < 0 ? 0 : (n > 4 ? 4 : n);
 }
-__device__ __forceinline__ int frag_col(int j) {
+__device__ __forceinline__ int frag_col(int j, int q) {
     const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
-    return wn * 128 + j * 32 + (lane & 31);
+    return wn * 128 + j * 32 + q * 8 + 4 * (lane >> 5);
+}
+
+// Four fp32 values as four bf16 (round to nearest even), packed for one
+// 8-byte store.
+__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
+    return make_uint2((uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16),
+                      (uint32_t)f32_to_bf16_rne(c) | ((uint32_t)f32_to_bf16_rne(d) << 16));
 }
 
 // Tile coordinates of tile v of a grouped GEMM over experts [e_begin, e_end):
@@ -191,6 +201,42 @@ __device__ __forceinline__ void tile_coords(const int32_t* mt_start, int e_begin
 // Tiles of a grouped GEMM (M tiles of all processed experts times N tiles).
 __device__ __forceinline__ int grouped_tiles(const int32_t* mt_start, int e_begin, int e_end, int N) {
     return (mt_start[e_end] - mt_start[e_begin]) * ceil_div(N, BN);
+}
+
+// Epilogue staging.  Fragment i of every wave covers tile rows 64i .. 64i+63
+// (row 64i + epi_row() for this lane); such a 64-row block is written to LDS
+// with row pitches 16 bytes longer than the data (256, 512 or 1024 bytes), so
+// the 32 rows of one write instruction fall on different banks, then copied
+// out in 16-byte chunks along rows.
+constexpr int kEpiRows = 64;
+constexpr int kEpiPitch16 = 16 * 16 + 16;  // 16 chunks of data per row
+constexpr int kEpiPitch32 = 32 * 16 + 16;
+constexpr int kEpiPitch64 = 64 * 16 + 16;
+static_assert(kEpiRows * (kEpiPitch16 + 2 * kEpiPitch32) <= kStages * kStageBytes - 4,
+              "the staged SwiGLU block must fit the ring (the layer kernel keeps its last dword)");
+
+__device__ __forceinline__ int epi_row() {
+    const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) >> 1;
+    return wm * 32 + (lane & 31);
+}
+
+// Before the first staged block: the ring's trailing loads have landed and no
+// wave reads the ring any more.
+__device__ __forceinline__ void epi_begin() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+}
+
+// Rows 0..63 of an LDS block (kChunks 16-byte chunks per row, pitch `pitch`)
+// to global rows dst + r * ld bytes; chunks at or beyond byte `limit` of a
+// row are not stored.
+template <int kChunks>
+__device__ __forceinline__ void epi_copy_out(const uint8_t* lds, int pitch, char* dst, int64_t ld, int limit) {
+#pragma unroll
+    for (int c = threadIdx.x; c < kEpiRows * kChunks; c += kGemmThreads) {
+        const int r = c / kChunks, ch = c % kChunks;
+        if (ch * 16 < limit) *(intx4*)(dst + r * ld + ch * 16) = *(const intx4*)(lds + r * pitch + ch * 16);
+    }
 }
 
 // One 256 x 256 output tile (expert e, M tile ml of the expert, N tile ntile)
@@ -234,53 +280,83 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs p, int e, int ml, int n
         default: tile_mainloop<0>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT, DenseK{}); break;
     }
 
+    // The tile leaves through LDS, 64 rows at a time, so that every global
+    // store is a 16-byte run along a row (whole cache lines) rather than the
+    // accumulators' 4-column runs down 32 rows.  N is a multiple of 64, so a
+    // 4-column run, and a 16-byte chunk, lies wholly inside or outside it.
+    epi_begin();
+    const int rl = epi_row();
     if (EPI == kEpiSwiGLU) {
         // columns come in 64-wide groups of 32 gate then 32 up columns
-        const int I = p.N / 2;
+        const int I = p.N / 2, hc0 = n0 / 2;
+        const bool f32gu = p.GUf != nullptr, anygu = f32gu || p.GU != nullptr;
+        uint8_t* hb = smem;                                  // [64][128] bf16
+        uint8_t* gb = smem + kEpiRows * kEpiPitch16;         // [64][128] fp32 or bf16
+        uint8_t* ub = gb + kEpiRows * kEpiPitch32;
+        const int gpitch = f32gu ? kEpiPitch32 : kEpiPitch16;
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int hcol = n0 / 2 + (wave & 1) * 64 + jj * 32 + (lane & 31);
-            if (hcol < I) {
+        for (int i = 0; i < 4; ++i) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+            for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float g = acc[i][2 * jj][r], u = acc[i][2 * jj + 1][r];
-                        const float h = g / (1.0f + __expf(-g)) * u;
-                        const int64_t row = prow0 + frag_row(i, r);
-                        p.C[row * p.ldc + hcol] = f32_to_bf16_rne(h);
-                        if (p.GUf) {
-                            p.GUf[row * 2 * I + hcol] = g;
-                            p.GUf[row * 2 * I + I + hcol] = u;
-                        } else if (p.GU) {
-                            p.GU[row * 2 * I + hcol] = f32_to_bf16_rne(g);
-                            p.GU[row * 2 * I + I + hcol] = f32_to_bf16_rne(u);
-                        }
+                for (int q = 0; q < 4; ++q) {
+                    const int hc = (wave & 1) * 64 + jj * 32 + q * 8 + 4 * (lane >> 5);
+                    float g[4], u[4], h[4];
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        g[s] = acc[i][2 * jj][4 * q + s];
+                        u[s] = acc[i][2 * jj + 1][4 * q + s];
+                        h[s] = g[s] / (1.0f + __expf(-g[s])) * u[s];
                     }
+                    *(uint2*)(hb + rl * kEpiPitch16 + hc * 2) = pack_bf16x4(h[0], h[1], h[2], h[3]);
+                    if (f32gu) {
+                        *(floatx4*)(gb + rl * kEpiPitch32 + hc * 4) = floatx4{g[0], g[1], g[2], g[3]};
+                        *(floatx4*)(ub + rl * kEpiPitch32 + hc * 4) = floatx4{u[0], u[1], u[2], u[3]};
+                    } else if (anygu) {
+                        *(uint2*)(gb + rl * kEpiPitch16 + hc * 2) = pack_bf16x4(g[0], g[1], g[2], g[3]);
+                        *(uint2*)(ub + rl * kEpiPitch16 + hc * 2) = pack_bf16x4(u[0], u[1], u[2], u[3]);
+                    }
+                }
+            __syncthreads();
+            const int64_t row0 = prow0 + i * 64;
+            const int lim = I - hc0;
+            epi_copy_out<16>(hb, kEpiPitch16, (char*)(p.C + row0 * p.ldc + hc0), (int64_t)p.ldc * 2, lim * 2);
+            if (f32gu) {
+                epi_copy_out<32>(gb, gpitch, (char*)(p.GUf + row0 * 2 * I + hc0), (int64_t)I * 8, lim * 4);
+                epi_copy_out<32>(ub, gpitch, (char*)(p.GUf + row0 * 2 * I + I + hc0), (int64_t)I * 8, lim * 4);
+            } else if (anygu) {
+                epi_copy_out<16>(gb, gpitch, (char*)(p.GU + row0 * 2 * I + hc0), (int64_t)I * 4, lim * 2);
+                epi_copy_out<16>(ub, gpitch, (char*)(p.GU + row0 * 2 * I + I + hc0), (int64_t)I * 4, lim * 2);
             }
+            __syncthreads();
         }
     } else if (p.Cf) {  // kEpiStore, fp32 output
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int col = n0 + frag_col(j);
-            if (col < p.N) {
+        for (int i = 0; i < 4; ++i) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) p.Cf[(int64_t)(prow0 + frag_row(i, r)) * p.ldc + col] = acc[i][j][r];
-            }
+                for (int q = 0; q < 4; ++q)
+                    *(floatx4*)(smem + rl * kEpiPitch64 + frag_col(j, q) * 4) =
+                        floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            __syncthreads();
+            epi_copy_out<64>(smem, kEpiPitch64, (char*)(p.Cf + (int64_t)(prow0 + i * 64) * p.ldc + n0),
+                             (int64_t)p.ldc * 4, (p.N - n0) * 4);
+            __syncthreads();
         }
     } else {  // kEpiStore, bf16 output
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int col = n0 + frag_col(j);
-            if (col < p.N) {
+        for (int i = 0; i < 4; ++i) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        p.C[(int64_t)(prow0 + frag_row(i, r)) * p.ldc + col] = f32_to_bf16_rne(acc[i][j][r]);
-            }
+                for (int q = 0; q < 4; ++q)
+                    *(uint2*)(smem + rl * kEpiPitch32 + frag_col(j, q) * 2) =
+                        pack_bf16x4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            __syncthreads();
+            epi_copy_out<32>(smem, kEpiPitch32, (char*)(p.C + (int64_t)(prow0 + i * 64) * p.ldc + n0),
+                             (int64_t)p.ldc * 2, (p.N - n0) * 2);
+            __syncthreads();
         }
     }
 }
