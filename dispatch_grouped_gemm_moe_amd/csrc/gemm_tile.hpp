@@ -174,11 +174,18 @@ __device__ __forceinline__ int frag_col(int j, int q) {
     return wn * 128 + j * 32 + q * 8 + 4 * (lane >> 5);
 }
 
-// Four fp32 values as four bf16 (round to nearest even), packed for one
-// 8-byte store.
+// Four fp32 values as four bf16 (round to nearest even, gfx950's packed
+// conversion), packed for one 8-byte store.
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
-    return make_uint2((uint32_t)f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16),
-                      (uint32_t)f32_to_bf16_rne(c) | ((uint32_t)f32_to_bf16_rne(d) << 16));
+    return make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2{a, b}), bf16x2)),
+                      __builtin_bit_cast(uint32_t, __builtin_convertvector((floatx2{c, d}), bf16x2)));
+}
+
+// silu(g) * u with the hardware reciprocal (about 1 ulp) for the logistic.
+__device__ __forceinline__ float swiglu(float g, float u) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
 // Tile coordinates of tile v of a grouped GEMM over experts [e_begin, e_end):
@@ -232,8 +239,12 @@ __device__ __forceinline__ void epi_begin() {
 // row are not stored.
 template <int kChunks>
 __device__ __forceinline__ void epi_copy_out(const uint8_t* lds, int pitch, char* dst, int64_t ld, int limit) {
+    // an opaque copy of the thread index: its offsets are recomputed here
+    // (a few adds) instead of being hoisted out of the tile loop and spilled
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
 #pragma unroll
-    for (int c = threadIdx.x; c < kEpiRows * kChunks; c += kGemmThreads) {
+    for (int c = tid; c < kEpiRows * kChunks; c += kGemmThreads) {
         const int r = c / kChunks, ch = c % kChunks;
         if (ch * 16 < limit) *(intx4*)(dst + r * ld + ch * 16) = *(const intx4*)(lds + r * pitch + ch * 16);
     }
@@ -306,7 +317,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs p, int e, int ml, int n
                     for (int s = 0; s < 4; ++s) {
                         g[s] = acc[i][2 * jj][4 * q + s];
                         u[s] = acc[i][2 * jj + 1][4 * q + s];
-                        h[s] = g[s] / (1.0f + __expf(-g[s])) * u[s];
+                        h[s] = swiglu(g[s], u[s]);
                     }
                     *(uint2*)(hb + rl * kEpiPitch16 + hc * 2) = pack_bf16x4(h[0], h[1], h[2], h[3]);
                     if (f32gu) {
