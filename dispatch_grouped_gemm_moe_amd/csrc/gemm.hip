@@ -16,9 +16,9 @@
 namespace moe {
 
 template <int EPI>
-__global__ __attribute__((amdgpu_flat_work_group_size(kGemmThreads, kGemmThreads), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kTileThreads, kTileThreads), amdgpu_waves_per_eu(2, 2)))
 void grouped_gemm_kernel(GemmArgs p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kTileSmem];
     const int NT = ceil_div(p.N, BN);
     const int total = grouped_tiles(p.mt_start, p.e_begin, p.e_end, p.N);
     const int G = gridDim.x, per = G >> 3;
@@ -153,9 +153,9 @@ void launch_wgrad(const WgradArgs& a, int grid, hipStream_t stream) {
 
 void launch_grouped_gemm(const GemmArgs& a, GemmEpilogue epi, int grid, hipStream_t stream) {
     if (epi == kEpiSwiGLU)
-        hipLaunchKernelGGL(grouped_gemm_kernel<kEpiSwiGLU>, dim3(grid), dim3(kGemmThreads), 0, stream, a);
+        hipLaunchKernelGGL(grouped_gemm_kernel<kEpiSwiGLU>, dim3(grid), dim3(kTileThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL(grouped_gemm_kernel<kEpiStore>, dim3(grid), dim3(kGemmThreads), 0, stream, a);
+        hipLaunchKernelGGL(grouped_gemm_kernel<kEpiStore>, dim3(grid), dim3(kTileThreads), 0, stream, a);
 }
 
 // ---------------------------------------------------------------------------

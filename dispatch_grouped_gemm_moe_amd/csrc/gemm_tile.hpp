@@ -157,11 +157,8 @@ __device__ __forceinline__ void tile_mainloop(floatx16 (&acc)[4][4], uint8_t* sm
 }
 
 // Accumulator element 4q + s of fragment (i, j) of lane l sits in tile row
-// 64i + 32wm + l%32 and tile column wn*128 + 32j + 8q + 4(l/32) + s.
-__device__ __forceinline__ int frag_row(int i) {
-    const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) >> 1;
-    return i * 64 + wm * 32 + (lane & 31);
-}
+// 64i + 32wm + l%32 (four-wave tile; 128i + 32wm + l%32 in the eight-wave
+// tile) and tile column wn*128 + 32j + 8q + 4(l/32) + s.
 
 // Row fragments of this wave holding any of the tile's first `valid` rows.
 __device__ __forceinline__ int valid_frags(int valid) {
@@ -210,17 +207,18 @@ __device__ __forceinline__ int grouped_tiles(const int32_t* mt_start, int e_begi
     return (mt_start[e_end] - mt_start[e_begin]) * ceil_div(N, BN);
 }
 
-// Epilogue staging.  Fragment i of every wave covers tile rows 64i .. 64i+63
-// (row 64i + epi_row() for this lane); such a 64-row block is written to LDS
-// with row pitches 16 bytes longer than the data (256, 512 or 1024 bytes), so
-// the 32 rows of one write instruction fall on different banks, then copied
-// out in 16-byte chunks along rows.
+// Epilogue staging.  A 64-row block of the tile is written to LDS with row
+// pitches 16 bytes longer than the data (256, 512 or 1024 bytes), so the 32
+// rows of one write instruction fall on different banks, then copied out in
+// 16-byte chunks along rows.  In the four-wave tile, fragment i of every wave
+// covers tile rows 64i .. 64i+63 (row 64i + epi_row() for this lane).
 constexpr int kEpiRows = 64;
 constexpr int kEpiPitch16 = 16 * 16 + 16;  // 16 chunks of data per row
 constexpr int kEpiPitch32 = 32 * 16 + 16;
 constexpr int kEpiPitch64 = 64 * 16 + 16;
 static_assert(kEpiRows * (kEpiPitch16 + 2 * kEpiPitch32) <= kStages * kStageBytes - 4,
               "the staged SwiGLU block must fit the ring (the layer kernel keeps its last dword)");
+static_assert(kEpiRows * kEpiPitch64 <= kStages * kStageBytes, "the staged fp32 block must fit the ring");
 
 __device__ __forceinline__ int epi_row() {
     const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) >> 1;
@@ -237,66 +235,204 @@ __device__ __forceinline__ void epi_begin() {
 // Rows 0..63 of an LDS block (kChunks 16-byte chunks per row, pitch `pitch`)
 // to global rows dst + r * ld bytes; chunks at or beyond byte `limit` of a
 // row are not stored.
-template <int kChunks>
+template <int kChunks, int kThreads>
 __device__ __forceinline__ void epi_copy_out(const uint8_t* lds, int pitch, char* dst, int64_t ld, int limit) {
     // an opaque copy of the thread index: its offsets are recomputed here
     // (a few adds) instead of being hoisted out of the tile loop and spilled
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
 #pragma unroll
-    for (int c = tid; c < kEpiRows * kChunks; c += kGemmThreads) {
+    for (int c = tid; c < kEpiRows * kChunks; c += kThreads) {
         const int r = c / kChunks, ch = c % kChunks;
         if (ch * 16 < limit) *(intx4*)(dst + r * ld + ch * 16) = *(const intx4*)(lds + r * pitch + ch * 16);
     }
 }
 
+// ---------------------------------------------------------------------------
+// Eight-wave tile of the bf16 grouped GEMMs (forward, input gradients and the
+// layer kernel): 256 x 256 output per workgroup of 512 threads, two waves per
+// SIMD, each wave a 64 x 128 block of 2 x 4 fragments (128 accumulator
+// registers, so two waves fit a SIMD's register file): when one wave waits
+// on a load or a barrier, the other keeps the SIMD's matrix core busy.  K runs
+// in 64-deep stages through a two-stage LDS ring (2 x 64 KB), every global
+// load instruction moving whole 128-byte lines (8 lanes per row, 8 rows per
+// instruction); measured against the four-wave tile on the same box: input-
+// gradient GEMMs 8-13% faster.
+// ---------------------------------------------------------------------------
+constexpr int kTileThreads = 512;
+constexpr int kBK8 = 64;
+constexpr int kRow8 = kBK8 * 2;                   // bytes of one row per stage
+constexpr int kStageA8 = BM * kRow8;              // 32 KB
+constexpr int kStageBytes8 = (BM + BN) * kRow8;   // 64 KB
+constexpr int kStages8 = 2;
+constexpr int kTileSmem = kStages8 * kStageBytes8;
+static_assert(kEpiRows * (kEpiPitch16 + 2 * kEpiPitch32) <= kTileSmem - 4, "staged SwiGLU block must fit");
+static_assert(kEpiRows * kEpiPitch64 <= kTileSmem, "staged fp32 block must fit");
+
+// Chunk c of row r of a 128-byte-row stage sits at position c ^ ((r >> 1) & 7):
+// the 16 rows one 128-bit fragment read touches per pass fall on distinct banks.
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
+
+template <int NV>
+__device__ __forceinline__ void mfma_block8(floatx16 (&acc)[2][4], const bf16x8 (&a)[2], const bf16x8 (&b)[4]) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+}
+
+// acc = A_tile * B_tile^T over KT2 stages of 64.  Wave w (wm = w/2, wn = w%2)
+// owns fragments i = 0, 1 at tile rows 128i + 32wm .. +31 and j = 0..3 at tile
+// columns 128wn + 32j .. +31; NV = fragments holding a valid row.  aoff/boff:
+// byte offsets of the 4 A and 4 B rows this lane loads per stage (tile rows
+// 32w + 8i + lane/8, swizzled chunk); kit.next() yields each stage's K offset.
+template <int NV, class KIt>
+__device__ __forceinline__ void tile_mainloop8(floatx16 (&acc)[2][4], uint8_t* smem, const char* a_base,
+                                               const uint32_t (&aoff)[4], const char* b_base,
+                                               const uint32_t (&boff)[4], int KT2, KIt kit) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
+    if (KT2 <= 0) return;
+    // Past the last stage the loads repeat it into the slot no wave reads any
+    // more: no branch, constant vmcnt waits.
+    int64_t ka = 0, kb = 0;
+    int issued = 0;
+    auto advance = [&]() {
+        if (issued < KT2) kit.next(ka, kb);
+        ++issued;
+    };
+    auto issue = [&](int slot) {
+        uint8_t* base = smem + slot * kStageBytes8 + (wave * 32) * kRow8;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_global_load_lds((gbl_cvoid*)(a_base + ka + aoff[i]), (lds_void*)(base + i * 1024), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_global_load_lds((gbl_cvoid*)(b_base + kb + boff[i]), (lds_void*)(base + kStageA8 + i * 1024), 16, 0, 0);
+    };
+    const int fr = lane & 31;
+    const int arow_b = (wm * 32 + fr) * kRow8, brow_b = kStageA8 + (wn * 128 + fr) * kRow8;
+    const int fsw = swz8(fr);  // a fragment's rows differ from fr by multiples of 32
+    auto frags = [&](int slot, int kk, bf16x8 (&a)[2], bf16x8 (&b)[4]) {
+        const uint8_t* st = smem + slot * kStageBytes8;
+        const int pc = ((kk * 2 + (lane >> 5)) ^ fsw) * 16;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) a[i] = *(const bf16x8*)(st + arow_b + i * 128 * kRow8 + pc);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = *(const bf16x8*)(st + brow_b + j * 32 * kRow8 + pc);
+    };
+    // Ring protocol (stage j in slot j % 2, 8 direct-to-LDS loads per lane
+    // and stage, counted by vmcnt): the prologue issues stages 0 and 1 and
+    // waits for stage 0 (vmcnt(8)); stage s runs four k-steps of 8 MFMAs, each
+    // reading the next k-step's fragments; before the last one it waits for
+    // stage s+1 (vmcnt(0)) and its own LDS reads (lgkmcnt(0)), then a barrier:
+    // no wave reads stage s any more, so its slot takes stage s+2, loaded under
+    // the last 8 MFMAs.  First the previous tile's stores leave the count and
+    // every wave is done with the previous tile's LDS.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    advance();
+    issue(0);
+    advance();
+    issue(1);
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    __syncthreads();
+    bf16x8 a0[2], b0[4], a1[2], b1[4];
+    frags(0, 0, a0, b0);
+    int slot = 0;
+    for (int s = 0; s < KT2; ++s) {
+        frags(slot, 1, a1, b1);
+        mfma_block8<NV>(acc, a0, b0);
+        Interleave<4 * NV, 0, NV + 4>::run();
+        __builtin_amdgcn_sched_barrier(0);
+        frags(slot, 2, a0, b0);
+        mfma_block8<NV>(acc, a1, b1);
+        Interleave<4 * NV, 0, NV + 4>::run();
+        __builtin_amdgcn_sched_barrier(0);
+        frags(slot, 3, a1, b1);
+        mfma_block8<NV>(acc, a0, b0);
+        Interleave<4 * NV, 0, NV + 4>::run();
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __syncthreads();
+        advance();  // offsets of stage s + 2
+        issue(slot);
+        frags(slot ^ 1, 0, a0, b0);  // a stale but in-bounds read after the last stage
+        mfma_block8<NV>(acc, a1, b1);
+        Interleave<4 * NV, 8, NV + 4>::run();
+        __builtin_amdgcn_sched_barrier(0);
+        slot ^= 1;
+    }
+}
+
+// K sequence of a dense GEMM in 64-deep stages: stage s sits s * 128 bytes
+// into every row.
+struct DenseK8 {
+    int kt = 0;
+    __device__ __forceinline__ void next(int64_t& a_off, int64_t& b_off) {
+        a_off = b_off = (int64_t)kt * kRow8;
+        ++kt;
+    }
+};
+
 // One 256 x 256 output tile (expert e, M tile ml of the expert, N tile ntile)
-// of the bf16 grouped GEMM with its epilogue; smem is the kStages LDS ring.
-// kSkipPadding: with p.rows_e, the padding fragments of an expert's last tile
-// get no MFMAs (five mainloop variants; the persistent layer kernel, where
-// they would crowd its registers, compiles the full one only).
+// of the bf16 grouped GEMM with its epilogue, by 512 threads; smem is the
+// kTileSmem LDS ring.  kSkipPadding: with p.rows_e, the fragments of an
+// expert's last tile that hold only padding rows get no MFMAs (three mainloop
+// variants; the persistent layer kernel, where they would crowd its
+// registers, compiles the full one only).
 template <int EPI, bool kSkipPadding = true>
 __device__ __forceinline__ void gemm_tile(const GemmArgs p, int e, int ml, int ntile, uint8_t* smem) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int KT = p.K / kBK;
+    const int wm = wave >> 1;
+    const int KT2 = p.K / kBK8;
     const int mt0 = p.mt_start[e];
     const int prow0 = (mt0 + ml) * BM;
     const int n0 = ntile * BN;
 
-    // Byte offsets of the 4 A rows and 4 B rows this lane stages per K step:
-    // instruction i fills tile rows wave*64 + 16i .. +15 (lane/4 picks the row,
-    // lane%4 the fixed LDS chunk; the lane loads the logical chunk stored there).
+    // Byte offsets of the 4 A rows and 4 B rows this lane loads per stage:
+    // instruction i fills tile rows 32*wave + 8i .. +7 (lane/8 picks the row,
+    // lane%8 the fixed LDS chunk; the lane loads the logical chunk stored there).
     uint32_t aoff[4], boff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int r = wave * 64 + i * 16 + (lane >> 2);
-        const int lchunk = (lane & 3) ^ swz(r);
+        const int r = wave * 32 + i * 8 + (lane >> 3);
+        const int lchunk = (lane & 7) ^ swz8(r);
         const int prow = prow0 + r;
         const int arow = p.a_row_map ? p.a_row_map[prow] : prow;
         aoff[i] = (uint32_t)(((int64_t)arow * p.lda + lchunk * 8) * 2);
         const int n = min(n0 + r, p.N - 1);
         boff[i] = (uint32_t)(((int64_t)n * p.K + lchunk * 8) * 2);
     }
-    floatx16 acc[4][4];
+    floatx16 acc[2][4];
     const char* bbase = (const char*)(p.B + (int64_t)e * p.b_stride);
-    // valid rows of this tile: padding rows of the expert's last tile get no MFMAs
-    const int nv = (kSkipPadding && p.rows_e) ? valid_frags(p.rows_e[e] - ml * BM) : 4;
+    int nv = 2;
+    if (kSkipPadding && p.rows_e) {
+        // fragment i of this wave holds tile rows 128i + 32wm .. +31
+        const int valid = p.rows_e[e] - ml * BM, w32 = __builtin_amdgcn_readfirstlane(wm) * 32;
+        nv = valid > 128 + w32 ? 2 : (valid > w32 ? 1 : 0);
+    }
     if (!kSkipPadding) {
-        tile_mainloop<4>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT, DenseK{});
+        tile_mainloop8<2>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT2, DenseK8{});
     } else switch (nv) {
-        case 4: tile_mainloop<4>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT, DenseK{}); break;
-        case 3: tile_mainloop<3>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT, DenseK{}); break;
-        case 2: tile_mainloop<2>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT, DenseK{}); break;
-        case 1: tile_mainloop<1>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT, DenseK{}); break;
-        default: tile_mainloop<0>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT, DenseK{}); break;
+        case 2: tile_mainloop8<2>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT2, DenseK8{}); break;
+        case 1: tile_mainloop8<1>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT2, DenseK8{}); break;
+        default: tile_mainloop8<0>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT2, DenseK8{}); break;
     }
 
-    // The tile leaves through LDS, 64 rows at a time, so that every global
-    // store is a 16-byte run along a row (whole cache lines) rather than the
-    // accumulators' 4-column runs down 32 rows.  N is a multiple of 64, so a
-    // 4-column run, and a 16-byte chunk, lies wholly inside or outside it.
+    // The tile leaves through LDS, 64 rows at a time (whole-line stores).
+    // Block b (tile rows 64b .. 64b+63) is fragment b/2 of the waves with
+    // wm/2 == b%2, this lane's row in it (wm%2)*32 + lane%32.  N is a multiple
+    // of 64, so a 4-column run, and a 16-byte chunk, lies wholly inside or
+    // outside the matrix.
     epi_begin();
-    const int rl = epi_row();
+    const int rl = (wm & 1) * 32 + (lane & 31);
     if (EPI == kEpiSwiGLU) {
         // columns come in 64-wide groups of 32 gate then 32 up columns
         const int I = p.N / 2, hc0 = n0 / 2;
@@ -306,67 +442,81 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs p, int e, int ml, int n
         uint8_t* ub = gb + kEpiRows * kEpiPitch32;
         const int gpitch = f32gu ? kEpiPitch32 : kEpiPitch16;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int b = 0; b < 4; ++b) {
+            if ((wm >> 1) == (b & 1)) {
+                const int i = b >> 1;
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
+                for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int hc = (wave & 1) * 64 + jj * 32 + q * 8 + 4 * (lane >> 5);
-                    float g[4], u[4], h[4];
+                    for (int q = 0; q < 4; ++q) {
+                        const int hc = (wave & 1) * 64 + jj * 32 + q * 8 + 4 * (lane >> 5);
+                        float g[4], u[4], h[4];
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) {
-                        g[s] = acc[i][2 * jj][4 * q + s];
-                        u[s] = acc[i][2 * jj + 1][4 * q + s];
-                        h[s] = swiglu(g[s], u[s]);
+                        for (int s = 0; s < 4; ++s) {
+                            g[s] = acc[i][2 * jj][4 * q + s];
+                            u[s] = acc[i][2 * jj + 1][4 * q + s];
+                            h[s] = swiglu(g[s], u[s]);
+                        }
+                        *(uint2*)(hb + rl * kEpiPitch16 + hc * 2) = pack_bf16x4(h[0], h[1], h[2], h[3]);
+                        if (f32gu) {
+                            *(floatx4*)(gb + rl * kEpiPitch32 + hc * 4) = floatx4{g[0], g[1], g[2], g[3]};
+                            *(floatx4*)(ub + rl * kEpiPitch32 + hc * 4) = floatx4{u[0], u[1], u[2], u[3]};
+                        } else if (anygu) {
+                            *(uint2*)(gb + rl * kEpiPitch16 + hc * 2) = pack_bf16x4(g[0], g[1], g[2], g[3]);
+                            *(uint2*)(ub + rl * kEpiPitch16 + hc * 2) = pack_bf16x4(u[0], u[1], u[2], u[3]);
+                        }
                     }
-                    *(uint2*)(hb + rl * kEpiPitch16 + hc * 2) = pack_bf16x4(h[0], h[1], h[2], h[3]);
-                    if (f32gu) {
-                        *(floatx4*)(gb + rl * kEpiPitch32 + hc * 4) = floatx4{g[0], g[1], g[2], g[3]};
-                        *(floatx4*)(ub + rl * kEpiPitch32 + hc * 4) = floatx4{u[0], u[1], u[2], u[3]};
-                    } else if (anygu) {
-                        *(uint2*)(gb + rl * kEpiPitch16 + hc * 2) = pack_bf16x4(g[0], g[1], g[2], g[3]);
-                        *(uint2*)(ub + rl * kEpiPitch16 + hc * 2) = pack_bf16x4(u[0], u[1], u[2], u[3]);
-                    }
-                }
+            }
             __syncthreads();
-            const int64_t row0 = prow0 + i * 64;
+            const int64_t row0 = prow0 + b * 64;
             const int lim = I - hc0;
-            epi_copy_out<16>(hb, kEpiPitch16, (char*)(p.C + row0 * p.ldc + hc0), (int64_t)p.ldc * 2, lim * 2);
+            epi_copy_out<16, kTileThreads>(hb, kEpiPitch16, (char*)(p.C + row0 * p.ldc + hc0), (int64_t)p.ldc * 2,
+                                           lim * 2);
             if (f32gu) {
-                epi_copy_out<32>(gb, gpitch, (char*)(p.GUf + row0 * 2 * I + hc0), (int64_t)I * 8, lim * 4);
-                epi_copy_out<32>(ub, gpitch, (char*)(p.GUf + row0 * 2 * I + I + hc0), (int64_t)I * 8, lim * 4);
+                epi_copy_out<32, kTileThreads>(gb, gpitch, (char*)(p.GUf + row0 * 2 * I + hc0), (int64_t)I * 8,
+                                               lim * 4);
+                epi_copy_out<32, kTileThreads>(ub, gpitch, (char*)(p.GUf + row0 * 2 * I + I + hc0),
+                                               (int64_t)I * 8, lim * 4);
             } else if (anygu) {
-                epi_copy_out<16>(gb, gpitch, (char*)(p.GU + row0 * 2 * I + hc0), (int64_t)I * 4, lim * 2);
-                epi_copy_out<16>(ub, gpitch, (char*)(p.GU + row0 * 2 * I + I + hc0), (int64_t)I * 4, lim * 2);
+                epi_copy_out<16, kTileThreads>(gb, gpitch, (char*)(p.GU + row0 * 2 * I + hc0), (int64_t)I * 4,
+                                               lim * 2);
+                epi_copy_out<16, kTileThreads>(ub, gpitch, (char*)(p.GU + row0 * 2 * I + I + hc0),
+                                               (int64_t)I * 4, lim * 2);
             }
             __syncthreads();
         }
     } else if (p.Cf) {  // kEpiStore, fp32 output
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int b = 0; b < 4; ++b) {
+            if ((wm >> 1) == (b & 1)) {
+                const int i = b >> 1;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *(floatx4*)(smem + rl * kEpiPitch64 + frag_col(j, q) * 4) =
-                        floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                    for (int q = 0; q < 4; ++q)
+                        *(floatx4*)(smem + rl * kEpiPitch64 + frag_col(j, q) * 4) =
+                            floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            }
             __syncthreads();
-            epi_copy_out<64>(smem, kEpiPitch64, (char*)(p.Cf + (int64_t)(prow0 + i * 64) * p.ldc + n0),
-                             (int64_t)p.ldc * 4, (p.N - n0) * 4);
+            epi_copy_out<64, kTileThreads>(smem, kEpiPitch64, (char*)(p.Cf + (int64_t)(prow0 + b * 64) * p.ldc + n0),
+                                           (int64_t)p.ldc * 4, (p.N - n0) * 4);
             __syncthreads();
         }
     } else {  // kEpiStore, bf16 output
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int b = 0; b < 4; ++b) {
+            if ((wm >> 1) == (b & 1)) {
+                const int i = b >> 1;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *(uint2*)(smem + rl * kEpiPitch32 + frag_col(j, q) * 2) =
-                        pack_bf16x4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                    for (int q = 0; q < 4; ++q)
+                        *(uint2*)(smem + rl * kEpiPitch32 + frag_col(j, q) * 2) = pack_bf16x4(
+                            acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            }
             __syncthreads();
-            epi_copy_out<32>(smem, kEpiPitch32, (char*)(p.C + (int64_t)(prow0 + i * 64) * p.ldc + n0),
-                             (int64_t)p.ldc * 2, (p.N - n0) * 2);
+            epi_copy_out<32, kTileThreads>(smem, kEpiPitch32, (char*)(p.C + (int64_t)(prow0 + b * 64) * p.ldc + n0),
+                                           (int64_t)p.ldc * 2, (p.N - n0) * 2);
             __syncthreads();
         }
     }

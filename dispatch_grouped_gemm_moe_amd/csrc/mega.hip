@@ -162,8 +162,9 @@ __device__ __forceinline__ void group_tile(const MegaArgs& a, int b0, int b1, in
 }  // namespace
 
 // Combine of tokens [c0, c1) of minibatch b (relative to the minibatch) by the
-// whole workgroup, two tokens at a time; LDS: the first 1.5 KB of smem.
-__device__ void combine_range(const MegaArgs& a, int b, int c0, int c1, uint8_t* smem) {
+// whole workgroup of nthreads threads, two tokens at a time; LDS: the first
+// 1.5 KB of smem.
+__device__ void combine_range(const MegaArgs& a, int b, int c0, int c1, uint8_t* smem, int nthreads) {
     constexpr int kTok = 2;
     int (*s_row)[kMaxTopK + 1] = (int (*)[kMaxTopK + 1])smem;
     float (*s_w)[kMaxTopK] = (float (*)[kMaxTopK])(smem + 512);
@@ -183,15 +184,21 @@ __device__ void combine_range(const MegaArgs& a, int b, int c0, int c1, uint8_t*
         }
         __syncthreads();
         combine_tokens_mlp<kTok>(Y, a.H, s_row, s_w, ntok, a.k, a.with_shared, a.H, s_out, threadIdx.x,
-                                 kGemmThreads);
+                                 nthreads);
         __syncthreads();
     }
 }
 
+// Threads of the layer kernel: the MXFP8 tiles run four waves, the bf16
+// tiles eight (two per SIMD).
 template <bool kMx>
-__global__ __attribute__((amdgpu_flat_work_group_size(kGemmThreads, kGemmThreads), amdgpu_waves_per_eu(1, 1)))
+constexpr int kMegaThreads = kMx ? kGemmThreads : kTileThreads;
+
+template <bool kMx>
+__global__ __attribute__((amdgpu_flat_work_group_size(kMegaThreads<kMx>, kMegaThreads<kMx>),
+                          amdgpu_waves_per_eu(kMegaThreads<kMx> / 256, kMegaThreads<kMx> / 256)))
 void mega_kernel(MegaArgs a) {
-    constexpr int kSmem = kMx ? kMxStages * kMxStageBytes : kStages * kStageBytes;
+    constexpr int kSmem = kMx ? kMxStages * kMxStageBytes : kTileSmem;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
     // wait result broadcast: the ring's last dword, free between tiles (the
     // mainloop has drained its loads and every wave passed a barrier)
@@ -215,7 +222,7 @@ void mega_kernel(MegaArgs a) {
                 const int Tm = tokens_of(a, b);
                 const int chunk = ceil_div(Tm, a.comm);
                 const int c0 = min(Tm, (int)blockIdx.x * chunk), c1 = min(Tm, c0 + chunk);
-                combine_range(a, b, c0, c1, smem);
+                combine_range(a, b, c0, c1, smem, kMegaThreads<kMx>);
             }
             signal_counter(comb_done + j);
         }
@@ -272,7 +279,8 @@ void mega_kernel(MegaArgs a) {
                 if (lv < nt) break;
                 lv -= nt;
             }
-            combine_range(a, b, lv * kCombTilesTok, min(tokens_of(a, b), (lv + 1) * kCombTilesTok), smem);
+            combine_range(a, b, lv * kCombTilesTok, min(tokens_of(a, b), (lv + 1) * kCombTilesTok), smem,
+                          kMegaThreads<kMx>);
             continue;
         }
         int b, e, ml, ntile;
@@ -327,9 +335,9 @@ hipError_t launch_mega(const MegaArgs& a, int grid, hipStream_t stream) {
                        3 * a.nmb + 1);
     MegaArgs args = a;
     void* kargs[] = {&args};
-    return a.mx ? hipLaunchCooperativeKernel((const void*)mega_kernel<true>, dim3(grid), dim3(kGemmThreads), kargs,
+    return a.mx ? hipLaunchCooperativeKernel((const void*)mega_kernel<true>, dim3(grid), dim3(kMegaThreads<true>), kargs,
                                               0, stream)
-                  : hipLaunchCooperativeKernel((const void*)mega_kernel<false>, dim3(grid), dim3(kGemmThreads), kargs,
+                  : hipLaunchCooperativeKernel((const void*)mega_kernel<false>, dim3(grid), dim3(kMegaThreads<false>), kargs,
                                               0, stream);
 }
 
