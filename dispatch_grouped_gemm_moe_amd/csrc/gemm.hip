@@ -41,8 +41,10 @@ void grouped_gemm_kernel(GemmArgs p) {
 // ---------------------------------------------------------------------------
 
 // K sequence of expert e's rows: for each minibatch b its padded row range
-// [mt_b[e], mt_b[e+1]) x BM, in 32-row K steps; A and B copies of
-// minibatch b lie a_mb / b_mb bytes after minibatch 0's.
+// [mt_b[e], mt_b[e+1]) x BM, in 64-row K stages up to the last one holding a
+// routed row (the dY-side operand is zero on every padding row, so the
+// padding rows a stage takes in add nothing); A and B copies of minibatch b
+// lie a_mb / b_mb bytes after minibatch 0's.
 struct SegmentK {
     const int32_t* mt;    // [nmb][mt_ld]
     const int32_t* rows;  // [nmb][mt_ld]
@@ -63,20 +65,20 @@ struct SegmentK {
             const __attribute__((address_space(4))) int32_t* crows =
                 (const __attribute__((address_space(4))) int32_t*)rows;
             row0 = (int64_t)cmt[(int64_t)b * mt_ld + e] * BM;
-            nsteps = ceil_div(crows[(int64_t)b * mt_ld + e], kBK);
+            nsteps = ceil_div(crows[(int64_t)b * mt_ld + e], kBK8);
             step = 0;
         }
-        const int64_t kbyte = (row0 + (int64_t)step * kBK) * 2;
+        const int64_t kbyte = (row0 + (int64_t)step * kBK8) * 2;
         a_off = (int64_t)b * a_mb + kbyte;
         b_off = (int64_t)b * b_mb + kbyte;
         ++step;
     }
 };
 
-__global__ __attribute__((amdgpu_flat_work_group_size(kGemmThreads, kGemmThreads), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kTileThreads, kTileThreads), amdgpu_waves_per_eu(2, 2)))
 void wgrad_kernel(WgradArgs p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kTileSmem];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1;
     const int MT = ceil_div(p.M, BM), NT = ceil_div(p.N, BN);
     const int G = gridDim.x, per = G >> 3;
     const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
@@ -95,39 +97,43 @@ void wgrad_kernel(WgradArgs p) {
         const int e = li / cnt, t = li - e * cnt;
         const int m0 = (mlo + t % bmt) * BM, n0 = (nlo + t / bmt) * BN;
         int KT = 0;
-        for (int b = 0; b < p.nmb; ++b) KT += ceil_div(p.rows[(int64_t)b * p.mt_ld + e], kBK);
+        for (int b = 0; b < p.nmb; ++b) KT += ceil_div(p.rows[(int64_t)b * p.mt_ld + e], kBK8);
         uint32_t aoff[4], boff[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = wave * 64 + i * 16 + (lane >> 2);
-            const int lchunk = (lane & 3) ^ swz(r);
+            const int r = wave * 32 + i * 8 + (lane >> 3);
+            const int lchunk = (lane & 7) ^ swz8(r);
             aoff[i] = (uint32_t)(((int64_t)min(m0 + r, p.M - 1) * p.ld + lchunk * 8) * 2);
             boff[i] = (uint32_t)(((int64_t)min(n0 + r, p.N - 1) * p.ld + lchunk * 8) * 2);
         }
         SegmentK kit{p.mt, p.rows, p.mt_ld, e, p.nmb, p.a_mb, p.b_mb};
-        floatx16 acc[4][4];
-        tile_mainloop<4>(acc, smem, (const char*)p.A, aoff, (const char*)p.B, boff, KT, kit);
+        floatx16 acc[2][4];
+        tile_mainloop8<2>(acc, smem, (const char*)p.A, aoff, (const char*)p.B, boff, KT, kit);
         // columns < n_split go to C0, the rest to C1 (column - n_split); the
         // last expert writes to the shared-expert outputs when they are given
         const bool shared = p.Cs0 && e == p.Et - 1;
         float* c0 = shared ? p.Cs0 : p.C0 + (int64_t)e * p.M * p.n_split;
         float* c1 = shared ? p.Cs1 : (p.C1 ? p.C1 + (int64_t)e * p.M * (p.N - p.n_split) : nullptr);
-        // Staged through LDS 64 rows at a time (full-line stores).  M, N and
-        // n_split are multiples of 64: a 16-byte chunk lies on one side of the
-        // split and inside or outside the matrix as a whole.
+        // Staged through LDS 64 rows at a time (full-line stores); block b is
+        // fragment b/2 of the waves with wm/2 == b%2.  M, N and n_split are
+        // multiples of 64: a 16-byte chunk lies on one side of the split and
+        // inside or outside the matrix as a whole.
         epi_begin();
-        const int rl = epi_row();
+        const int rl = (wm & 1) * 32 + (lane & 31);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int b = 0; b < 4; ++b) {
+            if ((wm >> 1) == (b & 1)) {
+                const int i = b >> 1;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *(floatx4*)(smem + rl * kEpiPitch64 + frag_col(j, q) * 4) =
-                        floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                    for (int q = 0; q < 4; ++q)
+                        *(floatx4*)(smem + rl * kEpiPitch64 + frag_col(j, q) * 4) =
+                            floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            }
             __syncthreads();
-            for (int c = threadIdx.x; c < kEpiRows * 64; c += kGemmThreads) {
-                const int r = c >> 6, col = n0 + (c & 63) * 4, m = m0 + i * 64 + r;
+            for (int c = threadIdx.x; c < kEpiRows * 64; c += kTileThreads) {
+                const int r = c >> 6, col = n0 + (c & 63) * 4, m = m0 + b * 64 + r;
                 if (m >= p.M || col >= p.N) continue;
                 float* dst = col < p.n_split ? c0 + (int64_t)m * p.n_split + col
                                              : c1 + (int64_t)m * (p.N - p.n_split) + (col - p.n_split);
@@ -148,7 +154,7 @@ void launch_wgrad(const WgradArgs& a, int grid, hipStream_t stream) {
         if (cost[i] < cost[best]) best = i;
     w.mq = 8 >> best;
     w.nq = 1 << best;
-    hipLaunchKernelGGL(wgrad_kernel, dim3(grid), dim3(kGemmThreads), 0, stream, w);
+    hipLaunchKernelGGL(wgrad_kernel, dim3(grid), dim3(kTileThreads), 0, stream, w);
 }
 
 void launch_grouped_gemm(const GemmArgs& a, GemmEpilogue epi, int grid, hipStream_t stream) {
