@@ -7,21 +7,6 @@
 
 namespace moe {
 
-// LDS ring of kStages pipeline stages; a stage holds the A tile [BM][BK] then
-// the B tile [BN][BK] (bf16, BK = 32: 64-byte rows of four 16-byte chunks).
-// Chunk c of row r sits at position c ^ f(r), f(r) = (r >> 2) & 3.  With this
-// swizzle the 128-bit fragment reads (lane l: row l%32, chunk 2*kstep + l/32)
-// are free of bank conflicts on gfx950's LDS; swizzles that also mix in row
-// bit 1 (or use r & 3) measured 2-way conflicted with rocprofv3's
-// SQ_LDS_BANK_CONFLICT, as did unswizzled rows.
-constexpr int kBK = 32;
-constexpr int kRowBytes = kBK * 2;
-constexpr int kStageA = BM * kRowBytes;
-constexpr int kStageBytes = (BM + BN) * kRowBytes;
-constexpr int kStages = 5;  // 160 KB of LDS: loads run up to 4 K steps ahead
-
-__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
-
 // Scheduling: interleave M MFMAs, V global loads and D LDS reads round robin.
 template <int M, int V, int D>
 struct Interleave {
@@ -34,133 +19,14 @@ struct Interleave {
     }
 };
 
-// MFMAs of the first NV row fragments (the others are all padding rows).
 // The B fragment is the MFMA's first operand, so each accumulator holds the
-// transposed 32 x 32 block: a lane keeps one tile row and runs of four
-// consecutive tile columns, which the epilogues store 8 or 16 bytes at a time.
-template <int NV>
-__device__ __forceinline__ void mfma_block(floatx16 (&acc)[4][4], const bf16x8 (&a)[4], const bf16x8 (&b)[4]) {
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
-}
+// transposed 32 x 32 block: accumulator element 4q + s of fragment (i, j) of
+// lane l sits in tile row 128i + 32wm + l%32 and tile column
+// wn*128 + 32j + 8q + 4(l/32) + s -- one tile row, runs of four consecutive
+// columns, which the epilogues stage 8 or 16 bytes at a time.
 
-
-// K sequence of a dense GEMM: K step kt sits kt * 64 bytes into every row.
-struct DenseK {
-    int kt = 0;
-    __device__ __forceinline__ void next(int64_t& a_off, int64_t& b_off) {
-        a_off = b_off = (int64_t)kt * kBK * 2;
-        ++kt;
-    }
-};
-
-// One 256 x 256 output tile: acc = A_tile * B_tile^T over KT K steps.
-// a_base/b_base + aoff[i]/boff[i] address the 4 A and 4 B rows this lane
-// stages (tile rows wave*64 + 16i + lane/4, swizzled chunk); kit.next() gives
-// the byte offset of each successive K step, called in K order.
-// Row fragments: fragment i of wave (wm, wn) holds tile rows 64i + 32wm ..
-// +31, so a tile's valid rows (a prefix) spread evenly over both wave rows, and
-// NV (the fragments of this wave holding any valid row) cuts the MFMAs and
-// fragment reads of both alike.  Loads and barriers do not depend on NV.
-template <int NV, class KIt>
-__device__ __forceinline__ void tile_mainloop(floatx16 (&acc)[4][4], uint8_t* smem, const char* a_base,
-                                              const uint32_t (&aoff)[4], const char* b_base,
-                                              const uint32_t (&boff)[4], int KT, KIt kit) {
-    const int lane = threadIdx.x & 63;
-    // the wave index is uniform: keep it (and every LDS base built from it) scalar
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
-    if (KT <= 0) return;
-
-    // Byte offsets of the next K step to load.  Past the last step the loads
-    // repeat it: they land in the slot of a step every wave has finished with,
-    // so the loads need no branch (and interleave with the MFMAs) and every
-    // vmcnt wait below is a constant.
-    int64_t ka = 0, kb = 0;
-    int issued = 0;
-    auto advance = [&]() {
-        if (issued < KT) kit.next(ka, kb);
-        ++issued;
-    };
-    auto issue = [&](int slot) {
-        uint8_t* base = smem + slot * kStageBytes + (wave * 64) * kRowBytes;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_global_load_lds((gbl_cvoid*)(a_base + ka + aoff[i]), (lds_void*)(base + i * 1024), 16, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_global_load_lds((gbl_cvoid*)(b_base + kb + boff[i]), (lds_void*)(base + kStageA + i * 1024), 16, 0, 0);
-    };
-    // MFMA operand fragments of k-step kk (16 deep) of the K step in slot `slot`.
-    const int fr = lane & 31;
-    const int arow_b = (wm * 32 + fr) * kRowBytes, brow_b = kStageA + (wn * 128 + fr) * kRowBytes;
-    const int fsw = swz(fr);
-    auto frags = [&](int slot, int kk, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
-        const uint8_t* st = smem + slot * kStageBytes;
-        const int pc = ((kk * 2 + (lane >> 5)) ^ fsw) * 16;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) a[i] = *(const bf16x8*)(st + arow_b + i * 64 * kRowBytes + pc);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = *(const bf16x8*)(st + brow_b + j * 32 * kRowBytes + pc);
-    };
-
-    // Ring protocol (S = kStages slots, K step j lives in slot j % S, each
-    // step is 8 direct-to-LDS loads per lane, counted by vmcnt; S steps are
-    // always in flight):
-    //  - prologue: issue steps 0..S-1, wait for step 0 (vmcnt(8(S-1)));
-    //  - K step kt: before the barrier wait for step kt+1 (the S-2 newer steps
-    //    stay in flight: vmcnt(8(S-2))) and for this wave's own LDS reads of
-    //    step kt (lgkmcnt(0)); after the barrier no wave reads step kt any
-    //    more, so its slot takes step kt+S, loaded under the next 16 MFMAs.
-    // First the previous tile's stores leave the vmcnt count and every wave is
-    // done reading the previous tile's stages.
-    static_assert(kStages == 5, "the vmcnt immediates below assume 5 stages of 8 loads");
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kStages; ++j) {
-        advance();
-        issue(j);
-    }
-    asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
-    __syncthreads();
-    bf16x8 a0[4], b0[4], a1[4], b1[4];
-    frags(0, 0, a0, b0);
-    int slot = 0;  // slot of step kt
-    for (int kt = 0; kt < KT; ++kt) {
-        const int next_slot = slot + 1 == kStages ? 0 : slot + 1;
-        advance();  // offsets of step kt + S
-        // k-step 0 of this K step: read k-step 1's fragments under 16 MFMAs
-        frags(slot, 1, a1, b1);
-        mfma_block<NV>(acc, a0, b0);
-        Interleave<4 * NV, 0, NV + 4>::run();
-        __builtin_amdgcn_sched_barrier(0);
-        // Every wave has read step kt and step kt+1 has landed: refill step
-        // kt's slot with step kt+S and read step kt+1's first fragments under
-        // the last 16 MFMAs.
-        asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)" ::: "memory");
-        __syncthreads();
-        issue(slot);
-        frags(next_slot, 0, a0, b0);  // a stale but in-bounds read after the last step
-        mfma_block<NV>(acc, a1, b1);
-        Interleave<4 * NV, 8, NV + 4>::run();
-        __builtin_amdgcn_sched_barrier(0);
-        slot = next_slot;
-    }
-}
-
-// Accumulator element 4q + s of fragment (i, j) of lane l sits in tile row
-// 64i + 32wm + l%32 (four-wave tile; 128i + 32wm + l%32 in the eight-wave
-// tile) and tile column wn*128 + 32j + 8q + 4(l/32) + s.
-
-// Row fragments of this wave holding any of the tile's first `valid` rows.
+// Row fragments of this wave holding any of the tile's first `valid` rows, in
+// the four-wave MXFP8 tile (fragment i of wave row wm: rows 64i + 32wm ..).
 __device__ __forceinline__ int valid_frags(int valid) {
     const int wm = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >> 1;
     const int n = (valid - 32 * wm + 63) / 64;
@@ -210,21 +76,11 @@ __device__ __forceinline__ int grouped_tiles(const int32_t* mt_start, int e_begi
 // Epilogue staging.  A 64-row block of the tile is written to LDS with row
 // pitches 16 bytes longer than the data (256, 512 or 1024 bytes), so the 32
 // rows of one write instruction fall on different banks, then copied out in
-// 16-byte chunks along rows.  In the four-wave tile, fragment i of every wave
-// covers tile rows 64i .. 64i+63 (row 64i + epi_row() for this lane).
+// 16-byte chunks along rows.
 constexpr int kEpiRows = 64;
 constexpr int kEpiPitch16 = 16 * 16 + 16;  // 16 chunks of data per row
 constexpr int kEpiPitch32 = 32 * 16 + 16;
 constexpr int kEpiPitch64 = 64 * 16 + 16;
-static_assert(kEpiRows * (kEpiPitch16 + 2 * kEpiPitch32) <= kStages * kStageBytes - 4,
-              "the staged SwiGLU block must fit the ring (the layer kernel keeps its last dword)");
-static_assert(kEpiRows * kEpiPitch64 <= kStages * kStageBytes, "the staged fp32 block must fit the ring");
-
-__device__ __forceinline__ int epi_row() {
-    const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) >> 1;
-    return wm * 32 + (lane & 31);
-}
-
 // Before the first staged block: the ring's trailing loads have landed and no
 // wave reads the ring any more.
 __device__ __forceinline__ void epi_begin() {
