@@ -18,6 +18,10 @@ constexpr int kMxStageSB = kMxStageSA + BM * 4;
 constexpr int kMxStageBytes = kMxStageSB + BN * 4;
 constexpr int kMxStages = 4;  // 136 KB
 constexpr int kMxLoads = 10;  // direct-to-LDS loads per lane per K step
+constexpr int kEpiPitch8 = 8 * 16 + 16;  // staged codes: 128 bytes of data per row
+static_assert(kEpiRows * (kEpiPitch8 + 2 * kEpiPitch32) <= kMxStages * kMxStageBytes - 4,
+              "the staged SwiGLU block must fit the ring (the layer kernel keeps its last dword)");
+static_assert(kEpiRows * kEpiPitch64 <= kMxStages * kMxStageBytes, "the staged fp32 block must fit the ring");
 
 __device__ __forceinline__ int mx_swz(int r) { return (r >> 2) & 3; }
 
@@ -101,13 +105,16 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
+    // B is the first operand (with its scales), so each accumulator holds the
+    // transposed block: element 4q + s of fragment (i, j) of lane l sits in
+    // tile row 64i + 32wm + l%32 and column wn*128 + 32j + 8q + 4(l/32) + s.
     auto mfmas = [&](const intx8 (&a)[4], const intx8 (&b)[4], const int (&sa)[4], const int (&sb)[4]) {
 #pragma unroll
         for (int i = 0; i < NV; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 0, 0, 0, sa[i], 0,
-                                                                             sb[j]);
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a[i], acc[i][j], 0, 0, 0, sb[j], 0,
+                                                                             sa[i]);
     };
 
     // Ring protocol as in the bf16 path, with 10 loads per K step and every
@@ -146,84 +153,93 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
     }
     if (kt < KT) step(kt, a0, b0, s0a, s0b, a1, b1, s1a, s1b);
 
+    // The tile leaves through LDS, 64 rows at a time (whole-line stores): block
+    // i (tile rows 64i .. 64i+63) is fragment i of every wave, this lane's row
+    // in it wm*32 + lane%32.  N is a multiple of 64, so a 4-column run, and a
+    // 16-byte chunk, lies wholly inside or outside the matrix.
+    epi_begin();
+    const int rl = wm * 32 + fr;
     if (EPI == kEpiSwiGLU) {
-        // h = silu(g) * u, then MXFP8 along I: the 32 columns of a block are
-        // lanes 0..31 (or 32..63) of one fragment row; routed rows only.
-        const int I = p.N / 2;
+        // h = silu(g) * u, then MXFP8 along I in 32-column blocks: a block of a
+        // row is lanes l and l+32 of one fragment (16 values each).  Routed
+        // and padding rows alike (the padding rows' codes are never read).
+        const int I = p.N / 2, hc0 = n0 / 2;
+        const bool live = hc0 + wn * 64 < I;  // I is a multiple of 64: both blocks of the pair alike
+        uint8_t* qb = smem;                                 // [64][128] codes
+        uint8_t* gb = smem + kEpiRows * kEpiPitch8;         // [64][128] fp32 g
+        uint8_t* ub = gb + kEpiRows * kEpiPitch32;          // [64][128] fp32 u
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int hcol = n0 / 2 + wn * 64 + jj * 32 + fr;
-            const int blk = (n0 / 2 + wn * 64 + jj * 32) / 32;
-            const bool live = n0 / 2 + wn * 64 + jj * 32 < I;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float g = acc[i][2 * jj][r], u = acc[i][2 * jj + 1][r];
-                    const float h = g / (1.0f + __expf(-g)) * u;
-                    float m = fabsf(h);
-                    m = fmaxf(m, __shfl_xor(m, 16, kWave));
-                    m = fmaxf(m, __shfl_xor(m, 8, kWave));
-                    m = fmaxf(m, __shfl_xor(m, 4, kWave));
-                    m = fmaxf(m, __shfl_xor(m, 2, kWave));
-                    m = fmaxf(m, __shfl_xor(m, 1, kWave));
-                    const int ex = mx_scale_exp(m);
-                    const int row = prow0 + i * 64 + wm * 32 + (r >> 2) * 8 + 4 * half + (r & 3);
-                    if (live) {
-                        const int q = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(h, -ex), 0.0f, 0, false);
-                        p.Cq[(int64_t)row * I + hcol] = (uint8_t)(q & 0xff);
-                        if (fr == 0) p.Cs[((int64_t)(blk >> 1) * p.cs_rows + row) * 4 + (blk & 1)] = (uint8_t)(ex + 127);
-                        if (fr == 0 && (blk & 1) == 0) {
-                            p.Cs[((int64_t)(blk >> 1) * p.cs_rows + row) * 4 + 2] = 0;
-                            p.Cs[((int64_t)(blk >> 1) * p.cs_rows + row) * 4 + 3] = 0;
-                        }
-                    }
-                }
-        }
-        if (p.GU) {  // g | u kept in fp32 for the backward
+        for (int i = 0; i < 4; ++i) {
+            uint32_t sdw = 0;
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
-                const int hcol = n0 / 2 + wn * 64 + jj * 32 + fr;
-                if (n0 / 2 + wn * 64 + jj * 32 < I) {
+                float g[16], u[16], h[16];
+                float m = 0.0f;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
+                for (int c = 0; c < 16; ++c) {
+                    g[c] = acc[i][2 * jj][c];
+                    u[c] = acc[i][2 * jj + 1][c];
+                    h[c] = swiglu(g[c], u[c]);
+                    m = fmaxf(m, fabsf(h[c]));
+                }
+                m = fmaxf(m, __shfl_xor(m, 32, kWave));
+                const int ex = mx_scale_exp(m);
+                sdw |= (uint32_t)(ex + 127) << (8 * jj);
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int row = prow0 + i * 64 + wm * 32 + (r >> 2) * 8 + 4 * half + (r & 3);
-                            float* dst = p.GU + (int64_t)row * p.N + hcol;
-                            dst[0] = acc[i][2 * jj][r];
-                            dst[I] = acc[i][2 * jj + 1][r];
-                        }
+                for (int q = 0; q < 4; ++q) {
+                    const int hc = wn * 64 + jj * 32 + q * 8 + 4 * half;
+                    *(uint32_t*)(qb + rl * kEpiPitch8 + hc) = fp8x4(ldexpf(h[4 * q], -ex), ldexpf(h[4 * q + 1], -ex),
+                                                                   ldexpf(h[4 * q + 2], -ex), ldexpf(h[4 * q + 3], -ex));
+                    if (p.GU) {
+                        *(floatx4*)(gb + rl * kEpiPitch32 + hc * 4) = floatx4{g[4 * q], g[4 * q + 1], g[4 * q + 2], g[4 * q + 3]};
+                        *(floatx4*)(ub + rl * kEpiPitch32 + hc * 4) = floatx4{u[4 * q], u[4 * q + 1], u[4 * q + 2], u[4 * q + 3]};
+                    }
                 }
             }
+            // the row's two block scales of this 64-column pair, as the GEMM
+            // operand layout's dword {block 0, block 1, 0, 0}; lanes 0..31 hold
+            // 32 consecutive rows, so the stores are one 128-byte run
+            const int64_t row = prow0 + i * 64 + rl;
+            if (live && half == 0) *(uint32_t*)(p.Cs + ((int64_t)((hc0 + wn * 64) >> 6) * p.cs_rows + row) * 4) = sdw;
+            __syncthreads();
+            const int64_t row0 = prow0 + i * 64;
+            const int lim = I - hc0;
+            epi_copy_out<8, kGemmThreads>(qb, kEpiPitch8, (char*)(p.Cq + row0 * I + hc0), (int64_t)I, lim);
+            if (p.GU) {
+                epi_copy_out<32, kGemmThreads>(gb, kEpiPitch32, (char*)(p.GU + row0 * p.N + hc0), (int64_t)p.N * 4,
+                                               lim * 4);
+                epi_copy_out<32, kGemmThreads>(ub, kEpiPitch32, (char*)(p.GU + row0 * p.N + I + hc0),
+                                               (int64_t)p.N * 4, lim * 4);
+            }
+            __syncthreads();
         }
     } else if (p.Cf) {  // fp32 output
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int col = n0 + wn * 128 + j * 32 + fr;
-            if (col < p.N) {
+        for (int i = 0; i < 4; ++i) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int row = prow0 + i * 64 + wm * 32 + (r >> 2) * 8 + 4 * half + (r & 3);
-                        p.Cf[(int64_t)row * p.ldc + col] = acc[i][j][r];
-                    }
-            }
+                for (int q = 0; q < 4; ++q)
+                    *(floatx4*)(smem + rl * kEpiPitch64 + frag_col(j, q) * 4) =
+                        floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            __syncthreads();
+            epi_copy_out<64, kGemmThreads>(smem, kEpiPitch64, (char*)(p.Cf + (int64_t)(prow0 + i * 64) * p.ldc + n0),
+                                           (int64_t)p.ldc * 4, (p.N - n0) * 4);
+            __syncthreads();
         }
     } else {  // bf16 output
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int col = n0 + wn * 128 + j * 32 + fr;
-            if (col < p.N) {
+        for (int i = 0; i < 4; ++i) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int row = prow0 + i * 64 + wm * 32 + (r >> 2) * 8 + 4 * half + (r & 3);
-                        p.C[(int64_t)row * p.ldc + col] = f32_to_bf16_rne(acc[i][j][r]);
-                    }
-            }
+                for (int q = 0; q < 4; ++q)
+                    *(uint2*)(smem + rl * kEpiPitch32 + frag_col(j, q) * 2) = pack_bf16x4(
+                        acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            __syncthreads();
+            epi_copy_out<32, kGemmThreads>(smem, kEpiPitch32, (char*)(p.C + (int64_t)(prow0 + i * 64) * p.ldc + n0),
+                                           (int64_t)p.ldc * 2, (p.N - n0) * 2);
+            __syncthreads();
         }
     }
 }
