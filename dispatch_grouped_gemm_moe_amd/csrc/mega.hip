@@ -189,16 +189,16 @@ __device__ void combine_range(const MegaArgs& a, int b, int c0, int c1, uint8_t*
     }
 }
 
-// Threads of the layer kernel: the MXFP8 tiles run four waves, the bf16
-// tiles eight (two per SIMD).
+// Threads of the layer kernel: the bf16 and MXFP8 tiles both run eight waves
+// (two per SIMD).
 template <bool kMx>
-constexpr int kMegaThreads = kMx ? kGemmThreads : kTileThreads;
+constexpr int kMegaThreads = kTileThreads;
 
 template <bool kMx>
 __global__ __attribute__((amdgpu_flat_work_group_size(kMegaThreads<kMx>, kMegaThreads<kMx>),
                           amdgpu_waves_per_eu(kMegaThreads<kMx> / 256, kMegaThreads<kMx> / 256)))
 void mega_kernel(MegaArgs a) {
-    constexpr int kSmem = kMx ? kMxStages * kMxStageBytes : kTileSmem;
+    constexpr int kSmem = kMx ? kMxSmem : kTileSmem;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
     // wait result broadcast: the ring's last dword, free between tiles (the
     // mainloop has drained its loads and every wave passed a barrier)

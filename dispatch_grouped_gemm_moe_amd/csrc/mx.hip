@@ -84,9 +84,9 @@ void launch_mx_quant(const uint16_t* src, int64_t rows, int cols, int layout, ui
 // ---------------------------------------------------------------------------
 
 template <int EPI>
-__global__ __attribute__((amdgpu_flat_work_group_size(kGemmThreads, kGemmThreads), amdgpu_waves_per_eu(1, 1)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kTileThreads, kTileThreads), amdgpu_waves_per_eu(2, 2)))
 void mx_gemm_kernel(MxGemmArgs p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[kMxStages * kMxStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kMxSmem];
     const int NT = ceil_div(p.N, BN);
     const int total = grouped_tiles(p.mt_start, p.e_begin, p.e_end, p.N);
     const int G = gridDim.x, per = G >> 3;
@@ -102,9 +102,9 @@ void mx_gemm_kernel(MxGemmArgs p) {
 
 void launch_mx_gemm(const MxGemmArgs& a, GemmEpilogue epi, int grid, hipStream_t stream) {
     if (epi == kEpiSwiGLU)
-        hipLaunchKernelGGL(mx_gemm_kernel<kEpiSwiGLU>, dim3(grid), dim3(kGemmThreads), 0, stream, a);
+        hipLaunchKernelGGL(mx_gemm_kernel<kEpiSwiGLU>, dim3(grid), dim3(kTileThreads), 0, stream, a);
     else
-        hipLaunchKernelGGL(mx_gemm_kernel<kEpiStore>, dim3(grid), dim3(kGemmThreads), 0, stream, a);
+        hipLaunchKernelGGL(mx_gemm_kernel<kEpiStore>, dim3(grid), dim3(kTileThreads), 0, stream, a);
 }
 
 }  // namespace moe

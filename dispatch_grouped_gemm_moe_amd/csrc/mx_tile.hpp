@@ -9,106 +9,123 @@
 
 namespace moe {
 
-// LDS stage: A codes [256][64 B], B codes [256][64 B], A scales [256][4 B],
-// B scales [256][4 B].  Code rows use the bf16 path's conflict-free swizzle.
-constexpr int kMxRow = 64;
-constexpr int kMxStageA = BM * kMxRow;
-constexpr int kMxStageSA = (BM + BN) * kMxRow;
-constexpr int kMxStageSB = kMxStageSA + BM * 4;
-constexpr int kMxStageBytes = kMxStageSB + BN * 4;
-constexpr int kMxStages = 4;  // 136 KB
-constexpr int kMxLoads = 10;  // direct-to-LDS loads per lane per K step
+// Eight-wave MXFP8 tile: 256 x 256 output per workgroup of 512 threads, two
+// waves per SIMD, each wave a 64 x 128 block of 2 x 4 fragments of
+// v_mfma_scale_f32_32x32x64_f8f6f4 (as the bf16 tile).  A stage holds two
+// 64-deep K steps: A and B codes as 128-byte rows (whole-line loads, 8 lanes
+// per row), then the E8M0 scale dwords of both K steps for A and for B;
+// two stages (136 KB).  An odd number of K steps ends on a half stage whose
+// second K step repeats the last one in LDS and gets no MFMAs.
+constexpr int kMxRow = 128;                               // code bytes of a row per stage
+constexpr int kMxStageA = BM * kMxRow;                    // 32 KB
+constexpr int kMxStageSA = (BM + BN) * kMxRow;            // scales: [2 K steps][256 rows] dwords
+constexpr int kMxStageSB = kMxStageSA + 2 * BM * 4;
+constexpr int kMxStageBytes = kMxStageSB + 2 * BN * 4;    // 68 KB
+constexpr int kMxStages = 2;
+constexpr int kMxSmem = kMxStages * kMxStageBytes;
 constexpr int kEpiPitch8 = 8 * 16 + 16;  // staged codes: 128 bytes of data per row
-static_assert(kEpiRows * (kEpiPitch8 + 2 * kEpiPitch32) <= kMxStages * kMxStageBytes - 4,
+static_assert(kEpiRows * (kEpiPitch8 + 2 * kEpiPitch32) <= kMxSmem - 4,
               "the staged SwiGLU block must fit the ring (the layer kernel keeps its last dword)");
-static_assert(kEpiRows * kEpiPitch64 <= kMxStages * kMxStageBytes, "the staged fp32 block must fit the ring");
-
-__device__ __forceinline__ int mx_swz(int r) { return (r >> 2) & 3; }
-
+static_assert(kEpiRows * kEpiPitch64 <= kMxSmem, "the staged fp32 block must fit the ring");
 
 // One 256 x 256 output tile (expert e, M tile ml of the expert, N tile ntile)
-// of the MXFP8 grouped GEMM with its epilogue; smem is the kMxStages LDS ring.
-// Row fragments as in the bf16 tile: fragment i of wave (wm, wn) holds tile
-// rows 64i + 32wm .. +31, and only the first NV of them (those holding a valid
-// row of the expert's last tile) get MFMAs and fragment reads.
+// of the MXFP8 grouped GEMM with its epilogue, by 512 threads; smem is the
+// kMxSmem LDS ring.  Wave w (wm = w/2, wn = w%2) owns fragments i = 0, 1 at
+// tile rows 128i + 32wm .. +31 and j = 0..3 at columns 128wn + 32j .. +31;
+// only the first NV row fragments (those holding a valid row of the expert's
+// last tile) get MFMAs and fragment reads.
 template <int EPI, int NV>
 __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, int ntile, uint8_t* smem) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar LDS bases
     const int wm = wave >> 1, wn = wave & 1;
-    const int KT = p.K / 64;
+    const int KT = p.K / 64, KS = (KT + 1) / 2;
     const int mt0 = p.mt_start[e];
     const int prow0 = (mt0 + ml) * BM;
     const int n0 = ntile * BN;
 
-    // per-lane staging: code rows wave*64 + 16i + lane/4 (swizzled chunk),
-    // scale row wave*64 + lane (one dword per row and K step)
+    // Code loads: instruction i fills tile rows 32*wave + 8i .. +7 (lane/8 the
+    // row, lane%8 the fixed LDS chunk, loading the logical chunk stored there;
+    // chunks 4..7 hold the stage's second K step).  Scale loads: lane L =
+    // 64*wave + lane takes K step L/256 of row L%256, one dword for A, one for B.
     const char* a_base = (const char*)p.A;
     const char* b_base = (const char*)(p.B + (int64_t)e * p.b_stride);
-    const char* sa_base = (const char*)p.SA;
-    const char* sb_base = (const char*)(p.SB + (int64_t)e * p.sb_stride);
     uint32_t aoff[4], boff[4];
+    int himask = 0;  // bit i: this lane's chunk of instruction i belongs to the stage's second K step
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int r = wave * 64 + i * 16 + (lane >> 2);
-        const int lchunk = (lane & 3) ^ mx_swz(r);
+        const int r = wave * 32 + i * 8 + (lane >> 3);
+        const int lchunk = (lane & 7) ^ swz8(r);
+        himask |= (lchunk >> 2) << i;
         const int prow = prow0 + r;
         const int arow = p.a_row_map ? p.a_row_map[prow] : prow;
         aoff[i] = (uint32_t)((int64_t)arow * p.lda + lchunk * 16);
         boff[i] = (uint32_t)((int64_t)min(n0 + r, p.N - 1) * p.K + lchunk * 16);
     }
-    const int srow = wave * 64 + lane;
+    const int sl = wave * 64 + lane, sks = sl >> 8, srow = sl & 255;
     const int sarow = p.a_row_map ? p.a_row_map[prow0 + srow] : prow0 + srow;
-    const uint32_t saoff = (uint32_t)sarow * 4, sboff = (uint32_t)min(n0 + srow, p.N - 1) * 4;
+    const char* sa_lane = (const char*)p.SA + (int64_t)sarow * 4;
+    const char* sb_lane = (const char*)(p.SB + (int64_t)e * p.sb_stride) + (int64_t)min(n0 + srow, p.N - 1) * 4;
 
-    // Loads past the last K step repeat it (into the slot of a step every wave
-    // has finished with), so they need no branch and the waits are constants.
-    auto issue = [&](int kt_, int slot) {
-        const int kt = kt_ < KT ? kt_ : KT - 1;
+    // Loads past the last stage repeat it (into the slot no wave reads any
+    // more), so they need no branch and the waits are constants.  On a half
+    // stage (odd K steps) the second K step's code chunks and scales repeat
+    // the first's.
+    auto issue = [&](int s_, int slot) {
+        const int s = s_ < KS ? s_ : KS - 1;
+        // a half stage's second K step repeats the first: the lanes of the
+        // upper chunks step back 64 bytes
+        const int back = 2 * s + 1 >= KT ? himask : 0;
+        const uint32_t kb = (uint32_t)s * 128;
+        const int kts = min(2 * s + sks, KT - 1);
         uint8_t* st = smem + slot * kMxStageBytes;
-        uint8_t* base = st + (wave * 64) * kMxRow;
-        const uint32_t kb = (uint32_t)kt * 64;
+        uint8_t* base = st + (wave * 32) * kMxRow;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_global_load_lds((gbl_cvoid*)(a_base + aoff[i] + kb), (lds_void*)(base + i * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((gbl_cvoid*)(a_base + aoff[i] + kb - ((back >> i) & 1) * 64),
+                                             (lds_void*)(base + i * 1024), 16, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_global_load_lds((gbl_cvoid*)(b_base + boff[i] + kb), (lds_void*)(base + kMxStageA + i * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((gbl_cvoid*)(sa_base + (int64_t)kt * p.sa_kstride + saoff),
+            __builtin_amdgcn_global_load_lds((gbl_cvoid*)(b_base + boff[i] + kb - ((back >> i) & 1) * 64),
+                                             (lds_void*)(base + kMxStageA + i * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gbl_cvoid*)(sa_lane + (int64_t)kts * p.sa_kstride),
                                          (lds_void*)(st + kMxStageSA + wave * 256), 4, 0, 0);
-        __builtin_amdgcn_global_load_lds((gbl_cvoid*)(sb_base + (int64_t)kt * p.sb_kstride + sboff),
+        __builtin_amdgcn_global_load_lds((gbl_cvoid*)(sb_lane + (int64_t)kts * p.sb_kstride),
                                          (lds_void*)(st + kMxStageSB + wave * 256), 4, 0, 0);
     };
     const int fr = lane & 31, half = lane >> 5;
-    const int fsw = mx_swz(fr);
-    const int pc0 = (half ^ fsw) * 16, pc1 = ((2 + half) ^ fsw) * 16;
+    const int fsw = swz8(fr);  // a fragment's rows differ from fr by multiples of 32
     const int arow_b = (wm * 32 + fr) * kMxRow, brow_b = kMxStageA + (wn * 128 + fr) * kMxRow;
-    auto frags = [&](int slot, intx8 (&a)[4], intx8 (&b)[4], int (&sa)[4], int (&sb)[4]) {
+    // fragments of K step ks (0, 1) of the stage in `slot`: per lane, bytes
+    // 0..15 from the row's first 32-block of the K step, 16..31 from its second;
+    // the scale of (row, block) from byte `half` of the row's scale dword
+    auto frags = [&](int slot, int ks, intx8 (&a)[2], intx8 (&b)[4], int (&sa)[2], int (&sb)[4]) {
         const uint8_t* st = smem + slot * kMxStageBytes;
+        const int pc0 = ((4 * ks + half) ^ fsw) * 16, pc1 = ((4 * ks + 2 + half) ^ fsw) * 16;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const intx4 lo4 = *(const intx4*)(st + arow_b + i * 64 * kMxRow + pc0);
-            const intx4 hi4 = *(const intx4*)(st + arow_b + i * 64 * kMxRow + pc1);
+            const intx4 lo4 = *(const intx4*)(st + arow_b + i * 128 * kMxRow + pc0);
+            const intx4 hi4 = *(const intx4*)(st + arow_b + i * 128 * kMxRow + pc1);
             a[i] = intx8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-            sa[i] = st[kMxStageSA + (i * 64 + wm * 32 + fr) * 4 + half];
+            sa[i] = st[kMxStageSA + ks * 1024 + (i * 128 + wm * 32 + fr) * 4 + half];
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const intx4 lo4 = *(const intx4*)(st + brow_b + j * 32 * kMxRow + pc0);
             const intx4 hi4 = *(const intx4*)(st + brow_b + j * 32 * kMxRow + pc1);
             b[j] = intx8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-            sb[j] = st[kMxStageSB + (wn * 128 + j * 32 + fr) * 4 + half];
+            sb[j] = st[kMxStageSB + ks * 1024 + (wn * 128 + j * 32 + fr) * 4 + half];
         }
     };
-    floatx16 acc[4][4];
+    floatx16 acc[2][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
     // B is the first operand (with its scales), so each accumulator holds the
     // transposed block: element 4q + s of fragment (i, j) of lane l sits in
-    // tile row 64i + 32wm + l%32 and column wn*128 + 32j + 8q + 4(l/32) + s.
-    auto mfmas = [&](const intx8 (&a)[4], const intx8 (&b)[4], const int (&sa)[4], const int (&sb)[4]) {
+    // tile row 128i + 32wm + l%32 and column wn*128 + 32j + 8q + 4(l/32) + s.
+    auto mfmas = [&](const intx8 (&a)[2], const intx8 (&b)[4], const int (&sa)[2], const int (&sb)[4]) {
 #pragma unroll
         for (int i = 0; i < NV; ++i)
 #pragma unroll
@@ -117,48 +134,45 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
                                                                              sa[i]);
     };
 
-    // Ring protocol as in the bf16 path, with 10 loads per K step and every
-    // slot always in flight: before computing step kt, wait until step kt+1
-    // has landed (the 2 newer steps stay in flight: vmcnt(20)) and this wave's
-    // reads of step kt are done, barrier, refill step kt's slot with step
-    // kt + kMxStages, and read step kt+1's fragments under step kt's MFMAs.
-    static_assert(kMxStages == 4, "the vmcnt immediates below assume 4 stages of 10 loads");
+    // Ring protocol (stage j in slot j % 2, 10 direct-to-LDS loads per lane and
+    // stage): the prologue issues stages 0 and 1 and waits for stage 0
+    // (vmcnt(10)); stage s reads and runs its first K step, reads the second's
+    // fragments, waits for stage s+1 (vmcnt(0)) and its own LDS reads,
+    // barrier, refills its slot with stage s+2 under the second K step's
+    // MFMAs.  Fragments are single-buffered (the scaled operands are twice the
+    // bf16 ones and two waves share a SIMD's registers): a wave waiting on its
+    // reads leaves the matrix core to the SIMD's other wave.
+    static_assert(kMxStages == 2, "the vmcnt immediates below assume 2 stages of 10 loads");
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < kMxStages; ++j) issue(j, j);
-    asm volatile("s_waitcnt vmcnt(30)" ::: "memory");
+    issue(0, 0);
+    issue(1, 1);
+    asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
     __syncthreads();
-    intx8 a0[4], b0[4], a1[4], b1[4];
-    int s0a[4], s0b[4], s1a[4], s1b[4];
-    frags(0, a0, b0, s0a, s0b);
-    int slot = 0;  // slot of step kt
-    auto step = [&](int kt, intx8 (&ac)[4], intx8 (&bc)[4], int (&sac)[4], int (&sbc)[4], intx8 (&an)[4],
-                    intx8 (&bn)[4], int (&san)[4], int (&sbn)[4]) {
-        const int next_slot = slot + 1 == kMxStages ? 0 : slot + 1;
-        asm volatile("s_waitcnt vmcnt(20) lgkmcnt(0)" ::: "memory");
-        __syncthreads();
-        issue(kt + kMxStages, slot);
-        frags(next_slot, an, bn, san, sbn);  // stale but in-bounds on the last step
-        mfmas(ac, bc, sac, sbc);
-        // 4NV MFMAs, 10 loads, 3 LDS reads per fragment (two code halves, one scale)
-        Interleave<4 * NV, 10, 3 * (NV + 4)>::run();
+    intx8 fa[2], fb[4];
+    int fsa[2], fsb[4];
+    int slot = 0;
+    for (int s = 0; s < KS; ++s) {
+        frags(slot, 0, fa, fb, fsa, fsb);
+        mfmas(fa, fb, fsa, fsb);
         __builtin_amdgcn_sched_barrier(0);
-        slot = next_slot;
-    };
-    int kt = 0;
-    for (; kt + 1 < KT; kt += 2) {
-        step(kt, a0, b0, s0a, s0b, a1, b1, s1a, s1b);
-        step(kt + 1, a1, b1, s1a, s1b, a0, b0, s0a, s0b);
+        frags(slot, 1, fa, fb, fsa, fsb);
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __syncthreads();
+        issue(s + 2, slot);
+        if (2 * s + 1 < KT) mfmas(fa, fb, fsa, fsb);
+        Interleave<4 * NV, 10, 0>::run();
+        __builtin_amdgcn_sched_barrier(0);
+        slot ^= 1;
     }
-    if (kt < KT) step(kt, a0, b0, s0a, s0b, a1, b1, s1a, s1b);
 
-    // The tile leaves through LDS, 64 rows at a time (whole-line stores): block
-    // i (tile rows 64i .. 64i+63) is fragment i of every wave, this lane's row
-    // in it wm*32 + lane%32.  N is a multiple of 64, so a 4-column run, and a
-    // 16-byte chunk, lies wholly inside or outside the matrix.
+    // The tile leaves through LDS, 64 rows at a time (whole-line stores).
+    // Block b (tile rows 64b .. 64b+63) is fragment b/2 of the waves with
+    // wm/2 == b%2, this lane's row in it (wm%2)*32 + lane%32.  N is a multiple
+    // of 64, so a 4-column run, and a 16-byte chunk, lies wholly inside or
+    // outside the matrix.
     epi_begin();
-    const int rl = wm * 32 + fr;
+    const int rl = (wm & 1) * 32 + fr;
     if (EPI == kEpiSwiGLU) {
         // h = silu(g) * u, then MXFP8 along I in 32-column blocks: a block of a
         // row is lanes l and l+32 of one fragment (16 values each).  Routed
@@ -169,81 +183,93 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
         uint8_t* gb = smem + kEpiRows * kEpiPitch8;         // [64][128] fp32 g
         uint8_t* ub = gb + kEpiRows * kEpiPitch32;          // [64][128] fp32 u
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t sdw = 0;
+        for (int bl = 0; bl < 4; ++bl) {
+            if ((wm >> 1) == (bl & 1)) {
+                const int i = bl >> 1;
+                uint32_t sdw = 0;
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-                float g[16], u[16], h[16];
-                float m = 0.0f;
+                for (int jj = 0; jj < 2; ++jj) {
+                    float g[16], u[16], h[16];
+                    float m = 0.0f;
 #pragma unroll
-                for (int c = 0; c < 16; ++c) {
-                    g[c] = acc[i][2 * jj][c];
-                    u[c] = acc[i][2 * jj + 1][c];
-                    h[c] = swiglu(g[c], u[c]);
-                    m = fmaxf(m, fabsf(h[c]));
-                }
-                m = fmaxf(m, __shfl_xor(m, 32, kWave));
-                const int ex = mx_scale_exp(m);
-                sdw |= (uint32_t)(ex + 127) << (8 * jj);
+                    for (int c = 0; c < 16; ++c) {
+                        g[c] = acc[i][2 * jj][c];
+                        u[c] = acc[i][2 * jj + 1][c];
+                        h[c] = swiglu(g[c], u[c]);
+                        m = fmaxf(m, fabsf(h[c]));
+                    }
+                    m = fmaxf(m, __shfl_xor(m, 32, kWave));
+                    const int ex = mx_scale_exp(m);
+                    sdw |= (uint32_t)(ex + 127) << (8 * jj);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int hc = wn * 64 + jj * 32 + q * 8 + 4 * half;
-                    *(uint32_t*)(qb + rl * kEpiPitch8 + hc) = fp8x4(ldexpf(h[4 * q], -ex), ldexpf(h[4 * q + 1], -ex),
-                                                                   ldexpf(h[4 * q + 2], -ex), ldexpf(h[4 * q + 3], -ex));
-                    if (p.GU) {
-                        *(floatx4*)(gb + rl * kEpiPitch32 + hc * 4) = floatx4{g[4 * q], g[4 * q + 1], g[4 * q + 2], g[4 * q + 3]};
-                        *(floatx4*)(ub + rl * kEpiPitch32 + hc * 4) = floatx4{u[4 * q], u[4 * q + 1], u[4 * q + 2], u[4 * q + 3]};
+                    for (int q = 0; q < 4; ++q) {
+                        const int hc = wn * 64 + jj * 32 + q * 8 + 4 * half;
+                        *(uint32_t*)(qb + rl * kEpiPitch8 + hc) =
+                            fp8x4(ldexpf(h[4 * q], -ex), ldexpf(h[4 * q + 1], -ex), ldexpf(h[4 * q + 2], -ex),
+                                  ldexpf(h[4 * q + 3], -ex));
+                        if (p.GU) {
+                            *(floatx4*)(gb + rl * kEpiPitch32 + hc * 4) =
+                                floatx4{g[4 * q], g[4 * q + 1], g[4 * q + 2], g[4 * q + 3]};
+                            *(floatx4*)(ub + rl * kEpiPitch32 + hc * 4) =
+                                floatx4{u[4 * q], u[4 * q + 1], u[4 * q + 2], u[4 * q + 3]};
+                        }
                     }
                 }
+                // the row's two block scales of this 64-column pair, as the GEMM
+                // operand layout's dword {block 0, block 1, 0, 0}; lanes 0..31
+                // hold 32 consecutive rows, so the stores are one 128-byte run
+                const int64_t row = prow0 + bl * 64 + rl;
+                if (live && half == 0)
+                    *(uint32_t*)(p.Cs + ((int64_t)((hc0 + wn * 64) >> 6) * p.cs_rows + row) * 4) = sdw;
             }
-            // the row's two block scales of this 64-column pair, as the GEMM
-            // operand layout's dword {block 0, block 1, 0, 0}; lanes 0..31 hold
-            // 32 consecutive rows, so the stores are one 128-byte run
-            const int64_t row = prow0 + i * 64 + rl;
-            if (live && half == 0) *(uint32_t*)(p.Cs + ((int64_t)((hc0 + wn * 64) >> 6) * p.cs_rows + row) * 4) = sdw;
             __syncthreads();
-            const int64_t row0 = prow0 + i * 64;
+            const int64_t row0 = prow0 + bl * 64;
             const int lim = I - hc0;
-            epi_copy_out<8, kGemmThreads>(qb, kEpiPitch8, (char*)(p.Cq + row0 * I + hc0), (int64_t)I, lim);
+            epi_copy_out<8, kTileThreads>(qb, kEpiPitch8, (char*)(p.Cq + row0 * I + hc0), (int64_t)I, lim);
             if (p.GU) {
-                epi_copy_out<32, kGemmThreads>(gb, kEpiPitch32, (char*)(p.GU + row0 * p.N + hc0), (int64_t)p.N * 4,
+                epi_copy_out<32, kTileThreads>(gb, kEpiPitch32, (char*)(p.GU + row0 * p.N + hc0), (int64_t)p.N * 4,
                                                lim * 4);
-                epi_copy_out<32, kGemmThreads>(ub, kEpiPitch32, (char*)(p.GU + row0 * p.N + I + hc0),
+                epi_copy_out<32, kTileThreads>(ub, kEpiPitch32, (char*)(p.GU + row0 * p.N + I + hc0),
                                                (int64_t)p.N * 4, lim * 4);
             }
             __syncthreads();
         }
     } else if (p.Cf) {  // fp32 output
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int bl = 0; bl < 4; ++bl) {
+            if ((wm >> 1) == (bl & 1)) {
+                const int i = bl >> 1;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *(floatx4*)(smem + rl * kEpiPitch64 + frag_col(j, q) * 4) =
-                        floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                    for (int q = 0; q < 4; ++q)
+                        *(floatx4*)(smem + rl * kEpiPitch64 + frag_col(j, q) * 4) =
+                            floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            }
             __syncthreads();
-            epi_copy_out<64, kGemmThreads>(smem, kEpiPitch64, (char*)(p.Cf + (int64_t)(prow0 + i * 64) * p.ldc + n0),
+            epi_copy_out<64, kTileThreads>(smem, kEpiPitch64, (char*)(p.Cf + (int64_t)(prow0 + bl * 64) * p.ldc + n0),
                                            (int64_t)p.ldc * 4, (p.N - n0) * 4);
             __syncthreads();
         }
     } else {  // bf16 output
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int bl = 0; bl < 4; ++bl) {
+            if ((wm >> 1) == (bl & 1)) {
+                const int i = bl >> 1;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *(uint2*)(smem + rl * kEpiPitch32 + frag_col(j, q) * 2) = pack_bf16x4(
-                        acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                    for (int q = 0; q < 4; ++q)
+                        *(uint2*)(smem + rl * kEpiPitch32 + frag_col(j, q) * 2) = pack_bf16x4(
+                            acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+            }
             __syncthreads();
-            epi_copy_out<32, kGemmThreads>(smem, kEpiPitch32, (char*)(p.C + (int64_t)(prow0 + i * 64) * p.ldc + n0),
+            epi_copy_out<32, kTileThreads>(smem, kEpiPitch32, (char*)(p.C + (int64_t)(prow0 + bl * 64) * p.ldc + n0),
                                            (int64_t)p.ldc * 2, (p.N - n0) * 2);
             __syncthreads();
         }
     }
 }
-
 
 // One 256 x 256 output tile (expert e, M tile ml, N tile ntile) of the MXFP8
 // grouped GEMM; with p.rows_e and kSkipPadding the padding fragments of an
@@ -251,12 +277,13 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
 template <int EPI, bool kSkipPadding = true>
 __device__ __forceinline__ void mx_gemm_tile(const MxGemmArgs p, int e, int ml, int ntile, uint8_t* smem) {
     if (!kSkipPadding || !p.rows_e) {
-        mx_tile_body<EPI, 4>(p, e, ml, ntile, smem);
+        mx_tile_body<EPI, 2>(p, e, ml, ntile, smem);
         return;
     }
-    switch (valid_frags(p.rows_e[e] - ml * BM)) {
-        case 4: mx_tile_body<EPI, 4>(p, e, ml, ntile, smem); break;
-        case 3: mx_tile_body<EPI, 3>(p, e, ml, ntile, smem); break;
+    // fragment i of this wave holds tile rows 128i + 32wm .. +31
+    const int valid = p.rows_e[e] - ml * BM;
+    const int w32 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 7) * 32;
+    switch (valid > 128 + w32 ? 2 : (valid > w32 ? 1 : 0)) {
         case 2: mx_tile_body<EPI, 2>(p, e, ml, ntile, smem); break;
         case 1: mx_tile_body<EPI, 1>(p, e, ml, ntile, smem); break;
         default: mx_tile_body<EPI, 0>(p, e, ml, ntile, smem); break;
