@@ -46,6 +46,11 @@ def main():
                     help="forward as one launch per grouped GEMM instead of the persistent layer kernel")
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-cache", action="store_true",
+                    help="write a 512 MiB scratch buffer before every timed step (more than the 256 MB "
+                         "Infinity Cache) and time each step alone with HIP events on the stream")
+    ap.add_argument("--copy-bandwidth-mib", type=int, default=0,
+                    help="first time a plain copy of this many MiB and log its HBM bandwidth")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run one plain elementwise copy (negation) of this many MiB, "
                          "the yardstick for HBM byte counters")
@@ -75,6 +80,21 @@ def main():
     if args.minibatch is not None:
         w = w.replace(minibatch=args.minibatch)
     log("workload", w)
+    if args.copy_bandwidth_mib:
+        # a plain elementwise copy, timed (4 repetitions after one warm-up): the
+        # HBM bandwidth a streaming kernel reaches on this machine (read + write)
+        a = torch.ones(args.copy_bandwidth_mib << 19, dtype=torch.bfloat16, device="cuda")
+        b = torch.empty_like(a)
+        torch.neg(a, out=b)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(4):
+            torch.neg(a, out=b)
+        e1.record()
+        torch.cuda.synchronize()
+        log("copy of %d MiB: %.2f TB/s (read + write)" % (
+            args.copy_bandwidth_mib, 4 * 2 * a.numel() * 2 / (e0.elapsed_time(e1) / 1e3) / 1e12))
+        del a, b
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 19  # bf16 elements
         a = torch.ones(n, dtype=torch.bfloat16, device="cuda")
@@ -124,11 +144,26 @@ def main():
     torch.cuda.synchronize()
     moe.moe_timing_enable(True)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    if args.cold_cache:
+        # the scratch writes stay outside the timed events (and outside the
+        # per-kernel timing, which only sees the library's launches)
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for i in range(args.steps):
+            scratch.fill_(i & 0xff)
+            evs[i][0].record()
+            step()
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        elapsed = sum(a.elapsed_time(b) for a, b in evs) / 1e3
+        del scratch
+    else:
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
     kt = moe.moe_timing_read()
     moe.moe_timing_enable(False)
 
@@ -189,7 +224,8 @@ def main():
                    "router_bias": w.router_bias, "shared_expert": w.shared_expert,
                    "ring_slots": sizes.ring_slots, "comm_cus": sizes.comm_cus,
                    "forward": "per-GEMM launches" if kt["layer"][1] == 0 else "persistent layer kernel",
-                   "pass": "forward+backward" if bwd else "forward"},
+                   "pass": "forward+backward" if bwd else "forward",
+                   "cache": "cold: 512 MiB written before each step" if args.cold_cache else "warm"},
         "roofline": {"bound": "mfma", "kernel": "moe::" + dom, "roles": dom_roles,
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic_for(dom, w.name),
