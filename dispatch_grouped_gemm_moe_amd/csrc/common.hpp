@@ -14,13 +14,11 @@ typedef int intx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
-// Grouped-GEMM tile: 256 x 256 output per workgroup, 64-deep K steps, four
-// waves in a 2 x 2 arrangement, each wave owning a 128 x 128 sub-tile made of
-// 4 x 4 MFMA 32x32x16 fragments.
+// Grouped-GEMM tile: 256 x 256 output per workgroup of eight waves (two per
+// SIMD), each wave owning a 64 x 128 block of 2 x 4 MFMA 32x32 fragments;
+// the tile kernels are in gemm_tile.hpp (bf16) and mx_tile.hpp (MXFP8).
 constexpr int BM = 256;
 constexpr int BN = 256;
-constexpr int BK = 64;
-constexpr int kGemmThreads = 256;
 
 // The gate/up weights are packed so that every 64 output columns of the
 // first GEMM hold 32 gate columns followed by the 32 up columns with the same

@@ -23,15 +23,8 @@ struct Interleave {
 // transposed 32 x 32 block: accumulator element 4q + s of fragment (i, j) of
 // lane l sits in tile row 128i + 32wm + l%32 and tile column
 // wn*128 + 32j + 8q + 4(l/32) + s -- one tile row, runs of four consecutive
-// columns, which the epilogues stage 8 or 16 bytes at a time.
-
-// Row fragments of this wave holding any of the tile's first `valid` rows, in
-// the four-wave MXFP8 tile (fragment i of wave row wm: rows 64i + 32wm ..).
-__device__ __forceinline__ int valid_frags(int valid) {
-    const int wm = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >> 1;
-    const int n = (valid - 32 * wm + 63) / 64;
-    return n < 0 ? 0 : (n > 4 ? 4 : n);
-}
+// columns, which the epilogues stage 8 or 16 bytes at a time.  frag_col(j, q):
+// the tile column of this lane's run q of fragment j.
 __device__ __forceinline__ int frag_col(int j, int q) {
     const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
     return wn * 128 + j * 32 + q * 8 + 4 * (lane >> 5);
