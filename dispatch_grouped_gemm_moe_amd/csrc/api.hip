@@ -108,10 +108,9 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     p->slots -= p->slots % p->group;
     p->comm_cus = c->comm_cus > 0 ? c->comm_cus : kCommWorkers;  // dedicated combine workgroups
     // The layer kernel's tile sequence runs gate|up(b+1) before down(b), so a
-    // ring of one slot would make gate|up(b+1) wait on a later tile.  MXFP8
-    // with the bf16 shared expert and identity experts take the per-GEMM path.
-    p->mega = !(c->flags & MOE_F_LAUNCH_PER_GEMM) && !p->identity && !(p->mx && p->shared) &&
-              p->comm_cus < kNumCUs - 8;
+    // ring of one slot would make gate|up(b+1) wait on a later tile.  Identity
+    // experts take the per-GEMM path.
+    p->mega = !(c->flags & MOE_F_LAUNCH_PER_GEMM) && !p->identity && p->comm_cus < kNumCUs - 8;
     p->ld_tok_prow = c->k + (p->shared ? 1 : 0);
     const int64_t rows = (int64_t)p->Mb * p->ld_tok_prow;
     // sum over experts of ceil(c_e / BM) <= ceil(rows / BM) + Et - 1
@@ -425,7 +424,7 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
     if (p.mega && ring_ok && ncu >= p.comm_cus + 16) {
         MegaArgs a{};
         a.T = p.T; a.H = p.H; a.I = p.I; a.k = p.k; a.Mb = p.Mb; a.nmb = p.nmb; a.S = p.slots;
-        a.comm = p.comm_cus; a.e_end = p.mx ? p.E : p.Et; a.with_shared = p.shared ? 1 : 0;
+        a.comm = p.comm_cus; a.e_end = p.Et; a.e_mx = p.mx ? p.E : 0; a.with_shared = p.shared ? 1 : 0;
         a.ld_tok_prow = p.ld_tok_prow; a.mx = p.mx ? 1 : 0; a.group = p.group;
         a.lay0 = lay0; a.lay_bytes = p.lay_bytes; a.ly_prow_token = p.ly_prow_token; a.ly_tok_prow = p.ly_tok_prow;
         a.mt_all = mt_all; a.rows_all = rows_all; a.mt_ld = p.Et + 1;

@@ -109,6 +109,7 @@ void launch_mx_quant(const uint16_t* src, int64_t rows, int cols, int layout, ui
 // 1 ring slot (combine), 2 combine input, 3 down input.
 struct MegaArgs {
     int T, H, I, k, Mb, nmb, S, comm, e_end, with_shared, ld_tok_prow, mx;
+    int e_mx;  // experts [0, e_mx) run MXFP8 tiles (m1/m2), the rest (the shared expert) bf16 (g1/g2)
     int group;  // minibatches per GEMM / combine phase; S is a multiple of it
     const uint8_t* lay0;
     int64_t lay_bytes, ly_prow_token, ly_tok_prow;

@@ -198,7 +198,7 @@ template <bool kMx>
 __global__ __attribute__((amdgpu_flat_work_group_size(kMegaThreads<kMx>, kMegaThreads<kMx>),
                           amdgpu_waves_per_eu(kMegaThreads<kMx> / 256, kMegaThreads<kMx> / 256)))
 void mega_kernel(MegaArgs a) {
-    constexpr int kSmem = kMx ? kMxSmem : kTileSmem;
+    constexpr int kSmem = kMx ? (kMxSmem > kTileSmem ? kMxSmem : kTileSmem) : kTileSmem;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
     // wait result broadcast: the ring's last dword, free between tiles (the
     // mainloop has drained its loads and every wave passed a barrier)
@@ -291,8 +291,12 @@ void mega_kernel(MegaArgs a) {
         uint8_t* slot = a.slot0 + (int64_t)(b % a.S) * a.slot_bytes;
         uint8_t* svb = a.saved_mb0 ? a.saved_mb0 + (int64_t)b * a.sv_mb : nullptr;
         uint16_t* Y = svb ? (uint16_t*)(svb + a.sv_y) : (uint16_t*)(slot + a.sl_y);
+        // MXFP8 routed experts run scaled-MFMA tiles; bf16 experts (every
+        // expert of a bf16 layer, the shared expert of an MXFP8 one) bf16 tiles.
+        // Under MXFP8 the saved g|u is fp32 for both.
+        const bool mx_tile = kMx && e < a.e_mx;
         if (kind == kGateUp) {
-            if constexpr (kMx) {
+            if (mx_tile) {
                 MxGemmArgs m = a.m1;
                 m.a_row_map = (const int32_t*)(lay + a.ly_prow_token);
                 m.mt_start = mt; m.hdr = hdr;
@@ -304,11 +308,12 @@ void mega_kernel(MegaArgs a) {
                 gg.a_row_map = (const int32_t*)(lay + a.ly_prow_token);
                 gg.mt_start = mt; gg.hdr = hdr;
                 gg.C = (uint16_t*)(slot + a.sl_h);
-                gg.GU = svb ? (uint16_t*)svb : nullptr;
+                gg.GU = (!kMx && svb) ? (uint16_t*)svb : nullptr;
+                gg.GUf = (kMx && svb) ? (float*)svb : nullptr;
                 gemm_tile<kEpiSwiGLU, false>(gg, e, ml, ntile, smem);
             }
         } else {
-            if constexpr (kMx) {
+            if (mx_tile) {
                 MxGemmArgs m = a.m2;
                 m.A = slot + a.sl_hq; m.SA = slot + a.sl_sh;
                 m.mt_start = mt; m.hdr = hdr;

@@ -10,7 +10,7 @@ import torch
 
 import dispatch_grouped_gemm_moe_amd as moe
 import oracle as O
-from moe_inputs import Workload, make_inputs, KIMI_BF16
+from moe_inputs import Workload, make_inputs, KIMI_BF16, KIMI_FWD_BWD
 
 pytestmark = pytest.mark.gpu
 
@@ -38,6 +38,12 @@ CASES = [
     (_wl("lk_group2_comm8", T=1500, H=256, I=128, E=8, k=2, minibatch=192), 6, 8, False),
     (_wl("lk_group_auto", T=2000, H=256, I=192, E=6, k=3, minibatch=256), 0, 0, False),
     (_wl("lk_mx_group2", T=1200, H=512, I=256, E=4, k=2, minibatch=128, prec="mxfp8"), 6, 0, False),
+    # MXFP8 routed experts with the bf16 shared expert's tiles in the same launch
+    (_wl("lk_mx_shared", T=700, H=384, I=192, E=6, k=2, minibatch=128, shared_expert=True, prec="mxfp8"), 0, 0, False),
+    (_wl("lk_mx_shared_saved", T=700, H=384, I=192, E=6, k=2, minibatch=128, shared_expert=True, prec="mxfp8",
+         router_bias="normal"), 3, 8, True),
+    (_wl("lk_mx_shared_group", T=1200, H=512, I=256, E=4, k=2, minibatch=128, shared_expert=True, prec="mxfp8"),
+     6, 0, True),
 ]
 
 
@@ -63,9 +69,10 @@ def test_layer_kernel_matches_per_gemm_launches(gpu_lib, case):
         assert err <= 1e-2, err
 
 
-def test_layer_kernel_full_size_matches_per_gemm_launches(gpu_lib):
-    inp = make_inputs(KIMI_BF16)
-    print(KIMI_BF16.name, flush=True)
-    a = _forward(inp, 0, 0, 0, False)
-    b = _forward(inp, moe.MOE_F_LAUNCH_PER_GEMM, 0, 0, False)
+@pytest.mark.parametrize("w", [KIMI_BF16, KIMI_FWD_BWD], ids=lambda w: w.name)
+def test_layer_kernel_full_size_matches_per_gemm_launches(gpu_lib, w):
+    inp = make_inputs(w)
+    print(w.name, flush=True)
+    a = _forward(inp, 0, 0, 0, w.backward)
+    b = _forward(inp, moe.MOE_F_LAUNCH_PER_GEMM, 0, 0, w.backward)
     assert torch.equal(a, b)
