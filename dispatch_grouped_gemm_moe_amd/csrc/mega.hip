@@ -189,14 +189,10 @@ __device__ void combine_range(const MegaArgs& a, int b, int c0, int c1, uint8_t*
     }
 }
 
-// Threads of the layer kernel: the bf16 and MXFP8 tiles both run eight waves
-// (two per SIMD).
-template <bool kMx>
-constexpr int kMegaThreads = kTileThreads;
 
+// 512 threads: the bf16 and MXFP8 tiles both run eight waves (two per SIMD)
 template <bool kMx>
-__global__ __attribute__((amdgpu_flat_work_group_size(kMegaThreads<kMx>, kMegaThreads<kMx>),
-                          amdgpu_waves_per_eu(kMegaThreads<kMx> / 256, kMegaThreads<kMx> / 256)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kTileThreads, kTileThreads), amdgpu_waves_per_eu(2, 2)))
 void mega_kernel(MegaArgs a) {
     constexpr int kSmem = kMx ? (kMxSmem > kTileSmem ? kMxSmem : kTileSmem) : kTileSmem;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
@@ -222,7 +218,7 @@ void mega_kernel(MegaArgs a) {
                 const int Tm = tokens_of(a, b);
                 const int chunk = ceil_div(Tm, a.comm);
                 const int c0 = min(Tm, (int)blockIdx.x * chunk), c1 = min(Tm, c0 + chunk);
-                combine_range(a, b, c0, c1, smem, kMegaThreads<kMx>);
+                combine_range(a, b, c0, c1, smem, kTileThreads);
             }
             signal_counter(comb_done + j);
         }
@@ -280,7 +276,7 @@ void mega_kernel(MegaArgs a) {
                 lv -= nt;
             }
             combine_range(a, b, lv * kCombTilesTok, min(tokens_of(a, b), (lv + 1) * kCombTilesTok), smem,
-                          kMegaThreads<kMx>);
+                          kTileThreads);
             continue;
         }
         int b, e, ml, ntile;
@@ -340,9 +336,9 @@ hipError_t launch_mega(const MegaArgs& a, int grid, hipStream_t stream) {
                        3 * a.nmb + 1);
     MegaArgs args = a;
     void* kargs[] = {&args};
-    return a.mx ? hipLaunchCooperativeKernel((const void*)mega_kernel<true>, dim3(grid), dim3(kMegaThreads<true>), kargs,
+    return a.mx ? hipLaunchCooperativeKernel((const void*)mega_kernel<true>, dim3(grid), dim3(kTileThreads), kargs,
                                               0, stream)
-                  : hipLaunchCooperativeKernel((const void*)mega_kernel<false>, dim3(grid), dim3(kMegaThreads<false>), kargs,
+                  : hipLaunchCooperativeKernel((const void*)mega_kernel<false>, dim3(grid), dim3(kTileThreads), kargs,
                                               0, stream);
 }
 
