@@ -162,7 +162,7 @@ struct WgradArgs {
     int M, N, n_split, Et, nmb, mt_ld;
     const int32_t* mt;  // [nmb][mt_ld] first BM-tile of each expert, per minibatch
     const int32_t* rows;  // [nmb][mt_ld] rows of each expert, per minibatch: K stops at the last
-                          // 32-row step holding one (the rest of the tile is zero padding)
+                          // 64-row stage holding one (the rest of the tile is zero padding)
     float* C0;
     float* C1;
     float* Cs0;
