@@ -24,6 +24,7 @@ BWD_CASES = [
     _wl("bwd_shared", T=300, H=384, I=192, E=6, k=2, minibatch=128, shared_expert=True, router_bias="normal"),
     _wl("bwd_tiles", T=700, H=512, I=256, E=4, k=3, minibatch=256),
     _wl("bwd_k1", T=96, H=256, I=128, E=5, k=1),
+    _wl("bwd_k64", T=200, H=64, I=64, E=4, k=2, minibatch=128, shared_expert=True),  # one K stage per GEMM
 ]
 
 

@@ -28,6 +28,7 @@ MXB_CASES = [
     _wl("mxb_shared", T=300, H=384, I=192, E=6, k=2, minibatch=128, shared_expert=True, router_bias="normal"),
     _wl("mxb_tiles", T=700, H=512, I=256, E=4, k=3, minibatch=256, router_bias="zipf"),
     _wl("mxb_wide", T=256, H=256, I=128, E=4, k=2, minibatch=128, router_bias="normal", wide_range=True),
+    _wl("mxb_k64", T=200, H=64, I=64, E=4, k=2, minibatch=128, shared_expert=True),  # half stages only
 ]
 
 

@@ -45,6 +45,8 @@ MX_CASES = [
     _wl("mx_tiny", T=64, H=128, I=64, E=8, k=2, minibatch=64),
     _wl("mx_tiles", T=900, H=512, I=256, E=4, k=2, minibatch=400, router_bias="zipf"),
     _wl("mx_shared", T=300, H=384, I=192, E=6, k=2, minibatch=128, shared_expert=True),
+    # one 64-deep K step per GEMM: every ring stage is a half stage
+    _wl("mx_k64", T=200, H=64, I=64, E=4, k=2, minibatch=128, shared_expert=True),
 ]
 
 
