@@ -46,6 +46,8 @@ def main():
                     help="forward as one launch per grouped GEMM instead of the persistent layer kernel")
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mfma-loop", action="store_true",
+                    help="skip the sustained-MFMA measurement (a pure MFMA loop on the layer's own input values)")
     ap.add_argument("--cold-cache", action="store_true",
                     help="write a 512 MiB scratch buffer before every timed step (more than the 256 MB "
                          "Infinity Cache) and time each step alone with HIP events on the stream")
@@ -239,10 +241,60 @@ def main():
         },
     }
 
+    if not args.no_mfma_loop:
+        loops = {"bf16": mfma_loop(moe, torch, x, inp.Wg, False)}
+        if mx:
+            loops["mxfp8"] = mfma_loop(moe, torch, x, inp.Wg, True)
+        res["detail"]["mfma_loop"] = loops
+        loop = loops["mxfp8" if peak == PEAK_FP8_TFLOPS else "bf16"]
+        res["roofline"]["sustained_peak"] = loop["tflops"]
+        res["roofline"]["frac_of_sustained"] = achieved / loop["tflops"]
     if not args.no_cpu_baseline:
         n = args.cpu_sample or (256 if bwd else 2048)
         res["cpu_baseline"] = cpu_baseline(inp, n, bwd)
     print(json.dumps(res), flush=True)
+
+
+def mfma_loop(moe, torch, x, w, mx: bool) -> dict:
+    """Sustained MFMA rate of the chip: a pure MFMA loop (one 8-wave workgroup
+    per CU, no memory traffic) whose two operands are the layer's own values
+    (one from x, one from the gate weights; bf16, or their MXFP8 E4M3 codes),
+    then zeros.  Under this load the chip lowers its shader clock to its power
+    budget, further for random mantissas than for zeros; the loop's rate is
+    the ceiling a GEMM of that precision on such operands can reach here."""
+    blocks = 256
+    iters = 4096 if mx else 16384
+    flops = blocks * 8.0 * iters * 32 * (131072 if mx else 32768)
+    clocks = torch.zeros(2, dtype=torch.int64, device="cuda")
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+    xs = x.reshape(-1)[:16384].contiguous()
+    ws = w.reshape(-1)[:16384].to("cuda").contiguous()
+    if mx:
+        def codes_of(v):
+            c = torch.empty(v.numel(), dtype=torch.uint8, device="cuda")
+            sc = torch.empty(v.numel() // 32, dtype=torch.uint8, device="cuda")
+            moe.moe_mx_quantize(v.view(1, -1), c.view(1, -1), sc.view(1, -1))
+            return c
+        xs, ws = codes_of(xs), codes_of(ws)
+    # lane t takes its first operand from piece 2t and its second from piece
+    # 2t+1 (16 bytes per bf16 operand, 32 per E4M3 one): interleave x and W
+    piece = 32 if mx else 8
+    src = torch.stack([xs.view(-1, piece), ws.view(-1, piece)], 1).reshape(-1).contiguous()
+    out = {"kind": "MXFP8 (v_mfma_scale_f32_32x32x64_f8f6f4, E4M3 codes of x and Wg)" if mx else
+           "bf16 (v_mfma_f32_32x32x16_bf16, values of x and Wg)", "workgroups": blocks, "mfma_per_wave": iters * 32}
+    for name, ops in (("", src), ("zeros_", torch.zeros_like(src))):
+        moe.moe_diag_mfma_loop(1 if mx else 0, ops, blocks, 64, clocks, sink)  # warm-up
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        moe.moe_diag_mfma_loop(1 if mx else 0, ops, blocks, iters, clocks, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        cyc, ref = clocks.tolist()
+        out[name + "tflops"] = flops / (ms / 1e3) / 1e12
+        out[name + "clock_ghz"] = cyc / (ref / 100e6) / 1e9
+        out[name + "ms"] = ms
+    return out
 
 
 def traffic_for(symbol: str, workload: str):

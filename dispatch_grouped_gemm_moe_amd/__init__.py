@@ -25,7 +25,7 @@ MOE_F_LAUNCH_PER_GEMM = 1 << 2
 EXPORTS = ("moe_status_string", "moe_abi_version", "moe_validate_cfg", "moe_query_sizes",
            "moe_prepare_weights", "moe_route", "moe_dispatch_layout", "moe_layer_fwd",
            "moe_layer_bwd", "moe_read_device_status", "moe_mx_quantize", "moe_timing_enable",
-           "moe_timing_read")
+           "moe_timing_read", "moe_diag_mfma_loop")
 KERNEL_KINDS = ("route", "layout", "gemm_gate_up", "gemm_down", "combine", "gather", "other", "wgrad",
                 "dgrad_down", "dgrad_gate_up", "shared_gemm", "layer")
 
@@ -87,6 +87,7 @@ def _load():
             "moe_mx_quantize": (ctypes.c_int, [P, ctypes.c_int64, I32, P, P, P]),
             "moe_timing_enable": (ctypes.c_int, [I32]),
             "moe_timing_read": (ctypes.c_int, [ctypes.POINTER(moe_kernel_times)]),
+            "moe_diag_mfma_loop": (ctypes.c_int, [I32, P, ctypes.c_int64, I32, I32, P, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(lib, name)
@@ -185,6 +186,14 @@ def moe_mx_quantize(src, codes, scales, stream=None):
     rows, cols = src.shape
     _check("moe_mx_quantize", _load().moe_mx_quantize(_ptr(src), rows, cols, _ptr(codes), _ptr(scales),
                                                       _stream(stream)))
+
+
+def moe_diag_mfma_loop(kind, operands, blocks, iters, clocks, sink, stream=None):
+    """Sustained-MFMA diagnostic: kind 0 = bf16, 1 = MXFP8 (E4M3 codes); operands
+    >= 16 KiB, clocks int64 [2], sink fp32 [blocks*512]."""
+    _check("moe_diag_mfma_loop", _load().moe_diag_mfma_loop(kind, _ptr(operands),
+                                                            operands.numel() * operands.element_size(), blocks,
+                                                            iters, _ptr(clocks), _ptr(sink), _stream(stream)))
 
 
 def moe_timing_enable(on: bool):

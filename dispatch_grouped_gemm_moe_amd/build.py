@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_lib")
 LIB_NAME = "libmoe_mi355x.so"
-SOURCES = ["api.hip", "route.hip", "gemm.hip", "bwd.hip", "mx.hip", "mega.hip"]
+SOURCES = ["api.hip", "route.hip", "gemm.hip", "bwd.hip", "mx.hip", "mega.hip", "diag.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -287,6 +287,26 @@ typedef struct moe_kernel_times {
 moe_status moe_timing_enable(int32_t on);
 moe_status moe_timing_read(moe_kernel_times *out);
 
+/*
+ * Sustained MFMA rate (diagnostic, for benchmarks; not part of the layer).
+ * Launches `blocks` workgroups of 512 threads (eight waves; one workgroup per
+ * CU when blocks = 256) on `stream`; every wave issues iters x 32 independent
+ * matrix instructions on eight fp32 accumulators: kind 0 = v_mfma_f32_32x32x16_bf16
+ * (32768 flops each) on bf16 operands, kind 1 = v_mfma_scale_f32_32x32x64_f8f6f4
+ * (131072 flops each) on OCP E4M3 codes with unit E8M0 scales.  Each lane
+ * reads its operands once from `operands` (device, operand_bytes >= 16 KiB,
+ * 16-byte aligned; the caller picks the values, which set how far the chip
+ * lowers its clock under the load).  No memory is touched inside the loop.
+ * Writes clocks[0] = shader-clock cycles and clocks[1] = 100 MHz reference
+ * ticks over workgroup 0's loop (device, 8-byte aligned), and one float per
+ * thread to sink [blocks * 512] (device) so the work is not elided.  The caller
+ * times the launch with events on `stream`.  MOE_E_INVALID for an unknown
+ * kind, null or misaligned pointers, blocks outside 1..65536, iters < 1;
+ * MOE_E_HIP if the launch fails.  Allocates nothing.
+ */
+moe_status moe_diag_mfma_loop(int32_t kind, const void *operands, int64_t operand_bytes, int32_t blocks,
+                              int32_t iters, uint64_t *clocks, float *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
