@@ -18,6 +18,7 @@ constexpr int kNumCUs = 256;      // MI355X compute units
 constexpr int kBalanceRows = 320;  // bf16 machine balance: ~2.5 PFLOP/s over 8 TB/s, in rows
 constexpr int kCommWorkers = 0;    // layer kernel: combine as tiles of the GEMM workgroups (no dedicated CUs)
 constexpr int kGroupTokens = 8192; // layer kernel: tokens per GEMM phase (minibatches grouped up to this)
+constexpr int kBwdChunkTokens = 5120;  // backward: tokens per phase chunk (minibatches grouped up to this)
 constexpr int kMaxGroup = 4;
 constexpr uint64_t kSpinTicks = 200000000;  // 2 s at the 100 MHz s_memrealtime clock: bound of every device wait
 constexpr size_t kAlign = 256;
@@ -27,6 +28,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 struct Plan {
     int T, H, I, E, k, Et, Mb, nmb, slots, comm_cus, prec;
     int group;  // minibatches per phase of the layer kernel
+    int bchunk; // minibatches per phase chunk of the backward
     bool shared, identity;
     int ld_tok_prow;  // k (+1 with the shared expert)
     int64_t rpad;     // padded GEMM rows of one minibatch
@@ -102,6 +104,10 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     // kGroupTokens tokens (an expert's weight panels then serve that many
     // tokens' rows), with three groups of ring slots in flight.
     const int g_auto = std::max(1, std::min({kMaxGroup, kGroupTokens / p->Mb, p->nmb}));
+    // The backward runs its phases over chunks of minibatches of about
+    // kBwdChunkTokens tokens; with the shared expert, whose GEMMs have only
+    // a minibatch's tokens each, over every minibatch at once.
+    p->bchunk = (c->flags & MOE_F_SHARED_EXPERT) ? p->nmb : std::max(1, std::min(kBwdChunkTokens / p->Mb, p->nmb));
     p->group = c->ring_slots > 0 ? std::max(1, std::min(c->ring_slots / 3, g_auto)) : g_auto;
     p->slots = c->ring_slots > 0 ? c->ring_slots : 3 * p->group;
     p->slots = std::min(p->slots, ceil_div(p->nmb, p->group) * p->group);  // no slot without a minibatch
@@ -186,18 +192,21 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     p->wb_dgut = o; o = align_up(o + nmb * 2 * I * rp * 2);
     p->wb_ht = o; o = align_up(o + nmb * I * rp * 2);
     p->wb_dsel = o; o = align_up(o + nmb * rp * 4);
-    p->wb_dy = o; o = align_up(o + rp * H * 2);
-    p->wb_dgu = o; o = align_up(o + rp * 2 * I * 2);
-    p->wb_dh = o; o = align_up(o + rp * I * (p->mx ? 4 : 2));
-    p->wb_dx = o; o = align_up(o + rp * H * 2);
-    p->wb_dgp = o; o = align_up(o + rp * (H / 64) * 4);
+    // one copy per minibatch of a backward chunk: the chunk's input-gradient
+    // GEMMs run as one launch over its minibatches
+    const size_t nc = (size_t)p->bchunk;
+    p->wb_dy = o; o = align_up(o + nc * rp * H * 2);
+    p->wb_dgu = o; o = align_up(o + nc * rp * 2 * I * 2);
+    p->wb_dh = o; o = align_up(o + nc * rp * I * (p->mx ? 4 : 2));
+    p->wb_dx = o; o = align_up(o + nc * rp * H * 2);
+    p->wb_dgp = o; o = align_up(o + nc * rp * (H / 64) * 4);
     p->wb_dlog = o; o = align_up(o + (size_t)c->T * c->E * 4);
     p->wb_dwrp = o; o = align_up(o + (size_t)dwr_chunks(c->T) * H * c->E * 4);
     if (p->mx) {
-        p->wb_dyq = o; o = align_up(o + rp * H);
-        p->wb_sdy = o; o = align_up(o + (H / 64) * rp * 4);
-        p->wb_dguq = o; o = align_up(o + rp * 2 * I);
-        p->wb_sdgu = o; o = align_up(o + (2 * I / 64) * rp * 4);
+        p->wb_dyq = o; o = align_up(o + nc * rp * H);
+        p->wb_sdy = o; o = align_up(o + nc * (H / 64) * rp * 4);
+        p->wb_dguq = o; o = align_up(o + nc * rp * 2 * I);
+        p->wb_sdgu = o; o = align_up(o + nc * (2 * I / 64) * rp * 4);
     }
     p->ws_bwd = o;
     return MOE_OK;
@@ -555,89 +564,111 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
         ls.prow_token = ls.tok_prow = ls.prow_slot = (int64_t)p.lay_bytes / 4;
         TIMED(MOE_K_LAYOUT, s, launch_layout_batched(idx, p.T, p.Mb, E, k, p.shared ? 1 : 0, o, ls, s));
     }
-    for (int b = 0; b < p.nmb; ++b) {
-        const int t0 = b * p.Mb;
-        const int Tm = (p.T - t0) < p.Mb ? (p.T - t0) : p.Mb;
-        uint8_t* lay = wsb + p.wb_lay0 + (size_t)b * p.lay_bytes;
-        LayoutHeader* hdr = (LayoutHeader*)(lay + p.ly_hdr);
-        int32_t* mt = mt_all + (size_t)b * (Et + 1);
-        int32_t* prow_token = (int32_t*)(lay + p.ly_prow_token);
-        int32_t* tok_prow = (int32_t*)(lay + p.ly_tok_prow);
-        int32_t* prow_slot = (int32_t*)(lay + p.ly_prow_slot);
-        const uint8_t* svb = sv + p.sv_mb0 + (size_t)b * p.sv_mb;
-        const uint16_t* GUb = (const uint16_t*)svb;  // fp32 under MXFP8
-        const uint16_t* Yb = (const uint16_t*)(svb + p.sv_y);
-        uint16_t* dYT = dYT_all + (size_t)b * H * rp;
-        uint16_t* xgT = xgT_all + (size_t)b * H * rp;
-        uint16_t* dGUT = dGUT_all + (size_t)b * 2 * I * rp;
-        uint16_t* HT = HT_all + (size_t)b * I * rp;
-        float* dsel = dsel_all + (size_t)b * rp;
-
-
-        RcombArgs rc{};
-        rc.dout = dout; rc.x = x; rc.Y = Yb; rc.topk_w = gw; rc.prow_token = prow_token;
-        rc.prow_slot = prow_slot; rc.hdr = hdr; rc.dY = dY; rc.dYT = dYT; rc.xgT = xgT; rc.dgp = dgp;
-        rc.dsel = dsel; rc.H = H; rc.k = k; rc.nhb = H / 64; rc.ldt = rp;
-        rc.dYq = p.mx ? wsb + p.wb_dyq : nullptr;  // MXFP8: dY quantised from fp32 here
-        rc.sdY = p.mx ? wsb + p.wb_sdy : nullptr;
-        TIMED(MOE_K_GATHER, s, launch_rcomb_gather(rc, (int)rp, s));
-
-        // MXFP8: the routed experts' input-gradient GEMMs take E4M3 operands
-        // quantised along their K (dY along H here, dG | dU along I below);
-        // the shared expert stays bf16.
-        const int e_bf16 = p.mx ? E : 0;
-        float* dHf = p.mx ? (float*)dH : nullptr;  // fp32 under MXFP8
+    // The backward runs in phases over chunks of minibatches: reverse-combine
+    // of each minibatch of the chunk, one launch of the down input-gradient
+    // GEMM over all of them, the SwiGLU backward of each, one launch of the
+    // gate|up input-gradient GEMM, then the reverse-dispatch of each (a GEMM
+    // launch then has one partial last wave of tiles per chunk instead of one
+    // per minibatch).  The per-minibatch buffers hold one chunk; minibatch b
+    // uses copy b - b0.
+    const int e_bf16 = p.mx ? E : 0;  // MXFP8: experts [0, E) on the scaled-MFMA kernel, the shared expert bf16
+    const int32_t* rows_all = (const int32_t*)(wsb + p.wb_rows);
+    const int64_t nhb = H / 64;
+    float* dHf = p.mx ? (float*)dH : nullptr;  // fp32 under MXFP8
+    auto lay_of = [&](int b) { return wsb + p.wb_lay0 + (size_t)b * p.lay_bytes; };
+    for (int b0 = 0; b0 < p.nmb; b0 += p.bchunk) {
+        const int b1 = (b0 + p.bchunk) < p.nmb ? b0 + p.bchunk : p.nmb;
+        const int32_t* mt_c = mt_all + (size_t)b0 * (Et + 1);
+        const int32_t* rows_c = rows_all + (size_t)b0 * (Et + 1);
+        for (int b = b0; b < b1; ++b) {
+            const size_t j = (size_t)(b - b0);
+            uint8_t* lay = lay_of(b);
+            const uint8_t* svb = sv + p.sv_mb0 + (size_t)b * p.sv_mb;
+            RcombArgs rc{};
+            rc.dout = dout; rc.x = x; rc.Y = (const uint16_t*)(svb + p.sv_y); rc.topk_w = gw;
+            rc.prow_token = (int32_t*)(lay + p.ly_prow_token);
+            rc.prow_slot = (int32_t*)(lay + p.ly_prow_slot); rc.hdr = (LayoutHeader*)(lay + p.ly_hdr);
+            rc.dY = dY + j * rp * H; rc.dYT = dYT_all + (size_t)b * H * rp; rc.xgT = xgT_all + (size_t)b * H * rp;
+            rc.dgp = dgp + j * rp * nhb; rc.dsel = dsel_all + (size_t)b * rp;
+            rc.H = H; rc.k = k; rc.nhb = (int)nhb; rc.ldt = rp;
+            // MXFP8: dY quantised from fp32 here (along H, the down input-gradient GEMM's K)
+            rc.dYq = p.mx ? wsb + p.wb_dyq + j * rp * H : nullptr;
+            rc.sdY = p.mx ? wsb + p.wb_sdy + j * nhb * rp * 4 : nullptr;
+            TIMED(MOE_K_GATHER, s, launch_rcomb_gather(rc, (int)rp, s));
+        }
         if (p.mx) {
             MxGemmArgs m1{};  // dH = Q(dY) Q(Wd)^T
             m1.A = wsb + p.wb_dyq; m1.a_row_map = nullptr; m1.lda = H;
             m1.SA = wsb + p.wb_sdy; m1.sa_kstride = rp * 4;
             m1.B = pk + p.pk_wdq; m1.b_stride = (int64_t)I * H;
             m1.SB = pk + p.pk_sd; m1.sb_stride = (int64_t)(H / 64) * I * 4; m1.sb_kstride = (int64_t)I * 4;
-            m1.N = I; m1.K = H; m1.mt_start = mt; m1.hdr = hdr; m1.e_begin = 0; m1.e_end = E;
+            m1.N = I; m1.K = H; m1.mt_start = mt_c; m1.hdr = nullptr; m1.e_begin = 0; m1.e_end = E;
             m1.C = nullptr; m1.ldc = I; m1.Cq = nullptr; m1.Cs = nullptr; m1.cs_rows = 0; m1.GU = nullptr;
-            m1.Cf = dHf; m1.rows_e = (const int32_t*)(wsb + p.wb_rows) + (size_t)b * (Et + 1);
+            m1.Cf = dHf; m1.rows_e = rows_c;
+            m1.nmb = b1 - b0; m1.mt_ld = Et + 1; m1.a_mb = rp * H; m1.sa_mb = nhb * rp * 4; m1.c_mb = rp * I;
             TIMED(MOE_K_DGRAD_DOWN, s, launch_mx_gemm(m1, kEpiStore, grid, s));
         }
-        GemmArgs g1{};  // dH = dY Wd^T
-        g1.A = dY; g1.a_row_map = nullptr; g1.lda = H;
-        g1.B = Wdc; g1.b_stride = (int64_t)I * H;
-        g1.C = dH; g1.ldc = I; g1.N = I; g1.K = H;
-        g1.mt_start = mt; g1.hdr = hdr; g1.Et = Et; g1.GU = nullptr; g1.e_begin = e_bf16; g1.e_end = Et;
-        g1.GUf = nullptr; g1.Cf = dHf; g1.rows_e = (const int32_t*)(wsb + p.wb_rows) + (size_t)b * (Et + 1);
-        if (e_bf16 < Et)
+        if (e_bf16 < Et) {
+            GemmArgs g1{};  // dH = dY Wd^T
+            g1.A = dY; g1.a_row_map = nullptr; g1.lda = H;
+            g1.B = Wdc; g1.b_stride = (int64_t)I * H;
+            g1.C = dH; g1.ldc = I; g1.N = I; g1.K = H;
+            g1.mt_start = mt_c; g1.hdr = nullptr; g1.Et = Et; g1.GU = nullptr; g1.e_begin = e_bf16; g1.e_end = Et;
+            g1.GUf = nullptr; g1.Cf = dHf; g1.rows_e = rows_c;
+            g1.nmb = b1 - b0; g1.mt_ld = Et + 1; g1.a_mb = rp * H; g1.c_mb = rp * I;
             TIMED(p.mx ? MOE_K_SHARED_GEMM : MOE_K_DGRAD_DOWN, s, launch_grouped_gemm(g1, kEpiStore, grid, s));
-        SwigluBwdArgs sb{};
-        sb.dH = dH; sb.GU = GUb; sb.hdr = hdr; sb.dGU = dGU; sb.dGUT = dGUT; sb.HT = HT; sb.I = I; sb.ldt = rp;
-        sb.dHf = dHf; sb.GUf = p.mx ? (const float*)GUb : nullptr;  // MXFP8: fp32 inputs, dG|dU quantised here
-        sb.dGUq = p.mx ? wsb + p.wb_dguq : nullptr; sb.sdGU = p.mx ? wsb + p.wb_sdgu : nullptr;
-        TIMED(MOE_K_GATHER, s, launch_swiglu_bwd(sb, (int)rp, s));
+        }
+        for (int b = b0; b < b1; ++b) {
+            const size_t j = (size_t)(b - b0);
+            uint8_t* lay = lay_of(b);
+            const uint8_t* svb = sv + p.sv_mb0 + (size_t)b * p.sv_mb;
+            const size_t bh = j * rp * I;  // this minibatch's dH elements
+            SwigluBwdArgs sb{};
+            sb.dH = p.mx ? nullptr : dH + bh; sb.GU = (const uint16_t*)svb; sb.hdr = (LayoutHeader*)(lay + p.ly_hdr);
+            sb.dGU = dGU + 2 * bh; sb.dGUT = dGUT_all + (size_t)b * 2 * I * rp; sb.HT = HT_all + (size_t)b * I * rp;
+            sb.I = I; sb.ldt = rp;
+            // MXFP8: fp32 inputs, dG|dU quantised here (along I, the gate|up input-gradient GEMM's K)
+            sb.dHf = p.mx ? dHf + bh : nullptr; sb.GUf = p.mx ? (const float*)svb : nullptr;
+            sb.dGUq = p.mx ? wsb + p.wb_dguq + 2 * bh : nullptr;
+            sb.sdGU = p.mx ? wsb + p.wb_sdgu + j * (2 * I / 64) * rp * 4 : nullptr;
+            TIMED(MOE_K_GATHER, s, launch_swiglu_bwd(sb, (int)rp, s));
+        }
         if (p.mx) {
             MxGemmArgs m2{};  // dX = Q(dG | dU) Q(Wg | Wu)^T
             m2.A = wsb + p.wb_dguq; m2.a_row_map = nullptr; m2.lda = 2 * I;
             m2.SA = wsb + p.wb_sdgu; m2.sa_kstride = rp * 4;
             m2.B = pk + p.pk_wguq; m2.b_stride = (int64_t)H * 2 * I;
             m2.SB = pk + p.pk_sgu; m2.sb_stride = (int64_t)(2 * I / 64) * H * 4; m2.sb_kstride = (int64_t)H * 4;
-            m2.N = H; m2.K = 2 * I; m2.mt_start = mt; m2.hdr = hdr; m2.e_begin = 0; m2.e_end = E;
+            m2.N = H; m2.K = 2 * I; m2.mt_start = mt_c; m2.hdr = nullptr; m2.e_begin = 0; m2.e_end = E;
             m2.C = dXb; m2.ldc = H; m2.Cq = nullptr; m2.Cs = nullptr; m2.cs_rows = 0; m2.GU = nullptr;
-            m2.Cf = nullptr; m2.rows_e = (const int32_t*)(wsb + p.wb_rows) + (size_t)b * (Et + 1);
+            m2.Cf = nullptr; m2.rows_e = rows_c;
+            m2.nmb = b1 - b0; m2.mt_ld = Et + 1; m2.a_mb = rp * 2 * I; m2.sa_mb = (2 * I / 64) * rp * 4; m2.c_mb = rp * H;
             TIMED(MOE_K_DGRAD_GATE_UP, s, launch_mx_gemm(m2, kEpiStore, grid, s));
         }
-        GemmArgs g2{};  // dX = dG Wg^T + dU Wu^T
-        g2.A = dGU; g2.a_row_map = nullptr; g2.lda = 2 * I;
-        g2.B = Wgu; g2.b_stride = (int64_t)H * 2 * I;
-        g2.C = dXb; g2.ldc = H; g2.N = H; g2.K = 2 * I;
-        g2.mt_start = mt; g2.hdr = hdr; g2.Et = Et;
-        g2.GU = nullptr; g2.e_begin = e_bf16; g2.e_end = Et; g2.GUf = nullptr; g2.Cf = nullptr;
-        g2.rows_e = (const int32_t*)(wsb + p.wb_rows) + (size_t)b * (Et + 1);
-        if (e_bf16 < Et)
+        if (e_bf16 < Et) {
+            GemmArgs g2{};  // dX = dG Wg^T + dU Wu^T
+            g2.A = dGU; g2.a_row_map = nullptr; g2.lda = 2 * I;
+            g2.B = Wgu; g2.b_stride = (int64_t)H * 2 * I;
+            g2.C = dXb; g2.ldc = H; g2.N = H; g2.K = 2 * I;
+            g2.mt_start = mt_c; g2.hdr = nullptr; g2.Et = Et;
+            g2.GU = nullptr; g2.e_begin = e_bf16; g2.e_end = Et; g2.GUf = nullptr; g2.Cf = nullptr;
+            g2.rows_e = rows_c;
+            g2.nmb = b1 - b0; g2.mt_ld = Et + 1; g2.a_mb = rp * 2 * I; g2.c_mb = rp * H;
             TIMED(p.mx ? MOE_K_SHARED_GEMM : MOE_K_DGRAD_GATE_UP, s, launch_grouped_gemm(g2, kEpiStore, grid, s));
-
-        RdispArgs rd{};
-        rd.dX = dXb; rd.dgp = dgp; rd.tok_prow = tok_prow; rd.topk_idx = idx; rd.topk_w = gw; rd.WrT = WrT;
-        rd.dsel = dsel; rd.dgate = dgate; rd.dx = dx; rd.t0 = t0; rd.H = H; rd.k = k; rd.ld = p.ld_tok_prow;
-        rd.with_shared = p.shared ? 1 : 0; rd.nhb = H / 64;
-        rd.dlogits = (float*)(wsb + p.wb_dlog); rd.E = E;
-        TIMED(MOE_K_COMBINE, s, launch_rdispatch(rd, Tm, s));
+        }
+        for (int b = b0; b < b1; ++b) {
+            const size_t j = (size_t)(b - b0);
+            const int t0 = b * p.Mb;
+            const int Tm = (p.T - t0) < p.Mb ? (p.T - t0) : p.Mb;
+            uint8_t* lay = lay_of(b);
+            RdispArgs rd{};
+            rd.dX = dXb + j * rp * H; rd.dgp = dgp + j * rp * nhb;
+            rd.tok_prow = (int32_t*)(lay + p.ly_tok_prow); rd.topk_idx = idx; rd.topk_w = gw; rd.WrT = WrT;
+            rd.dsel = dsel_all + (size_t)b * rp; rd.dgate = dgate; rd.dx = dx; rd.t0 = t0; rd.H = H; rd.k = k;
+            rd.ld = p.ld_tok_prow; rd.with_shared = p.shared ? 1 : 0; rd.nhb = (int)nhb;
+            rd.dlogits = (float*)(wsb + p.wb_dlog); rd.E = E;
+            TIMED(MOE_K_COMBINE, s, launch_rdispatch(rd, Tm, s));
+        }
     }
     WgradArgs wa{};  // [dWg | dWu][e] = x_e^T [dG | dU]_e over every row of expert e
     wa.A = xgT_all; wa.B = dGUT_all; wa.ld = rp;

@@ -20,18 +20,27 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kTileThreads, kTileThreads
 void grouped_gemm_kernel(GemmArgs p) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kTileSmem];
     const int NT = ceil_div(p.N, BN);
-    const int total = grouped_tiles(p.mt_start, p.e_begin, p.e_end, p.N);
+    const int total = launch_tiles(p);
     const int G = gridDim.x, per = G >> 3;
     // Workgroups are dealt to the 8 XCDs round-robin; the 'per' workgroups of
     // one XCD take consecutive tiles so that they share weight and row tiles
     // in that XCD's L2.
     const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
     for (int it = 0;; ++it) {
-        const int v = it * G + xcd * per + local;
+        int v = it * G + xcd * per + local;
         if (v >= total) break;
+        GemmArgs q = p;
+        if (p.nmb > 1) {
+            const int b = minibatch_of_tile(p, v);
+            q.mt_start += (int64_t)b * p.mt_ld;
+            if (q.rows_e) q.rows_e += (int64_t)b * p.mt_ld;
+            if (!q.a_row_map) q.A += b * p.a_mb;
+            if (q.C) q.C += b * p.c_mb;
+            if (q.Cf) q.Cf += b * p.c_mb;
+        }
         int e, ml, ntile;
-        tile_coords(p.mt_start, p.e_begin, p.e_end, NT, v, e, ml, ntile);
-        gemm_tile<EPI>(p, e, ml, ntile, smem);
+        tile_coords(q.mt_start, q.e_begin, q.e_end, NT, v, e, ml, ntile);
+        gemm_tile<EPI>(q, e, ml, ntile, smem);
     }
 }
 

@@ -66,6 +66,27 @@ __device__ __forceinline__ int grouped_tiles(const int32_t* mt_start, int e_begi
     return (mt_start[e_end] - mt_start[e_begin]) * ceil_div(N, BN);
 }
 
+// A launch over p.nmb minibatches (GemmArgs / MxGemmArgs): its total tile
+// count, and for tile v the minibatch holding it (v becomes the tile index
+// within that minibatch).
+template <class Args>
+__device__ __forceinline__ int launch_tiles(const Args& p) {
+    const int nmb = p.nmb > 1 ? p.nmb : 1;
+    int total = 0;
+    for (int b = 0; b < nmb; ++b) total += grouped_tiles(p.mt_start + (int64_t)b * p.mt_ld, p.e_begin, p.e_end, p.N);
+    return total;
+}
+template <class Args>
+__device__ __forceinline__ int minibatch_of_tile(const Args& p, int& v) {
+    int b = 0;
+    for (; b + 1 < p.nmb; ++b) {
+        const int nt = grouped_tiles(p.mt_start + (int64_t)b * p.mt_ld, p.e_begin, p.e_end, p.N);
+        if (v < nt) break;
+        v -= nt;
+    }
+    return b;
+}
+
 // Epilogue staging.  A 64-row block of the tile is written to LDS with row
 // pitches 16 bytes longer than the data (256, 512 or 1024 bytes), so the 32
 // rows of one write instruction fall on different banks, then copied out in

@@ -60,6 +60,12 @@ struct GemmArgs {
     float* GUf;
     float* Cf;                 // kEpiStore, optional: fp32 output instead of C
     const int32_t* rows_e;     // optional [Et] rows of each expert: padding fragments get no MFMAs
+    // Several minibatches in one launch (kEpiStore, nmb > 1): minibatch b's
+    // tile map and row counts sit b * mt_ld ints after mt_start / rows_e, its
+    // A rows (a_row_map NULL) a_mb elements and its C / Cf rows c_mb elements
+    // after minibatch 0's; the tiles run minibatch by minibatch.
+    int nmb, mt_ld;
+    int64_t a_mb, c_mb;
 };
 
 enum GemmEpilogue { kEpiSwiGLU = 0, kEpiStore = 1 };
@@ -90,6 +96,10 @@ struct MxGemmArgs {
     float* GU;                 // kEpiSwiGLU, optional: fp32 g | u [R_pad][N] kept for the backward
     float* Cf;                 // kEpiStore, optional: fp32 output instead of C
     const int32_t* rows_e;     // optional [Et] rows of each expert: padding fragments get no MFMAs
+    // Several minibatches in one launch (kEpiStore, nmb > 1), as in GemmArgs;
+    // a_mb and sa_mb are bytes of codes and scales, c_mb elements of C / Cf.
+    int nmb, mt_ld;
+    int64_t a_mb, sa_mb, c_mb;
 };
 void launch_mx_gemm(const MxGemmArgs& a, GemmEpilogue epi, int grid, hipStream_t stream);
 // bf16 [rows][cols] -> E4M3 codes [rows][cols] and E8M0 scales; layout 0:

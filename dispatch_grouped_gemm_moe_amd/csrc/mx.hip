@@ -88,15 +88,25 @@ __global__ __attribute__((amdgpu_flat_work_group_size(kTileThreads, kTileThreads
 void mx_gemm_kernel(MxGemmArgs p) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kMxSmem];
     const int NT = ceil_div(p.N, BN);
-    const int total = grouped_tiles(p.mt_start, p.e_begin, p.e_end, p.N);
+    const int total = launch_tiles(p);
     const int G = gridDim.x, per = G >> 3;
     const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
     for (int it = 0;; ++it) {
-        const int v = it * G + xcd * per + local;
+        int v = it * G + xcd * per + local;
         if (v >= total) break;
+        MxGemmArgs q = p;
+        if (p.nmb > 1) {
+            const int b = minibatch_of_tile(p, v);
+            q.mt_start += (int64_t)b * p.mt_ld;
+            if (q.rows_e) q.rows_e += (int64_t)b * p.mt_ld;
+            if (!q.a_row_map) q.A += b * p.a_mb;
+            q.SA += b * p.sa_mb;
+            if (q.C) q.C += b * p.c_mb;
+            if (q.Cf) q.Cf += b * p.c_mb;
+        }
         int e, ml, ntile;
-        tile_coords(p.mt_start, p.e_begin, p.e_end, NT, v, e, ml, ntile);
-        mx_gemm_tile<EPI>(p, e, ml, ntile, smem);
+        tile_coords(q.mt_start, q.e_begin, q.e_end, NT, v, e, ml, ntile);
+        mx_gemm_tile<EPI>(q, e, ml, ntile, smem);
     }
 }
 
