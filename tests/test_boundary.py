@@ -72,6 +72,13 @@ def test_query_sizes_h7168_i2048():
 def test_query_sizes_automatic_minibatch_and_shared_expert():
     s = moe.moe_query_sizes(moe.make_cfg(4096, 2048, 1024, 64, 6))
     assert 1 <= s.num_minibatches <= 2 and s.minibatch * s.num_minibatches >= 4096
+    # H=7168 I=2048 E=32 k=8: two waves of gate|up tiles and the balance rows come
+    # at 1280 tokens, but the expected padding of the experts' last M tiles
+    # (E x 128 rows) falls to a sixteenth of the rows only at 8192 tokens
+    s = moe.moe_query_sizes(moe.make_cfg(16384, 7168, 2048, 32, 8))
+    assert s.minibatch == 8192 and s.num_minibatches == 2
+    s = moe.moe_query_sizes(moe.make_cfg(65536, 7168, 2048, 32, 8))
+    assert s.minibatch == 8192 and s.num_minibatches == 8
     a = moe.moe_query_sizes(moe.make_cfg(1024, 512, 256, 8, 2))
     b = moe.moe_query_sizes(moe.make_cfg(1024, 512, 256, 8, 2, flags=moe.MOE_F_SHARED_EXPERT))
     assert b.packed_weights > a.packed_weights and b.workspace_fwd > a.workspace_fwd

@@ -121,3 +121,21 @@ def test_full_size_backward_dout_on_sampled_tokens_only(full):
         errs["dWsu"] = O.rel_inf_err(_host(g["dWsu"]), c["dWu"])
         errs["dWsd"] = O.rel_inf_err(_host(g["dWsd"]), c["dWd"])
     _check(errs, TOL[w.prec], "%s dout on %d tokens (%d experts reached)" % (w.name, len(S), len(reached)))
+
+
+def test_full_size_ten_runs_bitwise_identical(full):
+    """Ten forward + backward passes at full size, launched as the benchmark
+    launches them, give bitwise-identical outputs and gradients (every sum in
+    the layer has a fixed order)."""
+    layer, inp = full.layer, full.inp
+    first = None
+    for run in range(10):
+        out = layer.forward().clone()
+        g = layer.backward(inp.dout, to_cpu=False)
+        g["out"] = out
+        if first is None:
+            first = g
+            continue
+        for n in first:
+            assert torch.equal(g[n], first[n]), (run, n)
+    print("%s: 10 runs bitwise identical (%s)" % (full.w.name, ", ".join(sorted(first))))
