@@ -20,7 +20,8 @@ namespace moe {
 constexpr int kTile = 64;
 
 // One workgroup per 64 padded rows x 64 hidden columns of a minibatch.
-//   dY[prow][h]   = bf16(w * dout[t][h])  (0 on padding rows)
+//   dY[prow][h]   = bf16(w * dout[t][h])  (0 on padding rows), if dY is set
+//   row_w[prow]   = w (0 on padding rows), if row_w is set
 //   dYT[h][prow]  = the same, transposed (weight-gradient operand)
 //   xgT[h][prow]  = x[t][h], transposed (weight-gradient operand)
 //   dgp[prow][hb] = sum over the block's 64 columns of dout[t][h] * Y[prow][h]
@@ -71,7 +72,10 @@ __global__ __launch_bounds__(256) void rcomb_gather_kernel(RcombArgs p) {
     part = part + __shfl_xor(part, 2, kWave);
     if ((tid & 3) == 0) {
         if (slot >= 0 && slot < p.k) p.dgp[(int64_t)prow * p.nhb + blockIdx.y] = part;
-        if (blockIdx.y == 0) p.dsel[prow] = 0.0f;
+        if (blockIdx.y == 0) {
+            p.dsel[prow] = 0.0f;
+            if (p.row_w) p.row_w[prow] = w;
+        }
     }
     uint16_t dy[16];
     float dyf[16];
@@ -85,7 +89,7 @@ __global__ __launch_bounds__(256) void rcomb_gather_kernel(RcombArgs p) {
     if (p.dYq)  // MXFP8 operand of the down input-gradient GEMM, from the fp32 values
         mx_quant_row64(dyf, tid & 3, p.dYq + (int64_t)prow * p.H + h0,
                        (uint32_t*)(p.sdY + ((int64_t)(h0 / 64) * p.ldt + prow) * 4));
-    {
+    if (p.dY) {
         intx4* dst = (intx4*)(p.dY + (int64_t)prow * p.H + h0 + c0);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {

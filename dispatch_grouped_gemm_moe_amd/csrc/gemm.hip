@@ -34,7 +34,9 @@ void grouped_gemm_kernel(GemmArgs p) {
             const int b = minibatch_of_tile(p, v);
             q.mt_start += (int64_t)b * p.mt_ld;
             if (q.rows_e) q.rows_e += (int64_t)b * p.mt_ld;
-            if (!q.a_row_map) q.A += b * p.a_mb;
+            if (q.a_row_map) q.a_row_map += b * p.map_mb;
+            else q.A += b * p.a_mb;
+            if (q.row_scale) q.row_scale += b * p.rs_mb;
             if (q.C) q.C += b * p.c_mb;
             if (q.Cf) q.Cf += b * p.c_mb;
         }

@@ -360,12 +360,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs p, int e, int ml, int n
         for (int b = 0; b < 4; ++b) {
             if ((wm >> 1) == (b & 1)) {
                 const int i = b >> 1;
+                const float sc = p.row_scale ? p.row_scale[prow0 + b * 64 + rl] : 1.0f;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
                         *(floatx4*)(smem + rl * kEpiPitch64 + frag_col(j, q) * 4) =
-                            floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                            floatx4{acc[i][j][4 * q] * sc, acc[i][j][4 * q + 1] * sc, acc[i][j][4 * q + 2] * sc,
+                                    acc[i][j][4 * q + 3] * sc};
             }
             __syncthreads();
             epi_copy_out<64, kTileThreads>(smem, kEpiPitch64, (char*)(p.Cf + (int64_t)(prow0 + b * 64) * p.ldc + n0),
@@ -377,12 +379,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs p, int e, int ml, int n
         for (int b = 0; b < 4; ++b) {
             if ((wm >> 1) == (b & 1)) {
                 const int i = b >> 1;
+                const float sc = p.row_scale ? p.row_scale[prow0 + b * 64 + rl] : 1.0f;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        *(uint2*)(smem + rl * kEpiPitch32 + frag_col(j, q) * 2) = pack_bf16x4(
-                            acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                        *(uint2*)(smem + rl * kEpiPitch32 + frag_col(j, q) * 2) =
+                            pack_bf16x4(acc[i][j][4 * q] * sc, acc[i][j][4 * q + 1] * sc, acc[i][j][4 * q + 2] * sc,
+                                        acc[i][j][4 * q + 3] * sc);
             }
             __syncthreads();
             epi_copy_out<32, kTileThreads>(smem, kEpiPitch32, (char*)(p.C + (int64_t)(prow0 + b * 64) * p.ldc + n0),

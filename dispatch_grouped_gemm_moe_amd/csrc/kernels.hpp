@@ -62,10 +62,14 @@ struct GemmArgs {
     const int32_t* rows_e;     // optional [Et] rows of each expert: padding fragments get no MFMAs
     // Several minibatches in one launch (kEpiStore, nmb > 1): minibatch b's
     // tile map and row counts sit b * mt_ld ints after mt_start / rows_e, its
-    // A rows (a_row_map NULL) a_mb elements and its C / Cf rows c_mb elements
-    // after minibatch 0's; the tiles run minibatch by minibatch.
+    // A rows (a_row_map NULL) a_mb elements, its row map map_mb ints, its
+    // row scales rs_mb floats and its C / Cf rows c_mb elements after
+    // minibatch 0's; the tiles run minibatch by minibatch.
     int nmb, mt_ld;
-    int64_t a_mb, c_mb;
+    int64_t a_mb, c_mb, map_mb, rs_mb;
+    // kEpiStore, optional: output row r is acc * row_scale[r] (fp32) before
+    // it is rounded and stored
+    const float* row_scale;
 };
 
 enum GemmEpilogue { kEpiSwiGLU = 0, kEpiStore = 1 };
@@ -203,7 +207,8 @@ struct RcombArgs {
     const int32_t* prow_token;
     const int32_t* prow_slot;
     const LayoutHeader* hdr;
-    uint16_t* dY;              // [R_pad][H]
+    uint16_t* dY;              // [R_pad][H], or NULL: not written
+    float* row_w;              // [R_pad], or NULL: each padded row's weight (gate weight, 1 for the shared expert, 0 on padding)
     uint16_t* dYT;             // [H][ldt]
     uint16_t* xgT;             // [H][ldt]
     float* dgp;                // [R_pad][nhb] partial gate gradients
