@@ -251,13 +251,18 @@ struct DenseK8 {
     }
 };
 
+// How a tile treats the padding rows of an expert's last tile (with
+// p.rows_e): kPadNone runs every fragment; kPadHalf drops every wave's second
+// fragment row (tile rows 128..255) when the tile holds at most 128 valid
+// rows (two mainloop variants, uniform over the workgroup); kPadPerWave drops
+// each wave's fragments that hold only padding rows (three variants).
+constexpr int kPadNone = 0, kPadHalf = 1, kPadPerWave = 2;
+
 // One 256 x 256 output tile (expert e, M tile ml of the expert, N tile ntile)
 // of the bf16 grouped GEMM with its epilogue, by 512 threads; smem is the
-// kTileSmem LDS ring.  kSkipPadding: with p.rows_e, the fragments of an
-// expert's last tile that hold only padding rows get no MFMAs (three mainloop
-// variants; the persistent layer kernel, where they would crowd its
-// registers, compiles the full one only).
-template <int EPI, bool kSkipPadding = true>
+// kTileSmem LDS ring.  Padding rows are skipped as kPad says (their outputs
+// are then zero; no caller reads them).
+template <int EPI, int kPad = kPadPerWave>
 __device__ __forceinline__ void gemm_tile(const GemmArgs p, int e, int ml, int ntile, uint8_t* smem) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 1;
@@ -283,13 +288,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs p, int e, int ml, int n
     floatx16 acc[2][4];
     const char* bbase = (const char*)(p.B + (int64_t)e * p.b_stride);
     int nv = 2;
-    if (kSkipPadding && p.rows_e) {
+    if (kPad != kPadNone && p.rows_e) {
         // fragment i of this wave holds tile rows 128i + 32wm .. +31
         const int valid = p.rows_e[e] - ml * BM, w32 = __builtin_amdgcn_readfirstlane(wm) * 32;
-        nv = valid > 128 + w32 ? 2 : (valid > w32 ? 1 : 0);
+        nv = kPad == kPadHalf ? (valid > 128 ? 2 : 1) : (valid > 128 + w32 ? 2 : (valid > w32 ? 1 : 0));
     }
-    if (!kSkipPadding) {
+    if (kPad == kPadNone) {
         tile_mainloop8<2>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT2, DenseK8{});
+    } else if (kPad == kPadHalf) {
+        if (nv == 2) tile_mainloop8<2>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT2, DenseK8{});
+        else tile_mainloop8<1>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT2, DenseK8{});
     } else switch (nv) {
         case 2: tile_mainloop8<2>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT2, DenseK8{}); break;
         case 1: tile_mainloop8<1>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT2, DenseK8{}); break;

@@ -272,16 +272,21 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
 }
 
 // One 256 x 256 output tile (expert e, M tile ml, N tile ntile) of the MXFP8
-// grouped GEMM; with p.rows_e and kSkipPadding the padding fragments of an
-// expert's last tile get no MFMAs (the layer kernel compiles the full loop).
-template <int EPI, bool kSkipPadding = true>
+// grouped GEMM; with p.rows_e the padding fragments of an expert's last tile
+// get no MFMAs as kPad says (gemm_tile.hpp).
+template <int EPI, int kPad = kPadPerWave>
 __device__ __forceinline__ void mx_gemm_tile(const MxGemmArgs p, int e, int ml, int ntile, uint8_t* smem) {
-    if (!kSkipPadding || !p.rows_e) {
+    if (kPad == kPadNone || !p.rows_e) {
         mx_tile_body<EPI, 2>(p, e, ml, ntile, smem);
         return;
     }
     // fragment i of this wave holds tile rows 128i + 32wm .. +31
     const int valid = p.rows_e[e] - ml * BM;
+    if (kPad == kPadHalf) {
+        if (valid > 128) mx_tile_body<EPI, 2>(p, e, ml, ntile, smem);
+        else mx_tile_body<EPI, 1>(p, e, ml, ntile, smem);
+        return;
+    }
     const int w32 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 7) * 32;
     switch (valid > 128 + w32 ? 2 : (valid > w32 ? 1 : 0)) {
         case 2: mx_tile_body<EPI, 2>(p, e, ml, ntile, smem); break;
