@@ -63,7 +63,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const int sr = tid >> 3, sq = (tid & 7) * 4;
 
     for (int e0 = 0; e0 < E; e0 += kRouteEC) {
-        auto stage = [&](int c, int buf) {
+        // the router weight of chunk c: this thread's 4 experts of one h row
+        auto load_w = [&](int c) {
             const int h = c * kWave + sr;
             const float* wrow = Wr + (size_t)h * E + e0 + sq;
             floatx4 w4;
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
 #pragma unroll
                 for (int q = 0; q < 4; ++q) w4[q] = (e0 + sq + q < E) ? wrow[q] : 0.0f;
             }
-            *(floatx4*)&s_w[buf][sr][sq] = w4;
+            return w4;
         };
         float acc[kRouteWaveTokens][kRouteEC];
 #pragma unroll
@@ -88,11 +89,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
         };
         uint16_t xnext[kRouteWaveTokens];
         __syncthreads();  // previous pass done with s_w
-        stage(0, 0);
+        *(floatx4*)&s_w[0][sr][sq] = load_w(0);
+        // chunk c + 1's weights are loaded during chunk c - 1 and written to
+        // LDS after chunk c's barrier, so no chunk waits on a global load
+        floatx4 wnext = nchunk > 1 ? load_w(1) : floatx4{0, 0, 0, 0};
         load_x(0, xnext);
         for (int c = 0; c < nchunk; ++c) {
             __syncthreads();  // chunk c staged; chunk c-1's buffer free
-            if (c + 1 < nchunk) stage(c + 1, (c + 1) & 1);
+            if (c + 1 < nchunk) *(floatx4*)&s_w[(c + 1) & 1][sr][sq] = wnext;
+            if (c + 2 < nchunk) wnext = load_w(c + 2);
             float xv[kRouteWaveTokens];
 #pragma unroll
             for (int tt = 0; tt < kRouteWaveTokens; ++tt) xv[tt] = bf16_to_f32(xnext[tt]);
