@@ -54,7 +54,7 @@ struct Plan {
     size_t sv_idx, sv_w, sv_mb0, sv_mb, sv_y, saved;
     // backward workspace (bytes)
     size_t wb_wrt, wb_mt, wb_rows, wb_lay0, lay_bytes, ly_hdr, ly_prow_token, ly_tok_prow, ly_prow_slot;
-    size_t wb_dyt, wb_xgt, wb_dgut, wb_ht, wb_dsel, wb_dy, wb_dgu, wb_dh, wb_dx, wb_dgp, wb_roww, ws_bwd;
+    size_t wb_dyt, wb_xgt, wb_dgut, wb_ht, wb_dsel, wb_dgu, wb_dh, wb_dx, wb_dgp, wb_roww, ws_bwd;
     size_t wb_dyq, wb_sdy, wb_dguq, wb_sdgu;  // MXFP8 operands of the input-gradient GEMMs
     size_t wb_dlog, wb_dwrp;                  // dense d out / d logits, router-gradient partial sums
 };
@@ -204,10 +204,9 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     // one copy per minibatch of a backward chunk: the chunk's input-gradient
     // GEMMs run as one launch over its minibatches
     const size_t nc = (size_t)p->bchunk;
-    // dY row-major only under MXFP8 (the shared expert's bf16 input-gradient
-    // GEMM reads it); in bf16 the down input-gradient GEMM gathers dout rows
-    // and scales each output row by its weight (row_w)
-    p->wb_dy = o; o = align_up(o + (p->mx ? nc * rp * H * 2 : 0));
+    // no row-major dY: the bf16 down input-gradient GEMM gathers dout rows and
+    // scales each output row by its weight (row_w); the MXFP8 one reads the
+    // quantised dY
     p->wb_roww = o; o = align_up(o + nc * rp * 4);
     p->wb_dgu = o; o = align_up(o + nc * rp * 2 * I * 2);
     p->wb_dh = o; o = align_up(o + nc * rp * I * (p->mx ? 4 : 2));
@@ -553,7 +552,6 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
     uint16_t* dGUT_all = (uint16_t*)(wsb + p.wb_dgut);
     uint16_t* HT_all = (uint16_t*)(wsb + p.wb_ht);
     float* dsel_all = (float*)(wsb + p.wb_dsel);
-    uint16_t* dY = (uint16_t*)(wsb + p.wb_dy);
     uint16_t* dGU = (uint16_t*)(wsb + p.wb_dgu);
     uint16_t* dH = (uint16_t*)(wsb + p.wb_dh);
     uint16_t* dXb = (uint16_t*)(wsb + p.wb_dx);
@@ -602,8 +600,8 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             rc.dout = dout; rc.x = x; rc.Y = (const uint16_t*)(svb + p.sv_y); rc.topk_w = gw;
             rc.prow_token = (int32_t*)(lay + p.ly_prow_token);
             rc.prow_slot = (int32_t*)(lay + p.ly_prow_slot); rc.hdr = (LayoutHeader*)(lay + p.ly_hdr);
-            rc.dY = p.mx ? dY + j * rp * H : nullptr;
-            rc.row_w = p.mx ? nullptr : roww + j * rp;
+            rc.dY = nullptr;
+            rc.row_w = roww + j * rp;
             rc.dYT = dYT_all + (size_t)b * H * rp; rc.xgT = xgT_all + (size_t)b * H * rp;
             rc.dgp = dgp + j * rp * nhb; rc.dsel = dsel_all + (size_t)b * rp;
             rc.H = H; rc.k = k; rc.nhb = (int)nhb; rc.ldt = rp;
@@ -625,16 +623,12 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             TIMED(MOE_K_DGRAD_DOWN, s, launch_mx_gemm(m1, kEpiStore, grid, s));
         }
         if (e_bf16 < Et) {
-            // dH = dY Wd^T; in bf16 with dY_r = w_r dout[t_r] taken as the
-            // gathered dout rows times Wd^T, each output row scaled by w_r
+            // dH = dY Wd^T with dY_r = w_r dout[t_r]: the gathered dout rows
+            // times Wd^T, each output row scaled by w_r (1 for the shared expert)
             GemmArgs g1{};
-            if (p.mx) {
-                g1.A = dY; g1.a_row_map = nullptr; g1.a_mb = rp * H;
-            } else {
-                g1.A = dout; g1.a_row_map = (const int32_t*)(lay_of(b0) + p.ly_prow_token);
-                g1.map_mb = (int64_t)p.lay_bytes / 4;
-                g1.row_scale = roww; g1.rs_mb = rp;
-            }
+            g1.A = dout; g1.a_row_map = (const int32_t*)(lay_of(b0) + p.ly_prow_token);
+            g1.map_mb = (int64_t)p.lay_bytes / 4;
+            g1.row_scale = roww; g1.rs_mb = rp;
             g1.lda = H;
             g1.B = Wdc; g1.b_stride = (int64_t)I * H;
             g1.C = dH; g1.ldc = I; g1.N = I; g1.K = H;
