@@ -219,11 +219,13 @@ void launch_swiglu_bwd(const SwigluBwdArgs& a, int rpad, hipStream_t stream) {
 // One workgroup per token of a minibatch: gate gradients, softmax backward and
 //   dx[t] = sum_j dX[prow_j] (+ dX[shared row]) + sum_j dsel_j * WrT[idx_j]
 constexpr int kRdThreads = 128;
+constexpr int kRdPartBlock = 128;  // gate-gradient partials staged per pass
 
 __global__ __launch_bounds__(kRdThreads) void rdispatch_kernel(RdispArgs p) {
     __shared__ int s_row[kMaxTopK + 1];
     __shared__ int s_idx[kMaxTopK];
     __shared__ float s_w[kMaxTopK], s_dg[kMaxTopK], s_ds[kMaxTopK];
+    __shared__ float s_part[kMaxTopK][kRdPartBlock + 1];
     const int tl = blockIdx.x, t = p.t0 + tl, tid = threadIdx.x;
     const int k = p.k;
     if (tid < k + p.with_shared) s_row[tid] = p.tok_prow[(int64_t)tl * p.ld + tid];
@@ -232,12 +234,22 @@ __global__ __launch_bounds__(kRdThreads) void rdispatch_kernel(RdispArgs p) {
         s_w[tid] = p.topk_w[(int64_t)t * k + tid];
     }
     __syncthreads();
-    if (tid < k) {  // d out / d w[t,j]: the block partials in column order
-        const float* src = p.dgp + (int64_t)s_row[tid] * p.nhb;
-        float g = 0.0f;
-        for (int hb = 0; hb < p.nhb; ++hb) g = g + src[hb];
-        s_dg[tid] = g;
+    // d out / d w[t,j]: the block partials of slot j added in column order.
+    // All threads stage them in LDS with independent loads first, so the
+    // ordered sum waits on no chain of global loads.
+    float g = 0.0f;
+    for (int hb0 = 0; hb0 < p.nhb; hb0 += kRdPartBlock) {
+        const int nb = min(kRdPartBlock, p.nhb - hb0);
+        for (int i = tid; i < k * nb; i += kRdThreads) {
+            const int j = i / nb, hb = i - j * nb;
+            s_part[j][hb] = p.dgp[(int64_t)s_row[j] * p.nhb + hb0 + hb];
+        }
+        __syncthreads();
+        if (tid < k)
+            for (int hb = 0; hb < nb; ++hb) g = g + s_part[tid][hb];
+        __syncthreads();
     }
+    if (tid < k) s_dg[tid] = g;
     __syncthreads();
     if (tid == 0) {
         float dot = 0.0f;
