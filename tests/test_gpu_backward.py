@@ -25,6 +25,11 @@ BWD_CASES = [
     _wl("bwd_tiles", T=700, H=512, I=256, E=4, k=3, minibatch=256),
     _wl("bwd_k1", T=96, H=256, I=128, E=5, k=1),
     _wl("bwd_k64", T=200, H=64, I=64, E=4, k=2, minibatch=128, shared_expert=True),  # one K stage per GEMM
+    # backward chunks (minibatches per input-gradient GEMM launch, about 5120
+    # tokens): two chunks of two minibatches, the last minibatch ragged ...
+    _wl("bwd_chunks2", T=7000, H=256, I=128, E=8, k=2, minibatch=2000, router_bias="normal"),
+    # ... and three chunks of one minibatch
+    _wl("bwd_chunks1", T=6000, H=256, I=128, E=8, k=2, minibatch=2600),
 ]
 
 

@@ -29,6 +29,9 @@ MXB_CASES = [
     _wl("mxb_tiles", T=700, H=512, I=256, E=4, k=3, minibatch=256, router_bias="zipf"),
     _wl("mxb_wide", T=256, H=256, I=128, E=4, k=2, minibatch=128, router_bias="normal", wide_range=True),
     _wl("mxb_k64", T=200, H=64, I=64, E=4, k=2, minibatch=128, shared_expert=True),  # half stages only
+    # backward chunks: two of two minibatches; with the shared expert one chunk of five
+    _wl("mxb_chunks2", T=7000, H=256, I=128, E=8, k=2, minibatch=2000, router_bias="zipf"),
+    _wl("mxb_chunks_shared", T=5000, H=256, I=128, E=8, k=2, minibatch=1200, shared_expert=True),
 ]
 
 
