@@ -84,6 +84,18 @@ def test_query_sizes_automatic_minibatch_and_shared_expert():
     assert b.packed_weights > a.packed_weights and b.workspace_fwd > a.workspace_fwd
 
 
+def test_diag_mfma_loop_rejects_bad_arguments():
+    lib = moe.lib()
+    fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: validation fails first
+    assert lib.moe_diag_mfma_loop(2, fake, 1 << 16, 256, 16, fake, fake, None) == moe.MOE_E_INVALID
+    assert lib.moe_diag_mfma_loop(0, None, 1 << 16, 256, 16, fake, fake, None) == moe.MOE_E_INVALID
+    assert lib.moe_diag_mfma_loop(0, fake, 1024, 256, 16, fake, fake, None) == moe.MOE_E_INVALID
+    assert lib.moe_diag_mfma_loop(1, fake, 1 << 16, 0, 16, fake, fake, None) == moe.MOE_E_INVALID
+    assert lib.moe_diag_mfma_loop(1, fake, 1 << 16, 256, 0, fake, fake, None) == moe.MOE_E_INVALID
+    assert lib.moe_diag_mfma_loop(0, ctypes.c_void_p((1 << 20) + 8), 1 << 16, 256, 16, fake, fake,
+                                  None) == moe.MOE_E_INVALID
+
+
 def test_null_pointers_are_rejected_before_any_launch():
     lib = moe.lib()
     cfg = moe.make_cfg(64, 128, 64, 8, 2)
