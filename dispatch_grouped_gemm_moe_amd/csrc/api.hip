@@ -20,6 +20,7 @@ constexpr int kPadShare = 16;      // automatic minibatch: expected tile padding
 constexpr int kCommWorkers = 0;    // layer kernel: combine as tiles of the GEMM workgroups (no dedicated CUs)
 constexpr int kGroupTokens = 8192; // layer kernel: tokens per GEMM phase (minibatches grouped up to this)
 constexpr int kBwdChunkTokens = 5120;  // backward: tokens per phase chunk (minibatches grouped up to this)
+constexpr int kBwdChunkTokensShared = 20480;  // the same with the shared expert
 constexpr int kMaxGroup = 4;
 constexpr uint64_t kSpinTicks = 200000000;  // 2 s at the 100 MHz s_memrealtime clock: bound of every device wait
 constexpr size_t kAlign = 256;
@@ -115,8 +116,10 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     const int g_auto = std::max(1, std::min({kMaxGroup, kGroupTokens / p->Mb, p->nmb}));
     // The backward runs its phases over chunks of minibatches of about
     // kBwdChunkTokens tokens; with the shared expert, whose GEMMs have only
-    // a minibatch's tokens each, over every minibatch at once.
-    p->bchunk = (c->flags & MOE_F_SHARED_EXPERT) ? p->nmb : std::max(1, std::min(kBwdChunkTokens / p->Mb, p->nmb));
+    // a minibatch's tokens each, of up to kBwdChunkTokensShared (every
+    // minibatch at once for 16384 tokens in minibatches of 2560).
+    const int chunk_tokens = (c->flags & MOE_F_SHARED_EXPERT) ? kBwdChunkTokensShared : kBwdChunkTokens;
+    p->bchunk = std::max(1, std::min(chunk_tokens / p->Mb, p->nmb));
     p->group = c->ring_slots > 0 ? std::max(1, std::min(c->ring_slots / 3, g_auto)) : g_auto;
     p->slots = c->ring_slots > 0 ? c->ring_slots : 3 * p->group;
     p->slots = std::min(p->slots, ceil_div(p->nmb, p->group) * p->group);  // no slot without a minibatch

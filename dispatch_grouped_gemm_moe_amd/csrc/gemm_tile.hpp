@@ -252,11 +252,10 @@ struct DenseK8 {
 };
 
 // How a tile treats the padding rows of an expert's last tile (with
-// p.rows_e): kPadNone runs every fragment; kPadHalf drops every wave's second
-// fragment row (tile rows 128..255) when the tile holds at most 128 valid
-// rows (two mainloop variants, uniform over the workgroup); kPadPerWave drops
-// each wave's fragments that hold only padding rows (three variants).
-constexpr int kPadNone = 0, kPadHalf = 1, kPadPerWave = 2;
+// p.rows_e): kPadNone runs every fragment; kPadPerWave drops each wave's
+// fragments that hold only padding rows (a mainloop variant per count of
+// valid fragments).
+constexpr int kPadNone = 0, kPadPerWave = 1;
 
 // One 256 x 256 output tile (expert e, M tile ml of the expert, N tile ntile)
 // of the bf16 grouped GEMM with its epilogue, by 512 threads; smem is the
@@ -291,13 +290,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs p, int e, int ml, int n
     if (kPad != kPadNone && p.rows_e) {
         // fragment i of this wave holds tile rows 128i + 32wm .. +31
         const int valid = p.rows_e[e] - ml * BM, w32 = __builtin_amdgcn_readfirstlane(wm) * 32;
-        nv = kPad == kPadHalf ? (valid > 128 ? 2 : 1) : (valid > 128 + w32 ? 2 : (valid > w32 ? 1 : 0));
+        nv = valid > 128 + w32 ? 2 : (valid > w32 ? 1 : 0);
     }
     if (kPad == kPadNone) {
         tile_mainloop8<2>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT2, DenseK8{});
-    } else if (kPad == kPadHalf) {
-        if (nv == 2) tile_mainloop8<2>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT2, DenseK8{});
-        else tile_mainloop8<1>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT2, DenseK8{});
     } else switch (nv) {
         case 2: tile_mainloop8<2>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT2, DenseK8{}); break;
         case 1: tile_mainloop8<1>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT2, DenseK8{}); break;

@@ -282,11 +282,6 @@ __device__ __forceinline__ void mx_gemm_tile(const MxGemmArgs p, int e, int ml, 
     }
     // fragment i of this wave holds tile rows 128i + 32wm .. +31
     const int valid = p.rows_e[e] - ml * BM;
-    if (kPad == kPadHalf) {
-        if (valid > 128) mx_tile_body<EPI, 2>(p, e, ml, ntile, smem);
-        else mx_tile_body<EPI, 1>(p, e, ml, ntile, smem);
-        return;
-    }
     const int w32 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 7) * 32;
     switch (valid > 128 + w32 ? 2 : (valid > w32 ? 1 : 0)) {
         case 2: mx_tile_body<EPI, 2>(p, e, ml, ntile, smem); break;
