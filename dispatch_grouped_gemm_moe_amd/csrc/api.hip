@@ -144,13 +144,13 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     if (p->mx) {
         const size_t E = c->E;
         p->pk_w1q = o; o = align_up(o + E * 2 * I * H);
-        p->pk_s1 = o; o = align_up(o + E * (H / 64) * 2 * I * 4);
+        p->pk_s1 = o; o = align_up(o + E * mx_groups(H) * 2 * I * 4);
         p->pk_w2q = o; o = align_up(o + E * H * I);
-        p->pk_s2 = o; o = align_up(o + E * (I / 64) * H * 4);
+        p->pk_s2 = o; o = align_up(o + E * mx_groups(I) * H * 4);
         p->pk_wdq = o; o = align_up(o + E * I * H);
-        p->pk_sd = o; o = align_up(o + E * (H / 64) * I * 4);
+        p->pk_sd = o; o = align_up(o + E * mx_groups(H) * I * 4);
         p->pk_wguq = o; o = align_up(o + E * H * 2 * I);
-        p->pk_sgu = o; o = align_up(o + E * (2 * I / 64) * H * 4);
+        p->pk_sgu = o; o = align_up(o + E * mx_groups(2 * I) * H * 4);
     }
     p->packed = o;
 
@@ -161,7 +161,7 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     o = align_up(p->ws_w + Tk * 4);
     if (p->mx) {
         p->ws_xq = o; o = align_up(o + (size_t)c->T * H);
-        p->ws_sx = o; o = align_up(o + (size_t)(H / 64) * c->T * 4);
+        p->ws_sx = o; o = align_up(o + (size_t)mx_groups(H) * c->T * 4);
     }
     {  // one minibatch's layout block (also used by the backward)
         size_t l = 0;
@@ -181,7 +181,7 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     p->sl_y = o; o = align_up(o + (size_t)p->rpad * H * 2);
     if (p->mx) {
         p->sl_hq = o; o = align_up(o + (size_t)p->rpad * I);
-        p->sl_sh = o; o = align_up(o + (size_t)(I / 64) * p->rpad * 4);
+        p->sl_sh = o; o = align_up(o + (size_t)mx_groups(I) * p->rpad * 4);
     }
     p->slot_bytes = o;
     p->ws_fwd = p->ws_slot0 + (size_t)p->slots * p->slot_bytes;
@@ -219,9 +219,9 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     p->wb_dwrp = o; o = align_up(o + (size_t)dwr_chunks(c->T) * H * c->E * 4);
     if (p->mx) {
         p->wb_dyq = o; o = align_up(o + nc * rp * H);
-        p->wb_sdy = o; o = align_up(o + nc * (H / 64) * rp * 4);
+        p->wb_sdy = o; o = align_up(o + nc * mx_groups(H) * rp * 4);
         p->wb_dguq = o; o = align_up(o + nc * rp * 2 * I);
-        p->wb_sdgu = o; o = align_up(o + nc * (2 * I / 64) * rp * 4);
+        p->wb_sdgu = o; o = align_up(o + nc * mx_groups(2 * I) * rp * 4);
     }
     p->ws_bwd = o;
     return MOE_OK;
@@ -330,13 +330,13 @@ moe_status moe_prepare_weights(const moe_cfg* cfg, const uint16_t* Wg, const uin
     if (p.mx) {  // E4M3 codes + E8M0 scales along each GEMM's K, expert by expert
         for (int e = 0; e < p.E; ++e) {
             launch_mx_quant(W1t + (size_t)e * 2 * I * H, 2 * p.I, p.H, 1, base + p.pk_w1q + (size_t)e * 2 * I * H,
-                            base + p.pk_s1 + (size_t)e * (H / 64) * 2 * I * 4, s);
+                            base + p.pk_s1 + (size_t)e * mx_groups(H) * 2 * I * 4, s);
             launch_mx_quant(W2t + (size_t)e * H * I, p.H, p.I, 1, base + p.pk_w2q + (size_t)e * H * I,
-                            base + p.pk_s2 + (size_t)e * (I / 64) * H * 4, s);
+                            base + p.pk_s2 + (size_t)e * mx_groups(I) * H * 4, s);
             launch_mx_quant(Wdc + (size_t)e * I * H, p.I, p.H, 1, base + p.pk_wdq + (size_t)e * I * H,
-                            base + p.pk_sd + (size_t)e * (H / 64) * I * 4, s);
+                            base + p.pk_sd + (size_t)e * mx_groups(H) * I * 4, s);
             launch_mx_quant(Wgu + (size_t)e * H * 2 * I, p.H, 2 * p.I, 1, base + p.pk_wguq + (size_t)e * H * 2 * I,
-                            base + p.pk_sgu + (size_t)e * (2 * I / 64) * H * 4, s);
+                            base + p.pk_sgu + (size_t)e * mx_groups(2 * I) * H * 4, s);
         }
     }
     if (p.shared) {
@@ -430,11 +430,11 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
     if (p.mx) {
         m1.A = xq; m1.lda = p.H; m1.SA = sx; m1.sa_kstride = (int64_t)p.T * 4;
         m1.B = pk + p.pk_w1q; m1.b_stride = (int64_t)2 * p.I * p.H;
-        m1.SB = pk + p.pk_s1; m1.sb_stride = (int64_t)(p.H / 64) * 2 * p.I * 4; m1.sb_kstride = (int64_t)2 * p.I * 4;
+        m1.SB = pk + p.pk_s1; m1.sb_stride = mx_groups(p.H) * 2 * p.I * 4; m1.sb_kstride = (int64_t)2 * p.I * 4;
         m1.N = 2 * p.I; m1.K = p.H; m1.e_begin = 0; m1.e_end = p.E; m1.cs_rows = p.rpad;
         m2.lda = p.I; m2.sa_kstride = (int64_t)p.rpad * 4;
         m2.B = pk + p.pk_w2q; m2.b_stride = (int64_t)p.H * p.I;
-        m2.SB = pk + p.pk_s2; m2.sb_stride = (int64_t)(p.I / 64) * p.H * 4; m2.sb_kstride = (int64_t)p.H * 4;
+        m2.SB = pk + p.pk_s2; m2.sb_stride = mx_groups(p.I) * p.H * 4; m2.sb_kstride = (int64_t)p.H * 4;
         m2.N = p.H; m2.K = p.I; m2.e_begin = 0; m2.e_end = p.E; m2.ldc = p.H;
     }
 
@@ -610,7 +610,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             rc.H = H; rc.k = k; rc.nhb = (int)nhb; rc.ldt = rp;
             // MXFP8: dY quantised from fp32 here (along H, the down input-gradient GEMM's K)
             rc.dYq = p.mx ? wsb + p.wb_dyq + j * rp * H : nullptr;
-            rc.sdY = p.mx ? wsb + p.wb_sdy + j * nhb * rp * 4 : nullptr;
+            rc.sdY = p.mx ? wsb + p.wb_sdy + j * mx_groups(H) * rp * 4 : nullptr;
             TIMED(MOE_K_GATHER, s, launch_rcomb_gather(rc, (int)rp, s));
         }
         if (p.mx) {
@@ -618,11 +618,11 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             m1.A = wsb + p.wb_dyq; m1.a_row_map = nullptr; m1.lda = H;
             m1.SA = wsb + p.wb_sdy; m1.sa_kstride = rp * 4;
             m1.B = pk + p.pk_wdq; m1.b_stride = (int64_t)I * H;
-            m1.SB = pk + p.pk_sd; m1.sb_stride = (int64_t)(H / 64) * I * 4; m1.sb_kstride = (int64_t)I * 4;
+            m1.SB = pk + p.pk_sd; m1.sb_stride = mx_groups(H) * I * 4; m1.sb_kstride = (int64_t)I * 4;
             m1.N = I; m1.K = H; m1.mt_start = mt_c; m1.hdr = nullptr; m1.e_begin = 0; m1.e_end = E;
             m1.C = nullptr; m1.ldc = I; m1.Cq = nullptr; m1.Cs = nullptr; m1.cs_rows = 0; m1.GU = nullptr;
             m1.Cf = dHf; m1.rows_e = rows_c;
-            m1.nmb = b1 - b0; m1.mt_ld = Et + 1; m1.a_mb = rp * H; m1.sa_mb = nhb * rp * 4; m1.c_mb = rp * I;
+            m1.nmb = b1 - b0; m1.mt_ld = Et + 1; m1.a_mb = rp * H; m1.sa_mb = mx_groups(H) * rp * 4; m1.c_mb = rp * I;
             TIMED(MOE_K_DGRAD_DOWN, s, launch_mx_gemm(m1, kEpiStore, grid, s));
         }
         if (e_bf16 < Et) {
@@ -652,7 +652,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             // MXFP8: fp32 inputs, dG|dU quantised here (along I, the gate|up input-gradient GEMM's K)
             sb.dHf = p.mx ? dHf + bh : nullptr; sb.GUf = p.mx ? (const float*)svb : nullptr;
             sb.dGUq = p.mx ? wsb + p.wb_dguq + 2 * bh : nullptr;
-            sb.sdGU = p.mx ? wsb + p.wb_sdgu + j * (2 * I / 64) * rp * 4 : nullptr;
+            sb.sdGU = p.mx ? wsb + p.wb_sdgu + j * mx_groups(2 * I) * rp * 4 : nullptr;
             TIMED(MOE_K_GATHER, s, launch_swiglu_bwd(sb, (int)rp, s));
         }
         if (p.mx) {
@@ -660,11 +660,11 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             m2.A = wsb + p.wb_dguq; m2.a_row_map = nullptr; m2.lda = 2 * I;
             m2.SA = wsb + p.wb_sdgu; m2.sa_kstride = rp * 4;
             m2.B = pk + p.pk_wguq; m2.b_stride = (int64_t)H * 2 * I;
-            m2.SB = pk + p.pk_sgu; m2.sb_stride = (int64_t)(2 * I / 64) * H * 4; m2.sb_kstride = (int64_t)H * 4;
+            m2.SB = pk + p.pk_sgu; m2.sb_stride = mx_groups(2 * I) * H * 4; m2.sb_kstride = (int64_t)H * 4;
             m2.N = H; m2.K = 2 * I; m2.mt_start = mt_c; m2.hdr = nullptr; m2.e_begin = 0; m2.e_end = E;
             m2.C = dXb; m2.ldc = H; m2.Cq = nullptr; m2.Cs = nullptr; m2.cs_rows = 0; m2.GU = nullptr;
             m2.Cf = nullptr; m2.rows_e = rows_c;
-            m2.nmb = b1 - b0; m2.mt_ld = Et + 1; m2.a_mb = rp * 2 * I; m2.sa_mb = (2 * I / 64) * rp * 4; m2.c_mb = rp * H;
+            m2.nmb = b1 - b0; m2.mt_ld = Et + 1; m2.a_mb = rp * 2 * I; m2.sa_mb = mx_groups(2 * I) * rp * 4; m2.c_mb = rp * H;
             TIMED(MOE_K_DGRAD_GATE_UP, s, launch_mx_gemm(m2, kEpiStore, grid, s));
         }
         if (e_bf16 < Et) {

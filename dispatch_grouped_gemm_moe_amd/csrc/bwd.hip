@@ -87,8 +87,7 @@ __global__ __launch_bounds__(256) void rcomb_gather_kernel(RcombArgs p) {
         sX[c0 + c][r] = f32_to_bf16_rne(xv[c]);
     }
     if (p.dYq)  // MXFP8 operand of the down input-gradient GEMM, from the fp32 values
-        mx_quant_row64(dyf, tid & 3, p.dYq + (int64_t)prow * p.H + h0,
-                       (uint32_t*)(p.sdY + ((int64_t)(h0 / 64) * p.ldt + prow) * 4));
+        mx_quant_row64(dyf, tid & 3, p.dYq + (int64_t)prow * p.H + h0, p.sdY, p.ldt, prow, h0 / 64, p.H / 64);
     if (p.dY) {
         intx4* dst = (intx4*)(p.dY + (int64_t)prow * p.H + h0 + c0);
 #pragma unroll
@@ -193,10 +192,8 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdArgs p) {
     pack16_bf16(dg, (intx4*)(p.dGU + prow * 2 * I + i0 + c0));
     pack16_bf16(du, (intx4*)(p.dGU + prow * 2 * I + I + i0 + c0));
     if (p.dGUq) {  // MXFP8 operand of the gate|up input-gradient GEMM, from the fp32 values
-        mx_quant_row64(dgf, tid & 3, p.dGUq + prow * 2 * I + i0,
-                       (uint32_t*)(p.sdGU + ((int64_t)(i0 / 64) * p.ldt + prow) * 4));
-        mx_quant_row64(duf, tid & 3, p.dGUq + prow * 2 * I + I + i0,
-                       (uint32_t*)(p.sdGU + ((int64_t)((I + i0) / 64) * p.ldt + prow) * 4));
+        mx_quant_row64(dgf, tid & 3, p.dGUq + prow * 2 * I + i0, p.sdGU, p.ldt, prow, i0 / 64, 2 * I / 64);
+        mx_quant_row64(duf, tid & 3, p.dGUq + prow * 2 * I + I + i0, p.sdGU, p.ldt, prow, (I + i0) / 64, 2 * I / 64);
     }
     __syncthreads();
     const int ic = tid >> 2, r0 = (tid & 3) * 16;

@@ -74,10 +74,18 @@ struct GemmArgs {
 
 enum GemmEpilogue { kEpiSwiGLU = 0, kEpiStore = 1 };
 
+// GEMM operand scale layout of MXFP8 rows of `cols` elements:
+// [mx_groups(cols)][rows][4] bytes, byte b of the dword of (group g, row) the
+// E8M0 scale of the row's 32-element block 4g + b (bytes past the row's last
+// block zero).  One dword per row thus covers the 128 K elements a GEMM stage
+// consumes, so a stage's scales of both operands are a single 4-byte load per
+// lane of the workgroup.
+__host__ __device__ constexpr int64_t mx_groups(int64_t cols) { return (cols + 127) / 128; }
+
 // MXFP8 grouped GEMM: E4M3 codes with E8M0 scales on both operands.
 // Codes: A rows [.][lda] bytes (gathered through a_row_map), B [Et][N][K] bytes.
-// Scales (one dword per row and 64-element K step, bytes 0 and 1 used):
-// SA + kt * sa_kstride + row * 4 and SB + e * sb_stride + kt * sb_kstride + n * 4.
+// Scales in the operand scale layout (one dword per row and 128-element K
+// group): SA + g * sa_kstride + row * 4 and SB + e * sb_stride + g * sb_kstride + n * 4.
 struct MxGemmArgs {
     const uint8_t* A;
     const int32_t* a_row_map;
@@ -95,7 +103,7 @@ struct MxGemmArgs {
     uint16_t* C;               // kEpiStore: bf16 [R_pad][ldc]
     int64_t ldc;
     uint8_t* Cq;               // kEpiSwiGLU: h codes [R_pad][N/2]
-    uint8_t* Cs;               // kEpiSwiGLU: h scales [N/2/64][cs_rows][4]
+    uint8_t* Cs;               // kEpiSwiGLU: h scales, operand layout [mx_groups(N/2)][cs_rows][4]
     int64_t cs_rows;
     float* GU;                 // kEpiSwiGLU, optional: fp32 g | u [R_pad][N] kept for the backward
     float* Cf;                 // kEpiStore, optional: fp32 output instead of C
@@ -107,7 +115,7 @@ struct MxGemmArgs {
 };
 void launch_mx_gemm(const MxGemmArgs& a, GemmEpilogue epi, int grid, hipStream_t stream);
 // bf16 [rows][cols] -> E4M3 codes [rows][cols] and E8M0 scales; layout 0:
-// [rows][cols/32], layout 1: [cols/64][rows][4] (bytes 0, 1 = blocks 2j, 2j+1).
+// [rows][cols/32], layout 1: the GEMM operand scale layout.
 // With hdr, rows from hdr->m_tiles * BM on are skipped.
 void launch_mx_quant(const uint16_t* src, int64_t rows, int cols, int layout, uint8_t* codes, uint8_t* scales,
                      hipStream_t stream, const LayoutHeader* hdr = nullptr);
@@ -156,7 +164,8 @@ struct SwigluBwdArgs {
     int I;
     int64_t ldt;
     // MXFP8: fp32 inputs instead of dH / GU, and dG | dU also quantised along
-    // I from fp32: codes [R_pad][2I], scales [2I/64][ldt][4]
+    // I from fp32: codes [R_pad][2I], scales in the operand layout
+    // [mx_groups(2I)][ldt][4]
     const float* dHf;
     const float* GUf;
     uint8_t* dGUq;
@@ -216,7 +225,7 @@ struct RcombArgs {
     int H, k, nhb;
     int64_t ldt;
     // MXFP8, optional: dY quantised along H from fp32, codes [R_pad][H],
-    // scales [H/64][ldt][4]
+    // scales in the operand layout [mx_groups(H)][ldt][4]
     uint8_t* dYq;
     uint8_t* sdY;
 };

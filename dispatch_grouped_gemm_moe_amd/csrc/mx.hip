@@ -26,9 +26,10 @@ namespace moe {
 
 // ---------------------------------------------------------------------------
 // quantiser: bf16 rows [rows][cols] -> E4M3 codes [rows][cols] + scales.
-// scale layout 0: [rows][cols/32] bytes.  Layout 1 (GEMM operand): [cols/64][rows][4]
-// bytes, bytes 0 and 1 holding the scales of blocks 2j and 2j+1, bytes 2, 3 zero.
-// One thread per 32-element block.
+// scale layout 0: [rows][cols/32] bytes.  Layout 1: the GEMM operand scale
+// layout [mx_groups(cols)][rows][4], byte b of group g the scale of block 4g + b.
+// One thread per 32-element block; the thread of a row's last block also
+// zeroes the bytes of its group past the row's end.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restrict__ src, int64_t rows, int cols,
                                                        int layout, uint8_t* __restrict__ codes,
@@ -66,9 +67,10 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restric
     if (layout == 0) {
         scales[r * nb + b] = sc;
     } else {
-        uint8_t* d = scales + ((int64_t)(b >> 1) * rows + r) * 4;
-        d[b & 1] = sc;
-        if ((b & 1) == 0) { d[2] = 0; d[3] = 0; }
+        uint8_t* d = scales + ((int64_t)(b >> 2) * rows + r) * 4;
+        d[b & 3] = sc;
+        if (b + 1 == nb)
+            for (int z = (b & 3) + 1; z < 4; ++z) d[z] = 0;
     }
 }
 

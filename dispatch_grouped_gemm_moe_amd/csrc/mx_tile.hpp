@@ -13,14 +13,15 @@ namespace moe {
 // waves per SIMD, each wave a 64 x 128 block of 2 x 4 fragments of
 // v_mfma_scale_f32_32x32x64_f8f6f4 (as the bf16 tile).  A stage holds two
 // 64-deep K steps: A and B codes as 128-byte rows (whole-line loads, 8 lanes
-// per row), then the E8M0 scale dwords of both K steps for A and for B;
-// two stages (136 KB).  An odd number of K steps ends on a half stage whose
+// per row), then one scale dword per A row and per B row (the operand scale
+// layout's group: the four E8M0 block scales of the stage's 128 columns);
+// two stages (132 KB).  An odd number of K steps ends on a half stage whose
 // second K step repeats the last one in LDS and gets no MFMAs.
 constexpr int kMxRow = 128;                               // code bytes of a row per stage
 constexpr int kMxStageA = BM * kMxRow;                    // 32 KB
-constexpr int kMxStageSA = (BM + BN) * kMxRow;            // scales: [2 K steps][256 rows] dwords
-constexpr int kMxStageSB = kMxStageSA + 2 * BM * 4;
-constexpr int kMxStageBytes = kMxStageSB + 2 * BN * 4;    // 68 KB
+constexpr int kMxStageSA = (BM + BN) * kMxRow;            // scales: [256 A rows] dwords
+constexpr int kMxStageSB = kMxStageSA + BM * 4;           //         [256 B rows] dwords
+constexpr int kMxStageBytes = kMxStageSB + BN * 4;        // 66 KB
 constexpr int kMxStages = 2;
 constexpr int kMxSmem = kMxStages * kMxStageBytes;
 constexpr int kEpiPitch8 = 8 * 16 + 16;  // staged codes: 128 bytes of data per row
@@ -46,8 +47,9 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
 
     // Code loads: instruction i fills tile rows 32*wave + 8i .. +7 (lane/8 the
     // row, lane%8 the fixed LDS chunk, loading the logical chunk stored there;
-    // chunks 4..7 hold the stage's second K step).  Scale loads: lane L =
-    // 64*wave + lane takes K step L/256 of row L%256, one dword for A, one for B.
+    // chunks 4..7 hold the stage's second K step).  Scale load: waves 0..3
+    // take the dwords of A rows 64*wave + lane, waves 4..7 those of B rows
+    // 64*(wave-4) + lane, which land as the stage's SA and SB arrays.
     const char* a_base = (const char*)p.A;
     const char* b_base = (const char*)(p.B + (int64_t)e * p.b_stride);
     uint32_t aoff[4], boff[4];
@@ -62,22 +64,28 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
         aoff[i] = (uint32_t)((int64_t)arow * p.lda + lchunk * 16);
         boff[i] = (uint32_t)((int64_t)min(n0 + r, p.N - 1) * p.K + lchunk * 16);
     }
-    const int sl = wave * 64 + lane, sks = sl >> 8, srow = sl & 255;
-    const int sarow = p.a_row_map ? p.a_row_map[prow0 + srow] : prow0 + srow;
-    const char* sa_lane = (const char*)p.SA + (int64_t)sarow * 4;
-    const char* sb_lane = (const char*)(p.SB + (int64_t)e * p.sb_stride) + (int64_t)min(n0 + srow, p.N - 1) * 4;
+    const int srow = (wave & 3) * 64 + lane;
+    const char* s_lane;
+    int64_t s_kstride;
+    if (wave >= 4) {
+        s_lane = (const char*)(p.SB + (int64_t)e * p.sb_stride) + (int64_t)min(n0 + srow, p.N - 1) * 4;
+        s_kstride = p.sb_kstride;
+    } else {
+        const int sarow = p.a_row_map ? p.a_row_map[prow0 + srow] : prow0 + srow;
+        s_lane = (const char*)p.SA + (int64_t)sarow * 4;
+        s_kstride = p.sa_kstride;
+    }
 
     // Loads past the last stage repeat it (into the slot no wave reads any
     // more), so they need no branch and the waits are constants.  On a half
     // stage (odd K steps) the second K step's code chunks and scales repeat
-    // the first's.
+    // the first's (and the upper half of the stage's scale dwords is zero).
     auto issue = [&](int s_, int slot) {
         const int s = s_ < KS ? s_ : KS - 1;
         // a half stage's second K step repeats the first: the lanes of the
         // upper chunks step back 64 bytes
         const int back = 2 * s + 1 >= KT ? himask : 0;
         const uint32_t kb = (uint32_t)s * 128;
-        const int kts = min(2 * s + sks, KT - 1);
         uint8_t* st = smem + slot * kMxStageBytes;
         uint8_t* base = st + (wave * 32) * kMxRow;
 #pragma unroll
@@ -88,17 +96,15 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
         for (int i = 0; i < 4; ++i)
             __builtin_amdgcn_global_load_lds((gbl_cvoid*)(b_base + boff[i] + kb - ((back >> i) & 1) * 64),
                                              (lds_void*)(base + kMxStageA + i * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((gbl_cvoid*)(sa_lane + (int64_t)kts * p.sa_kstride),
+        __builtin_amdgcn_global_load_lds((gbl_cvoid*)(s_lane + (int64_t)s * s_kstride),
                                          (lds_void*)(st + kMxStageSA + wave * 256), 4, 0, 0);
-        __builtin_amdgcn_global_load_lds((gbl_cvoid*)(sb_lane + (int64_t)kts * p.sb_kstride),
-                                         (lds_void*)(st + kMxStageSB + wave * 256), 4, 0, 0);
     };
     const int fr = lane & 31, half = lane >> 5;
     const int fsw = swz8(fr);  // a fragment's rows differ from fr by multiples of 32
     const int arow_b = (wm * 32 + fr) * kMxRow, brow_b = kMxStageA + (wn * 128 + fr) * kMxRow;
     // fragments of K step ks (0, 1) of the stage in `slot`: per lane, bytes
     // 0..15 from the row's first 32-block of the K step, 16..31 from its second;
-    // the scale of (row, block) from byte `half` of the row's scale dword
+    // the scale of (row, block) from byte 2 * ks + half of the row's scale dword
     auto frags = [&](int slot, int ks, intx8 (&a)[2], intx8 (&b)[4], int (&sa)[2], int (&sb)[4]) {
         const uint8_t* st = smem + slot * kMxStageBytes;
         const int pc0 = ((4 * ks + half) ^ fsw) * 16, pc1 = ((4 * ks + 2 + half) ^ fsw) * 16;
@@ -107,14 +113,14 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
             const intx4 lo4 = *(const intx4*)(st + arow_b + i * 128 * kMxRow + pc0);
             const intx4 hi4 = *(const intx4*)(st + arow_b + i * 128 * kMxRow + pc1);
             a[i] = intx8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-            sa[i] = st[kMxStageSA + ks * 1024 + (i * 128 + wm * 32 + fr) * 4 + half];
+            sa[i] = st[kMxStageSA + (i * 128 + wm * 32 + fr) * 4 + 2 * ks + half];
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const intx4 lo4 = *(const intx4*)(st + brow_b + j * 32 * kMxRow + pc0);
             const intx4 hi4 = *(const intx4*)(st + brow_b + j * 32 * kMxRow + pc1);
             b[j] = intx8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-            sb[j] = st[kMxStageSB + ks * 1024 + (wn * 128 + j * 32 + fr) * 4 + half];
+            sb[j] = st[kMxStageSB + (wn * 128 + j * 32 + fr) * 4 + 2 * ks + half];
         }
     };
     floatx16 acc[2][4];
@@ -134,20 +140,20 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
                                                                              sa[i]);
     };
 
-    // Ring protocol (stage j in slot j % 2, 10 direct-to-LDS loads per lane and
+    // Ring protocol (stage j in slot j % 2, 9 direct-to-LDS loads per lane and
     // stage): the prologue issues stages 0 and 1 and waits for stage 0
-    // (vmcnt(10)); stage s reads and runs its first K step, reads the second's
+    // (vmcnt(9)); stage s reads and runs its first K step, reads the second's
     // fragments, waits for stage s+1 (vmcnt(0)) and its own LDS reads,
     // barrier, refills its slot with stage s+2 under the second K step's
     // MFMAs.  Fragments are single-buffered (the scaled operands are twice the
     // bf16 ones and two waves share a SIMD's registers): a wave waiting on its
     // reads leaves the matrix core to the SIMD's other wave.
-    static_assert(kMxStages == 2, "the vmcnt immediates below assume 2 stages of 10 loads");
+    static_assert(kMxStages == 2, "the vmcnt immediates below assume 2 stages of 9 loads");
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     issue(0, 0);
     issue(1, 1);
-    asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
     __syncthreads();
     intx8 fa[2], fb[4];
     int fsa[2], fsb[4];
@@ -161,7 +167,7 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
         __syncthreads();
         issue(s + 2, slot);
         if (2 * s + 1 < KT) mfmas(fa, fb, fsa, fsb);
-        Interleave<4 * NV, 10, 0>::run();
+        Interleave<4 * NV, 9, 0>::run();
         __builtin_amdgcn_sched_barrier(0);
         slot ^= 1;
     }
@@ -215,12 +221,10 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
                         }
                     }
                 }
-                // the row's two block scales of this 64-column pair, as the GEMM
-                // operand layout's dword {block 0, block 1, 0, 0}; lanes 0..31
-                // hold 32 consecutive rows, so the stores are one 128-byte run
+                // the row's two block scales of this 64-column pair, into the
+                // operand scale layout; lanes 0..31 hold 32 consecutive rows
                 const int64_t row = prow0 + bl * 64 + rl;
-                if (live && half == 0)
-                    *(uint32_t*)(p.Cs + ((int64_t)((hc0 + wn * 64) >> 6) * p.cs_rows + row) * 4) = sdw;
+                if (live && half == 0) mx_store_scale_pair(p.Cs, p.cs_rows, row, (hc0 + wn * 64) >> 6, I / 64, sdw);
             }
             __syncthreads();
             const int64_t row0 = prow0 + bl * 64;

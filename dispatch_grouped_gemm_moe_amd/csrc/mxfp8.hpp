@@ -31,11 +31,25 @@ __device__ __forceinline__ intx4 fp8x16(const float* v, int e) {
     return o;
 }
 
+// The two scales (pair = block 2j | block 2j+1 << 8) of 64-element block j of
+// a row in the GEMM operand scale layout (scales [groups][rows][4]): half j % 2
+// of the row's dword of group j / 2.  The last block of a row with an odd
+// number of them writes the whole dword, its upper half zero.
+__device__ __forceinline__ void mx_store_scale_pair(uint8_t* scales, int64_t rows, int64_t row, int j, int nj,
+                                                    uint32_t pair) {
+    uint8_t* d = scales + ((int64_t)(j >> 1) * rows + row) * 4;
+    if ((j & 1) == 0 && j + 1 == nj)
+        *(uint32_t*)d = pair;
+    else
+        *(uint16_t*)(d + 2 * (j & 1)) = (uint16_t)pair;
+}
+
 // A row's 64 values held as 16 per thread by four consecutive lanes (lane % 4 =
 // 16-column group): quantise along the row, write the 64 codes at `codes` (this
-// lane's 16 at codes + 16 * (lane % 4)) and the two block scales as one dword
-// {block 0, block 1, 0, 0} at `scale_dword` (GEMM operand scale layout).
-__device__ __forceinline__ void mx_quant_row64(const float* v, int lane4, uint8_t* codes, uint32_t* scale_dword) {
+// lane's 16 at codes + 16 * (lane % 4)) and the two block scales as 64-element
+// block j of nj of row `row` in the operand scale layout `scales` [.][rows][4].
+__device__ __forceinline__ void mx_quant_row64(const float* v, int lane4, uint8_t* codes, uint8_t* scales,
+                                               int64_t rows, int64_t row, int j, int nj) {
     float m = 0.0f;
 #pragma unroll
     for (int c = 0; c < 16; ++c) m = fmaxf(m, fabsf(v[c]));
@@ -43,7 +57,7 @@ __device__ __forceinline__ void mx_quant_row64(const float* v, int lane4, uint8_
     const int e = mx_scale_exp(m);
     *(intx4*)(codes + 16 * lane4) = fp8x16(v, e);
     const int e_hi = __shfl_xor(e, 2, kWave);
-    if (lane4 == 0) *scale_dword = (uint32_t)(e + 127) | ((uint32_t)(e_hi + 127) << 8);
+    if (lane4 == 0) mx_store_scale_pair(scales, rows, row, j, nj, (uint32_t)(e + 127) | ((uint32_t)(e_hi + 127) << 8));
 }
 
 }  // namespace moe
