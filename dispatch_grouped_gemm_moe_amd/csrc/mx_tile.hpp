@@ -103,8 +103,10 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
     const int fsw = swz8(fr);  // a fragment's rows differ from fr by multiples of 32
     const int arow_b = (wm * 32 + fr) * kMxRow, brow_b = kMxStageA + (wn * 128 + fr) * kMxRow;
     // fragments of K step ks (0, 1) of the stage in `slot`: per lane, bytes
-    // 0..15 from the row's first 32-block of the K step, 16..31 from its second;
-    // the scale of (row, block) from byte 2 * ks + half of the row's scale dword
+    // 0..15 from the row's first 32-block of the K step, 16..31 from its second.
+    // With ks = 0 also the rows' scale dwords, shifted right by 8 * half: then
+    // byte 2 * ks of the register is the scale of (row, block half) of K step
+    // ks, which the MFMA's scale byte select takes as an immediate.
     auto frags = [&](int slot, int ks, intx8 (&a)[2], intx8 (&b)[4], int (&sa)[2], int (&sb)[4]) {
         const uint8_t* st = smem + slot * kMxStageBytes;
         const int pc0 = ((4 * ks + half) ^ fsw) * 16, pc1 = ((4 * ks + 2 + half) ^ fsw) * 16;
@@ -113,14 +115,14 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
             const intx4 lo4 = *(const intx4*)(st + arow_b + i * 128 * kMxRow + pc0);
             const intx4 hi4 = *(const intx4*)(st + arow_b + i * 128 * kMxRow + pc1);
             a[i] = intx8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-            sa[i] = st[kMxStageSA + (i * 128 + wm * 32 + fr) * 4 + 2 * ks + half];
+            if (ks == 0) sa[i] = (int)(*(const uint32_t*)(st + kMxStageSA + (i * 128 + wm * 32 + fr) * 4) >> (8 * half));
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const intx4 lo4 = *(const intx4*)(st + brow_b + j * 32 * kMxRow + pc0);
             const intx4 hi4 = *(const intx4*)(st + brow_b + j * 32 * kMxRow + pc1);
             b[j] = intx8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-            sb[j] = st[kMxStageSB + (wn * 128 + j * 32 + fr) * 4 + 2 * ks + half];
+            if (ks == 0) sb[j] = (int)(*(const uint32_t*)(st + kMxStageSB + (wn * 128 + j * 32 + fr) * 4) >> (8 * half));
         }
     };
     floatx16 acc[2][4];
@@ -131,13 +133,15 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
     // B is the first operand (with its scales), so each accumulator holds the
     // transposed block: element 4q + s of fragment (i, j) of lane l sits in
     // tile row 128i + 32wm + l%32 and column wn*128 + 32j + 8q + 4(l/32) + s.
-    auto mfmas = [&](const intx8 (&a)[2], const intx8 (&b)[4], const int (&sa)[2], const int (&sb)[4]) {
+    // ksc: the K step (std::integral_constant), whose scales are byte 2 * ks.
+    auto mfmas = [&](auto ksc, const intx8 (&a)[2], const intx8 (&b)[4], const int (&sa)[2], const int (&sb)[4]) {
+        constexpr int sel = 2 * decltype(ksc)::value;
 #pragma unroll
         for (int i = 0; i < NV; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a[i], acc[i][j], 0, 0, 0, sb[j], 0,
-                                                                             sa[i]);
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a[i], acc[i][j], 0, 0, sel, sb[j],
+                                                                             sel, sa[i]);
     };
 
     // Ring protocol (stage j in slot j % 2, 9 direct-to-LDS loads per lane and
@@ -160,13 +164,13 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
     int slot = 0;
     for (int s = 0; s < KS; ++s) {
         frags(slot, 0, fa, fb, fsa, fsb);
-        mfmas(fa, fb, fsa, fsb);
+        mfmas(std::integral_constant<int, 0>{}, fa, fb, fsa, fsb);
         __builtin_amdgcn_sched_barrier(0);
         frags(slot, 1, fa, fb, fsa, fsb);
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         __syncthreads();
         issue(s + 2, slot);
-        if (2 * s + 1 < KT) mfmas(fa, fb, fsa, fsb);
+        if (2 * s + 1 < KT) mfmas(std::integral_constant<int, 1>{}, fa, fb, fsa, fsb);
         Interleave<4 * NV, 9, 0>::run();
         __builtin_amdgcn_sched_barrier(0);
         slot ^= 1;
