@@ -648,6 +648,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             SwigluBwdArgs sb{};
             sb.dH = p.mx ? nullptr : dH + bh; sb.GU = (const uint16_t*)svb; sb.hdr = (LayoutHeader*)(lay + p.ly_hdr);
             sb.dGU = dGU + 2 * bh; sb.dGUT = dGUT_all + (size_t)b * 2 * I * rp; sb.HT = HT_all + (size_t)b * I * rp;
+            sb.dgu_tile0 = mt_all + (size_t)b * (Et + 1) + e_bf16;  // bf16: tile 0 (every row)
             sb.I = I; sb.ldt = rp;
             // MXFP8: fp32 inputs, dG|dU quantised here (along I, the gate|up input-gradient GEMM's K)
             sb.dHf = p.mx ? dHf + bh : nullptr; sb.GUf = p.mx ? (const float*)svb : nullptr;

@@ -143,8 +143,10 @@ __device__ __forceinline__ void pack16_bf16(const uint16_t* v, intx4* dst) {
 }
 
 // SwiGLU backward, one workgroup per 64 padded rows x 64 intermediate columns:
-// row-major dG | dU for the input-gradient GEMM, transposed dG | dU and h for
-// the weight-gradient GEMMs (through LDS, so every store is coalesced).
+// row-major dG | dU for the bf16 input-gradient GEMM (only the rows of the
+// experts it runs: the MXFP8 experts take the quantised copy), transposed
+// dG | dU and h for the weight-gradient GEMMs (through LDS, so every store is
+// coalesced).
 __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdArgs p) {
     __shared__ uint16_t sG[kTile][kTile + 2];
     __shared__ uint16_t sU[kTile][kTile + 2];
@@ -189,8 +191,10 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdArgs p) {
         sU[c0 + c][r] = du[c];
         sH[c0 + c][r] = hh[c];
     }
-    pack16_bf16(dg, (intx4*)(p.dGU + prow * 2 * I + i0 + c0));
-    pack16_bf16(du, (intx4*)(p.dGU + prow * 2 * I + I + i0 + c0));
+    if (prow >= (int64_t)*p.dgu_tile0 * BM) {
+        pack16_bf16(dg, (intx4*)(p.dGU + prow * 2 * I + i0 + c0));
+        pack16_bf16(du, (intx4*)(p.dGU + prow * 2 * I + I + i0 + c0));
+    }
     if (p.dGUq) {  // MXFP8 operand of the gate|up input-gradient GEMM, from the fp32 values
         mx_quant_row64(dgf, tid & 3, p.dGUq + prow * 2 * I + i0, p.sdGU, p.ldt, prow, i0 / 64, 2 * I / 64);
         mx_quant_row64(duf, tid & 3, p.dGUq + prow * 2 * I + I + i0, p.sdGU, p.ldt, prow, (I + i0) / 64, 2 * I / 64);

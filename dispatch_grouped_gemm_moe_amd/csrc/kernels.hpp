@@ -158,7 +158,8 @@ struct SwigluBwdArgs {
     const uint16_t* dH;        // [R_pad][I]
     const uint16_t* GU;        // [R_pad][2I]
     const LayoutHeader* hdr;
-    uint16_t* dGU;             // [R_pad][2I]  dG | dU
+    uint16_t* dGU;             // [R_pad][2I]  dG | dU, rows from tile *dgu_tile0 on
+    const int32_t* dgu_tile0;  // first tile of the experts whose input gradient runs in bf16
     uint16_t* dGUT;            // [2I][ldt]    transposed dG | dU
     uint16_t* HT;              // [I][ldt]     transposed h
     int I;
