@@ -181,10 +181,15 @@ def main():
     flops = {"gemm_gate_up": 4 * hr, "gemm_down": 2 * hr}
     if bwd:
         flops.update({"dgrad_down": 2 * hr, "dgrad_gate_up": 4 * hr, "wgrad": 6 * hi})
-    if mx and shared_rows:
-        flops["shared_gemm"] = (12.0 if bwd else 6.0) * H * I * shared_rows
-    if kt["layer"][1] > 0:  # the persistent layer kernel runs both forward GEMMs (and combine)
-        flops["layer"] = flops.pop("gemm_gate_up") + flops.pop("gemm_down")
+    shared_fwd = 6.0 * H * I * shared_rows if mx else 0.0
+    if mx and shared_rows and bwd:  # the shared expert's bf16 input-gradient GEMMs
+        flops["shared_gemm"] = 6.0 * H * I * shared_rows
+    if kt["layer"][1] > 0:
+        # the persistent layer kernel runs both forward GEMMs (and combine),
+        # under MXFP8 with the shared expert's bf16 tiles in the same launch
+        flops["layer"] = flops.pop("gemm_gate_up") + flops.pop("gemm_down") + shared_fwd
+    elif shared_fwd:  # per-GEMM forward: the shared expert's launches are timed as their own kind
+        flops["shared_gemm"] = flops.get("shared_gemm", 0.0) + shared_fwd
     symbol = {"gemm_gate_up": "mx_gemm_kernel<0>" if mx else "grouped_gemm_kernel<0>",
               "gemm_down": "mx_gemm_kernel<1>" if mx else "grouped_gemm_kernel<1>",
               "dgrad_down": "mx_gemm_kernel<1>" if mx else "grouped_gemm_kernel<1>",

@@ -611,6 +611,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             // MXFP8: dY quantised from fp32 here (along H, the down input-gradient GEMM's K)
             rc.dYq = p.mx ? wsb + p.wb_dyq + j * rp * H : nullptr;
             rc.sdY = p.mx ? wsb + p.wb_sdy + j * mx_groups(H) * rp * 4 : nullptr;
+            rc.dyq_tile_end = mt_all + (size_t)b * (Et + 1) + e_bf16;
             TIMED(MOE_K_GATHER, s, launch_rcomb_gather(rc, (int)rp, s));
         }
         if (p.mx) {

@@ -24,6 +24,8 @@ constexpr int kTile = 64;
 //   row_w[prow]   = w (0 on padding rows), if row_w is set
 //   dYT[h][prow]  = the same, transposed (weight-gradient operand)
 //   xgT[h][prow]  = x[t][h], transposed (weight-gradient operand)
+//   dYq, sdY      = MXFP8 codes and scales of w * dout[t] (rows before tile
+//                   *dyq_tile_end), if dYq is set
 //   dgp[prow][hb] = sum over the block's 64 columns of dout[t][h] * Y[prow][h]
 //                   (routed rows; in column order, then a fixed pair tree)
 //   dsel[prow]    = 0 (filled for routed rows by the reverse-dispatch)
@@ -86,7 +88,8 @@ __global__ __launch_bounds__(256) void rcomb_gather_kernel(RcombArgs p) {
         sY[c0 + c][r] = dy[c];
         sX[c0 + c][r] = f32_to_bf16_rne(xv[c]);
     }
-    if (p.dYq)  // MXFP8 operand of the down input-gradient GEMM, from the fp32 values
+    // MXFP8 operand of the down input-gradient GEMM, from the fp32 values
+    if (p.dYq && prow < *p.dyq_tile_end * BM)
         mx_quant_row64(dyf, tid & 3, p.dYq + (int64_t)prow * p.H + h0, p.sdY, p.ldt, prow, h0 / 64, p.H / 64);
     if (p.dY) {
         intx4* dst = (intx4*)(p.dY + (int64_t)prow * p.H + h0 + c0);

@@ -226,9 +226,11 @@ struct RcombArgs {
     int H, k, nhb;
     int64_t ldt;
     // MXFP8, optional: dY quantised along H from fp32, codes [R_pad][H],
-    // scales in the operand layout [mx_groups(H)][ldt][4]
+    // scales in the operand layout [mx_groups(H)][ldt][4]; only rows before
+    // tile *dyq_tile_end (the experts whose input gradient runs in MXFP8)
     uint8_t* dYq;
     uint8_t* sdY;
+    const int32_t* dyq_tile_end;
 };
 void launch_rcomb_gather(const RcombArgs& a, int rpad, hipStream_t stream);
 
