@@ -102,28 +102,26 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
     const int fr = lane & 31, half = lane >> 5;
     const int fsw = swz8(fr);  // a fragment's rows differ from fr by multiples of 32
     const int arow_b = (wm * 32 + fr) * kMxRow, brow_b = kMxStageA + (wn * 128 + fr) * kMxRow;
-    // fragments of K step ks (0, 1) of the stage in `slot`: per lane, bytes
+    // Fragments of K step ks (0, 1) of the stage in `slot`: per lane, bytes
     // 0..15 from the row's first 32-block of the K step, 16..31 from its second.
     // With ks = 0 also the rows' scale dwords, shifted right by 8 * half: then
     // byte 2 * ks of the register is the scale of (row, block half) of K step
     // ks, which the MFMA's scale byte select takes as an immediate.
-    auto frags = [&](int slot, int ks, intx8 (&a)[2], intx8 (&b)[4], int (&sa)[2], int (&sb)[4]) {
+    auto read_a = [&](int slot, int ks, int i, intx8& a, int& sa) {
         const uint8_t* st = smem + slot * kMxStageBytes;
         const int pc0 = ((4 * ks + half) ^ fsw) * 16, pc1 = ((4 * ks + 2 + half) ^ fsw) * 16;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const intx4 lo4 = *(const intx4*)(st + arow_b + i * 128 * kMxRow + pc0);
-            const intx4 hi4 = *(const intx4*)(st + arow_b + i * 128 * kMxRow + pc1);
-            a[i] = intx8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-            if (ks == 0) sa[i] = (int)(*(const uint32_t*)(st + kMxStageSA + (i * 128 + wm * 32 + fr) * 4) >> (8 * half));
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const intx4 lo4 = *(const intx4*)(st + brow_b + j * 32 * kMxRow + pc0);
-            const intx4 hi4 = *(const intx4*)(st + brow_b + j * 32 * kMxRow + pc1);
-            b[j] = intx8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-            if (ks == 0) sb[j] = (int)(*(const uint32_t*)(st + kMxStageSB + (wn * 128 + j * 32 + fr) * 4) >> (8 * half));
-        }
+        const intx4 lo4 = *(const intx4*)(st + arow_b + i * 128 * kMxRow + pc0);
+        const intx4 hi4 = *(const intx4*)(st + arow_b + i * 128 * kMxRow + pc1);
+        a = intx8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        if (ks == 0) sa = (int)(*(const uint32_t*)(st + kMxStageSA + (i * 128 + wm * 32 + fr) * 4) >> (8 * half));
+    };
+    auto read_b = [&](int slot, int ks, int j, intx8& b, int& sb) {
+        const uint8_t* st = smem + slot * kMxStageBytes;
+        const int pc0 = ((4 * ks + half) ^ fsw) * 16, pc1 = ((4 * ks + 2 + half) ^ fsw) * 16;
+        const intx4 lo4 = *(const intx4*)(st + brow_b + j * 32 * kMxRow + pc0);
+        const intx4 hi4 = *(const intx4*)(st + brow_b + j * 32 * kMxRow + pc1);
+        b = intx8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        if (ks == 0) sb = (int)(*(const uint32_t*)(st + kMxStageSB + (wn * 128 + j * 32 + fr) * 4) >> (8 * half));
     };
     floatx16 acc[2][4];
 #pragma unroll
@@ -133,25 +131,35 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
     // B is the first operand (with its scales), so each accumulator holds the
     // transposed block: element 4q + s of fragment (i, j) of lane l sits in
     // tile row 128i + 32wm + l%32 and column wn*128 + 32j + 8q + 4(l/32) + s.
-    // ksc: the K step (std::integral_constant), whose scales are byte 2 * ks.
-    auto mfmas = [&](auto ksc, const intx8 (&a)[2], const intx8 (&b)[4], const int (&sa)[2], const int (&sb)[4]) {
+    // The MFMAs of K step ksc (std::integral_constant; its scales are byte
+    // 2 * ks) on the fragments in registers, B fragment by B fragment.  The
+    // fragments are single-buffered (the scaled operands are twice the bf16
+    // ones and two waves share a SIMD's registers), so as soon as B fragment
+    // j's last MFMA is issued its registers take fragment j of K step rks of
+    // the stage in rslot, and the A fragments follow the last one: the next K
+    // step's LDS reads overlap this one's MFMAs.
+    auto mfmas_then = [&](auto ksc, int rslot, int rks, intx8 (&a)[2], intx8 (&b)[4], int (&sa)[2], int (&sb)[4]) {
         constexpr int sel = 2 * decltype(ksc)::value;
 #pragma unroll
-        for (int i = 0; i < NV; ++i)
+        for (int j = 0; j < 4; ++j) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int i = 0; i < NV; ++i)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a[i], acc[i][j], 0, 0, sel, sb[j],
                                                                              sel, sa[i]);
+            read_b(rslot, rks, j, b[j], sb[j]);
+        }
+#pragma unroll
+        for (int i = 0; i < NV; ++i) read_a(rslot, rks, i, a[i], sa[i]);
     };
 
     // Ring protocol (stage j in slot j % 2, 9 direct-to-LDS loads per lane and
-    // stage): the prologue issues stages 0 and 1 and waits for stage 0
-    // (vmcnt(9)); stage s reads and runs its first K step, reads the second's
-    // fragments, waits for stage s+1 (vmcnt(0)) and its own LDS reads,
-    // barrier, refills its slot with stage s+2 under the second K step's
-    // MFMAs.  Fragments are single-buffered (the scaled operands are twice the
-    // bf16 ones and two waves share a SIMD's registers): a wave waiting on its
-    // reads leaves the matrix core to the SIMD's other wave.
+    // stage): the prologue issues stages 0 and 1, waits for stage 0
+    // (vmcnt(9)) and reads its first K step's fragments.  Full stage s runs
+    // its first K step while reading its second's fragments, waits for stage
+    // s+1 (vmcnt(0)) and its own LDS reads, barrier (no wave reads stage s any
+    // more), refills its slot with stage s+2 and runs its second K step while
+    // reading the first K step of stage s+1.  An odd number of K steps ends on
+    // a half stage, whose one K step is read by then.
     static_assert(kMxStages == 2, "the vmcnt immediates below assume 2 stages of 9 loads");
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -161,19 +169,32 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
     __syncthreads();
     intx8 fa[2], fb[4];
     int fsa[2], fsb[4];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) read_a(0, 0, i, fa[i], fsa[i]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) read_b(0, 0, j, fb[j], fsb[j]);
     int slot = 0;
-    for (int s = 0; s < KS; ++s) {
-        frags(slot, 0, fa, fb, fsa, fsb);
-        mfmas(std::integral_constant<int, 0>{}, fa, fb, fsa, fsb);
+    for (int s = 0; s < KT / 2; ++s) {
+        mfmas_then(std::integral_constant<int, 0>{}, slot, 1, fa, fb, fsa, fsb);
+        Interleave<4 * NV, 0, 8 + 2 * NV>::run();
         __builtin_amdgcn_sched_barrier(0);
-        frags(slot, 1, fa, fb, fsa, fsb);
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         __syncthreads();
         issue(s + 2, slot);
-        if (2 * s + 1 < KT) mfmas(std::integral_constant<int, 1>{}, fa, fb, fsa, fsb);
-        Interleave<4 * NV, 9, 0>::run();
+        // after the last full stage this reads the half stage, or a stale but
+        // in-bounds repeat of the last stage that nothing uses
+        mfmas_then(std::integral_constant<int, 1>{}, slot ^ 1, 0, fa, fb, fsa, fsb);
+        Interleave<4 * NV, 9, 8 + 2 * NV>::run();
         __builtin_amdgcn_sched_barrier(0);
         slot ^= 1;
+    }
+    if (KT & 1) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, 0, fsb[j], 0,
+                                                                             fsa[i]);
     }
 
     // The tile leaves through LDS, 64 rows at a time (whole-line stores).
