@@ -224,6 +224,7 @@ void launch_swiglu_bwd(const SwigluBwdArgs& a, int rpad, hipStream_t stream) {
 //   dx[t] = sum_j dX[prow_j] (+ dX[shared row]) + sum_j dsel_j * WrT[idx_j]
 constexpr int kRdThreads = 128;
 constexpr int kRdPartBlock = 128;  // gate-gradient partials staged per pass
+constexpr int kRdBatch = 8;        // rows loaded before their adds
 
 __global__ __launch_bounds__(kRdThreads) void rdispatch_kernel(RdispArgs p) {
     __shared__ int s_row[kMaxTopK + 1];
@@ -271,27 +272,47 @@ __global__ __launch_bounds__(kRdThreads) void rdispatch_kernel(RdispArgs p) {
         for (int j = 0; j < k; ++j) v = s_idx[j] == e ? s_ds[j] : v;
         p.dlogits[(int64_t)t * p.E + e] = v;
     }
+    // Rows are taken kRdBatch at a time: every load of a batch is issued
+    // before its first add, and the adds then run in slot order (the fixed
+    // summation order), so the loads overlap without changing a bit.
+    const int nrows = k + p.with_shared;
     for (int c = tid; c < p.H / 8; c += kRdThreads) {
         float acc[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-        const int nrows = k + p.with_shared;
-        for (int j = 0; j < nrows; ++j) {
-            const intx4 raw = *(const intx4*)(p.dX + (int64_t)s_row[j] * p.H + c * 8);
+        for (int j0 = 0; j0 < nrows; j0 += kRdBatch) {
+            intx4 raw[kRdBatch];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc[2 * e] = acc[2 * e] + __builtin_bit_cast(float, (uint32_t)raw[e] << 16);
-                acc[2 * e + 1] = acc[2 * e + 1] + __builtin_bit_cast(float, (uint32_t)raw[e] & 0xffff0000u);
+            for (int u = 0; u < kRdBatch; ++u)
+                if (j0 + u < nrows) raw[u] = *(const intx4*)(p.dX + (int64_t)s_row[j0 + u] * p.H + c * 8);
+#pragma unroll
+            for (int u = 0; u < kRdBatch; ++u) {
+                if (j0 + u >= nrows) break;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[2 * e] = acc[2 * e] + __builtin_bit_cast(float, (uint32_t)raw[u][e] << 16);
+                    acc[2 * e + 1] = acc[2 * e + 1] + __builtin_bit_cast(float, (uint32_t)raw[u][e] & 0xffff0000u);
+                }
             }
         }
-        for (int j = 0; j < k; ++j) {
-            const floatx4* wr = (const floatx4*)(p.WrT + (int64_t)s_idx[j] * p.H + c * 8);
-            const floatx4 w0 = wr[0], w1 = wr[1];
-            const float ds = s_ds[j];
+        for (int j0 = 0; j0 < k; j0 += kRdBatch) {
+            floatx4 w0[kRdBatch], w1[kRdBatch];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                acc[q] = __builtin_fmaf(ds, w0[q], acc[q]);
-                acc[4 + q] = __builtin_fmaf(ds, w1[q], acc[4 + q]);
+            for (int u = 0; u < kRdBatch; ++u)
+                if (j0 + u < k) {
+                    const floatx4* wr = (const floatx4*)(p.WrT + (int64_t)s_idx[j0 + u] * p.H + c * 8);
+                    w0[u] = wr[0];
+                    w1[u] = wr[1];
+                }
+#pragma unroll
+            for (int u = 0; u < kRdBatch; ++u) {
+                if (j0 + u >= k) break;
+                const float ds = s_ds[j0 + u];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[q] = __builtin_fmaf(ds, w0[u][q], acc[q]);
+                    acc[4 + q] = __builtin_fmaf(ds, w1[u][q], acc[4 + q]);
+                }
             }
         }
         intx4 o;
