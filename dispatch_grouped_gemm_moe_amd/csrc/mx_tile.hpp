@@ -78,8 +78,8 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
 
     // Loads past the last stage repeat it (into the slot no wave reads any
     // more), so they need no branch and the waits are constants.  On a half
-    // stage (odd K steps) the second K step's code chunks and scales repeat
-    // the first's (and the upper half of the stage's scale dwords is zero).
+    // stage (odd K steps) the second K step's code chunks repeat the first's
+    // and the upper half of the stage's scale dwords is zero; neither is used.
     auto issue = [&](int s_, int slot) {
         const int s = s_ < KS ? s_ : KS - 1;
         // a half stage's second K step repeats the first: the lanes of the
