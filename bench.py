@@ -170,26 +170,7 @@ def main():
     moe.moe_timing_enable(False)
 
     T, H, I, E, k = w.T, w.H, w.I, w.E, w.k
-    shared_rows = T if w.shared_expert else 0
-    rows = T * k + shared_rows  # routed (+ shared) rows per step
-    hi = float(H) * I * rows  # padding rows excluded from every figure below
-    # algorithmic flops per step of each grouped-GEMM role, and the kernel
-    # symbol that runs it (rocprofv3 reports per symbol).  MXFP8 runs the
-    # routed experts on the scaled-MFMA kernel and the shared expert in bf16
-    # (its own timing kind); bf16 runs both in the same launches.
-    hr = float(H) * I * (T * k if mx else rows)
-    flops = {"gemm_gate_up": 4 * hr, "gemm_down": 2 * hr}
-    if bwd:
-        flops.update({"dgrad_down": 2 * hr, "dgrad_gate_up": 4 * hr, "wgrad": 6 * hi})
-    shared_fwd = 6.0 * H * I * shared_rows if mx else 0.0
-    if mx and shared_rows and bwd:  # the shared expert's bf16 input-gradient GEMMs
-        flops["shared_gemm"] = 6.0 * H * I * shared_rows
-    if kt["layer"][1] > 0:
-        # the persistent layer kernel runs both forward GEMMs (and combine),
-        # under MXFP8 with the shared expert's bf16 tiles in the same launch
-        flops["layer"] = flops.pop("gemm_gate_up") + flops.pop("gemm_down") + shared_fwd
-    elif shared_fwd:  # per-GEMM forward: the shared expert's launches are timed as their own kind
-        flops["shared_gemm"] = flops.get("shared_gemm", 0.0) + shared_fwd
+    flops = role_flops(T, H, I, k, w.shared_expert, mx, bwd, kt["layer"][1] > 0)
     symbol = {"gemm_gate_up": "mx_gemm_kernel<0>" if mx else "grouped_gemm_kernel<0>",
               "gemm_down": "mx_gemm_kernel<1>" if mx else "grouped_gemm_kernel<1>",
               "dgrad_down": "mx_gemm_kernel<1>" if mx else "grouped_gemm_kernel<1>",
@@ -300,6 +281,33 @@ def mfma_loop(moe, torch, x, w, mx: bool) -> dict:
         out[name + "clock_ghz"] = cyc / (ref / 100e6) / 1e9
         out[name + "ms"] = ms
     return out
+
+
+def role_flops(T: int, H: int, I: int, k: int, shared: bool, mx: bool, bwd: bool, layer_kernel: bool) -> dict:
+    """Algorithmic flops per step of each timing kind of the grouped GEMMs
+    (padding rows excluded): 6*H*I per routed or shared row and pass (gate|up
+    4*H*I, down 2*H*I), for the forward, the input gradients and the weight
+    gradients.  MXFP8 runs the routed experts on the scaled-MFMA kernels and
+    the shared expert in bf16: its backward input-gradient launches are their
+    own kind, and its forward GEMMs run in the persistent layer kernel when
+    that runs (their own kind otherwise).  bf16 runs both in the same
+    launches."""
+    shared_rows = T if shared else 0
+    hi = float(H) * I * (T * k + shared_rows)
+    hr = float(H) * I * (T * k if mx else T * k + shared_rows)
+    flops = {"gemm_gate_up": 4 * hr, "gemm_down": 2 * hr}
+    if bwd:
+        flops.update({"dgrad_down": 2 * hr, "dgrad_gate_up": 4 * hr, "wgrad": 6 * hi})
+    shared_fwd = 6.0 * H * I * shared_rows if mx else 0.0
+    if mx and shared_rows and bwd:  # the shared expert's bf16 input-gradient GEMMs
+        flops["shared_gemm"] = 6.0 * H * I * shared_rows
+    if layer_kernel:
+        # the persistent layer kernel runs both forward GEMMs (and combine),
+        # under MXFP8 with the shared expert's bf16 tiles in the same launch
+        flops["layer"] = flops.pop("gemm_gate_up") + flops.pop("gemm_down") + shared_fwd
+    elif shared_fwd:  # per-GEMM forward: the shared expert's launches are timed as their own kind
+        flops["shared_gemm"] = flops.get("shared_gemm", 0.0) + shared_fwd
+    return flops
 
 
 def traffic_for(symbol: str, workload: str):

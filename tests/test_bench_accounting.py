@@ -1,0 +1,51 @@
+"""CPU checks of bench.py's algorithmic-flop accounting per timing kind.
+
+A grouped GEMM over M rows with an N x K weight costs 2*M*N*K flops, so one
+routed or shared row costs 4*H*I in gate|up (N = 2I, K = H) and 2*H*I in down
+(N = H, K = I) per pass; the backward repeats that for the input gradients and
+again for the weight gradients.  Whatever kinds the launches are timed under,
+every row's flops must be counted once and only once."""
+import itertools
+
+import pytest
+
+import bench
+
+T, H, I, K = 1000, 384, 192, 4
+HI = float(H) * I
+
+
+@pytest.mark.parametrize("shared,mx,bwd,layer", list(itertools.product([False, True], repeat=4)))
+def test_every_row_counted_once(shared, mx, bwd, layer):
+    f = bench.role_flops(T, H, I, K, shared, mx, bwd, layer)
+    rows = T * K + (T if shared else 0)
+    assert sum(f.values()) == (18 if bwd else 6) * HI * rows
+    assert all(v > 0 for v in f.values())
+    if layer:
+        assert "gemm_gate_up" not in f and "gemm_down" not in f
+        # the layer kernel runs every forward GEMM, the shared expert's included
+        assert f["layer"] == 6 * HI * rows
+    else:
+        assert "layer" not in f
+    if bwd:
+        assert f["wgrad"] == 6 * HI * rows
+
+
+def test_mxfp8_shared_expert_kinds():
+    # routed rows on the scaled-MFMA kernels; the shared expert's backward
+    # input gradients are their own kind (bf16)
+    f = bench.role_flops(T, H, I, K, True, True, True, True)
+    assert f["dgrad_down"] == 2 * HI * T * K and f["dgrad_gate_up"] == 4 * HI * T * K
+    assert f["shared_gemm"] == 6 * HI * T
+    # forward only, through the layer kernel: no shared-expert launches at all
+    assert "shared_gemm" not in bench.role_flops(T, H, I, K, True, True, False, True)
+    # forward only, one launch per GEMM: the shared expert's forward launches
+    f = bench.role_flops(T, H, I, K, True, True, False, False)
+    assert f["shared_gemm"] == 6 * HI * T
+    assert f["gemm_gate_up"] == 4 * HI * T * K and f["gemm_down"] == 2 * HI * T * K
+
+
+def test_bf16_runs_shared_rows_with_the_routed_ones():
+    f = bench.role_flops(T, H, I, K, True, False, True, True)
+    assert "shared_gemm" not in f
+    assert f["dgrad_down"] == 2 * HI * (T * K + T) and f["dgrad_gate_up"] == 4 * HI * (T * K + T)
