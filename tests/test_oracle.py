@@ -618,3 +618,30 @@ def test_mx_backward_scales_exactly_with_dout_and_stays_near_plain():
     plain = O.layer_backward(inp, fwd=O.layer_forward(inp, keep=True, mx=False), mx=False)
     for n in ("dx", "dWg", "dWu", "dWd"):
         assert 1e-4 < O.rel_inf_err(g1[n], plain[n]) < 0.15, n
+
+
+# ------------------------------------------------------------ error metric
+
+def test_rel_inf_err_hand_cases():
+    """The metric behind every tolerance: max_i |got_i - ref_i| / max_i |ref_i|,
+    over the whole tensor.  Each case is worked by hand and fails a plausible
+    slip: a missing abs on the difference, a missing abs on the reference, a
+    per-row instead of a global maximum, a mean instead of a maximum."""
+    # |diff| = [0, 2], max |ref| = 4 (a negative entry): 0.5.  Without the abs
+    # on the reference the denominator would be 1 (ratio 2); without the abs on
+    # the difference the numerator would be 0.
+    assert O.rel_inf_err([1.0, -6.0], [1.0, -4.0]) == 0.5
+    # |diff| = [1, 2], max |ref| = 2: 1.0 (max(got - ref) alone would be -1)
+    assert O.rel_inf_err([1.0, -3.0], [2.0, -1.0]) == 1.0
+    # 2-D: the maxima run over every element, not row by row:
+    # |diff| max = 0.5 (row 1), max |ref| = 8 (row 0): 1/16.  Row-wise ratios
+    # would give 0.25 for row 1; the mean |diff| (0.125) over 8 would be 1/64.
+    got = np.array([[8.0, 1.0], [2.0, 1.5]])
+    ref = np.array([[8.0, 1.0], [2.0, 2.0]])
+    assert O.rel_inf_err(got, ref) == 1.0 / 16.0
+    # an all-zero reference divides by 1: the absolute error itself
+    assert O.rel_inf_err([0.0, -0.25], [0.0, 0.0]) == 0.25
+    assert O.rel_inf_err(np.zeros(3), np.zeros(3)) == 0.0
+    # bf16 and fp32 inputs widen exactly before the difference is taken
+    a = torch.tensor([1.0 + 2.0 ** -7], dtype=torch.bfloat16).float().numpy()
+    assert O.rel_inf_err(a, np.array([1.0])) == 2.0 ** -7
