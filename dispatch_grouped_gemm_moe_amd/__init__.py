@@ -20,6 +20,8 @@ MOE_PREC_BF16, MOE_PREC_MXFP8 = 0, 1
 MOE_F_SHARED_EXPERT = 1 << 0
 MOE_F_IDENTITY_EXPERTS = 1 << 1
 MOE_F_LAUNCH_PER_GEMM = 1 << 2
+MOE_F_DEBUG_DROP_SIGNAL = 1 << 3
+MOE_DEV_OK, MOE_DEV_WAIT_TIMEOUT = 0, 1
 
 # every symbol include/moe.h declares
 EXPORTS = ("moe_status_string", "moe_abi_version", "moe_validate_cfg", "moe_query_sizes",
@@ -78,7 +80,7 @@ def _load():
             "moe_validate_cfg": (ctypes.c_int, [cfgp]),
             "moe_query_sizes": (ctypes.c_int, [cfgp, ctypes.POINTER(moe_sizes)]),
             "moe_prepare_weights": (ctypes.c_int, [cfgp, P, P, P, P, P, P, P, SZ, P]),
-            "moe_route": (ctypes.c_int, [cfgp, P, P, P, P, P, P, P]),
+            "moe_route": (ctypes.c_int, [cfgp, P, P, P, P, P, P, P, P, P]),
             "moe_dispatch_layout": (ctypes.c_int, [cfgp, P, P, P, P, P, P]),
             "moe_layer_fwd": (ctypes.c_int, [cfgp, ctypes.POINTER(moe_weights), P, P, P, SZ, P, SZ, P]),
             "moe_layer_bwd": (ctypes.c_int, [cfgp, ctypes.POINTER(moe_weights), P, P, P, SZ, P, P, P,
@@ -143,9 +145,10 @@ def moe_prepare_weights(cfg, Wg, Wu, Wd, packed, Wsg=None, Wsu=None, Wsd=None, s
         _ptr(packed), packed.numel() * packed.element_size(), _stream(stream)))
 
 
-def moe_route(cfg, x, Wr, bias, topk_idx, topk_w, logits=None, stream=None):
+def moe_route(cfg, x, Wr, bias, topk_idx, topk_w, logits=None, x_codes=None, x_scales=None, stream=None):
     _check("moe_route", _load().moe_route(ctypes.byref(cfg), _ptr(x), _ptr(Wr), _ptr(bias),
-                                          _ptr(topk_idx), _ptr(topk_w), _ptr(logits), _stream(stream)))
+                                          _ptr(topk_idx), _ptr(topk_w), _ptr(logits), _ptr(x_codes),
+                                          _ptr(x_scales), _stream(stream)))
 
 
 def moe_dispatch_layout(cfg, topk_idx, counts, offsets, row_token, tok_row, stream=None):

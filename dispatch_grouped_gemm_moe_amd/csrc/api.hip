@@ -65,7 +65,8 @@ moe_status validate(const moe_cfg* c) {
     if (c->T < 1 || c->E < 1 || c->k < 1 || c->k > c->E || c->H < 1 || c->I < 1) return MOE_E_INVALID;
     if (c->minibatch < 0 || c->ring_slots < 0 || c->comm_cus < 0) return MOE_E_INVALID;
     if (c->prec != MOE_PREC_BF16 && c->prec != MOE_PREC_MXFP8) return MOE_E_INVALID;
-    if (c->flags & ~(uint32_t)(MOE_F_SHARED_EXPERT | MOE_F_IDENTITY_EXPERTS | MOE_F_LAUNCH_PER_GEMM))
+    if (c->flags & ~(uint32_t)(MOE_F_SHARED_EXPERT | MOE_F_IDENTITY_EXPERTS | MOE_F_LAUNCH_PER_GEMM |
+                               MOE_F_DEBUG_DROP_SIGNAL))
         return MOE_E_INVALID;
     if (c->H % 64 || c->I % 64 || c->E > kMaxExperts || c->k > kMaxTopK) return MOE_E_UNSUPPORTED;
     if ((int64_t)c->T * c->k > (1ll << 30) || (int64_t)c->T * c->H > (1ll << 40)) return MOE_E_UNSUPPORTED;
@@ -349,12 +350,16 @@ moe_status moe_prepare_weights(const moe_cfg* cfg, const uint16_t* Wg, const uin
 }
 
 moe_status moe_route(const moe_cfg* cfg, const uint16_t* x, const float* Wr, const float* bias,
-                     int32_t* topk_idx, float* topk_w, float* logits, void* stream) {
+                     int32_t* topk_idx, float* topk_w, float* logits, uint8_t* x_codes, uint8_t* x_scales,
+                     void* stream) {
     moe_status st = validate(cfg);
     if (st != MOE_OK) return st;
     if (!x || !Wr || !topk_idx || !topk_w) return MOE_E_INVALID;
+    if ((x_codes == nullptr) != (x_scales == nullptr) || (x_codes && (!aligned(x_codes, 16) || !aligned(x, 16))))
+        return MOE_E_INVALID;
     TIMED(MOE_K_ROUTE, (hipStream_t)stream,
-          launch_route(x, Wr, bias, cfg->T, cfg->H, cfg->E, cfg->k, topk_idx, topk_w, logits, (hipStream_t)stream));
+          launch_route(x, Wr, bias, cfg->T, cfg->H, cfg->E, cfg->k, topk_idx, topk_w, logits, (hipStream_t)stream,
+                       x_codes, x_scales));
     return check_launch();
 }
 
@@ -373,18 +378,21 @@ moe_status moe_dispatch_layout(const moe_cfg* cfg, const int32_t* topk_idx, int3
     return check_launch();
 }
 
-moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_t* x, uint16_t* out,
-                         void* saved, size_t saved_bytes, void* ws, size_t ws_bytes, void* stream) {
-    Plan p;
-    moe_status st = make_plan(cfg, &p);
-    if (st != MOE_OK) return st;
+// Host checks of a forward call's buffers (nothing is enqueued).
+static moe_status check_fwd(const Plan& p, const moe_weights* w, const uint16_t* x, const uint16_t* out,
+                            const void* saved, size_t saved_bytes, const void* ws, size_t ws_bytes) {
     if (!w || !w->Wr || !w->packed || !x || !out || !ws) return MOE_E_INVALID;
     if (!aligned(x, 16) || !aligned(out, 16) || !aligned(ws, kAlign) || !aligned(w->packed, kAlign))
         return MOE_E_INVALID;
     if (saved && !aligned(saved, kAlign)) return MOE_E_INVALID;
     if (w->packed_bytes < p.packed || ws_bytes < p.ws_fwd) return MOE_E_WORKSPACE;
     if (saved && saved_bytes < p.saved) return MOE_E_WORKSPACE;
-    hipStream_t s = (hipStream_t)stream;
+    return MOE_OK;
+}
+
+// The forward's launches (arguments already checked by check_fwd).
+static moe_status enqueue_fwd(const moe_cfg* cfg, const Plan& p, const moe_weights* w, const uint16_t* x,
+                              uint16_t* out, void* saved, void* ws, hipStream_t s) {
     uint8_t* wsb = (uint8_t*)ws;
     int32_t* idx = saved ? (int32_t*)((uint8_t*)saved + p.sv_idx) : (int32_t*)(wsb + p.ws_idx);
     float* gw = saved ? (float*)((uint8_t*)saved + p.sv_w) : (float*)(wsb + p.ws_w);
@@ -398,10 +406,12 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
     uint8_t* sx = wsb + p.ws_sx;
     const int grid = kNumCUs;
 
-    // route every token, then lay out every minibatch (one workgroup each)
-    TIMED(MOE_K_ROUTE, s, launch_route(x, w->Wr, w->bias, p.T, p.H, p.E, p.k, idx, gw, nullptr, s));
-    if (p.mx && !p.identity)  // dispatch-side quantisation: every token row once, along H
-        TIMED(MOE_K_GATHER, s, launch_mx_quant(x, p.T, p.H, 1, xq, sx, s));
+    // route every token (under MXFP8 also the dispatch-side quantisation of
+    // every token row, along H, from the values the router reads), then lay
+    // out every minibatch (one workgroup each)
+    const bool quant_x = p.mx && !p.identity;
+    TIMED(MOE_K_ROUTE, s, launch_route(x, w->Wr, w->bias, p.T, p.H, p.E, p.k, idx, gw, nullptr, s,
+                                       quant_x ? xq : nullptr, quant_x ? sx : nullptr));
     {
         LayoutOut o{};
         o.hdr = (LayoutHeader*)(lay0 + p.ly_hdr);
@@ -462,6 +472,7 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
         a.counters = (int*)(wsb + p.ws_cnt);
         a.status = (int*)(wsb + p.ws_status);
         a.spin_ticks = kSpinTicks;
+        a.debug_drop = (cfg->flags & MOE_F_DEBUG_DROP_SIGNAL) ? 1 : 0;
         const int mgrid = p.comm_cus + ((ncu - p.comm_cus) / 8) * 8;
         hipError_t err = hipSuccess;
         TIMED(MOE_K_LAYER, s, err = launch_mega(a, mgrid, s));
@@ -521,6 +532,15 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
                              (p.shared && !p.identity) ? 1 : 0, p.H, Tm, out + (size_t)t0 * p.H, s));
     }
     return check_launch();
+}
+
+moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_t* x, uint16_t* out,
+                         void* saved, size_t saved_bytes, void* ws, size_t ws_bytes, void* stream) {
+    Plan p;
+    moe_status st = make_plan(cfg, &p);
+    if (st != MOE_OK) return st;
+    if ((st = check_fwd(p, w, x, out, saved, saved_bytes, ws, ws_bytes)) != MOE_OK) return st;
+    return enqueue_fwd(cfg, p, w, x, out, saved, ws, (hipStream_t)stream);
 }
 
 moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_t* x, const uint16_t* dout,
@@ -738,21 +758,38 @@ moe_status moe_mx_quantize(const uint16_t* src, int64_t rows, int32_t cols, uint
     return check_launch();
 }
 
+// Destroys every timing event (they must not outlive the runtime's own
+// teardown at process exit, which runs after profiling tools have finalised).
+static moe_status release_timing_events() {
+    moe_status st = MOE_OK;
+    for (hipEvent_t e : g_timing.ev)
+        if (e && hipEventDestroy(e) != hipSuccess) st = MOE_E_HIP;
+    g_timing.ev.clear();
+    g_timing.kind.clear();
+    g_timing.used = 0;
+    return st;
+}
+
 moe_status moe_timing_enable(int32_t on) {
-    if (on) {
-        if (g_timing.ev.empty()) {
-            g_timing.ev.resize(2 * kTimingPairs);
-            g_timing.kind.resize(kTimingPairs);
-            for (auto& e : g_timing.ev)
-                if (hipEventCreate(&e) != hipSuccess) {
-                    g_timing.ev.clear();
-                    return MOE_E_HIP;
-                }
-        }
-        g_timing.used = 0;
-        g_timing.dropped = 0;
+    if (!on) {
+        // the recorded pairs may still be pending on their streams: wait for
+        // them before the events go
+        for (int i = 0; i < g_timing.used; ++i) (void)hipEventSynchronize(g_timing.ev[2 * i + 1]);
+        g_timing.on = false;
+        return release_timing_events();
     }
-    g_timing.on = on != 0;
+    if (g_timing.ev.empty()) {
+        g_timing.ev.assign(2 * kTimingPairs, nullptr);
+        g_timing.kind.resize(kTimingPairs);
+        for (auto& e : g_timing.ev)
+            if (hipEventCreate(&e) != hipSuccess) {
+                release_timing_events();
+                return MOE_E_HIP;
+            }
+    }
+    g_timing.used = 0;
+    g_timing.dropped = 0;
+    g_timing.on = true;
     return MOE_OK;
 }
 

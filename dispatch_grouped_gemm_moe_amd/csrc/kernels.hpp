@@ -24,8 +24,12 @@ struct LayoutOut {
     int32_t token_base;   // added to tokens written into prow_token
 };
 
+// With xq / xs (MXFP8 dispatch), the router also writes every token row's
+// E4M3 codes xq [T][H] and E8M0 scales xs in the GEMM operand scale layout
+// [mx_groups(H)][T][4] (the quantisation of launch_mx_quant, bit for bit).
 void launch_route(const uint16_t* x, const float* Wr, const float* bias, int T, int H, int E, int k,
-                  int32_t* topk_idx, float* topk_w, float* logits, hipStream_t stream);
+                  int32_t* topk_idx, float* topk_w, float* logits, hipStream_t stream, uint8_t* xq = nullptr,
+                  uint8_t* xs = nullptr);
 
 void launch_layout(const int32_t* idx, int Tm, int E, int k, int with_shared, const LayoutOut& o,
                    hipStream_t stream);
@@ -149,6 +153,7 @@ struct MegaArgs {
     int* counters;
     int* status;
     uint64_t spin_ticks;  // bound of every wait, in s_memrealtime ticks (100 MHz)
+    int debug_drop;       // GEMM workgroup 0 skips its signal of gate|up phase 0 (watchdog test)
 };
 hipError_t launch_mega(const MegaArgs& a, int grid, hipStream_t stream);
 

@@ -249,7 +249,8 @@ void mega_kernel(MegaArgs a) {
     for (int it = 0;; ++it) {
         const int64_t v = (int64_t)it * G + xcd * per + local;
         while (more && v >= qstart + qtiles) {  // done with this phase: publish
-            signal_counter(counter_of(cur.kind, cur.j));
+            const bool dropped = a.debug_drop && g == 0 && cur.kind == kGateUp && cur.j == 0;
+            if (!dropped) signal_counter(counter_of(cur.kind, cur.j));
             qstart += qtiles;
             more = cur.next(ng, comb_tiles);
             if (more) qtiles = phase_tiles(cur.kind, cur.j);

@@ -40,38 +40,11 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restric
     const int64_t r = i / nb;
     const int b = (int)(i - r * nb);
     if (hdr && r >= (int64_t)hdr->m_tiles * BM) return;  // rows past the minibatch's last tile
-    const intx4* s = (const intx4*)(src + r * cols + b * 32);
-    float v[32];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const intx4 raw = s[q];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            v[8 * q + 2 * e] = __builtin_bit_cast(float, (uint32_t)raw[e] << 16);
-            v[8 * q + 2 * e + 1] = __builtin_bit_cast(float, (uint32_t)raw[e] & 0xffff0000u);
-        }
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 32; ++c) amax = fmaxf(amax, fabsf(v[c]));
-    const int e = mx_scale_exp(amax);
-    intx4 out[2];
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-        out[q >> 2][q & 3] = (int)fp8x4(ldexpf(v[4 * q], -e), ldexpf(v[4 * q + 1], -e), ldexpf(v[4 * q + 2], -e),
-                                        ldexpf(v[4 * q + 3], -e));
-    intx4* dst = (intx4*)(codes + r * cols + b * 32);
-    dst[0] = out[0];
-    dst[1] = out[1];
-    const uint8_t sc = (uint8_t)(e + 127);
-    if (layout == 0) {
+    const uint8_t sc = mx_quant_block32(src + r * cols + b * 32, codes + r * cols + b * 32);
+    if (layout == 0)
         scales[r * nb + b] = sc;
-    } else {
-        uint8_t* d = scales + ((int64_t)(b >> 2) * rows + r) * 4;
-        d[b & 3] = sc;
-        if (b + 1 == nb)
-            for (int z = (b & 3) + 1; z < 4; ++z) d[z] = 0;
-    }
+    else
+        mx_store_scale_byte(scales, rows, r, b, nb, sc);
 }
 
 void launch_mx_quant(const uint16_t* src, int64_t rows, int cols, int layout, uint8_t* codes, uint8_t* scales,

@@ -31,6 +31,41 @@ __device__ __forceinline__ intx4 fp8x16(const float* v, int e) {
     return o;
 }
 
+// One 32-element block of a bf16 row (src, 16-byte aligned) -> 32 E4M3 codes
+// at dst (16-byte aligned); returns the E8M0 scale byte (e + 127).
+__device__ __forceinline__ uint8_t mx_quant_block32(const uint16_t* __restrict__ src, uint8_t* __restrict__ dst) {
+    const intx4* s = (const intx4*)src;
+    float v[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const intx4 raw = s[q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[8 * q + 2 * e] = __builtin_bit_cast(float, (uint32_t)raw[e] << 16);
+            v[8 * q + 2 * e + 1] = __builtin_bit_cast(float, (uint32_t)raw[e] & 0xffff0000u);
+        }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) amax = fmaxf(amax, fabsf(v[c]));
+    const int e = mx_scale_exp(amax);
+    intx4* d = (intx4*)dst;
+    d[0] = fp8x16(v, e);
+    d[1] = fp8x16(v + 16, e);
+    return (uint8_t)(e + 127);
+}
+
+// Scale byte of block b of a row with nb blocks into the GEMM operand scale
+// layout [mx_groups(cols)][rows][4]; the row's last block also zeroes the
+// bytes of its group past the row's end.
+__device__ __forceinline__ void mx_store_scale_byte(uint8_t* scales, int64_t rows, int64_t row, int b, int nb,
+                                                    uint8_t sc) {
+    uint8_t* d = scales + ((int64_t)(b >> 2) * rows + row) * 4;
+    d[b & 3] = sc;
+    if (b + 1 == nb)
+        for (int z = (b & 3) + 1; z < 4; ++z) d[z] = 0;
+}
+
 // The two scales (pair = block 2j | block 2j+1 << 8) of 64-element block j of
 // a row in the GEMM operand scale layout (scales [groups][rows][4]): half j % 2
 // of the row's dword of group j / 2.  The last block of a row with an odd

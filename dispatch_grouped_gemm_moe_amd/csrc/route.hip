@@ -16,6 +16,7 @@
 // ballots in token order, so the layout is deterministic.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "mxfp8.hpp"
 
 namespace moe {
 
@@ -50,7 +51,7 @@ template <bool kVec4>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ Wr, const float* __restrict__ bias,
     int T, int H, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
-    float* __restrict__ logits_out) {
+    float* __restrict__ logits_out, uint8_t* __restrict__ xq, uint8_t* __restrict__ xs) {
     __shared__ float s_logit[kRouteTokens][kMaxExperts];
     __shared__ __attribute__((aligned(16))) float s_w[2][kWave][kRouteWRow];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -126,6 +127,19 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     }
     __syncthreads();
 
+    // MXFP8 dispatch-side quantisation of this workgroup's token rows (the
+    // rows the router has just read, so mostly cache hits): one thread per
+    // 32-element block, codes along H and the operand-layout scales.
+    if (xq) {
+        const int nb = H / 32;
+        for (int i = tid; i < nt * nb; i += kRouteThreads) {
+            const int tt = i / nb, b = i - tt * nb;
+            const int64_t t = t0 + tt;
+            const uint8_t sc = mx_quant_block32(x + t * H + b * 32, xq + t * H + b * 32);
+            mx_store_scale_byte(xs, T, t, b, nb, sc);
+        }
+    }
+
     // Top-k per token: one wave per token; lane l holds experts l, l+64, ...
     for (int tt = wave; tt < nt; tt += kRouteThreads / kWave) {
         const int t = t0 + tt;
@@ -180,15 +194,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
 }
 
 void launch_route(const uint16_t* x, const float* Wr, const float* bias, int T, int H, int E, int k,
-                  int32_t* topk_idx, float* topk_w, float* logits, hipStream_t stream) {
+                  int32_t* topk_idx, float* topk_w, float* logits, hipStream_t stream, uint8_t* xq, uint8_t* xs) {
     const int blocks = ceil_div(T, kRouteTokens);
     const bool vec4 = (E % 4 == 0) && (((uintptr_t)Wr & 15) == 0);
     if (vec4)
         hipLaunchKernelGGL(route_kernel<true>, dim3(blocks), dim3(kRouteThreads), 0, stream, x, Wr, bias, T,
-                           H, E, k, topk_idx, topk_w, logits);
+                           H, E, k, topk_idx, topk_w, logits, xq, xs);
     else
         hipLaunchKernelGGL(route_kernel<false>, dim3(blocks), dim3(kRouteThreads), 0, stream, x, Wr, bias, T,
-                           H, E, k, topk_idx, topk_w, logits);
+                           H, E, k, topk_idx, topk_w, logits, xq, xs);
 }
 
 // ---------------------------------------------------------------------------

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum moe_status {
     MOE_OK = 0,
@@ -65,7 +65,14 @@ enum moe_flags {
     /* run the forward's expert GEMMs and combine as one launch per grouped GEMM
        and per combine, minibatch by minibatch, instead of the persistent layer
        kernel (same results bit for bit) */
-    MOE_F_LAUNCH_PER_GEMM = 1u << 2
+    MOE_F_LAUNCH_PER_GEMM = 1u << 2,
+    /* debug, for testing the watchdog: in the persistent layer kernel, GEMM
+       workgroup 0 never signals that it has finished the first gate|up phase.
+       The waits on that phase then run into their bound (2 s), the launch
+       drains, the device status word records MOE_DEV_WAIT_TIMEOUT with the wait
+       site as detail, and `out` is unspecified.  No effect on a forward that
+       runs one launch per GEMM. */
+    MOE_F_DEBUG_DROP_SIGNAL = 1u << 3
 };
 
 /* Layer shape and execution choices. */
@@ -156,10 +163,21 @@ moe_status moe_prepare_weights(const moe_cfg *cfg, const uint16_t *Wg, const uin
  *   topk_w[t,j] = softmax over the k selected logits (fp32).
  *   x [T,H] bf16; Wr [H,E] fp32; bias [E] fp32 or NULL;
  *   topk_idx [T,k] int32; topk_w [T,k] fp32; logits [T,E] fp32 or NULL.
- * Inputs must be finite.
+ * Optionally, the MXFP8 dispatch quantisation of every token row, computed
+ * from the values the router reads ([KC] 02: MXFP8 quantisation inside the
+ * dispatch instead of a separate kernel; the MXFP8 forward runs exactly this):
+ *   x_codes [T,H] uint8: E4M3 codes of x along H, by the rule of
+ *       moe_mx_quantize (16-byte aligned);
+ *   x_scales: the E8M0 scales (e + 127) in the GEMM operand layout
+ *       [ceil(H/128)][T][4] bytes: byte b of dword (g, t) is the scale of
+ *       token t's 32-element block 4g + b, bytes past the row's end zero;
+ *   both NULL (nothing written) or both set.
+ * Inputs must be finite.  MOE_E_INVALID if only one of x_codes, x_scales is
+ * given, or x_codes is given and it or x is not 16-byte aligned.
  */
 moe_status moe_route(const moe_cfg *cfg, const uint16_t *x, const float *Wr, const float *bias,
-                     int32_t *topk_idx, float *topk_w, float *logits, void *stream);
+                     int32_t *topk_idx, float *topk_w, float *logits, uint8_t *x_codes,
+                     uint8_t *x_scales, void *stream);
 
 /*
  * Dispatch layout ([KC] 01: count the tokens of every expert, decide where each
@@ -171,10 +189,10 @@ moe_status moe_route(const moe_cfg *cfg, const uint16_t *x, const float *Wr, con
  *   row_token[T*k] token of each row; rows of expert e are
  *                  offsets[e] .. offsets[e+1]-1 in ascending token order
  *   tok_row  [T,k] row holding slot j of token t (inverse of row_token)
- * Needs no workspace.  If any index lies outside [0,E) the kernel writes
- * offsets[E] = -1 and leaves the other outputs unspecified (the host cannot see
- * device data without a sync, so this is the error report of this call).
- * An expert repeated within a token gets one row per slot, in slot order.
+ * Needs no workspace.  If any index lies outside [0,E), or an expert appears
+ * twice among one token's k indices, the kernel writes offsets[E] = -1 and
+ * leaves the other outputs unspecified (the host cannot see device data
+ * without a sync, so this is the error report of this call).
  */
 moe_status moe_dispatch_layout(const moe_cfg *cfg, const int32_t *topk_idx, int32_t *counts,
                                int32_t *offsets, int32_t *row_token, int32_t *tok_row,
@@ -260,7 +278,9 @@ moe_status moe_mx_quantize(const uint16_t *src, int64_t rows, int32_t cols, uint
  * returns, per kernel kind, the launch count and the summed event time since
  * the last moe_timing_enable(1).  Recording costs a few microseconds per
  * launch; with timing off nothing is recorded.  Not re-entrant across threads.
- * moe_timing_enable allocates HIP events (host call; never inside a capture).
+ * moe_timing_enable(1) creates the HIP events (host call; never inside a
+ * capture); moe_timing_enable(0) waits for the recorded launches and destroys
+ * the events, so read the times before switching timing off.
  */
 typedef enum moe_kernel_kind {
     MOE_K_ROUTE = 0,

@@ -37,6 +37,21 @@ class Layer:
                           self.bufs.ws, saved=self.bufs.saved if keep else None)
         return self.out
 
+    def forward_path(self, keep=True):
+        """Runs forward(keep) and reports which path it took: "layer kernel" if
+        the persistent layer kernel was launched (once), "per-GEMM" if the
+        forward ran one launch per grouped GEMM (the library's launch timing)."""
+        torch.cuda.synchronize()
+        moe.moe_timing_enable(True)
+        try:
+            self.forward(keep)
+            kt = moe.moe_timing_read()
+        finally:
+            moe.moe_timing_enable(False)
+        layer, per_gemm = kt["layer"][0], kt["gemm_gate_up"][0] + kt["shared_gemm"][0] + kt["gather"][0]
+        assert layer in (0, 1), kt
+        return "layer kernel" if layer == 1 else ("per-GEMM" if per_gemm else "none")
+
     def device_status(self):
         return moe.moe_read_device_status(self.bufs.ws)
 

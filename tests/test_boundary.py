@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert moe.moe_abi_version() == 1
+    assert moe.moe_abi_version() == 2
     lib = moe.lib()
     assert lib.moe_status_string(0) == b"ok"
     assert lib.moe_status_string(3) == b"buffer too small"
@@ -99,13 +99,20 @@ def test_diag_mfma_loop_rejects_bad_arguments():
 def test_null_pointers_are_rejected_before_any_launch():
     lib = moe.lib()
     cfg = moe.make_cfg(64, 128, 64, 8, 2)
-    st = lib.moe_route(ctypes.byref(cfg), None, None, None, None, None, None, None)
+    st = lib.moe_route(ctypes.byref(cfg), None, None, None, None, None, None, None, None, None)
     assert st == moe.MOE_E_INVALID
     st = lib.moe_dispatch_layout(ctypes.byref(cfg), None, None, None, None, None, None)
     assert st == moe.MOE_E_INVALID
     st = lib.moe_layer_fwd(ctypes.byref(cfg), None, None, None, None, 0, None, 0, None)
     assert st == moe.MOE_E_INVALID
-    st = lib.moe_route(None, None, None, None, None, None, None, None)
+    st = lib.moe_route(None, None, None, None, None, None, None, None, None, None)
+    assert st == moe.MOE_E_INVALID
+    # the dispatch-quantisation outputs come as a pair, the codes 16-byte aligned
+    fake = ctypes.c_void_p(1 << 20)
+    st = lib.moe_route(ctypes.byref(cfg), fake, fake, None, fake, fake, None, fake, None, None)
+    assert st == moe.MOE_E_INVALID
+    st = lib.moe_route(ctypes.byref(cfg), fake, fake, None, fake, fake, None, ctypes.c_void_p((1 << 20) + 8),
+                       fake, None)
     assert st == moe.MOE_E_INVALID
 
 

@@ -4,8 +4,11 @@ benchmark launches it (same configuration, default ring slots and CU split),
 against the fp64 CPU oracle on outputs it can compute one at a time.
 
 With the benchmark's dout:
-* dx and the gate gradients of sampled tokens, the first and last among them
-  (each token's gradients depend on that token alone);
+* dx and the gate gradients of sampled tokens (each token's gradients depend
+  on that token alone), chosen so that every 128-row block of every
+  (minibatch, expert) segment -- the shared expert's too -- holds a sampled
+  row, and so every M tile of every input-gradient GEMM; the first and last
+  token among them;
 * sampled columns of dWg and dWu and rows of dWd of the most-loaded, the
   least-loaded and the last expert, over all of their tokens, and sampled
   shared-expert columns;
@@ -29,8 +32,9 @@ import torch
 
 import oracle as O
 from moe_inputs import KIMI_BF16, KIMI_FWD_BWD, LayerInputs, make_inputs
+from sampling import covering_tokens
 
-pytestmark = pytest.mark.gpu
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
 TOL = {"bf16": 1e-2, "mxfp8": 5e-2}
 
@@ -43,8 +47,8 @@ def full(request, gpu_lib):
     layer = Layer(inp)
     layer.forward()
     torch.cuda.synchronize()
-    S = np.random.default_rng(17).choice(np.arange(1, w.T - 1), size=22, replace=False)
-    S = np.concatenate([[0], np.sort(S), [w.T - 1]])
+    _, idx, _ = O.route(O.as_f32(inp.x), inp.Wr, inp.bias, w.k)
+    S = np.union1d(covering_tokens(idx, w.minibatch, shared=w.shared_expert), [0, w.T - 1])
     print("%s: layer forward done; oracle on %d tokens" % (w.name, len(S)), flush=True)
     fwd = O.layer_forward(inp, tokens=S, keep=True)
     ref = O.layer_backward(inp, dout=inp.dout[S], fwd=fwd, weight_grads=False)
