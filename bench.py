@@ -46,6 +46,11 @@ def main():
                     help="forward as one launch per grouped GEMM instead of the persistent layer kernel")
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens the CPU oracle is timed on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="time only the main workload (by default the MXFP8 forward, the MXFP8 + shared "
+                         "forward + backward, the bf16 forward and the per-GEMM bf16 forward are timed as well, "
+                         "into detail.workloads)")
+    ap.add_argument("--extra-steps", type=int, default=5)
     ap.add_argument("--no-mfma-loop", action="store_true",
                     help="skip the sustained-MFMA measurement (a pure MFMA loop on the layer's own input values)")
     ap.add_argument("--cold-cache", action="store_true",
@@ -105,17 +110,73 @@ def main():
         torch.neg(a, out=b)
         torch.cuda.synchronize()
         del a, b
-    t_gen = time.time()
-    from moe_inputs import make_inputs
-    mx = w.prec == "mxfp8"
-    bwd = args.passes == "fwdbwd"
-    inp = make_inputs(w, with_dout=bwd)
-    log("inputs drawn in %.1f s" % (time.time() - t_gen))
 
-    flags = (moe.MOE_F_SHARED_EXPERT if w.shared_expert else 0) | (moe.MOE_F_LAUNCH_PER_GEMM if args.launch_per_gemm else 0)
+    bwd = args.passes == "fwdbwd"
+    m = measure(moe, torch, w, bwd, args.steps, args.warmup, comm_cus=args.comm_cus, ring_slots=args.ring_slots,
+                launch_per_gemm=args.launch_per_gemm, cold_cache=args.cold_cache,
+                mfma_loops=not args.no_mfma_loop, keep_inputs=not args.no_cpu_baseline)
+    inp = m.pop("inputs", None)
+    mx = w.prec == "mxfp8"
+    res = {
+        "metric": "MoE layer %s tokens/s at H=%d I=%d (%s) + %% MFMA peak" % (
+            "fwd+bwd" if bwd else "fwd", w.H, w.I, "MXFP8" if mx else "bf16"),
+        "value": m["value"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": m["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8-e4m3" if mx else "bf16",
+        "data": "synthetic",
+        "config": m["config"],
+        "roofline": m["roofline"],
+        "detail": m["detail"],
+    }
+    if not args.no_extra:
+        # the other measured workloads of the layer, each timed the same way
+        # (inputs resident in HBM, warm-up steps, then timed steps) after the
+        # main one's buffers are released
+        extras = {}
+        for name, e_bwd, flags in (("h7168_i2048_e32_k8_mxfp8_zipf", False, {}),
+                                   ("h7168_i2048_e32_k8_mxfp8_shared_fwdbwd", True, {}),
+                                   ("h7168_i2048_e32_k8_bf16", False, {}),
+                                   ("h7168_i2048_e32_k8_bf16", False, {"launch_per_gemm": True})):
+            key = "%s/%s%s" % (name, "fwdbwd" if e_bwd else "fwd", "/per_gemm" if flags else "")
+            log("timing", key)
+            r = measure(moe, torch, WORKLOADS[name], e_bwd, args.extra_steps, 2, mfma_loops=False, **flags)
+            extras[key] = {"value": r["value"], "unit": "tokens/s", "ms_per_step": r["ms_per_step"],
+                           "steps": args.extra_steps, "config": r["config"], "roofline": r["roofline"],
+                           "tflops_by_role": r["detail"]["tflops_by_role"],
+                           "hbm_gbs_by_role": r["detail"]["hbm_gbs_by_role"],
+                           "per_step_ms": r["detail"]["per_step_ms"]}
+        res["detail"]["workloads"] = extras
+    if not args.no_cpu_baseline:
+        n = args.cpu_sample or 2048
+        res["cpu_baseline"] = cpu_baseline(inp, n, bwd)
+    print(json.dumps(res), flush=True)
+
+
+def measure(moe, torch, w, bwd: bool, steps: int, warmup: int, comm_cus: int = 0, ring_slots: int = 0,
+            launch_per_gemm: bool = False, cold_cache: bool = False, mfma_loops: bool = False,
+            keep_inputs: bool = False) -> dict:
+    """Times `steps` layer steps of workload `w` (forward, or forward + backward)
+    after `warmup` untimed ones, with every input already in HBM; returns the
+    throughput, the dominant kernel's roofline position and the per-kernel-kind
+    breakdown (HIP events recorded by the library on the stream each kernel
+    runs on).  Releases every device buffer and the timing events before it
+    returns."""
+    from moe_inputs import make_inputs
+    t_gen = time.time()
+    mx = w.prec == "mxfp8"
+    inp = make_inputs(w, with_dout=bwd)
+    log("%s: inputs drawn in %.1f s" % (w.name, time.time() - t_gen))
+    flags = (moe.MOE_F_SHARED_EXPERT if w.shared_expert else 0) | (moe.MOE_F_LAUNCH_PER_GEMM if launch_per_gemm else 0)
     cfg = moe.make_cfg(w.T, w.H, w.I, w.E, w.k, minibatch=w.minibatch, flags=flags,
                        prec=moe.MOE_PREC_MXFP8 if mx else moe.MOE_PREC_BF16,
-                       comm_cus=args.comm_cus, ring_slots=args.ring_slots)
+                       comm_cus=comm_cus, ring_slots=ring_slots)
     sizes = moe.moe_query_sizes(cfg)
     bufs = moe.alloc_buffers(cfg, with_saved=bwd)
     dev = lambda t: None if t is None else t.to("cuda").contiguous()
@@ -125,52 +186,55 @@ def main():
     torch.cuda.synchronize()
     del Wg, Wu, Wd
     out = torch.empty_like(x)
+    T, H, I, E, k = w.T, w.H, w.I, w.E, w.k
+    grads = {}
     if bwd:
-        T, H, I, E = w.T, w.H, w.I, w.E
-        dout = dev(inp.dout)
-        dx = torch.empty_like(x)
-        dWg = torch.empty(E, H, I, dtype=torch.float32, device="cuda")
-        dWu = torch.empty_like(dWg)
-        dWd = torch.empty(E, I, H, dtype=torch.float32, device="cuda")
-        dWr = torch.empty(H, E, dtype=torch.float32, device="cuda")
-        dWs = torch.empty(3 * H * I, dtype=torch.float32, device="cuda") if w.shared_expert else None
+        grads = dict(dout=dev(inp.dout), dx=torch.empty_like(x),
+                     dWg=torch.empty(E, H, I, dtype=torch.float32, device="cuda"),
+                     dWu=torch.empty(E, H, I, dtype=torch.float32, device="cuda"),
+                     dWd=torch.empty(E, I, H, dtype=torch.float32, device="cuda"),
+                     dWr=torch.empty(H, E, dtype=torch.float32, device="cuda"),
+                     dWs=torch.empty(3 * H * I, dtype=torch.float32, device="cuda") if w.shared_expert else None)
 
     def step():
         moe.moe_layer_fwd(cfg, Wr, bias, bufs.packed, x, out, bufs.ws, saved=bufs.saved)
         if bwd:
-            moe.moe_layer_bwd(cfg, Wr, bias, bufs.packed, x, dout, bufs.saved, dx, dWg, dWu, dWd, dWr,
-                              bufs.ws, dWs=dWs)
+            g = grads
+            moe.moe_layer_bwd(cfg, Wr, bias, bufs.packed, x, g["dout"], bufs.saved, g["dx"], g["dWg"], g["dWu"],
+                              g["dWd"], g["dWr"], bufs.ws, dWs=g["dWs"])
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     moe.moe_timing_enable(True)
     torch.cuda.synchronize()
-    if args.cold_cache:
-        # the scratch writes stay outside the timed events (and outside the
-        # per-kernel timing, which only sees the library's launches)
-        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-        for i in range(args.steps):
-            scratch.fill_(i & 0xff)
-            evs[i][0].record()
-            step()
-            evs[i][1].record()
-        torch.cuda.synchronize()
-        elapsed = sum(a.elapsed_time(b) for a, b in evs) / 1e3
-        del scratch
-    else:
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            step()
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
-    kt = moe.moe_timing_read()
-    moe.moe_timing_enable(False)
+    try:
+        if cold_cache:
+            # the scratch writes stay outside the timed events (and outside the
+            # per-kernel timing, which only sees the library's launches)
+            scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(steps)]
+            for i in range(steps):
+                scratch.fill_(i & 0xff)
+                evs[i][0].record()
+                step()
+                evs[i][1].record()
+            torch.cuda.synchronize()
+            elapsed = sum(a.elapsed_time(b) for a, b in evs) / 1e3
+            del scratch
+        else:
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                step()
+            torch.cuda.synchronize()
+            elapsed = time.perf_counter() - t0
+        kt = moe.moe_timing_read()
+    finally:
+        moe.moe_timing_enable(False)  # waits for the recorded launches and destroys the events
 
-    T, H, I, E, k = w.T, w.H, w.I, w.E, w.k
-    flops = role_flops(T, H, I, k, w.shared_expert, mx, bwd, kt["layer"][1] > 0)
+    layer_kernel = kt["layer"][0] > 0
+    flops = role_flops(T, H, I, k, w.shared_expert, mx, bwd, layer_kernel)
     symbol = {"gemm_gate_up": "mx_gemm_kernel<0>" if mx else "grouped_gemm_kernel<0>",
               "gemm_down": "mx_gemm_kernel<1>" if mx else "grouped_gemm_kernel<1>",
               "dgrad_down": "mx_gemm_kernel<1>" if mx else "grouped_gemm_kernel<1>",
@@ -181,53 +245,41 @@ def main():
     for kd, fl in flops.items():
         n, ms = kt[kd]
         agg = by_sym.setdefault(symbol[kd], [0.0, 0.0, 0, []])
-        agg[0] += fl * args.steps
+        agg[0] += fl * steps
         agg[1] += ms
         agg[2] += n
         agg[3].append(kd)
-    ms_step = elapsed * 1e3 / args.steps
-    value = T * args.steps / elapsed
+    ms_step = elapsed * 1e3 / steps
     dom = max(by_sym, key=lambda sy: by_sym[sy][1])
     dom_flops, ms_dom, n_dom, dom_roles = by_sym[dom]
     achieved = dom_flops / (ms_dom / 1e3) / 1e12
     # the scaled-MFMA kernels (and the MXFP8 layer kernel) are priced at the FP8 peak
     peak = PEAK_FP8_TFLOPS if (mx and (dom.startswith("mx_") or dom == "mega_kernel<true>")) else PEAK_BF16_TFLOPS
-    total_flops = sum(flops.values())
+    nbytes = role_bytes(T, H, I, k, E, w.shared_expert, mx, bwd, layer_kernel)
     res = {
-        "metric": "MoE layer %s tokens/s at H=%d I=%d (%s) + %% MFMA peak" % (
-            "fwd+bwd" if bwd else "fwd", H, I, "MXFP8" if mx else "bf16"),
-        "value": value,
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "value": T * steps / elapsed,
         "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "mxfp8-e4m3" if mx else "bf16",
-        "data": "synthetic",
         "config": {"workload": w.name, "tokens": T, "hidden": H, "intermediate": I, "experts": E,
                    "top_k": k, "minibatch": sizes.minibatch, "minibatches": sizes.num_minibatches,
-                   "router_bias": w.router_bias, "shared_expert": w.shared_expert,
+                   "router_bias": w.router_bias, "shared_expert": w.shared_expert, "precision": w.prec,
                    "ring_slots": sizes.ring_slots, "comm_cus": sizes.comm_cus,
-                   "forward": "per-GEMM launches" if kt["layer"][1] == 0 else "persistent layer kernel",
+                   "forward": "persistent layer kernel" if layer_kernel else "per-GEMM launches",
                    "pass": "forward+backward" if bwd else "forward",
-                   "cache": "cold: 512 MiB written before each step" if args.cold_cache else "warm"},
+                   "cache": "cold: 512 MiB written before each step" if cold_cache else "warm"},
         "roofline": {"bound": "mfma", "kernel": "moe::" + dom, "roles": dom_roles,
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": traffic_for(dom, w.name),
                      "avg_launch_ms": ms_dom / max(n_dom, 1), "launches": n_dom},
         "detail": {
-            "layer_mfma_frac": total_flops / (ms_step / 1e3) / 1e12 / (PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS),
-            "tflops_by_role": {kd: flops[kd] * args.steps / (kt[kd][1] / 1e3) / 1e12
-                               for kd in flops if kt[kd][1] > 0},
-            "per_step_ms": {kind: v[1] / args.steps for kind, v in kt.items() if kind != "dropped"},
+            "layer_mfma_frac": sum(flops.values()) / (ms_step / 1e3) / 1e12 / (PEAK_FP8_TFLOPS if mx else PEAK_BF16_TFLOPS),
+            "tflops_by_role": {kd: flops[kd] * steps / (kt[kd][1] / 1e3) / 1e12 for kd in flops if kt[kd][1] > 0},
+            # algorithmic bytes (padding rows excluded) over the kind's event time
+            "hbm_gbs_by_role": {kd: b * steps / (kt[kd][1] / 1e3) / 1e9 for kd, b in nbytes.items() if kt[kd][1] > 0},
+            "per_step_ms": {kind: v[1] / steps for kind, v in kt.items() if kind != "dropped"},
             "timing_dropped": kt["dropped"],
         },
     }
-
-    if not args.no_mfma_loop:
+    if mfma_loops:
         loops = {"bf16": mfma_loop(moe, torch, x, inp.Wg, False)}
         if mx:
             loops["mxfp8"] = mfma_loop(moe, torch, x, inp.Wg, True)
@@ -235,10 +287,40 @@ def main():
         loop = loops["mxfp8" if peak == PEAK_FP8_TFLOPS else "bf16"]
         res["roofline"]["sustained_peak"] = loop["tflops"]
         res["roofline"]["frac_of_sustained"] = achieved / loop["tflops"]
-    if not args.no_cpu_baseline:
-        n = args.cpu_sample or (256 if bwd else 2048)
-        res["cpu_baseline"] = cpu_baseline(inp, n, bwd)
-    print(json.dumps(res), flush=True)
+    if keep_inputs:
+        res["inputs"] = inp
+    del bufs, x, Wr, bias, out, grads
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def role_bytes(T: int, H: int, I: int, k: int, E: int, shared: bool, mx: bool, bwd: bool, layer_kernel: bool) -> dict:
+    """Algorithmic HBM bytes per step of the data-movement kernel kinds (routed
+    and shared rows; padding rows excluded):
+      route: x read once, router weight, indices and weights written (MXFP8:
+        the dispatch-side E4M3 codes and E8M0 scales of every token row);
+      combine (per-GEMM forward): k (+1 shared) expert-output rows read and one
+        output row written per token; in a backward step the kind is the
+        reverse-dispatch: k (+1) input-gradient rows read, dx written;
+      gather (backward): reverse-combine (dout, x and Y rows read; transposed
+        dY and x written; MXFP8 codes + scales of dY) and SwiGLU backward (dH
+        and g|u read, fp32 under MXFP8; dG|dU row-major for bf16 GEMMs,
+        transposed dG|dU and h written; MXFP8 codes + scales of dG|dU)."""
+    ks = k + (1 if shared else 0)
+    R, Rr = T * ks, T * k  # rows (routed + shared), routed rows
+    q = 1.0 + 1.0 / 32  # MXFP8 code + scale bytes per element
+    b = {"route": T * H * 2 + H * E * 4 + T * k * 8 + (T * H * q if mx else 0.0)}
+    if bwd:
+        b["combine"] = T * (ks * H * 2 + H * 2)
+        rows_mx = Rr if mx else 0
+        rows_bf16 = R - rows_mx
+        f = 4 if mx else 2
+        b["gather"] = (R * (3 * H * 2 + 2 * H * 2) + rows_mx * H * q
+                       + R * (I * f + 2 * I * f + 2 * I * 2 + I * 2) + rows_bf16 * 2 * I * 2 + rows_mx * 2 * I * q)
+    elif not layer_kernel:
+        b["combine"] = T * (ks * H * 2 + H * 2)
+    return b
 
 
 def mfma_loop(moe, torch, x, w, mx: bool) -> dict:
@@ -399,9 +481,23 @@ def summarize_traffic(fetch_csv: str, write_csv: str, workload: str, copy_mib: i
     print(json.dumps({k: v["hbm_bytes_per_launch"] for k, v in rec["kernels"].items()}, indent=1))
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, n_tokens: int, bwd: bool) -> dict:
     """The CPU oracle (as it stands) on the first n_tokens tokens of the workload,
-    taken as a layer of n_tokens tokens with the same weights."""
+    taken as a layer of n_tokens tokens with the same weights.  The oracle
+    widens every expert's bf16 weights to fp64 (a cost independent of the
+    token count), timed on its own as well so that the sample's share of it is
+    visible."""
     import numpy as np
     import threadpoolctl
     import oracle
@@ -411,19 +507,27 @@ def cpu_baseline(inp, n_tokens: int, bwd: bool) -> dict:
     sub = LayerInputs(inp.w.replace(T=n), inp.x[:n], inp.Wr, inp.bias, inp.Wg, inp.Wu, inp.Wd,
                       inp.Wsg, inp.Wsu, inp.Wsd, inp.dout[:n] if inp.dout is not None else None)
     oracle.router_logits(np.zeros((1, inp.w.H), np.float32), np.zeros((inp.w.H, 1), np.float32))
-    t0 = time.perf_counter()
     mx = inp.w.prec == "mxfp8"
+    t0 = time.perf_counter()
     fwd = oracle.layer_forward(sub, keep=bwd)
     if bwd:
         oracle.layer_backward(sub, fwd=fwd)
     dt = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for e in range(inp.w.E):  # the per-expert fp64 widening alone
+        for t in (inp.Wg, inp.Wu, inp.Wd):
+            oracle.as_f64(t[e])
+    dt_w = time.perf_counter() - t0
     blas = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
     omp = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": n / dt, "unit": "tokens/s", "cores": max(blas, omp), "kind": "oracle",
+            "cpu": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": "first %d of %d tokens as a %d-token layer: fixed-order fp32 routing (C, OpenMP) + "
-                      "fp64 expert SwiGLU FFN and combine%s%s (numpy/OpenBLAS); %.1f s"
+                      "fp64 expert SwiGLU FFN and combine%s%s (numpy/OpenBLAS, fp64 throughout, not tuned); "
+                      "%.1f s, of which about %.1f s widen the expert weights to fp64 %s"
                       % (n, inp.w.T, n, " + fp64 backward" if bwd else "",
-                         " with the MXFP8 quantisation points (C quantiser)" if mx else "", dt)}
+                         " with the MXFP8 quantisation points (C quantiser)" if mx else "", dt, dt_w,
+                         "(twice: forward and backward)" if bwd else "(once)")}
 
 
 if __name__ == "__main__":

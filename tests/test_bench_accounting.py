@@ -49,3 +49,19 @@ def test_bf16_runs_shared_rows_with_the_routed_ones():
     f = bench.role_flops(T, H, I, K, True, False, True, True)
     assert "shared_gemm" not in f
     assert f["dgrad_down"] == 2 * HI * (T * K + T) and f["dgrad_gate_up"] == 4 * HI * (T * K + T)
+
+
+def test_data_movement_bytes():
+    """Per token: combine reads k (+1 shared) bf16 rows of H and writes one;
+    route reads the token's bf16 row once (plus the router weight once per
+    step) and writes k indices and k weights; under MXFP8 it also writes the
+    row's E4M3 codes and one E8M0 scale per 32 elements."""
+    E = 8
+    b = bench.role_bytes(T, H, I, K, E, False, False, False, False)
+    assert b["combine"] == T * (K * H * 2 + H * 2)
+    assert b["route"] == T * H * 2 + H * E * 4 + T * K * 8
+    bm = bench.role_bytes(T, H, I, K, E, True, True, False, True)
+    assert "combine" not in bm  # the layer kernel's combine is not timed on its own
+    assert bm["route"] - b["route"] == T * H * (1 + 1 / 32)
+    bb = bench.role_bytes(T, H, I, K, E, True, False, True, True)
+    assert bb["combine"] == T * ((K + 1) * H * 2 + H * 2) and bb["gather"] > 0
