@@ -46,7 +46,7 @@ struct Plan {
     // forward workspace (bytes): routing, MXFP8 x, every minibatch's layout
     // (first-tile maps [nmb][Et+1], then nmb blocks of lay_bytes), layer-kernel
     // counters, ring slots (h, Y, MXFP8 h codes and scales)
-    size_t ws_status, ws_idx, ws_w, ws_mt, ws_rows, ws_lay0, ws_cnt, ws_slot0, slot_bytes, ws_fwd;
+    size_t ws_status, ws_idx, ws_w, ws_mt, ws_prs, ws_rows, ws_lay0, ws_cnt, ws_slot0, slot_bytes, ws_fwd;
     size_t sl_h, sl_y, sl_hq, sl_sh;
     bool mega;  // forward through the persistent layer kernel
     size_t ws_xq, ws_sx;  // MXFP8 codes and scales of x
@@ -54,7 +54,7 @@ struct Plan {
     // under MXFP8) and Y [rpad][H]
     size_t sv_idx, sv_w, sv_mb0, sv_mb, sv_y, saved;
     // backward workspace (bytes)
-    size_t wb_wrt, wb_mt, wb_rows, wb_lay0, lay_bytes, ly_hdr, ly_prow_token, ly_tok_prow, ly_prow_slot;
+    size_t wb_wrt, wb_mt, wb_prs, wb_rows, wb_lay0, lay_bytes, ly_hdr, ly_prow_token, ly_tok_prow, ly_prow_slot;
     size_t wb_dyt, wb_xgt, wb_dgut, wb_ht, wb_dsel, wb_dgu, wb_dh, wb_dx, wb_dgp, wb_roww, ws_bwd;
     size_t wb_dyq, wb_sdy, wb_dguq, wb_sdgu;  // MXFP8 operands of the input-gradient GEMMs
     size_t wb_dlog, wb_dwrp;                  // dense d out / d logits, router-gradient partial sums
@@ -173,6 +173,7 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
         p->lay_bytes = l;
     }
     p->ws_mt = o; o = align_up(o + (size_t)p->nmb * (Et + 1) * 4);
+    p->ws_prs = o; o = align_up(o + (size_t)p->nmb * (Et + 1) * 4);
     p->ws_rows = o; o = align_up(o + (size_t)p->nmb * (Et + 1) * 4);
     p->ws_lay0 = o; o = align_up(o + (size_t)p->nmb * p->lay_bytes);
     p->ws_cnt = o; o = align_up(o + (size_t)(3 * p->nmb + 1) * 4);
@@ -198,6 +199,7 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     o = kAlign;  // device status word
     p->wb_wrt = o; o = align_up(o + (size_t)c->E * H * 4);
     p->wb_mt = o; o = align_up(o + nmb * (Et + 1) * 4);
+    p->wb_prs = o; o = align_up(o + nmb * (Et + 1) * 4);
     p->wb_rows = o; o = align_up(o + nmb * (Et + 1) * 4);
     p->wb_lay0 = o; o += nmb * p->lay_bytes;
     p->wb_dyt = o; o = align_up(o + nmb * H * rp * 2);
@@ -400,6 +402,7 @@ static moe_status enqueue_fwd(const moe_cfg* cfg, const Plan& p, const moe_weigh
     const uint16_t* W1t = (const uint16_t*)(pk + p.pk_w1t);
     const uint16_t* W2t = (const uint16_t*)(pk + p.pk_w2t);
     int32_t* mt_all = (int32_t*)(wsb + p.ws_mt);
+    int32_t* prs_all = (int32_t*)(wsb + p.ws_prs);
     int32_t* rows_all = (int32_t*)(wsb + p.ws_rows);
     uint8_t* lay0 = wsb + p.ws_lay0;
     uint8_t* xq = wsb + p.ws_xq;
@@ -416,13 +419,14 @@ static moe_status enqueue_fwd(const moe_cfg* cfg, const Plan& p, const moe_weigh
         LayoutOut o{};
         o.hdr = (LayoutHeader*)(lay0 + p.ly_hdr);
         o.mt_start = mt_all;
+        o.prow_start = prs_all;
         o.prow_token = (int32_t*)(lay0 + p.ly_prow_token);
         o.tok_prow = (int32_t*)(lay0 + p.ly_tok_prow);
         o.rows_e = rows_all;
         o.tok_prow_ld = p.ld_tok_prow;
         LayoutStrides ls{};
         ls.hdr = (int64_t)p.lay_bytes / (int64_t)sizeof(LayoutHeader);
-        ls.mt_start = ls.rows_e = p.Et + 1;
+        ls.mt_start = ls.rows_e = ls.prow_start = p.Et + 1;
         ls.prow_token = ls.tok_prow = (int64_t)p.lay_bytes / 4;
         TIMED(MOE_K_LAYOUT, s, launch_layout_batched(idx, p.T, p.Mb, p.E, p.k, p.shared ? 1 : 0, o, ls, s));
     }
@@ -461,7 +465,7 @@ static moe_status enqueue_fwd(const moe_cfg* cfg, const Plan& p, const moe_weigh
         a.comm = p.comm_cus; a.e_end = p.Et; a.e_mx = p.mx ? p.E : 0; a.with_shared = p.shared ? 1 : 0;
         a.ld_tok_prow = p.ld_tok_prow; a.mx = p.mx ? 1 : 0; a.group = p.group;
         a.lay0 = lay0; a.lay_bytes = p.lay_bytes; a.ly_prow_token = p.ly_prow_token; a.ly_tok_prow = p.ly_tok_prow;
-        a.mt_all = mt_all; a.rows_all = rows_all; a.mt_ld = p.Et + 1;
+        a.mt_all = mt_all; a.prs_all = prs_all; a.rows_all = rows_all; a.mt_ld = p.Et + 1;
         a.g1 = g1; a.g2 = g2; a.m1 = m1; a.m2 = m2;
         a.g1.e_begin = a.g2.e_begin = 0;
         a.slot0 = wsb + p.ws_slot0; a.slot_bytes = p.slot_bytes;
@@ -486,6 +490,7 @@ static moe_status enqueue_fwd(const moe_cfg* cfg, const Plan& p, const moe_weigh
         uint8_t* lay = lay0 + (size_t)b * p.lay_bytes;
         LayoutHeader* hdr = (LayoutHeader*)(lay + p.ly_hdr);
         int32_t* mt = mt_all + (size_t)b * (p.Et + 1);
+        int32_t* prs = prs_all + (size_t)b * (p.Et + 1);
         int32_t* prow_token = (int32_t*)(lay + p.ly_prow_token);
         int32_t* tok_prow = (int32_t*)(lay + p.ly_tok_prow);
         uint8_t* slot = wsb + p.ws_slot0 + (size_t)(b % p.slots) * p.slot_bytes;
@@ -507,23 +512,24 @@ static moe_status enqueue_fwd(const moe_cfg* cfg, const Plan& p, const moe_weigh
         } else {
             if (p.mx) {
                 MxGemmArgs m = m1;
-                m.a_row_map = prow_token; m.mt_start = mt; m.hdr = hdr;
+                m.a_row_map = prow_token; m.mt_start = mt; m.prow_start = prs; m.hdr = hdr;
                 m.Cq = slot + p.sl_hq; m.Cs = slot + p.sl_sh; m.GU = guf; m.rows_e = rows_all + (size_t)b * (p.Et + 1);
                 TIMED(MOE_K_GEMM_GATE_UP, s, launch_mx_gemm(m, kEpiSwiGLU, grid, s));
             }
             GemmArgs ga = g1;
-            ga.a_row_map = prow_token; ga.mt_start = mt; ga.hdr = hdr; ga.rows_e = rows_all + (size_t)b * (p.Et + 1);
+            ga.a_row_map = prow_token; ga.mt_start = mt; ga.prow_start = prs; ga.hdr = hdr; ga.rows_e = rows_all + (size_t)b * (p.Et + 1);
             ga.C = hbuf; ga.GU = gubuf; ga.GUf = guf;
             if (e_bf16 < p.Et)
                 TIMED(p.mx ? MOE_K_SHARED_GEMM : MOE_K_GEMM_GATE_UP, s, launch_grouped_gemm(ga, kEpiSwiGLU, grid, s));
             if (p.mx) {
                 MxGemmArgs m = m2;
-                m.A = slot + p.sl_hq; m.SA = slot + p.sl_sh; m.mt_start = mt; m.hdr = hdr; m.C = ybuf;
+                m.A = slot + p.sl_hq; m.SA = slot + p.sl_sh; m.mt_start = mt; m.prow_start = prs; m.hdr = hdr;
+                m.C = ybuf;
                 m.rows_e = rows_all + (size_t)b * (p.Et + 1);
                 TIMED(MOE_K_GEMM_DOWN, s, launch_mx_gemm(m, kEpiStore, grid, s));
             }
             GemmArgs gb = g2;
-            gb.A = hbuf; gb.mt_start = mt; gb.hdr = hdr; gb.C = ybuf; gb.rows_e = rows_all + (size_t)b * (p.Et + 1);
+            gb.A = hbuf; gb.mt_start = mt; gb.prow_start = prs; gb.hdr = hdr; gb.C = ybuf; gb.rows_e = rows_all + (size_t)b * (p.Et + 1);
             if (e_bf16 < p.Et)
                 TIMED(p.mx ? MOE_K_SHARED_GEMM : MOE_K_GEMM_DOWN, s, launch_grouped_gemm(gb, kEpiStore, grid, s));
         }
@@ -570,6 +576,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
     uint8_t* wsb = (uint8_t*)ws;
     float* WrT = (float*)(wsb + p.wb_wrt);
     int32_t* mt_all = (int32_t*)(wsb + p.wb_mt);
+    int32_t* prs_all = (int32_t*)(wsb + p.wb_prs);
     uint16_t* dYT_all = (uint16_t*)(wsb + p.wb_dyt);
     uint16_t* xgT_all = (uint16_t*)(wsb + p.wb_xgt);
     uint16_t* dGUT_all = (uint16_t*)(wsb + p.wb_dgut);
@@ -588,6 +595,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
         LayoutOut o{};
         o.hdr = (LayoutHeader*)(lay0 + p.ly_hdr);
         o.mt_start = mt_all;
+        o.prow_start = prs_all;
         o.prow_token = (int32_t*)(lay0 + p.ly_prow_token);
         o.tok_prow = (int32_t*)(lay0 + p.ly_tok_prow);
         o.prow_slot = (int32_t*)(lay0 + p.ly_prow_slot);
@@ -595,7 +603,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
         o.tok_prow_ld = p.ld_tok_prow;
         LayoutStrides ls{};
         ls.hdr = (int64_t)p.lay_bytes / (int64_t)sizeof(LayoutHeader);
-        ls.mt_start = ls.rows_e = Et + 1;
+        ls.mt_start = ls.rows_e = ls.prow_start = Et + 1;
         ls.prow_token = ls.tok_prow = ls.prow_slot = (int64_t)p.lay_bytes / 4;
         TIMED(MOE_K_LAYOUT, s, launch_layout_batched(idx, p.T, p.Mb, E, k, p.shared ? 1 : 0, o, ls, s));
     }
@@ -614,6 +622,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
     for (int b0 = 0; b0 < p.nmb; b0 += p.bchunk) {
         const int b1 = (b0 + p.bchunk) < p.nmb ? b0 + p.bchunk : p.nmb;
         const int32_t* mt_c = mt_all + (size_t)b0 * (Et + 1);
+        const int32_t* prs_c = prs_all + (size_t)b0 * (Et + 1);
         const int32_t* rows_c = rows_all + (size_t)b0 * (Et + 1);
         for (int b = b0; b < b1; ++b) {
             const size_t j = (size_t)(b - b0);
@@ -631,7 +640,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             // MXFP8: dY quantised from fp32 here (along H, the down input-gradient GEMM's K)
             rc.dYq = p.mx ? wsb + p.wb_dyq + j * rp * H : nullptr;
             rc.sdY = p.mx ? wsb + p.wb_sdy + j * mx_groups(H) * rp * 4 : nullptr;
-            rc.dyq_tile_end = mt_all + (size_t)b * (Et + 1) + e_bf16;
+            rc.dyq_row_end = prs_all + (size_t)b * (Et + 1) + e_bf16;
             TIMED(MOE_K_GATHER, s, launch_rcomb_gather(rc, (int)rp, s));
         }
         if (p.mx) {
@@ -640,7 +649,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             m1.SA = wsb + p.wb_sdy; m1.sa_kstride = rp * 4;
             m1.B = pk + p.pk_wdq; m1.b_stride = (int64_t)I * H;
             m1.SB = pk + p.pk_sd; m1.sb_stride = mx_groups(H) * I * 4; m1.sb_kstride = (int64_t)I * 4;
-            m1.N = I; m1.K = H; m1.mt_start = mt_c; m1.hdr = nullptr; m1.e_begin = 0; m1.e_end = E;
+            m1.N = I; m1.K = H; m1.mt_start = mt_c; m1.prow_start = prs_c; m1.hdr = nullptr; m1.e_begin = 0; m1.e_end = E;
             m1.C = nullptr; m1.ldc = I; m1.Cq = nullptr; m1.Cs = nullptr; m1.cs_rows = 0; m1.GU = nullptr;
             m1.Cf = dHf; m1.rows_e = rows_c;
             m1.nmb = b1 - b0; m1.mt_ld = Et + 1; m1.a_mb = rp * H; m1.sa_mb = mx_groups(H) * rp * 4; m1.c_mb = rp * I;
@@ -656,7 +665,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             g1.lda = H;
             g1.B = Wdc; g1.b_stride = (int64_t)I * H;
             g1.C = dH; g1.ldc = I; g1.N = I; g1.K = H;
-            g1.mt_start = mt_c; g1.hdr = nullptr; g1.Et = Et; g1.GU = nullptr; g1.e_begin = e_bf16; g1.e_end = Et;
+            g1.mt_start = mt_c; g1.prow_start = prs_c; g1.hdr = nullptr; g1.Et = Et; g1.GU = nullptr; g1.e_begin = e_bf16; g1.e_end = Et;
             g1.GUf = nullptr; g1.Cf = dHf; g1.rows_e = rows_c;
             g1.nmb = b1 - b0; g1.mt_ld = Et + 1; g1.c_mb = rp * I;
             TIMED(p.mx ? MOE_K_SHARED_GEMM : MOE_K_DGRAD_DOWN, s, launch_grouped_gemm(g1, kEpiStore, grid, s));
@@ -669,7 +678,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             SwigluBwdArgs sb{};
             sb.dH = p.mx ? nullptr : dH + bh; sb.GU = (const uint16_t*)svb; sb.hdr = (LayoutHeader*)(lay + p.ly_hdr);
             sb.dGU = dGU + 2 * bh; sb.dGUT = dGUT_all + (size_t)b * 2 * I * rp; sb.HT = HT_all + (size_t)b * I * rp;
-            sb.dgu_tile0 = mt_all + (size_t)b * (Et + 1) + e_bf16;  // bf16: tile 0 (every row)
+            sb.dgu_row0 = prs_all + (size_t)b * (Et + 1) + e_bf16;  // bf16: row 0 (every row)
             sb.I = I; sb.ldt = rp;
             // MXFP8: fp32 inputs, dG|dU quantised here (along I, the gate|up input-gradient GEMM's K)
             sb.dHf = p.mx ? dHf + bh : nullptr; sb.GUf = p.mx ? (const float*)svb : nullptr;
@@ -683,7 +692,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             m2.SA = wsb + p.wb_sdgu; m2.sa_kstride = rp * 4;
             m2.B = pk + p.pk_wguq; m2.b_stride = (int64_t)H * 2 * I;
             m2.SB = pk + p.pk_sgu; m2.sb_stride = mx_groups(2 * I) * H * 4; m2.sb_kstride = (int64_t)H * 4;
-            m2.N = H; m2.K = 2 * I; m2.mt_start = mt_c; m2.hdr = nullptr; m2.e_begin = 0; m2.e_end = E;
+            m2.N = H; m2.K = 2 * I; m2.mt_start = mt_c; m2.prow_start = prs_c; m2.hdr = nullptr; m2.e_begin = 0; m2.e_end = E;
             m2.C = dXb; m2.ldc = H; m2.Cq = nullptr; m2.Cs = nullptr; m2.cs_rows = 0; m2.GU = nullptr;
             m2.Cf = nullptr; m2.rows_e = rows_c;
             m2.nmb = b1 - b0; m2.mt_ld = Et + 1; m2.a_mb = rp * 2 * I; m2.sa_mb = mx_groups(2 * I) * rp * 4; m2.c_mb = rp * H;
@@ -694,7 +703,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             g2.A = dGU; g2.a_row_map = nullptr; g2.lda = 2 * I;
             g2.B = Wgu; g2.b_stride = (int64_t)H * 2 * I;
             g2.C = dXb; g2.ldc = H; g2.N = H; g2.K = 2 * I;
-            g2.mt_start = mt_c; g2.hdr = nullptr; g2.Et = Et;
+            g2.mt_start = mt_c; g2.prow_start = prs_c; g2.hdr = nullptr; g2.Et = Et;
             g2.GU = nullptr; g2.e_begin = e_bf16; g2.e_end = Et; g2.GUf = nullptr; g2.Cf = nullptr;
             g2.rows_e = rows_c;
             g2.nmb = b1 - b0; g2.mt_ld = Et + 1; g2.a_mb = rp * 2 * I; g2.c_mb = rp * H;
@@ -717,14 +726,14 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
     WgradArgs wa{};  // [dWg | dWu][e] = x_e^T [dG | dU]_e over every row of expert e
     wa.A = xgT_all; wa.B = dGUT_all; wa.ld = rp;
     wa.a_mb = (int64_t)H * rp * 2; wa.b_mb = (int64_t)2 * I * rp * 2;
-    wa.M = H; wa.N = 2 * I; wa.n_split = I; wa.Et = Et; wa.nmb = p.nmb; wa.mt_ld = Et + 1; wa.mt = mt_all; wa.rows = (const int32_t*)(wsb + p.wb_rows);
+    wa.M = H; wa.N = 2 * I; wa.n_split = I; wa.Et = Et; wa.nmb = p.nmb; wa.mt_ld = Et + 1; wa.prs = prs_all; wa.rows = (const int32_t*)(wsb + p.wb_rows);
     wa.C0 = dWg; wa.C1 = dWu;
     wa.Cs0 = p.shared ? dWs : nullptr; wa.Cs1 = p.shared ? dWs + (size_t)H * I : nullptr;
     TIMED(MOE_K_WGRAD, s, launch_wgrad(wa, grid, s));
     WgradArgs wd{};  // dWd[e] = h_e^T dY_e
     wd.A = HT_all; wd.B = dYT_all; wd.ld = rp;
     wd.a_mb = (int64_t)I * rp * 2; wd.b_mb = (int64_t)H * rp * 2;
-    wd.M = I; wd.N = H; wd.n_split = H; wd.Et = Et; wd.nmb = p.nmb; wd.mt_ld = Et + 1; wd.mt = mt_all; wd.rows = (const int32_t*)(wsb + p.wb_rows);
+    wd.M = I; wd.N = H; wd.n_split = H; wd.Et = Et; wd.nmb = p.nmb; wd.mt_ld = Et + 1; wd.prs = prs_all; wd.rows = (const int32_t*)(wsb + p.wb_rows);
     wd.C0 = dWd; wd.C1 = nullptr;
     wd.Cs0 = p.shared ? dWs + (size_t)2 * H * I : nullptr; wd.Cs1 = nullptr;
     TIMED(MOE_K_WGRAD, s, launch_wgrad(wd, grid, s));

@@ -24,8 +24,8 @@ constexpr int kTile = 64;
 //   row_w[prow]   = w (0 on padding rows), if row_w is set
 //   dYT[h][prow]  = the same, transposed (weight-gradient operand)
 //   xgT[h][prow]  = x[t][h], transposed (weight-gradient operand)
-//   dYq, sdY      = MXFP8 codes and scales of w * dout[t] (rows before tile
-//                   *dyq_tile_end), if dYq is set
+//   dYq, sdY      = MXFP8 codes and scales of w * dout[t] (rows before padded
+//                   row *dyq_row_end), if dYq is set
 //   dgp[prow][hb] = sum over the block's 64 columns of dout[t][h] * Y[prow][h]
 //                   (routed rows; in column order, then a fixed pair tree)
 //   dsel[prow]    = 0 (filled for routed rows by the reverse-dispatch)
@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void rcomb_gather_kernel(RcombArgs p) {
     __shared__ uint16_t sY[kTile][kTile + 2];
     __shared__ uint16_t sX[kTile][kTile + 2];
     const int prow0 = blockIdx.x * kTile, h0 = blockIdx.y * kTile;
-    if (prow0 >= p.hdr->m_tiles * BM) return;
+    if (prow0 >= p.hdr->prows) return;
     const int tid = threadIdx.x;
     const int r = tid >> 2, c0 = (tid & 3) * 16;
     const int prow = prow0 + r;
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(256) void rcomb_gather_kernel(RcombArgs p) {
         sX[c0 + c][r] = f32_to_bf16_rne(xv[c]);
     }
     // MXFP8 operand of the down input-gradient GEMM, from the fp32 values
-    if (p.dYq && prow < *p.dyq_tile_end * BM)
+    if (p.dYq && prow < *p.dyq_row_end)
         mx_quant_row64(dyf, tid & 3, p.dYq + (int64_t)prow * p.H + h0, p.sdY, p.ldt, prow, h0 / 64, p.H / 64);
     if (p.dY) {
         intx4* dst = (intx4*)(p.dY + (int64_t)prow * p.H + h0 + c0);
@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdArgs p) {
     __shared__ uint16_t sU[kTile][kTile + 2];
     __shared__ uint16_t sH[kTile][kTile + 2];
     const int prow0 = blockIdx.x * kTile, i0 = blockIdx.y * kTile;
-    if (prow0 >= p.hdr->m_tiles * BM) return;
+    if (prow0 >= p.hdr->prows) return;
     const int tid = threadIdx.x;
     const int r = tid >> 2, c0 = (tid & 3) * 16;
     const int64_t prow = prow0 + r;
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdArgs p) {
         sU[c0 + c][r] = du[c];
         sH[c0 + c][r] = hh[c];
     }
-    if (prow >= (int64_t)*p.dgu_tile0 * BM) {
+    if (prow >= (int64_t)*p.dgu_row0) {
         pack16_bf16(dg, (intx4*)(p.dGU + prow * 2 * I + i0 + c0));
         pack16_bf16(du, (intx4*)(p.dGU + prow * 2 * I + I + i0 + c0));
     }

@@ -19,6 +19,11 @@ constexpr int kWave = 64;
 // the tile kernels are in gemm_tile.hpp (bf16) and mx_tile.hpp (MXFP8).
 constexpr int BM = 256;
 constexpr int BN = 256;
+// Each expert's padded rows start on a kSegRows boundary.  An expert's M tiles
+// are BM rows, except its last, which has kSegRows when the expert's remaining
+// rows fit in it (a half tile: its second row of fragments is skipped), so an
+// expert pads to a multiple of 128 rows instead of 256.
+constexpr int kSegRows = 128;
 
 // The gate/up weights are packed so that every 64 output columns of the
 // first GEMM hold 32 gate columns followed by the 32 up columns with the same
@@ -34,11 +39,18 @@ constexpr int kMaxTopK = 16;
 // GEMM and combine kernels.  Experts are the E routed experts plus, when the
 // shared expert is on, one more "expert" E that takes every token in order.
 struct LayoutHeader {
-    int32_t m_tiles;  // total BM-row tiles over all experts
+    int32_t m_tiles;  // total M tiles over all experts
     int32_t rows;     // routed rows (T_mb * k)
     int32_t error;    // non-zero: an expert index was out of range
-    int32_t pad;
+    int32_t prows;    // padded rows over all experts (a multiple of kSegRows)
 };
+
+// Rows of M tile ml of an expert whose padded rows run from seg0 to seg1:
+// BM, or kSegRows for a last tile that is a half tile.
+__host__ __device__ __forceinline__ int tile_rows_of(int seg0, int seg1, int ml) {
+    const int left = seg1 - seg0 - ml * BM;
+    return left < BM ? left : BM;
+}
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
     uint32_t u = __builtin_bit_cast(uint32_t, f);

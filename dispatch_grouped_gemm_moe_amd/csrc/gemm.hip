@@ -33,6 +33,7 @@ void grouped_gemm_kernel(GemmArgs p) {
         if (p.nmb > 1) {
             const int b = minibatch_of_tile(p, v);
             q.mt_start += (int64_t)b * p.mt_ld;
+            q.prow_start += (int64_t)b * p.mt_ld;
             if (q.rows_e) q.rows_e += (int64_t)b * p.mt_ld;
             if (q.a_row_map) q.a_row_map += b * p.map_mb;
             else q.A += b * p.a_mb;
@@ -51,13 +52,13 @@ void grouped_gemm_kernel(GemmArgs p) {
 // expert e, minibatch by minibatch in order (a fixed summation order).
 // ---------------------------------------------------------------------------
 
-// K sequence of expert e's rows: for each minibatch b its padded row range
-// [mt_b[e], mt_b[e+1]) x BM, in 64-row K stages up to the last one holding a
-// routed row (the dY-side operand is zero on every padding row, so the
-// padding rows a stage takes in add nothing); A and B copies of minibatch b
-// lie a_mb / b_mb bytes after minibatch 0's.
+// K sequence of expert e's rows: for each minibatch b its padded rows from
+// prs_b[e] on, in 64-row K stages up to the last one holding a routed row
+// (the dY-side operand is zero on every padding row, so the padding rows a
+// stage takes in add nothing); A and B copies of minibatch b lie a_mb / b_mb
+// bytes after minibatch 0's.
 struct SegmentK {
-    const int32_t* mt;    // [nmb][mt_ld]
+    const int32_t* prs;   // [nmb][mt_ld] first padded row of each expert
     const int32_t* rows;  // [nmb][mt_ld]
     int mt_ld, e, nmb;
     int64_t a_mb, b_mb;
@@ -71,11 +72,11 @@ struct SegmentK {
             // the tile map is read-only here: read it through the constant
             // address space (scalar loads, counted by lgkmcnt) so that the
             // ring's vmcnt accounting sees only the ring's own loads
-            const __attribute__((address_space(4))) int32_t* cmt =
-                (const __attribute__((address_space(4))) int32_t*)mt;
+            const __attribute__((address_space(4))) int32_t* cprs =
+                (const __attribute__((address_space(4))) int32_t*)prs;
             const __attribute__((address_space(4))) int32_t* crows =
                 (const __attribute__((address_space(4))) int32_t*)rows;
-            row0 = (int64_t)cmt[(int64_t)b * mt_ld + e] * BM;
+            row0 = cprs[(int64_t)b * mt_ld + e];
             nsteps = ceil_div(crows[(int64_t)b * mt_ld + e], kBK8);
             step = 0;
         }
@@ -117,7 +118,7 @@ void wgrad_kernel(WgradArgs p) {
             aoff[i] = (uint32_t)(((int64_t)min(m0 + r, p.M - 1) * p.ld + lchunk * 8) * 2);
             boff[i] = (uint32_t)(((int64_t)min(n0 + r, p.N - 1) * p.ld + lchunk * 8) * 2);
         }
-        SegmentK kit{p.mt, p.rows, p.mt_ld, e, p.nmb, p.a_mb, p.b_mb};
+        SegmentK kit{p.prs, p.rows, p.mt_ld, e, p.nmb, p.a_mb, p.b_mb};
         floatx16 acc[2][4];
         tile_mainloop8<2>(acc, smem, (const char*)p.A, aoff, (const char*)p.B, boff, KT, kit);
         // columns < n_split go to C0, the rest to C1 (column - n_split); the
@@ -209,7 +210,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
                                                           const LayoutHeader* __restrict__ hdr,
                                                           uint16_t* __restrict__ Y, int64_t ldy) {
     const int prow = blockIdx.x;
-    if (prow >= hdr->m_tiles * BM) return;
+    if (prow >= hdr->prows) return;
     const int64_t src = (int64_t)prow_token[prow] * H;
     for (int c = threadIdx.x; c < H / 8; c += 256)
         *(intx4*)(Y + (int64_t)prow * ldy + c * 8) = *(const intx4*)(x + src + c * 8);

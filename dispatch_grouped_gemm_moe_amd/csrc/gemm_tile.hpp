@@ -157,10 +157,12 @@ __device__ __forceinline__ void mfma_block8(floatx16 (&acc)[2][4], const bf16x8 
 // columns 128wn + 32j .. +31; NV = fragments holding a valid row.  aoff/boff:
 // byte offsets of the 4 A and 4 B rows this lane loads per stage (tile rows
 // 32w + 8i + lane/8, swizzled chunk); kit.next() yields each stage's K offset.
+// load_a (wave-uniform): false for waves 4..7 of a half tile, whose A rows lie
+// outside the tile; they load only their B rows (no wave reads those A rows).
 template <int NV, class KIt>
 __device__ __forceinline__ void tile_mainloop8(floatx16 (&acc)[2][4], uint8_t* smem, const char* a_base,
                                                const uint32_t (&aoff)[4], const char* b_base,
-                                               const uint32_t (&boff)[4], int KT2, KIt kit) {
+                                               const uint32_t (&boff)[4], int KT2, KIt kit, bool load_a = true) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave >> 1, wn = wave & 1;
@@ -177,41 +179,61 @@ __device__ __forceinline__ void tile_mainloop8(floatx16 (&acc)[2][4], uint8_t* s
         if (issued < KT2) kit.next(ka, kb);
         ++issued;
     };
-    auto issue = [&](int slot) {
+    // load q of this lane for the stage going into `slot`: q = 0..3 its A rows,
+    // 4..7 its B rows
+    auto load1 = [&](int slot, int q) {
         uint8_t* base = smem + slot * kStageBytes8 + (wave * 32) * kRow8;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_global_load_lds((gbl_cvoid*)(a_base + ka + aoff[i]), (lds_void*)(base + i * 1024), 16, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_global_load_lds((gbl_cvoid*)(b_base + kb + boff[i]), (lds_void*)(base + kStageA8 + i * 1024), 16, 0, 0);
+        if (q < 4) {
+            if (load_a)
+                __builtin_amdgcn_global_load_lds((gbl_cvoid*)(a_base + ka + aoff[q]), (lds_void*)(base + q * 1024), 16,
+                                                 0, 0);
+        } else {
+            __builtin_amdgcn_global_load_lds((gbl_cvoid*)(b_base + kb + boff[q - 4]),
+                                             (lds_void*)(base + kStageA8 + (q - 4) * 1024), 16, 0, 0);
+        }
     };
     const int fr = lane & 31;
     const int arow_b = (wm * 32 + fr) * kRow8, brow_b = kStageA8 + (wn * 128 + fr) * kRow8;
     const int fsw = swz8(fr);  // a fragment's rows differ from fr by multiples of 32
-    auto frags = [&](int slot, int kk, bf16x8 (&a)[2], bf16x8 (&b)[4]) {
+    // fragment f of k-step kk of the stage in `slot`: f = 0, 1 A rows, 2..5 B rows
+    auto frag1 = [&](int slot, int kk, int f, bf16x8 (&a)[2], bf16x8 (&b)[4]) {
         const uint8_t* st = smem + slot * kStageBytes8;
         const int pc = ((kk * 2 + (lane >> 5)) ^ fsw) * 16;
+        if (f < 2) {
+            if (f < NV) a[f] = *(const bf16x8*)(st + arow_b + f * 128 * kRow8 + pc);
+        } else {
+            b[f - 2] = *(const bf16x8*)(st + brow_b + (f - 2) * 32 * kRow8 + pc);
+        }
+    };
+    auto frags = [&](int slot, int kk, bf16x8 (&a)[2], bf16x8 (&b)[4]) {
 #pragma unroll
-        for (int i = 0; i < NV; ++i) a[i] = *(const bf16x8*)(st + arow_b + i * 128 * kRow8 + pc);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = *(const bf16x8*)(st + brow_b + j * 32 * kRow8 + pc);
+        for (int f = 0; f < 6; ++f) frag1(slot, kk, f, a, b);
     };
     // Ring protocol (stage j in slot j % 2, 8 direct-to-LDS loads per lane
-    // and stage, counted by vmcnt): the prologue issues stages 0 and 1 and
-    // waits for stage 0 (vmcnt(8)); stage s runs four k-steps of 8 MFMAs, each
-    // reading the next k-step's fragments; before the last one it waits for
-    // stage s+1 (vmcnt(0)) and its own LDS reads (lgkmcnt(0)), then a barrier:
-    // no wave reads stage s any more, so its slot takes stage s+2, loaded under
-    // the last 8 MFMAs.  First the previous tile's stores leave the count and
-    // every wave is done with the previous tile's LDS.
+    // and stage, 4 for a wave without A rows, counted by vmcnt): the prologue
+    // issues stages 0 and 1 and waits for stage 0; stage s runs four k-steps of
+    // 8 MFMAs, each reading the next k-step's fragments; before the last one
+    // it waits for stage s+1 (vmcnt(0)) and its own LDS reads (lgkmcnt(0)),
+    // then a barrier: no wave reads stage s any more, so its slot takes stage
+    // s+2.  Those loads, and the next stage's first fragment reads, go out one
+    // per MFMA of the last k-step, pinned in that order: issued as a burst
+    // after the barrier, the eight waves' loads stalled their own MFMAs behind
+    // the busy load path (probe on the dense 20480 x 4096 x 7168 and
+    // 20480 x 7168 x 2048 GEMMs: +7% and +9%, same bits).  First the previous
+    // tile's stores leave the count and every wave is done with the previous
+    // tile's LDS.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     advance();
-    issue(0);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) load1(0, q);
     advance();
-    issue(1);
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+#pragma unroll
+    for (int q = 0; q < 8; ++q) load1(1, q);
+    if (load_a)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     __syncthreads();
     bf16x8 a0[2], b0[4], a1[2], b1[4];
     frags(0, 0, a0, b0);
@@ -232,11 +254,19 @@ __device__ __forceinline__ void tile_mainloop8(floatx16 (&acc)[2][4], uint8_t* s
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         __syncthreads();
         advance();  // offsets of stage s + 2
-        issue(slot);
-        frags(slot ^ 1, 0, a0, b0);  // a stale but in-bounds read after the last stage
-        mfma_block8<NV>(acc, a1, b1);
-        Interleave<4 * NV, 8, NV + 4>::run();
-        __builtin_amdgcn_sched_barrier(0);
+        // MFMA m of the last k-step, then load m of stage s + 2, then
+        // fragment read m of the next stage's first k-step (a stale but
+        // in-bounds read after the last stage)
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int i = m >> 2, j = m & 3;
+            if (i < NV) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1[j], a1[i], acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            load1(slot, m);
+            __builtin_amdgcn_sched_barrier(0);
+            if (m < 6) frag1(slot ^ 1, 0, m, a0, b0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         slot ^= 1;
     }
 }
@@ -252,9 +282,9 @@ struct DenseK8 {
 };
 
 // How a tile treats the padding rows of an expert's last tile (with
-// p.rows_e): kPadNone runs every fragment; kPadPerWave drops each wave's
-// fragments that hold only padding rows (a mainloop variant per count of
-// valid fragments).
+// p.rows_e): kPadNone runs every fragment, a half tile's too; kPadPerWave
+// drops each wave's fragments that hold only padding rows (a mainloop variant
+// per count of valid fragments) and a half tile's A loads past its rows.
 constexpr int kPadNone = 0, kPadPerWave = 1;
 
 // One 256 x 256 output tile (expert e, M tile ml of the expert, N tile ntile)
@@ -266,19 +296,24 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs p, int e, int ml, int n
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 1;
     const int KT2 = p.K / kBK8;
-    const int mt0 = p.mt_start[e];
-    const int prow0 = (mt0 + ml) * BM;
+    const int seg0 = p.prow_start[e];
+    const int prow0 = seg0 + ml * BM;
+    // BM rows, or kSegRows for an expert's last tile when it is a half tile:
+    // then the second row of fragments lies outside the tile and is skipped
+    const int trows = tile_rows_of(seg0, p.prow_start[e + 1], ml);
     const int n0 = ntile * BN;
 
     // Byte offsets of the 4 A rows and 4 B rows this lane loads per stage:
     // instruction i fills tile rows 32*wave + 8i .. +7 (lane/8 picks the row,
     // lane%8 the fixed LDS chunk; the lane loads the logical chunk stored there).
+    // A half tile's rows past kSegRows load its own rows again (cache hits):
+    // no read leaves the tile.
     uint32_t aoff[4], boff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = wave * 32 + i * 8 + (lane >> 3);
         const int lchunk = (lane & 7) ^ swz8(r);
-        const int prow = prow0 + r;
+        const int prow = prow0 + (r & (trows - 1));
         const int arow = p.a_row_map ? p.a_row_map[prow] : prow;
         aoff[i] = (uint32_t)(((int64_t)arow * p.lda + lchunk * 8) * 2);
         const int n = min(n0 + r, p.N - 1);
@@ -286,18 +321,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs p, int e, int ml, int n
     }
     floatx16 acc[2][4];
     const char* bbase = (const char*)(p.B + (int64_t)e * p.b_stride);
-    int nv = 2;
+    // kPadNone runs a half tile at full work (both fragment rows, every A load;
+    // its rows past kSegRows repeat its own rows and are not stored)
+    int nv = (kPad == kPadNone || trows == BM) ? 2 : 1;
     if (kPad != kPadNone && p.rows_e) {
         // fragment i of this wave holds tile rows 128i + 32wm .. +31
         const int valid = p.rows_e[e] - ml * BM, w32 = __builtin_amdgcn_readfirstlane(wm) * 32;
         nv = valid > 128 + w32 ? 2 : (valid > w32 ? 1 : 0);
     }
-    if (kPad == kPadNone) {
-        tile_mainloop8<2>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT2, DenseK8{});
-    } else switch (nv) {
-        case 2: tile_mainloop8<2>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT2, DenseK8{}); break;
-        case 1: tile_mainloop8<1>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT2, DenseK8{}); break;
-        default: tile_mainloop8<0>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT2, DenseK8{}); break;
+    // waves 4..7 hold tile rows 128..255: none of them in a half tile
+    const bool load_a = kPad == kPadNone || trows == BM || __builtin_amdgcn_readfirstlane(wave) < 4;
+    switch (nv) {
+        case 2: tile_mainloop8<2>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT2, DenseK8{}, load_a); break;
+        case 1: tile_mainloop8<1>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT2, DenseK8{}, load_a); break;
+        default: tile_mainloop8<0>(acc, smem, (const char*)p.A, aoff, bbase, boff, KT2, DenseK8{}, load_a); break;
     }
 
     // The tile leaves through LDS, 64 rows at a time (whole-line stores).
@@ -317,6 +354,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs p, int e, int ml, int n
         const int gpitch = f32gu ? kEpiPitch32 : kEpiPitch16;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
+            if (b * kEpiRows >= trows) break;  // a half tile stores its kSegRows rows only
             if ((wm >> 1) == (b & 1)) {
                 const int i = b >> 1;
 #pragma unroll
@@ -362,6 +400,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs p, int e, int ml, int n
     } else if (p.Cf) {  // kEpiStore, fp32 output
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
+            if (b * kEpiRows >= trows) break;  // a half tile stores its kSegRows rows only
             if ((wm >> 1) == (b & 1)) {
                 const int i = b >> 1;
                 const float sc = p.row_scale ? p.row_scale[prow0 + b * 64 + rl] : 1.0f;
@@ -381,6 +420,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs p, int e, int ml, int n
     } else {  // kEpiStore, bf16 output
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
+            if (b * kEpiRows >= trows) break;  // a half tile stores its kSegRows rows only
             if ((wm >> 1) == (b & 1)) {
                 const int i = b >> 1;
                 const float sc = p.row_scale ? p.row_scale[prow0 + b * 64 + rl] : 1.0f;

@@ -15,7 +15,8 @@ struct LayoutOut {
     int32_t* row_token;   // [Tm*k]   token (relative to the slice) of each unpadded row
     int32_t* tok_row;     // [Tm,k]   unpadded row of each slot
     LayoutHeader* hdr;    // tile count and error flag for the GEMM kernels
-    int32_t* mt_start;    // [Et+1]   first BM-tile of each expert (Et = E + shared)
+    int32_t* mt_start;    // [Et+1]   first M tile of each expert (Et = E + shared)
+    int32_t* prow_start;  // [Et+1]   first padded row of each expert (a multiple of kSegRows)
     int32_t* prow_token;  // [R_pad]  token (absolute) feeding each padded GEMM row
     int32_t* tok_prow;    // [Tm, tok_prow_ld] padded row of each slot; column k = shared row
     int32_t* prow_slot;   // [R_pad]  slot j of each padded row: 0..k-1 routed, k shared, -1 padding
@@ -37,7 +38,7 @@ void launch_layout(const int32_t* idx, int Tm, int E, int k, int with_shared, co
 // Element strides between consecutive minibatches' copies of each LayoutOut
 // array (hdr in LayoutHeader units).
 struct LayoutStrides {
-    int64_t counts, offsets, row_token, tok_row, hdr, mt_start, prow_token, tok_prow, prow_slot, rows_e;
+    int64_t counts, offsets, row_token, tok_row, hdr, mt_start, prow_token, tok_prow, prow_slot, rows_e, prow_start;
 };
 // Every minibatch of Mb tokens (the last one possibly shorter) in one launch,
 // one workgroup each; o holds minibatch 0's pointers.
@@ -54,7 +55,8 @@ struct GemmArgs {
     uint16_t* C;               // [R_pad][ldc] bf16 output
     int64_t ldc;
     int N, K;
-    const int32_t* mt_start;   // [Et+1]
+    const int32_t* mt_start;   // [Et+1] first M tile of each expert
+    const int32_t* prow_start; // [Et+1] first padded row of each expert (M tile ml starts ml * BM after it)
     const LayoutHeader* hdr;
     int Et;
     // kEpiSwiGLU: optional [R_pad][2I] copy of g | u (kept for the backward),
@@ -65,7 +67,8 @@ struct GemmArgs {
     float* Cf;                 // kEpiStore, optional: fp32 output instead of C
     const int32_t* rows_e;     // optional [Et] rows of each expert: padding fragments get no MFMAs
     // Several minibatches in one launch (kEpiStore, nmb > 1): minibatch b's
-    // tile map and row counts sit b * mt_ld ints after mt_start / rows_e, its
+    // tile map, row starts and row counts sit b * mt_ld ints after mt_start /
+    // prow_start / rows_e, its
     // A rows (a_row_map NULL) a_mb elements, its row map map_mb ints, its
     // row scales rs_mb floats and its C / Cf rows c_mb elements after
     // minibatch 0's; the tiles run minibatch by minibatch.
@@ -102,6 +105,7 @@ struct MxGemmArgs {
     int64_t sb_stride, sb_kstride;
     int N, K;
     const int32_t* mt_start;
+    const int32_t* prow_start;
     const LayoutHeader* hdr;
     int e_begin, e_end;
     uint16_t* C;               // kEpiStore: bf16 [R_pad][ldc]
@@ -120,7 +124,7 @@ struct MxGemmArgs {
 void launch_mx_gemm(const MxGemmArgs& a, GemmEpilogue epi, int grid, hipStream_t stream);
 // bf16 [rows][cols] -> E4M3 codes [rows][cols] and E8M0 scales; layout 0:
 // [rows][cols/32], layout 1: the GEMM operand scale layout.
-// With hdr, rows from hdr->m_tiles * BM on are skipped.
+// With hdr, rows from hdr->prows on are skipped.
 void launch_mx_quant(const uint16_t* src, int64_t rows, int cols, int layout, uint8_t* codes, uint8_t* scales,
                      hipStream_t stream, const LayoutHeader* hdr = nullptr);
 
@@ -140,6 +144,7 @@ struct MegaArgs {
     const uint8_t* lay0;
     int64_t lay_bytes, ly_prow_token, ly_tok_prow;
     const int32_t* mt_all;
+    const int32_t* prs_all;   // [nmb][mt_ld] first padded row of each expert per minibatch
     const int32_t* rows_all;  // [nmb][mt_ld] rows of each expert per minibatch
     int mt_ld;
     GemmArgs g1, g2;
@@ -163,8 +168,8 @@ struct SwigluBwdArgs {
     const uint16_t* dH;        // [R_pad][I]
     const uint16_t* GU;        // [R_pad][2I]
     const LayoutHeader* hdr;
-    uint16_t* dGU;             // [R_pad][2I]  dG | dU, rows from tile *dgu_tile0 on
-    const int32_t* dgu_tile0;  // first tile of the experts whose input gradient runs in bf16
+    uint16_t* dGU;             // [R_pad][2I]  dG | dU, rows from *dgu_row0 on
+    const int32_t* dgu_row0;   // first padded row of the experts whose input gradient runs in bf16
     uint16_t* dGUT;            // [2I][ldt]    transposed dG | dU
     uint16_t* HT;              // [I][ldt]     transposed h
     int I;
@@ -189,7 +194,7 @@ struct WgradArgs {
     const uint16_t* B;
     int64_t ld, a_mb, b_mb;
     int M, N, n_split, Et, nmb, mt_ld;
-    const int32_t* mt;  // [nmb][mt_ld] first BM-tile of each expert, per minibatch
+    const int32_t* prs;  // [nmb][mt_ld] first padded row of each expert, per minibatch
     const int32_t* rows;  // [nmb][mt_ld] rows of each expert, per minibatch: K stops at the last
                           // 64-row stage holding one (the rest of the tile is zero padding)
     float* C0;
@@ -232,10 +237,10 @@ struct RcombArgs {
     int64_t ldt;
     // MXFP8, optional: dY quantised along H from fp32, codes [R_pad][H],
     // scales in the operand layout [mx_groups(H)][ldt][4]; only rows before
-    // tile *dyq_tile_end (the experts whose input gradient runs in MXFP8)
+    // padded row *dyq_row_end (the experts whose input gradient runs in MXFP8)
     uint8_t* dYq;
     uint8_t* sdY;
-    const int32_t* dyq_tile_end;
+    const int32_t* dyq_row_end;
 };
 void launch_rcomb_gather(const RcombArgs& a, int rpad, hipStream_t stream);
 

@@ -284,6 +284,7 @@ void mega_kernel(MegaArgs a) {
         group_tile(a, b0, b1, kind == kGateUp ? NT1 : NT2, lv, b, e, ml, ntile);
         const uint8_t* lay = a.lay0 + (int64_t)b * a.lay_bytes;
         const int32_t* mt = a.mt_all + (int64_t)b * a.mt_ld;
+        const int32_t* prs = a.prs_all + (int64_t)b * a.mt_ld;
         const int32_t* rows = a.rows_all + (int64_t)b * a.mt_ld;
         const LayoutHeader* hdr = (const LayoutHeader*)lay;
         uint8_t* slot = a.slot0 + (int64_t)(b % a.S) * a.slot_bytes;
@@ -301,14 +302,14 @@ void mega_kernel(MegaArgs a) {
             if (mx_tile) {
                 MxGemmArgs m = a.m1;
                 m.a_row_map = (const int32_t*)(lay + a.ly_prow_token);
-                m.mt_start = mt; m.hdr = hdr;
+                m.mt_start = mt; m.prow_start = prs; m.hdr = hdr;
                 m.Cq = slot + a.sl_hq; m.Cs = slot + a.sl_sh;
                 m.GU = svb ? (float*)svb : nullptr;
                 mx_gemm_tile<kEpiSwiGLU, kPadNone>(m, e, ml, ntile, smem);
             } else {
                 GemmArgs gg = a.g1;
                 gg.a_row_map = (const int32_t*)(lay + a.ly_prow_token);
-                gg.mt_start = mt; gg.hdr = hdr; gg.rows_e = rows;
+                gg.mt_start = mt; gg.prow_start = prs; gg.hdr = hdr; gg.rows_e = rows;
                 gg.C = (uint16_t*)(slot + a.sl_h);
                 gg.GU = (!kMx && svb) ? (uint16_t*)svb : nullptr;
                 gg.GUf = (kMx && svb) ? (float*)svb : nullptr;
@@ -318,13 +319,13 @@ void mega_kernel(MegaArgs a) {
             if (mx_tile) {
                 MxGemmArgs m = a.m2;
                 m.A = slot + a.sl_hq; m.SA = slot + a.sl_sh;
-                m.mt_start = mt; m.hdr = hdr; m.rows_e = rows;
+                m.mt_start = mt; m.prow_start = prs; m.hdr = hdr; m.rows_e = rows;
                 m.C = Y;
                 mx_gemm_tile<kEpiStore, kPadPerWave>(m, e, ml, ntile, smem);
             } else {
                 GemmArgs gg = a.g2;
                 gg.A = (const uint16_t*)(slot + a.sl_h);
-                gg.mt_start = mt; gg.hdr = hdr; gg.rows_e = rows;
+                gg.mt_start = mt; gg.prow_start = prs; gg.hdr = hdr; gg.rows_e = rows;
                 gg.C = Y;
                 gemm_tile<kEpiStore, kPadPerWave>(gg, e, ml, ntile, smem);
             }

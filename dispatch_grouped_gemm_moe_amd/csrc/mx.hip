@@ -39,7 +39,7 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(const uint16_t* __restric
     if (i >= rows * nb) return;
     const int64_t r = i / nb;
     const int b = (int)(i - r * nb);
-    if (hdr && r >= (int64_t)hdr->m_tiles * BM) return;  // rows past the minibatch's last tile
+    if (hdr && r >= (int64_t)hdr->prows) return;  // rows past the minibatch's padded rows
     const uint8_t sc = mx_quant_block32(src + r * cols + b * 32, codes + r * cols + b * 32);
     if (layout == 0)
         scales[r * nb + b] = sc;
@@ -73,6 +73,7 @@ void mx_gemm_kernel(MxGemmArgs p) {
         if (p.nmb > 1) {
             const int b = minibatch_of_tile(p, v);
             q.mt_start += (int64_t)b * p.mt_ld;
+            q.prow_start += (int64_t)b * p.mt_ld;
             if (q.rows_e) q.rows_e += (int64_t)b * p.mt_ld;
             if (!q.a_row_map) q.A += b * p.a_mb;
             q.SA += b * p.sa_mb;

@@ -41,8 +41,11 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar LDS bases
     const int wm = wave >> 1, wn = wave & 1;
     const int KT = p.K / 64, KS = (KT + 1) / 2;
-    const int mt0 = p.mt_start[e];
-    const int prow0 = (mt0 + ml) * BM;
+    const int seg0 = p.prow_start[e];
+    const int prow0 = seg0 + ml * BM;
+    // BM rows, or kSegRows for an expert's last tile when it is a half tile
+    // (NV is then at most 1); rows past it load the tile's own rows again
+    const int trows = tile_rows_of(seg0, p.prow_start[e + 1], ml);
     const int n0 = ntile * BN;
 
     // Code loads: instruction i fills tile rows 32*wave + 8i .. +7 (lane/8 the
@@ -59,7 +62,7 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
         const int r = wave * 32 + i * 8 + (lane >> 3);
         const int lchunk = (lane & 7) ^ swz8(r);
         himask |= (lchunk >> 2) << i;
-        const int prow = prow0 + r;
+        const int prow = prow0 + (r & (trows - 1));
         const int arow = p.a_row_map ? p.a_row_map[prow] : prow;
         aoff[i] = (uint32_t)((int64_t)arow * p.lda + lchunk * 16);
         boff[i] = (uint32_t)((int64_t)min(n0 + r, p.N - 1) * p.K + lchunk * 16);
@@ -71,7 +74,8 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
         s_lane = (const char*)(p.SB + (int64_t)e * p.sb_stride) + (int64_t)min(n0 + srow, p.N - 1) * 4;
         s_kstride = p.sb_kstride;
     } else {
-        const int sarow = p.a_row_map ? p.a_row_map[prow0 + srow] : prow0 + srow;
+        const int sprow = prow0 + (srow & (trows - 1));
+        const int sarow = p.a_row_map ? p.a_row_map[sprow] : sprow;
         s_lane = (const char*)p.SA + (int64_t)sarow * 4;
         s_kstride = p.sa_kstride;
     }
@@ -215,6 +219,7 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
         uint8_t* ub = gb + kEpiRows * kEpiPitch32;          // [64][128] fp32 u
 #pragma unroll
         for (int bl = 0; bl < 4; ++bl) {
+            if (bl * kEpiRows >= trows) break;  // a half tile stores its kSegRows rows only
             if ((wm >> 1) == (bl & 1)) {
                 const int i = bl >> 1;
                 uint32_t sdw = 0;
@@ -266,6 +271,7 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
     } else if (p.Cf) {  // fp32 output
 #pragma unroll
         for (int bl = 0; bl < 4; ++bl) {
+            if (bl * kEpiRows >= trows) break;  // a half tile stores its kSegRows rows only
             if ((wm >> 1) == (bl & 1)) {
                 const int i = bl >> 1;
 #pragma unroll
@@ -283,6 +289,7 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
     } else {  // bf16 output
 #pragma unroll
         for (int bl = 0; bl < 4; ++bl) {
+            if (bl * kEpiRows >= trows) break;  // a half tile stores its kSegRows rows only
             if ((wm >> 1) == (bl & 1)) {
                 const int i = bl >> 1;
 #pragma unroll
@@ -305,11 +312,12 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
 // get no MFMAs as kPad says (gemm_tile.hpp).
 template <int EPI, int kPad = kPadPerWave>
 __device__ __forceinline__ void mx_gemm_tile(const MxGemmArgs p, int e, int ml, int ntile, uint8_t* smem) {
-    if (kPad == kPadNone || !p.rows_e) {
+    if (kPad == kPadNone || !p.rows_e) {  // every fragment (a half tile's rows past kSegRows are not stored)
         mx_tile_body<EPI, 2>(p, e, ml, ntile, smem);
         return;
     }
-    // fragment i of this wave holds tile rows 128i + 32wm .. +31
+    // fragment i of this wave holds tile rows 128i + 32wm .. +31 (a half
+    // tile has at most kSegRows valid rows, so NV <= 1)
     const int valid = p.rows_e[e] - ml * BM;
     const int w32 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 7) * 32;
     switch (valid > 128 + w32 ? 2 : (valid > w32 ? 1 : 0)) {

@@ -229,13 +229,14 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(const int32_t* _
         if (o.tok_prow) o.tok_prow += b * st.tok_prow;
         if (o.prow_slot) o.prow_slot += b * st.prow_slot;
         if (o.rows_e) o.rows_e += b * st.rows_e;
+        if (o.prow_start) o.prow_start += b * st.prow_start;
         o.token_base += t0;
         idx += (int64_t)t0 * k;
     }
     const int Tm = min(Mb, T - (int)blockIdx.x * Mb);
     __shared__ int s_cnt[kLayoutWaves][kMaxExperts + 1];  // per-wave counts, then running bases
     __shared__ int s_off[kMaxExperts + 2];                 // unpadded row offsets
-    __shared__ int s_poff[kMaxExperts + 2];                // padded (tile-aligned) row offsets
+    __shared__ int s_poff[kMaxExperts + 2];                // padded (kSegRows-aligned) row offsets
     __shared__ int s_tot[kMaxExperts + 1];                 // rows per expert
     __shared__ int s_err;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -267,10 +268,11 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(const int32_t* _
     if (s_err) {  // report, and leave an empty tile map so no GEMM tile runs
         if (tid == 0) {
             if (o.offsets) o.offsets[E] = -1;
-            if (o.hdr) { o.hdr->m_tiles = 0; o.hdr->rows = 0; o.hdr->error = 1; }
+            if (o.hdr) { o.hdr->m_tiles = 0; o.hdr->rows = 0; o.hdr->error = 1; o.hdr->prows = 0; }
         }
         for (int e = tid; e <= Et; e += kLayoutThreads) {
             if (o.mt_start) o.mt_start[e] = 0;
+            if (o.prow_start) o.prow_start[e] = 0;
             if (o.rows_e && e < Et) o.rows_e[e] = 0;
         }
         return;
@@ -288,14 +290,17 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(const int32_t* _
     }
     if (tid == 0 && with_shared) s_tot[E] = Tm;  // the shared expert takes every token
     __syncthreads();
-    // 2b. offsets and tile map (one thread: at most 257 experts)
+    // 2b. offsets and tile map (one thread: at most 257 experts).  Expert e's
+    // padded rows start at s_poff[e], a multiple of kSegRows; its ceil(tot/BM)
+    // M tiles are BM rows, the last a half tile when it holds at most kSegRows.
     if (tid == 0) {
-        int off = 0, mt = 0;
+        int off = 0, mt = 0, poff = 0;
         for (int e = 0; e < Et; ++e) {
             const int tot = s_tot[e];
             s_off[e] = off;
-            s_poff[e] = mt * BM;
+            s_poff[e] = poff;
             if (o.mt_start) o.mt_start[e] = mt;
+            if (o.prow_start) o.prow_start[e] = poff;
             if (o.rows_e) o.rows_e[e] = tot;
             if (e < E) {
                 if (o.counts) o.counts[e] = tot;
@@ -303,12 +308,14 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(const int32_t* _
                 off += tot;
             }
             mt += ceil_div(tot, BM);
+            poff += ceil_div(tot, kSegRows) * kSegRows;
         }
         s_off[Et] = off;
-        s_poff[Et] = mt * BM;
+        s_poff[Et] = poff;
         if (o.offsets) o.offsets[E] = off;
         if (o.mt_start) o.mt_start[Et] = mt;
-        if (o.hdr) { o.hdr->m_tiles = mt; o.hdr->rows = off; o.hdr->error = 0; }
+        if (o.prow_start) o.prow_start[Et] = poff;
+        if (o.hdr) { o.hdr->m_tiles = mt; o.hdr->rows = off; o.hdr->error = 0; o.hdr->prows = poff; }
     }
     __syncthreads();
 
