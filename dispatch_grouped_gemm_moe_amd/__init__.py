@@ -27,7 +27,8 @@ MOE_DEV_OK, MOE_DEV_WAIT_TIMEOUT = 0, 1
 EXPORTS = ("moe_status_string", "moe_abi_version", "moe_validate_cfg", "moe_query_sizes",
            "moe_prepare_weights", "moe_route", "moe_dispatch_layout", "moe_layer_fwd",
            "moe_layer_bwd", "moe_read_device_status", "moe_mx_quantize", "moe_timing_enable",
-           "moe_timing_read", "moe_diag_mfma_loop")
+           "moe_timing_read", "moe_diag_mfma_loop", "moe_layer_fwd_static")
+MOE_STATIC_WORKSPACE_BYTES = 256 << 20
 KERNEL_KINDS = ("route", "layout", "gemm_gate_up", "gemm_down", "combine", "gather", "other", "wgrad",
                 "dgrad_down", "dgrad_gate_up", "shared_gemm", "layer")
 
@@ -90,6 +91,7 @@ def _load():
             "moe_timing_enable": (ctypes.c_int, [I32]),
             "moe_timing_read": (ctypes.c_int, [ctypes.POINTER(moe_kernel_times)]),
             "moe_diag_mfma_loop": (ctypes.c_int, [I32, P, ctypes.c_int64, I32, I32, P, P, P]),
+            "moe_layer_fwd_static": (ctypes.c_int, [cfgp, ctypes.POINTER(moe_weights), P, P, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(lib, name)
@@ -168,6 +170,14 @@ def moe_layer_fwd(cfg, Wr, bias, packed, x, out, ws, saved=None, stream=None):
         ctypes.byref(cfg), ctypes.byref(w), _ptr(x), _ptr(out), _ptr(saved),
         0 if saved is None else saved.numel() * saved.element_size(), _ptr(ws),
         ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_layer_fwd_static(cfg, Wr, bias, packed, x, out, status=None, stream=None):
+    """Forward on the library's static workspace (allocates nothing); status: an
+    int32 device tensor of 2 elements that receives the device status word."""
+    w = _weights(Wr, bias, packed)
+    _check("moe_layer_fwd_static", _load().moe_layer_fwd_static(
+        ctypes.byref(cfg), ctypes.byref(w), _ptr(x), _ptr(out), _ptr(status), _stream(stream)))
 
 
 def moe_layer_bwd(cfg, Wr, bias, packed, x, dout, saved, dx, dWg, dWu, dWd, dWr, ws,

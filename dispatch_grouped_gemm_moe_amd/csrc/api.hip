@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "../../include/moe.h"
@@ -272,6 +273,44 @@ struct TimedLaunch {
     } while (0)
 
 moe_status check_launch() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP; }
+
+// ---------------------------------------------------------------------------
+// The allocation-free forward's workspace: this array, one copy per GPU (each
+// at its own device address), held from the library's load until the process
+// ends.  Host code never passes the array's name to a kernel (on the host it
+// is a stand-in, not a device address): it uses the address that
+// hipGetSymbolAddress returns on each device, looked up once per device.
+// ---------------------------------------------------------------------------
+constexpr size_t kStaticWsBytes = (size_t)MOE_STATIC_WORKSPACE_BYTES;
+static __device__ __align__(256) uint8_t scratch[kStaticWsBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device.
+moe_status scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_E_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MOE_E_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
+// The device status word (two ints at the start of a workspace): cleared by a
+// kernel (not a memset, so that a captured call records no memset node), and
+// copied out to the caller's buffer after the forward.
+__global__ void status_clear_kernel(int32_t* word) {
+    if (threadIdx.x < 2) word[threadIdx.x] = 0;
+}
+__global__ void status_copy_kernel(const int32_t* word, int32_t* dst) {
+    if (threadIdx.x < 2) dst[threadIdx.x] = word[threadIdx.x];
+}
 
 }  // namespace
 
@@ -547,6 +586,23 @@ moe_status moe_layer_fwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
     if (st != MOE_OK) return st;
     if ((st = check_fwd(p, w, x, out, saved, saved_bytes, ws, ws_bytes)) != MOE_OK) return st;
     return enqueue_fwd(cfg, p, w, x, out, saved, ws, (hipStream_t)stream);
+}
+
+moe_status moe_layer_fwd_static(const moe_cfg* cfg, const moe_weights* w, const uint16_t* x, uint16_t* out,
+                                int32_t* status, void* stream) {
+    Plan p;
+    moe_status st = make_plan(cfg, &p);
+    if (st != MOE_OK) return st;
+    if (p.ws_fwd > kStaticWsBytes) return MOE_E_WORKSPACE;  // before any device call
+    if (status && !aligned(status, 4)) return MOE_E_INVALID;
+    void* ws = nullptr;
+    if ((st = scratch_address(&ws)) != MOE_OK) return st;
+    if ((st = check_fwd(p, w, x, out, nullptr, 0, ws, kStaticWsBytes)) != MOE_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    hipLaunchKernelGGL(status_clear_kernel, dim3(1), dim3(64), 0, s, (int32_t*)ws);
+    if ((st = enqueue_fwd(cfg, p, w, x, out, nullptr, ws, s)) != MOE_OK) return st;
+    if (status) hipLaunchKernelGGL(status_copy_kernel, dim3(1), dim3(64), 0, s, (const int32_t*)ws, status);
+    return check_launch();
 }
 
 moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_t* x, const uint16_t* dout,

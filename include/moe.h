@@ -220,6 +220,31 @@ moe_status moe_layer_fwd(const moe_cfg *cfg, const moe_weights *w, const uint16_
                          size_t ws_bytes, void *stream);
 
 /*
+ * Layer forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * moe_layer_fwd with saved = NULL (nothing kept for a backward), whose
+ * workspace is the library's own static device array of
+ * MOE_STATIC_WORKSPACE_BYTES, one per GPU, held from the library's load until
+ * the process ends.  Same kernels and bitwise the same `out` as moe_layer_fwd.
+ *   cfg, w, x, out: as for moe_layer_fwd.
+ *   status: NULL, or a device int32[2] (4-byte aligned) that receives the
+ *       device status word of this call after the forward (code, detail: see
+ *       moe_read_device_status; {0, 0} when no kernel reported an error).
+ * Allocates nothing: the first call on a device looks up the array's device
+ * address once (hipGetSymbolAddress).  The status word is cleared by a kernel
+ * at the start of every call; the layer kernel's counters are cleared by the
+ * forward itself.
+ * MOE_E_WORKSPACE if moe_sizes.workspace_fwd of cfg exceeds
+ * MOE_STATIC_WORKSPACE_BYTES (checked before any device call; choose a
+ * smaller minibatch or ring).  Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (on different streams, or from
+ * different threads) race and give undefined results.
+ */
+#define MOE_STATIC_WORKSPACE_BYTES (256u << 20)
+moe_status moe_layer_fwd_static(const moe_cfg *cfg, const moe_weights *w, const uint16_t *x,
+                                uint16_t *out, int32_t *status, void *stream);
+
+/*
  * Layer backward ([KC] 01: training adds two exchanges in the reverse
  * direction; [KC] 02: reverse-combine then reverse-dispatch).  Gradients of
  * sum(out * dout) with the routing of the forward held fixed:
