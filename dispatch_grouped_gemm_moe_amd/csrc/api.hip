@@ -17,8 +17,7 @@ namespace {
 
 constexpr int kNumCUs = 256;      // MI355X compute units
 constexpr int kBalanceRows = 320;  // bf16 machine balance: ~2.5 PFLOP/s over 8 TB/s, in rows
-constexpr int kPadShare = 16;      // automatic minibatch: expected tile padding at most 1/16 of the rows
-constexpr int kCommWorkers = 0;    // layer kernel: combine as tiles of the GEMM workgroups (no dedicated CUs)
+constexpr int kPadShare = 32;      // automatic minibatch: expected padding rows at most 1/32 of the rows
 constexpr int kGroupTokens = 8192; // layer kernel: tokens per GEMM phase (minibatches grouped up to this)
 constexpr int kBwdChunkTokens = 5120;  // backward: tokens per phase chunk (minibatches grouped up to this)
 constexpr int kBwdChunkTokensShared = 20480;  // the same with the shared expert
@@ -78,12 +77,15 @@ int auto_minibatch(const moe_cfg* c) {
     // Smallest multiple of 256 tokens such that (i) the gate/up GEMM has at least
     // two full waves of output tiles on the GEMM CUs, (ii) the mean rows per
     // expert reach the machine balance, so weights are not re-streamed for a
-    // handful of rows, and (iii) the padding of each expert's last M tile
-    // (BM/2 rows per expert expected) is at most 1/kPadShare of the
-    // minibatch's rows: at H=7168, I=2048, E=32, k=8 the layer ran 15.1 /
-    // 13.5 / 12.5 / 12.0 / 12.05 ms per 16384 tokens (bf16 forward) at
-    // minibatches of 1408 / 2560 / 4096 / 8192 / 16384, flat once the
-    // padding fell to a sixteenth.  Then spread T evenly over that many
+    // handful of rows, and (iii) the padding of the experts' padded rows
+    // (kSegRows/2 rows per expert expected) is at most 1/kPadShare of the
+    // minibatch's rows.  Measured (layer kernel, 16384 tokens, one box): at
+    // H=7168, I=2048, E=32, k=8 bf16 14.21 / 12.24 / 12.18 / 11.13 / 11.11 /
+    // 10.67 ms and MXFP8 (Zipf router) 8.40 / 7.45 / 7.40 / 6.66 / 6.49 /
+    // 6.35 ms at minibatches of 1024 / 2048 / 2560 / 4096 / 6144 / 8192, and
+    // the rule picks 8192; at H=2048, I=1024, E=64, k=6 with 4096 tokens,
+    // 1.505 / 0.806 / 0.509 / 0.491 ms at 512 / 1024 / 2048 / 4096, and the
+    // rule picks one minibatch of 4096.  Then spread T evenly over that many
     // minibatches.
     const int nt1 = ceil_div(2 * c->I, BN);
     int mb = c->T;
@@ -91,7 +93,7 @@ int auto_minibatch(const moe_cfg* c) {
         const int64_t tiles = (int64_t)ceil_div(m * c->k, BM) * nt1;
         const int64_t rows = (int64_t)m * c->k;
         if (tiles >= 2 * kNumCUs && rows >= (int64_t)kBalanceRows * c->E &&
-            rows >= (int64_t)kPadShare * c->E * (BM / 2)) {
+            rows >= (int64_t)kPadShare * c->E * (kSegRows / 2)) {
             mb = m;
             break;
         }
@@ -100,6 +102,21 @@ int auto_minibatch(const moe_cfg* c) {
     mb = ceil_div(ceil_div(c->T, nmb), 64) * 64;
     return mb < c->T ? mb : c->T;
 }
+
+// Workgroups the layer kernel dedicates to combine when the cfg leaves it to
+// the library.  Dedicated workgroups take their CUs' share of the GEMM
+// throughput, and on one GPU no GEMM phase leaves CUs idle for them to use:
+// every active expert has at least one M tile per N tile, so even a few
+// dozen tokens give more gate|up tiles than CUs.  Combine therefore runs as
+// tiles of the GEMM workgroups (0).  Measured (layer kernel, one box):
+// H=7168, I=2048, E=32, k=8, 16384 tokens in minibatches of 2560: bf16
+// 12.18 ms with combine tiles against 17.55 / 14.14 / 13.44 ms with 8 / 16 /
+// 32 combine workgroups, MXFP8 7.47 against 13.17 / 9.58 / 8.53 ms;
+// H=2048, I=1024, E=64, k=6, 4096 tokens: combine tiles fastest at every
+// minibatch of 512 / 1024 / 2048 / 4096 (e.g. 0.491 against 1.280 / 0.906 ms
+// with 8 / 16 at 4096).  With several GPUs the communication role would also
+// drive link transfers; that is out of this build's scope.
+int auto_comm_cus(const moe_cfg*) { return 0; }
 
 moe_status make_plan(const moe_cfg* c, Plan* p) {
     moe_status st = validate(c);
@@ -126,7 +143,7 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     p->slots = c->ring_slots > 0 ? c->ring_slots : 3 * p->group;
     p->slots = std::min(p->slots, ceil_div(p->nmb, p->group) * p->group);  // no slot without a minibatch
     p->slots -= p->slots % p->group;
-    p->comm_cus = c->comm_cus > 0 ? c->comm_cus : kCommWorkers;  // dedicated combine workgroups
+    p->comm_cus = c->comm_cus > 0 ? c->comm_cus : auto_comm_cus(c);  // dedicated combine workgroups
     // The layer kernel's tile sequence runs gate|up(b+1) before down(b), so a
     // ring of one slot would make gate|up(b+1) wait on a later tile.  Identity
     // experts take the per-GEMM path.

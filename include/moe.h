@@ -89,7 +89,10 @@ typedef struct moe_cfg {
                            layer kernel runs as one phase */
     int32_t comm_cus;   /* workgroups (one per CU) dedicated to combine in the
                            persistent layer kernel; 0 = automatic: none, combine
-                           runs as tiles of the GEMM workgroups */
+                           runs as tiles of the GEMM workgroups (on one GPU
+                           every GEMM phase has more tiles than CUs, and
+                           dedicated combine workgroups measured slower at
+                           every shape, count and minibatch tried) */
     int32_t prec;       /* moe_prec */
     uint32_t flags;     /* moe_flags */
 } moe_cfg;
