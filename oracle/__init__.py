@@ -412,8 +412,37 @@ def mx_point(a, axis: int) -> np.ndarray:
     return mx_roundtrip(np.asarray(a, dtype=np.float64).astype(np.float32), axis)
 
 
+def segment_rows_product(t_sel, A, B, minibatch, q):
+    """sum over minibatches b of q(A_b)^T q(B_b), where A_b, B_b are the rows of
+    A, B whose token t_sel lies in minibatch b ([b*minibatch, (b+1)*minibatch))
+    and q quantises along the rows (axis 0), each segment on its own.  With
+    q = None: A^T B."""
+    if q is None:
+        return A.T @ B
+    out = np.zeros((A.shape[1], B.shape[1]))
+    seg = np.asarray(t_sel) // minibatch
+    for b in np.unique(seg):
+        r = seg == b
+        out += q(A[r], 0).T @ q(B[r], 0)
+    return out
+
+
+def mx_rows_point(a, axis: int) -> np.ndarray:
+    """A weight-gradient quantisation point: the values, rounded to fp32, are
+    quantised along `axis` (the token rows) in blocks of 32 rows from the
+    segment's first row; a last partial block is padded with zeros, which
+    leave its scale unchanged."""
+    a = np.asarray(a, dtype=np.float64)
+    assert axis == 0
+    n = a.shape[0]
+    pad = (-n) % MX_BLOCK
+    if pad:
+        a = np.concatenate([a, np.zeros((pad,) + a.shape[1:])], axis=0)
+    return mx_point(a, 0)[:n]
+
+
 def layer_backward(inp, dout=None, fwd=None, *, mx: bool | None = None, quantizer=None,
-                   weight_grads: bool = True):
+                   weight_grads: bool = True, mx_wgrad_minibatch: int | None = None):
     """Gradients of sum(out * dout) for the layer (fp64, routing frozen at the
     forward's selection).
 
@@ -430,12 +459,18 @@ def layer_backward(inp, dout=None, fwd=None, *, mx: bool | None = None, quantize
     forward's quantisation).  `quantizer(a, axis)` replaces `mx_point`.
     weight_grads=False leaves out the expert weight gradients (dWg, dWu, dWd and
     the shared expert's); every other result is unchanged.
+    mx_wgrad_minibatch (MXFP8 only): the routed experts' weight-gradient GEMMs
+    take MXFP8 operands too, quantised along their contraction axis, the
+    token rows: within each (minibatch of that many tokens, expert) segment,
+    in blocks of 32 rows in token order (x rows, h, dY, dG, dU; zero padding
+    past the segment's last row).  The shared expert stays bf16.
     """
     w_ = inp.w
     mx = (w_.prec == "mxfp8") if mx is None else mx
     if fwd is None:
         fwd = layer_forward(inp, keep=True, mx=mx)
     q = (quantizer or mx_point) if mx else None
+    qw = mx_rows_point if (mx and mx_wgrad_minibatch) else None
     dout = as_f64(inp.dout if dout is None else dout)
     x64, idx, gw, Y = fwd["x"], fwd["idx"], fwd["w"], fwd["Y"]
     T, H = x64.shape
@@ -455,9 +490,9 @@ def layer_backward(inp, dout=None, fwd=None, *, mx: bool | None = None, quantize
         du = dh * silu(g)
         dg = dh * u * silu_grad(g)
         if weight_grads:
-            dWd[e] = h.T @ dy
-            dWg[e] = X.T @ dg
-            dWu[e] = X.T @ du
+            dWd[e] = segment_rows_product(t_sel, h, dy, mx_wgrad_minibatch, qw)
+            dWg[e] = segment_rows_product(t_sel, X, dg, mx_wgrad_minibatch, qw)
+            dWu[e] = segment_rows_product(t_sel, X, du, mx_wgrad_minibatch, qw)
         if q:
             dxe = q(dg, 1) @ Wg.T + q(du, 1) @ Wu.T
         else:
@@ -487,7 +522,8 @@ def layer_backward(inp, dout=None, fwd=None, *, mx: bool | None = None, quantize
     return res
 
 
-def weight_grad_columns(inp, e: int, cols, dout=None, *, mx: bool | None = None, routing=None):
+def weight_grad_columns(inp, e: int, cols, dout=None, *, mx: bool | None = None, routing=None,
+                        mx_wgrad_minibatch: int | None = None):
     """Columns `cols` of one expert's weight gradients over all of its tokens:
     dWg[:, cols] and dWu[:, cols] [H, n], dWd[cols, :] [n, H] (e >= 0, routing
     frozen at the forward's selection), or the shared expert's dWsg, dWsu, dWsd
@@ -503,6 +539,10 @@ def weight_grad_columns(inp, e: int, cols, dout=None, *, mx: bool | None = None,
     MXFP8 x rows and weights, dH from MXFP8 dY and Wd, weight gradients on the
     unquantised x, h and dY.
     routing: (idx, w) of every token, from `route`, to reuse across calls.
+    mx_wgrad_minibatch: as in `layer_backward` (routed experts, MXFP8): the
+    weight-gradient operands are quantised along the token rows per
+    (minibatch, expert) segment; a block of 32 rows of one column lies inside
+    that column, so restricting to the columns commutes with it too.
     """
     w_ = inp.w
     mx = (w_.prec == "mxfp8") if mx is None else mx
@@ -533,6 +573,10 @@ def weight_grad_columns(inp, e: int, cols, dout=None, *, mx: bool | None = None,
     h = silu(g) * u
     du = dh * silu(g)
     dg = dh * u * silu_grad(g)
+    if e >= 0 and mx and mx_wgrad_minibatch:
+        return {"dWg": segment_rows_product(t_sel, X, dg, mx_wgrad_minibatch, mx_rows_point),
+                "dWu": segment_rows_product(t_sel, X, du, mx_wgrad_minibatch, mx_rows_point),
+                "dWd": segment_rows_product(t_sel, h, dy, mx_wgrad_minibatch, mx_rows_point)}
     return {"dWg": X.T @ dg, "dWu": X.T @ du, "dWd": h.T @ dy}
 
 

@@ -530,24 +530,18 @@ def _T(M):
     return [list(c) for c in zip(*M)]
 
 
-def test_mx_backward_matches_scalar_brute_force():
-    """Every MXFP8 quantisation point of the layer, and every contraction, by
-    scalar loops on a tiny layer: the forward (x along H; Wg, Wu along H; h
-    along I; Wd along I), the input-gradient GEMMs (dY and Wd along H; dG, dU
-    and Wg, Wu along I) and the unquantised weight gradients."""
-    w = tiny(T=5, H=64, I=64, E=3, k=2, router_bias="normal", prec="mxfp8", wide_range=True)
-    inp = make_inputs(w, with_dout=True)
-    fwd = O.layer_forward(inp, keep=True)
-    g = O.layer_backward(inp, fwd=fwd)
+def _brute_mx_rows(inp, idx, gw):
+    """Scalar brute force of the MXFP8 layer for every routed (t, j): the
+    forward (x along H; Wg, Wu along H; h along I; Wd along I) and the
+    input-gradient GEMMs (dY and Wd along H; dG, dU and Wg, Wu along I).
+    Returns {(t, j): dict(x, g, u, h, y, dy, dg, du, dx)} with plain lists."""
+    w = inp.w
     T, H, I, E, k = w.T, w.H, w.I, w.E, w.k
     x = inp.x.double().tolist()
     dout = inp.dout.double().tolist()
-    Wr = inp.Wr.double().tolist()
-    idx, gw = fwd["idx"], fwd["w"]
     sig = lambda z: 1.0 / (1.0 + math.exp(-z)) if z >= 0 else math.exp(z) / (1.0 + math.exp(z))
     xq = _brute_quant_rows(x)
-    ref = {"dx": [[0.0] * H for _ in range(T)], "dWg": np.zeros((E, H, I)), "dWu": np.zeros((E, H, I)),
-           "dWd": np.zeros((E, I, H)), "dgate": np.zeros((T, k)), "dWr": np.zeros((H, E)), "out": np.zeros((T, H))}
+    rows = {}
     for e in range(E):
         Wg, Wu, Wd = (t[e].double().tolist() for t in (inp.Wg, inp.Wu, inp.Wd))  # [H][I], [H][I], [I][H]
         Wgf, Wuf = _T(_brute_quant_rows(_T(Wg))), _T(_brute_quant_rows(_T(Wu)))  # forward: along H
@@ -562,20 +556,44 @@ def test_mx_backward_matches_scalar_brute_force():
                 hh = [gg[i] * sig(gg[i]) * uu[i] for i in range(I)]
                 hq = _brute_quant_rows([hh])[0]
                 y = [sum(hq[i] * Wdf[i][h] for i in range(I)) for h in range(H)]
-                ref["out"][t] += gw[t, j] * np.array(y)
-                ref["dgate"][t, j] = sum(dout[t][h] * y[h] for h in range(H))
                 dy = [gw[t, j] * dout[t][h] for h in range(H)]
                 dyq = _brute_quant_rows([dy])[0]
                 dh = [sum(dyq[h] * Wdb[i][h] for h in range(H)) for i in range(I)]
                 dg = [dh[i] * uu[i] * sig(gg[i]) * (1 + gg[i] * (1 - sig(gg[i]))) for i in range(I)]
                 du = [dh[i] * gg[i] * sig(gg[i]) for i in range(I)]
                 dgq, duq = _brute_quant_rows([dg])[0], _brute_quant_rows([du])[0]
-                for h in range(H):
-                    ref["dx"][t][h] += sum(dgq[i] * Wgb[h][i] + duq[i] * Wub[h][i] for i in range(I))
-                    for i in range(I):
-                        ref["dWg"][e, h, i] += x[t][h] * dg[i]
-                        ref["dWu"][e, h, i] += x[t][h] * du[i]
-                        ref["dWd"][e, i, h] += hh[i] * dy[h]
+                dx = [sum(dgq[i] * Wgb[h][i] + duq[i] * Wub[h][i] for i in range(I)) for h in range(H)]
+                rows[(t, j)] = dict(x=x[t], g=gg, u=uu, h=hh, y=y, dy=dy, dg=dg, du=du, dx=dx, e=e)
+    return rows
+
+
+def test_mx_backward_matches_scalar_brute_force():
+    """Every MXFP8 quantisation point of the layer, and every contraction, by
+    scalar loops on a tiny layer: the forward (x along H; Wg, Wu along H; h
+    along I; Wd along I), the input-gradient GEMMs (dY and Wd along H; dG, dU
+    and Wg, Wu along I) and the unquantised weight gradients."""
+    w = tiny(T=5, H=64, I=64, E=3, k=2, router_bias="normal", prec="mxfp8", wide_range=True)
+    inp = make_inputs(w, with_dout=True)
+    fwd = O.layer_forward(inp, keep=True)
+    g = O.layer_backward(inp, fwd=fwd)
+    T, H, I, E, k = w.T, w.H, w.I, w.E, w.k
+    x = inp.x.double().tolist()
+    dout = inp.dout.double().tolist()
+    Wr = inp.Wr.double().tolist()
+    idx, gw = fwd["idx"], fwd["w"]
+    rows = _brute_mx_rows(inp, idx, gw)
+    ref = {"dx": [[0.0] * H for _ in range(T)], "dWg": np.zeros((E, H, I)), "dWu": np.zeros((E, H, I)),
+           "dWd": np.zeros((E, I, H)), "dgate": np.zeros((T, k)), "dWr": np.zeros((H, E)), "out": np.zeros((T, H))}
+    for (t, j), r in rows.items():
+        e = r["e"]
+        ref["out"][t] += gw[t, j] * np.array(r["y"])
+        ref["dgate"][t, j] = sum(dout[t][h] * r["y"][h] for h in range(H))
+        for h in range(H):
+            ref["dx"][t][h] += r["dx"][h]
+            for i in range(I):
+                ref["dWg"][e, h, i] += x[t][h] * r["dg"][i]
+                ref["dWu"][e, h, i] += x[t][h] * r["du"][i]
+                ref["dWd"][e, i, h] += r["h"][i] * r["dy"][h]
     for t in range(T):  # router: softmax over the selected logits
         s = sum(gw[t, j] * ref["dgate"][t, j] for j in range(k))
         for j in range(k):
@@ -593,6 +611,67 @@ def test_mx_backward_matches_scalar_brute_force():
         np.testing.assert_allclose(c["dWg"], ref["dWg"][e][:, cols], rtol=1e-9, atol=1e-12)
         np.testing.assert_allclose(c["dWu"], ref["dWu"][e][:, cols], rtol=1e-9, atol=1e-12)
         np.testing.assert_allclose(c["dWd"], ref["dWd"][e][cols, :], rtol=1e-9, atol=1e-12)
+
+
+def _brute_quant_cols(M):
+    """Quantise every column of the row list M along the rows, in blocks of 32
+    rows from the first, a last partial block padded with zeros."""
+    n = len(M)
+    out = [[0.0] * len(M[0]) for _ in range(n)]
+    for c in range(len(M[0])):
+        for b in range(0, n, 32):
+            blk = [M[r][c] for r in range(b, min(n, b + 32))]
+            q = _brute_quant_block(blk + [0.0] * (32 - len(blk)))
+            for r in range(len(blk)):
+                out[b + r][c] = q[r]
+    return out
+
+
+def test_mx_weight_gradients_match_scalar_brute_force():
+    """The MXFP8 weight-gradient GEMMs (all six routed GEMMs in MXFP8): their
+    operands x, h, dY, dG, dU are quantised along the token rows of each
+    (minibatch, expert) segment in blocks of 32 rows, zero-padded, by scalar
+    loops here.  96 tokens, top-1 over 2 experts, minibatches of 80 and 16:
+    the first minibatch's segments span two blocks, the second's one partial
+    block; wide-range rows mix magnitudes along the quantised axis."""
+    mb = 80
+    w = tiny(T=96, H=64, I=64, E=2, k=1, router_bias="normal", prec="mxfp8", wide_range=True)
+    inp = make_inputs(w, with_dout=True)
+    fwd = O.layer_forward(inp, keep=True)
+    g = O.layer_backward(inp, fwd=fwd, mx_wgrad_minibatch=mb)
+    T, H, I, E = w.T, w.H, w.I, w.E
+    idx, gw = fwd["idx"], fwd["w"]
+    rows = _brute_mx_rows(inp, idx, gw)
+    ref = {"dWg": np.zeros((E, H, I)), "dWu": np.zeros((E, H, I)), "dWd": np.zeros((E, I, H))}
+    longest = 0
+    for e in range(E):
+        for t0 in range(0, T, mb):
+            seg = [rows[(t, 0)] for t in range(t0, min(T, t0 + mb)) if idx[t, 0] == e]
+            if not seg:
+                continue
+            longest = max(longest, len(seg))
+            Xq = _brute_quant_cols([r["x"] for r in seg])
+            dgq, duq = _brute_quant_cols([r["dg"] for r in seg]), _brute_quant_cols([r["du"] for r in seg])
+            hq, dyq = _brute_quant_cols([r["h"] for r in seg]), _brute_quant_cols([r["dy"] for r in seg])
+            ref["dWg"][e] += np.array(Xq).T @ np.array(dgq)
+            ref["dWu"][e] += np.array(Xq).T @ np.array(duq)
+            ref["dWd"][e] += np.array(hq).T @ np.array(dyq)
+    assert longest > 32  # a segment spans more than one block
+    for n in ref:
+        np.testing.assert_allclose(g[n], ref[n], rtol=1e-9, atol=1e-12, err_msg=n)
+        # the columns helper takes the same quantisation
+    for e in range(E):
+        c = O.weight_grad_columns(inp, e, [0, 33, 63], mx_wgrad_minibatch=mb)
+        np.testing.assert_allclose(c["dWg"], ref["dWg"][e][:, [0, 33, 63]], rtol=1e-9, atol=1e-12)
+        np.testing.assert_allclose(c["dWd"], ref["dWd"][e][[0, 33, 63], :], rtol=1e-9, atol=1e-12)
+    # the check is sensitive to the quantisation and to the segment restarts:
+    # unquantised weight gradients, or one segment over all tokens (blocks
+    # not restarting at the minibatch boundary), fail the same tolerance
+    plain = O.layer_backward(inp, fwd=fwd)
+    whole = O.layer_backward(inp, fwd=fwd, mx_wgrad_minibatch=T)
+    for n in ref:
+        assert O.rel_inf_err(plain[n], ref[n]) > 1e-3, n
+        assert not np.allclose(whole[n], ref[n], rtol=1e-9, atol=1e-12), n
 
 
 def test_mx_backward_with_identity_quantiser_is_the_plain_backward():
