@@ -48,8 +48,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="time only the main workload (by default the MXFP8 forward, the MXFP8 + shared "
-                         "forward + backward, the bf16 forward and the per-GEMM bf16 forward are timed as well, "
-                         "into detail.workloads)")
+                         "forward + backward with MXFP8 and with bf16 weight gradients, the bf16 forward and "
+                         "the per-GEMM bf16 forward are timed as well, into detail.workloads)")
+    ap.add_argument("--bf16-wgrad", action="store_true",
+                    help="MXFP8 workloads: bf16 weight-gradient operands (MOE_F_BF16_WGRAD)")
     ap.add_argument("--extra-steps", type=int, default=5)
     ap.add_argument("--no-mfma-loop", action="store_true",
                     help="skip the sustained-MFMA measurement (a pure MFMA loop on the layer's own input values)")
@@ -114,7 +116,8 @@ def main():
     bwd = args.passes == "fwdbwd"
     m = measure(moe, torch, w, bwd, args.steps, args.warmup, comm_cus=args.comm_cus, ring_slots=args.ring_slots,
                 launch_per_gemm=args.launch_per_gemm, cold_cache=args.cold_cache,
-                mfma_loops=not args.no_mfma_loop, keep_inputs=not args.no_cpu_baseline)
+                mfma_loops=not args.no_mfma_loop, keep_inputs=not args.no_cpu_baseline,
+                bf16_wgrad=args.bf16_wgrad)
     inp = m.pop("inputs", None)
     mx = w.prec == "mxfp8"
     res = {
@@ -142,9 +145,12 @@ def main():
         extras = {}
         for name, e_bwd, flags in (("h7168_i2048_e32_k8_mxfp8_zipf", False, {}),
                                    ("h7168_i2048_e32_k8_mxfp8_shared_fwdbwd", True, {}),
+                                   ("h7168_i2048_e32_k8_mxfp8_shared_fwdbwd", True, {"bf16_wgrad": True}),
                                    ("h7168_i2048_e32_k8_bf16", False, {}),
                                    ("h7168_i2048_e32_k8_bf16", False, {"launch_per_gemm": True})):
-            key = "%s/%s%s" % (name, "fwdbwd" if e_bwd else "fwd", "/per_gemm" if flags else "")
+            key = "%s/%s%s" % (name, "fwdbwd" if e_bwd else "fwd",
+                               "".join("/" + {"launch_per_gemm": "per_gemm", "bf16_wgrad": "bf16_wgrad"}[f]
+                                       for f in flags))
             log("timing", key)
             r = measure(moe, torch, WORKLOADS[name], e_bwd, args.extra_steps, 2, mfma_loops=False, **flags)
             extras[key] = {"value": r["value"], "unit": "tokens/s", "ms_per_step": r["ms_per_step"],
@@ -161,7 +167,7 @@ def main():
 
 def measure(moe, torch, w, bwd: bool, steps: int, warmup: int, comm_cus: int = 0, ring_slots: int = 0,
             launch_per_gemm: bool = False, cold_cache: bool = False, mfma_loops: bool = False,
-            keep_inputs: bool = False) -> dict:
+            keep_inputs: bool = False, bf16_wgrad: bool = False) -> dict:
     """Times `steps` layer steps of workload `w` (forward, or forward + backward)
     after `warmup` untimed ones, with every input already in HBM; returns the
     throughput, the dominant kernel's roofline position and the per-kernel-kind
@@ -173,7 +179,10 @@ def measure(moe, torch, w, bwd: bool, steps: int, warmup: int, comm_cus: int = 0
     mx = w.prec == "mxfp8"
     inp = make_inputs(w, with_dout=bwd)
     log("%s: inputs drawn in %.1f s" % (w.name, time.time() - t_gen))
+    mx_wgrad = mx and not bf16_wgrad
     flags = (moe.MOE_F_SHARED_EXPERT if w.shared_expert else 0) | (moe.MOE_F_LAUNCH_PER_GEMM if launch_per_gemm else 0)
+    if mx and bf16_wgrad:
+        flags |= moe.MOE_F_BF16_WGRAD
     cfg = moe.make_cfg(w.T, w.H, w.I, w.E, w.k, minibatch=w.minibatch, flags=flags,
                        prec=moe.MOE_PREC_MXFP8 if mx else moe.MOE_PREC_BF16,
                        comm_cus=comm_cus, ring_slots=ring_slots)
@@ -234,12 +243,13 @@ def measure(moe, torch, w, bwd: bool, steps: int, warmup: int, comm_cus: int = 0
         moe.moe_timing_enable(False)  # waits for the recorded launches and destroys the events
 
     layer_kernel = kt["layer"][0] > 0
-    flops = role_flops(T, H, I, k, w.shared_expert, mx, bwd, layer_kernel)
+    flops = role_flops(T, H, I, k, w.shared_expert, mx, bwd, layer_kernel, mx_wgrad)
     symbol = {"gemm_gate_up": "mx_gemm_kernel<0>" if mx else "grouped_gemm_kernel<0>",
               "gemm_down": "mx_gemm_kernel<1>" if mx else "grouped_gemm_kernel<1>",
               "dgrad_down": "mx_gemm_kernel<1>" if mx else "grouped_gemm_kernel<1>",
               "dgrad_gate_up": "mx_gemm_kernel<1>" if mx else "grouped_gemm_kernel<1>",
-              "wgrad": "wgrad_kernel", "shared_gemm": "grouped_gemm_kernel (bf16 shared expert)",
+              "wgrad": "mx_wgrad_kernel" if mx_wgrad else "wgrad_kernel",
+              "shared_gemm": "grouped_gemm_kernel (bf16 shared expert)",
               "layer": "mega_kernel<%s>" % ("true" if mx else "false")}
     by_sym = {}
     for kd, fl in flops.items():
@@ -255,7 +265,7 @@ def measure(moe, torch, w, bwd: bool, steps: int, warmup: int, comm_cus: int = 0
     achieved = dom_flops / (ms_dom / 1e3) / 1e12
     # the scaled-MFMA kernels (and the MXFP8 layer kernel) are priced at the FP8 peak
     peak = PEAK_FP8_TFLOPS if (mx and (dom.startswith("mx_") or dom == "mega_kernel<true>")) else PEAK_BF16_TFLOPS
-    nbytes = role_bytes(T, H, I, k, E, w.shared_expert, mx, bwd, layer_kernel)
+    nbytes = role_bytes(T, H, I, k, E, w.shared_expert, mx, bwd, layer_kernel, mx_wgrad)
     res = {
         "value": T * steps / elapsed,
         "ms_per_step": ms_step,
@@ -265,6 +275,7 @@ def measure(moe, torch, w, bwd: bool, steps: int, warmup: int, comm_cus: int = 0
                    "ring_slots": sizes.ring_slots, "comm_cus": sizes.comm_cus,
                    "forward": "persistent layer kernel" if layer_kernel else "per-GEMM launches",
                    "pass": "forward+backward" if bwd else "forward",
+                   "weight_gradients": ("mxfp8" if mx_wgrad else "bf16") if bwd else None,
                    "cache": "cold: 512 MiB written before each step" if cold_cache else "warm"},
         "roofline": {"bound": "mfma", "kernel": "moe::" + dom, "roles": dom_roles,
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
@@ -295,7 +306,8 @@ def measure(moe, torch, w, bwd: bool, steps: int, warmup: int, comm_cus: int = 0
     return res
 
 
-def role_bytes(T: int, H: int, I: int, k: int, E: int, shared: bool, mx: bool, bwd: bool, layer_kernel: bool) -> dict:
+def role_bytes(T: int, H: int, I: int, k: int, E: int, shared: bool, mx: bool, bwd: bool, layer_kernel: bool,
+               mx_wgrad: bool = False) -> dict:
     """Algorithmic HBM bytes per step of the data-movement kernel kinds (routed
     and shared rows; padding rows excluded):
       route: x read once, router weight, indices and weights written (MXFP8:
@@ -306,7 +318,9 @@ def role_bytes(T: int, H: int, I: int, k: int, E: int, shared: bool, mx: bool, b
       gather (backward): reverse-combine (dout, x and Y rows read; transposed
         dY and x written; MXFP8 codes + scales of dY) and SwiGLU backward (dH
         and g|u read, fp32 under MXFP8; dG|dU row-major for bf16 GEMMs,
-        transposed dG|dU and h written; MXFP8 codes + scales of dG|dU)."""
+        transposed dG|dU and h written; MXFP8 codes + scales of dG|dU).  With
+        MXFP8 weight gradients (mx_wgrad) the routed rows' transposed dY, x,
+        dG|dU and h are written as codes + scales instead of bf16."""
     ks = k + (1 if shared else 0)
     R, Rr = T * ks, T * k  # rows (routed + shared), routed rows
     q = 1.0 + 1.0 / 32  # MXFP8 code + scale bytes per element
@@ -315,9 +329,12 @@ def role_bytes(T: int, H: int, I: int, k: int, E: int, shared: bool, mx: bool, b
         b["combine"] = T * (ks * H * 2 + H * 2)
         rows_mx = Rr if mx else 0
         rows_bf16 = R - rows_mx
+        rows_w = Rr if (mx and mx_wgrad) else 0  # quantised weight-gradient operands
         f = 4 if mx else 2
-        b["gather"] = (R * (3 * H * 2 + 2 * H * 2) + rows_mx * H * q
-                       + R * (I * f + 2 * I * f + 2 * I * 2 + I * 2) + rows_bf16 * 2 * I * 2 + rows_mx * 2 * I * q)
+        rcomb = R * 3 * H * 2 + (R - rows_w) * 2 * H * 2 + rows_w * 2 * H * q + rows_mx * H * q
+        swiglu = (R * 3 * I * f + (R - rows_w) * 3 * I * 2 + rows_w * 3 * I * q
+                  + rows_bf16 * 2 * I * 2 + rows_mx * 2 * I * q)
+        b["gather"] = rcomb + swiglu
     elif not layer_kernel:
         b["combine"] = T * (ks * H * 2 + H * 2)
     return b
@@ -365,24 +382,28 @@ def mfma_loop(moe, torch, x, w, mx: bool) -> dict:
     return out
 
 
-def role_flops(T: int, H: int, I: int, k: int, shared: bool, mx: bool, bwd: bool, layer_kernel: bool) -> dict:
+def role_flops(T: int, H: int, I: int, k: int, shared: bool, mx: bool, bwd: bool, layer_kernel: bool,
+               mx_wgrad: bool = False) -> dict:
     """Algorithmic flops per step of each timing kind of the grouped GEMMs
     (padding rows excluded): 6*H*I per routed or shared row and pass (gate|up
     4*H*I, down 2*H*I), for the forward, the input gradients and the weight
     gradients.  MXFP8 runs the routed experts on the scaled-MFMA kernels and
     the shared expert in bf16: its backward input-gradient launches are their
     own kind, and its forward GEMMs run in the persistent layer kernel when
-    that runs (their own kind otherwise).  bf16 runs both in the same
-    launches."""
+    that runs (their own kind otherwise).  With MXFP8 weight gradients
+    (mx_wgrad) the weight-gradient kind is the routed experts' scaled-MFMA
+    launches and the shared expert's bf16 weight gradients join its kind.
+    bf16 runs both in the same launches."""
     shared_rows = T if shared else 0
     hi = float(H) * I * (T * k + shared_rows)
     hr = float(H) * I * (T * k if mx else T * k + shared_rows)
     flops = {"gemm_gate_up": 4 * hr, "gemm_down": 2 * hr}
     if bwd:
-        flops.update({"dgrad_down": 2 * hr, "dgrad_gate_up": 4 * hr, "wgrad": 6 * hi})
+        flops.update({"dgrad_down": 2 * hr, "dgrad_gate_up": 4 * hr,
+                      "wgrad": 6 * (float(H) * I * T * k if (mx and mx_wgrad) else hi)})
     shared_fwd = 6.0 * H * I * shared_rows if mx else 0.0
-    if mx and shared_rows and bwd:  # the shared expert's bf16 input-gradient GEMMs
-        flops["shared_gemm"] = 6.0 * H * I * shared_rows
+    if mx and shared_rows and bwd:  # the shared expert's bf16 input-gradient (and weight-gradient) GEMMs
+        flops["shared_gemm"] = 6.0 * H * I * shared_rows * (2 if mx_wgrad else 1)
     if layer_kernel:
         # the persistent layer kernel runs both forward GEMMs (and combine),
         # under MXFP8 with the shared expert's bf16 tiles in the same launch

@@ -21,6 +21,7 @@ MOE_F_SHARED_EXPERT = 1 << 0
 MOE_F_IDENTITY_EXPERTS = 1 << 1
 MOE_F_LAUNCH_PER_GEMM = 1 << 2
 MOE_F_DEBUG_DROP_SIGNAL = 1 << 3
+MOE_F_BF16_WGRAD = 1 << 4
 MOE_DEV_OK, MOE_DEV_WAIT_TIMEOUT = 0, 1
 
 # every symbol include/moe.h declares

@@ -57,6 +57,9 @@ struct Plan {
     size_t wb_wrt, wb_mt, wb_prs, wb_rows, wb_lay0, lay_bytes, ly_hdr, ly_prow_token, ly_tok_prow, ly_prow_slot;
     size_t wb_dyt, wb_xgt, wb_dgut, wb_ht, wb_dsel, wb_dgu, wb_dh, wb_dx, wb_dgp, wb_roww, ws_bwd;
     size_t wb_dyq, wb_sdy, wb_dguq, wb_sdgu;  // MXFP8 operands of the input-gradient GEMMs
+    bool mxw;  // MXFP8 weight gradients of the routed experts
+    // their operands, one copy per minibatch: codes and scales of dY, x, dG | dU, h
+    size_t wb_dytq, wb_sdyt, wb_xgtq, wb_sxgt, wb_dgutq, wb_sdgut, wb_htq, wb_sht;
     size_t wb_dlog, wb_dwrp;                  // dense d out / d logits, router-gradient partial sums
 };
 
@@ -66,8 +69,9 @@ moe_status validate(const moe_cfg* c) {
     if (c->minibatch < 0 || c->ring_slots < 0 || c->comm_cus < 0) return MOE_E_INVALID;
     if (c->prec != MOE_PREC_BF16 && c->prec != MOE_PREC_MXFP8) return MOE_E_INVALID;
     if (c->flags & ~(uint32_t)(MOE_F_SHARED_EXPERT | MOE_F_IDENTITY_EXPERTS | MOE_F_LAUNCH_PER_GEMM |
-                               MOE_F_DEBUG_DROP_SIGNAL))
+                               MOE_F_DEBUG_DROP_SIGNAL | MOE_F_BF16_WGRAD))
         return MOE_E_INVALID;
+    if ((c->flags & MOE_F_BF16_WGRAD) && c->prec != MOE_PREC_MXFP8) return MOE_E_INVALID;
     if (c->H % 64 || c->I % 64 || c->E > kMaxExperts || c->k > kMaxTopK) return MOE_E_UNSUPPORTED;
     if ((int64_t)c->T * c->k > (1ll << 30) || (int64_t)c->T * c->H > (1ll << 40)) return MOE_E_UNSUPPORTED;
     return MOE_OK;
@@ -126,6 +130,7 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     p->shared = (c->flags & MOE_F_SHARED_EXPERT) != 0;
     p->identity = (c->flags & MOE_F_IDENTITY_EXPERTS) != 0;
     p->mx = p->prec == MOE_PREC_MXFP8;
+    p->mxw = p->mx && !(c->flags & MOE_F_BF16_WGRAD);
     p->Et = c->E + (p->shared ? 1 : 0);
     p->Mb = c->minibatch > 0 ? (c->minibatch < c->T ? c->minibatch : c->T) : auto_minibatch(c);
     p->nmb = ceil_div(c->T, p->Mb);
@@ -153,6 +158,16 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     // sum over experts of ceil(c_e / BM) <= ceil(rows / BM) + Et - 1
     p->max_mtiles = (int)(ceil_div((int)rows, BM) + p->Et - 1);
     p->rpad = (int64_t)p->max_mtiles * BM;
+    // The GEMM tiles address a row of an operand by a 32-bit byte offset from
+    // the operand's (64-bit) base: the token matrix [T][H] and dout (gathered
+    // rows), a minibatch's padded-row matrices ([rpad][H], [rpad][2I] and their
+    // transposes) and one expert's weights ([2I][H]), bf16.
+    {
+        const int64_t lim = 1ll << 32, rp = p->rpad;
+        if ((int64_t)c->T * c->H * 2 >= lim || rp * c->H * 2 >= lim || rp * 2 * c->I * 2 >= lim ||
+            (int64_t)2 * c->I * c->H * 2 >= lim)
+            return MOE_E_UNSUPPORTED;
+    }
 
     const size_t H = c->H, I = c->I, Et = p->Et;
     p->pk_w1t = 0;
@@ -243,6 +258,16 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
         p->wb_sdy = o; o = align_up(o + nc * mx_groups(H) * rp * 4);
         p->wb_dguq = o; o = align_up(o + nc * rp * 2 * I);
         p->wb_sdgu = o; o = align_up(o + nc * mx_groups(2 * I) * rp * 4);
+    }
+    if (p->mxw) {  // rpad is a multiple of 256: whole scale groups of 128 rows
+        p->wb_dytq = o; o = align_up(o + nmb * H * rp);
+        p->wb_sdyt = o; o = align_up(o + nmb * mx_groups(rp) * H * 4);
+        p->wb_xgtq = o; o = align_up(o + nmb * H * rp);
+        p->wb_sxgt = o; o = align_up(o + nmb * mx_groups(rp) * H * 4);
+        p->wb_dgutq = o; o = align_up(o + nmb * 2 * I * rp);
+        p->wb_sdgut = o; o = align_up(o + nmb * mx_groups(rp) * 2 * I * 4);
+        p->wb_htq = o; o = align_up(o + nmb * I * rp);
+        p->wb_sht = o; o = align_up(o + nmb * mx_groups(rp) * I * 4);
     }
     p->ws_bwd = o;
     return MOE_OK;
@@ -347,7 +372,10 @@ const char* moe_status_string(moe_status s) {
 
 int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
 
-moe_status moe_validate_cfg(const moe_cfg* cfg) { return validate(cfg); }
+moe_status moe_validate_cfg(const moe_cfg* cfg) {
+    Plan p;
+    return make_plan(cfg, &p);  // the limits that depend on the padded rows too
+}
 
 moe_status moe_query_sizes(const moe_cfg* cfg, moe_sizes* out) {
     if (!out) return MOE_E_INVALID;
@@ -714,6 +742,12 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             rc.dYq = p.mx ? wsb + p.wb_dyq + j * rp * H : nullptr;
             rc.sdY = p.mx ? wsb + p.wb_sdy + j * mx_groups(H) * rp * 4 : nullptr;
             rc.dyq_row_end = prs_all + (size_t)b * (Et + 1) + e_bf16;
+            if (p.mxw) {  // weight-gradient operands of the MXFP8 experts (rows before dyq_row_end)
+                rc.dYTq = wsb + p.wb_dytq + (size_t)b * H * rp;
+                rc.sdYT = wsb + p.wb_sdyt + (size_t)b * mx_groups(rp) * H * 4;
+                rc.xgTq = wsb + p.wb_xgtq + (size_t)b * H * rp;
+                rc.sxgT = wsb + p.wb_sxgt + (size_t)b * mx_groups(rp) * H * 4;
+            }
             TIMED(MOE_K_GATHER, s, launch_rcomb_gather(rc, (int)rp, s));
         }
         if (p.mx) {
@@ -757,6 +791,13 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             sb.dHf = p.mx ? dHf + bh : nullptr; sb.GUf = p.mx ? (const float*)svb : nullptr;
             sb.dGUq = p.mx ? wsb + p.wb_dguq + 2 * bh : nullptr;
             sb.sdGU = p.mx ? wsb + p.wb_sdgu + j * mx_groups(2 * I) * rp * 4 : nullptr;
+            if (p.mxw) {  // weight-gradient operands of the MXFP8 experts (rows before dgu_row0)
+                sb.prow_slot = (const int32_t*)(lay + p.ly_prow_slot);
+                sb.dGUTq = wsb + p.wb_dgutq + (size_t)b * 2 * I * rp;
+                sb.sdGUT = wsb + p.wb_sdgut + (size_t)b * mx_groups(rp) * 2 * I * 4;
+                sb.HTq = wsb + p.wb_htq + (size_t)b * I * rp;
+                sb.sHT = wsb + p.wb_sht + (size_t)b * mx_groups(rp) * I * 4;
+            }
             TIMED(MOE_K_GATHER, s, launch_swiglu_bwd(sb, (int)rp, s));
         }
         if (p.mx) {
@@ -796,20 +837,43 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             TIMED(MOE_K_COMBINE, s, launch_rdispatch(rd, Tm, s));
         }
     }
-    WgradArgs wa{};  // [dWg | dWu][e] = x_e^T [dG | dU]_e over every row of expert e
-    wa.A = xgT_all; wa.B = dGUT_all; wa.ld = rp;
-    wa.a_mb = (int64_t)H * rp * 2; wa.b_mb = (int64_t)2 * I * rp * 2;
-    wa.M = H; wa.N = 2 * I; wa.n_split = I; wa.Et = Et; wa.nmb = p.nmb; wa.mt_ld = Et + 1; wa.prs = prs_all; wa.rows = (const int32_t*)(wsb + p.wb_rows);
-    wa.C0 = dWg; wa.C1 = dWu;
-    wa.Cs0 = p.shared ? dWs : nullptr; wa.Cs1 = p.shared ? dWs + (size_t)H * I : nullptr;
-    TIMED(MOE_K_WGRAD, s, launch_wgrad(wa, grid, s));
-    WgradArgs wd{};  // dWd[e] = h_e^T dY_e
-    wd.A = HT_all; wd.B = dYT_all; wd.ld = rp;
-    wd.a_mb = (int64_t)I * rp * 2; wd.b_mb = (int64_t)H * rp * 2;
-    wd.M = I; wd.N = H; wd.n_split = H; wd.Et = Et; wd.nmb = p.nmb; wd.mt_ld = Et + 1; wd.prs = prs_all; wd.rows = (const int32_t*)(wsb + p.wb_rows);
-    wd.C0 = dWd; wd.C1 = nullptr;
-    wd.Cs0 = p.shared ? dWs + (size_t)2 * H * I : nullptr; wd.Cs1 = nullptr;
-    TIMED(MOE_K_WGRAD, s, launch_wgrad(wd, grid, s));
+    // MXFP8 weight gradients: experts [0, E) on the scaled-MFMA kernel, the
+    // shared expert (if any) on the bf16 one
+    const int w_bf16 = p.mxw ? E : 0;
+    if (p.mxw) {
+        MxWgradArgs qa{};  // [dWg | dWu][e] = Q(x_e)^T Q([dG | dU]_e)
+        qa.A = wsb + p.wb_xgtq; qa.SA = wsb + p.wb_sxgt; qa.B = wsb + p.wb_dgutq; qa.SB = wsb + p.wb_sdgut;
+        qa.ld = rp; qa.a_mb = (int64_t)H * rp; qa.b_mb = (int64_t)2 * I * rp;
+        qa.sa_mb = mx_groups(rp) * H * 4; qa.sb_mb = mx_groups(rp) * 2 * I * 4;
+        qa.M = H; qa.N = 2 * I; qa.n_split = I; qa.E = E; qa.nmb = p.nmb; qa.mt_ld = Et + 1;
+        qa.prs = prs_all; qa.rows = rows_all; qa.C0 = dWg; qa.C1 = dWu;
+        TIMED(MOE_K_WGRAD, s, launch_mx_wgrad(qa, grid, s));
+        MxWgradArgs qd{};  // dWd[e] = Q(h_e)^T Q(dY_e)
+        qd.A = wsb + p.wb_htq; qd.SA = wsb + p.wb_sht; qd.B = wsb + p.wb_dytq; qd.SB = wsb + p.wb_sdyt;
+        qd.ld = rp; qd.a_mb = (int64_t)I * rp; qd.b_mb = (int64_t)H * rp;
+        qd.sa_mb = mx_groups(rp) * I * 4; qd.sb_mb = mx_groups(rp) * H * 4;
+        qd.M = I; qd.N = H; qd.n_split = H; qd.E = E; qd.nmb = p.nmb; qd.mt_ld = Et + 1;
+        qd.prs = prs_all; qd.rows = rows_all; qd.C0 = dWd; qd.C1 = nullptr;
+        TIMED(MOE_K_WGRAD, s, launch_mx_wgrad(qd, grid, s));
+    }
+    if (w_bf16 < Et) {
+        WgradArgs wa{};  // [dWg | dWu][e] = x_e^T [dG | dU]_e over every row of expert e
+        wa.A = xgT_all; wa.B = dGUT_all; wa.ld = rp;
+        wa.a_mb = (int64_t)H * rp * 2; wa.b_mb = (int64_t)2 * I * rp * 2;
+        wa.M = H; wa.N = 2 * I; wa.n_split = I; wa.Et = Et; wa.e_begin = w_bf16; wa.nmb = p.nmb; wa.mt_ld = Et + 1;
+        wa.prs = prs_all; wa.rows = rows_all;
+        wa.C0 = dWg; wa.C1 = dWu;
+        wa.Cs0 = p.shared ? dWs : nullptr; wa.Cs1 = p.shared ? dWs + (size_t)H * I : nullptr;
+        TIMED(p.mxw ? MOE_K_SHARED_GEMM : MOE_K_WGRAD, s, launch_wgrad(wa, grid, s));
+        WgradArgs wd{};  // dWd[e] = h_e^T dY_e
+        wd.A = HT_all; wd.B = dYT_all; wd.ld = rp;
+        wd.a_mb = (int64_t)I * rp * 2; wd.b_mb = (int64_t)H * rp * 2;
+        wd.M = I; wd.N = H; wd.n_split = H; wd.Et = Et; wd.e_begin = w_bf16; wd.nmb = p.nmb; wd.mt_ld = Et + 1;
+        wd.prs = prs_all; wd.rows = rows_all;
+        wd.C0 = dWd; wd.C1 = nullptr;
+        wd.Cs0 = p.shared ? dWs + (size_t)2 * H * I : nullptr; wd.Cs1 = nullptr;
+        TIMED(p.mxw ? MOE_K_SHARED_GEMM : MOE_K_WGRAD, s, launch_wgrad(wd, grid, s));
+    }
     DwrArgs dr{};
     dr.x = x; dr.dlogits = (const float*)(wsb + p.wb_dlog); dr.partial = (float*)(wsb + p.wb_dwrp);
     dr.dWr = dWr; dr.T = p.T; dr.H = H; dr.E = E;

@@ -11,6 +11,8 @@
 //     dsel = w * (dgate - <w, dgate>) is the softmax backward.
 // Every floating-point sum has a fixed order (no atomics), so results are
 // bitwise reproducible.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mxfp8.hpp"
@@ -29,8 +31,16 @@ constexpr int kTile = 64;
 //   dgp[prow][hb] = sum over the block's 64 columns of dout[t][h] * Y[prow][h]
 //                   (routed rows; in column order, then a fixed pair tree)
 //   dsel[prow]    = 0 (filled for routed rows by the reverse-dispatch)
+// MXW (MXFP8 weight gradients): a block of rows before *dyq_row_end writes
+// dYT and xgT as E4M3 codes quantised along the padded rows instead (dY from
+// its fp32 values, x zero on padding rows), a block from it on writes bf16.
+// The block of 64 rows lies inside one expert segment (segments start at
+// multiples of 128 rows), so the choice is uniform over the workgroup.
+template <bool MXW>
 __global__ __launch_bounds__(256) void rcomb_gather_kernel(RcombArgs p) {
-    __shared__ uint16_t sY[kTile][kTile + 2];
+    // MXW stages dY in fp32 (its quantisation input), else in bf16
+    using StY = typename std::conditional<MXW, float, uint16_t>::type;
+    __shared__ StY sY[kTile][kTile + (MXW ? 1 : 2)];
     __shared__ uint16_t sX[kTile][kTile + 2];
     const int prow0 = blockIdx.x * kTile, h0 = blockIdx.y * kTile;
     if (prow0 >= p.hdr->prows) return;
@@ -85,8 +95,13 @@ __global__ __launch_bounds__(256) void rcomb_gather_kernel(RcombArgs p) {
     for (int c = 0; c < 16; ++c) {
         dyf[c] = w * d[c];
         dy[c] = f32_to_bf16_rne(dyf[c]);
-        sY[c0 + c][r] = dy[c];
-        sX[c0 + c][r] = f32_to_bf16_rne(xv[c]);
+        if constexpr (MXW) {
+            sY[c0 + c][r] = dyf[c];
+            sX[c0 + c][r] = slot < 0 ? (uint16_t)0 : f32_to_bf16_rne(xv[c]);
+        } else {
+            sY[c0 + c][r] = dy[c];
+            sX[c0 + c][r] = f32_to_bf16_rne(xv[c]);
+        }
     }
     // MXFP8 operand of the down input-gradient GEMM, from the fp32 values
     if (p.dYq && prow < *p.dyq_row_end)
@@ -104,6 +119,21 @@ __global__ __launch_bounds__(256) void rcomb_gather_kernel(RcombArgs p) {
     __syncthreads();
     // transposed tiles: thread -> column h0 + tid/4, rows prow0 + 16*(tid%4) .. +16
     const int hc = tid >> 2, r0 = (tid & 3) * 16;
+    if constexpr (MXW) {
+        if (prow0 < *p.dyq_row_end) {
+            // four consecutive lanes hold the column's 64 rows: two 32-row blocks
+            float v[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) v[q] = sY[hc][r0 + q];
+            mx_quant_row64(v, tid & 3, p.dYTq + (int64_t)(h0 + hc) * p.ldt + prow0, p.sdYT, p.H, h0 + hc,
+                           prow0 / 64, (int)(p.ldt / 64));
+#pragma unroll
+            for (int q = 0; q < 16; ++q) v[q] = __builtin_bit_cast(float, (uint32_t)sX[hc][r0 + q] << 16);
+            mx_quant_row64(v, tid & 3, p.xgTq + (int64_t)(h0 + hc) * p.ldt + prow0, p.sxgT, p.H, h0 + hc,
+                           prow0 / 64, (int)(p.ldt / 64));
+            return;
+        }
+    }
     intx4* dyt = (intx4*)(p.dYT + (int64_t)(h0 + hc) * p.ldt + prow0 + r0);
     intx4* xgt = (intx4*)(p.xgT + (int64_t)(h0 + hc) * p.ldt + prow0 + r0);
 #pragma unroll
@@ -111,7 +141,15 @@ __global__ __launch_bounds__(256) void rcomb_gather_kernel(RcombArgs p) {
         intx4 a, b;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            a[e] = (int)((uint32_t)sY[hc][r0 + 8 * q + 2 * e] | ((uint32_t)sY[hc][r0 + 8 * q + 2 * e + 1] << 16));
+            uint16_t y0, y1;
+            if constexpr (MXW) {
+                y0 = f32_to_bf16_rne(sY[hc][r0 + 8 * q + 2 * e]);
+                y1 = f32_to_bf16_rne(sY[hc][r0 + 8 * q + 2 * e + 1]);
+            } else {
+                y0 = sY[hc][r0 + 8 * q + 2 * e];
+                y1 = sY[hc][r0 + 8 * q + 2 * e + 1];
+            }
+            a[e] = (int)((uint32_t)y0 | ((uint32_t)y1 << 16));
             b[e] = (int)((uint32_t)sX[hc][r0 + 8 * q + 2 * e] | ((uint32_t)sX[hc][r0 + 8 * q + 2 * e + 1] << 16));
         }
         dyt[q] = a;
@@ -120,7 +158,10 @@ __global__ __launch_bounds__(256) void rcomb_gather_kernel(RcombArgs p) {
 }
 
 void launch_rcomb_gather(const RcombArgs& a, int rpad, hipStream_t stream) {
-    hipLaunchKernelGGL(rcomb_gather_kernel, dim3(rpad / kTile, a.H / kTile), dim3(256), 0, stream, a);
+    if (a.xgTq)
+        hipLaunchKernelGGL(rcomb_gather_kernel<true>, dim3(rpad / kTile, a.H / kTile), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(rcomb_gather_kernel<false>, dim3(rpad / kTile, a.H / kTile), dim3(256), 0, stream, a);
 }
 
 __device__ __forceinline__ void unpack16_bf16(const intx4* src, float* f) {
@@ -149,11 +190,17 @@ __device__ __forceinline__ void pack16_bf16(const uint16_t* v, intx4* dst) {
 // row-major dG | dU for the bf16 input-gradient GEMM (only the rows of the
 // experts it runs: the MXFP8 experts take the quantised copy), transposed
 // dG | dU and h for the weight-gradient GEMMs (through LDS, so every store is
-// coalesced).
+// coalesced).  MXW (MXFP8 weight gradients): a block of rows before
+// *dgu_row0 writes the transposed dG | dU and h as E4M3 codes quantised
+// along the padded rows from their fp32 values (h zero on padding rows), a
+// block from it on writes bf16; the block lies inside one expert segment.
+template <bool MXW>
 __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdArgs p) {
-    __shared__ uint16_t sG[kTile][kTile + 2];
-    __shared__ uint16_t sU[kTile][kTile + 2];
-    __shared__ uint16_t sH[kTile][kTile + 2];
+    using St = typename std::conditional<MXW, float, uint16_t>::type;
+    constexpr int kPitch = kTile + (MXW ? 1 : 2);
+    __shared__ St sG[kTile][kPitch];
+    __shared__ St sU[kTile][kPitch];
+    __shared__ St sH[kTile][kPitch];
     const int prow0 = blockIdx.x * kTile, i0 = blockIdx.y * kTile;
     if (prow0 >= p.hdr->prows) return;
     const int tid = threadIdx.x;
@@ -179,6 +226,8 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdArgs p) {
         unpack16_bf16((const intx4*)(p.GU + prow * 2 * I + i0 + c0), g);
         unpack16_bf16((const intx4*)(p.GU + prow * 2 * I + I + i0 + c0), u);
     }
+    // MXW: h of a padding row is zero, so it cannot raise its block's scale
+    const bool pad = MXW && p.prow_slot[prow] < 0;
     uint16_t dg[16], du[16], hh[16];
     float dgf[16], duf[16];
 #pragma unroll
@@ -189,10 +238,16 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdArgs p) {
         duf[c] = dh[c] * silu;
         dg[c] = f32_to_bf16_rne(dgf[c]);
         du[c] = f32_to_bf16_rne(duf[c]);
-        hh[c] = f32_to_bf16_rne(silu * u[c]);
-        sG[c0 + c][r] = dg[c];
-        sU[c0 + c][r] = du[c];
-        sH[c0 + c][r] = hh[c];
+        if constexpr (MXW) {
+            sG[c0 + c][r] = dgf[c];
+            sU[c0 + c][r] = duf[c];
+            sH[c0 + c][r] = pad ? 0.0f : silu * u[c];
+        } else {
+            hh[c] = f32_to_bf16_rne(silu * u[c]);
+            sG[c0 + c][r] = dg[c];
+            sU[c0 + c][r] = du[c];
+            sH[c0 + c][r] = hh[c];
+        }
     }
     if (prow >= (int64_t)*p.dgu_row0) {
         pack16_bf16(dg, (intx4*)(p.dGU + prow * 2 * I + i0 + c0));
@@ -204,20 +259,45 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdArgs p) {
     }
     __syncthreads();
     const int ic = tid >> 2, r0 = (tid & 3) * 16;
-    uint16_t v[16];
+    if constexpr (MXW) {
+        if (prow0 < *p.dgu_row0) {
+            // four consecutive lanes hold the column's 64 rows: two 32-row blocks
+            const int j = prow0 / 64, nj = (int)(p.ldt / 64);
+            float v[16];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) v[q] = sG[ic][r0 + q];
+            for (int q = 0; q < 16; ++q) v[q] = sG[ic][r0 + q];
+            mx_quant_row64(v, tid & 3, p.dGUTq + (int64_t)(i0 + ic) * p.ldt + prow0, p.sdGUT, 2 * I, i0 + ic, j, nj);
+#pragma unroll
+            for (int q = 0; q < 16; ++q) v[q] = sU[ic][r0 + q];
+            mx_quant_row64(v, tid & 3, p.dGUTq + (int64_t)(I + i0 + ic) * p.ldt + prow0, p.sdGUT, 2 * I, I + i0 + ic,
+                           j, nj);
+#pragma unroll
+            for (int q = 0; q < 16; ++q) v[q] = sH[ic][r0 + q];
+            mx_quant_row64(v, tid & 3, p.HTq + (int64_t)(i0 + ic) * p.ldt + prow0, p.sHT, I, i0 + ic, j, nj);
+            return;
+        }
+    }
+    uint16_t v[16];
+    auto bf = [](St a) -> uint16_t {
+        if constexpr (MXW) return f32_to_bf16_rne(a);
+        else return a;
+    };
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v[q] = bf(sG[ic][r0 + q]);
     pack16_bf16(v, (intx4*)(p.dGUT + (int64_t)(i0 + ic) * p.ldt + prow0 + r0));
 #pragma unroll
-    for (int q = 0; q < 16; ++q) v[q] = sU[ic][r0 + q];
+    for (int q = 0; q < 16; ++q) v[q] = bf(sU[ic][r0 + q]);
     pack16_bf16(v, (intx4*)(p.dGUT + (int64_t)(I + i0 + ic) * p.ldt + prow0 + r0));
 #pragma unroll
-    for (int q = 0; q < 16; ++q) v[q] = sH[ic][r0 + q];
+    for (int q = 0; q < 16; ++q) v[q] = bf(sH[ic][r0 + q]);
     pack16_bf16(v, (intx4*)(p.HT + (int64_t)(i0 + ic) * p.ldt + prow0 + r0));
 }
 
 void launch_swiglu_bwd(const SwigluBwdArgs& a, int rpad, hipStream_t stream) {
-    hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(rpad / kTile, a.I / kTile), dim3(256), 0, stream, a);
+    if (a.HTq)
+        hipLaunchKernelGGL(swiglu_bwd_kernel<true>, dim3(rpad / kTile, a.I / kTile), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(swiglu_bwd_kernel<false>, dim3(rpad / kTile, a.I / kTile), dim3(256), 0, stream, a);
 }
 
 // One workgroup per token of a minibatch: gate gradients, softmax backward and

@@ -90,24 +90,11 @@ struct SegmentK {
 __global__ __attribute__((amdgpu_flat_work_group_size(kTileThreads, kTileThreads), amdgpu_waves_per_eu(2, 2)))
 void wgrad_kernel(WgradArgs p) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kTileSmem];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1;
-    const int MT = ceil_div(p.M, BM), NT = ceil_div(p.N, BN);
-    const int G = gridDim.x, per = G >> 3;
-    const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
-    // Every expert's MT x NT tile grid is cut into mq x nq = 8 blocks, block
-    // (xcd % mq, xcd / mq) going to XCD xcd, so each A panel is fetched into
-    // nq XCDs' L2s and each B panel into mq (the host picks the cut with the
-    // least traffic).  An XCD's 'per' workgroups walk its blocks expert by
-    // expert, M tile fastest.
-    const int bm = xcd % p.mq, bn = xcd / p.mq;
-    const int mlo = bm * MT / p.mq, mhi = (bm + 1) * MT / p.mq;
-    const int nlo = bn * NT / p.nq, nhi = (bn + 1) * NT / p.nq;
-    const int bmt = mhi - mlo, cnt = bmt * (nhi - nlo);
-    for (int it = 0;; ++it) {
-        const int li = it * per + local;
-        if (cnt == 0 || li >= p.Et * cnt) break;
-        const int e = li / cnt, t = li - e * cnt;
-        const int m0 = (mlo + t % bmt) * BM, n0 = (nlo + t / bmt) * BN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const WgradTiles tiles(p.M, p.N, p.mq, p.nq);
+    int e, m0, n0;
+    for (int it = 0; tiles.get(it, p.Et - p.e_begin, e, m0, n0); ++it) {
+        e += p.e_begin;
         int KT = 0;
         for (int b = 0; b < p.nmb; ++b) KT += ceil_div(p.rows[(int64_t)b * p.mt_ld + e], kBK8);
         uint32_t aoff[4], boff[4];
@@ -126,46 +113,13 @@ void wgrad_kernel(WgradArgs p) {
         const bool shared = p.Cs0 && e == p.Et - 1;
         float* c0 = shared ? p.Cs0 : p.C0 + (int64_t)e * p.M * p.n_split;
         float* c1 = shared ? p.Cs1 : (p.C1 ? p.C1 + (int64_t)e * p.M * (p.N - p.n_split) : nullptr);
-        // Staged through LDS 64 rows at a time (full-line stores); block b is
-        // fragment b/2 of the waves with wm/2 == b%2.  M, N and n_split are
-        // multiples of 64: a 16-byte chunk lies on one side of the split and
-        // inside or outside the matrix as a whole.
-        epi_begin();
-        const int rl = (wm & 1) * 32 + (lane & 31);
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            if ((wm >> 1) == (b & 1)) {
-                const int i = b >> 1;
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        *(floatx4*)(smem + rl * kEpiPitch64 + frag_col(j, q) * 4) =
-                            floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-            }
-            __syncthreads();
-            for (int c = threadIdx.x; c < kEpiRows * 64; c += kTileThreads) {
-                const int r = c >> 6, col = n0 + (c & 63) * 4, m = m0 + b * 64 + r;
-                if (m >= p.M || col >= p.N) continue;
-                float* dst = col < p.n_split ? c0 + (int64_t)m * p.n_split + col
-                                             : c1 + (int64_t)m * (p.N - p.n_split) + (col - p.n_split);
-                *(intx4*)dst = *(const intx4*)(smem + r * kEpiPitch64 + (c & 63) * 16);
-            }
-            __syncthreads();
-        }
+        wgrad_store(acc, smem, m0, n0, p.M, p.N, p.n_split, c0, c1);
     }
 }
 
 void launch_wgrad(const WgradArgs& a, int grid, hipStream_t stream) {
-    // cut with the least L2 fill traffic: A panels (M rows) land in nq XCDs, B
-    // panels (N rows) in mq
     WgradArgs w = a;
-    const int64_t cost[4] = {(int64_t)a.M + 8ll * a.N, 2ll * a.M + 4ll * a.N, 4ll * a.M + 2ll * a.N, 8ll * a.M + a.N};
-    int best = 0;
-    for (int i = 1; i < 4; ++i)
-        if (cost[i] < cost[best]) best = i;
-    w.mq = 8 >> best;
-    w.nq = 1 << best;
+    wgrad_cut(a.M, a.N, w.mq, w.nq);
     hipLaunchKernelGGL(wgrad_kernel, dim3(grid), dim3(kTileThreads), 0, stream, w);
 }
 

@@ -440,6 +440,84 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs p, int e, int ml, int n
     }
 }
 
+// ---------------------------------------------------------------------------
+// Weight-gradient tiles, shared by the bf16 and MXFP8 kernels.  Every expert's
+// MT x NT grid of 256 x 256 output tiles is cut into mq x nq = 8 blocks, block
+// (xcd % mq, xcd / mq) going to XCD xcd (workgroups are dealt to the 8 XCDs
+// round-robin), so each A panel is fetched into nq XCDs' L2s and each B panel
+// into mq.  An XCD's workgroups walk its blocks expert by expert, M tile
+// fastest.
+// ---------------------------------------------------------------------------
+struct WgradTiles {
+    int mlo, nlo, bmt, cnt, per, local;
+    __device__ WgradTiles(int M, int N, int mq, int nq) {
+        const int MT = ceil_div(M, BM), NT = ceil_div(N, BN);
+        const int xcd = blockIdx.x & 7, bm = xcd % mq, bn = xcd / mq;
+        per = gridDim.x >> 3;
+        local = blockIdx.x >> 3;
+        mlo = bm * MT / mq;
+        nlo = bn * NT / nq;
+        bmt = (bm + 1) * MT / mq - mlo;
+        cnt = bmt * ((bn + 1) * NT / nq - nlo);
+    }
+    // this workgroup's tile number `it` over experts [0, Et): false past the last
+    __device__ bool get(int it, int Et, int& e, int& m0, int& n0) const {
+        const int li = it * per + local;
+        if (cnt == 0 || li >= Et * cnt) return false;
+        e = li / cnt;
+        const int t = li - e * cnt;
+        m0 = (mlo + t % bmt) * BM;
+        n0 = (nlo + t / bmt) * BN;
+        return true;
+    }
+};
+
+// The XCD cut with the least L2 fill traffic: A panels (M rows) land in nq
+// XCDs, B panels (N rows) in mq.
+inline void wgrad_cut(int M, int N, int& mq, int& nq) {
+    const int64_t cost[4] = {(int64_t)M + 8ll * N, 2ll * M + 4ll * N, 4ll * M + 2ll * N, 8ll * M + N};
+    int best = 0;
+    for (int i = 1; i < 4; ++i)
+        if (cost[i] < cost[best]) best = i;
+    mq = 8 >> best;
+    nq = 1 << best;
+}
+
+// Stores a 256 x 256 fp32 weight-gradient tile (accumulators in the tiles'
+// fragment layout) at rows m0.., columns n0..: columns < n_split to c0
+// [M][n_split], the rest to c1 [M][N - n_split] at column - n_split.  Staged
+// through LDS 64 rows at a time (full-line stores); block b is fragment b/2 of
+// the waves with wm/2 == b%2.  M, N and n_split are multiples of 64: a 16-byte
+// chunk lies on one side of the split and inside or outside the matrix as a
+// whole.
+__device__ __forceinline__ void wgrad_store(const floatx16 (&acc)[2][4], uint8_t* smem, int m0, int n0, int M, int N,
+                                            int n_split, float* c0, float* c1) {
+    const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) >> 1;
+    epi_begin();
+    const int rl = (wm & 1) * 32 + (lane & 31);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        if ((wm >> 1) == (b & 1)) {
+            const int i = b >> 1;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *(floatx4*)(smem + rl * kEpiPitch64 + frag_col(j, q) * 4) =
+                        floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+        }
+        __syncthreads();
+        for (int c = threadIdx.x; c < kEpiRows * 64; c += kTileThreads) {
+            const int r = c >> 6, col = n0 + (c & 63) * 4, m = m0 + b * 64 + r;
+            if (m >= M || col >= N) continue;
+            float* dst = col < n_split ? c0 + (int64_t)m * n_split + col
+                                       : c1 + (int64_t)m * (N - n_split) + (col - n_split);
+            *(intx4*)dst = *(const intx4*)(smem + r * kEpiPitch64 + (c & 63) * 16);
+        }
+        __syncthreads();
+    }
+}
+
 __device__ __forceinline__ void bf16x8_to_f32(const intx4 raw, float* f) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {

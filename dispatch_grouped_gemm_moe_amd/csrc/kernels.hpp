@@ -181,6 +181,17 @@ struct SwigluBwdArgs {
     const float* GUf;
     uint8_t* dGUq;
     uint8_t* sdGU;
+    // MXFP8 weight-gradient operands, optional (all or none, with dHf): for the
+    // rows before *dgu_row0 (the MXFP8 experts' segments) dG | dU and h
+    // quantised along the padded rows from fp32, h zero on padding rows
+    // (prow_slot < 0): codes [2I][ldt] / [I][ldt], scales in the operand layout
+    // [mx_groups(ldt)][2I][4] / [mx_groups(ldt)][I][4]; dGUT and HT then hold
+    // only the rows from *dgu_row0 on
+    const int32_t* prow_slot;
+    uint8_t* dGUTq;
+    uint8_t* sdGUT;
+    uint8_t* HTq;
+    uint8_t* sHT;
 };
 void launch_swiglu_bwd(const SwigluBwdArgs& a, int rpad, hipStream_t stream);
 
@@ -194,6 +205,7 @@ struct WgradArgs {
     const uint16_t* B;
     int64_t ld, a_mb, b_mb;
     int M, N, n_split, Et, nmb, mt_ld;
+    int e_begin;         // experts [e_begin, Et); C0 / C1 are still indexed by e
     const int32_t* prs;  // [nmb][mt_ld] first padded row of each expert, per minibatch
     const int32_t* rows;  // [nmb][mt_ld] rows of each expert, per minibatch: K stops at the last
                           // 64-row stage holding one (the rest of the tile is zero padding)
@@ -206,6 +218,28 @@ struct WgradArgs {
 
 // grid: a multiple of 8 workgroups (XCD-aware dealing).
 void launch_wgrad(const WgradArgs& a, int grid, hipStream_t stream);
+
+// MXFP8 weight gradients of experts [0, E): C[e] = A_e^T B_e over every
+// padded row of expert e's segments, minibatch by minibatch in order, both
+// operands E4M3 codes with E8M0 scales per 32 rows.  A [M][ld] and B [N][ld]
+// codes (the padded rows along each row), scales in the operand layout
+// [ld / 128][M][4] and [ld / 128][N][4]; minibatch b's copies lie a_mb / b_mb
+// code bytes and sa_mb / sb_mb scale bytes after minibatch 0's.  Segments
+// start at multiples of 128 rows; padding rows hold zero codes.
+struct MxWgradArgs {
+    const uint8_t* A;
+    const uint8_t* B;
+    const uint8_t* SA;
+    const uint8_t* SB;
+    int64_t ld, a_mb, b_mb, sa_mb, sb_mb;
+    int M, N, n_split, E, nmb, mt_ld;
+    const int32_t* prs;   // [nmb][mt_ld] first padded row of each expert
+    const int32_t* rows;  // [nmb][mt_ld] rows of each expert: K stops at the last 128-row stage holding one
+    float* C0;            // columns < n_split: [E][M][n_split]
+    float* C1;            // the rest: [E][M][N - n_split], or NULL when n_split == N
+    int mq, nq;           // XCD blocking (set by launch_mx_wgrad)
+};
+void launch_mx_wgrad(const MxWgradArgs& a, int grid, hipStream_t stream);
 
 void launch_grouped_gemm(const GemmArgs& a, GemmEpilogue epi, int grid, hipStream_t stream);
 
@@ -241,6 +275,15 @@ struct RcombArgs {
     uint8_t* dYq;
     uint8_t* sdY;
     const int32_t* dyq_row_end;
+    // MXFP8 weight-gradient operands, optional (both or neither, with dYq):
+    // for the rows before *dyq_row_end, dY (from fp32) and x (zero on padding
+    // rows) quantised along the padded rows, codes [H][ldt], scales in the
+    // operand layout [mx_groups(ldt)][H][4]; dYT and xgT then hold only the
+    // rows from *dyq_row_end on
+    uint8_t* dYTq;
+    uint8_t* sdYT;
+    uint8_t* xgTq;
+    uint8_t* sxgT;
 };
 void launch_rcomb_gather(const RcombArgs& a, int rpad, hipStream_t stream);
 

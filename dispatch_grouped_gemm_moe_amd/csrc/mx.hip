@@ -93,4 +93,201 @@ void launch_mx_gemm(const MxGemmArgs& a, GemmEpilogue epi, int grid, hipStream_t
         hipLaunchKernelGGL(mx_gemm_kernel<kEpiStore>, dim3(grid), dim3(kTileThreads), 0, stream, a);
 }
 
+// ---------------------------------------------------------------------------
+// MXFP8 weight gradients: C[e] = A_e^T B_e, the contraction running over the
+// padded rows of expert e's segments, minibatch by minibatch in order (a fixed
+// summation order).  Both operands are stored transposed ([M][ld] and [N][ld]
+// codes, the padded rows along each row), quantised along those rows in
+// 32-row blocks, so a 128-row stage is one scale dword per operand row (the
+// operand scale layout's group), as in the forward tiles.  Segments start at
+// multiples of 128 rows and their padding rows are zero codes, so every stage
+// lies inside one segment and its padding adds nothing.
+// ---------------------------------------------------------------------------
+
+// Stage sequence of expert e: for each minibatch b the 128-row stages from
+// its segment's first padded row up to the last one holding a routed row.
+struct MxSegK {
+    const int32_t* prs;   // [nmb][mt_ld]
+    const int32_t* rows;  // [nmb][mt_ld]
+    int mt_ld, e, nmb;
+    int b = -1, step = 0, nsteps = 0;
+    int64_t row0 = 0;
+    __device__ __forceinline__ void next(int& bo, int64_t& r) {
+        while (step >= nsteps && b + 1 < nmb) {
+            ++b;
+            // read through the constant address space (scalar loads, counted by
+            // lgkmcnt): the ring's vmcnt accounting sees only its own loads
+            const __attribute__((address_space(4))) int32_t* cprs =
+                (const __attribute__((address_space(4))) int32_t*)prs;
+            const __attribute__((address_space(4))) int32_t* crows =
+                (const __attribute__((address_space(4))) int32_t*)rows;
+            row0 = cprs[(int64_t)b * mt_ld + e];
+            nsteps = ceil_div(crows[(int64_t)b * mt_ld + e], 128);
+            step = 0;
+        }
+        bo = b;
+        r = row0 + (int64_t)step * 128;
+        ++step;
+    }
+};
+
+__global__ __attribute__((amdgpu_flat_work_group_size(kTileThreads, kTileThreads), amdgpu_waves_per_eu(2, 2)))
+void mx_wgrad_kernel(MxWgradArgs p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kMxSmem];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar LDS bases
+    const int wm = wave >> 1, wn = wave & 1;
+    const int fr = lane & 31, half = lane >> 5;
+    const int fsw = swz8(fr);  // a fragment's rows differ from fr by multiples of 32
+    const int arow_b = (wm * 32 + fr) * kMxRow, brow_b = kMxStageA + (wn * 128 + fr) * kMxRow;
+    const WgradTiles tiles(p.M, p.N, p.mq, p.nq);
+    int e, m0, n0;
+    for (int it = 0; tiles.get(it, p.E, e, m0, n0); ++it) {
+        int KS = 0;
+        for (int b = 0; b < p.nmb; ++b) KS += ceil_div(p.rows[(int64_t)b * p.mt_ld + e], 128);
+        floatx16 acc[2][4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
+        if (KS > 0) {
+            // Code loads: instruction i fills tile rows 32*wave + 8i .. +7 of
+            // the A and of the B block (lane/8 the row, lane%8 the fixed LDS
+            // chunk, loading the logical chunk stored there; chunks 4..7 hold
+            // the stage's second 64-row K step).  Scale load: waves 0..3 take
+            // the dwords of A rows 64*wave + lane, waves 4..7 those of B rows
+            // 64*(wave-4) + lane, landing as the stage's SA and SB arrays.
+            uint32_t aoff[4], boff[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = wave * 32 + i * 8 + (lane >> 3);
+                const int lchunk = (lane & 7) ^ swz8(r);
+                aoff[i] = (uint32_t)((int64_t)min(m0 + r, p.M - 1) * p.ld + lchunk * 16);
+                boff[i] = (uint32_t)((int64_t)min(n0 + r, p.N - 1) * p.ld + lchunk * 16);
+            }
+            // per lane: 32-bit offsets; per stage: uniform bases (minibatch,
+            // stage row) in scalar registers
+            const int srow = (wave & 3) * 64 + lane;
+            const bool bscale = wave >= 4;
+            const uint32_t soff = (uint32_t)(bscale ? min(n0 + srow, p.N - 1) : min(m0 + srow, p.M - 1)) * 4;
+            const uint8_t* s_ptr = bscale ? p.SB : p.SA;
+            const int64_t s_group = (int64_t)(bscale ? p.N : p.M) * 4;  // scale bytes per 128 rows
+            const int64_t s_mb = bscale ? p.sb_mb : p.sa_mb;
+            MxSegK kit{p.prs, p.rows, p.mt_ld, e, p.nmb};
+            const uint8_t* abase = p.A;
+            const uint8_t* bbase = p.B;
+            const uint8_t* sbase = s_ptr;
+            uint32_t kr = 0;
+            int issued = 0;
+            // stage `issued` into `slot`; past the last stage the loads repeat
+            // it into the slot no wave reads any more (constant waits)
+            auto issue = [&](int slot) {
+                if (issued < KS) {
+                    int b;
+                    int64_t r;
+                    kit.next(b, r);
+                    abase = p.A + b * p.a_mb;
+                    bbase = p.B + b * p.b_mb;
+                    sbase = s_ptr + b * s_mb + (r >> 7) * s_group;
+                    kr = (uint32_t)r;
+                }
+                ++issued;
+                uint8_t* st = smem + slot * kMxStageBytes;
+                uint8_t* base = st + (wave * 32) * kMxRow;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    __builtin_amdgcn_global_load_lds((gbl_cvoid*)(abase + (aoff[i] + kr)), (lds_void*)(base + i * 1024),
+                                                     16, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    __builtin_amdgcn_global_load_lds((gbl_cvoid*)(bbase + (boff[i] + kr)),
+                                                     (lds_void*)(base + kMxStageA + i * 1024), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((gbl_cvoid*)(sbase + soff), (lds_void*)(st + kMxStageSA + wave * 256),
+                                                 4, 0, 0);
+            };
+            // fragments of K step ks of the stage in `slot` (as the forward
+            // tiles: bytes 0..15 from the first 32-block of the K step, 16..31
+            // from the second; with ks = 0 also the scale dwords, shifted so
+            // that byte 2 * ks is this lane's block scale)
+            auto read_a = [&](int slot, int ks, int i, intx8& a, int& sa) {
+                const uint8_t* st = smem + slot * kMxStageBytes;
+                const int pc0 = ((4 * ks + half) ^ fsw) * 16, pc1 = ((4 * ks + 2 + half) ^ fsw) * 16;
+                const intx4 lo4 = *(const intx4*)(st + arow_b + i * 128 * kMxRow + pc0);
+                const intx4 hi4 = *(const intx4*)(st + arow_b + i * 128 * kMxRow + pc1);
+                a = intx8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+                if (ks == 0)
+                    sa = (int)(*(const uint32_t*)(st + kMxStageSA + (i * 128 + wm * 32 + fr) * 4) >> (8 * half));
+            };
+            auto read_b = [&](int slot, int ks, int j, intx8& b, int& sb) {
+                const uint8_t* st = smem + slot * kMxStageBytes;
+                const int pc0 = ((4 * ks + half) ^ fsw) * 16, pc1 = ((4 * ks + 2 + half) ^ fsw) * 16;
+                const intx4 lo4 = *(const intx4*)(st + brow_b + j * 32 * kMxRow + pc0);
+                const intx4 hi4 = *(const intx4*)(st + brow_b + j * 32 * kMxRow + pc1);
+                b = intx8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+                if (ks == 0)
+                    sb = (int)(*(const uint32_t*)(st + kMxStageSB + (wn * 128 + j * 32 + fr) * 4) >> (8 * half));
+            };
+            // MFMAs of K step ksc on the fragments in registers, each B
+            // fragment's registers taking fragment j of K step rks of the stage
+            // in rslot as soon as its last MFMA is issued, the A fragments last
+            auto mfmas_then = [&](auto ksc_, int rslot, int rks, intx8(&a)[2], intx8(&b)[4], int(&sa)[2],
+                                  int(&sb)[4]) {
+                constexpr int sel = 2 * decltype(ksc_)::value;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a[i], acc[i][j], 0, 0, sel,
+                                                                                     sb[j], sel, sa[i]);
+                    read_b(rslot, rks, j, b[j], sb[j]);
+                }
+#pragma unroll
+                for (int i = 0; i < 2; ++i) read_a(rslot, rks, i, a[i], sa[i]);
+            };
+            // Ring (stage j in slot j % 2, 9 direct-to-LDS loads per lane and
+            // stage): the prologue issues stages 0 and 1, waits for stage 0 and
+            // reads its first K step.  Stage s runs its first K step while
+            // reading its second, waits for stage s+1 and its own LDS reads,
+            // barrier, refills its slot with stage s+2 and runs its second K
+            // step while reading stage s+1's first.  Every stage is full.
+            static_assert(kMxStages == 2, "the vmcnt immediates below assume 2 stages of 9 loads");
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            issue(0);
+            issue(1);
+            asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+            __syncthreads();
+            intx8 fa[2], fb[4];
+            int fsa[2], fsb[4];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) read_a(0, 0, i, fa[i], fsa[i]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) read_b(0, 0, j, fb[j], fsb[j]);
+            int slot = 0;
+            for (int s = 0; s < KS; ++s) {
+                mfmas_then(std::integral_constant<int, 0>{}, slot, 1, fa, fb, fsa, fsb);
+                Interleave<8, 0, 12>::run();
+                __builtin_amdgcn_sched_barrier(0);
+                asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+                __syncthreads();
+                issue(slot);
+                // the last stage reads a stale but in-bounds repeat that nothing uses
+                mfmas_then(std::integral_constant<int, 1>{}, slot ^ 1, 0, fa, fb, fsa, fsb);
+                Interleave<8, 9, 12>::run();
+                __builtin_amdgcn_sched_barrier(0);
+                slot ^= 1;
+            }
+        }
+        float* c0 = p.C0 + (int64_t)e * p.M * p.n_split;
+        float* c1 = p.C1 ? p.C1 + (int64_t)e * p.M * (p.N - p.n_split) : nullptr;
+        wgrad_store(acc, smem, m0, n0, p.M, p.N, p.n_split, c0, c1);
+    }
+}
+
+void launch_mx_wgrad(const MxWgradArgs& a, int grid, hipStream_t stream) {
+    MxWgradArgs w = a;
+    wgrad_cut(a.M, a.N, w.mq, w.nq);
+    hipLaunchKernelGGL(mx_wgrad_kernel, dim3(grid), dim3(kTileThreads), 0, stream, w);
+}
+
 }  // namespace moe

@@ -72,7 +72,12 @@ enum moe_flags {
        drains, the device status word records MOE_DEV_WAIT_TIMEOUT with the wait
        site as detail, and `out` is unspecified.  No effect on a forward that
        runs one launch per GEMM. */
-    MOE_F_DEBUG_DROP_SIGNAL = 1u << 3
+    MOE_F_DEBUG_DROP_SIGNAL = 1u << 3,
+    /* MOE_PREC_MXFP8 only (MOE_E_INVALID otherwise): the routed experts'
+       weight-gradient GEMMs take the unquantised bf16 operands instead of
+       MXFP8 ones (the variant that keeps only the four forward and
+       input-gradient GEMMs in MXFP8).  No effect on the forward. */
+    MOE_F_BF16_WGRAD = 1u << 4
 };
 
 /* Layer shape and execution choices. */
@@ -125,8 +130,12 @@ int32_t moe_abi_version(void);
 
 /*
  * Host-only check of a cfg (no GPU needed).  MOE_E_INVALID for T<1, E<1, k<1,
- * k>E, unknown prec or flags; MOE_E_UNSUPPORTED for H or I not a multiple of
- * 64, E>256, k>16, or a cfg whose buffers would overflow 32-bit row indices.
+ * k>E, unknown prec or flags, MOE_F_BF16_WGRAD without MOE_PREC_MXFP8;
+ * MOE_E_UNSUPPORTED for H or I not a multiple of 64, E>256, k>16, T*k>2^30,
+ * or a cfg past the kernels' 32-bit operand offsets: T*H*2, R*H*2, R*4I and
+ * 4*I*H bytes must stay below 4 GiB, R being a minibatch's padded rows
+ * (256 * (ceil(minibatch * (k + shared) / 256) + E + shared - 1)).
+ * moe_query_sizes and every layer call apply the same check.
  */
 moe_status moe_validate_cfg(const moe_cfg *cfg);
 
@@ -259,12 +268,17 @@ moe_status moe_layer_fwd_static(const moe_cfg *cfg, const moe_weights *w, const 
  * The router bias is an input, not a parameter: it has no gradient.
  * Each weight gradient sums expert e's rows minibatch by minibatch in token
  * order, so results are bitwise reproducible for a given minibatch size.
- * MOE_PREC_MXFP8: the routed experts' input-gradient GEMMs take E4M3 operands
- * with E8M0 scales per 32 elements of their contraction axis (dY and Wd along
- * H for dH = dY Wd^T; dG|dU and Wg|Wu along I for dX = dG Wg^T + dU Wu^T; the
- * MXFP8 routed experts of [RW] "Rebuilding the MoE layer around
- * communication"); weight gradients use the unquantised bf16 operands and the
- * shared expert stays bf16.
+ * MOE_PREC_MXFP8: every GEMM of the routed experts takes E4M3 operands with
+ * E8M0 scales per 32 elements of its contraction axis (the MXFP8 routed
+ * experts of [RW] "Rebuilding the MoE layer around communication"): dY and Wd
+ * along H for dH = dY Wd^T; dG|dU and Wg|Wu along I for
+ * dX = dG Wg^T + dU Wu^T; and for the weight gradients dWd = h^T dY,
+ * dWg = x^T dG, dWu = x^T dU the operands x (the expert's token rows), h, dY,
+ * dG and dU along the token rows: within each (minibatch, expert) segment in
+ * blocks of 32 rows in token order, the segment's last block zero-padded.
+ * Quantisation starts from the fp32 values (bf16 for x).  With
+ * MOE_F_BF16_WGRAD the weight gradients use the unquantised bf16 operands
+ * instead.  The shared expert stays bf16.
  * MOE_E_UNSUPPORTED in identity-expert mode.
  */
 moe_status moe_layer_bwd(const moe_cfg *cfg, const moe_weights *w, const uint16_t *x,
@@ -318,10 +332,12 @@ typedef enum moe_kernel_kind {
     MOE_K_COMBINE = 4,      /* combine, and the backward's reverse-dispatch */
     MOE_K_GATHER = 5,       /* elementwise passes: MXFP8 dispatch quantisation, reverse-combine, SwiGLU backward */
     MOE_K_OTHER = 6,
-    MOE_K_WGRAD = 7,        /* weight-gradient grouped GEMMs of the backward */
+    MOE_K_WGRAD = 7,        /* weight-gradient grouped GEMMs of the backward (MOE_PREC_MXFP8 without
+                               MOE_F_BF16_WGRAD: the routed experts' scaled-MFMA ones) */
     MOE_K_DGRAD_DOWN = 8,   /* backward: dH = dY Wd^T */
     MOE_K_DGRAD_GATE_UP = 9, /* backward: dX = dG Wg^T + dU Wu^T */
-    MOE_K_SHARED_GEMM = 10, /* MOE_PREC_MXFP8: the bf16 shared expert's forward and input-gradient GEMMs */
+    MOE_K_SHARED_GEMM = 10, /* MOE_PREC_MXFP8: the bf16 shared expert's forward and input-gradient GEMMs,
+                               and its weight-gradient GEMMs unless MOE_F_BF16_WGRAD */
     MOE_K_LAYER = 11,       /* the persistent layer kernel: every forward expert GEMM and combine */
     MOE_K_COUNT = 12
 } moe_kernel_kind;

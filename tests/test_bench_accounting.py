@@ -15,9 +15,9 @@ T, H, I, K = 1000, 384, 192, 4
 HI = float(H) * I
 
 
-@pytest.mark.parametrize("shared,mx,bwd,layer", list(itertools.product([False, True], repeat=4)))
-def test_every_row_counted_once(shared, mx, bwd, layer):
-    f = bench.role_flops(T, H, I, K, shared, mx, bwd, layer)
+@pytest.mark.parametrize("shared,mx,bwd,layer,mxw", list(itertools.product([False, True], repeat=5)))
+def test_every_row_counted_once(shared, mx, bwd, layer, mxw):
+    f = bench.role_flops(T, H, I, K, shared, mx, bwd, layer, mxw)
     rows = T * K + (T if shared else 0)
     assert sum(f.values()) == (18 if bwd else 6) * HI * rows
     assert all(v > 0 for v in f.values())
@@ -28,7 +28,9 @@ def test_every_row_counted_once(shared, mx, bwd, layer):
     else:
         assert "layer" not in f
     if bwd:
-        assert f["wgrad"] == 6 * HI * rows
+        # MXFP8 weight gradients: the routed rows on the scaled-MFMA kernel,
+        # the shared expert's with its other bf16 GEMMs
+        assert f["wgrad"] == 6 * HI * (T * K if (mx and mxw) else rows)
 
 
 def test_mxfp8_shared_expert_kinds():
@@ -65,3 +67,22 @@ def test_data_movement_bytes():
     assert bm["route"] - b["route"] == T * H * (1 + 1 / 32)
     bb = bench.role_bytes(T, H, I, K, E, True, False, True, True)
     assert bb["combine"] == T * ((K + 1) * H * 2 + H * 2) and bb["gather"] > 0
+
+
+def test_backward_gather_bytes():
+    """Reverse-combine reads dout, x and Y rows; SwiGLU backward reads dH and
+    g|u (fp32 under MXFP8).  Each writes the weight-gradient operands
+    transposed (dY, x; dG|dU, h): bf16, or for routed rows with MXFP8 weight
+    gradients one code byte plus a 32nd of a scale byte per element.  The
+    input-gradient GEMMs' operands: row-major bf16 dG|dU for bf16 rows, MXFP8
+    codes of dY and dG|dU for routed rows under MXFP8."""
+    E, q = 8, 1 + 1 / 32
+    R, Rr = T * (K + 1), T * K
+    b = bench.role_bytes(T, H, I, K, E, True, False, True, True)
+    assert b["gather"] == R * (3 * H * 2 + 2 * H * 2) + R * (3 * I * 2 + 3 * I * 2 + 2 * I * 2)
+    bm = bench.role_bytes(T, H, I, K, E, True, True, True, True)
+    assert bm["gather"] == (R * (3 * H * 2 + 2 * H * 2) + Rr * H * q
+                            + R * (3 * I * 4 + 3 * I * 2) + T * 2 * I * 2 + Rr * 2 * I * q)
+    bw = bench.role_bytes(T, H, I, K, E, True, True, True, True, True)
+    # the routed rows' four transposed operands shrink from 2 bytes to q per element
+    assert bm["gather"] - bw["gather"] == Rr * (2 * H + 3 * I) * (2 - q)

@@ -47,11 +47,38 @@ def test_abi_version_and_status_strings():
     (dict(I=32), moe.MOE_E_UNSUPPORTED),
     (dict(E=300, k=2), moe.MOE_E_UNSUPPORTED),
     (dict(E=32, k=17), moe.MOE_E_UNSUPPORTED),
+    (dict(flags=moe.MOE_F_BF16_WGRAD), moe.MOE_E_INVALID),  # MXFP8 only
+    (dict(flags=moe.MOE_F_BF16_WGRAD, prec=moe.MOE_PREC_MXFP8), moe.MOE_OK),
 ])
 def test_validate_cfg(kw, want):
     base = dict(T=64, H=128, I=64, E=8, k=2)
     base.update(kw)
     assert moe.moe_validate_cfg(moe.make_cfg(**base)) == want
+
+
+def test_32bit_operand_offsets_are_enforced():
+    # the kernels address operand rows with 32-bit byte offsets: the token
+    # matrix (T*H*2), a minibatch's padded rows (R*H*2, R*4I) and one expert's
+    # weights (4*I*H) must stay below 4 GiB
+    ok = moe.make_cfg(65536, 7168, 2048, 32, 8)  # automatic minibatch of 8192
+    assert moe.moe_validate_cfg(ok) == moe.MOE_OK
+    # 299,594 tokens of 7168 bf16 values pass 4 GiB
+    assert moe.moe_validate_cfg(moe.make_cfg(299593, 7168, 2048, 32, 8, minibatch=4096)) == moe.MOE_OK
+    big_t = moe.make_cfg(299594, 7168, 2048, 32, 8, minibatch=4096)
+    assert moe.moe_validate_cfg(big_t) == moe.MOE_E_UNSUPPORTED
+    # one minibatch of 40000 tokens at k=8: R >= 320000 padded rows, R*H*2 > 4 GiB
+    big_mb = moe.make_cfg(40000, 7168, 2048, 32, 8, minibatch=40000)
+    assert moe.moe_validate_cfg(big_mb) == moe.MOE_E_UNSUPPORTED
+    for cfg in (big_t, big_mb):
+        with pytest.raises(RuntimeError):
+            moe.moe_query_sizes(cfg)
+    # R = 256 * (ceil(4096 * 8 / 256) + 31) = 40704 rows: R*4I = 2^32 - ... at I = 26368
+    # is over, at I = 26304 (R*4I < 2^32) under, with H small enough for the rest
+    R = 256 * ((4096 * 8 + 255) // 256 + 32 - 1)
+    i_over = ((1 << 32) // (4 * R) + 64) // 64 * 64
+    assert R * 4 * i_over >= 1 << 32 and R * 4 * (i_over - 64) < 1 << 32
+    assert moe.moe_validate_cfg(moe.make_cfg(4096, 64, i_over - 64, 32, 8, minibatch=4096)) == moe.MOE_OK
+    assert moe.moe_validate_cfg(moe.make_cfg(4096, 64, i_over, 32, 8, minibatch=4096)) == moe.MOE_E_UNSUPPORTED
 
 
 def test_query_sizes_h7168_i2048():

@@ -22,6 +22,12 @@ gradients must be exactly zero off the sample, the weight gradients of experts
 that no sampled token reaches exactly zero, and two reached experts' weight
 gradients (and the shared expert's) are compared whole.
 
+Under MXFP8 the routed experts' weight gradients take MXFP8 operands quantised
+along the token rows of each (minibatch, expert) segment, so a 32-row block
+can hold tokens on and off the sample: with dout kept on the sample only, the
+oracle's weight gradients then run over every token of the expert (dout zero
+off the sample) instead of over the sampled tokens alone.
+
 Tolerances: max relative error 1e-2 for bf16, 5e-2 for MXFP8.
 """
 from types import SimpleNamespace
@@ -48,6 +54,8 @@ def full(request, gpu_lib):
     layer.forward()
     torch.cuda.synchronize()
     _, idx, _ = O.route(O.as_f32(inp.x), inp.Wr, inp.bias, w.k)
+    import dispatch_grouped_gemm_moe_amd as moe
+    assert moe.moe_query_sizes(layer.cfg).minibatch == w.minibatch
     S = np.union1d(covering_tokens(idx, w.minibatch, shared=w.shared_expert), [0, w.T - 1])
     print("%s: layer forward done; oracle on %d tokens" % (w.name, len(S)), flush=True)
     fwd = O.layer_forward(inp, tokens=S, keep=True)
@@ -77,8 +85,9 @@ def test_full_size_backward_sampled_outputs(full):
     counts = np.bincount(idx.ravel(), minlength=w.E)
     experts = sorted({int(counts.argmax()), int(counts.argmin()), w.E - 1})
     cols = [0, 1 + int(np.random.default_rng(18).integers(w.I - 2)), w.I - 1]
+    mxw = w.minibatch if w.prec == "mxfp8" else None  # MXFP8 weight gradients: their segments
     for e in experts:
-        c = O.weight_grad_columns(inp, e, cols, routing=(idx, gw))
+        c = O.weight_grad_columns(inp, e, cols, routing=(idx, gw), mx_wgrad_minibatch=mxw)
         errs["dWg[%d]" % e] = O.rel_inf_err(_host(g["dWg"][e][:, cols]), c["dWg"])
         errs["dWu[%d]" % e] = O.rel_inf_err(_host(g["dWu"][e][:, cols]), c["dWu"])
         errs["dWd[%d]" % e] = O.rel_inf_err(_host(g["dWd"][e][cols, :]), c["dWd"])
@@ -115,7 +124,12 @@ def test_full_size_backward_dout_on_sampled_tokens_only(full):
                       inp.Wsg, inp.Wsu, inp.Wsd, inp.dout[S])
     every = np.arange(w.I)
     for e in sorted({int(fwd["idx"][0, 0]), int(fwd["idx"][-1, -1])}):
-        c = O.weight_grad_columns(sub, e, every, routing=(fwd["idx"], fwd["w"]))
+        if w.prec == "mxfp8":  # row blocks span sampled and unsampled tokens: every token, masked dout
+            _, idx, gw = O.route(O.as_f32(inp.x), inp.Wr, inp.bias, w.k)
+            c = O.weight_grad_columns(inp, e, every, dout=masked, routing=(idx, gw),
+                                      mx_wgrad_minibatch=w.minibatch)
+        else:
+            c = O.weight_grad_columns(sub, e, every, routing=(fwd["idx"], fwd["w"]))
         errs["dWg[%d]" % e] = O.rel_inf_err(_host(g["dWg"][e]), c["dWg"])
         errs["dWu[%d]" % e] = O.rel_inf_err(_host(g["dWu"][e]), c["dWu"])
         errs["dWd[%d]" % e] = O.rel_inf_err(_host(g["dWd"][e]), c["dWd"])

@@ -1,13 +1,28 @@
 """GPU parity of the MXFP8 layer backward through the C ABI.
 
-The routed experts' input-gradient GEMMs run on E4M3 operands with E8M0
-scales (dY and Wd quantised along H, dG | dU and Wg | Wu along I); weight
-gradients and the shared expert stay bf16.  Every gradient is compared with
-the quantisation-aware oracle (the same quantisation points, fp64 elsewhere)
-within max relative error 5e-2; the error against the unquantised oracle is
-printed as context.  The wide-range cases scale rows and columns by their own
-powers of two, so a scale taken from the wrong block or axis shows up.
+Every GEMM of the routed experts runs on E4M3 operands with E8M0 scales: dY
+and Wd quantised along H, dG | dU and Wg | Wu along I, and the weight
+gradients' operands (x rows, h, dY, dG, dU) along the token rows of each
+(minibatch, expert) segment; the shared expert stays bf16.  Every gradient is
+compared with the quantisation-aware oracle (the same quantisation points,
+fp64 elsewhere) within max relative error 5e-2; the error against the
+unquantised oracle is printed as context.  The wide-range cases scale rows
+and columns by their own powers of two, so a scale taken from the wrong block
+or axis shows up.
+
+The weight gradients must also lie much closer to the oracle's MXFP8 reading
+than the bf16-operand reading does, in relative Frobenius norm: at most a
+fifth of that reading's distance (measured: 0.02-0.04 of it), where a kernel
+that skipped or misplaced the row quantisation would sit at about the whole
+distance.  The max-error metric cannot make that distinction on small cases:
+its value there comes from isolated E4M3 code flips (an operand within
+rounding distance of a code midpoint, which the GPU's fp32 arithmetic and the
+oracle's fp64 put on different sides), each moving one row or column of one
+expert's gradient by up to an eighth of that operand's contribution.
+MOE_F_BF16_WGRAD (bf16 weight-gradient operands) is compared with the
+oracle's bf16 weight gradients the same way.
 """
+import numpy as np
 import pytest
 import torch
 
@@ -35,21 +50,67 @@ MXB_CASES = [
 ]
 
 
+WGRADS = ("dWg", "dWu", "dWd")
+READING_FRAC = 0.2
+
+
+def _fro(a, b):
+    """||a - b||_F / ||b||_F"""
+    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
 @pytest.mark.parametrize("w", MXB_CASES, ids=lambda w: w.name)
 def test_mx_backward_matches_quantisation_aware_oracle(gpu_lib, w):
+    import dispatch_grouped_gemm_moe_amd as moe
     from gpu_harness import Layer
     inp = make_inputs(w, with_dout=True)
     layer = Layer(inp)
+    mb = moe.moe_query_sizes(layer.cfg).minibatch
+    print("%s: minibatch %d" % (w.name, mb), flush=True)
     layer.forward()
     got = layer.backward(inp.dout)
-    ref = O.layer_backward(inp, fwd=O.layer_forward(inp, keep=True))
+    fwd = O.layer_forward(inp, keep=True)
+    ref = O.layer_backward(inp, fwd=fwd, mx_wgrad_minibatch=mb)
+    bf16_wgrad = O.layer_backward(inp, fwd=fwd)
     plain = O.layer_backward(inp, fwd=O.layer_forward(inp, keep=True, mx=False), mx=False)
     names = ["dx", "dWg", "dWu", "dWd", "dWr", "dgate"] + (["dWsg", "dWsu", "dWsd"] if w.shared_expert else [])
     errs = {n: O.rel_inf_err(got[n].numpy(), ref[n]) for n in names}
     ctx = {n: O.rel_inf_err(got[n].numpy(), plain[n]) for n in names}
+    fro = {n: _fro(got[n].numpy(), ref[n]) for n in WGRADS}
+    gap = {n: _fro(bf16_wgrad[n], ref[n]) for n in WGRADS}
     print(w.name, " ".join("%s %.2e (unquantised %.2e)" % (n, errs[n], ctx[n]) for n in names))
+    print(w.name, "weight gradients, relative Frobenius error:",
+          " ".join("%s %.2e (bf16 reading %.2e)" % (n, fro[n], gap[n]) for n in WGRADS))
     for n, e in errs.items():
         assert e <= MX_TOL, (n, e)
+    for n in WGRADS:
+        assert fro[n] <= READING_FRAC * gap[n], (n, fro[n], gap[n])
+
+
+@pytest.mark.parametrize("w", [c for c in MXB_CASES if c.name in ("mxb_shared", "mxb_tiles", "mxb_chunks_shared")],
+                         ids=lambda w: w.name)
+def test_mx_backward_bf16_weight_gradients(gpu_lib, w):
+    import dispatch_grouped_gemm_moe_amd as moe
+    from gpu_harness import Layer
+    inp = make_inputs(w, with_dout=True)
+    layer = Layer(inp, flags=moe.MOE_F_BF16_WGRAD)
+    layer.forward()
+    got = layer.backward(inp.dout)
+    fwd = O.layer_forward(inp, keep=True)
+    ref = O.layer_backward(inp, fwd=fwd)
+    mxw = O.layer_backward(inp, fwd=fwd, mx_wgrad_minibatch=moe.moe_query_sizes(layer.cfg).minibatch)
+    names = ["dx", "dWg", "dWu", "dWd", "dWr", "dgate"] + (["dWsg", "dWsu", "dWsd"] if w.shared_expert else [])
+    errs = {n: O.rel_inf_err(got[n].numpy(), ref[n]) for n in names}
+    fro = {n: _fro(got[n].numpy(), ref[n]) for n in WGRADS}
+    gap = {n: _fro(mxw[n], ref[n]) for n in WGRADS}
+    print(w.name, "bf16 weight gradients:", " ".join("%s %.2e" % kv for kv in errs.items()),
+          "| relative Frobenius error:", " ".join("%s %.2e (MXFP8 reading %.2e)" % (n, fro[n], gap[n])
+                                                   for n in WGRADS))
+    for n, e in errs.items():
+        assert e <= MX_TOL, (n, e)
+    for n in WGRADS:
+        assert fro[n] <= READING_FRAC * gap[n], (n, fro[n], gap[n])
 
 
 def test_mx_forward_wide_range_matches_oracle(gpu_lib):
