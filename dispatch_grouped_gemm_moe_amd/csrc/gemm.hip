@@ -113,7 +113,7 @@ void wgrad_kernel(WgradArgs p) {
         const bool shared = p.Cs0 && e == p.Et - 1;
         float* c0 = shared ? p.Cs0 : p.C0 + (int64_t)e * p.M * p.n_split;
         float* c1 = shared ? p.Cs1 : (p.C1 ? p.C1 + (int64_t)e * p.M * (p.N - p.n_split) : nullptr);
-        wgrad_store(acc, smem, m0, n0, p.M, p.N, p.n_split, c0, c1);
+        wgrad_store(acc, m0, n0, p.M, p.N, p.n_split, c0, c1);
     }
 }
 

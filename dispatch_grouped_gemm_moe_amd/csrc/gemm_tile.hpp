@@ -485,36 +485,31 @@ inline void wgrad_cut(int M, int N, int& mq, int& nq) {
 
 // Stores a 256 x 256 fp32 weight-gradient tile (accumulators in the tiles'
 // fragment layout) at rows m0.., columns n0..: columns < n_split to c0
-// [M][n_split], the rest to c1 [M][N - n_split] at column - n_split.  Staged
-// through LDS 64 rows at a time (full-line stores); block b is fragment b/2 of
-// the waves with wm/2 == b%2.  M, N and n_split are multiples of 64: a 16-byte
-// chunk lies on one side of the split and inside or outside the matrix as a
-// whole.
-__device__ __forceinline__ void wgrad_store(const floatx16 (&acc)[2][4], uint8_t* smem, int m0, int n0, int M, int N,
-                                            int n_split, float* c0, float* c1) {
+// [M][n_split], the rest to c1 [M][N - n_split] at column - n_split.  Straight
+// from the registers: each store writes 16 bytes (a run of four columns) of 32
+// rows per half-wave, and the four runs of a fragment fill 128 contiguous
+// bytes of each row.  Staged through LDS as whole rows instead (four 64-row
+// blocks, two barriers each) the MXFP8 weight gradients of 16384 tokens at
+// H=7168, I=2048, E=32, k=8 took 7.72 ms per step against 7.22 ms; with
+// non-temporal stores 9.23 ms.  M, N and n_split are multiples of 64: a run
+// lies on one side of the split and inside or outside the matrix as a whole.
+__device__ __forceinline__ void wgrad_store(const floatx16 (&acc)[2][4], int m0, int n0, int M, int N, int n_split,
+                                            float* c0, float* c1) {
     const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) >> 1;
-    epi_begin();
-    const int rl = (wm & 1) * 32 + (lane & 31);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        if ((wm >> 1) == (b & 1)) {
-            const int i = b >> 1;
+    for (int i = 0; i < 2; ++i) {
+        const int m = m0 + 128 * i + 32 * wm + (lane & 31);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *(floatx4*)(smem + rl * kEpiPitch64 + frag_col(j, q) * 4) =
-                        floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        }
-        __syncthreads();
-        for (int c = threadIdx.x; c < kEpiRows * 64; c += kTileThreads) {
-            const int r = c >> 6, col = n0 + (c & 63) * 4, m = m0 + b * 64 + r;
-            if (m >= M || col >= N) continue;
-            float* dst = col < n_split ? c0 + (int64_t)m * n_split + col
-                                       : c1 + (int64_t)m * (N - n_split) + (col - n_split);
-            *(intx4*)dst = *(const intx4*)(smem + r * kEpiPitch64 + (c & 63) * 16);
-        }
-        __syncthreads();
+            for (int q = 0; q < 4; ++q) {
+                const int col = n0 + frag_col(j, q);
+                if (m >= M || col >= N) continue;
+                float* dst = col < n_split ? c0 + (int64_t)m * n_split + col
+                                           : c1 + (int64_t)m * (N - n_split) + (col - n_split);
+                *(floatx4*)dst = floatx4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                         acc[i][j][4 * q + 3]};
+            }
     }
 }
 

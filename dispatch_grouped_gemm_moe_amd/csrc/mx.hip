@@ -250,8 +250,10 @@ void mx_wgrad_kernel(MxWgradArgs p) {
             // reading its second, waits for stage s+1 and its own LDS reads,
             // barrier, refills its slot with stage s+2 and runs its second K
             // step while reading stage s+1's first.  Every stage is full.
+            // (the previous tile's stores may still be in flight: the vmcnt
+            // waits count them too, and only ever wait longer for them)
             static_assert(kMxStages == 2, "the vmcnt immediates below assume 2 stages of 9 loads");
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             __syncthreads();
             issue(0);
             issue(1);
@@ -280,7 +282,7 @@ void mx_wgrad_kernel(MxWgradArgs p) {
         }
         float* c0 = p.C0 + (int64_t)e * p.M * p.n_split;
         float* c1 = p.C1 ? p.C1 + (int64_t)e * p.M * (p.N - p.n_split) : nullptr;
-        wgrad_store(acc, smem, m0, n0, p.M, p.N, p.n_split, c0, c1);
+        wgrad_store(acc, m0, n0, p.M, p.N, p.n_split, c0, c1);
     }
 }
 
