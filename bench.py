@@ -250,7 +250,8 @@ def measure(moe, torch, w, bwd: bool, steps: int, warmup: int, comm_cus: int = 0
               "dgrad_gate_up": "mx_gemm_kernel<1>" if mx else "grouped_gemm_kernel<1>",
               "wgrad": "mx_wgrad_kernel" if mx_wgrad else "wgrad_kernel",
               "shared_gemm": "grouped_gemm_kernel (bf16 shared expert)",
-              "layer": "mega_kernel<%s>" % ("true" if mx else "false")}
+              "layer": "mega_kernel<%s, %s>" % ("true" if mx else "false",
+                                                 "true" if (not mx or w.shared_expert) else "false")}
     by_sym = {}
     for kd, fl in flops.items():
         n, ms = kt[kd]
@@ -264,7 +265,7 @@ def measure(moe, torch, w, bwd: bool, steps: int, warmup: int, comm_cus: int = 0
     dom_flops, ms_dom, n_dom, dom_roles = by_sym[dom]
     achieved = dom_flops / (ms_dom / 1e3) / 1e12
     # the scaled-MFMA kernels (and the MXFP8 layer kernel) are priced at the FP8 peak
-    peak = PEAK_FP8_TFLOPS if (mx and (dom.startswith("mx_") or dom == "mega_kernel<true>")) else PEAK_BF16_TFLOPS
+    peak = PEAK_FP8_TFLOPS if (mx and (dom.startswith("mx_") or dom.startswith("mega_kernel<true"))) else PEAK_BF16_TFLOPS
     nbytes = role_bytes(T, H, I, k, E, w.shared_expert, mx, bwd, layer_kernel, mx_wgrad)
     res = {
         "value": T * steps / elapsed,
@@ -531,8 +532,8 @@ def cpu_baseline(inp, n_tokens: int, bwd: bool) -> dict:
     mx = inp.w.prec == "mxfp8"
     t0 = time.perf_counter()
     fwd = oracle.layer_forward(sub, keep=bwd)
-    if bwd:
-        oracle.layer_backward(sub, fwd=fwd)
+    if bwd:  # MXFP8: the weight gradients' row quantisation too, as the library runs it by default
+        oracle.layer_backward(sub, fwd=fwd, mx_wgrad_minibatch=inp.w.minibatch if mx else None)
     dt = time.perf_counter() - t0
     t0 = time.perf_counter()
     for e in range(inp.w.E):  # the per-expert fp64 widening alone

@@ -190,10 +190,15 @@ __device__ void combine_range(const MegaArgs& a, int b, int c0, int c1, uint8_t*
 }
 
 
-// 512 threads: the bf16 and MXFP8 tiles both run eight waves (two per SIMD)
-template <bool kMx>
+// 512 threads: the bf16 and MXFP8 tiles both run eight waves (two per SIMD).
+// kMx: the routed experts run scaled-MFMA tiles; kBf16 (always with !kMx):
+// bf16 tiles are compiled in, for a bf16 layer or the shared expert of an
+// MXFP8 one.  Without them the MXFP8 kernel holds its state in 253 VGPRs with
+// no spill, against 256 with 38 spilled (and 199 against 411 SGPRs spilled).
+template <bool kMx, bool kBf16>
 __global__ __attribute__((amdgpu_flat_work_group_size(kTileThreads, kTileThreads), amdgpu_waves_per_eu(2, 2)))
 void mega_kernel(MegaArgs a) {
+    static_assert(kMx || kBf16, "a bf16 layer runs bf16 tiles");
     constexpr int kSmem = kMx ? (kMxSmem > kTileSmem ? kMxSmem : kTileSmem) : kTileSmem;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
     // wait result broadcast: the ring's last dword, free between tiles (the
@@ -297,7 +302,7 @@ void mega_kernel(MegaArgs a) {
         // (kPadPerWave; layer kernel 13.0 -> 12.7 ms bf16, 8.1 -> 8.0 ms
         // MXFP8); the gate|up tiles run every fragment: the same skip there
         // measured 4% slower.
-        const bool mx_tile = kMx && e < a.e_mx;
+        const bool mx_tile = kMx && (!kBf16 || e < a.e_mx);
         if (kind == kGateUp) {
             if (mx_tile) {
                 MxGemmArgs m = a.m1;
@@ -343,10 +348,10 @@ hipError_t launch_mega(const MegaArgs& a, int grid, hipStream_t stream) {
                        3 * a.nmb + 1);
     MegaArgs args = a;
     void* kargs[] = {&args};
-    return a.mx ? hipLaunchCooperativeKernel((const void*)mega_kernel<true>, dim3(grid), dim3(kTileThreads), kargs,
-                                              0, stream)
-                  : hipLaunchCooperativeKernel((const void*)mega_kernel<false>, dim3(grid), dim3(kTileThreads), kargs,
-                                              0, stream);
+    const void* fn = !a.mx ? (const void*)mega_kernel<false, true>
+                           : (a.e_mx < a.e_end ? (const void*)mega_kernel<true, true>   // with the shared expert
+                                               : (const void*)mega_kernel<true, false>);
+    return hipLaunchCooperativeKernel(fn, dim3(grid), dim3(kTileThreads), kargs, 0, stream);
 }
 
 }  // namespace moe
