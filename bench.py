@@ -316,12 +316,13 @@ def role_bytes(T: int, H: int, I: int, k: int, E: int, shared: bool, mx: bool, b
       combine (per-GEMM forward): k (+1 shared) expert-output rows read and one
         output row written per token; in a backward step the kind is the
         reverse-dispatch: k (+1) input-gradient rows read, dx written;
-      gather (backward): reverse-combine (dout, x and Y rows read; transposed
-        dY and x written; MXFP8 codes + scales of dY) and SwiGLU backward (dH
-        and g|u read, fp32 under MXFP8; dG|dU row-major for bf16 GEMMs,
-        transposed dG|dU and h written; MXFP8 codes + scales of dG|dU).  With
-        MXFP8 weight gradients (mx_wgrad) the routed rows' transposed dY, x,
-        dG|dU and h are written as codes + scales instead of bf16."""
+      gather (backward): reverse-combine (dout rows read, and Y rows of the
+        routed rows; MXFP8 codes + scales of dY) and SwiGLU backward (dH and
+        g|u read, fp32 under MXFP8; row-major dG|dU and w*h written for the
+        rows whose weight gradients take bf16 operands, MXFP8 codes + scales
+        of dG|dU for the MXFP8 input gradient).  With MXFP8 weight gradients
+        (mx_wgrad) the routed rows' x rows are read too, and their dY, x,
+        dG|dU and h are written transposed as codes + scales."""
     ks = k + (1 if shared else 0)
     R, Rr = T * ks, T * k  # rows (routed + shared), routed rows
     q = 1.0 + 1.0 / 32  # MXFP8 code + scale bytes per element
@@ -329,12 +330,10 @@ def role_bytes(T: int, H: int, I: int, k: int, E: int, shared: bool, mx: bool, b
     if bwd:
         b["combine"] = T * (ks * H * 2 + H * 2)
         rows_mx = Rr if mx else 0
-        rows_bf16 = R - rows_mx
         rows_w = Rr if (mx and mx_wgrad) else 0  # quantised weight-gradient operands
         f = 4 if mx else 2
-        rcomb = R * 3 * H * 2 + (R - rows_w) * 2 * H * 2 + rows_w * 2 * H * q + rows_mx * H * q
-        swiglu = (R * 3 * I * f + (R - rows_w) * 3 * I * 2 + rows_w * 3 * I * q
-                  + rows_bf16 * 2 * I * 2 + rows_mx * 2 * I * q)
+        rcomb = R * H * 2 + Rr * H * 2 + rows_w * H * 2 + rows_w * 2 * H * q + rows_mx * H * q
+        swiglu = R * 3 * I * f + (R - rows_w) * 3 * I * 2 + rows_w * 3 * I * q + rows_mx * 2 * I * q
         b["gather"] = rcomb + swiglu
     elif not layer_kernel:
         b["combine"] = T * (ks * H * 2 + H * 2)

@@ -55,7 +55,7 @@ struct Plan {
     size_t sv_idx, sv_w, sv_mb0, sv_mb, sv_y, saved;
     // backward workspace (bytes)
     size_t wb_wrt, wb_mt, wb_prs, wb_rows, wb_lay0, lay_bytes, ly_hdr, ly_prow_token, ly_tok_prow, ly_prow_slot;
-    size_t wb_dyt, wb_xgt, wb_dgut, wb_ht, wb_dsel, wb_dgu, wb_dh, wb_dx, wb_dgp, wb_roww, ws_bwd;
+    size_t wb_dgu, wb_hw, wb_dsel, wb_dh, wb_dx, wb_dgp, wb_roww, ws_bwd;
     size_t wb_dyq, wb_sdy, wb_dguq, wb_sdgu;  // MXFP8 operands of the input-gradient GEMMs
     bool mxw;  // MXFP8 weight gradients of the routed experts
     // their operands, one copy per minibatch: codes and scales of dY, x, dG | dU, h
@@ -235,10 +235,11 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     p->wb_prs = o; o = align_up(o + nmb * (Et + 1) * 4);
     p->wb_rows = o; o = align_up(o + nmb * (Et + 1) * 4);
     p->wb_lay0 = o; o += nmb * p->lay_bytes;
-    p->wb_dyt = o; o = align_up(o + nmb * H * rp * 2);
-    p->wb_xgt = o; o = align_up(o + nmb * H * rp * 2);
-    p->wb_dgut = o; o = align_up(o + nmb * 2 * I * rp * 2);
-    p->wb_ht = o; o = align_up(o + nmb * I * rp * 2);
+    // bf16 weight-gradient row operands of every minibatch (the other
+    // operands, x and dout, are read through the row map): dG | dU, which the
+    // bf16 gate|up input-gradient GEMM also reads, and w * h
+    p->wb_dgu = o; o = align_up(o + nmb * rp * 2 * I * 2);
+    p->wb_hw = o; o = align_up(o + nmb * rp * I * 2);
     p->wb_dsel = o; o = align_up(o + nmb * rp * 4);
     // one copy per minibatch of a backward chunk: the chunk's input-gradient
     // GEMMs run as one launch over its minibatches
@@ -247,7 +248,6 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     // scales each output row by its weight (row_w); the MXFP8 one reads the
     // quantised dY
     p->wb_roww = o; o = align_up(o + nc * rp * 4);
-    p->wb_dgu = o; o = align_up(o + nc * rp * 2 * I * 2);
     p->wb_dh = o; o = align_up(o + nc * rp * I * (p->mx ? 4 : 2));
     p->wb_dx = o; o = align_up(o + nc * rp * H * 2);
     p->wb_dgp = o; o = align_up(o + nc * rp * (H / 64) * 4);
@@ -678,12 +678,9 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
     float* WrT = (float*)(wsb + p.wb_wrt);
     int32_t* mt_all = (int32_t*)(wsb + p.wb_mt);
     int32_t* prs_all = (int32_t*)(wsb + p.wb_prs);
-    uint16_t* dYT_all = (uint16_t*)(wsb + p.wb_dyt);
-    uint16_t* xgT_all = (uint16_t*)(wsb + p.wb_xgt);
-    uint16_t* dGUT_all = (uint16_t*)(wsb + p.wb_dgut);
-    uint16_t* HT_all = (uint16_t*)(wsb + p.wb_ht);
+    uint16_t* dGU_all = (uint16_t*)(wsb + p.wb_dgu);
+    uint16_t* HW_all = (uint16_t*)(wsb + p.wb_hw);
     float* dsel_all = (float*)(wsb + p.wb_dsel);
-    uint16_t* dGU = (uint16_t*)(wsb + p.wb_dgu);
     uint16_t* dH = (uint16_t*)(wsb + p.wb_dh);
     uint16_t* dXb = (uint16_t*)(wsb + p.wb_dx);
     float* dgp = (float*)(wsb + p.wb_dgp);
@@ -716,6 +713,9 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
     // per minibatch).  The per-minibatch buffers hold one chunk; minibatch b
     // uses copy b - b0.
     const int e_bf16 = p.mx ? E : 0;  // MXFP8: experts [0, E) on the scaled-MFMA kernel, the shared expert bf16
+    // weight gradients: under MXFP8 ones experts [0, E) on the scaled-MFMA
+    // kernel, the shared expert (if any) on the bf16 one
+    const int w_bf16 = p.mxw ? E : 0;
     const int32_t* rows_all = (const int32_t*)(wsb + p.wb_rows);
     const int64_t nhb = H / 64;
     float* dHf = p.mx ? (float*)dH : nullptr;  // fp32 under MXFP8
@@ -733,9 +733,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             rc.dout = dout; rc.x = x; rc.Y = (const uint16_t*)(svb + p.sv_y); rc.topk_w = gw;
             rc.prow_token = (int32_t*)(lay + p.ly_prow_token);
             rc.prow_slot = (int32_t*)(lay + p.ly_prow_slot); rc.hdr = (LayoutHeader*)(lay + p.ly_hdr);
-            rc.dY = nullptr;
             rc.row_w = roww + j * rp;
-            rc.dYT = dYT_all + (size_t)b * H * rp; rc.xgT = xgT_all + (size_t)b * H * rp;
             rc.dgp = dgp + j * rp * nhb; rc.dsel = dsel_all + (size_t)b * rp;
             rc.H = H; rc.k = k; rc.nhb = (int)nhb; rc.ldt = rp;
             // MXFP8: dY quantised from fp32 here (along H, the down input-gradient GEMM's K)
@@ -784,8 +782,9 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             const size_t bh = j * rp * I;  // this minibatch's dH elements
             SwigluBwdArgs sb{};
             sb.dH = p.mx ? nullptr : dH + bh; sb.GU = (const uint16_t*)svb; sb.hdr = (LayoutHeader*)(lay + p.ly_hdr);
-            sb.dGU = dGU + 2 * bh; sb.dGUT = dGUT_all + (size_t)b * 2 * I * rp; sb.HT = HT_all + (size_t)b * I * rp;
-            sb.dgu_row0 = prs_all + (size_t)b * (Et + 1) + e_bf16;  // bf16: row 0 (every row)
+            sb.row_w = roww + j * rp;
+            sb.dGU = dGU_all + (size_t)b * rp * 2 * I; sb.HW = HW_all + (size_t)b * rp * I;
+            sb.dgu_row0 = prs_all + (size_t)b * (Et + 1) + w_bf16;  // bf16 weight gradients: row 0 (every row)
             sb.I = I; sb.ldt = rp;
             // MXFP8: fp32 inputs, dG|dU quantised here (along I, the gate|up input-gradient GEMM's K)
             sb.dHf = p.mx ? dHf + bh : nullptr; sb.GUf = p.mx ? (const float*)svb : nullptr;
@@ -814,7 +813,7 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
         }
         if (e_bf16 < Et) {
             GemmArgs g2{};  // dX = dG Wg^T + dU Wu^T
-            g2.A = dGU; g2.a_row_map = nullptr; g2.lda = 2 * I;
+            g2.A = dGU_all + (size_t)b0 * rp * 2 * I; g2.a_row_map = nullptr; g2.lda = 2 * I;
             g2.B = Wgu; g2.b_stride = (int64_t)H * 2 * I;
             g2.C = dXb; g2.ldc = H; g2.N = H; g2.K = 2 * I;
             g2.mt_start = mt_c; g2.prow_start = prs_c; g2.hdr = nullptr; g2.Et = Et;
@@ -837,9 +836,6 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
             TIMED(MOE_K_COMBINE, s, launch_rdispatch(rd, Tm, s));
         }
     }
-    // MXFP8 weight gradients: experts [0, E) on the scaled-MFMA kernel, the
-    // shared expert (if any) on the bf16 one
-    const int w_bf16 = p.mxw ? E : 0;
     if (p.mxw) {
         MxWgradArgs qa{};  // [dWg | dWu][e] = Q(x_e)^T Q([dG | dU]_e)
         qa.A = wsb + p.wb_xgtq; qa.SA = wsb + p.wb_sxgt; qa.B = wsb + p.wb_dgutq; qa.SB = wsb + p.wb_sdgut;
@@ -857,17 +853,20 @@ moe_status moe_layer_bwd(const moe_cfg* cfg, const moe_weights* w, const uint16_
         TIMED(MOE_K_WGRAD, s, launch_mx_wgrad(qd, grid, s));
     }
     if (w_bf16 < Et) {
+        // row -> token maps of the minibatches: the gathered operands x and dout
+        const int32_t* map0 = (const int32_t*)(lay_of(0) + p.ly_prow_token);
+        const int64_t map_mb = (int64_t)p.lay_bytes / 4;
         WgradArgs wa{};  // [dWg | dWu][e] = x_e^T [dG | dU]_e over every row of expert e
-        wa.A = xgT_all; wa.B = dGUT_all; wa.ld = rp;
-        wa.a_mb = (int64_t)H * rp * 2; wa.b_mb = (int64_t)2 * I * rp * 2;
+        wa.A = x; wa.lda = H; wa.gather = 1; wa.map = map0; wa.map_mb = map_mb;
+        wa.B = dGU_all; wa.ldb = 2 * I; wa.b_mb = rp * 2 * I;
         wa.M = H; wa.N = 2 * I; wa.n_split = I; wa.Et = Et; wa.e_begin = w_bf16; wa.nmb = p.nmb; wa.mt_ld = Et + 1;
         wa.prs = prs_all; wa.rows = rows_all;
         wa.C0 = dWg; wa.C1 = dWu;
         wa.Cs0 = p.shared ? dWs : nullptr; wa.Cs1 = p.shared ? dWs + (size_t)H * I : nullptr;
         TIMED(p.mxw ? MOE_K_SHARED_GEMM : MOE_K_WGRAD, s, launch_wgrad(wa, grid, s));
-        WgradArgs wd{};  // dWd[e] = h_e^T dY_e
-        wd.A = HT_all; wd.B = dYT_all; wd.ld = rp;
-        wd.a_mb = (int64_t)I * rp * 2; wd.b_mb = (int64_t)H * rp * 2;
+        WgradArgs wd{};  // dWd[e] = h_e^T dY_e = (w h)_e^T dout[t_r]
+        wd.A = HW_all; wd.lda = I; wd.a_mb = rp * I;
+        wd.B = dout; wd.ldb = H; wd.gather = 2; wd.map = map0; wd.map_mb = map_mb;
         wd.M = I; wd.N = H; wd.n_split = H; wd.Et = Et; wd.e_begin = w_bf16; wd.nmb = p.nmb; wd.mt_ld = Et + 1;
         wd.prs = prs_all; wd.rows = rows_all;
         wd.C0 = dWd; wd.C1 = nullptr;

@@ -11,8 +11,6 @@
 //     dsel = w * (dgate - <w, dgate>) is the softmax backward.
 // Every floating-point sum has a fixed order (no atomics), so results are
 // bitwise reproducible.
-#include <type_traits>
-
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mxfp8.hpp"
@@ -21,27 +19,45 @@ namespace moe {
 
 constexpr int kTile = 64;
 
+__device__ __forceinline__ void unpack16_bf16(const intx4* src, float* f) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const intx4 a = src[q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f[8 * q + 2 * e] = __builtin_bit_cast(float, (uint32_t)a[e] << 16);
+            f[8 * q + 2 * e + 1] = __builtin_bit_cast(float, (uint32_t)a[e] & 0xffff0000u);
+        }
+    }
+}
+
+__device__ __forceinline__ void pack16_bf16(const uint16_t* v, intx4* dst) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        intx4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (int)((uint32_t)v[8 * q + 2 * e] | ((uint32_t)v[8 * q + 2 * e + 1] << 16));
+        dst[q] = o;
+    }
+}
+
 // One workgroup per 64 padded rows x 64 hidden columns of a minibatch.
-//   dY[prow][h]   = bf16(w * dout[t][h])  (0 on padding rows), if dY is set
 //   row_w[prow]   = w (0 on padding rows), if row_w is set
-//   dYT[h][prow]  = the same, transposed (weight-gradient operand)
-//   xgT[h][prow]  = x[t][h], transposed (weight-gradient operand)
 //   dYq, sdY      = MXFP8 codes and scales of w * dout[t] (rows before padded
 //                   row *dyq_row_end), if dYq is set
 //   dgp[prow][hb] = sum over the block's 64 columns of dout[t][h] * Y[prow][h]
 //                   (routed rows; in column order, then a fixed pair tree)
 //   dsel[prow]    = 0 (filled for routed rows by the reverse-dispatch)
-// MXW (MXFP8 weight gradients): a block of rows before *dyq_row_end writes
-// dYT and xgT as E4M3 codes quantised along the padded rows instead (dY from
-// its fp32 values, x zero on padding rows), a block from it on writes bf16.
-// The block of 64 rows lies inside one expert segment (segments start at
-// multiples of 128 rows), so the choice is uniform over the workgroup.
+// MXW (MXFP8 weight gradients): a block of rows before *dyq_row_end also
+// writes dY (from its fp32 values) and x (zero on padding rows), quantised
+// along the padded rows, through LDS transposes.  The block of 64 rows lies
+// inside one expert segment (segments start at multiples of 128 rows), so the
+// choice is uniform over the workgroup.  bf16 weight gradients need neither
+// copy: they read dout and x rows through the row map.
 template <bool MXW>
 __global__ __launch_bounds__(256) void rcomb_gather_kernel(RcombArgs p) {
-    // MXW stages dY in fp32 (its quantisation input), else in bf16
-    using StY = typename std::conditional<MXW, float, uint16_t>::type;
-    __shared__ StY sY[kTile][kTile + (MXW ? 1 : 2)];
-    __shared__ uint16_t sX[kTile][kTile + 2];
+    __shared__ float sY[MXW ? kTile : 1][kTile + 1];
+    __shared__ uint16_t sX[MXW ? kTile : 1][kTile + 2];
     const int prow0 = blockIdx.x * kTile, h0 = blockIdx.y * kTile;
     if (prow0 >= p.hdr->prows) return;
     const int tid = threadIdx.x;
@@ -50,19 +66,16 @@ __global__ __launch_bounds__(256) void rcomb_gather_kernel(RcombArgs p) {
     const int slot = p.prow_slot[prow];
     const int t = p.prow_token[prow];
     const float w = slot < 0 ? 0.0f : (slot < p.k ? p.topk_w[(int64_t)t * p.k + slot] : 1.0f);
-    float d[16], xv[16];
+    float d[16];
     {
         const intx4* src = (const intx4*)(p.dout + (int64_t)t * p.H + h0 + c0);
-        const intx4* xs = (const intx4*)(p.x + (int64_t)t * p.H + h0 + c0);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            const intx4 a = src[q], b = xs[q];
+            const intx4 a = src[q];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 d[8 * q + 2 * e] = __builtin_bit_cast(float, (uint32_t)a[e] << 16);
                 d[8 * q + 2 * e + 1] = __builtin_bit_cast(float, (uint32_t)a[e] & 0xffff0000u);
-                xv[8 * q + 2 * e] = __builtin_bit_cast(float, (uint32_t)b[e] << 16);
-                xv[8 * q + 2 * e + 1] = __builtin_bit_cast(float, (uint32_t)b[e] & 0xffff0000u);
             }
         }
     }
@@ -89,71 +102,34 @@ __global__ __launch_bounds__(256) void rcomb_gather_kernel(RcombArgs p) {
             if (p.row_w) p.row_w[prow] = w;
         }
     }
-    uint16_t dy[16];
     float dyf[16];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-        dyf[c] = w * d[c];
-        dy[c] = f32_to_bf16_rne(dyf[c]);
-        if constexpr (MXW) {
-            sY[c0 + c][r] = dyf[c];
-            sX[c0 + c][r] = slot < 0 ? (uint16_t)0 : f32_to_bf16_rne(xv[c]);
-        } else {
-            sY[c0 + c][r] = dy[c];
-            sX[c0 + c][r] = f32_to_bf16_rne(xv[c]);
-        }
-    }
+    for (int c = 0; c < 16; ++c) dyf[c] = w * d[c];
     // MXFP8 operand of the down input-gradient GEMM, from the fp32 values
     if (p.dYq && prow < *p.dyq_row_end)
         mx_quant_row64(dyf, tid & 3, p.dYq + (int64_t)prow * p.H + h0, p.sdY, p.ldt, prow, h0 / 64, p.H / 64);
-    if (p.dY) {
-        intx4* dst = (intx4*)(p.dY + (int64_t)prow * p.H + h0 + c0);
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            intx4 o;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = (int)((uint32_t)dy[8 * q + 2 * e] | ((uint32_t)dy[8 * q + 2 * e + 1] << 16));
-            dst[q] = o;
-        }
-    }
-    __syncthreads();
-    // transposed tiles: thread -> column h0 + tid/4, rows prow0 + 16*(tid%4) .. +16
-    const int hc = tid >> 2, r0 = (tid & 3) * 16;
     if constexpr (MXW) {
-        if (prow0 < *p.dyq_row_end) {
-            // four consecutive lanes hold the column's 64 rows: two 32-row blocks
-            float v[16];
+        if (prow0 >= *p.dyq_row_end) return;
+        float xv[16];
+        unpack16_bf16((const intx4*)(p.x + (int64_t)t * p.H + h0 + c0), xv);
 #pragma unroll
-            for (int q = 0; q < 16; ++q) v[q] = sY[hc][r0 + q];
-            mx_quant_row64(v, tid & 3, p.dYTq + (int64_t)(h0 + hc) * p.ldt + prow0, p.sdYT, p.H, h0 + hc,
-                           prow0 / 64, (int)(p.ldt / 64));
-#pragma unroll
-            for (int q = 0; q < 16; ++q) v[q] = __builtin_bit_cast(float, (uint32_t)sX[hc][r0 + q] << 16);
-            mx_quant_row64(v, tid & 3, p.xgTq + (int64_t)(h0 + hc) * p.ldt + prow0, p.sxgT, p.H, h0 + hc,
-                           prow0 / 64, (int)(p.ldt / 64));
-            return;
+        for (int c = 0; c < 16; ++c) {
+            sY[c0 + c][r] = dyf[c];
+            sX[c0 + c][r] = slot < 0 ? (uint16_t)0 : f32_to_bf16_rne(xv[c]);
         }
-    }
-    intx4* dyt = (intx4*)(p.dYT + (int64_t)(h0 + hc) * p.ldt + prow0 + r0);
-    intx4* xgt = (intx4*)(p.xgT + (int64_t)(h0 + hc) * p.ldt + prow0 + r0);
+        __syncthreads();
+        // transposed tiles: thread -> column h0 + tid/4, rows prow0 + 16*(tid%4) .. +16;
+        // four consecutive lanes hold the column's 64 rows: two 32-row blocks
+        const int hc = tid >> 2, r0 = (tid & 3) * 16;
+        float v[16];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        intx4 a, b;
+        for (int q = 0; q < 16; ++q) v[q] = sY[hc][r0 + q];
+        mx_quant_row64(v, tid & 3, p.dYTq + (int64_t)(h0 + hc) * p.ldt + prow0, p.sdYT, p.H, h0 + hc,
+                       prow0 / 64, (int)(p.ldt / 64));
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            uint16_t y0, y1;
-            if constexpr (MXW) {
-                y0 = f32_to_bf16_rne(sY[hc][r0 + 8 * q + 2 * e]);
-                y1 = f32_to_bf16_rne(sY[hc][r0 + 8 * q + 2 * e + 1]);
-            } else {
-                y0 = sY[hc][r0 + 8 * q + 2 * e];
-                y1 = sY[hc][r0 + 8 * q + 2 * e + 1];
-            }
-            a[e] = (int)((uint32_t)y0 | ((uint32_t)y1 << 16));
-            b[e] = (int)((uint32_t)sX[hc][r0 + 8 * q + 2 * e] | ((uint32_t)sX[hc][r0 + 8 * q + 2 * e + 1] << 16));
-        }
-        dyt[q] = a;
-        xgt[q] = b;
+        for (int q = 0; q < 16; ++q) v[q] = __builtin_bit_cast(float, (uint32_t)sX[hc][r0 + q] << 16);
+        mx_quant_row64(v, tid & 3, p.xgTq + (int64_t)(h0 + hc) * p.ldt + prow0, p.sxgT, p.H, h0 + hc,
+                       prow0 / 64, (int)(p.ldt / 64));
     }
 }
 
@@ -164,43 +140,21 @@ void launch_rcomb_gather(const RcombArgs& a, int rpad, hipStream_t stream) {
         hipLaunchKernelGGL(rcomb_gather_kernel<false>, dim3(rpad / kTile, a.H / kTile), dim3(256), 0, stream, a);
 }
 
-__device__ __forceinline__ void unpack16_bf16(const intx4* src, float* f) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        const intx4 a = src[q];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            f[8 * q + 2 * e] = __builtin_bit_cast(float, (uint32_t)a[e] << 16);
-            f[8 * q + 2 * e + 1] = __builtin_bit_cast(float, (uint32_t)a[e] & 0xffff0000u);
-        }
-    }
-}
-
-__device__ __forceinline__ void pack16_bf16(const uint16_t* v, intx4* dst) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        intx4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = (int)((uint32_t)v[8 * q + 2 * e] | ((uint32_t)v[8 * q + 2 * e + 1] << 16));
-        dst[q] = o;
-    }
-}
-
-// SwiGLU backward, one workgroup per 64 padded rows x 64 intermediate columns:
-// row-major dG | dU for the bf16 input-gradient GEMM (only the rows of the
-// experts it runs: the MXFP8 experts take the quantised copy), transposed
-// dG | dU and h for the weight-gradient GEMMs (through LDS, so every store is
-// coalesced).  MXW (MXFP8 weight gradients): a block of rows before
-// *dgu_row0 writes the transposed dG | dU and h as E4M3 codes quantised
-// along the padded rows from their fp32 values (h zero on padding rows), a
-// block from it on writes bf16; the block lies inside one expert segment.
+// SwiGLU backward, one workgroup per 64 padded rows x 64 intermediate columns.
+// For the rows from *dgu_row0 on (the experts whose weight gradient, and so
+// input gradient, takes bf16 operands) it writes row-major dG | dU, operand of
+// the gate|up input-gradient GEMM and of the gate|up weight gradient, and
+// w * h (zero on padding rows), the down weight gradient's row operand; the
+// MXFP8 input gradient's rows take the quantised dG | dU.  MXW (MXFP8 weight
+// gradients): a block of rows before *dgu_row0 also writes dG | dU and h as
+// E4M3 codes quantised along the padded rows from their fp32 values (h zero
+// on padding rows), through LDS transposes; the block lies inside one expert
+// segment.
 template <bool MXW>
 __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdArgs p) {
-    using St = typename std::conditional<MXW, float, uint16_t>::type;
-    constexpr int kPitch = kTile + (MXW ? 1 : 2);
-    __shared__ St sG[kTile][kPitch];
-    __shared__ St sU[kTile][kPitch];
-    __shared__ St sH[kTile][kPitch];
+    __shared__ float sG[MXW ? kTile : 1][kTile + 1];
+    __shared__ float sU[MXW ? kTile : 1][kTile + 1];
+    __shared__ float sH[MXW ? kTile : 1][kTile + 1];
     const int prow0 = blockIdx.x * kTile, i0 = blockIdx.y * kTile;
     if (prow0 >= p.hdr->prows) return;
     const int tid = threadIdx.x;
@@ -226,71 +180,58 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(SwigluBwdArgs p) {
         unpack16_bf16((const intx4*)(p.GU + prow * 2 * I + i0 + c0), g);
         unpack16_bf16((const intx4*)(p.GU + prow * 2 * I + I + i0 + c0), u);
     }
-    // MXW: h of a padding row is zero, so it cannot raise its block's scale
-    const bool pad = MXW && p.prow_slot[prow] < 0;
-    uint16_t dg[16], du[16], hh[16];
-    float dgf[16], duf[16];
+    float dgf[16], duf[16], hf[16];
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
         const float sg = 1.0f / (1.0f + __expf(-g[c]));
         const float silu = g[c] * sg;
         dgf[c] = dh[c] * u[c] * (sg * (1.0f + g[c] * (1.0f - sg)));
         duf[c] = dh[c] * silu;
-        dg[c] = f32_to_bf16_rne(dgf[c]);
-        du[c] = f32_to_bf16_rne(duf[c]);
-        if constexpr (MXW) {
-            sG[c0 + c][r] = dgf[c];
-            sU[c0 + c][r] = duf[c];
-            sH[c0 + c][r] = pad ? 0.0f : silu * u[c];
-        } else {
-            hh[c] = f32_to_bf16_rne(silu * u[c]);
-            sG[c0 + c][r] = dg[c];
-            sU[c0 + c][r] = du[c];
-            sH[c0 + c][r] = hh[c];
-        }
+        hf[c] = silu * u[c];
     }
     if (prow >= (int64_t)*p.dgu_row0) {
-        pack16_bf16(dg, (intx4*)(p.dGU + prow * 2 * I + i0 + c0));
-        pack16_bf16(du, (intx4*)(p.dGU + prow * 2 * I + I + i0 + c0));
+        const float w = p.row_w[prow];
+        uint16_t v[16];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) v[c] = f32_to_bf16_rne(dgf[c]);
+        pack16_bf16(v, (intx4*)(p.dGU + prow * 2 * I + i0 + c0));
+#pragma unroll
+        for (int c = 0; c < 16; ++c) v[c] = f32_to_bf16_rne(duf[c]);
+        pack16_bf16(v, (intx4*)(p.dGU + prow * 2 * I + I + i0 + c0));
+#pragma unroll
+        for (int c = 0; c < 16; ++c) v[c] = w == 0.0f ? (uint16_t)0 : f32_to_bf16_rne(w * hf[c]);
+        pack16_bf16(v, (intx4*)(p.HW + prow * I + i0 + c0));
     }
     if (p.dGUq) {  // MXFP8 operand of the gate|up input-gradient GEMM, from the fp32 values
         mx_quant_row64(dgf, tid & 3, p.dGUq + prow * 2 * I + i0, p.sdGU, p.ldt, prow, i0 / 64, 2 * I / 64);
         mx_quant_row64(duf, tid & 3, p.dGUq + prow * 2 * I + I + i0, p.sdGU, p.ldt, prow, (I + i0) / 64, 2 * I / 64);
     }
-    __syncthreads();
-    const int ic = tid >> 2, r0 = (tid & 3) * 16;
     if constexpr (MXW) {
-        if (prow0 < *p.dgu_row0) {
-            // four consecutive lanes hold the column's 64 rows: two 32-row blocks
-            const int j = prow0 / 64, nj = (int)(p.ldt / 64);
-            float v[16];
+        if (prow0 >= *p.dgu_row0) return;
+        // h of a padding row is zero, so it cannot raise its block's scale
+        const bool pad = p.prow_slot[prow] < 0;
 #pragma unroll
-            for (int q = 0; q < 16; ++q) v[q] = sG[ic][r0 + q];
-            mx_quant_row64(v, tid & 3, p.dGUTq + (int64_t)(i0 + ic) * p.ldt + prow0, p.sdGUT, 2 * I, i0 + ic, j, nj);
-#pragma unroll
-            for (int q = 0; q < 16; ++q) v[q] = sU[ic][r0 + q];
-            mx_quant_row64(v, tid & 3, p.dGUTq + (int64_t)(I + i0 + ic) * p.ldt + prow0, p.sdGUT, 2 * I, I + i0 + ic,
-                           j, nj);
-#pragma unroll
-            for (int q = 0; q < 16; ++q) v[q] = sH[ic][r0 + q];
-            mx_quant_row64(v, tid & 3, p.HTq + (int64_t)(i0 + ic) * p.ldt + prow0, p.sHT, I, i0 + ic, j, nj);
-            return;
+        for (int c = 0; c < 16; ++c) {
+            sG[c0 + c][r] = dgf[c];
+            sU[c0 + c][r] = duf[c];
+            sH[c0 + c][r] = pad ? 0.0f : hf[c];
         }
+        __syncthreads();
+        // four consecutive lanes hold a column's 64 rows: two 32-row blocks
+        const int ic = tid >> 2, r0 = (tid & 3) * 16;
+        const int j = prow0 / 64, nj = (int)(p.ldt / 64);
+        float v[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) v[q] = sG[ic][r0 + q];
+        mx_quant_row64(v, tid & 3, p.dGUTq + (int64_t)(i0 + ic) * p.ldt + prow0, p.sdGUT, 2 * I, i0 + ic, j, nj);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) v[q] = sU[ic][r0 + q];
+        mx_quant_row64(v, tid & 3, p.dGUTq + (int64_t)(I + i0 + ic) * p.ldt + prow0, p.sdGUT, 2 * I, I + i0 + ic,
+                       j, nj);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) v[q] = sH[ic][r0 + q];
+        mx_quant_row64(v, tid & 3, p.HTq + (int64_t)(i0 + ic) * p.ldt + prow0, p.sHT, I, i0 + ic, j, nj);
     }
-    uint16_t v[16];
-    auto bf = [](St a) -> uint16_t {
-        if constexpr (MXW) return f32_to_bf16_rne(a);
-        else return a;
-    };
-#pragma unroll
-    for (int q = 0; q < 16; ++q) v[q] = bf(sG[ic][r0 + q]);
-    pack16_bf16(v, (intx4*)(p.dGUT + (int64_t)(i0 + ic) * p.ldt + prow0 + r0));
-#pragma unroll
-    for (int q = 0; q < 16; ++q) v[q] = bf(sU[ic][r0 + q]);
-    pack16_bf16(v, (intx4*)(p.dGUT + (int64_t)(I + i0 + ic) * p.ldt + prow0 + r0));
-#pragma unroll
-    for (int q = 0; q < 16; ++q) v[q] = bf(sH[ic][r0 + q]);
-    pack16_bf16(v, (intx4*)(p.HT + (int64_t)(i0 + ic) * p.ldt + prow0 + r0));
 }
 
 void launch_swiglu_bwd(const SwigluBwdArgs& a, int rpad, hipStream_t stream) {

@@ -48,66 +48,102 @@ void grouped_gemm_kernel(GemmArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// weight gradients: C[e] = A_e^T-rows x B_e^T-rows over every routed row of
-// expert e, minibatch by minibatch in order (a fixed summation order).
+// weight gradients: C[e] = A_e^T B_e over every routed row of expert e,
+// minibatch by minibatch in order (a fixed summation order), from token-major
+// operands: one read directly from its row-major buffer, the other (x or
+// dout) gathered from the token matrix by the layout's row -> token map.
 // ---------------------------------------------------------------------------
 
 // K sequence of expert e's rows: for each minibatch b its padded rows from
-// prs_b[e] on, in 64-row K stages up to the last one holding a routed row
-// (the dY-side operand is zero on every padding row, so the padding rows a
-// stage takes in add nothing); A and B copies of minibatch b lie a_mb / b_mb
-// bytes after minibatch 0's.
-struct SegmentK {
-    const int32_t* prs;   // [nmb][mt_ld] first padded row of each expert
-    const int32_t* rows;  // [nmb][mt_ld]
+// prs_b[e] on, in 64-row stages up to the last one holding a routed row (the
+// padding rows a stage takes in add nothing: the directly read operand is
+// zero on them, and the gathered one holds a real token's finite row).
+// Operand X of A, B is read directly (row prow of minibatch b at X + b * x_mb
+// + prow * ldx bytes) or, for X = kGather, gathered (row prow of minibatch b
+// is token map[b * map_mb + prow] of a [T][ldx-byte] matrix).  Wave w loads K
+// rows 8w .. 8w + 7 of a stage; their tokens come with one scalar load issued
+// a stage before they are used.
+template <int kGather>
+struct TokenK {
+    const int32_t* prs;
+    const int32_t* rows;
     int mt_ld, e, nmb;
-    int64_t a_mb, b_mb;
-    // current minibatch, K step within it, its step count and first row: the
-    // tile map is read only when the sequence enters the next minibatch
-    int b = -1, step = 0, nsteps = 0;
-    int64_t row0 = 0;
-    __device__ __forceinline__ void next(int64_t& a_off, int64_t& b_off) {
+    const char* A;
+    const char* B;
+    const int32_t* map;
+    int64_t a_mb, b_mb, map_mb;  // bytes, bytes, elements
+    uint32_t lda, ldb;           // bytes
+    uint32_t acol[2], bcol[2];   // this lane's column bytes (load q takes [q % 2])
+    int wave, hi;                // hi = lane / 32: the lane's K row of a load pair
+    int b = -1, step = 0, nsteps = 0, row0 = 0;
+    const char* da;              // minibatch b's copy of a directly read operand
+    const char* db;
+    const int32_t* mapb;         // minibatch b's row -> token map
+    intx8 tok;                   // tokens of rows 8 wave .. +7 of the stage next() returns
+    __device__ __forceinline__ void seek() {
+        // the tile map and row map are read-only here: read them through the
+        // constant address space (scalar loads, counted by lgkmcnt) so that
+        // the ring's vmcnt accounting sees only the ring's own loads
+        typedef const __attribute__((address_space(4))) int32_t cint;
         while (step >= nsteps && b + 1 < nmb) {
             ++b;
-            // the tile map is read-only here: read it through the constant
-            // address space (scalar loads, counted by lgkmcnt) so that the
-            // ring's vmcnt accounting sees only the ring's own loads
-            const __attribute__((address_space(4))) int32_t* cprs =
-                (const __attribute__((address_space(4))) int32_t*)prs;
-            const __attribute__((address_space(4))) int32_t* crows =
-                (const __attribute__((address_space(4))) int32_t*)rows;
-            row0 = cprs[(int64_t)b * mt_ld + e];
-            nsteps = ceil_div(crows[(int64_t)b * mt_ld + e], kBK8);
+            row0 = ((cint*)prs)[(int64_t)b * mt_ld + e];
+            nsteps = ceil_div(((cint*)rows)[(int64_t)b * mt_ld + e], kBK8);
             step = 0;
+            da = A + b * a_mb;
+            db = B + b * b_mb;
+            mapb = map + b * map_mb;
         }
-        const int64_t kbyte = (row0 + (int64_t)step * kBK8) * 2;
-        a_off = (int64_t)b * a_mb + kbyte;
-        b_off = (int64_t)b * b_mb + kbyte;
+        if (kGather && step < nsteps)
+            tok = *(const __attribute__((address_space(4))) intx8*)(mapb + row0 + step * kBK8 + 8 * wave);
+    }
+    // offsets stay below 4 GiB: a token matrix and one minibatch's copy of an
+    // operand are checked to on the host
+    __device__ __forceinline__ void next(const char* (&pa)[4], const char* (&pb)[4]) {
+        const uint32_t r = (uint32_t)(row0 + step * kBK8 + 8 * wave + hi);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            // the pair's two tokens as scalars, then one select per lane
+            const int t0 = __builtin_amdgcn_readfirstlane(tok[2 * q]);
+            const int t1 = __builtin_amdgcn_readfirstlane(tok[2 * q + 1]);
+            const uint32_t t = (uint32_t)(hi ? t1 : t0);
+            pa[q] = kGather == 1 ? A + (t * lda + acol[q & 1]) : da + ((r + 2 * q) * lda + acol[q & 1]);
+            pb[q] = kGather == 2 ? B + (t * ldb + bcol[q & 1]) : db + ((r + 2 * q) * ldb + bcol[q & 1]);
+        }
         ++step;
+        seek();
     }
 };
 
+template <int kGather>
 __global__ __attribute__((amdgpu_flat_work_group_size(kTileThreads, kTileThreads), amdgpu_waves_per_eu(2, 2)))
 void wgrad_kernel(WgradArgs p) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kTileSmem];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
     const WgradTiles tiles(p.M, p.N, p.mq, p.nq);
     int e, m0, n0;
     for (int it = 0; tiles.get(it, p.Et - p.e_begin, e, m0, n0); ++it) {
         e += p.e_begin;
         int KT = 0;
         for (int b = 0; b < p.nmb; ++b) KT += ceil_div(p.rows[(int64_t)b * p.mt_ld + e], kBK8);
-        uint32_t aoff[4], boff[4];
+        TokenK<kGather> kit;
+        kit.prs = p.prs; kit.rows = p.rows; kit.mt_ld = p.mt_ld; kit.e = e; kit.nmb = p.nmb;
+        kit.A = (const char*)p.A; kit.B = (const char*)p.B;
+        kit.lda = (uint32_t)p.lda * 2; kit.ldb = (uint32_t)p.ldb * 2; kit.a_mb = p.a_mb * 2; kit.b_mb = p.b_mb * 2;
+        kit.map = p.map; kit.map_mb = p.map_mb;
+        kit.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        kit.hi = lane >> 5;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = wave * 32 + i * 8 + (lane >> 3);
-            const int lchunk = (lane & 7) ^ swz8(r);
-            aoff[i] = (uint32_t)(((int64_t)min(m0 + r, p.M - 1) * p.ld + lchunk * 8) * 2);
-            boff[i] = (uint32_t)(((int64_t)min(n0 + r, p.N - 1) * p.ld + lchunk * 8) * 2);
+        for (int h = 0; h < 2; ++h) {
+            // M and N are multiples of 64: columns past them (a last tile's)
+            // read the matrix's last columns again and are not stored
+            const int c = kmajor_chunk(lane, h);
+            kit.acol[h] = (uint32_t)min(m0 + 8 * c, p.M - 8) * 2;
+            kit.bcol[h] = (uint32_t)min(n0 + 8 * c, p.N - 8) * 2;
         }
-        SegmentK kit{p.prs, p.rows, p.mt_ld, e, p.nmb, p.a_mb, p.b_mb};
+        kit.seek();
         floatx16 acc[2][4];
-        tile_mainloop8<2>(acc, smem, (const char*)p.A, aoff, (const char*)p.B, boff, KT, kit);
+        tile_mainloop8t(acc, smem, KT, kit);
         // columns < n_split go to C0, the rest to C1 (column - n_split); the
         // last expert writes to the shared-expert outputs when they are given
         const bool shared = p.Cs0 && e == p.Et - 1;
@@ -120,7 +156,12 @@ void wgrad_kernel(WgradArgs p) {
 void launch_wgrad(const WgradArgs& a, int grid, hipStream_t stream) {
     WgradArgs w = a;
     wgrad_cut(a.M, a.N, w.mq, w.nq);
-    hipLaunchKernelGGL(wgrad_kernel, dim3(grid), dim3(kTileThreads), 0, stream, w);
+    if (a.gather == 1)
+        hipLaunchKernelGGL(wgrad_kernel<1>, dim3(grid), dim3(kTileThreads), 0, stream, w);
+    else if (a.gather == 2)
+        hipLaunchKernelGGL(wgrad_kernel<2>, dim3(grid), dim3(kTileThreads), 0, stream, w);
+    else
+        hipLaunchKernelGGL(wgrad_kernel<0>, dim3(grid), dim3(kTileThreads), 0, stream, w);
 }
 
 void launch_grouped_gemm(const GemmArgs& a, GemmEpilogue epi, int grid, hipStream_t stream) {

@@ -2,6 +2,8 @@
 // one-launch-per-GEMM kernels and the persistent layer kernel.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -280,6 +282,185 @@ struct DenseK8 {
         ++kt;
     }
 };
+
+// ---------------------------------------------------------------------------
+// Token-major operands (the weight-gradient GEMMs, which contract over token
+// rows): a stage holds 64 K rows of 256 columns (512 bytes) of each operand,
+// in the same 2 x 64 KB ring and with the same direct-to-LDS loads as the
+// eight-wave tile (load q of wave w fills K rows 2(4w + q) and 2(4w + q) + 1,
+// lane l row 2(4w + q) + l/32 and LDS chunk l % 32).  The MFMA fragments need
+// eight K-consecutive values per lane; gfx950's transposing LDS read
+// ds_read_b64_tr_b16 gathers them: within each group of 16 lanes every lane
+// points at four consecutive 16-bit elements of a row, and lane j receives
+// element j % 4 of the rows that lanes j/4 + 4q point at (q = 0..3).  So lane
+// j = 4c + s of a group points at K row k0 + j/4, columns c0 + 4(j % 4) ..,
+// and receives column c0 + j at K rows k0 .. k0 + 3; two reads make a
+// fragment.  A K row's 16-byte chunk c sits at position c ^ 4(kr % 4), so the
+// four K rows of a read fall on distinct banks.
+// ---------------------------------------------------------------------------
+constexpr int kRowT = BM * 2;  // bytes of one K row of a stage
+static_assert(kRowT * kBK8 == kStageA8, "a token-major stage fills the same ring slot");
+
+// Logical 16-byte chunk that lane `lane`'s load q brings into its fixed LDS
+// position (K row 2(4w + q) + lane/32, chunk lane % 32); depends on q % 2 only.
+__device__ __forceinline__ int kmajor_chunk(int lane, int q) {
+    return (lane & 31) ^ (4 * (2 * (q & 1) + (lane >> 5)));
+}
+
+// acc = A^T B over KT2 stages of 64 token rows, A and B token-major (tile
+// columns m0.. of A, n0.. of B).  kit.next(pa, pb) yields each stage's eight
+// per-lane load addresses (pa[q], pb[q]: load q of this lane).  A k-step's
+// twelve fragment reads go out in one asm block together with four MFMAs of
+// the previous k-step and end with the block's own lgkmcnt wait, so the
+// reads' latency lies under those MFMAs.  (Written as builtins, the compiler,
+// unable to tell the transposing reads from the ring's direct-to-LDS writes,
+// waits for every load in flight before each of them.)  Same accumulator
+// layout and ring protocol as tile_mainloop8.
+template <class KIt>
+__device__ __forceinline__ void tile_mainloop8t(floatx16 (&acc)[2][4], uint8_t* smem, int KT2, KIt& kit) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
+    if (KT2 <= 0) return;
+    const char* pa[4];
+    const char* pb[4];
+    int issued = 0;
+    auto advance = [&]() {
+        if (issued < KT2) kit.next(pa, pb);
+        ++issued;
+    };
+    auto load1 = [&](int slot, int q) {
+        uint8_t* base = smem + slot * kStageBytes8 + wave * 4096;
+        if (q < 4)
+            __builtin_amdgcn_global_load_lds((gbl_cvoid*)pa[q], (lds_void*)(base + q * 1024), 16, 0, 0);
+        else
+            __builtin_amdgcn_global_load_lds((gbl_cvoid*)pb[q - 4], (lds_void*)(base + kStageA8 + (q - 4) * 1024),
+                                             16, 0, 0);
+    };
+    // this lane's read: group g = lane/16, j = lane % 16; K row 8(g/2) + j/4
+    // (+4 for the second read of a fragment), columns 16(g % 2) + 4(j % 4) of
+    // the fragment's 32; the swizzle term 4(j/4) lands in the chunk bits that
+    // hold the fragment's 32-column block
+    const int tg = lane >> 4, tj = lane & 15;
+    const int tsub = (8 * (tg >> 1) + (tj >> 2)) * kRowT + (2 * (tg & 1) + ((tj >> 1) & 1)) * 16 + 8 * (tj & 1);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+    const uint32_t ta = lds0 + tsub + 64 * (wm ^ (tj >> 2));
+    uint32_t tb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tb[j] = lds0 + kStageA8 + tsub + 256 * wn + 64 * (j ^ (tj >> 2));
+    typedef int intx2 __attribute__((ext_vector_type(2)));
+    // Reads of k-step kk of the stage in `slot` into (an, bn); with them the
+    // four MFMAs of fragment row I of the previous k-step, on (a, b), then the
+    // wait.  Every accumulator the asm MFMAs write is next read by an MFMA or
+    // a store at least four MFMAs later.
+    auto rd_mfma = [&](int slot, auto kkc, auto ic, const bf16x8 (&a)[2], const bf16x8 (&b)[4], bf16x8 (&an)[2],
+                       bf16x8 (&bn)[4]) {
+        constexpr int K0 = decltype(kkc)::value * 16 * kRowT;
+        constexpr int I = decltype(ic)::value;
+        const uint32_t so = slot * kStageBytes8;
+        intx2 r[12];
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %16 offset:%26\n"
+            "ds_read_b64_tr_b16 %1, %16 offset:%27\n"
+            "ds_read_b64_tr_b16 %2, %16 offset:%28\n"
+            "ds_read_b64_tr_b16 %3, %16 offset:%29\n"
+            "ds_read_b64_tr_b16 %4, %17 offset:%26\n"
+            "ds_read_b64_tr_b16 %5, %17 offset:%27\n"
+            "ds_read_b64_tr_b16 %6, %18 offset:%26\n"
+            "ds_read_b64_tr_b16 %7, %18 offset:%27\n"
+            "ds_read_b64_tr_b16 %8, %19 offset:%26\n"
+            "ds_read_b64_tr_b16 %9, %19 offset:%27\n"
+            "ds_read_b64_tr_b16 %10, %20 offset:%26\n"
+            "ds_read_b64_tr_b16 %11, %20 offset:%27\n"
+            "v_mfma_f32_32x32x16_bf16 %12, %22, %21, %12\n"
+            "v_mfma_f32_32x32x16_bf16 %13, %23, %21, %13\n"
+            "v_mfma_f32_32x32x16_bf16 %14, %24, %21, %14\n"
+            "v_mfma_f32_32x32x16_bf16 %15, %25, %21, %15\n"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+              "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]),
+              "+v"(acc[I][0]), "+v"(acc[I][1]), "+v"(acc[I][2]), "+v"(acc[I][3])
+            : "v"(ta + so), "v"(tb[0] + so), "v"(tb[1] + so), "v"(tb[2] + so), "v"(tb[3] + so), "v"(a[I]),
+              "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]), "i"(K0), "i"(K0 + 4 * kRowT), "i"(K0 + 256),
+              "i"(K0 + 4 * kRowT + 256)
+            : "memory");
+        an[0] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r[0], r[1], 0, 1, 2, 3));
+        an[1] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r[2], r[3], 0, 1, 2, 3));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            bn[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r[4 + 2 * j], r[5 + 2 * j], 0, 1, 2, 3));
+    };
+    auto mfma_row = [&](int i, const bf16x8 (&a)[2], const bf16x8 (&b)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+    };
+    using KS0 = std::integral_constant<int, 0>;
+    using KS1 = std::integral_constant<int, 1>;
+    using KS2 = std::integral_constant<int, 2>;
+    using KS3 = std::integral_constant<int, 3>;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    advance();
+#pragma unroll
+    for (int q = 0; q < 8; ++q) load1(0, q);
+    advance();
+#pragma unroll
+    for (int q = 0; q < 8; ++q) load1(1, q);
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    __syncthreads();
+    bf16x8 a0[2], b0[4], a1[2], b1[4];
+    {
+        // k-step 0 of stage 0: its reads cover no MFMA yet (acc is zero, so
+        // the block's four MFMAs on the zero fragments below add nothing)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) a1[i] = bf16x8{};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b1[j] = bf16x8{};
+        rd_mfma(0, KS0{}, I0{}, a1, b1, a0, b0);
+    }
+    int slot = 0;
+    for (int s = 0; s < KT2; ++s) {
+        __builtin_amdgcn_sched_barrier(0);
+        rd_mfma(slot, KS1{}, I0{}, a0, b0, a1, b1);
+        mfma_row(1, a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        rd_mfma(slot, KS2{}, I0{}, a1, b1, a0, b0);
+        mfma_row(1, a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        rd_mfma(slot, KS3{}, I0{}, a0, b0, a1, b1);
+        mfma_row(1, a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __syncthreads();
+        advance();  // addresses of stage s + 2
+        // the last k-step: fragment row 0's MFMAs with the A loads of stage
+        // s + 2 between them, then the next stage's first reads (a stale but
+        // in-bounds read after the last stage) under fragment row 1's MFMAs,
+        // then the B loads
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            acc[0][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1[m], a1[0], acc[0][m], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            load1(slot, m);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        rd_mfma(slot ^ 1, KS0{}, I1{}, a1, b1, a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 4; q < 8; ++q) load1(slot, q);
+        __builtin_amdgcn_sched_barrier(0);
+        slot ^= 1;
+    }
+    // the last asm MFMAs' results reach VALU reads in the caller's epilogue:
+    // wait states the compiler cannot count through the asm
+    asm volatile("s_nop 7\n s_nop 7\n s_nop 7" ::: "memory");
+}
 
 // How a tile treats the padding rows of an expert's last tile (with
 // p.rows_e): kPadNone runs every fragment, a half tile's too; kPadPerWave

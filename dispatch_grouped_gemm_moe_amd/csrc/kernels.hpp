@@ -167,11 +167,13 @@ hipError_t launch_mega(const MegaArgs& a, int grid, hipStream_t stream);
 struct SwigluBwdArgs {
     const uint16_t* dH;        // [R_pad][I]
     const uint16_t* GU;        // [R_pad][2I]
+    const float* row_w;        // [R_pad] each padded row's weight (0 on padding rows)
     const LayoutHeader* hdr;
-    uint16_t* dGU;             // [R_pad][2I]  dG | dU, rows from *dgu_row0 on
-    const int32_t* dgu_row0;   // first padded row of the experts whose input gradient runs in bf16
-    uint16_t* dGUT;            // [2I][ldt]    transposed dG | dU
-    uint16_t* HT;              // [I][ldt]     transposed h
+    // bf16 operands of the rows from *dgu_row0 on (the experts whose weight
+    // gradient, and so input gradient, takes bf16 operands):
+    uint16_t* dGU;             // [R_pad][2I]  dG | dU
+    uint16_t* HW;              // [R_pad][I]   w * h, zero on padding rows (the down weight gradient's row operand)
+    const int32_t* dgu_row0;
     int I;
     int64_t ldt;
     // MXFP8: fp32 inputs instead of dH / GU, and dG | dU also quantised along
@@ -185,8 +187,7 @@ struct SwigluBwdArgs {
     // rows before *dgu_row0 (the MXFP8 experts' segments) dG | dU and h
     // quantised along the padded rows from fp32, h zero on padding rows
     // (prow_slot < 0): codes [2I][ldt] / [I][ldt], scales in the operand layout
-    // [mx_groups(ldt)][2I][4] / [mx_groups(ldt)][I][4]; dGUT and HT then hold
-    // only the rows from *dgu_row0 on
+    // [mx_groups(ldt)][2I][4] / [mx_groups(ldt)][I][4]
     const int32_t* prow_slot;
     uint8_t* dGUTq;
     uint8_t* sdGUT;
@@ -195,15 +196,22 @@ struct SwigluBwdArgs {
 };
 void launch_swiglu_bwd(const SwigluBwdArgs& a, int rpad, hipStream_t stream);
 
-// Weight-gradient GEMM: C[e][m][n] = sum over expert e's padded rows r of every
-// minibatch of A[m][r] * B[n][r]; A, B are row-major [M or N][ld] copies, one
-// per minibatch, a_mb / b_mb bytes apart.  Padding rows must hold zeros in A
-// or B.  Columns n < n_split go to C0 [Et][M][n_split], the rest to
+// Weight-gradient GEMM from token-major operands: C[e][m][n] = sum over expert
+// e's padded rows r of every minibatch of A[r][m] * B[r][n].  Each operand is
+// either a row-major [rows][lda or ldb] buffer per minibatch (a_mb / b_mb
+// elements apart) or, for the one `gather` names (1: A, 2: B, 0: neither),
+// the token matrix [T][ld] whose row map[b * map_mb + r] is row r of
+// minibatch b.  Padding rows must hold zeros in the directly read operand
+// (the gathered one then reads a real token's row).  M and N are multiples of
+// 64.  Columns n < n_split go to C0 [Et][M][n_split], the rest to
 // C1 [Et][M][N - n_split]; with Cs0 set, the last expert writes to Cs0/Cs1.
 struct WgradArgs {
     const uint16_t* A;
     const uint16_t* B;
-    int64_t ld, a_mb, b_mb;
+    int64_t lda, ldb, a_mb, b_mb;
+    int gather;
+    const int32_t* map;  // [nmb][map_mb] row -> token (the layouts' prow_token)
+    int64_t map_mb;
     int M, N, n_split, Et, nmb, mt_ld;
     int e_begin;         // experts [e_begin, Et); C0 / C1 are still indexed by e
     const int32_t* prs;  // [nmb][mt_ld] first padded row of each expert, per minibatch
@@ -255,16 +263,13 @@ void launch_gather_rows(const uint16_t* x, int H, const int32_t* prow_token, con
 // Backward: reverse-combine gather over the padded rows of one minibatch.
 struct RcombArgs {
     const uint16_t* dout;      // [T][H]
-    const uint16_t* x;         // [T][H]
+    const uint16_t* x;         // [T][H] (read for the MXFP8 weight-gradient operands only)
     const uint16_t* Y;         // [R_pad][H] saved expert outputs of the minibatch
     const float* topk_w;       // [T][k]
     const int32_t* prow_token;
     const int32_t* prow_slot;
     const LayoutHeader* hdr;
-    uint16_t* dY;              // [R_pad][H], or NULL: not written
     float* row_w;              // [R_pad], or NULL: each padded row's weight (gate weight, 1 for the shared expert, 0 on padding)
-    uint16_t* dYT;             // [H][ldt]
-    uint16_t* xgT;             // [H][ldt]
     float* dgp;                // [R_pad][nhb] partial gate gradients
     float* dsel;               // [R_pad] zeroed
     int H, k, nhb;
@@ -278,8 +283,8 @@ struct RcombArgs {
     // MXFP8 weight-gradient operands, optional (both or neither, with dYq):
     // for the rows before *dyq_row_end, dY (from fp32) and x (zero on padding
     // rows) quantised along the padded rows, codes [H][ldt], scales in the
-    // operand layout [mx_groups(ldt)][H][4]; dYT and xgT then hold only the
-    // rows from *dyq_row_end on
+    // operand layout [mx_groups(ldt)][H][4].  (bf16 weight gradients need no
+    // copy: they read dout and x through the row map.)
     uint8_t* dYTq;
     uint8_t* sdYT;
     uint8_t* xgTq;

@@ -70,19 +70,22 @@ def test_data_movement_bytes():
 
 
 def test_backward_gather_bytes():
-    """Reverse-combine reads dout, x and Y rows; SwiGLU backward reads dH and
-    g|u (fp32 under MXFP8).  Each writes the weight-gradient operands
-    transposed (dY, x; dG|dU, h): bf16, or for routed rows with MXFP8 weight
-    gradients one code byte plus a 32nd of a scale byte per element.  The
-    input-gradient GEMMs' operands: row-major bf16 dG|dU for bf16 rows, MXFP8
-    codes of dY and dG|dU for routed rows under MXFP8."""
+    """Reverse-combine reads the dout row of every row and the Y row of every
+    routed row; SwiGLU backward reads dH and g|u (fp32 under MXFP8) and writes
+    row-major dG|dU and w*h for the rows whose weight gradients are bf16 (x
+    and dout reach those GEMMs through the row map, with no copy).  Under
+    MXFP8 the input-gradient GEMMs take codes + scales of dY and dG|dU for the
+    routed rows (one code byte plus a 32nd of a scale byte per element); with
+    MXFP8 weight gradients the routed rows' x rows are read as well, and dY,
+    x, dG|dU and h are written transposed as codes + scales instead of the
+    bf16 row-major dG|dU and w*h."""
     E, q = 8, 1 + 1 / 32
     R, Rr = T * (K + 1), T * K
     b = bench.role_bytes(T, H, I, K, E, True, False, True, True)
-    assert b["gather"] == R * (3 * H * 2 + 2 * H * 2) + R * (3 * I * 2 + 3 * I * 2 + 2 * I * 2)
+    assert b["gather"] == R * H * 2 + Rr * H * 2 + R * (3 * I * 2 + 3 * I * 2)
     bm = bench.role_bytes(T, H, I, K, E, True, True, True, True)
-    assert bm["gather"] == (R * (3 * H * 2 + 2 * H * 2) + Rr * H * q
-                            + R * (3 * I * 4 + 3 * I * 2) + T * 2 * I * 2 + Rr * 2 * I * q)
+    assert bm["gather"] == (R * H * 2 + Rr * H * 2 + Rr * H * q
+                            + R * (3 * I * 4 + 3 * I * 2) + Rr * 2 * I * q)
     bw = bench.role_bytes(T, H, I, K, E, True, True, True, True, True)
-    # the routed rows' four transposed operands shrink from 2 bytes to q per element
-    assert bm["gather"] - bw["gather"] == Rr * (2 * H + 3 * I) * (2 - q)
+    assert bw["gather"] == (R * H * 2 + Rr * H * 2 + Rr * H * 2 + Rr * 2 * H * q + Rr * H * q
+                            + R * 3 * I * 4 + T * 3 * I * 2 + Rr * 3 * I * q + Rr * 2 * I * q)
