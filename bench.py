@@ -248,7 +248,8 @@ def measure(moe, torch, w, bwd: bool, steps: int, warmup: int, comm_cus: int = 0
               "gemm_down": "mx_gemm_kernel<1>" if mx else "grouped_gemm_kernel<1>",
               "dgrad_down": "mx_gemm_kernel<1>" if mx else "grouped_gemm_kernel<1>",
               "dgrad_gate_up": "mx_gemm_kernel<1>" if mx else "grouped_gemm_kernel<1>",
-              "wgrad": "mx_wgrad_kernel" if mx_wgrad else "wgrad_kernel",
+              # bf16: <1> gate|up (x rows gathered), <2> down (dout rows gathered), one launch each
+              "wgrad": "mx_wgrad_kernel" if mx_wgrad else "wgrad_kernel<1|2>",
               "shared_gemm": "grouped_gemm_kernel (bf16 shared expert)",
               "layer": "mega_kernel<%s, %s>" % ("true" if mx else "false",
                                                  "true" if (not mx or w.shared_expert) else "false")}
@@ -424,10 +425,18 @@ def traffic_for(symbol: str, workload: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    ent = rec.get("kernels", {}).get("moe::%s@%s" % (symbol, workload))
-    if not ent or ent.get("source_sha256") != _source_sha():
-        return None
-    return ent["hbm_bytes_per_launch"]
+    # "name<a|b>": the mean over the instances name<a> and name<b>
+    names = [symbol]
+    if "|" in symbol and symbol.endswith(">"):
+        base, inner = symbol[:-1].split("<", 1)
+        names = ["%s<%s>" % (base, v) for v in inner.split("|")]
+    vals = []
+    for nm in names:
+        ent = rec.get("kernels", {}).get("moe::%s@%s" % (nm, workload))
+        if not ent or ent.get("source_sha256") != _source_sha():
+            return None
+        vals.append(ent["hbm_bytes_per_launch"])
+    return sum(vals) / len(vals)
 
 
 def _kernel_symbol(name: str) -> str:
@@ -484,6 +493,8 @@ def summarize_traffic(fetch_csv: str, write_csv: str, workload: str, copy_mib: i
     here = os.path.dirname(os.path.abspath(__file__))
     out = os.path.join(here, "profiles", "traffic.json")
     rec = json.load(open(out)) if os.path.exists(out) else {"kernels": {}}
+    sha = _source_sha()  # entries taken on other sources are stale: drop them
+    rec["kernels"] = {k: v for k, v in rec.get("kernels", {}).items() if v.get("source_sha256") == sha}
     rec["note"] = ("HBM bytes per launch = mean FETCH_SIZE * fetch_factor + mean WRITE_SIZE * write_factor "
                    "(KiB -> bytes); the factors make a plain %d MiB elementwise copy read and write "
                    "exactly %d MiB" % (copy_mib, copy_mib))
@@ -496,7 +507,7 @@ def summarize_traffic(fetch_csv: str, write_csv: str, workload: str, copy_mib: i
             "dispatches": len(fetch[sym]), "fetch_kib": fk, "write_kib": wk,
             "fetch_factor": f_fac, "write_factor": w_fac,
             "hbm_bytes_per_launch": (fk * f_fac + wk * w_fac) * 1024.0,
-            "source_sha256": _source_sha()}
+            "source_sha256": sha}
     with open(out, "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
     print(json.dumps({k: v["hbm_bytes_per_launch"] for k, v in rec["kernels"].items()}, indent=1))
