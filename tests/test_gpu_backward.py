@@ -60,3 +60,36 @@ def test_backward_bitwise_repeatable(gpu_lib):
     b = layer.backward(inp.dout)
     for n in a:
         assert torch.equal(a[n], b[n]), n
+
+
+@pytest.mark.parametrize("shared", [False, True], ids=["routed", "shared"])
+def test_backward_empty_and_sparse_segments(gpu_lib, shared):
+    """Minibatches of 12 tokens over 8 experts (k = 2): most (minibatch,
+    expert) segments hold a few rows or none, and the last expert is never
+    chosen (its router bias lowered by 1e4).  The weight gradients' K sequence
+    then skips empty segments and stops inside ragged ones; the unused
+    expert's weight gradients must be exactly zero and every gradient within
+    the bf16 tolerance of the oracle."""
+    import dispatch_grouped_gemm_moe_amd as moe
+    from gpu_harness import Layer
+    w = _wl("bwd_sparse" + ("_shared" if shared else ""), T=60, H=256, I=128, E=8, k=2, minibatch=12,
+            shared_expert=shared)
+    inp = make_inputs(w, with_dout=True)
+    inp.bias = torch.zeros(w.E)
+    inp.bias[-1] = -1e4
+    _, idx, _ = O.route(O.as_f32(inp.x), inp.Wr, inp.bias, w.k)
+    assert not (idx == w.E - 1).any()
+    seg_rows = [np.bincount(idx[t0:t0 + w.minibatch].ravel(), minlength=w.E) for t0 in range(0, w.T, w.minibatch)]
+    assert sum(int((c[:-1] == 0).sum()) for c in seg_rows) > 0, "no empty segment among the used experts"
+    layer = Layer(inp)
+    assert moe.moe_query_sizes(layer.cfg).minibatch == w.minibatch
+    layer.forward()
+    got = layer.backward(inp.dout)
+    ref = O.layer_backward(inp, fwd=O.layer_forward(inp, keep=True, mx=False))
+    for n in ("dWg", "dWu", "dWd"):
+        assert not got[n][w.E - 1].any(), n
+    names = ["dx", "dWg", "dWu", "dWd", "dWr", "dgate"] + (["dWsg", "dWsu", "dWsd"] if shared else [])
+    errs = {n: O.rel_inf_err(got[n].numpy(), ref[n]) for n in names}
+    print(w.name, "segment rows per minibatch", [c.tolist() for c in seg_rows], " ".join("%s %.2e" % kv for kv in errs.items()))
+    for n, e in errs.items():
+        assert e <= BF16_TOL, (n, e)
