@@ -251,8 +251,10 @@ def measure(moe, torch, w, bwd: bool, steps: int, warmup: int, comm_cus: int = 0
               # bf16: <1> gate|up (x rows gathered), <2> down (dout rows gathered), one launch each
               "wgrad": "mx_wgrad_kernel" if mx_wgrad else "wgrad_kernel<1|2>",
               "shared_gemm": "grouped_gemm_kernel (bf16 shared expert)",
+              # bf16 tiles compiled in: a bf16 layer, or the shared expert's
+              # tiles of an MXFP8 inference forward
               "layer": "mega_kernel<%s, %s>" % ("true" if mx else "false",
-                                                 "true" if (not mx or w.shared_expert) else "false")}
+                                                 "true" if (not mx or (w.shared_expert and not bwd)) else "false")}
     by_sym = {}
     for kd, fl in flops.items():
         n, ms = kt[kd]
@@ -390,8 +392,9 @@ def role_flops(T: int, H: int, I: int, k: int, shared: bool, mx: bool, bwd: bool
     4*H*I, down 2*H*I), for the forward, the input gradients and the weight
     gradients.  MXFP8 runs the routed experts on the scaled-MFMA kernels and
     the shared expert in bf16: its backward input-gradient launches are their
-    own kind, and its forward GEMMs run in the persistent layer kernel when
-    that runs (their own kind otherwise).  With MXFP8 weight gradients
+    own kind, and so are its forward GEMMs, except in an inference forward
+    through the persistent layer kernel, which runs them as tiles of its own
+    (a training forward runs them as two launches before the layer kernel).  With MXFP8 weight gradients
     (mx_wgrad) the weight-gradient kind is the routed experts' scaled-MFMA
     launches and the shared expert's bf16 weight gradients join its kind.
     bf16 runs both in the same launches."""
@@ -406,9 +409,13 @@ def role_flops(T: int, H: int, I: int, k: int, shared: bool, mx: bool, bwd: bool
     if mx and shared_rows and bwd:  # the shared expert's bf16 input-gradient (and weight-gradient) GEMMs
         flops["shared_gemm"] = 6.0 * H * I * shared_rows * (2 if mx_wgrad else 1)
     if layer_kernel:
-        # the persistent layer kernel runs both forward GEMMs (and combine),
-        # under MXFP8 with the shared expert's bf16 tiles in the same launch
-        flops["layer"] = flops.pop("gemm_gate_up") + flops.pop("gemm_down") + shared_fwd
+        # the persistent layer kernel runs both forward GEMMs (and combine);
+        # under MXFP8 the shared expert's bf16 tiles run in it for inference
+        # and as launches of their own before it in training
+        in_layer = shared_fwd if not bwd else 0.0
+        flops["layer"] = flops.pop("gemm_gate_up") + flops.pop("gemm_down") + in_layer
+        if shared_fwd and bwd:
+            flops["shared_gemm"] = flops.get("shared_gemm", 0.0) + shared_fwd
     elif shared_fwd:  # per-GEMM forward: the shared expert's launches are timed as their own kind
         flops["shared_gemm"] = flops.get("shared_gemm", 0.0) + shared_fwd
     return flops

@@ -52,7 +52,7 @@ struct Plan {
     size_t ws_xq, ws_sx;  // MXFP8 codes and scales of x
     // saved (bytes): routing, then per minibatch g|u [rpad][2I] (bf16, or fp32
     // under MXFP8) and Y [rpad][H]
-    size_t sv_idx, sv_w, sv_mb0, sv_mb, sv_y, saved;
+    size_t sv_idx, sv_w, sv_mb0, sv_mb, sv_y, sv_hs, saved;
     // backward workspace (bytes)
     size_t wb_wrt, wb_mt, wb_prs, wb_rows, wb_lay0, lay_bytes, ly_hdr, ly_prow_token, ly_tok_prow, ly_prow_slot;
     size_t wb_dgu, wb_hw, wb_dsel, wb_dh, wb_dx, wb_dgp, wb_roww, ws_bwd;
@@ -227,6 +227,10 @@ moe_status make_plan(const moe_cfg* c, Plan* p) {
     p->sv_mb0 = align_up(p->sv_w + Tk * 4);
     p->sv_y = align_up(rp * 2 * I * (p->mx ? 4 : 2));  // g|u: fp32 under MXFP8 (its quantisation input)
     p->sv_mb = align_up(p->sv_y + rp * H * 2);
+    // MXFP8 with the shared expert: its bf16 h rows, written by the shared
+    // expert's own forward launches before the layer kernel
+    p->sv_hs = p->sv_mb;
+    if (p->mx && p->shared) p->sv_mb = align_up(p->sv_hs + rp * I * 2);
     p->saved = p->sv_mb0 + nmb * p->sv_mb;
 
     o = kAlign;  // device status word
@@ -544,9 +548,32 @@ static moe_status enqueue_fwd(const moe_cfg* cfg, const Plan& p, const moe_weigh
     const int Sg = p.slots / p.group, ng = ceil_div(p.nmb, p.group);
     const bool ring_ok = ng <= Sg || (Sg >= 2 && (p.comm_cus > 0 || saved || Sg >= 3));
     if (p.mega && ring_ok && ncu >= p.comm_cus + 16) {
+        // Training under MXFP8 with the shared expert: the shared expert's two
+        // bf16 GEMMs run first, each as one launch over every minibatch,
+        // writing its saved g|u, its h and its Y rows; the layer kernel then
+        // runs the routed experts' scaled-MFMA tiles only (the instance
+        // without bf16 tile code) and its combine adds the shared rows.
+        const bool shared_first = p.mx && p.shared && saved != nullptr;
+        if (shared_first) {
+            uint8_t* sv0 = (uint8_t*)saved + p.sv_mb0;
+            GemmArgs ga = g1;  // experts [E, E + 1): the shared expert
+            ga.a_row_map = (const int32_t*)(lay0 + p.ly_prow_token); ga.map_mb = (int64_t)p.lay_bytes / 4;
+            ga.mt_start = mt_all; ga.prow_start = prs_all; ga.rows_e = rows_all; ga.hdr = nullptr;
+            ga.nmb = p.nmb; ga.mt_ld = p.Et + 1;
+            ga.C = (uint16_t*)(sv0 + p.sv_hs); ga.c_mb = (int64_t)p.sv_mb / 2;
+            ga.GUf = (float*)sv0; ga.gu_mb = (int64_t)p.sv_mb / 4;
+            TIMED(MOE_K_SHARED_GEMM, s, launch_grouped_gemm(ga, kEpiSwiGLU, grid, s));
+            GemmArgs gb = g2;
+            gb.A = (const uint16_t*)(sv0 + p.sv_hs); gb.a_mb = (int64_t)p.sv_mb / 2;
+            gb.mt_start = mt_all; gb.prow_start = prs_all; gb.rows_e = rows_all; gb.hdr = nullptr;
+            gb.nmb = p.nmb; gb.mt_ld = p.Et + 1;
+            gb.C = (uint16_t*)(sv0 + p.sv_y); gb.c_mb = (int64_t)p.sv_mb / 2;
+            TIMED(MOE_K_SHARED_GEMM, s, launch_grouped_gemm(gb, kEpiStore, grid, s));
+        }
         MegaArgs a{};
         a.T = p.T; a.H = p.H; a.I = p.I; a.k = p.k; a.Mb = p.Mb; a.nmb = p.nmb; a.S = p.slots;
-        a.comm = p.comm_cus; a.e_end = p.Et; a.e_mx = p.mx ? p.E : 0; a.with_shared = p.shared ? 1 : 0;
+        a.comm = p.comm_cus; a.e_end = shared_first ? p.E : p.Et; a.e_mx = p.mx ? p.E : 0;
+        a.with_shared = p.shared ? 1 : 0;
         a.ld_tok_prow = p.ld_tok_prow; a.mx = p.mx ? 1 : 0; a.group = p.group;
         a.lay0 = lay0; a.lay_bytes = p.lay_bytes; a.ly_prow_token = p.ly_prow_token; a.ly_tok_prow = p.ly_tok_prow;
         a.mt_all = mt_all; a.prs_all = prs_all; a.rows_all = rows_all; a.mt_ld = p.Et + 1;

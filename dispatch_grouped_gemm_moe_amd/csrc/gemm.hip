@@ -40,6 +40,8 @@ void grouped_gemm_kernel(GemmArgs p) {
             if (q.row_scale) q.row_scale += b * p.rs_mb;
             if (q.C) q.C += b * p.c_mb;
             if (q.Cf) q.Cf += b * p.c_mb;
+            if (q.GU) q.GU += b * p.gu_mb;
+            if (q.GUf) q.GUf += b * p.gu_mb;
         }
         int e, ml, ntile;
         tile_coords(q.mt_start, q.e_begin, q.e_end, NT, v, e, ml, ntile);

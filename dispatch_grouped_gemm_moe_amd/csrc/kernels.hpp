@@ -66,14 +66,14 @@ struct GemmArgs {
     float* GUf;
     float* Cf;                 // kEpiStore, optional: fp32 output instead of C
     const int32_t* rows_e;     // optional [Et] rows of each expert: padding fragments get no MFMAs
-    // Several minibatches in one launch (kEpiStore, nmb > 1): minibatch b's
-    // tile map, row starts and row counts sit b * mt_ld ints after mt_start /
-    // prow_start / rows_e, its
-    // A rows (a_row_map NULL) a_mb elements, its row map map_mb ints, its
-    // row scales rs_mb floats and its C / Cf rows c_mb elements after
-    // minibatch 0's; the tiles run minibatch by minibatch.
+    // Several minibatches in one launch (nmb > 1): minibatch b's tile map,
+    // row starts and row counts sit b * mt_ld ints after mt_start /
+    // prow_start / rows_e, its A rows (a_row_map NULL) a_mb elements, its row
+    // map map_mb ints, its row scales rs_mb floats, its C / Cf rows c_mb
+    // elements and its g | u rows (GU / GUf) gu_mb elements after minibatch
+    // 0's; the tiles run minibatch by minibatch.
     int nmb, mt_ld;
-    int64_t a_mb, c_mb, map_mb, rs_mb;
+    int64_t a_mb, c_mb, map_mb, rs_mb, gu_mb;
     // kEpiStore, optional: output row r is acc * row_scale[r] (fp32) before
     // it is rounded and stored
     const float* row_scale;

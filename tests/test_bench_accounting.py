@@ -23,8 +23,10 @@ def test_every_row_counted_once(shared, mx, bwd, layer, mxw):
     assert all(v > 0 for v in f.values())
     if layer:
         assert "gemm_gate_up" not in f and "gemm_down" not in f
-        # the layer kernel runs every forward GEMM, the shared expert's included
-        assert f["layer"] == 6 * HI * rows
+        # the layer kernel runs every forward GEMM, the shared expert's
+        # included, except in MXFP8 training, where the shared expert's two
+        # bf16 GEMMs run as launches of their own before it
+        assert f["layer"] == 6 * HI * (T * K if (mx and shared and bwd) else rows)
     else:
         assert "layer" not in f
     if bwd:
@@ -38,7 +40,8 @@ def test_mxfp8_shared_expert_kinds():
     # input gradients are their own kind (bf16)
     f = bench.role_flops(T, H, I, K, True, True, True, True)
     assert f["dgrad_down"] == 2 * HI * T * K and f["dgrad_gate_up"] == 4 * HI * T * K
-    assert f["shared_gemm"] == 6 * HI * T
+    # training: the shared expert's forward launches and its input gradients
+    assert f["shared_gemm"] == 2 * 6 * HI * T
     # forward only, through the layer kernel: no shared-expert launches at all
     assert "shared_gemm" not in bench.role_flops(T, H, I, K, True, True, False, True)
     # forward only, one launch per GEMM: the shared expert's forward launches
