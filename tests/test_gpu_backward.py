@@ -30,6 +30,9 @@ BWD_CASES = [
     _wl("bwd_chunks2", T=7000, H=256, I=128, E=8, k=2, minibatch=2000, router_bias="normal"),
     # ... and three chunks of one minibatch
     _wl("bwd_chunks1", T=6000, H=256, I=128, E=8, k=2, minibatch=2600),
+    # many experts with few rows each (most segments one half tile or empty)
+    _wl("bwd_e64", T=600, H=256, I=128, E=64, k=6, minibatch=256),
+    _wl("bwd_e256", T=300, H=128, I=64, E=256, k=16, minibatch=150, shared_expert=True),
 ]
 
 

@@ -47,6 +47,9 @@ MXB_CASES = [
     # backward chunks: two of two minibatches; with the shared expert one chunk of five
     _wl("mxb_chunks2", T=7000, H=256, I=128, E=8, k=2, minibatch=2000, router_bias="zipf"),
     _wl("mxb_chunks_shared", T=5000, H=256, I=128, E=8, k=2, minibatch=1200, shared_expert=True),
+    # many experts with few rows each (most segments one half tile or empty)
+    _wl("mxb_e64", T=600, H=256, I=128, E=64, k=6, minibatch=256),
+    _wl("mxb_e256", T=300, H=128, I=64, E=256, k=16, minibatch=150, shared_expert=True),
 ]
 
 

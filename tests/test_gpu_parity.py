@@ -101,6 +101,7 @@ FWD_CASES = [
     _wl("fwd_shared", T=200, H=384, I=192, E=6, k=2, minibatch=128, shared_expert=True),
     _wl("fwd_k1", T=96, H=128, I=64, E=3, k=1),
     _wl("fwd_k64", T=200, H=64, I=64, E=4, k=2, minibatch=128, shared_expert=True),  # one K stage per GEMM
+    _wl("fwd_e256", T=300, H=128, I=64, E=256, k=16, minibatch=150, shared_expert=True),  # top-16 of 256
 ]
 
 
