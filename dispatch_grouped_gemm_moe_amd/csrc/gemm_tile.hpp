@@ -630,7 +630,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs p, int e, int ml, int n
 // fastest.
 // ---------------------------------------------------------------------------
 struct WgradTiles {
-    int mlo, nlo, bmt, cnt, per, local;
+    int mlo, nlo, bmt, bnt, cnt, per, local, G;
     __device__ WgradTiles(int M, int N, int mq, int nq) {
         const int MT = ceil_div(M, BM), NT = ceil_div(N, BN);
         const int xcd = blockIdx.x & 7, bm = xcd % mq, bn = xcd / mq;
@@ -639,7 +639,12 @@ struct WgradTiles {
         mlo = bm * MT / mq;
         nlo = bn * NT / nq;
         bmt = (bm + 1) * MT / mq - mlo;
-        cnt = bmt * ((bn + 1) * NT / nq - nlo);
+        bnt = (bn + 1) * NT / nq - nlo;
+        cnt = bmt * bnt;
+        // a block's M tiles in groups of G, a group's tiles together (M
+        // fastest): the XCD's `per` workgroups then run a G x bnt patch at a
+        // time, each A panel read by bnt of them at once and each B panel by G
+        G = per / bnt > 1 ? per / bnt : 1;
     }
     // this workgroup's tile number `it` over experts [0, Et): false past the last
     __device__ bool get(int it, int Et, int& e, int& m0, int& n0) const {
@@ -647,8 +652,10 @@ struct WgradTiles {
         if (cnt == 0 || li >= Et * cnt) return false;
         e = li / cnt;
         const int t = li - e * cnt;
-        m0 = (mlo + t % bmt) * BM;
-        n0 = (nlo + t / bmt) * BN;
+        const int g = t / (G * bnt), tt = t - g * G * bnt;
+        const int gs = bmt - g * G < G ? bmt - g * G : G;  // M tiles of group g
+        m0 = (mlo + g * G + tt % gs) * BM;
+        n0 = (nlo + tt / gs) * BN;
         return true;
     }
 };
