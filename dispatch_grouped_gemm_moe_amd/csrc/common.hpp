@@ -45,6 +45,13 @@ struct LayoutHeader {
     int32_t prows;    // padded rows over all experts (a multiple of kSegRows)
 };
 
+// One entry of a layout table (tile and row starts, row counts), which an
+// earlier launch wrote and no kernel changes while it is read: a scalar load,
+// so waiting for it does not wait for the vector loads and stores in flight.
+__device__ __forceinline__ int32_t ld_layout(const int32_t* p) {
+    return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+
 // Rows of M tile ml of an expert whose padded rows run from seg0 to seg1:
 // BM, or kSegRows for a last tile that is a half tile.
 __host__ __device__ __forceinline__ int tile_rows_of(int seg0, int seg1, int ml) {

@@ -18,7 +18,9 @@ namespace moe {
 template <int EPI>
 __global__ __attribute__((amdgpu_flat_work_group_size(kTileThreads, kTileThreads), amdgpu_waves_per_eu(2, 2)))
 void grouped_gemm_kernel(GemmArgs p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[kTileSmem];
+    // plain-store tiles chain (the ring plus the staging block past it)
+    constexpr bool kChain = EPI == kEpiStore;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kChain ? kTileSmem + kStgBytes : kTileSmem];
     const int NT = ceil_div(p.N, BN);
     const int total = launch_tiles(p);
     const int G = gridDim.x, per = G >> 3;
@@ -26,10 +28,9 @@ void grouped_gemm_kernel(GemmArgs p) {
     // one XCD take consecutive tiles so that they share weight and row tiles
     // in that XCD's L2.
     const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
-    for (int it = 0;; ++it) {
-        int v = it * G + xcd * per + local;
-        if (v >= total) break;
-        GemmArgs q = p;
+    // tile v: its minibatch's arguments and its coordinates
+    auto tile_of = [&](int v, GemmArgs& q, int& e, int& ml, int& ntile) {
+        q = p;
         if (p.nmb > 1) {
             const int b = minibatch_of_tile(p, v);
             q.mt_start += (int64_t)b * p.mt_ld;
@@ -43,9 +44,28 @@ void grouped_gemm_kernel(GemmArgs p) {
             if (q.GU) q.GU += b * p.gu_mb;
             if (q.GUf) q.GUf += b * p.gu_mb;
         }
-        int e, ml, ntile;
         tile_coords(q.mt_start, q.e_begin, q.e_end, NT, v, e, ml, ntile);
-        gemm_tile<EPI>(q, e, ml, ntile, smem);
+    };
+    const bool chain = kChain && tiles_chain(p);
+    TileEntry en;
+    for (int it = 0;; ++it) {
+        const int v = it * G + xcd * per + local;
+        if (v >= total) break;
+        GemmArgs q;
+        int e, ml, ntile;
+        tile_of(v, q, e, ml, ntile);
+        if constexpr (kChain) {
+            TileLink ln;
+            if (chain && v + G < total) {
+                GemmArgs qn;
+                int e2, ml2, nt2;
+                tile_of(v + G, qn, e2, ml2, nt2);
+                ln = tile_link(q, e, ml, ntile, qn, e2, ml2, nt2);
+            }
+            gemm_tile<EPI, kPadPerWave, true>(q, e, ml, ntile, smem, &en, &ln);
+        } else {
+            gemm_tile<EPI>(q, e, ml, ntile, smem);
+        }
     }
 }
 

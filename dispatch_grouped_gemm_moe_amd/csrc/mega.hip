@@ -129,30 +129,38 @@ __device__ __forceinline__ const int32_t* mt_of(const MegaArgs& a, int b) { retu
 
 __device__ __forceinline__ int tokens_of(const MegaArgs& a, int b) { return min(a.Mb, a.T - b * a.Mb); }
 
+// Tile-table entry; kS: a scalar load (the bf16 kernel, whose chained tiles
+// must not wait for loads in flight; in the MXFP8 kernels the extra scalar
+// registers cost vector-register spills).
+template <bool kS>
+__device__ __forceinline__ int mt_entry(const int32_t* p) { return kS ? ld_layout(p) : *p; }
+
 // M tiles of experts [0, e) summed over the minibatches [b0, b1)
+template <bool kS>
 __device__ __forceinline__ int group_mtiles_before(const MegaArgs& a, int b0, int b1, int e) {
     int n = 0;
-    for (int b = b0; b < b1; ++b) n += mt_of(a, b)[e] - mt_of(a, b)[0];
+    for (int b = b0; b < b1; ++b) n += mt_entry<kS>(mt_of(a, b) + e) - mt_entry<kS>(mt_of(a, b));
     return n;
 }
 
 // Tile lv of a GEMM phase over minibatches [b0, b1): expert-major, then N
 // tile, then M tile, the M tiles of expert e running over minibatch b0's, then
 // b0+1's, ...: returns the minibatch b and the tile (e, ml, ntile) in it.
+template <bool kS>
 __device__ __forceinline__ void group_tile(const MegaArgs& a, int b0, int b1, int NT, int lv, int& b, int& e,
                                            int& ml, int& ntile) {
     int lo = 0, hi = a.e_end - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (group_mtiles_before(a, b0, b1, mid) * NT <= lv) lo = mid; else hi = mid - 1;
+        if (group_mtiles_before<kS>(a, b0, b1, mid) * NT <= lv) lo = mid; else hi = mid - 1;
     }
     e = lo;
-    const int loc = lv - group_mtiles_before(a, b0, b1, e) * NT;
-    const int mte = group_mtiles_before(a, b0, b1, e + 1) - group_mtiles_before(a, b0, b1, e);
+    const int loc = lv - group_mtiles_before<kS>(a, b0, b1, e) * NT;
+    const int mte = group_mtiles_before<kS>(a, b0, b1, e + 1) - group_mtiles_before<kS>(a, b0, b1, e);
     ntile = loc / mte;
     int m = loc - ntile * mte;
     for (b = b0; b < b1 - 1; ++b) {
-        const int mb = mt_of(a, b)[e + 1] - mt_of(a, b)[e];
+        const int mb = mt_entry<kS>(mt_of(a, b) + e + 1) - mt_entry<kS>(mt_of(a, b) + e);
         if (m < mb) break;
         m -= mb;
     }
@@ -199,10 +207,11 @@ template <bool kMx, bool kBf16>
 __global__ __attribute__((amdgpu_flat_work_group_size(kTileThreads, kTileThreads), amdgpu_waves_per_eu(2, 2)))
 void mega_kernel(MegaArgs a) {
     static_assert(kMx || kBf16, "a bf16 layer runs bf16 tiles");
-    constexpr int kSmem = kMx ? (kMxSmem > kTileSmem ? kMxSmem : kTileSmem) : kTileSmem;
+    // the bf16 kernel's down tiles chain: the ring plus the staging block past it
+    constexpr int kSmem = kMx ? (kMxSmem > kTileSmem ? kMxSmem : kTileSmem) : kTileSmem + kStgBytes;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[kSmem];
-    // wait result broadcast: the ring's last dword, free between tiles (the
-    // mainloop has drained its loads and every wave passed a barrier)
+    // wait result broadcast: the last dword, free between tiles (a phase's last
+    // tile has drained its loads, and every wave passed a barrier)
     int& s_flag = *(int*)(smem + kSmem - 4);
     int* gu_done = a.counters;
     int* d_done = a.counters + a.nmb;
@@ -241,7 +250,7 @@ void mega_kernel(MegaArgs a) {
             for (int b = b0; b < b1; ++b) n += ceil_div(tokens_of(a, b), kCombTilesTok);
             return n;
         }
-        return group_mtiles_before(a, b0, b1, a.e_end) * (kind == kGateUp ? NT1 : NT2);
+        return group_mtiles_before<!kMx>(a, b0, b1, a.e_end) * (kind == kGateUp ? NT1 : NT2);
     };
     auto counter_of = [&](int kind, int j) -> int* {
         return kind == kGateUp ? gu_done + j : (kind == kDown ? d_done + j : comb_done + j);
@@ -251,6 +260,7 @@ void mega_kernel(MegaArgs a) {
     int64_t qstart = 0;
     int qtiles = phase_tiles(cur.kind, cur.j);
     bool ready = false;  // inputs of the current phase waited for
+    TileEntry en;        // how the next chained down tile starts
     for (int it = 0;; ++it) {
         const int64_t v = (int64_t)it * G + xcd * per + local;
         while (more && v >= qstart + qtiles) {  // done with this phase: publish
@@ -286,7 +296,7 @@ void mega_kernel(MegaArgs a) {
             continue;
         }
         int b, e, ml, ntile;
-        group_tile(a, b0, b1, kind == kGateUp ? NT1 : NT2, lv, b, e, ml, ntile);
+        group_tile<!kMx>(a, b0, b1, kind == kGateUp ? NT1 : NT2, lv, b, e, ml, ntile);
         const uint8_t* lay = a.lay0 + (int64_t)b * a.lay_bytes;
         const int32_t* mt = a.mt_all + (int64_t)b * a.mt_ld;
         const int32_t* prs = a.prs_all + (int64_t)b * a.mt_ld;
@@ -332,7 +342,23 @@ void mega_kernel(MegaArgs a) {
                 gg.A = (const uint16_t*)(slot + a.sl_h);
                 gg.mt_start = mt; gg.prow_start = prs; gg.hdr = hdr; gg.rows_e = rows;
                 gg.C = Y;
-                gemm_tile<kEpiStore, kPadPerWave>(gg, e, ml, ntile, smem);
+                if constexpr (!kMx) {
+                    // the workgroup's next down tile of this phase starts on
+                    // stages loaded with this tile's last two
+                    TileLink ln;
+                    const int64_t vn = v + G;
+                    if (vn < qstart + qtiles && tiles_chain(gg)) {
+                        int b2, e2, ml2, nt2;
+                        group_tile<!kMx>(a, b0, b1, NT2, (int)(vn - qstart), b2, e2, ml2, nt2);
+                        GemmArgs gn = a.g2;
+                        gn.A = (const uint16_t*)(a.slot0 + (int64_t)(b2 % a.S) * a.slot_bytes + a.sl_h);
+                        gn.prow_start = a.prs_all + (int64_t)b2 * a.mt_ld;
+                        ln = tile_link(gg, e, ml, ntile, gn, e2, ml2, nt2);
+                    }
+                    gemm_tile<kEpiStore, kPadPerWave, true>(gg, e, ml, ntile, smem, &en, &ln);
+                } else {
+                    gemm_tile<kEpiStore, kPadPerWave>(gg, e, ml, ntile, smem);
+                }
             }
         }
     }

@@ -22,7 +22,7 @@ namespace moe {
 
 #pragma clang fp contract(off)
 
-constexpr int kRouteWaveTokens = 4;                       // tokens per wave
+constexpr int kRouteWaveTokens = 2;                       // tokens per wave
 constexpr int kRouteThreads = 512;                        // eight waves
 constexpr int kRouteTokens = kRouteWaveTokens * kRouteThreads / kWave;  // per workgroup
 constexpr int kRouteEC = 32;                              // experts per accumulation pass
@@ -42,11 +42,15 @@ __device__ __forceinline__ float lane_tree64(float v) {
     return v;
 }
 
-// A wave scores 4 tokens against up to 32 experts per pass: lane l runs the
-// partial sums p[l] of all 128 (token, expert) pairs over h = l, l+64, ...
+// A wave scores 2 tokens against up to 32 experts per pass: lane l runs the
+// partial sums p[l] of all 64 (token, expert) pairs over h = l, l+64, ...
 // The router weight rows of each 64-wide h chunk (32 experts) are staged once
-// per workgroup in LDS, double-buffered, and read by its 8 waves (32 tokens),
-// so a Wr element is fetched once per 32 tokens instead of once per 4.
+// per workgroup in LDS, double-buffered, and read by its 8 waves (16 tokens),
+// so a Wr element is fetched once per 16 tokens instead of once per 2.  Two
+// tokens per wave keep the kernel at 128 VGPRs, two workgroups per CU; four
+// tokens need 190 VGPRs, one workgroup per CU (0.24 against 0.35 ms at 16384
+// tokens, H 7168, 32 experts), and at one token the LDS reads of the staged
+// weights cost as much as the FMAs they feed.
 template <bool kVec4>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ Wr, const float* __restrict__ bias,
