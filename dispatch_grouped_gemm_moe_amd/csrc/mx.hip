@@ -61,15 +61,16 @@ void launch_mx_quant(const uint16_t* src, int64_t rows, int cols, int layout, ui
 template <int EPI>
 __global__ __attribute__((amdgpu_flat_work_group_size(kTileThreads, kTileThreads), amdgpu_waves_per_eu(2, 2)))
 void mx_gemm_kernel(MxGemmArgs p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[kMxSmem];
+    // plain-store tiles chain (the ring plus the staging block past it)
+    constexpr bool kChain = EPI == kEpiStore;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[kChain ? kMxSmem + kMxStgBytes : kMxSmem];
     const int NT = ceil_div(p.N, BN);
     const int total = launch_tiles(p);
     const int G = gridDim.x, per = G >> 3;
     const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
-    for (int it = 0;; ++it) {
-        int v = it * G + xcd * per + local;
-        if (v >= total) break;
-        MxGemmArgs q = p;
+    // tile v: its minibatch's arguments and its coordinates
+    auto tile_of = [&](int v, MxGemmArgs& q, int& e, int& ml, int& ntile) {
+        q = p;
         if (p.nmb > 1) {
             const int b = minibatch_of_tile(p, v);
             q.mt_start += (int64_t)b * p.mt_ld;
@@ -80,9 +81,28 @@ void mx_gemm_kernel(MxGemmArgs p) {
             if (q.C) q.C += b * p.c_mb;
             if (q.Cf) q.Cf += b * p.c_mb;
         }
-        int e, ml, ntile;
         tile_coords(q.mt_start, q.e_begin, q.e_end, NT, v, e, ml, ntile);
-        mx_gemm_tile<EPI>(q, e, ml, ntile, smem);
+    };
+    const bool chain = kChain && mx_tiles_chain(p);
+    TileEntry en;
+    for (int it = 0;; ++it) {
+        const int v = it * G + xcd * per + local;
+        if (v >= total) break;
+        MxGemmArgs q;
+        int e, ml, ntile;
+        tile_of(v, q, e, ml, ntile);
+        if constexpr (kChain) {
+            MxLink ln;
+            if (chain && v + G < total) {
+                MxGemmArgs qn;
+                int e2, ml2, nt2;
+                tile_of(v + G, qn, e2, ml2, nt2);
+                ln = mx_tile_link(q, e, ml, ntile, qn, e2, ml2, nt2);
+            }
+            mx_gemm_tile<EPI, kPadPerWave, true>(q, e, ml, ntile, smem, &en, &ln);
+        } else {
+            mx_gemm_tile<EPI>(q, e, ml, ntile, smem);
+        }
     }
 }
 

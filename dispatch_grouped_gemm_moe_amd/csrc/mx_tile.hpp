@@ -29,23 +29,41 @@ static_assert(kEpiRows * (kEpiPitch8 + 2 * kEpiPitch32) <= kMxSmem - 4,
               "the staged SwiGLU block must fit the ring (the layer kernel keeps its last dword)");
 static_assert(kEpiRows * kEpiPitch64 <= kMxSmem, "the staged fp32 block must fit the ring");
 
+// Chained MXFP8 tiles (as the bf16 ones, gemm_tile.hpp): the staging block of
+// a chained tile's bf16 output sits past the ring, 32 rows of 512 bytes (the
+// ring leaves 28 KB of LDS).  MxLink carries the successor's load addresses as
+// differences from this tile's, per wave: A code rows, B code rows and this
+// lane's scale dwords.
+constexpr int kMxStgRows = 32;
+constexpr int kMxStgBytes = kMxStgRows * kStgPitch;
+static_assert(kMxSmem + kMxStgBytes <= 160 * 1024, "ring and staging block fit the LDS");
+struct MxLink {
+    int64_t da = 0, db = 0, ds = 0;  // successor minus this tile: A codes, B codes, scale source
+    bool next = false;
+};
+
 // One 256 x 256 output tile (expert e, M tile ml of the expert, N tile ntile)
 // of the MXFP8 grouped GEMM with its epilogue, by 512 threads; smem is the
 // kMxSmem LDS ring.  Wave w (wm = w/2, wn = w%2) owns fragments i = 0, 1 at
 // tile rows 128i + 32wm .. +31 and j = 0..3 at columns 128wn + 32j .. +31;
 // only the first NV row fragments (those holding a valid row of the expert's
 // last tile) get MFMAs and fragment reads.
-template <int EPI, int NV>
-__device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, int ntile, uint8_t* smem) {
+// kChain: the tile starts as en says, loads its successor's stages 0 and 1
+// with the two loads past its last stage when ln.next, and (bf16 output)
+// stages its output past the ring; smem then holds kMxSmem + kMxStgBytes.
+template <int EPI, int NV, bool kChain = false>
+__device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, int ntile, uint8_t* smem,
+                                             TileEntry en = {}, MxLink ln = {}) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar LDS bases
     const int wm = wave >> 1, wn = wave & 1;
     const int KT = p.K / 64, KS = (KT + 1) / 2;
-    const int seg0 = p.prow_start[e];
+    auto lay = [&](const int32_t* q) -> int { return kChain ? ld_layout(q) : *q; };
+    const int seg0 = lay(p.prow_start + e);
     const int prow0 = seg0 + ml * BM;
     // BM rows, or kSegRows for an expert's last tile when it is a half tile
     // (NV is then at most 1); rows past it load the tile's own rows again
-    const int trows = tile_rows_of(seg0, p.prow_start[e + 1], ml);
+    const int trows = tile_rows_of(seg0, lay(p.prow_start + e + 1), ml);
     const int n0 = ntile * BN;
 
     // Code loads: instruction i fills tile rows 32*wave + 8i .. +7 (lane/8 the
@@ -85,23 +103,46 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
     // stage (odd K steps) the second K step's code chunks repeat the first's
     // and the upper half of the stage's scale dwords is zero; neither is used.
     auto issue = [&](int s_, int slot) {
-        const int s = s_ < KS ? s_ : KS - 1;
-        // a half stage's second K step repeats the first: the lanes of the
-        // upper chunks step back 64 bytes
-        const int back = 2 * s + 1 >= KT ? himask : 0;
-        const uint32_t kb = (uint32_t)s * 128;
         uint8_t* st = smem + slot * kMxStageBytes;
         uint8_t* base = st + (wave * 32) * kMxRow;
+        if constexpr (kChain) {
+            // past the last stage, the successor's stage s_ - KS (a full
+            // stage); one load sequence, its bases picked by scalar selects
+            // (a branch to a second sequence costs vector registers)
+            const bool nx = ln.next && s_ >= KS;
+            const int s = nx ? s_ - KS : (s_ < KS ? s_ : KS - 1);
+            const int back = !nx && 2 * s + 1 >= KT ? himask : 0;
+            const char* ab = a_base + (nx ? ln.da : 0);
+            const char* bb = b_base + (nx ? ln.db : 0);
+            const int64_t so = (int64_t)s * s_kstride + (nx ? ln.ds : 0);
+            const uint32_t kb = (uint32_t)s * 128;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_global_load_lds((gbl_cvoid*)(a_base + aoff[i] + kb - ((back >> i) & 1) * 64),
-                                             (lds_void*)(base + i * 1024), 16, 0, 0);
+            for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_global_load_lds((gbl_cvoid*)(ab + aoff[i] + kb - ((back >> i) & 1) * 64),
+                                                 (lds_void*)(base + i * 1024), 16, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_global_load_lds((gbl_cvoid*)(b_base + boff[i] + kb - ((back >> i) & 1) * 64),
-                                             (lds_void*)(base + kMxStageA + i * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((gbl_cvoid*)(s_lane + (int64_t)s * s_kstride),
-                                         (lds_void*)(st + kMxStageSA + wave * 256), 4, 0, 0);
+            for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_global_load_lds((gbl_cvoid*)(bb + boff[i] + kb - ((back >> i) & 1) * 64),
+                                                 (lds_void*)(base + kMxStageA + i * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((gbl_cvoid*)(s_lane + so), (lds_void*)(st + kMxStageSA + wave * 256), 4,
+                                             0, 0);
+        } else {
+            const int s = s_ < KS ? s_ : KS - 1;
+            // a half stage's second K step repeats the first: the lanes of the
+            // upper chunks step back 64 bytes
+            const int back = 2 * s + 1 >= KT ? himask : 0;
+            const uint32_t kb = (uint32_t)s * 128;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_global_load_lds((gbl_cvoid*)(a_base + aoff[i] + kb - ((back >> i) & 1) * 64),
+                                                 (lds_void*)(base + i * 1024), 16, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                __builtin_amdgcn_global_load_lds((gbl_cvoid*)(b_base + boff[i] + kb - ((back >> i) & 1) * 64),
+                                                 (lds_void*)(base + kMxStageA + i * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((gbl_cvoid*)(s_lane + (int64_t)s * s_kstride),
+                                             (lds_void*)(st + kMxStageSA + wave * 256), 4, 0, 0);
+        }
     };
     const int fr = lane & 31, half = lane >> 5;
     const int fsw = swz8(fr);  // a fragment's rows differ from fr by multiples of 32
@@ -164,20 +205,25 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
     // more), refills its slot with stage s+2 and runs its second K step while
     // reading the first K step of stage s+1.  An odd number of K steps ends on
     // a half stage, whose one K step is read by then.
+    // A chained tile's stages 0 and 1 went out with its predecessor's last
+    // two: stage 0 was waited for before the predecessor's last barrier.
     static_assert(kMxStages == 2, "the vmcnt immediates below assume 2 stages of 9 loads");
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    issue(0, 0);
-    issue(1, 1);
-    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-    __syncthreads();
+    const int s0 = kChain ? en.slot0 : 0;
+    if (!(kChain && en.pre)) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        issue(0, s0);
+        issue(1, s0 ^ 1);
+        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+        __syncthreads();
+    }
     intx8 fa[2], fb[4];
     int fsa[2], fsb[4];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) read_a(0, 0, i, fa[i], fsa[i]);
+    for (int i = 0; i < NV; ++i) read_a(s0, 0, i, fa[i], fsa[i]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) read_b(0, 0, j, fb[j], fsb[j]);
-    int slot = 0;
+    for (int j = 0; j < 4; ++j) read_b(s0, 0, j, fb[j], fsb[j]);
+    int slot = s0;
     for (int s = 0; s < KT / 2; ++s) {
         mfmas_then(std::integral_constant<int, 0>{}, slot, 1, fa, fb, fsa, fsb);
         Interleave<4 * NV, 0, 8 + 2 * NV>::run();
@@ -199,6 +245,62 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
             for (int j = 0; j < 4; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], acc[i][j], 0, 0, 0, fsb[j], 0,
                                                                              fsa[i]);
+    }
+
+    if constexpr (kChain && EPI == kEpiStore) {
+        if (!p.Cf) {
+            // bf16 output through the block past the ring, 32 rows at a time:
+            // tile rows 64 bl + 32 h .. are fragment bl/2 of the two waves
+            // with wm == 2 (bl % 2) + h, row lane % 32.  Chunk c of staged row
+            // r at c ^ r; asm LDS accesses and LDS-only barriers, so nothing
+            // waits for the successor's loads in flight (as gemm_tile).
+            if (!ln.next) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+            const uint32_t stg = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem + kMxSmem;
+            int tid = threadIdx.x;  // opaque: the lane addresses are formed here, not kept live
+            asm volatile("" : "+v"(tid));
+            const int rs = tid & 31;
+            const uint32_t wrow = stg + rs * kStgPitch + 8 * ((tid >> 5) & 1);
+            const int wc0 = ((tid >> 6) & 1) * 16;
+            const int r0 = tid >> 5, ch = tid & 31;  // copy-out: rows r0, r0 + 16 of a block, chunk ch
+            const bool col_in = ch * 16 < (p.N - n0) * 2;
+#pragma unroll
+            for (int bl = 0; bl < 4; ++bl) {
+                if (bl * kEpiRows >= trows) break;  // a half tile stores its kSegRows rows only
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    if (wm == 2 * (bl & 1) + h) {
+                        const int i = bl >> 1;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const uint32_t la = wrow + (((wc0 + 4 * j + q) ^ rs) << 4);
+                                const uint2 pv = pack_bf16x4(acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                                             acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                                const u32x2 v2 = {pv.x, pv.y};
+                                asm volatile("ds_write_b64 %0, %1" ::"v"(la), "v"(v2) : "memory");
+                            }
+                    }
+                    lds_barrier();
+                    const uint32_t ra0 = stg + r0 * kStgPitch + ((ch ^ r0) << 4);
+                    const uint32_t ra1 = stg + (r0 + 16) * kStgPitch + ((ch ^ (r0 + 16)) << 4);
+                    u32x4 d0, d1;
+                    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                                 : "=&v"(d0), "=&v"(d1)
+                                 : "v"(ra0), "v"(ra1)
+                                 : "memory");
+                    char* dst = (char*)(p.C + (int64_t)(prow0 + bl * 64 + h * 32 + r0) * p.ldc + n0) + ch * 16;
+                    if (col_in) {
+                        *(u32x4*)dst = d0;
+                        *(u32x4*)(dst + (int64_t)p.ldc * 2 * 16) = d1;
+                    }
+                    lds_barrier();
+                }
+            }
+            return;
+        }
     }
 
     // The tile leaves through LDS, 64 rows at a time (whole-line stores).
@@ -310,21 +412,64 @@ __device__ __forceinline__ void mx_tile_body(const MxGemmArgs p, int e, int ml, 
 // One 256 x 256 output tile (expert e, M tile ml, N tile ntile) of the MXFP8
 // grouped GEMM; with p.rows_e the padding fragments of an expert's last tile
 // get no MFMAs as kPad says (gemm_tile.hpp).
-template <int EPI, int kPad = kPadPerWave>
-__device__ __forceinline__ void mx_gemm_tile(const MxGemmArgs p, int e, int ml, int ntile, uint8_t* smem) {
+// kChain: as mx_tile_body; *en is set for the successor.
+template <int EPI, int kPad = kPadPerWave, bool kChain = false>
+__device__ __forceinline__ void mx_gemm_tile(const MxGemmArgs p, int e, int ml, int ntile, uint8_t* smem,
+                                             TileEntry* en = nullptr, const MxLink* ln = nullptr) {
+    const TileEntry te = kChain ? *en : TileEntry{};
+    const MxLink tl = kChain ? *ln : MxLink{};
+    if constexpr (kChain) {
+        en->pre = tl.next;
+        en->slot0 = te.slot0 ^ (((p.K / 64 + 1) / 2) & 1);  // the successor's stage 0 follows this tile's stages
+    }
     if (kPad == kPadNone || !p.rows_e) {  // every fragment (a half tile's rows past kSegRows are not stored)
-        mx_tile_body<EPI, 2>(p, e, ml, ntile, smem);
+        mx_tile_body<EPI, 2, kChain>(p, e, ml, ntile, smem, te, tl);
         return;
     }
     // fragment i of this wave holds tile rows 128i + 32wm .. +31 (a half
     // tile has at most kSegRows valid rows, so NV <= 1)
-    const int valid = p.rows_e[e] - ml * BM;
+    const int valid = (kChain ? ld_layout(p.rows_e + e) : p.rows_e[e]) - ml * BM;
     const int w32 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 7) * 32;
     switch (valid > 128 + w32 ? 2 : (valid > w32 ? 1 : 0)) {
-        case 2: mx_tile_body<EPI, 2>(p, e, ml, ntile, smem); break;
-        case 1: mx_tile_body<EPI, 1>(p, e, ml, ntile, smem); break;
-        default: mx_tile_body<EPI, 0>(p, e, ml, ntile, smem); break;
+        case 2: mx_tile_body<EPI, 2, kChain>(p, e, ml, ntile, smem, te, tl); break;
+        case 1: mx_tile_body<EPI, 1, kChain>(p, e, ml, ntile, smem, te, tl); break;
+        default: mx_tile_body<EPI, 0, kChain>(p, e, ml, ntile, smem, te, tl); break;
     }
+}
+
+// Whether a launch's kEpiStore MXFP8 tiles can chain: bf16 output, A rows
+// read directly, whole N tiles, and an even number of K steps, at least four
+// (two full stages).
+__device__ __forceinline__ bool mx_tiles_chain(const MxGemmArgs& p) {
+    return p.C && !p.Cf && !p.a_row_map && p.N % BN == 0 && p.K % 128 == 0 && p.K >= 256;
+}
+
+// The link from tile (p, e, ml, ntile) to its successor (pn, e2, ml2, nt2) of
+// the same launch.  mx_tile_body's code rows of a lane are prow0 + (r &
+// (trows - 1)), r = 32 wave + 8i + lane/8 (so r >= 128 for waves 4..7), B rows
+// n0 + r; its scale dword comes from A row prow0 + (srow & (trows - 1)),
+// srow = 64 (wave % 4) + lane (>= 128 for waves 2, 3), for waves 0..3 and from
+// B row n0 + srow for waves 4..7.
+__device__ __forceinline__ MxLink mx_tile_link(const MxGemmArgs& p, int e, int ml, int ntile, const MxGemmArgs& pn,
+                                               int e2, int ml2, int nt2) {
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int seg0 = ld_layout(p.prow_start + e), prow0 = seg0 + ml * BM;
+    const int trows = tile_rows_of(seg0, ld_layout(p.prow_start + e + 1), ml);
+    const int seg2 = ld_layout(pn.prow_start + e2), prow2 = seg2 + ml2 * BM;
+    const int trows2 = tile_rows_of(seg2, ld_layout(pn.prow_start + e2 + 1), ml2);
+    // upper-half rows of a half tile fold back by kSegRows
+    const int fold = (trows < BM ? kSegRows : 0) - (trows2 < BM ? kSegRows : 0);
+    MxLink ln;
+    ln.da = ((const char*)pn.A - (const char*)p.A) + ((int64_t)(prow2 - prow0) + (wave >= 4 ? fold : 0)) * p.lda;
+    ln.db = ((const char*)(pn.B + (int64_t)e2 * pn.b_stride) - (const char*)(p.B + (int64_t)e * p.b_stride)) +
+            (int64_t)(nt2 - ntile) * BN * p.K;
+    if (wave >= 4)
+        ln.ds = ((const char*)(pn.SB + (int64_t)e2 * pn.sb_stride) - (const char*)(p.SB + (int64_t)e * p.sb_stride)) +
+                (int64_t)(nt2 - ntile) * BN * 4;
+    else
+        ln.ds = ((const char*)pn.SA - (const char*)p.SA) + ((int64_t)(prow2 - prow0) + (wave >= 2 ? fold : 0)) * 4;
+    ln.next = true;
+    return ln;
 }
 
 }  // namespace moe
