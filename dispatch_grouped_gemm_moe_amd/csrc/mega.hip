@@ -14,10 +14,10 @@
 // (one workgroup per minibatch) and the dispatch gather is the GEMM's own
 // row-mapped direct-to-LDS load, so the token-moving work is combine.  The
 // GEMM workgroups walk one static sequence of tiles, dealt XCD-aware as in the
-// one-GEMM-per-launch kernels: step s holds gate|up(s), then combine(s-2) when
-// combine runs as tiles, then down(s-1):
-//   gate|up(0), gate|up(1), down(0), gate|up(2), [combine(0),] down(1), ...
-// The skew puts a whole phase between a phase and the one that reads its
+// one-GEMM-per-launch kernels: step s holds gate|up(s), then down(s-1), then
+// combine(s-2) when combine runs as tiles:
+//   gate|up(0), gate|up(1), down(0), gate|up(2), down(1), [combine(0),] ...
+// The skew puts at least one phase between a phase and the one that reads its
 // output, so inputs are rarely unfinished when a workgroup reaches them, and a
 // workgroup waits at most once per phase.  Combine runs either
 //   * on comm dedicated workgroups (blockIdx < comm), minibatch by minibatch,
@@ -59,19 +59,31 @@ constexpr int kCombTilesTok = 16;  // tokens per combine tile
 // Cursor over the phases of the tile sequence, in units of minibatch groups
 // (a group is `group` consecutive minibatches whose GEMM tiles run as one
 // phase, so an expert's weight panels serve the row tiles of all of them).
-// Step s holds gate|up(s), then (with combine tiles) combine(s-2), then
-// down(s-1), each only if its group exists: gate|up(0), gate|up(1), down(0),
-// gate|up(2), combine(0), down(1), ...  Every phase depends only on phases at
-// least one phase earlier.
+// Step s holds gate|up(s), then down(s-1), then (with combine tiles)
+// combine(s-2), each only if its group exists: gate|up(0), gate|up(1),
+// down(0), gate|up(2), down(1), combine(0), down(2), combine(1), combine(2).
+// Every phase depends only on phases at least one phase earlier, so a
+// workgroup's wait finds the phase it needs drained by the others while it
+// ran the phase in between; only the last combine follows its down phase
+// closely.  With combine(s-2) before down(s-1) (comb_first), combine(j) came
+// right after down(j) for the last two groups (each a wait for the slowest
+// workgroup's down tiles); that order stays for the layer whose Y rows live
+// in a ring of three groups, where gate|up(s) waits for combine(s-3) to free
+// the slot and would otherwise come right after it.
 struct PhaseCursor {
     int s = 0, slot = -1, kind = 0, j = 0;
-    __device__ bool next(int ng, bool with_combine) {
+    __device__ bool next(int ng, bool with_combine, bool comb_first) {
         for (;;) {
             if (++slot > 2) { slot = 0; ++s; }
             if (s > ng + 1) return false;
-            if (slot == 0) { kind = kGateUp; j = s; }
-            else if (slot == 1) { if (!with_combine) continue; kind = kCombine; j = s - 2; }
-            else { kind = kDown; j = s - 1; }
+            if (slot == 0) {
+                kind = kGateUp; j = s;
+            } else if ((slot == 1) == comb_first) {
+                if (!with_combine) continue;
+                kind = kCombine; j = s - 2;
+            } else {
+                kind = kDown; j = s - 1;
+            }
             if (j >= 0 && j < ng) return true;
         }
     }
@@ -258,7 +270,8 @@ void mega_kernel(MegaArgs a) {
         return kind == kGateUp ? gu_done + j : (kind == kDown ? d_done + j : comb_done + j);
     };
     PhaseCursor cur;
-    bool more = cur.next(ng, comb_tiles);
+    const bool comb_first = y_in_ring && Sg == 3;
+    bool more = cur.next(ng, comb_tiles, comb_first);
     int64_t qstart = 0;
     int qtiles = phase_tiles(cur.kind, cur.j);
     bool ready = false;  // inputs of the current phase waited for
@@ -269,7 +282,7 @@ void mega_kernel(MegaArgs a) {
             const bool dropped = a.debug_drop && g == 0 && cur.kind == kGateUp && cur.j == 0;
             if (!dropped) signal_counter(counter_of(cur.kind, cur.j));
             qstart += qtiles;
-            more = cur.next(ng, comb_tiles);
+            more = cur.next(ng, comb_tiles, comb_first);
             if (more) qtiles = phase_tiles(cur.kind, cur.j);
             ready = false;
         }
