@@ -49,6 +49,10 @@ CASES = [
     (_wl("lk_mx_saved", T=900, H=512, I=256, E=4, k=2, minibatch=160, prec="mxfp8"), 3, 8, True, LK),
     (_wl("lk_mx_tiles", T=900, H=512, I=256, E=4, k=2, minibatch=128, prec="mxfp8"), 0, 0, False, LK),
     (_wl("lk_mx_three_slots", T=1200, H=512, I=256, E=4, k=2, minibatch=128, prec="mxfp8"), 3, 0, False, LK),
+    # four one-minibatch slot groups with Y in the ring: down(s-1) runs before
+    # combine(s-2), and gate|up waits for the combine four groups back
+    (_wl("lk_four_slots", T=1500, H=256, I=128, E=8, k=2, minibatch=192, router_bias="normal"), 4, 0, False, LK),
+    (_wl("lk_mx_four_slots", T=1200, H=512, I=256, E=4, k=2, minibatch=128, prec="mxfp8"), 4, 0, False, LK),
     # minibatches grouped into phases (ring slots = 3 groups; ragged last group)
     (_wl("lk_group2", T=1500, H=256, I=128, E=8, k=2, minibatch=192, router_bias="normal"), 6, 0, False, LK),
     (_wl("lk_group3_saved", T=1500, H=256, I=128, E=8, k=2, minibatch=160), 9, 0, True, LK),
